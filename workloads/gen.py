@@ -1,0 +1,206 @@
+"""Seeded synthetic inputs for a Csa2Config, in the stored formats the hot path reads.
+
+Recipe (all draws from one torch.Generator seeded with ``seed`` on ``device``):
+
+* q, main latent rows, SWA rows, indexer query and index-key rows: N(0,1),
+  or N(0,1)/sqrt(dim) when ``value_scale == "inv_sqrt_d"`` (dim = the latent
+  dim 512; the same factor is used for the 128-dim index vectors).  Stored
+  rows are drawn directly in their post-RoPE form: an isotropic Gaussian pair
+  is invariant under rotation, so no rotation is needed to get the right
+  distribution.
+* attn_sink and the indexer head weights w: N(0,1).
+* decode positions: context-1 for every sequence, or (ragged) uniform in
+  [0, context-1] with the first sequences pinned to 0, 1, window-1, window and
+  context-1.
+* REINDEX candidates: per query, min(n_blocks, visible blocks) distinct block
+  ids drawn uniformly among the visible blocks, always containing the newest
+  (partly filled) block, sorted ascending, -1 padded.
+* FP8-E4M3 rows: per-row float32 scale amax/448, values cast with torch's
+  float8_e4m3fn conversion.  FP8 indexer query: one float32 scale per (row,
+  head), folded into w (w_eff = w * scale), as the anatomy page's indexer
+  figure describes.
+* FP4-E2M1 rows: one E8M0 scale per 32 elements, 2^ceil(log2(amax/6)); the
+  scaled values are rounded to the nearest E2M1 magnitude (ties to the even
+  code) and packed two per byte, element 2i in the low nibble.
+
+Nothing here scores, selects, normalises or rotates.
+"""
+
+import math
+
+import torch
+
+from .configs import Csa2Config
+
+_E2M1_MAG = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _normal(g, shape, device, std, dtype=torch.float32):
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(dtype)
+
+
+def store_dense(x, dtype):
+    if dtype == "f32":
+        return x.to(torch.float32).contiguous()
+    if dtype == "bf16":
+        return x.to(torch.bfloat16).contiguous()
+    raise ValueError(dtype)
+
+
+def encode_fp8_rows(x):
+    """x float32 [..., D] -> (codes uint8 [..., D], row scale float32 [...])."""
+    amax = x.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    codes = (x / scale.unsqueeze(-1)).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.contiguous(), scale.to(torch.float32).contiguous()
+
+
+def encode_fp4_rows(x):
+    """x float32 [..., D] -> (packed uint8 [..., D/2], E8M0 scales uint8 [..., D/32])."""
+    shp = x.shape
+    d = shp[-1]
+    assert d % 32 == 0
+    xb = x.reshape(*shp[:-1], d // 32, 32)
+    amax = xb.abs().amax(dim=-1)
+    e = torch.where(amax > 0, torch.ceil(torch.log2(amax / 6.0)), torch.full_like(amax, -127.0))
+    e = e.clamp_(-127.0, 127.0)
+    y = xb / torch.exp2(e).unsqueeze(-1)
+    mag = y.abs().clamp_(max=6.0)
+    grid = torch.tensor(_E2M1_MAG, device=x.device, dtype=torch.float32)
+    mids = (grid[1:] + grid[:-1]) * 0.5
+    code = torch.bucketize(mag, mids, right=False)            # ties go to the lower magnitude
+    tie = mag == mids[code.clamp(max=6)]
+    code = torch.where(tie & (code % 2 == 1), code + 1, code)  # ... unless that code is odd
+    code = code.to(torch.uint8) | ((y < 0).to(torch.uint8) << 3)
+    code = code.reshape(*shp[:-1], d)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).contiguous()
+    scale = (e + 127.0).to(torch.uint8).reshape(*shp[:-1], d // 32).contiguous()
+    return packed, scale
+
+
+def _store_rows(g, shape, device, std, dtype, chunk_leading=False):
+    """Draw rows of ``shape`` and store as ``dtype``; returns dict of tensors."""
+    if dtype in ("f32", "bf16"):
+        if chunk_leading and len(shape) == 3:
+            out = torch.empty(shape, device=device, dtype=torch.float32 if dtype == "f32" else torch.bfloat16)
+            for b in range(shape[0]):
+                out[b] = store_dense(_normal(g, shape[1:], device, std), dtype)
+            return {"data": out}
+        return {"data": store_dense(_normal(g, shape, device, std), dtype)}
+    if dtype == "fp8":
+        if chunk_leading and len(shape) == 3:
+            codes = torch.empty(shape, device=device, dtype=torch.uint8)
+            scale = torch.empty(shape[:-1], device=device, dtype=torch.float32)
+            for b in range(shape[0]):
+                codes[b], scale[b] = encode_fp8_rows(_normal(g, shape[1:], device, std))
+            return {"data": codes, "scale": scale}
+        codes, scale = encode_fp8_rows(_normal(g, shape, device, std))
+        return {"data": codes, "scale": scale}
+    if dtype == "fp4":
+        if chunk_leading and len(shape) == 3:
+            packed = torch.empty(shape[:-1] + (shape[-1] // 2,), device=device, dtype=torch.uint8)
+            scale = torch.empty(shape[:-1] + (shape[-1] // 32,), device=device, dtype=torch.uint8)
+            for b in range(shape[0]):
+                packed[b], scale[b] = encode_fp4_rows(_normal(g, shape[1:], device, std))
+            return {"data": packed, "scale": scale}
+        packed, scale = encode_fp4_rows(_normal(g, shape, device, std))
+        return {"data": packed, "scale": scale}
+    raise ValueError(dtype)
+
+
+def decode_positions(cfg: Csa2Config, g, device):
+    b = cfg.batch
+    if not cfg.ragged:
+        return torch.full((b,), cfg.context - 1, dtype=torch.int64, device=device)
+    pos = torch.randint(0, cfg.context, (b,), generator=g, device=device, dtype=torch.int64)
+    pins = [0, 1, cfg.window - 1, cfg.window, cfg.context - 1]
+    for i, p in enumerate(pins[: b]):
+        pos[i] = min(p, cfg.context - 1)
+    return pos
+
+
+def make_candidates(cfg: Csa2Config, pos, g, device):
+    """Ascending, -1 padded candidate block ids per query row."""
+    rows = pos.shape[0]
+    nb, br = cfg.n_blocks, cfg.block_rows
+    cand = torch.full((rows, nb), -1, dtype=torch.int32, device=device)
+    for r in range(rows):
+        nv = (int(pos[r]) + 1) // cfg.ratio
+        vis_blocks = (nv + br - 1) // br
+        if vis_blocks == 0:
+            continue
+        newest = vis_blocks - 1
+        take = min(nb, vis_blocks)
+        if take == vis_blocks:
+            ids = torch.arange(vis_blocks, device=device)
+        else:
+            perm = torch.randperm(vis_blocks - 1, generator=g, device=device)[: take - 1]
+            ids = torch.cat([perm, torch.tensor([newest], device=device)])
+        cand[r, :take] = torch.sort(ids).values.to(torch.int32)
+    return cand
+
+
+def make_inputs(cfg: Csa2Config, seed: int, device="cpu"):
+    """All inputs of one call of the hot path for ``cfg`` (dict of tensors and ints)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    std = 1.0 / math.sqrt(cfg.dim) if cfg.value_scale == "inv_sqrt_d" else 1.0
+    H, D, HI, DI, W = cfg.heads, cfg.dim, cfg.idx_heads, cfg.idx_dim, cfg.window
+    out = {"cfg": cfg, "seed": int(seed)}
+    if cfg.phase == "decode":
+        B = cfg.batch
+        N = cfg.n_main_rows
+        pos = decode_positions(cfg, g, device)
+        out["pos"] = pos
+        out["kv_row_base"] = torch.arange(B, dtype=torch.int64, device=device) * N
+        m = _store_rows(g, (B, N, D), device, std, cfg.main_dtype, chunk_leading=True)
+        out["main"], out["main_scale"] = m["data"], m.get("scale")
+        s = _store_rows(g, (B, W, D), device, std, cfg.swa_dtype)
+        out["swa"], out["swa_scale"] = s["data"], s.get("scale")
+        k = _store_rows(g, (B, N, DI), device, std, cfg.idx_dtype, chunk_leading=True)
+        out["kI"], out["kI_scale"] = k["data"], k.get("scale")
+        rows = B
+        out["layers"] = [{
+            "q": store_dense(_normal(g, (B, H, D), device, std), cfg.q_dtype),
+            "sink": _normal(g, (H,), device, 1.0),
+        }]
+    else:
+        T = cfg.q_tokens
+        p0 = cfg.context - T
+        N = cfg.n_main_rows
+        pos = torch.arange(p0, p0 + T, dtype=torch.int64, device=device)
+        out["pos"] = pos
+        out["kv_row_base"] = torch.zeros(T, dtype=torch.int64, device=device)
+        m = _store_rows(g, (N, D), device, std, cfg.main_dtype)
+        out["main"], out["main_scale"] = m["data"], m.get("scale")
+        k = _store_rows(g, (N, DI), device, std, cfg.idx_dtype)
+        out["kI"], out["kI_scale"] = k["data"], k.get("scale")
+        swa_pos0 = max(0, p0 - W + 1)
+        swa_rows = p0 + T - swa_pos0
+        out["swa_pos0"] = swa_pos0
+        layers = []
+        for _ in range(1 + cfg.reuse_layers):
+            s = _store_rows(g, (swa_rows, D), device, std, cfg.swa_dtype)
+            layers.append({
+                "q": store_dense(_normal(g, (T, H, D), device, std), cfg.q_dtype),
+                "swa": s["data"], "swa_scale": s.get("scale"),
+                "sink": _normal(g, (H,), device, 1.0),
+            })
+        out["layers"] = layers
+        rows = T
+    # indexer query and weights (the FULL / REINDEX layer's own)
+    w = _normal(g, (rows, HI), device, 1.0)
+    if cfg.idx_dtype == "fp8":
+        qraw = _normal(g, (rows, HI, DI), device, std)
+        codes, qscale = encode_fp8_rows(qraw)
+        out["qI"] = codes
+        out["w"] = (w * qscale).contiguous()
+    else:
+        out["qI"] = store_dense(_normal(g, (rows, HI, DI), device, std), cfg.idx_dtype)
+        out["w"] = w.contiguous()
+    if cfg.index_mode == "reindex":
+        out["cand"] = make_candidates(cfg, pos, g, device)
+    return out
