@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Throughput of the CSA2 hot path on one MI355X, with roofline and CPU-oracle baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one batch of synthetic inputs that
+are already resident in HBM:
+  decode  : indexer_score -> topk_select -> sparse_attn_decode
+  prefill : indexer_score -> topk_select -> sparse_attn_prefill for the FULL
+            layer and every REUSE layer (same indices, own q / SWA / sink)
+The default workload is the 1M-context low-precision decode (64 sequences,
+FP8 index plane, FP4 main plane, FP8 SWA ring).  Prints one JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn query-tokens/s + achieved HBM GB/s, decode at 1M context, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_CONFIG = "lowp_full_decode_1m"
+
+_ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+def algorithmic_bytes(cfg, x):
+    """Bytes each kernel of one step must move at least once (reads + writes)."""
+    import torch
+    pos = x["pos"].cpu()
+    nv = ((pos + 1) // cfg.ratio).clamp(max=cfg.n_main_rows)
+    rows = pos.shape[0]
+    idx_row = cfg.idx_dim * _ELEM[cfg.idx_dtype] + (4 if cfg.idx_dtype == "fp8" else 0)
+    qI = rows * cfg.idx_heads * cfg.idx_dim * _ELEM[cfg.idx_dtype] + rows * cfg.idx_heads * 4
+    if cfg.index_mode == "reindex":
+        cand = x["cand"].cpu().long()
+        cols = cand.repeat_interleave(cfg.block_rows, dim=1) * cfg.block_rows + \
+            torch.arange(cfg.block_rows).repeat(cfg.n_blocks)
+        valid = (cand.repeat_interleave(cfg.block_rows, dim=1) >= 0) & (cols < nv[:, None])
+        scored_rows = int(valid.sum())
+        extra = rows * cfg.n_blocks * 4
+    else:
+        scored_rows = int(nv.sum())
+        extra = 0
+    idx_bytes = scored_rows * idx_row + qI + extra + rows * cfg.width * 4
+    topk_bytes = rows * cfg.width * 4 + rows * cfg.topk * 4 + extra
+    main_row = cfg.dim // 2 + cfg.dim // 32 if cfg.main_dtype == "fp4" else cfg.dim * _ELEM[cfg.main_dtype]
+    swa_row = cfg.dim * _ELEM[cfg.swa_dtype] + (4 if cfg.swa_dtype == "fp8" else 0)
+    sel = torch.minimum(nv, torch.tensor(cfg.topk))
+    win = torch.minimum(pos + 1, torch.tensor(cfg.window))
+    qo = rows * cfg.heads * cfg.dim * (_ELEM[cfg.q_dtype] + _ELEM[cfg.out_dtype])
+    attn_bytes = int(sel.sum()) * main_row + int(win.sum()) * swa_row + qo + rows * cfg.topk * 4
+    return {"indexer_score": idx_bytes, "topk_select": topk_bytes, "sparse_attn": attn_bytes,
+            "scored_rows": scored_rows}
+
+
+def cpu_baseline(cfg, x, budget_s=20.0):
+    """The oracle (float64 NumPy) on the host, one query row at a time, for about budget_s seconds."""
+    import numpy as np
+    import torch
+    import oracle
+    from threadpoolctl import threadpool_info
+    tests_dir = os.path.join(ROOT, "tests")
+    sys.path.insert(0, tests_dir)
+    from harness import oracle_attention, oracle_scores, oracle_topk  # noqa: E402
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    done, t_total = 0, 0.0
+    rows = x["pos"].shape[0]
+    for r in range(rows):
+        # Copy this row's inputs to the host before timing (not part of the oracle's work).
+        sub = _host_slice(cfg, x, r)
+        sub_cfg = cfg.replace(batch=1, q_tokens=1)
+        t0 = time.perf_counter()
+        s = oracle_scores(sub_cfg, sub, np.array([0]))
+        idx = oracle_topk(sub_cfg, sub, s, np.array([0]))
+        for layer in range(len(sub["layers"])):
+            oracle_attention(sub_cfg, sub, idx, np.array([0]), layer=layer)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    return {"value": done / t_total, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {rows} query rows of the {cfg.name} batch, whole path (indexer, top-k, attention"
+                      f"{' x %d layers' % len(x['layers']) if len(x['layers']) > 1 else ''}), float64 NumPy; "
+                      f"host copy excluded; {t_total:.1f} s"}
+
+
+def _host_slice(cfg, x, r):
+    """Inputs of query row r alone, on the host (decode: its sequence; prefill: the shared planes)."""
+    import torch
+    out = {"cfg": cfg}
+    cpu = lambda t: None if t is None else t.detach().cpu()
+    if cfg.phase == "decode":
+        b = r
+        out["pos"] = cpu(x["pos"][b:b + 1])
+        out["kv_row_base"] = torch.zeros(1, dtype=torch.int64)
+        out["main"] = cpu(x["main"][b:b + 1])
+        out["main_scale"] = cpu(None if x["main_scale"] is None else x["main_scale"][b:b + 1])
+        out["kI"] = cpu(x["kI"][b:b + 1])
+        out["kI_scale"] = cpu(None if x["kI_scale"] is None else x["kI_scale"][b:b + 1])
+        out["swa"] = cpu(x["swa"][b:b + 1])
+        out["swa_scale"] = cpu(None if x["swa_scale"] is None else x["swa_scale"][b:b + 1])
+        out["layers"] = [{"q": cpu(L["q"][b:b + 1]), "sink": cpu(L["sink"])} for L in x["layers"]]
+    else:
+        out["pos"] = cpu(x["pos"][r:r + 1])
+        out["kv_row_base"] = torch.zeros(1, dtype=torch.int64)
+        out["main"], out["main_scale"] = cpu(x["main"]), cpu(x["main_scale"])
+        out["kI"], out["kI_scale"] = cpu(x["kI"]), cpu(x["kI_scale"])
+        out["swa_pos0"] = x["swa_pos0"]
+        out["layers"] = [{"q": cpu(L["q"][r:r + 1]), "swa": cpu(L["swa"]), "swa_scale": cpu(L["swa_scale"]),
+                          "sink": cpu(L["sink"])} for L in x["layers"]]
+    out["qI"] = cpu(x["qI"][r:r + 1])
+    out["w"] = cpu(x["w"][r:r + 1])
+    if "cand" in x:
+        out["cand"] = cpu(x["cand"][r:r + 1])
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
+              f"sequence with no communication, so N GPUs would each run this same workload.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_latent_attention_amd as csa2
+    from workloads import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {cfg.name} seed {args.seed}", file=sys.stderr, flush=True)
+    x = make_inputs(cfg, args.seed, device=dev)
+    torch.cuda.synchronize()
+
+    rows = x["pos"].shape[0]
+    scores = torch.empty(rows, cfg.width, dtype=torch.float32, device=dev)
+    idx = torch.empty(rows, cfg.topk, dtype=torch.int32, device=dev)
+    outs = [torch.empty_like(L["q"]) for L in x["layers"]]
+    freqs = csa2.rope_inv_freq(cfg.rope_dim, cfg.rope_theta, cfg.yarn_factor, cfg.yarn_orig).to(dev)
+    kI = x["kI"].reshape(-1, cfg.idx_dim)
+    kIs = None if x["kI_scale"] is None else x["kI_scale"].reshape(-1)
+    kv = x["main"].reshape(-1, x["main"].shape[-1])
+    kvs = None if x["main_scale"] is None else x["main_scale"].reshape(-1, x["main_scale"].shape[-1])
+    tau_i = 1.0 / math.sqrt(cfg.idx_dim * cfg.idx_heads)
+    tau = 1.0 / math.sqrt(cfg.dim)
+    akw = dict(rope_dim=cfg.rope_dim, kv_fp4=cfg.main_dtype == "fp4", swa_fp8=cfg.swa_dtype == "fp8", kv_scale=kvs)
+    attn_ws = None
+    if cfg.phase == "decode":
+        n = csa2.attn_workspace_size(rows, cfg.heads, cfg.dim, cfg.window, cfg.topk)
+        attn_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    topk_ws = torch.empty(max(csa2.topk_workspace_size(rows, cfg.width, cfg.topk), 1), dtype=torch.uint8, device=dev)
+
+    names = ["indexer_score", "topk_select", "sparse_attn"]
+    evs = {n: [] for n in names}
+
+    def step(record):
+        def ev():
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            return e
+        e0 = ev() if record else None
+        csa2.indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, tau_i, scores, k_scale=kIs,
+                           cand=x.get("cand"), block_rows=cfg.block_rows, fp8=cfg.idx_dtype == "fp8")
+        e1 = ev() if record else None
+        csa2.topk_select(scores, x["pos"], cfg.ratio, idx, cand=x.get("cand"), block_rows=cfg.block_rows,
+                         workspace=topk_ws)
+        e2 = ev() if record else None
+        for li, L in enumerate(x["layers"]):
+            if cfg.phase == "decode":
+                csa2.sparse_attn_decode(L["q"], x["pos"], idx, kv, x["kv_row_base"], x["swa"], L["sink"], freqs,
+                                        cfg.ratio, cfg.window, tau, outs[li], swa_scale=x["swa_scale"],
+                                        workspace=attn_ws, **akw)
+            else:
+                csa2.sparse_attn_prefill(L["q"], x["pos"], idx, kv, L["swa"], x["swa_pos0"], L["sink"], freqs,
+                                         cfg.ratio, cfg.window, tau, outs[li], swa_scale=L["swa_scale"],
+                                         kv_row_base=x["kv_row_base"], **akw)
+        e3 = ev() if record else None
+        if record:
+            evs["indexer_score"].append((e0, e1))
+            evs["topk_select"].append((e1, e2))
+            evs["sparse_attn"].append((e2, e3))
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    kern_ms = {n: sum(a.elapsed_time(b) for a, b in evs[n]) / args.steps for n in names}
+
+    ab = algorithmic_bytes(cfg, x)
+    dominant = max(names, key=lambda n: kern_ms[n])
+    achieved = ab[dominant] / (kern_ms[dominant] * 1e-3) / 1e9
+    roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": ab[dominant]}
+    q_tokens = rows
+    line = {
+        "metric": METRIC, "value": round(q_tokens / (ms_step * 1e-3), 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": {"fp8": "fp8+bf16", "bf16": "bf16", "f32": "f32"}[cfg.idx_dtype],
+        "data": "synthetic (seeded; stored formats drawn as in workloads/gen.py)",
+        "config": {"workload": cfg.name, "sequences": cfg.batch, "query_rows": rows, "context": cfg.context,
+                   "ratio": cfg.ratio, "heads": cfg.heads, "dim": cfg.dim, "topk": cfg.topk, "window": cfg.window,
+                   "index": f"{cfg.index_mode} {cfg.idx_heads}x{cfg.idx_dim} {cfg.idx_dtype}",
+                   "main_kv": cfg.main_dtype, "swa": cfg.swa_dtype, "attention_layers": len(x["layers"])},
+        "kernels_ms": {n: round(v, 4) for n, v in kern_ms.items()},
+        "kernels_gbs": {n: round(ab[n] / (kern_ms[n] * 1e-3) / 1e9, 1) for n in names},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

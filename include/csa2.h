@@ -1,0 +1,275 @@
+/*
+ * csa2.h -- C ABI of the CSA2 sparse-attention hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The path, as the pages define it for DeepSeek-V4.1-Flash:
+ *   1. the lightning indexer scores compressed KV rows
+ *      ("DeepSeek-V4.1-Flash 架构解剖", special module "indexer", fig. 3b and
+ *      its score formula; "万字长文解析DeekSeekV4.1flash", appendix A.15.2);
+ *   2. top-k (k = 512) selects rows per query: FULL over every visible row,
+ *      REINDEX over a 2048 x 8 candidate pool, REUSE takes another layer's
+ *      selection unchanged (anatomy page, figs. 2b, 2c, 2d);
+ *   3. one softmax over the layer's SWA rows plus the selected rows, 64 query
+ *      heads over one shared 512-dim latent with K == V, a per-head sink in the
+ *      denominator, then the inverse rotation of the output's rope tail
+ *      (anatomy page, shared attention path and "出来之后"; "DeepSeek-V4-Pro
+ *      架构解剖", attention merge fig. 2d formula).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE memory owned by the caller.  The library
+ *     keeps no state between calls, never frees caller memory, and allocates
+ *     nothing: scratch space comes in through an explicit workspace argument
+ *     whose size the matching *_workspace_size() call reports.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream); the
+ *     call returns after the launches, without synchronising.  Calls are
+ *     re-entrant; two calls on different streams must not share a workspace.
+ *   - Arrays are dense and row-major with the shapes stated below.
+ *   - Every output element is written (invalid score columns get -inf,
+ *     unfilled top-k slots get -1).
+ *   - Arguments are validated on the host before any launch.  An invalid
+ *     argument returns CSA2_ERR_INVALID_ARG, a shape/dtype combination with no
+ *     compiled kernel returns CSA2_ERR_UNSUPPORTED (never a fallback), a
+ *     workspace that is too small returns CSA2_ERR_WORKSPACE; nothing is
+ *     launched in those cases.  A HIP launch error returns CSA2_ERR_HIP.
+ *   - Caller contracts the library cannot check (it does not read device
+ *     memory on the host): planes hold every row a query may touch
+ *     (row_base[r] + n_visible(r) rows), candidate blocks are ascending,
+ *     FP8/FP4 scales are non-negative.
+ *
+ * Geometry shared by all calls.  For a query at absolute position pos and
+ * compression ratio m, compressed row j is visible iff j < (pos + 1) / m
+ * (integer division; the group-causal mask: a row becomes visible once the
+ * query has passed its group's last token, "DeepSeek-V4.1-Flash 结构说明",
+ * section 4.1).  SWA entry e of a window of W covers position
+ * pos - (W - 1) + e and is absent when that position is negative.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_ABI_VERSION 1
+
+/* Status codes. */
+#define CSA2_OK 0
+#define CSA2_ERR_INVALID_ARG 1
+#define CSA2_ERR_UNSUPPORTED 2
+#define CSA2_ERR_WORKSPACE 3
+#define CSA2_ERR_HIP 4
+
+/* Element types of stored tensors. */
+#define CSA2_F32 0      /* IEEE binary32 */
+#define CSA2_BF16 1     /* bfloat16 */
+#define CSA2_FP8_E4M3 2 /* OCP FP8 E4M3 "FN" (bias 7, S.1111.111 = NaN), one byte per element */
+#define CSA2_FP4_E2M1 3 /* OCP FP4 E2M1, two per byte (element 2i in the low nibble) */
+
+/* Indexer modes. */
+#define CSA2_MODE_FULL 0
+#define CSA2_MODE_REINDEX 1
+
+typedef struct ihipStream_t* csa2_stream_t; /* == hipStream_t */
+
+/* ABI version of the loaded library (CSA2_ABI_VERSION it was built with). */
+int32_t csa2_abi_version(void);
+
+/* Static, human-readable text for a status code. */
+const char* csa2_status_string(int32_t status);
+
+/* ------------------------------------------------------------------------ */
+/* Lightning-indexer scores.
+ *
+ *   score[r, c] = scale * sum_{h < heads} w[r, h] * ReLU(<q[r, h, :], k(row(r, c), :)>)
+ *
+ * ("DeepSeek-V4.1-Flash 架构解剖", special module "indexer", score formula:
+ * a weighted sum over indexer heads of per-head dot products, w without an
+ * activation, scale = dim^-1/2 * heads^-1/2; the per-head ReLU is the long
+ * essay's appendix A.15.2 pseudo-code.)
+ *
+ * FULL:    row(r, c) = row_base[r] + c, valid iff c < (pos[r] + 1) / ratio.
+ *          Only valid columns are read; columns [n_visible, width) get -inf.
+ * REINDEX: column c = i * block_rows + t maps to plane row
+ *          row_base[r] + cand[r, i] * block_rows + t, valid iff
+ *          cand[r, i] >= 0 and cand[r, i] * block_rows + t < (pos[r] + 1) / ratio
+ *          (anatomy page, fig. 2c REINDEX: re-score only the 2048 x 8
+ *          candidate rows).  width must equal n_blocks * block_rows.
+ *
+ * FP8 (k_dtype == q_dtype == CSA2_FP8_E4M3): k is scaled by k_scale[row]; the
+ * query's per-(row, head) scale is folded into w by the caller (anatomy page,
+ * fig. 3b: the FP32 scale is folded into w, not passed separately).
+ *
+ * Supported: (heads, dim) in {(4, 32), (64, 128)}; q_dtype == k_dtype in
+ * {F32, BF16, FP8_E4M3}.  rows * width fits in int64.
+ */
+typedef struct csa2_index_args {
+    uint32_t struct_size;       /* sizeof(csa2_index_args) */
+    int32_t mode;               /* CSA2_MODE_FULL | CSA2_MODE_REINDEX */
+    int32_t rows;               /* query rows, >= 0 */
+    int32_t heads;              /* indexer heads H_I */
+    int32_t dim;                /* indexer head dim D_I */
+    int32_t ratio;              /* compression ratio m, 1 or 2 */
+    int32_t q_dtype;            /* element type of q */
+    int32_t k_dtype;            /* element type of k */
+    int32_t n_blocks;           /* REINDEX: candidate blocks per row (ignored for FULL) */
+    int32_t block_rows;         /* REINDEX: rows per candidate block, 1..64 */
+    int32_t _pad0;
+    int64_t width;              /* columns per score row (FULL: >= every n_visible) */
+    const void* q;              /* [rows, heads, dim] */
+    const float* w;             /* [rows, heads] effective head weights */
+    const void* k;              /* index-key plane [*, dim] */
+    const float* k_scale;       /* FP8: [*] per-row scale, same row numbering as k; else NULL */
+    const int64_t* row_base;    /* [rows] first plane row of the query's sequence */
+    const int64_t* pos;         /* [rows] absolute query positions, >= 0 */
+    const int32_t* cand;        /* REINDEX: [rows, n_blocks] block ids, ascending, -1 padded; else NULL */
+    float scale;                /* score scale (dim^-1/2 * heads^-1/2 in the pages' model) */
+    int32_t _pad1;
+    float* scores;              /* out: [rows, width] float32 */
+} csa2_index_args;
+
+int32_t csa2_indexer_score(const csa2_index_args* args, csa2_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Per-row top-k of indexer scores.
+ *
+ * Selects, per row, the k valid columns with the largest scores, ranking by
+ * score descending and breaking ties by the lower column; NaN ranks as -inf
+ * and -0 equals +0.  The chosen columns are written in increasing column
+ * order, mapped to plane rows (FULL: the column itself; REINDEX:
+ * cand[r, i] * block_rows + t, which is increasing when the candidate blocks
+ * are ascending), followed by -1 when fewer than k columns are valid
+ * ("DeepSeek-V4.1-Flash 架构解剖", fig. 2d REUSE: selected [rows, 512],
+ * ascending, -1 filled; special module "indexer": -1 means the history is
+ * shorter than k).  Validity is the same as in csa2_indexer_score: FULL
+ * column c < (pos[r] + 1) / ratio, REINDEX through cand.  Row r of `out`
+ * holds plane-relative rows (without row_base), the numbering
+ * csa2_sparse_attn_* expects in `idx`.
+ *
+ * Supported: 1 <= k <= 2048; width < 2^31.
+ */
+typedef struct csa2_topk_args {
+    uint32_t struct_size;       /* sizeof(csa2_topk_args) */
+    int32_t rows;               /* score rows, >= 0 */
+    int32_t k;                  /* selections per row */
+    int32_t ratio;              /* compression ratio m, 1 or 2 */
+    int32_t n_blocks;           /* REINDEX: candidate blocks per row; 0 selects FULL validity */
+    int32_t block_rows;         /* REINDEX: rows per block */
+    int64_t width;              /* columns per score row (REINDEX: n_blocks * block_rows) */
+    const float* scores;        /* [rows, width] */
+    const int64_t* pos;         /* [rows] absolute query positions */
+    const int32_t* cand;        /* REINDEX: [rows, n_blocks]; NULL for FULL */
+    int32_t* out;               /* out: [rows, k] int32 */
+} csa2_topk_args;
+
+/* Bytes of workspace csa2_topk_select needs for these sizes (may be 0). */
+size_t csa2_topk_workspace_size(int32_t rows, int64_t width, int32_t k);
+
+int32_t csa2_topk_select(const csa2_topk_args* args, void* workspace, size_t workspace_bytes,
+                         csa2_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Sparse sink attention.
+ *
+ * For query row r, head h and the entry multiset S(r) = {valid SWA entries}
+ * plus {kv row row_base[r] + idx[r, i] : 0 <= idx[r, i] < (pos[r] + 1) / ratio}
+ * (no de-duplication; -1 and out-of-range indices are skipped):
+ *
+ *   s_j      = softmax_scale * <q[r, h, :], v_j>
+ *   o[r, h]  = sum_j e^{s_j} v_j / (e^{sink[h]} + sum_j e^{s_j})
+ *   out[r,h] = o[r, h] with pair (D-R+2i, D-R+2i+1) rotated by -pos[r] * inv_freq[i]
+ *
+ * K and V are the same stored row; q arrives already rotated; the sink is an
+ * unscaled logit without a value ("DeepSeek-V4-Pro 架构解剖", attention merge
+ * fig. 2d formula; "DeepSeek-V4.1-Flash 架构解剖", "四种层合并出来的是什么形状"
+ * and "出来之后"; "DeepSeek-V4.1-Flash 结构说明", sections 4.1 and 6.1).  An
+ * empty S gives out = 0.
+ *
+ * SWA source:
+ *   decode  (csa2_sparse_attn_decode): one ring per query row, swa [rows, window, dim];
+ *           slot s holds position pos - ((pos - s) mod window), absent if negative
+ *           (structure page, section 4.4: the ring is written at start_pos mod 128).
+ *   prefill (csa2_sparse_attn_prefill): one linear array swa [swa_rows, dim] whose
+ *           row t holds position swa_pos0 + t, shared by all query rows; query r
+ *           sees positions max(0, pos[r] - window + 1) .. pos[r] that the array holds.
+ *
+ * Storage: q and out are F32 or BF16 [rows, heads, dim].  kv is F32 or BF16
+ * [*, dim], or FP4_E2M1 packed [*, dim/2] bytes with kv_scale = E8M0 bytes
+ * [*, dim/32] (one power-of-two scale per 32 elements).  swa is F32 or BF16,
+ * or FP8_E4M3 with swa_scale = float32 per swa row ([rows, window] in decode,
+ * [swa_rows] in prefill).
+ *
+ * Supported: (heads, dim, rope_dim) in {(4, 64, 16), (64, 512, 64)}; window
+ * and topk multiples of 16; F32 only together with F32 everywhere (the
+ * (4, 64, 16) shape); otherwise BF16 q/out with kv BF16 or FP4 and swa BF16
+ * or FP8.  rope_inv_freq holds rope_dim/2 float64 frequencies in device
+ * memory (see csa2_rope_inv_freq).
+ *
+ * Decode splits the entry list of each row over `splits` workgroups and
+ * merges their partial softmax states; the workspace holds those partials.
+ */
+typedef struct csa2_attn_args {
+    uint32_t struct_size;       /* sizeof(csa2_attn_args) */
+    int32_t rows;               /* query rows, >= 0 */
+    int32_t heads;              /* query heads H */
+    int32_t dim;                /* latent dim D */
+    int32_t rope_dim;           /* rotated tail R */
+    int32_t topk;               /* idx entries per row */
+    int32_t ratio;              /* compression ratio m, 1 or 2 */
+    int32_t window;             /* SWA window W */
+    int32_t q_dtype;
+    int32_t kv_dtype;
+    int32_t swa_dtype;
+    int32_t out_dtype;
+    int32_t splits;             /* decode: workgroups per row (0 = library choice); prefill: ignored */
+    int32_t _pad0;
+    int64_t swa_rows;           /* prefill: rows of the linear SWA array */
+    int64_t swa_pos0;           /* prefill: position of linear SWA row 0 */
+    const void* q;              /* [rows, heads, dim], rope tail already rotated */
+    const int64_t* pos;         /* [rows] absolute positions, >= 0 */
+    const int32_t* idx;         /* [rows, topk] plane-relative selected rows, -1 padded */
+    const void* kv;             /* main plane rows */
+    const uint8_t* kv_scale;    /* FP4: E8M0 [*, dim/32]; else NULL */
+    const int64_t* kv_row_base; /* [rows] first kv row of the query's sequence */
+    const void* swa;            /* SWA rows (ring or linear, see above) */
+    const float* swa_scale;     /* FP8: per-row scales; else NULL */
+    const float* sink;          /* [heads] */
+    const double* rope_inv_freq;/* [rope_dim/2] device float64 */
+    float softmax_scale;        /* dim^-1/2 in the pages' model */
+    int32_t _pad1;
+    void* out;                  /* out: [rows, heads, dim] */
+} csa2_attn_args;
+
+/* Bytes of workspace csa2_sparse_attn_decode needs for these sizes and splits
+ * (splits = 0: the library's choice, the same one the call makes). */
+size_t csa2_attn_workspace_size(int32_t rows, int32_t heads, int32_t dim, int32_t window, int32_t topk,
+                                int32_t splits);
+
+int32_t csa2_sparse_attn_decode(const csa2_attn_args* args, void* workspace, size_t workspace_bytes,
+                                csa2_stream_t stream);
+
+int32_t csa2_sparse_attn_prefill(const csa2_attn_args* args, csa2_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host helper: RoPE frequencies in float64, written to HOST memory.
+ *
+ * out[i] = theta^(-2i/rope_dim) for i < rope_dim/2 ("DeepSeek-V4.1-Flash
+ * 结构说明", section 6.1: 32 frequencies base^(-2i/64), adjacent-pair
+ * rotation).  With yarn_factor > 1 and yarn_orig_len > 0 each frequency is
+ * interpolated by the YaRN NTK-by-parts rule (section 6.3 splits the
+ * frequencies into three bands by how many turns they make within the
+ * original length; the band formula is the YaRN paper's, with alpha = 1 and
+ * beta = 32): r = yarn_orig_len * f / (2 pi); g = clamp((r - 1) / 31, 0, 1);
+ * f' = (1 - g) f / yarn_factor + g f.
+ * Returns CSA2_ERR_INVALID_ARG for odd or non-positive rope_dim, theta <= 1,
+ * yarn_factor < 1 or a NULL out.
+ */
+int32_t csa2_rope_inv_freq(int32_t rope_dim, double theta, double yarn_factor, int64_t yarn_orig_len,
+                           double* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

@@ -1,0 +1,285 @@
+"""Python binding of libcsa2 (the CSA2 sparse-attention hot path for MI355X / gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libcsa2.so``.  Torch tensors provide device memory and the current HIP
+stream.  The library must have been built (``python -m
+sparse_latent_attention_amd.build``); importing this package without it
+raises ``ImportError`` -- there is no CPU fallback.
+
+Entry points (same names as the C ABI in include/csa2.h):
+
+* ``indexer_score``        lightning-indexer scores, FULL or REINDEX
+* ``topk_select``          per-row top-k of the scores
+* ``sparse_attn_decode``   sink attention, SWA ring per query row
+* ``sparse_attn_prefill``  sink attention, one linear SWA array
+* ``rope_inv_freq``        float64 RoPE / YaRN frequency table (host)
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcsa2.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_latent_attention_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# Element types and modes (include/csa2.h).
+F32, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
+MODE_FULL, MODE_REINDEX = 0, 1
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+
+_vp = ctypes.c_void_p
+_i32, _i64, _u32, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
+
+
+class IndexArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _u32), ("mode", _i32), ("rows", _i32), ("heads", _i32), ("dim", _i32), ("ratio", _i32),
+        ("q_dtype", _i32), ("k_dtype", _i32), ("n_blocks", _i32), ("block_rows", _i32), ("_pad0", _i32),
+        ("width", _i64), ("q", _vp), ("w", _vp), ("k", _vp), ("k_scale", _vp), ("row_base", _vp), ("pos", _vp),
+        ("cand", _vp), ("scale", _f32), ("_pad1", _i32), ("scores", _vp),
+    ]
+
+
+class TopkArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _u32), ("rows", _i32), ("k", _i32), ("ratio", _i32), ("n_blocks", _i32),
+        ("block_rows", _i32), ("width", _i64), ("scores", _vp), ("pos", _vp), ("cand", _vp), ("out", _vp),
+    ]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _u32), ("rows", _i32), ("heads", _i32), ("dim", _i32), ("rope_dim", _i32), ("topk", _i32),
+        ("ratio", _i32), ("window", _i32), ("q_dtype", _i32), ("kv_dtype", _i32), ("swa_dtype", _i32),
+        ("out_dtype", _i32), ("splits", _i32), ("_pad0", _i32), ("swa_rows", _i64), ("swa_pos0", _i64),
+        ("q", _vp), ("pos", _vp), ("idx", _vp), ("kv", _vp), ("kv_scale", _vp), ("kv_row_base", _vp),
+        ("swa", _vp), ("swa_scale", _vp), ("sink", _vp), ("rope_inv_freq", _vp), ("softmax_scale", _f32),
+        ("_pad1", _i32), ("out", _vp),
+    ]
+
+
+_lib.csa2_abi_version.restype = _i32
+_lib.csa2_status_string.restype = ctypes.c_char_p
+_lib.csa2_status_string.argtypes = [_i32]
+_lib.csa2_indexer_score.restype = _i32
+_lib.csa2_indexer_score.argtypes = [ctypes.POINTER(IndexArgs), _vp]
+_lib.csa2_topk_workspace_size.restype = ctypes.c_size_t
+_lib.csa2_topk_workspace_size.argtypes = [_i32, _i64, _i32]
+_lib.csa2_topk_select.restype = _i32
+_lib.csa2_topk_select.argtypes = [ctypes.POINTER(TopkArgs), _vp, ctypes.c_size_t, _vp]
+_lib.csa2_attn_workspace_size.restype = ctypes.c_size_t
+_lib.csa2_attn_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
+_lib.csa2_sparse_attn_decode.restype = _i32
+_lib.csa2_sparse_attn_decode.argtypes = [ctypes.POINTER(AttnArgs), _vp, ctypes.c_size_t, _vp]
+_lib.csa2_sparse_attn_prefill.restype = _i32
+_lib.csa2_sparse_attn_prefill.argtypes = [ctypes.POINTER(AttnArgs), _vp]
+_lib.csa2_rope_inv_freq.restype = _i32
+_lib.csa2_rope_inv_freq.argtypes = [_i32, ctypes.c_double, ctypes.c_double, _i64, ctypes.POINTER(ctypes.c_double)]
+
+ABI_VERSION = _lib.csa2_abi_version()
+EXPORTED = ("csa2_abi_version", "csa2_status_string", "csa2_indexer_score", "csa2_topk_workspace_size",
+            "csa2_topk_select", "csa2_attn_workspace_size", "csa2_sparse_attn_decode", "csa2_sparse_attn_prefill",
+            "csa2_rope_inv_freq")
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+def status_string(status):
+    return _lib.csa2_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != OK:
+        raise Csa2Error(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("csa2: all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("csa2: all tensors must be contiguous")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dense_code(t, name):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"csa2: {name} must be float32 or bfloat16, got {t.dtype}")
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype:
+        raise ValueError(f"csa2: {name} must be {dtype}, got {t.dtype}")
+
+
+def rope_inv_freq(rope_dim, theta, yarn_factor=1.0, yarn_orig_len=0):
+    """float64 frequency table computed by the library on the host (CPU tensor)."""
+    out = (ctypes.c_double * (rope_dim // 2))()
+    _check("csa2_rope_inv_freq", _lib.csa2_rope_inv_freq(int(rope_dim), float(theta), float(yarn_factor),
+                                                          int(yarn_orig_len), out))
+    return torch.tensor(list(out), dtype=torch.float64)
+
+
+def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None, cand=None, block_rows=8,
+                  fp8=False, stream=None):
+    """Fills ``scores`` [rows, width] (float32).  REINDEX when ``cand`` is given.
+
+    q [rows, H_I, D_I] and k [*, D_I] are float32/bfloat16, or uint8 FP8-E4M3
+    codes with ``fp8=True`` (then ``k_scale`` [*] float32 is required and the
+    query scales are already folded into w).
+    """
+    _dev(q, w, k, row_base, pos, scores, k_scale, cand)
+    rows, heads, dim = q.shape
+    if fp8:
+        _need(q, torch.uint8, "q")
+        _need(k, torch.uint8, "k")
+        code = FP8_E4M3
+    else:
+        code = _dense_code(q, "q")
+        if k.dtype != q.dtype:
+            raise ValueError("csa2: q and k must share a dtype")
+    _need(w, torch.float32, "w")
+    _need(scores, torch.float32, "scores")
+    _need(row_base, torch.int64, "row_base")
+    _need(pos, torch.int64, "pos")
+    if w.shape != (rows, heads) or k.shape[-1] != dim or scores.shape[0] != rows or row_base.shape != (rows,) \
+            or pos.shape != (rows,):
+        raise ValueError("csa2.indexer_score: inconsistent shapes")
+    a = IndexArgs()
+    a.struct_size = ctypes.sizeof(IndexArgs)
+    a.mode = MODE_REINDEX if cand is not None else MODE_FULL
+    a.rows, a.heads, a.dim, a.ratio = rows, heads, dim, int(ratio)
+    a.q_dtype = a.k_dtype = code
+    a.width = scores.shape[1]
+    if cand is not None:
+        _need(cand, torch.int32, "cand")
+        if cand.shape[0] != rows:
+            raise ValueError("csa2.indexer_score: cand rows")
+        a.n_blocks, a.block_rows = cand.shape[1], int(block_rows)
+    a.q, a.w, a.k, a.k_scale = _ptr(q), _ptr(w), _ptr(k), _ptr(k_scale)
+    a.row_base, a.pos, a.cand, a.scores = _ptr(row_base), _ptr(pos), _ptr(cand), _ptr(scores)
+    a.scale = float(scale)
+    _check("csa2_indexer_score", _lib.csa2_indexer_score(ctypes.byref(a), _stream(stream)))
+    return scores
+
+
+def topk_workspace_size(rows, width, k):
+    return int(_lib.csa2_topk_workspace_size(int(rows), int(width), int(k)))
+
+
+def topk_select(scores, pos, ratio, out, *, cand=None, block_rows=8, workspace=None, stream=None):
+    """Fills ``out`` [rows, k] int32 with the selected plane rows (ascending, -1 padded)."""
+    _dev(scores, pos, out, cand, workspace)
+    _need(scores, torch.float32, "scores")
+    _need(pos, torch.int64, "pos")
+    _need(out, torch.int32, "out")
+    rows, width = scores.shape
+    if out.shape[0] != rows or pos.shape != (rows,):
+        raise ValueError("csa2.topk_select: inconsistent shapes")
+    a = TopkArgs()
+    a.struct_size = ctypes.sizeof(TopkArgs)
+    a.rows, a.k, a.ratio, a.width = rows, out.shape[1], int(ratio), width
+    if cand is not None:
+        _need(cand, torch.int32, "cand")
+        a.n_blocks, a.block_rows = cand.shape[1], int(block_rows)
+    a.scores, a.pos, a.cand, a.out = _ptr(scores), _ptr(pos), _ptr(cand), _ptr(out)
+    need = topk_workspace_size(rows, width, a.k)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("csa2_topk_select", _lib.csa2_topk_select(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def _attn_args(q, pos, idx, kv, kv_scale, kv_row_base, swa, swa_scale, sink, inv_freq, ratio, window,
+               softmax_scale, out, rope_dim, kv_fp4, swa_fp8):
+    _dev(q, pos, idx, kv, kv_scale, kv_row_base, swa, swa_scale, sink, inv_freq, out)
+    rows, heads, dim = q.shape
+    _need(pos, torch.int64, "pos")
+    _need(idx, torch.int32, "idx")
+    _need(sink, torch.float32, "sink")
+    _need(inv_freq, torch.float64, "rope_inv_freq")
+    _need(kv_row_base, torch.int64, "kv_row_base")
+    if kv_fp4:
+        _need(kv, torch.uint8, "kv")
+        _need(kv_scale, torch.uint8, "kv_scale")
+    if swa_fp8:
+        _need(swa, torch.uint8, "swa")
+        _need(swa_scale, torch.float32, "swa_scale")
+    if out.shape != q.shape or idx.shape[0] != rows or pos.shape != (rows,) or sink.shape != (heads,) \
+            or inv_freq.shape != (rope_dim // 2,) or kv_row_base.shape != (rows,):
+        raise ValueError("csa2.sparse_attn: inconsistent shapes")
+    a = AttnArgs()
+    a.struct_size = ctypes.sizeof(AttnArgs)
+    a.rows, a.heads, a.dim, a.rope_dim, a.topk = rows, heads, dim, int(rope_dim), idx.shape[1]
+    a.ratio, a.window = int(ratio), int(window)
+    a.q_dtype, a.out_dtype = _dense_code(q, "q"), _dense_code(out, "out")
+    a.kv_dtype = FP4_E2M1 if kv_fp4 else _dense_code(kv, "kv")
+    a.swa_dtype = FP8_E4M3 if swa_fp8 else _dense_code(swa, "swa")
+    a.q, a.pos, a.idx, a.kv, a.kv_scale = _ptr(q), _ptr(pos), _ptr(idx), _ptr(kv), _ptr(kv_scale)
+    a.kv_row_base, a.swa, a.swa_scale, a.sink = _ptr(kv_row_base), _ptr(swa), _ptr(swa_scale), _ptr(sink)
+    a.rope_inv_freq, a.softmax_scale, a.out = _ptr(inv_freq), float(softmax_scale), _ptr(out)
+    return a
+
+
+def attn_workspace_size(rows, heads, dim, window, topk, splits=0):
+    return int(_lib.csa2_attn_workspace_size(int(rows), int(heads), int(dim), int(window), int(topk), int(splits)))
+
+
+def sparse_attn_decode(q, pos, idx, kv, kv_row_base, swa, sink, inv_freq, ratio, window, softmax_scale, out, *,
+                       rope_dim=64, kv_scale=None, swa_scale=None, kv_fp4=False, swa_fp8=False, splits=0,
+                       workspace=None, stream=None):
+    """Decode attention: ``swa`` is one ring [rows, window, D] per query row."""
+    a = _attn_args(q, pos, idx, kv, kv_scale, kv_row_base, swa, swa_scale, sink, inv_freq, ratio, window,
+                   softmax_scale, out, rope_dim, kv_fp4, swa_fp8)
+    if tuple(swa.shape) != (a.rows, a.window, a.dim):
+        raise ValueError("csa2.sparse_attn_decode: swa must be [rows, window, dim]")
+    if swa_fp8 and tuple(swa_scale.shape) != (a.rows, a.window):
+        raise ValueError("csa2.sparse_attn_decode: swa_scale must be [rows, window]")
+    a.splits = int(splits)
+    need = attn_workspace_size(a.rows, a.heads, a.dim, a.window, a.topk, a.splits)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _dev(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("csa2_sparse_attn_decode",
+           _lib.csa2_sparse_attn_decode(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def sparse_attn_prefill(q, pos, idx, kv, swa, swa_pos0, sink, inv_freq, ratio, window, softmax_scale, out, *,
+                        rope_dim=64, kv_row_base=None, kv_scale=None, swa_scale=None, kv_fp4=False, swa_fp8=False,
+                        stream=None):
+    """Prefill attention: ``swa`` is one linear array [swa_rows, D]; row t holds position swa_pos0 + t."""
+    if kv_row_base is None:
+        kv_row_base = torch.zeros(q.shape[0], dtype=torch.int64, device=q.device)
+    a = _attn_args(q, pos, idx, kv, kv_scale, kv_row_base, swa, swa_scale, sink, inv_freq, ratio, window,
+                   softmax_scale, out, rope_dim, kv_fp4, swa_fp8)
+    if swa.dim() != 2 or swa.shape[1] != a.dim or (swa_fp8 and tuple(swa_scale.shape) != (swa.shape[0],)):
+        raise ValueError("csa2.sparse_attn_prefill: swa must be [swa_rows, dim] (and swa_scale [swa_rows])")
+    a.swa_rows, a.swa_pos0 = swa.shape[0], int(swa_pos0)
+    _check("csa2_sparse_attn_prefill", _lib.csa2_sparse_attn_prefill(ctypes.byref(a), _stream(stream)))
+    return out

@@ -1,0 +1,79 @@
+// Internal launch interface between the C ABI layer (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa2.h"
+
+namespace csa2 {
+
+struct IndexParams {
+    const void* q;
+    const float* w;
+    const void* k;
+    const float* k_scale;
+    const int64_t* row_base;
+    const int64_t* pos;
+    const int32_t* cand;
+    float* scores;
+    int64_t width;
+    int64_t cols_per_wg;
+    int32_t n_blocks;
+    int32_t block_rows;
+    int32_t ratio;
+    float scale;
+};
+
+hipError_t launch_indexer_score(const IndexParams& p, int rows, int heads, int dim, int dtype, bool reindex,
+                                hipStream_t stream);
+bool indexer_supported(int heads, int dim, int dtype);
+
+struct TopkParams {
+    const float* scores;
+    const int64_t* pos;
+    const int32_t* cand;
+    int32_t* out;
+    int64_t width;
+    int32_t k;
+    int32_t ratio;
+    int32_t n_blocks;  // 0: FULL validity
+    int32_t block_rows;
+};
+
+hipError_t launch_topk_select(const TopkParams& p, int rows, hipStream_t stream);
+
+struct AttnParams {
+    const void* q;
+    const int64_t* pos;
+    const int32_t* idx;
+    const void* kv;
+    const uint8_t* kv_scale;
+    const int64_t* kv_row_base;
+    const void* swa;
+    const float* swa_scale;
+    const float* sink;
+    const double* inv_freq;
+    void* out;
+    float* ws_acc;  // decode partials: [rows, splits, heads, dim]
+    float* ws_ml;   // decode partials: [rows, splits, heads, 2] (max in log2 units, sum)
+    int64_t swa_rows;
+    int64_t swa_pos0;
+    int32_t rows;
+    int32_t topk;
+    int32_t ratio;
+    int32_t window;
+    int32_t splits;
+    int32_t tiles_per_split;
+    float scale_log2;  // softmax_scale * log2(e)
+};
+
+struct AttnShape {
+    int heads, dim, rope_dim;
+    int q_dtype, kv_dtype, swa_dtype, out_dtype;
+};
+
+bool attn_supported(const AttnShape& s);
+hipError_t launch_sparse_attn(const AttnParams& p, const AttnShape& s, bool decode, hipStream_t stream);
+
+}  // namespace csa2

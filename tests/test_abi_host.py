@@ -1,0 +1,175 @@
+"""Host-only checks of the C ABI library: it loads, exports what include/csa2.h declares,
+the binding's struct layouts match the C compiler's, and argument validation rejects
+bad calls before any launch (no GPU needed for any of these)."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+csa2 = pytest.importorskip("sparse_latent_attention_amd")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(csa2.LIB_PATH)
+    names = _declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(csa2.EXPORTED)
+    assert csa2.ABI_VERSION == 1
+
+
+def test_struct_layouts_match_c_compiler():
+    prog = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "csa2.h"
+#define F(T, f) printf(#T " " #f " %zu\n", offsetof(T, f));
+int main(void) {
+  printf("csa2_index_args sizeof %zu\n", sizeof(csa2_index_args));
+  printf("csa2_topk_args sizeof %zu\n", sizeof(csa2_topk_args));
+  printf("csa2_attn_args sizeof %zu\n", sizeof(csa2_attn_args));
+  F(csa2_index_args, width) F(csa2_index_args, q) F(csa2_index_args, cand) F(csa2_index_args, scale) F(csa2_index_args, scores)
+  F(csa2_topk_args, width) F(csa2_topk_args, scores) F(csa2_topk_args, out)
+  F(csa2_attn_args, swa_rows) F(csa2_attn_args, q) F(csa2_attn_args, rope_inv_freq) F(csa2_attn_args, softmax_scale) F(csa2_attn_args, out)
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(src, "w").write(prog)
+        subprocess.run(["gcc", "-I", os.path.dirname(HEADER), src, "-o", exe], check=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    cls = {"csa2_index_args": csa2.IndexArgs, "csa2_topk_args": csa2.TopkArgs, "csa2_attn_args": csa2.AttnArgs}
+    for line in out.strip().splitlines():
+        t, f, v = line.split()
+        if f == "sizeof":
+            assert ctypes.sizeof(cls[t]) == int(v), line
+        else:
+            assert getattr(cls[t], f).offset == int(v), line
+
+
+def _index_args(**kw):
+    a = csa2.IndexArgs()
+    a.struct_size = ctypes.sizeof(csa2.IndexArgs)
+    a.mode, a.rows, a.heads, a.dim, a.ratio = 0, 4, 64, 128, 2
+    a.q_dtype = a.k_dtype = csa2.BF16
+    a.width = 100
+    for p in ("q", "w", "k", "row_base", "pos", "scores"):
+        setattr(a, p, ctypes.c_void_p(0x1000))
+    a.scale = 0.01
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("struct_size", 8, csa2.ERR_INVALID_ARG),
+    ("mode", 7, csa2.ERR_INVALID_ARG),
+    ("ratio", 3, csa2.ERR_INVALID_ARG),
+    ("heads", 32, csa2.ERR_UNSUPPORTED),
+    ("k_dtype", csa2.F32, csa2.ERR_UNSUPPORTED),
+    ("rows", -1, csa2.ERR_INVALID_ARG),
+    ("q", None, csa2.ERR_INVALID_ARG),
+    ("k_scale", ctypes.c_void_p(0x1000), csa2.ERR_INVALID_ARG),
+    ("scale", float("nan"), csa2.ERR_INVALID_ARG),
+])
+def test_indexer_validation(field, value, status):
+    a = _index_args(**{field: value})
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == status
+
+
+def test_indexer_reindex_width_must_match_pool():
+    a = _index_args(mode=csa2.MODE_REINDEX, cand=ctypes.c_void_p(0x1000), n_blocks=2048, block_rows=8, width=100)
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+    a = _index_args(mode=csa2.MODE_REINDEX, cand=None, n_blocks=2048, block_rows=8, width=16384)
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+
+
+def test_empty_calls_launch_nothing():
+    a = _index_args(rows=0)
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.OK
+    t = csa2.TopkArgs()
+    t.struct_size, t.rows, t.k, t.ratio, t.width = ctypes.sizeof(csa2.TopkArgs), 0, 512, 1, 1000
+    assert csa2._lib.csa2_topk_select(ctypes.byref(t), None, 0, None) == csa2.OK
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("k", 0, csa2.ERR_INVALID_ARG), ("k", 4096, csa2.ERR_INVALID_ARG), ("ratio", 0, csa2.ERR_INVALID_ARG),
+    ("width", 1 << 31, csa2.ERR_INVALID_ARG), ("n_blocks", 3, csa2.ERR_INVALID_ARG),
+])
+def test_topk_validation(field, value, status):
+    t = csa2.TopkArgs()
+    t.struct_size, t.rows, t.k, t.ratio, t.width = ctypes.sizeof(csa2.TopkArgs), 2, 512, 1, 1000
+    t.scores = t.pos = t.out = ctypes.c_void_p(0x1000)
+    setattr(t, field, value)
+    assert csa2._lib.csa2_topk_select(ctypes.byref(t), None, 0, None) == status
+
+
+def _attn_args(**kw):
+    a = csa2.AttnArgs()
+    a.struct_size = ctypes.sizeof(csa2.AttnArgs)
+    a.rows, a.heads, a.dim, a.rope_dim, a.topk, a.ratio, a.window = 4, 64, 512, 64, 512, 1, 128
+    a.q_dtype = a.kv_dtype = a.swa_dtype = a.out_dtype = csa2.BF16
+    for p in ("q", "pos", "idx", "kv", "kv_row_base", "swa", "sink", "rope_inv_freq", "out"):
+        setattr(a, p, ctypes.c_void_p(0x1000))
+    a.softmax_scale = 0.044
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("window", 100, csa2.ERR_INVALID_ARG), ("topk", 500, csa2.ERR_INVALID_ARG), ("ratio", 4, csa2.ERR_INVALID_ARG),
+    ("heads", 32, csa2.ERR_UNSUPPORTED), ("kv_dtype", csa2.FP8_E4M3, csa2.ERR_UNSUPPORTED),
+    ("q_dtype", csa2.F32, csa2.ERR_UNSUPPORTED), ("kv_dtype", csa2.FP4_E2M1, csa2.ERR_INVALID_ARG),
+    ("softmax_scale", 0.0, csa2.ERR_INVALID_ARG), ("sink", None, csa2.ERR_INVALID_ARG),
+    ("q", ctypes.c_void_p(0x1004), csa2.ERR_INVALID_ARG),
+])
+def test_attention_validation(field, value, status):
+    a = _attn_args(**{field: value})
+    assert csa2._lib.csa2_sparse_attn_prefill(ctypes.byref(a), None) == status
+
+
+def test_decode_rejects_small_workspace():
+    a = _attn_args(rows=8, splits=4)
+    need = csa2.attn_workspace_size(8, 64, 512, 128, 512, 4)
+    assert need > 0
+    assert csa2._lib.csa2_sparse_attn_decode(ctypes.byref(a), ctypes.c_void_p(0x1000), need - 1, None) == \
+        csa2.ERR_WORKSPACE
+
+
+def test_status_strings():
+    for s in range(5):
+        assert csa2.status_string(s)
+    assert csa2.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("dim,theta,factor,orig", [(64, 160000.0, 16.0, 65536), (16, 10000.0, 1.0, 0),
+                                                   (64, 10000.0, 1.0, 0)])
+def test_rope_table_matches_oracle(dim, theta, factor, orig):
+    import oracle
+    ours = csa2.rope_inv_freq(dim, theta, factor, orig).numpy()
+    ref = oracle.rope.inv_freq(dim, theta, factor, orig)
+    assert np.allclose(ours, ref, rtol=1e-14, atol=0)
+
+
+def test_rope_table_rejects_bad_args():
+    out = (ctypes.c_double * 8)()
+    assert csa2._lib.csa2_rope_inv_freq(15, 1e4, 1.0, 0, out) == csa2.ERR_INVALID_ARG
+    assert csa2._lib.csa2_rope_inv_freq(16, 0.5, 1.0, 0, out) == csa2.ERR_INVALID_ARG
+    assert csa2._lib.csa2_rope_inv_freq(16, 1e4, 1.0, 0, None) == csa2.ERR_INVALID_ARG

@@ -1,0 +1,162 @@
+"""GPU parity of the HIP path against the oracle at sizes the oracle finishes in seconds.
+
+Each config is a reduced copy of one of the five workloads (same dtypes and
+head shapes) with ragged positions, widths that are not multiples of the tile
+sizes, rows whose history is shorter than top-k, and rows at position 0.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import CONFIGS, make_inputs
+
+from harness import (BF16_ATOL, BF16_RTOL, F32_ATOL, F32_RTOL, SCORE_TOL, assert_close, gpu_attention, gpu_scores,
+                     gpu_topk, oracle_attention, oracle_score_bound, oracle_scores, oracle_topk,
+                     topk_band_mismatches)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny_full_fp32": CONFIGS["tiny_full_fp32"],
+    "tiny_dense_k128": CONFIGS["tiny_full_fp32"].replace(topk=128),
+    "full_decode_small": CONFIGS["full_decode_64k"].replace(batch=7, q_tokens=7, context=3001, ragged=True),
+    "full_decode_small_unit": CONFIGS["full_decode_64k"].replace(batch=4, q_tokens=4, context=2500, ragged=True,
+                                                                 value_scale="unit"),
+    "reindex_small": CONFIGS["reindex_decode_1m"].replace(batch=7, q_tokens=7, context=40001, n_blocks=200,
+                                                          ragged=True),
+    "lowp_small": CONFIGS["lowp_full_decode_1m"].replace(batch=7, q_tokens=7, context=5003, ragged=True),
+    "prefill_small": CONFIGS["prefill_4096_at_128k"].replace(q_tokens=300, context=2000, reuse_layers=2),
+}
+
+
+def _tol(cfg):
+    return (F32_ATOL, F32_RTOL) if cfg.out_dtype == "f32" else (BF16_ATOL, BF16_RTOL)
+
+
+@pytest.fixture(scope="module", params=list(SMALL))
+def case(request):
+    cfg = SMALL[request.param]
+    print(f"\n[case] {request.param} seed=11 rows={cfg.q_tokens} width={cfg.width}", flush=True)
+    x = make_inputs(cfg, 11, device="cuda")
+    scores = gpu_scores(cfg, x)
+    idx = gpu_topk(cfg, x, scores)
+    torch.cuda.synchronize()
+    return request.param, cfg, x, scores, idx
+
+
+def test_indexer_scores(case):
+    name, cfg, x, scores, _ = case
+    rows = np.arange(cfg.q_tokens)
+    ref = oracle_scores(cfg, x, rows)
+    bound = oracle_score_bound(cfg, x, rows)
+    got = scores.cpu().numpy().astype(np.float64)
+    inval = ~np.isfinite(bound)
+    assert np.all(got[inval] == -np.inf) and np.all(ref[inval] == -np.inf)
+    err = np.abs(got[~inval] - ref[~inval])
+    ratio = float((err / bound[~inval]).max()) if err.size else 0.0
+    print(f"[{name}] score max |d|/A = {ratio:.3e}")
+    assert ratio <= SCORE_TOL
+
+
+def test_topk_bit_exact_on_gpu_scores(case):
+    name, cfg, x, scores, idx = case
+    rows = np.arange(cfg.q_tokens)
+    ref = oracle_topk(cfg, x, scores.cpu().numpy().astype(np.float64), rows)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+def test_topk_end_to_end_band(case):
+    name, cfg, x, scores, idx = case
+    rows = np.arange(cfg.q_tokens)
+    s_ref = oracle_scores(cfg, x, rows)
+    ref = oracle_topk(cfg, x, s_ref, rows)
+    bound = oracle_score_bound(cfg, x, rows)
+    n_diff, n_bad = topk_band_mismatches(cfg, x, rows, idx.cpu().numpy(), ref, s_ref, bound)
+    print(f"[{name}] end-to-end index differences: {n_diff} (outside the band: {n_bad})")
+    assert n_bad == 0
+
+
+def test_attention_all_layers(case):
+    name, cfg, x, scores, idx = case
+    rows = np.arange(cfg.q_tokens)
+    atol, rtol = _tol(cfg)
+    idx_np = idx.cpu().numpy()
+    for layer in range(len(x["layers"])):
+        out = gpu_attention(cfg, x, idx, layer=layer)
+        ref = oracle_attention(cfg, x, idx_np, rows, layer=layer)
+        e = assert_close(out, ref, atol, rtol, f"{name} layer {layer}")
+        print(f"[{name}] layer {layer} attention max_abs {e:.3e}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 40])
+def test_decode_splits_agree(splits):
+    cfg = SMALL["full_decode_small"]
+    x = make_inputs(cfg, 5, device="cuda")
+    idx = gpu_topk(cfg, x, gpu_scores(cfg, x))
+    out = gpu_attention(cfg, x, idx, splits=splits)
+    ref = oracle_attention(cfg, x, idx.cpu().numpy(), np.arange(cfg.q_tokens))
+    assert_close(out, ref, BF16_ATOL, BF16_RTOL, f"splits={splits}")
+
+
+def test_injected_indices_and_masks():
+    # -1 padding, duplicates, rows the group-causal mask hides, far out-of-range rows
+    cfg = SMALL["lowp_small"]
+    x = make_inputs(cfg, 3, device="cuda")
+    B, k = cfg.batch, cfg.topk
+    g = torch.Generator().manual_seed(0)
+    idx = torch.randint(0, cfg.n_main_rows, (B, k), generator=g, dtype=torch.int32)
+    idx[:, 0:16] = -1
+    idx[:, 16:32] = idx[:, 32:48]                     # duplicates count twice
+    idx[:, 48] = cfg.n_main_rows + 5                  # beyond the plane: masked (never read)
+    idx[:, 49] = 2 ** 31 - 1
+    idx[:, 50] = -7
+    idx = idx.cuda()
+    out = gpu_attention(cfg, x, idx)
+    ref = oracle_attention(cfg, x, idx.cpu().numpy(), np.arange(B))
+    assert_close(out, ref, BF16_ATOL, BF16_RTOL, "injected indices")
+
+
+def test_sink_minus_inf():
+    cfg = SMALL["full_decode_small_unit"]
+    x = make_inputs(cfg, 4, device="cuda")
+    x["layers"][0]["sink"] = torch.full_like(x["layers"][0]["sink"], -math.inf)
+    idx = gpu_topk(cfg, x, gpu_scores(cfg, x))
+    out = gpu_attention(cfg, x, idx)
+    ref = oracle_attention(cfg, x, idx.cpu().numpy(), np.arange(cfg.q_tokens))
+    assert_close(out, ref, BF16_ATOL, BF16_RTOL, "sink=-inf")
+
+
+def test_topk_crafted_scores():
+    # ties, NaN, -0, -inf and short rows, on the GPU kernel directly
+    import sparse_latent_attention_amd as csa2
+    rng = np.random.default_rng(1)
+    rows, width, k = 9, 3000, 512
+    s = rng.integers(-3, 4, (rows, width)).astype(np.float32) * 0.5
+    s[0] = 1.0                                      # all equal: lowest columns win
+    s[1, rng.random(width) < 0.3] = np.nan
+    s[2, rng.random(width) < 0.5] = -0.0
+    s[3] = -np.inf
+    s[4, :] = np.arange(width, dtype=np.float32)    # distinct
+    s[5] = rng.standard_normal(width).astype(np.float32)
+    pos = np.array([2999, 2999, 2999, 2999, 2999, 2999, 100, 0, 511], dtype=np.int64)
+    sc = torch.from_numpy(s).cuda()
+    pt = torch.from_numpy(pos).cuda()
+    out = torch.empty(rows, k, dtype=torch.int32, device="cuda")
+    csa2.topk_select(sc, pt, 1, out)
+    ref = oracle.topk.topk_full(s.astype(np.float64), pos, 1, k)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_deterministic():
+    cfg = SMALL["reindex_small"]
+    x = make_inputs(cfg, 8, device="cuda")
+    a = gpu_scores(cfg, x)
+    ia = gpu_topk(cfg, x, a)
+    oa = gpu_attention(cfg, x, ia)
+    b = gpu_scores(cfg, x)
+    ib = gpu_topk(cfg, x, b)
+    ob = gpu_attention(cfg, x, ib)
+    assert torch.equal(a, b) and torch.equal(ia, ib) and torch.equal(oa, ob)
