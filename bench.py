@@ -59,6 +59,38 @@ def algorithmic_bytes(cfg, x):
             "scored_rows": scored_rows}
 
 
+KERNEL_SOURCES = {
+    "indexer_score": ["indexer.hip", "common.hpp", "kernels.hpp"],
+    "topk_select": ["topk.hip", "common.hpp", "kernels.hpp"],
+    "sparse_attn": ["attention.hip", "common.hpp", "kernels.hpp"],
+}
+
+
+def kernel_source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(ROOT, "sparse_latent_attention_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if it was
+    taken on the current sources of this kernel (profiles/traffic_<workload>.md, json block)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(block)["kernels"].get(kernel)
+    except (IndexError, ValueError, KeyError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return int(round((rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024))
+
+
 def cpu_baseline(cfg, x, budget_s=20.0):
     """The oracle (float64 NumPy) on the host, one query row at a time, for about budget_s seconds."""
     import numpy as np
@@ -130,6 +162,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="after the bench, run a plain 1 GiB float32 copy kernel 3 times (the reference for "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE scaling: 1 GiB read + 1 GiB written per launch)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
@@ -159,14 +194,29 @@ def main():
     tau_i = 1.0 / math.sqrt(cfg.idx_dim * cfg.idx_heads)
     tau = 1.0 / math.sqrt(cfg.dim)
     akw = dict(rope_dim=cfg.rope_dim, kv_fp4=cfg.main_dtype == "fp4", swa_fp8=cfg.swa_dtype == "fp8", kv_scale=kvs)
-    attn_ws = None
-    if cfg.phase == "decode":
-        n = csa2.attn_workspace_size(rows, cfg.heads, cfg.dim, cfg.window, cfg.topk)
-        attn_ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     topk_ws = torch.empty(max(csa2.topk_workspace_size(rows, cfg.width, cfg.topk), 1), dtype=torch.uint8, device=dev)
 
     names = ["indexer_score", "topk_select", "sparse_attn"]
     evs = {n: [] for n in names}
+    # Arguments are marshalled once; each step only crosses into the library.
+    # The indexer also builds the score-key histogram when top-k takes its wide-row path.
+    key_hist = (torch.empty(rows, 4096, dtype=torch.int32, device=dev)
+                if csa2.topk_uses_key_hist(rows, cfg.width, cfg.topk) else None)
+    call_idx = csa2.prepare_indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, tau_i, scores,
+                                          k_scale=kIs, cand=x.get("cand"), block_rows=cfg.block_rows,
+                                          fp8=cfg.idx_dtype == "fp8", key_hist=key_hist)
+    call_topk = csa2.prepare_topk_select(scores, x["pos"], cfg.ratio, idx, cand=x.get("cand"),
+                                         block_rows=cfg.block_rows, workspace=topk_ws, key_hist=key_hist)
+    call_attn = []
+    for li, L in enumerate(x["layers"]):
+        if cfg.phase == "decode":
+            call_attn.append(csa2.prepare_sparse_attn_decode(
+                L["q"], x["pos"], idx, kv, x["kv_row_base"], x["swa"], L["sink"], freqs, cfg.ratio, cfg.window, tau,
+                outs[li], swa_scale=x["swa_scale"], **akw))
+        else:
+            call_attn.append(csa2.prepare_sparse_attn_prefill(
+                L["q"], x["pos"], idx, kv, L["swa"], x["swa_pos0"], L["sink"], freqs, cfg.ratio, cfg.window, tau,
+                outs[li], swa_scale=L["swa_scale"], kv_row_base=x["kv_row_base"], **akw))
 
     def step(record):
         def ev():
@@ -174,21 +224,12 @@ def main():
             e.record()
             return e
         e0 = ev() if record else None
-        csa2.indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, tau_i, scores, k_scale=kIs,
-                           cand=x.get("cand"), block_rows=cfg.block_rows, fp8=cfg.idx_dtype == "fp8")
+        call_idx()
         e1 = ev() if record else None
-        csa2.topk_select(scores, x["pos"], cfg.ratio, idx, cand=x.get("cand"), block_rows=cfg.block_rows,
-                         workspace=topk_ws)
+        call_topk()
         e2 = ev() if record else None
-        for li, L in enumerate(x["layers"]):
-            if cfg.phase == "decode":
-                csa2.sparse_attn_decode(L["q"], x["pos"], idx, kv, x["kv_row_base"], x["swa"], L["sink"], freqs,
-                                        cfg.ratio, cfg.window, tau, outs[li], swa_scale=x["swa_scale"],
-                                        workspace=attn_ws, **akw)
-            else:
-                csa2.sparse_attn_prefill(L["q"], x["pos"], idx, kv, L["swa"], x["swa_pos0"], L["sink"], freqs,
-                                         cfg.ratio, cfg.window, tau, outs[li], swa_scale=L["swa_scale"],
-                                         kv_row_base=x["kv_row_base"], **akw)
+        for c in call_attn:
+            c()
         e3 = ev() if record else None
         if record:
             evs["indexer_score"].append((e0, e1))
@@ -212,8 +253,9 @@ def main():
     dominant = max(names, key=lambda n: kern_ms[n])
     achieved = ab[dominant] / (kern_ms[dominant] * 1e-3) / 1e9
     roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "algorithmic_bytes_per_launch": ab[dominant]}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dominant, cfg.name),
+                "algorithmic_bytes_per_launch": ab[dominant], "source_hash": kernel_source_hash(dominant)}
     q_tokens = rows
     line = {
         "metric": METRIC, "value": round(q_tokens / (ms_step * 1e-3), 1), "unit": "query-tokens/s", "n_gpus": 1,
@@ -233,6 +275,14 @@ def main():
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_budget)
     print(json.dumps(line), flush=True)
+    if args.calibrate:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy": {"bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
+                                               "launches": 3}}), flush=True)
 
 
 if __name__ == "__main__":

@@ -127,6 +127,12 @@ typedef struct csa2_index_args {
     float scale;                /* score scale (dim^-1/2 * heads^-1/2 in the pages' model) */
     int32_t _pad1;
     float* scores;              /* out: [rows, width] float32 */
+    uint32_t* key_hist;         /* optional out: [rows, 4096], or NULL.  The call zeroes it, then
+                                 * counts every valid score of row r in bin key(score) >> 20, where
+                                 * key is the order-preserving 32-bit key csa2_topk_select ranks by
+                                 * (bits | 0x80000000 for scores >= +0, ~bits below, NaN as -inf,
+                                 * -0 as +0).  Passing it on to csa2_topk_select saves that call a
+                                 * full pass over the scores. */
 } csa2_index_args;
 
 int32_t csa2_indexer_score(const csa2_index_args* args, csa2_stream_t stream);
@@ -161,6 +167,8 @@ typedef struct csa2_topk_args {
     const int64_t* pos;         /* [rows] absolute query positions */
     const int32_t* cand;        /* REINDEX: [rows, n_blocks]; NULL for FULL */
     int32_t* out;               /* out: [rows, k] int32 */
+    const uint32_t* key_hist;   /* optional: [rows, 4096] histogram csa2_indexer_score wrote for exactly
+                                 * these scores and this validity, or NULL */
 } csa2_topk_args;
 
 /* Bytes of workspace csa2_topk_select needs for these sizes (may be 0). */
@@ -201,13 +209,15 @@ int32_t csa2_topk_select(const csa2_topk_args* args, void* workspace, size_t wor
  * [swa_rows] in prefill).
  *
  * Supported: (heads, dim, rope_dim) in {(4, 64, 16), (64, 512, 64)}; window
- * and topk multiples of 16; F32 only together with F32 everywhere (the
+ * a multiple of 16 in [16, 1024] and topk a multiple of 16 in [0, 2048]; F32 only together with F32 everywhere (the
  * (4, 64, 16) shape); otherwise BF16 q/out with kv BF16 or FP4 and swa BF16
  * or FP8.  rope_inv_freq holds rope_dim/2 float64 frequencies in device
  * memory (see csa2_rope_inv_freq).
  *
- * Decode splits the entry list of each row over `splits` workgroups and
- * merges their partial softmax states; the workspace holds those partials.
+ * Decode with few rows gives each (row, 16-head group) its own workgroup and
+ * merges the partial softmax states of its waves on chip; no workspace is
+ * needed (csa2_attn_workspace_size returns 0; the workspace arguments of
+ * csa2_sparse_attn_decode are accepted and ignored).
  */
 typedef struct csa2_attn_args {
     uint32_t struct_size;       /* sizeof(csa2_attn_args) */
@@ -222,7 +232,7 @@ typedef struct csa2_attn_args {
     int32_t kv_dtype;
     int32_t swa_dtype;
     int32_t out_dtype;
-    int32_t splits;             /* decode: workgroups per row (0 = library choice); prefill: ignored */
+    int32_t splits;             /* reserved, must be 0 */
     int32_t _pad0;
     int64_t swa_rows;           /* prefill: rows of the linear SWA array */
     int64_t swa_pos0;           /* prefill: position of linear SWA row 0 */
@@ -241,8 +251,7 @@ typedef struct csa2_attn_args {
     void* out;                  /* out: [rows, heads, dim] */
 } csa2_attn_args;
 
-/* Bytes of workspace csa2_sparse_attn_decode needs for these sizes and splits
- * (splits = 0: the library's choice, the same one the call makes). */
+/* Bytes of workspace csa2_sparse_attn_decode needs (currently always 0). */
 size_t csa2_attn_workspace_size(int32_t rows, int32_t heads, int32_t dim, int32_t window, int32_t topk,
                                 int32_t splits);
 

@@ -42,7 +42,7 @@ class IndexArgs(ctypes.Structure):
         ("struct_size", _u32), ("mode", _i32), ("rows", _i32), ("heads", _i32), ("dim", _i32), ("ratio", _i32),
         ("q_dtype", _i32), ("k_dtype", _i32), ("n_blocks", _i32), ("block_rows", _i32), ("_pad0", _i32),
         ("width", _i64), ("q", _vp), ("w", _vp), ("k", _vp), ("k_scale", _vp), ("row_base", _vp), ("pos", _vp),
-        ("cand", _vp), ("scale", _f32), ("_pad1", _i32), ("scores", _vp),
+        ("cand", _vp), ("scale", _f32), ("_pad1", _i32), ("scores", _vp), ("key_hist", _vp),
     ]
 
 
@@ -50,6 +50,7 @@ class TopkArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", _u32), ("rows", _i32), ("k", _i32), ("ratio", _i32), ("n_blocks", _i32),
         ("block_rows", _i32), ("width", _i64), ("scores", _vp), ("pos", _vp), ("cand", _vp), ("out", _vp),
+        ("key_hist", _vp),
     ]
 
 
@@ -144,14 +145,17 @@ def rope_inv_freq(rope_dim, theta, yarn_factor=1.0, yarn_orig_len=0):
 
 
 def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None, cand=None, block_rows=8,
-                  fp8=False, stream=None):
+                  fp8=False, key_hist=None, stream=None):
     """Fills ``scores`` [rows, width] (float32).  REINDEX when ``cand`` is given.
 
     q [rows, H_I, D_I] and k [*, D_I] are float32/bfloat16, or uint8 FP8-E4M3
     codes with ``fp8=True`` (then ``k_scale`` [*] float32 is required and the
-    query scales are already folded into w).
+    query scales are already folded into w).  ``key_hist`` (int32 [rows, 4096])
+    optionally receives the score-key histogram topk_select can reuse.
     """
-    _dev(q, w, k, row_base, pos, scores, k_scale, cand)
+    _dev(q, w, k, row_base, pos, scores, k_scale, cand, key_hist)
+    if key_hist is not None and (key_hist.dtype != torch.int32 or tuple(key_hist.shape) != (q.shape[0], 4096)):
+        raise ValueError("csa2.indexer_score: key_hist must be int32 [rows, 4096]")
     rows, heads, dim = q.shape
     if fp8:
         _need(q, torch.uint8, "q")
@@ -181,6 +185,7 @@ def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None,
         a.n_blocks, a.block_rows = cand.shape[1], int(block_rows)
     a.q, a.w, a.k, a.k_scale = _ptr(q), _ptr(w), _ptr(k), _ptr(k_scale)
     a.row_base, a.pos, a.cand, a.scores = _ptr(row_base), _ptr(pos), _ptr(cand), _ptr(scores)
+    a.key_hist = _ptr(key_hist)
     a.scale = float(scale)
     _check("csa2_indexer_score", _lib.csa2_indexer_score(ctypes.byref(a), _stream(stream)))
     return scores
@@ -190,9 +195,17 @@ def topk_workspace_size(rows, width, k):
     return int(_lib.csa2_topk_workspace_size(int(rows), int(width), int(k)))
 
 
-def topk_select(scores, pos, ratio, out, *, cand=None, block_rows=8, workspace=None, stream=None):
-    """Fills ``out`` [rows, k] int32 with the selected plane rows (ascending, -1 padded)."""
-    _dev(scores, pos, out, cand, workspace)
+def topk_uses_key_hist(rows, width, k=512):
+    """Whether topk_select takes its wide-row path for this shape (the one that reads ``key_hist``)."""
+    return topk_workspace_size(rows, width, k) > 0
+
+
+def topk_select(scores, pos, ratio, out, *, cand=None, block_rows=8, key_hist=None, workspace=None, stream=None):
+    """Fills ``out`` [rows, k] int32 with the selected plane rows (ascending, -1 padded).
+
+    ``key_hist`` is the histogram indexer_score wrote for these scores, if any.
+    """
+    _dev(scores, pos, out, cand, workspace, key_hist)
     _need(scores, torch.float32, "scores")
     _need(pos, torch.int64, "pos")
     _need(out, torch.int32, "out")
@@ -206,6 +219,7 @@ def topk_select(scores, pos, ratio, out, *, cand=None, block_rows=8, workspace=N
         _need(cand, torch.int32, "cand")
         a.n_blocks, a.block_rows = cand.shape[1], int(block_rows)
     a.scores, a.pos, a.cand, a.out = _ptr(scores), _ptr(pos), _ptr(cand), _ptr(out)
+    a.key_hist = _ptr(key_hist)
     need = topk_workspace_size(rows, width, a.k)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
@@ -250,8 +264,7 @@ def attn_workspace_size(rows, heads, dim, window, topk, splits=0):
 
 
 def sparse_attn_decode(q, pos, idx, kv, kv_row_base, swa, sink, inv_freq, ratio, window, softmax_scale, out, *,
-                       rope_dim=64, kv_scale=None, swa_scale=None, kv_fp4=False, swa_fp8=False, splits=0,
-                       workspace=None, stream=None):
+                       rope_dim=64, kv_scale=None, swa_scale=None, kv_fp4=False, swa_fp8=False, stream=None):
     """Decode attention: ``swa`` is one ring [rows, window, D] per query row."""
     a = _attn_args(q, pos, idx, kv, kv_scale, kv_row_base, swa, swa_scale, sink, inv_freq, ratio, window,
                    softmax_scale, out, rope_dim, kv_fp4, swa_fp8)
@@ -259,14 +272,7 @@ def sparse_attn_decode(q, pos, idx, kv, kv_row_base, swa, sink, inv_freq, ratio,
         raise ValueError("csa2.sparse_attn_decode: swa must be [rows, window, dim]")
     if swa_fp8 and tuple(swa_scale.shape) != (a.rows, a.window):
         raise ValueError("csa2.sparse_attn_decode: swa_scale must be [rows, window]")
-    a.splits = int(splits)
-    need = attn_workspace_size(a.rows, a.heads, a.dim, a.window, a.topk, a.splits)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    _dev(workspace)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("csa2_sparse_attn_decode",
-           _lib.csa2_sparse_attn_decode(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)))
+    _check("csa2_sparse_attn_decode", _lib.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, _stream(stream)))
     return out
 
 
@@ -283,3 +289,55 @@ def sparse_attn_prefill(q, pos, idx, kv, swa, swa_pos0, sink, inv_freq, ratio, w
     a.swa_rows, a.swa_pos0 = swa.shape[0], int(swa_pos0)
     _check("csa2_sparse_attn_prefill", _lib.csa2_sparse_attn_prefill(ctypes.byref(a), _stream(stream)))
     return out
+
+
+class Prepared:
+    """A C ABI call with its arguments marshalled once: ``call()`` only crosses into the library.
+
+    The tensors used to build it must stay alive and unchanged in shape while it is used.
+    """
+
+    def __init__(self, fn_name, fn, args, stream):
+        self.fn_name, self._fn, self._args, self._stream = fn_name, fn, args, stream
+
+    def __call__(self):
+        _check(self.fn_name, self._fn(*self._args, self._stream))
+
+
+def _prepare(fn_name, call, stream):
+    """Runs ``call`` once with a recording stub to capture the marshalled arguments."""
+    captured = {}
+    real = getattr(_lib, fn_name)
+
+    def stub(*a):
+        captured["args"] = a[:-1]
+        return OK
+
+    setattr(_lib, fn_name, stub)
+    try:
+        call()
+    finally:
+        setattr(_lib, fn_name, real)
+    return Prepared(fn_name, real, captured["args"], _stream(stream))
+
+
+def prepare_indexer_score(*args, stream=None, **kw):
+    return _prepare("csa2_indexer_score", lambda: indexer_score(*args, stream=stream, **kw), stream)
+
+
+def prepare_topk_select(*args, stream=None, **kw):
+    if "workspace" not in kw or kw["workspace"] is None:
+        scores, out = args[0], args[3]
+        need = topk_workspace_size(scores.shape[0], scores.shape[1], out.shape[1])
+        kw["workspace"] = torch.empty(max(need, 1), dtype=torch.uint8, device=scores.device)
+    p = _prepare("csa2_topk_select", lambda: topk_select(*args, stream=stream, **kw), stream)
+    p.workspace = kw["workspace"]
+    return p
+
+
+def prepare_sparse_attn_decode(*args, stream=None, **kw):
+    return _prepare("csa2_sparse_attn_decode", lambda: sparse_attn_decode(*args, stream=stream, **kw), stream)
+
+
+def prepare_sparse_attn_prefill(*args, stream=None, **kw):
+    return _prepare("csa2_sparse_attn_prefill", lambda: sparse_attn_prefill(*args, stream=stream, **kw), stream)

@@ -30,10 +30,14 @@ CFLAGS = [
 ]
 
 
+# Per-source extra flags.  The indexer keeps its MFMA results in ordinary VGPRs
+# (it has registers to spare), which removes one AGPR-to-VGPR move per result.
+EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-    cmd = [HIPCC] + CFLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + CFLAGS + EXTRA.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature and says so; that line is noise
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

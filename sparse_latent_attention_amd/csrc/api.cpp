@@ -23,16 +23,6 @@ size_t elem_bytes(int dtype) {
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
 
-// Tiles of 16 entries per decode workgroup for a row with `tiles` tiles split `splits` ways.
-int32_t tiles_per_split(int32_t tiles, int32_t splits) { return (tiles + splits - 1) / splits; }
-
-// Library choice of decode splits: enough workgroups to cover the 256 compute
-// units about twice, and at least 2 tiles of work per workgroup.
-int32_t choose_splits(int32_t rows, int32_t tiles) {
-    int32_t s = 1;
-    while (rows * s < 512 && s * 2 <= tiles / 2) s *= 2;
-    return s;
-}
 
 }  // namespace
 
@@ -92,7 +82,7 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
 
     csa2::IndexParams p;
     p.q = a->q; p.w = a->w; p.k = a->k; p.k_scale = a->k_scale; p.row_base = a->row_base; p.pos = a->pos;
-    p.cand = reindex ? a->cand : nullptr; p.scores = a->scores; p.width = a->width;
+    p.cand = reindex ? a->cand : nullptr; p.scores = a->scores; p.key_hist = a->key_hist; p.width = a->width;
     p.n_blocks = reindex ? a->n_blocks : 0; p.block_rows = reindex ? a->block_rows : 1; p.ratio = a->ratio;
     p.scale = a->scale;
     // Columns per workgroup: multiples of 256 (4 waves x 64), aiming at ~4096 workgroups.
@@ -108,12 +98,12 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
 }
 
 size_t csa2_topk_workspace_size(int32_t rows, int64_t width, int32_t k) {
-    (void)rows; (void)width; (void)k;
-    return 0;
+    (void)k;
+    if (rows <= 0 || width <= 0 || width >= (1LL << 31)) return 0;
+    return csa2::topk_workspace_bytes(rows, width);
 }
 
 int32_t csa2_topk_select(const csa2_topk_args* a, void* workspace, size_t workspace_bytes, csa2_stream_t stream) {
-    (void)workspace;
     if (a == nullptr || a->struct_size < sizeof(csa2_topk_args)) return CSA2_ERR_INVALID_ARG;
     if (a->rows < 0 || a->k < 1 || a->k > 2048 || a->width < 0 || a->width >= (1LL << 31)) return CSA2_ERR_INVALID_ARG;
     if (a->ratio != 1 && a->ratio != 2) return CSA2_ERR_INVALID_ARG;
@@ -122,19 +112,23 @@ int32_t csa2_topk_select(const csa2_topk_args* a, void* workspace, size_t worksp
         if (a->cand == nullptr || a->block_rows <= 0 || a->block_rows > 64) return CSA2_ERR_INVALID_ARG;
         if (a->width != (int64_t)a->n_blocks * a->block_rows) return CSA2_ERR_INVALID_ARG;
     }
-    if (workspace_bytes < csa2_topk_workspace_size(a->rows, a->width, a->k)) return CSA2_ERR_WORKSPACE;
+    const size_t need = csa2_topk_workspace_size(a->rows, a->width, a->k);
+    if (workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 256))) return CSA2_ERR_INVALID_ARG;
     if (a->rows == 0) return CSA2_OK;
     if (a->pos == nullptr || a->out == nullptr || (a->scores == nullptr && a->width > 0)) return CSA2_ERR_INVALID_ARG;
     csa2::TopkParams p;
     p.scores = a->scores; p.pos = a->pos; p.cand = a->n_blocks > 0 ? a->cand : nullptr; p.out = a->out;
+    p.key_hist = a->key_hist;
     p.width = a->width; p.k = a->k; p.ratio = a->ratio; p.n_blocks = a->n_blocks;
     p.block_rows = a->n_blocks > 0 ? a->block_rows : 1;
-    return hip_status(csa2::launch_topk_select(p, a->rows, reinterpret_cast<hipStream_t>(stream)));
+    return hip_status(csa2::launch_topk_select(p, a->rows, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
 static int32_t validate_attn(const csa2_attn_args* a, bool decode) {
     if (a == nullptr || a->struct_size < sizeof(csa2_attn_args)) return CSA2_ERR_INVALID_ARG;
-    if (a->rows < 0 || a->topk < 0 || a->window < 16 || (a->window % 16) != 0 || (a->topk % 16) != 0)
+    if (a->rows < 0 || a->topk < 0 || a->topk > 2048 || a->window < 16 || a->window > 1024 || (a->window % 16) != 0 ||
+        (a->topk % 16) != 0 || a->splits != 0)
         return CSA2_ERR_INVALID_ARG;
     if (a->ratio != 1 && a->ratio != 2) return CSA2_ERR_INVALID_ARG;
     if (!(a->softmax_scale > 0.f) || !isfinite(a->softmax_scale)) return CSA2_ERR_INVALID_ARG;
@@ -157,43 +151,24 @@ static csa2::AttnParams attn_params(const csa2_attn_args* a) {
     csa2::AttnParams p;
     p.q = a->q; p.pos = a->pos; p.idx = a->idx; p.kv = a->kv; p.kv_scale = a->kv_scale; p.kv_row_base = a->kv_row_base;
     p.swa = a->swa; p.swa_scale = a->swa_scale; p.sink = a->sink; p.inv_freq = a->rope_inv_freq; p.out = a->out;
-    p.ws_acc = nullptr; p.ws_ml = nullptr; p.swa_rows = a->swa_rows; p.swa_pos0 = a->swa_pos0; p.rows = a->rows;
-    p.topk = a->topk; p.ratio = a->ratio; p.window = a->window; p.splits = 1;
-    p.tiles_per_split = (a->window + a->topk) / 16;
+    p.swa_rows = a->swa_rows; p.swa_pos0 = a->swa_pos0; p.rows = a->rows;
+    p.topk = a->topk; p.ratio = a->ratio; p.window = a->window;
     p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
     return p;
 }
 
 size_t csa2_attn_workspace_size(int32_t rows, int32_t heads, int32_t dim, int32_t window, int32_t topk,
                                 int32_t splits) {
-    if (rows <= 0 || heads <= 0 || dim <= 0 || window < 0 || topk < 0) return 0;
-    const int32_t tiles = (window + topk) / 16;
-    if (splits <= 0) splits = choose_splits(rows, tiles);
-    if (splits <= 1) return 0;
-    const size_t per = (size_t)rows * (size_t)splits * (size_t)heads;
-    return per * (size_t)dim * sizeof(float) + per * 2 * sizeof(float) + 256;
+    (void)rows; (void)heads; (void)dim; (void)window; (void)topk; (void)splits;
+    return 0;  // partial softmax states are merged on chip
 }
 
 int32_t csa2_sparse_attn_decode(const csa2_attn_args* a, void* workspace, size_t workspace_bytes,
                                 csa2_stream_t stream) {
+    (void)workspace; (void)workspace_bytes;
     int32_t st = validate_attn(a, true);
     if (st != CSA2_OK || a->rows == 0) return st;
-    const int32_t tiles = (a->window + a->topk) / 16;
-    int32_t splits = a->splits;
-    if (splits < 0 || splits > 65535) return CSA2_ERR_INVALID_ARG;
-    if (splits == 0) splits = choose_splits(a->rows, tiles);
-    if (splits > tiles) splits = tiles;
-    const size_t need = csa2_attn_workspace_size(a->rows, a->heads, a->dim, a->window, a->topk, splits);
-    if (workspace_bytes < need) return CSA2_ERR_WORKSPACE;
-    if (need > 0 && (workspace == nullptr || !aligned(workspace, 16))) return CSA2_ERR_INVALID_ARG;
     csa2::AttnParams p = attn_params(a);
-    p.splits = splits;
-    p.tiles_per_split = tiles_per_split(tiles, splits);
-    if (splits > 1) {
-        const size_t per = (size_t)a->rows * (size_t)splits * (size_t)a->heads;
-        p.ws_acc = reinterpret_cast<float*>(workspace);
-        p.ws_ml = p.ws_acc + per * (size_t)a->dim;
-    }
     csa2::AttnShape s{a->heads, a->dim, a->rope_dim, a->q_dtype, a->kv_dtype, a->swa_dtype, a->out_dtype};
     return hip_status(csa2::launch_sparse_attn(p, s, true, reinterpret_cast<hipStream_t>(stream)));
 }

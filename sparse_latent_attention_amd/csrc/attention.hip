@@ -7,23 +7,33 @@
 // Flash 架构解剖", shared attention path, "四种层合并出来的是什么形状" and
 // "出来之后"; "DeepSeek-V4.1-Flash 结构说明", sections 4.1 and 6.1.)
 //
-// Design.  One workgroup handles one query row (and, in decode, one slice of
-// its entry list).  The entry list is W SWA entries followed by topk selected
-// rows, walked in tiles of 16 entries; W and topk are multiples of 16, so a
-// tile comes from one source.  Per tile:
-//   1. gather: each thread fetches 8 contiguous elements of 4 rows (one load
-//      instruction of a wave covers a whole row), decodes FP4/FP8 in
-//      registers, and stores the tile twice into LDS: row-major Kt[j][d] (the
-//      QK^T operand) and Vt[j/4][d][j%4] (the PV operand, 4 entries of one
-//      column contiguous).  K == V, so both copies come from one HBM read.
-//   2. each wave owns 16 heads: S^T[16 entries x 16 heads] = Kt . q^T with
-//      16x16x32 MFMAs (q stays in registers), an online-softmax update with
-//      the running max/sum per head, then out^T[d][h] += Vt^T . P^T with
-//      16x16x16 MFMAs.  The S^T result layout is exactly the P^T operand
-//      layout, so P never leaves registers.
-// The sink enters as the initial softmax state (max = sink, sum = 1).  Invalid
-// entries (absent SWA slots, -1 or out-of-range indices, rows the group-causal
-// mask hides) are zero-filled in LDS and get probability 0.
+// Shared design.  A query row's entry list is W SWA entries followed by topk
+// selected rows, walked in tiles of 16 entries (W and topk are multiples of 16,
+// so a tile comes from one source).  A tile is gathered once from HBM: each
+// thread owns "pairs" (4 rows x 8 contiguous elements; one wave load
+// instruction covers a whole row), decodes FP4/FP8 in registers, and stores
+// the tile twice into LDS -- row-major Kt[j][d] (the QK^T operand) and
+// Vt[j/4][d][j%4] (the PV operand, 4 entries of one column contiguous).  K == V,
+// so both copies come from one read.  A wave owns 16 heads: 16x16x32 MFMAs give
+// S^T[16 entries x 16 heads] = Kt . q^T with q in registers, an online softmax
+// updates the running max/sum per head, and out^T[d][h] += Vt^T . P^T with
+// 16x16x16 MFMAs; the S^T result layout is exactly the P^T operand layout, so
+// P never leaves registers.  The sink is the initial softmax state (max =
+// sink, sum = 1).  Invalid entries (absent SWA slots, -1 or out-of-range
+// indices, rows the group-causal mask hides) are zero-filled and get
+// probability 0.  The raw bytes of the next tile are loaded into registers
+// while the current tile is computed.
+//
+// Two kernels share that machinery:
+//   * attn_rows_kernel (prefill, and decode with many rows): one workgroup per
+//     query row, one wave per 16-head group, all waves on the same tile;
+//     two LDS tile buffers so one barrier per tile suffices.
+//   * attn_decode_kernel (decode with few rows): one workgroup per (row,
+//     16-head group) so small batches still fill the chip; its 4 waves take
+//     interleaved tiles with private LDS buffers and merge their softmax
+//     states through LDS at the end -- no partial results leave the chip.
+//     The workgroups of one row sit on the same XCD, so the 4x re-gather of
+//     that row's entries is served by one L2.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -68,63 +78,6 @@ __device__ __forceinline__ void pack_zero<float>(Pack8<float>& o) {
     for (int e = 0; e < 8; ++e) o.v[e] = 0.f;
 }
 
-// Loads elements [8*x8, 8*x8+8) of stored row `row` and converts them.
-//   F32/BF16: dense rows of D elements.  FP8: D codes per row times fscale[row].
-//   FP4: D/2 packed bytes per row times 2^(e8[row*D/32 + blk] - 127).
-template <int DT, int D, class CT>
-struct RowLoad;
-
-template <int D>
-struct RowLoad<CSA2_BF16, D, __bf16> {
-    static __device__ __forceinline__ void run(const void* base, const float*, const uint8_t*, int64_t row, int x8,
-                                               Pack8<__bf16>& o) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + row * D + 8 * x8);
-        o.w[0] = v[0]; o.w[1] = v[1]; o.w[2] = v[2]; o.w[3] = v[3];
-    }
-};
-
-template <int D>
-struct RowLoad<CSA2_F32, D, float> {
-    static __device__ __forceinline__ void run(const void* base, const float*, const uint8_t*, int64_t row, int x8,
-                                               Pack8<float>& o) {
-        const float* p = reinterpret_cast<const float*>(base) + row * D + 8 * x8;
-        const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-        o.v[0] = a[0]; o.v[1] = a[1]; o.v[2] = a[2]; o.v[3] = a[3];
-        o.v[4] = b[0]; o.v[5] = b[1]; o.v[6] = b[2]; o.v[7] = b[3];
-    }
-};
-
-template <int D>
-struct RowLoad<CSA2_FP8_E4M3, D, __bf16> {
-    static __device__ __forceinline__ void run(const void* base, const float* fscale, const uint8_t*, int64_t row,
-                                               int x8, Pack8<__bf16>& o) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(base) + row * D + 8 * x8);
-        const float s = fscale[row];
-        float f[8];
-        f32x2 a = fp8x2_to_f32<false>(v[0]), b = fp8x2_to_f32<true>(v[0]);
-        f32x2 c = fp8x2_to_f32<false>(v[1]), d = fp8x2_to_f32<true>(v[1]);
-        f[0] = a[0] * s; f[1] = a[1] * s; f[2] = b[0] * s; f[3] = b[1] * s;
-        f[4] = c[0] * s; f[5] = c[1] * s; f[6] = d[0] * s; f[7] = d[1] * s;
-        pack_from_floats<__bf16>(f, o);
-    }
-};
-
-template <int D>
-struct RowLoad<CSA2_FP4_E2M1, D, __bf16> {
-    static __device__ __forceinline__ void run(const void* base, const float*, const uint8_t* e8, int64_t row, int x8,
-                                               Pack8<__bf16>& o) {
-        const uint32_t v =
-            *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(base) + row * (D / 2) + 4 * x8);
-        const float s = e8m0_to_f32(e8[row * (D / 32) + (8 * x8) / 32]);
-        float f[8];
-        f32x2 a = fp4x2_to_f32<0>(v), b = fp4x2_to_f32<1>(v), c = fp4x2_to_f32<2>(v), d = fp4x2_to_f32<3>(v);
-        f[0] = a[0] * s; f[1] = a[1] * s; f[2] = b[0] * s; f[3] = b[1] * s;
-        f[4] = c[0] * s; f[5] = c[1] * s; f[6] = d[0] * s; f[7] = d[1] * s;
-        pack_from_floats<__bf16>(f, o);
-    }
-};
-
 // LDS tile writers.
 template <class CT, int D, int KS>
 __device__ __forceinline__ void store_k(CT* Kt, int j, int x8, const Pack8<CT>& v);
@@ -142,9 +95,12 @@ __device__ __forceinline__ void store_k<float, 64, 68>(float* Kt, int j, int x8,
     *reinterpret_cast<f32x4*>(p + 4) = f32x4{v.v[4], v.v[5], v.v[6], v.v[7]};
 }
 
-// Vt layout: Vt[jb * VS + d * 4 + i] holds entry 4*jb + i, element d.
+// Vt layout: Vt[jb * VS + vcol(d) + i] holds entry 4*jb + i, element d, where
+// vcol(d) = 4d + 4(d/8) leaves a 4-element gap after every 8 columns so the
+// lanes of a store (8 columns apart) spread over the LDS banks.
+__device__ __forceinline__ int vcol(int d) { return 4 * d + 4 * (d >> 3); }
 template <>
-__device__ __forceinline__ void store_v4<__bf16, 512, 512 * 4 + 64>(__bf16* Vt, int jb, int x8,
+__device__ __forceinline__ void store_v4<__bf16, 512, 2368>(__bf16* Vt, int jb, int x8,
                                                                    const Pack8<__bf16> (&v)[4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -154,17 +110,17 @@ __device__ __forceinline__ void store_v4<__bf16, 512, 512 * 4 + 64>(__bf16* Vt, 
         const uint32_t hi01 = (v[0].w[q] >> 16) | (v[1].w[q] & 0xffff0000u);
         const uint32_t hi23 = (v[2].w[q] >> 16) | (v[3].w[q] & 0xffff0000u);
         const int d = 8 * x8 + 2 * q;
-        *reinterpret_cast<u32x2*>(Vt + jb * (512 * 4 + 64) + d * 4) = u32x2{lo01, lo23};
-        *reinterpret_cast<u32x2*>(Vt + jb * (512 * 4 + 64) + (d + 1) * 4) = u32x2{hi01, hi23};
+        *reinterpret_cast<u32x2*>(Vt + jb * 2368 + vcol(d)) = u32x2{lo01, lo23};
+        *reinterpret_cast<u32x2*>(Vt + jb * 2368 + vcol(d + 1)) = u32x2{hi01, hi23};
     }
 }
 template <>
-__device__ __forceinline__ void store_v4<float, 64, 64 * 4 + 16>(float* Vt, int jb, int x8,
+__device__ __forceinline__ void store_v4<float, 64, 304>(float* Vt, int jb, int x8,
                                                                 const Pack8<float> (&v)[4]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int d = 8 * x8 + e;
-        *reinterpret_cast<f32x4*>(Vt + jb * (64 * 4 + 16) + d * 4) = f32x4{v[0].v[e], v[1].v[e], v[2].v[e], v[3].v[e]};
+        *reinterpret_cast<f32x4*>(Vt + jb * 304 + vcol(d)) = f32x4{v[0].v[e], v[1].v[e], v[2].v[e], v[3].v[e]};
     }
 }
 
@@ -257,55 +213,351 @@ __device__ __forceinline__ void rope_angle(int64_t pos, double f, float& c, floa
     s = (float)sd;
 }
 
+
+// Raw bytes of one pair (4 rows x 8 elements) of a tile, as loaded from HBM.
+struct RawPair {
+    u32x4 v[4];    // BF16: 16 B per row; F32: elements 0..3; FP8: .x .y; FP4: .x
+    u32x4 v2[4];   // F32: elements 4..7
+    float s[4];    // FP8 row scale or FP4 block scale
+    uint32_t valid;  // bit i: row i of the pair exists and is visible
+};
+
+template <int DT, int D>
+__device__ __forceinline__ void raw_load_row(const void* base, const float* fscale, const uint8_t* e8, int64_t row,
+                                             int x8, RawPair& raw, int i) {
+    if (DT == CSA2_BF16) {
+        raw.v[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + row * D + 8 * x8);
+    } else if (DT == CSA2_F32) {
+        const float* pf = reinterpret_cast<const float*>(base) + row * D + 8 * x8;
+        raw.v[i] = *reinterpret_cast<const u32x4*>(pf);
+        raw.v2[i] = *reinterpret_cast<const u32x4*>(pf + 4);
+    } else if (DT == CSA2_FP8_E4M3) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(base) + row * D + 8 * x8);
+        raw.v[i].x = w.x;
+        raw.v[i].y = w.y;
+        raw.s[i] = fscale[row];
+    } else {  // FP4-E2M1 with one E8M0 per 32
+        raw.v[i].x = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(base) + row * (D / 2) + 4 * x8);
+        raw.s[i] = e8m0_to_f32(e8[row * (D / 32) + (8 * x8) / 32]);
+    }
+}
+
+template <int DT, class CT>
+__device__ __forceinline__ void raw_convert(const RawPair& raw, int i, Pack8<CT>& o) {
+    if (!((raw.valid >> i) & 1u)) {
+        pack_zero<CT>(o);
+        return;
+    }
+    if constexpr (DT == CSA2_BF16) {
+        o.w[0] = raw.v[i].x; o.w[1] = raw.v[i].y; o.w[2] = raw.v[i].z; o.w[3] = raw.v[i].w;
+    } else if constexpr (DT == CSA2_F32) {
+        o.v[0] = __uint_as_float(raw.v[i].x); o.v[1] = __uint_as_float(raw.v[i].y);
+        o.v[2] = __uint_as_float(raw.v[i].z); o.v[3] = __uint_as_float(raw.v[i].w);
+        o.v[4] = __uint_as_float(raw.v2[i].x); o.v[5] = __uint_as_float(raw.v2[i].y);
+        o.v[6] = __uint_as_float(raw.v2[i].z); o.v[7] = __uint_as_float(raw.v2[i].w);
+    } else if constexpr (DT == CSA2_FP8_E4M3) {
+        const float sc = raw.s[i];
+        const f32x2 a = fp8x2_to_f32<false>(raw.v[i].x), b = fp8x2_to_f32<true>(raw.v[i].x);
+        const f32x2 c = fp8x2_to_f32<false>(raw.v[i].y), d = fp8x2_to_f32<true>(raw.v[i].y);
+        const float f[8] = {a[0] * sc, a[1] * sc, b[0] * sc, b[1] * sc, c[0] * sc, c[1] * sc, d[0] * sc, d[1] * sc};
+        pack_from_floats<CT>(f, o);
+    } else {
+        const float sc = raw.s[i];
+        const uint32_t w = raw.v[i].x;
+        const f32x2 a = fp4x2_to_f32<0>(w), b = fp4x2_to_f32<1>(w), c = fp4x2_to_f32<2>(w), d = fp4x2_to_f32<3>(w);
+        const float f[8] = {a[0] * sc, a[1] * sc, b[0] * sc, b[1] * sc, c[0] * sc, c[1] * sc, d[0] * sc, d[1] * sc};
+        pack_from_floats<CT>(f, o);
+    }
+}
+
+constexpr int kMaxTiles = 192;  // (window + topk) / 16 at most (window <= 1024, topk <= 2048)
+constexpr int kMaxTopk = 2048;
+
+// Per-row geometry the gather needs.
+struct RowCtx {
+    int64_t pos, nv, kv_base;
+    int r;
+};
+
+// Loads the raw bytes of pair (jb, x8) of tile `tile` (predicated on validity).
+// `sel` is the row's selected-index list, staged in LDS.
+template <int D, int KVT, int SWT, bool DECODE>
+__device__ __forceinline__ void load_pair(const AttnParams& p, const RowCtx& c, const int32_t* sel, int tile, int jb,
+                                          int x8, RawPair& raw) {
+    const int W = p.window;
+    raw.valid = 0u;
+    if (tile * 16 < W) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tile * 16 + 4 * jb + i;
+            int64_t srow;
+            bool valid;
+            if (DECODE) {
+                // Ring slot e holds position pos - ((pos - e) mod W); that position is
+                // negative (the slot was never written) exactly when e > pos.
+                valid = e <= c.pos;
+                srow = (int64_t)c.r * W + e;
+            } else {
+                const int64_t a = c.pos - (W - 1) + e;                // linear window position
+                srow = a - p.swa_pos0;
+                valid = a >= 0 && srow >= 0 && srow < p.swa_rows;
+            }
+            if (valid) raw_load_row<SWT, D>(p.swa, p.swa_scale, nullptr, srow, x8, raw, i);
+            raw.valid |= (valid ? 1u : 0u) << i;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tile * 16 + 4 * jb + i;
+            const int32_t id = sel[e - W];
+            const bool valid = id >= 0 && (int64_t)id < c.nv;  // group-causal mask
+            if (valid) raw_load_row<KVT, D>(p.kv, nullptr, p.kv_scale, c.kv_base + id, x8, raw, i);
+            raw.valid |= (valid ? 1u : 0u) << i;
+        }
+    }
+}
+
+// Decodes a loaded pair and writes it into the tile buffers.
+template <int D, class CT, int KS, int VS, int KVT, int SWT>
+__device__ __forceinline__ void store_pair(const RawPair& raw, bool swa_tile, CT* Kt, CT* Vt, int jb, int x8) {
+    Pack8<CT> v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (swa_tile) raw_convert<SWT, CT>(raw, i, v[i]);
+        else raw_convert<KVT, CT>(raw, i, v[i]);
+        store_k<CT, D, KS>(Kt, 4 * jb + i, x8, v[i]);
+    }
+    store_v4<CT, D, VS>(Vt, jb, x8, v);
+}
+
+template <class CT, int D>
+struct TileGeom {
+    static constexpr int KS = (D == 512) ? 520 : 68;                // Kt row stride (elements)
+    static constexpr int VS = (D == 512) ? 2368 : 304;  // Vt block stride (elements): 4D + D/2 + padding
+    static constexpr int K_ELEMS = 16 * KS;
+    static constexpr int V_ELEMS = 4 * VS;
+    static constexpr int BYTES = (K_ELEMS + V_ELEMS) * (int)sizeof(CT);
+};
+
+// One wave's work on one tile for its 16 heads: scores, online softmax, PV.
+template <int D, class CT, int KS, int VS>
+__device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_t vm, const typename Mma<CT>::Frag8* qf,
+                                             float scale_log2, int g, int li, float& m, float& l, f32x4* acc) {
+    typedef Mma<CT> M;
+    constexpr int NS = D / 32, NDT = D / 16;
+    // Four independent accumulation chains keep the matrix cores busy.
+    constexpr int NC = NS >= 4 ? 4 : NS;
+    f32x4 part[NC];
+#pragma unroll
+    for (int k = 0; k < NC; ++k) part[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) part[s % NC] = M::k32(part[s % NC], lds_frag8<CT>(Kt + li * KS + 32 * s + 8 * g), qf[s]);
+    f32x4 st = part[0];
+#pragma unroll
+    for (int k = 1; k < NC; ++k) st += part[k];
+    float x[4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        x[rr] = ((vm >> (4 * g + rr)) & 1u) ? st[rr] * scale_log2 : kNegInf;
+        tmax = fmaxf(tmax, x[rr]);
+    }
+    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+    // Lazy rescaling: m is only a reference point (the result is the same for any
+    // m), so it moves -- and acc and l are rescaled -- only when some head's scores
+    // exceed it by more than 2^8; the probabilities then stay below 256.
+    if (__ballot(tmax > m + 8.f) != 0ull) {
+        const float m_new = fmaxf(m, tmax);
+        const float alpha = exp2f(m - m_new);  // 0 when m was -inf
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+        m = m_new;
+    }
+    const float m_use = (m == kNegInf) ? 0.f : m;
+    float pr4[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        pr4[rr] = exp2f(x[rr] - m_use);
+        psum += pr4[rr];
+    }
+    l += psum;
+    const typename M::Frag4 pb = p_frag<CT>(pr4);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = M::k16(acc[dt], lds_frag4<CT>(Vt + g * VS + vcol(16 * dt + li)), pb);
+}
+
+// Normalises, rotates the rope tail back and stores 4 consecutive elements.
+template <int D, int R, int OT>
+__device__ __forceinline__ void emit4(void* out, int64_t off, int d0, f32x4 a, float inv, const float* rope_cs) {
+    float o0 = a[0] * inv, o1 = a[1] * inv, o2 = a[2] * inv, o3 = a[3] * inv;
+    if (d0 >= D - R) {
+        const int i0 = (d0 - (D - R)) / 2;
+        const float c0 = rope_cs[2 * i0], s0 = rope_cs[2 * i0 + 1];
+        const float c1 = rope_cs[2 * i0 + 2], s1 = rope_cs[2 * i0 + 3];
+        const float b0 = o0 * c0 + o1 * s0, b1 = o1 * c0 - o0 * s0;
+        const float b2 = o2 * c1 + o3 * s1, b3 = o3 * c1 - o2 * s1;
+        o0 = b0; o1 = b1; o2 = b2; o3 = b3;
+    }
+    store_out4<OT>(out, off, o0, o1, o2, o3);
+}
+
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// One workgroup per query row; wave w owns heads 16w .. 16w+15; shared tiles.
 template <int H, int D, int R, class CT, int QT, int KVT, int SWT, int OT, bool DECODE>
-__global__ __launch_bounds__(64 * ((H + 15) / 16)) void sparse_attn_kernel(const AttnParams p) {
+__global__ __launch_bounds__(64 * ((H + 15) / 16)) void attn_rows_kernel(const AttnParams p) {
     constexpr int NW = (H + 15) / 16;
     constexpr int NT = 64 * NW;
-    constexpr int KS = (D == 512) ? 520 : 68;               // Kt row stride (elements)
-    constexpr int VS = (D == 512) ? 512 * 4 + 64 : 64 * 4 + 16;  // Vt block stride (elements)
-    constexpr int NDT = D / 16;                              // 16-wide output tiles per head
-    constexpr int NS = D / 32;                               // k-steps of QK^T
-    constexpr int PAIRS = 4 * (D / 8);                       // (row-block, 8-element chunk) pairs per tile
-    typedef Mma<CT> M;
+    typedef TileGeom<CT, D> G;
+    constexpr int NS = D / 32, NDT = D / 16;
+    constexpr int PAIRS = 4 * (D / 8);
+    constexpr int PPT = (PAIRS + NT - 1) / NT;  // pairs per thread
 
-    __shared__ __attribute__((aligned(16))) CT Kt[16 * KS];
-    __shared__ __attribute__((aligned(16))) CT Vt[4 * VS];
-    __shared__ float rope_cs[R];  // [i] cos at 2i, sin at 2i+1
-    __shared__ uint32_t vmask;
+    __shared__ __attribute__((aligned(16))) CT tiles[2][G::K_ELEMS + G::V_ELEMS];
+    __shared__ float rope_cs[R];
+    __shared__ uint32_t vmask[kMaxTiles];  // validity bits of each tile's 16 entries, written once
+    __shared__ int32_t sel[kMaxTopk];      // this row's selected indices
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
-    const int r = blockIdx.x;
-    const int split = DECODE ? (int)blockIdx.y : 0;
-
-    const int64_t pos = p.pos[r];
-    const int64_t nv = (pos + 1) / p.ratio;
-    const int W = p.window;
-    const int n_tiles = (W + p.topk) / 16;
-    const int t_begin = split * p.tiles_per_split;
-    const int t_end = (t_begin + p.tiles_per_split < n_tiles) ? t_begin + p.tiles_per_split : n_tiles;
+    RowCtx c;
+    c.r = blockIdx.x;
+    c.pos = p.pos[c.r];
+    c.nv = (c.pos + 1) / p.ratio;
+    c.kv_base = p.kv_row_base[c.r];
+    const int n_tiles = (p.window + p.topk) / 16;
 
     if (tid < R / 2) {
-        float c, s;
-        rope_angle(pos, p.inv_freq[tid], c, s);
-        rope_cs[2 * tid] = c;
-        rope_cs[2 * tid + 1] = s;
+        float cs, sn;
+        rope_angle(c.pos, p.inv_freq[tid], cs, sn);
+        rope_cs[2 * tid] = cs;
+        rope_cs[2 * tid + 1] = sn;
     }
-    __syncthreads();  // rope_cs complete before any epilogue reads it
+    for (int i = tid; i < n_tiles; i += NT) vmask[i] = 0u;
+    for (int i = tid; i < p.topk; i += NT) sel[i] = p.idx[(int64_t)c.r * p.topk + i];
 
-    // Query fragments for this wave's 16 heads.
     const int h = 16 * wave + li;
-    typename M::Frag8 qf[NS];
+    typename Mma<CT>::Frag8 qf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-        qf[s] = (h < H) ? load_q_frag<QT, CT, D>(p.q, ((int64_t)r * H + h) * D, s, g) : zero_frag8<CT>();
-
-    // Softmax state (log2 units).  Split 0 starts from the sink: max = sink, sum = 1.
+        qf[s] = (h < H) ? load_q_frag<QT, CT, D>(p.q, ((int64_t)c.r * H + h) * D, s, g) : zero_frag8<CT>();
     float m = kNegInf, l = 0.f;
-    if (split == 0 && h < H) {
+    if (h < H) {
+        m = p.sink[h] * kLog2e;  // the sink is the initial state: max = sink, sum = 1
+        l = (g == 0) ? 1.f : 0.f;
+    }
+    f32x4 acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    RawPair raw[PPT];
+    auto load_tile = [&](int tile) {
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int pr = tid + k * NT;
+            if (pr < PAIRS) load_pair<D, KVT, SWT, DECODE>(p, c, sel, tile, pr / (D / 8), pr % (D / 8), raw[k]);
+        }
+    };
+    auto store_tile = [&](int tile, int b) {  // tile into buffer b
+        CT* Kt = tiles[b];
+        CT* Vt = tiles[b] + G::K_ELEMS;
+        uint32_t bits = 0;
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int pr = tid + k * NT;
+            if (pr < PAIRS) {
+                const int jb = pr / (D / 8), x8 = pr % (D / 8);
+                store_pair<D, CT, G::KS, G::VS, KVT, SWT>(raw[k], tile * 16 < p.window, Kt, Vt, jb, x8);
+                if (x8 == 0) bits |= raw[k].valid << (4 * jb);
+            }
+        }
+        if (bits) atomicOr(&vmask[tile], bits);
+    };
+
+    __syncthreads();  // rope table and vmask reset visible
+    if (n_tiles > 0) {
+        load_tile(0);
+        store_tile(0, 0);
+        if (n_tiles > 1) load_tile(1);
+    }
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+        const int b = t & 1;
+        const CT* Kt = tiles[b];
+        const CT* Vt = tiles[b] + G::K_ELEMS;
+        tile_compute<D, CT, G::KS, G::VS>(Kt, Vt, vmask[t], qf, p.scale_log2, g, li, m, l, acc);
+        if (t + 1 < n_tiles) {
+            store_tile(t + 1, b ^ 1);
+            if (t + 2 < n_tiles) load_tile(t + 2);
+        }
+        __syncthreads();
+    }
+
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    if (h >= H) return;
+    const float inv = 1.f / l;
+    const int64_t obase = ((int64_t)c.r * H + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+        const int d0 = 16 * dt + 4 * g;
+        emit4<D, R, OT>(p.out, obase + d0, d0, acc[dt], inv, rope_cs);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup per (query row, 16-head group); 4 waves take interleaved tiles.
+template <int H, int D, int R, class CT, int QT, int KVT, int SWT, int OT>
+__global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
+    constexpr int NHG = (H + 15) / 16;  // head groups per row
+    typedef TileGeom<CT, D> G;
+    constexpr int NS = D / 32, NDT = D / 16;
+    constexpr int PAIRS = 4 * (D / 8);
+    constexpr int PPL = (PAIRS + 63) / 64;          // pairs per lane (each wave gathers its own tile)
+    constexpr int ACC_STRIDE = D + 4;               // merge slice row stride (floats)
+    constexpr int TILE_BYTES = G::BYTES;
+    constexpr int MERGE_BYTES = 4 * 16 * ACC_STRIDE * 4;
+    constexpr int SMEM = (4 * TILE_BYTES > MERGE_BYTES) ? 4 * TILE_BYTES : MERGE_BYTES;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+    __shared__ float rope_cs[R];
+    __shared__ float ml[4][2][16];
+    __shared__ int32_t sel[kMaxTopk];  // this row's selected indices
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, li = lane & 15;
+
+    // Workgroups of one row share an XCD: ids are dispatched round-robin over 8 XCDs.
+    const int id = blockIdx.x;
+    const int blk = id / (8 * NHG), o = id % (8 * NHG);
+    const int hg = o / 8;
+    RowCtx c;
+    c.r = 8 * blk + (o % 8);
+    if (c.r >= p.rows) return;  // padding workgroup (before any barrier)
+    c.pos = p.pos[c.r];
+    c.nv = (c.pos + 1) / p.ratio;
+    c.kv_base = p.kv_row_base[c.r];
+    const int n_tiles = (p.window + p.topk) / 16;
+
+    if (tid < R / 2) {
+        float cs, sn;
+        rope_angle(c.pos, p.inv_freq[tid], cs, sn);
+        rope_cs[2 * tid] = cs;
+        rope_cs[2 * tid + 1] = sn;
+    }
+
+    const int h = 16 * hg + li;
+    typename Mma<CT>::Frag8 qf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        qf[s] = (h < H) ? load_q_frag<QT, CT, D>(p.q, ((int64_t)c.r * H + h) * D, s, g) : zero_frag8<CT>();
+    // Wave 0 carries the sink (max = sink, sum = 1); the others start empty.
+    float m = kNegInf, l = 0.f;
+    if (wave == 0 && h < H) {
         m = p.sink[h] * kLog2e;
         l = (g == 0) ? 1.f : 0.f;
     }
@@ -313,165 +565,94 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16)) void sparse_attn_kernel(const
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int64_t kv_base = p.kv_row_base[r];
-
-    for (int tile = t_begin; tile < t_end; ++tile) {
-        const bool swa_tile = tile * 16 < W;
-        // ---- gather 16 entries into Kt / Vt -------------------------------------
-        if (tid == 0) vmask = 0u;
-        __syncthreads();
-        for (int pr = tid; pr < PAIRS; pr += NT) {
-            const int jb = pr / (D / 8);
-            const int x8 = pr - jb * (D / 8);
-            Pack8<CT> v[4];
-            uint32_t vbits = 0;
+    CT* Kt = reinterpret_cast<CT*>(smem + wave * TILE_BYTES);
+    CT* Vt = Kt + G::K_ELEMS;
+    RawPair raw[PPL];
+    auto load_tile = [&](int tile) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = tile * 16 + 4 * jb + i;
-                bool valid;
-                if (swa_tile) {
-                    int64_t srow;
-                    if (DECODE) {
-                        const int64_t a = pos - ((pos - e) % W + W) % W;
-                        valid = a >= 0;
-                        srow = (int64_t)r * W + e;
-                    } else {
-                        const int64_t a = pos - (W - 1) + e;
-                        srow = a - p.swa_pos0;
-                        valid = a >= 0 && srow >= 0 && srow < p.swa_rows;
-                    }
-                    if (valid) RowLoad<SWT, D, CT>::run(p.swa, p.swa_scale, nullptr, srow, x8, v[i]);
-                    else pack_zero<CT>(v[i]);
-                } else {
-                    const int32_t id = p.idx[(int64_t)r * p.topk + (e - W)];
-                    valid = id >= 0 && (int64_t)id < nv;
-                    if (valid) RowLoad<KVT, D, CT>::run(p.kv, nullptr, p.kv_scale, kv_base + id, x8, v[i]);
-                    else pack_zero<CT>(v[i]);
-                }
-                vbits |= (valid ? 1u : 0u) << (4 * jb + i);
-                store_k<CT, D, KS>(Kt, 4 * jb + i, x8, v[i]);
+        for (int k = 0; k < PPL; ++k) {
+            const int pr = lane + 64 * k;
+            if (pr < PAIRS) load_pair<D, KVT, SWT, true>(p, c, sel, tile, pr / (D / 8), pr % (D / 8), raw[k]);
+        }
+    };
+
+    for (int i = tid; i < p.topk; i += 256) sel[i] = p.idx[(int64_t)c.r * p.topk + i];
+    __syncthreads();  // sel and rope_cs complete
+    int t = wave;
+    if (t < n_tiles) load_tile(t);
+    for (; t < n_tiles; t += 4) {
+        uint32_t vm = 0;
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+            const int pr = lane + 64 * k;
+            if (pr < PAIRS) {
+                const int jb = pr / (D / 8), x8 = pr % (D / 8);
+                store_pair<D, CT, G::KS, G::VS, KVT, SWT>(raw[k], t * 16 < p.window, Kt, Vt, jb, x8);
+                if (x8 == 0) vm |= raw[k].valid << (4 * jb);
             }
-            store_v4<CT, D, VS>(Vt, jb, x8, v);
-            if (x8 == 0) atomicOr(&vmask, vbits);
         }
-        __syncthreads();
-
-        // ---- scores S^T[j = 4g + rr][h] ------------------------------------------
-        f32x4 st = {0.f, 0.f, 0.f, 0.f};
+        // validity of the tile's 16 entries: OR of what the x8 == 0 lanes hold
 #pragma unroll
-        for (int s = 0; s < NS; ++s) st = M::k32(st, lds_frag8<CT>(Kt + li * KS + 32 * s + 8 * g), qf[s]);
-        const uint32_t vm = vmask;
-        float x[4];
-        float tmax = kNegInf;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            x[rr] = ((vm >> (4 * g + rr)) & 1u) ? st[rr] * p.scale_log2 : kNegInf;
-            tmax = fmaxf(tmax, x[rr]);
-        }
-        tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m, tmax);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = exp2f(m - m_use);
-        float pr4[4];
-        float psum = 0.f;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            pr4[rr] = exp2f(x[rr] - m_use);
-            psum += pr4[rr];
-        }
-        l = l * alpha + psum;
-        m = m_new;
-        const typename M::Frag4 pb = p_frag<CT>(pr4);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            acc[dt] *= alpha;
-            acc[dt] = M::k16(acc[dt], lds_frag4<CT>(Vt + g * VS + (16 * dt + li) * 4), pb);
-        }
-        __syncthreads();
+        for (int o = 32; o >= 1; o >>= 1) vm |= (uint32_t)__shfl_xor((int)vm, o, 64);
+        if (t + 4 < n_tiles) load_tile(t + 4);  // next tile's bytes in flight during this tile
+        wave_lds_fence();
+        tile_compute<D, CT, G::KS, G::VS>(Kt, Vt, vm, qf, p.scale_log2, g, li, m, l, acc);
+        wave_lds_fence();
     }
 
-    // ---- epilogue ---------------------------------------------------------------
+    // ---- merge the 4 waves' softmax states ------------------------------------
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
-    if (h >= H) return;
-    if (DECODE && p.splits > 1) {
-        const int64_t prow = ((int64_t)r * p.splits + split) * H + h;
-        float* wa = p.ws_acc + prow * D;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-            *reinterpret_cast<f32x4*>(wa + 16 * dt + 4 * g) = acc[dt];
-        if (g == 0) {
-            p.ws_ml[2 * prow] = m;
-            p.ws_ml[2 * prow + 1] = l;
-        }
-        return;
+    __syncthreads();  // every wave is done with its tile buffer; rope_cs is complete
+    if (g == 0) {
+        ml[wave][0][li] = m;
+        ml[wave][1][li] = l;
     }
-    const float inv = 1.f / l;
-    const int64_t obase = ((int64_t)r * H + h) * D;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-        const int d0 = 16 * dt + 4 * g;
-        float o0 = acc[dt][0] * inv, o1 = acc[dt][1] * inv, o2 = acc[dt][2] * inv, o3 = acc[dt][3] * inv;
-        if (d0 >= D - R) {
-            const int i0 = (d0 - (D - R)) / 2;
-            const float c0 = rope_cs[2 * i0], s0 = rope_cs[2 * i0 + 1];
-            const float c1 = rope_cs[2 * i0 + 2], s1 = rope_cs[2 * i0 + 3];
-            const float a0 = o0 * c0 + o1 * s0, a1 = o1 * c0 - o0 * s0;
-            const float a2 = o2 * c1 + o3 * s1, a3 = o3 * c1 - o2 * s1;
-            o0 = a0; o1 = a1; o2 = a2; o3 = a3;
-        }
-        store_out4<OT>(p.out, obase + d0, o0, o1, o2, o3);
-    }
-}
-
-// Combines the per-split partial states of one (row, head) and applies the
-// inverse rotation.  One workgroup of D/4 threads per (row, head).
-template <int D, int R, int OT>
-__global__ __launch_bounds__(D / 4) void attn_merge_kernel(const AttnParams p, int heads) {
-    const int rh = blockIdx.x;  // row * heads + head
-    const int r = rh / heads;
-    const int t = threadIdx.x;
-    const int d0 = 4 * t;
+    __syncthreads();
     float mx = kNegInf;
-    for (int s = 0; s < p.splits; ++s) mx = fmaxf(mx, p.ws_ml[2 * ((int64_t)(r * p.splits + s) * heads + (rh - r * heads))]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, ml[w][0][li]);
     const float mu = (mx == kNegInf) ? 0.f : mx;
     float L = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < p.splits; ++s) {
-        const int64_t prow = (int64_t)(r * p.splits + s) * heads + (rh - r * heads);
-        const float wgt = exp2f(p.ws_ml[2 * prow] - mu);
-        L += wgt * p.ws_ml[2 * prow + 1];
-        o += wgt * *reinterpret_cast<const f32x4*>(p.ws_acc + prow * D + d0);
-    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) L += ml[w][1][li] * exp2f(ml[w][0][li] - mu);
+    const float mine = exp2f(m - mu);
+    float* slice = reinterpret_cast<float*>(smem) + wave * 16 * ACC_STRIDE;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4*>(slice + li * ACC_STRIDE + 16 * dt + 4 * g) = acc[dt] * mine;
+    __syncthreads();
+    if (h >= H) return;
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    float o0 = o[0] * inv, o1 = o[1] * inv, o2 = o[2] * inv, o3 = o[3] * inv;
-    if (d0 >= D - R) {
-        const int i0 = (d0 - (D - R)) / 2;
-        float c0, s0, c1, s1;
-        rope_angle(p.pos[r], p.inv_freq[i0], c0, s0);
-        rope_angle(p.pos[r], p.inv_freq[i0 + 1], c1, s1);
-        const float a0 = o0 * c0 + o1 * s0, a1 = o1 * c0 - o0 * s0;
-        const float a2 = o2 * c1 + o3 * s1, a3 = o3 * c1 - o2 * s1;
-        o0 = a0; o1 = a1; o2 = a2; o3 = a3;
+    const float* base = reinterpret_cast<const float*>(smem);
+    const int64_t obase = ((int64_t)c.r * H + h) * D;
+    for (int dt = wave; dt < NDT; dt += 4) {
+        const int off = li * ACC_STRIDE + 16 * dt + 4 * g;
+        f32x4 sum = *reinterpret_cast<const f32x4*>(base + off);
+#pragma unroll
+        for (int w = 1; w < 4; ++w) sum += *reinterpret_cast<const f32x4*>(base + w * 16 * ACC_STRIDE + off);
+        const int d0 = 16 * dt + 4 * g;
+        emit4<D, R, OT>(p.out, obase + d0, d0, sum, inv, rope_cs);
     }
-    store_out4<OT>(p.out, (int64_t)rh * D + d0, o0, o1, o2, o3);
 }
 
 // ---------------------------------------------------------------------------
 template <int H, int D, int R, class CT, int QT, int KVT, int SWT, int OT>
 static hipError_t launch_attn(const AttnParams& p, bool decode, hipStream_t stream) {
-    constexpr int NT = 64 * ((H + 15) / 16);
-    if (decode) {
-        dim3 grid((unsigned)p.rows, (unsigned)p.splits);
-        hipLaunchKernelGGL((sparse_attn_kernel<H, D, R, CT, QT, KVT, SWT, OT, true>), grid, dim3(NT), 0, stream, p);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess || p.splits <= 1) return e;
-        hipLaunchKernelGGL((attn_merge_kernel<D, R, OT>), dim3((unsigned)(p.rows * H)), dim3(D / 4), 0, stream, p, H);
+    constexpr int NHG = (H + 15) / 16;
+    constexpr int NT = 64 * NHG;
+    if (decode && p.rows * NHG < 1024) {
+        const int blocks = ((p.rows + 7) / 8) * 8 * NHG;
+        hipLaunchKernelGGL((attn_decode_kernel<H, D, R, CT, QT, KVT, SWT, OT>), dim3((unsigned)blocks), dim3(256), 0,
+                           stream, p);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((sparse_attn_kernel<H, D, R, CT, QT, KVT, SWT, OT, false>), dim3((unsigned)p.rows), dim3(NT), 0,
-                       stream, p);
+    if (decode)
+        hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, true>), dim3((unsigned)p.rows), dim3(NT), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, false>), dim3((unsigned)p.rows), dim3(NT), 0,
+                           stream, p);
     return hipGetLastError();
 }
 

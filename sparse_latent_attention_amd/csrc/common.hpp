@@ -59,6 +59,17 @@ __device__ __forceinline__ f32x2 fp4x2_to_f32(uint32_t w) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
 }
 
+// Order-preserving 32-bit key of a score: NaN ranks as -inf and -0 as +0, and
+// key(a) < key(b) exactly when a < b otherwise.  Its top 12 bits are the bin
+// of the top-k histogram.
+__device__ __forceinline__ uint32_t order_key(float s) {
+    uint32_t u = __float_as_uint(s);
+    if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;  // NaN -> -inf
+    if (u == 0x80000000u) u = 0u;                           // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+constexpr int kKeyBins = 4096;  // bins of the top 12 key bits
+
 // Wave-level lane exchange (ds_bpermute based).
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 

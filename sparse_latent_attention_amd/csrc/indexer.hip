@@ -24,6 +24,11 @@ namespace csa2 {
 
 namespace {
 
+// ReLU as an integer max on the float's bits: every negative float and -0 has
+// a negative signed pattern and becomes +0; +0, positive values and +inf are
+// unchanged.  One instruction, where fmaxf would also canonicalise NaNs.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Plane row of column c and whether it is valid.
 template <bool REINDEX>
 __device__ __forceinline__ bool column_row(const IndexParams& p, int r, int64_t c, int64_t nv, int64_t base,
@@ -103,8 +108,10 @@ struct IdxOps<CSA2_FP8_E4M3, 128> {
 
 }  // namespace
 
-template <int KT, int HI, int DI, bool REINDEX>
+template <int KT, int HI, int DI, bool REINDEX, bool HIST>
 __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p) {
+    // Per-workgroup histogram of the score keys' top 12 bits (one row per workgroup).
+    __shared__ uint32_t hist[HIST ? kKeyBins : 1];
     typedef IdxOps<KT, DI> Ops;
     typedef typename Ops::Frag Frag;
     constexpr int HT = (HI + 15) / 16;  // 16-head MFMA tiles
@@ -139,6 +146,11 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p)
         }
     }
 
+    if (HIST) {
+        for (int b = threadIdx.x; b < kKeyBins; b += 256) hist[b] = 0u;
+        __syncthreads();
+    }
+
     for (int64_t cb = c_begin + 64 * wave; cb < c_end; cb += 256) {
         const int64_t c_out = cb + lane;
         if (cb >= c_live) {  // nothing visible in these 64 columns
@@ -161,7 +173,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p)
 #pragma unroll
                 for (int s = 0; s < S; ++s) acc = Ops::mma(acc, qa[t][s], kb[s]);
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) acc_sum += wr[t][rr] * fmaxf(acc[rr], 0.f);
+                for (int rr = 0; rr < 4; ++rr) acc_sum += wr[t][rr] * relu_bits(acc[rr]);
             }
             v[u] = acc_sum;
         }
@@ -180,9 +192,21 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p)
             const bool valid = column_row<REINDEX>(p, r, c_out, nv, base, prow);
             float sc = p.scale;
             if (KT == CSA2_FP8_E4M3 && valid) sc *= p.k_scale[prow];
-            srow[c_out] = valid ? sc * kk : kNegInf;
+            const float score = valid ? sc * kk : kNegInf;
+            srow[c_out] = score;
+            if (HIST && valid) atomicAdd(&hist[order_key(score) >> 20], 1u);
         }
     }
+    if (HIST) {
+        __syncthreads();
+        uint32_t* g = p.key_hist + (int64_t)r * kKeyBins;
+        for (int b = threadIdx.x; b < kKeyBins; b += 256)
+            if (hist[b]) atomicAdd(&g[b], hist[b]);
+    }
+}
+
+__global__ __launch_bounds__(256) void key_hist_zero_kernel(uint32_t* h, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) h[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -190,7 +214,14 @@ template <int KT, int HI, int DI, bool REINDEX>
 static hipError_t launch_one(const IndexParams& p, int rows, hipStream_t stream) {
     const int64_t chunks = (p.width + p.cols_per_wg - 1) / p.cols_per_wg;
     dim3 grid((unsigned)chunks, (unsigned)rows);
-    hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, REINDEX>), grid, dim3(256), 0, stream, p);
+    if (p.key_hist == nullptr) {
+        hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, REINDEX, false>), grid, dim3(256), 0, stream, p);
+        return hipGetLastError();
+    }
+    const int64_t nh = (int64_t)rows * kKeyBins;
+    hipLaunchKernelGGL(key_hist_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)),
+                       dim3(256), 0, stream, p.key_hist, nh);
+    hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, REINDEX, true>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ struct IndexParams {
     const int64_t* pos;
     const int32_t* cand;
     float* scores;
+    uint32_t* key_hist;  // optional [rows, 4096]
     int64_t width;
     int64_t cols_per_wg;
     int32_t n_blocks;
@@ -34,6 +35,7 @@ struct TopkParams {
     const int64_t* pos;
     const int32_t* cand;
     int32_t* out;
+    const uint32_t* key_hist;  // optional [rows, 4096] from the indexer
     int64_t width;
     int32_t k;
     int32_t ratio;
@@ -41,7 +43,9 @@ struct TopkParams {
     int32_t block_rows;
 };
 
-hipError_t launch_topk_select(const TopkParams& p, int rows, hipStream_t stream);
+// Bytes of workspace the launch plan for (rows, width) needs (0: one workgroup per row).
+size_t topk_workspace_bytes(int rows, int64_t width);
+hipError_t launch_topk_select(const TopkParams& p, int rows, void* workspace, hipStream_t stream);
 
 struct AttnParams {
     const void* q;
@@ -55,16 +59,12 @@ struct AttnParams {
     const float* sink;
     const double* inv_freq;
     void* out;
-    float* ws_acc;  // decode partials: [rows, splits, heads, dim]
-    float* ws_ml;   // decode partials: [rows, splits, heads, 2] (max in log2 units, sum)
     int64_t swa_rows;
     int64_t swa_pos0;
     int32_t rows;
     int32_t topk;
     int32_t ratio;
     int32_t window;
-    int32_t splits;
-    int32_t tiles_per_split;
     float scale_log2;  // softmax_scale * log2(e)
 };
 

@@ -1,22 +1,33 @@
-// Per-row top-k of indexer scores for gfx950 (one 1024-thread workgroup per row).
+// Per-row top-k of indexer scores for gfx950.
 //
 // Contract ("DeepSeek-V4.1-Flash 架构解剖", fig. 2d REUSE and special module
 // "indexer"): the k valid columns with the largest scores, ties to the lower
 // column, NaN ranked as -inf, -0 equal to +0; written in increasing column
 // order as plane rows, then -1 padding.
 //
-// Method: exact radix select on a 32-bit order-preserving key, then one
-// ordered compaction pass.
-//   key(s) = bits(s) | 0x80000000 for s >= +0, ~bits(s) for s < 0, after
-//   mapping NaN to -inf and -0 to +0, so key order == score order.
-//   Passes 1-3 histogram bits [31:20], [19:8] and [7:0] of the keys that share
-//   the prefix found so far (4096/4096/256 LDS bins) and fix, digit by digit,
-//   the k-th largest key T and the count n_gt of keys above it.
-//   The compaction walks the row in column order, 1024 columns at a time; a
-//   column is taken if key > T, or key == T and fewer than k - n_gt equal keys
-//   precede it.  Its output slot is (#greater before it) + min(#equal before
-//   it, k - n_gt), computed with wave ballots and one barrier per chunk, so the
-//   output is already in column order with no sort.
+// Exact select.  Scores map to an order-preserving 32-bit key
+//   key(s) = bits(s) | 0x80000000 for s >= +0, ~bits(s) for s < 0,
+// after NaN -> -inf and -0 -> +0, so key order is score order.  Three
+// histogram passes over bits [31:20], [19:8] and [7:0] (LDS bins) fix the k-th
+// largest key T and the number n_gt of keys above it.  A final pass walks the
+// positions in column order, 1024 at a time; a position is taken if key > T,
+// or key == T and fewer than k - n_gt equal keys precede it, and lands in slot
+// (#greater before it) + min(#equal before it, k - n_gt).  Slots are computed
+// with wave ballots and one barrier per 1024 positions, and come out in column
+// order, so nothing is sorted.
+//
+// Two ways to feed that select:
+//   * narrow rows or many rows: one 1024-thread workgroup per row reads the
+//     score row directly (4 passes over a row that stays in L2);
+//   * wide rows (the 1M-column decode): the row is cut into chunks handled by
+//     separate workgroups.  (1) each chunk adds its 12-bit histogram into a
+//     per-row global histogram; (2) one workgroup per row finds the bin b1 of
+//     the k-th largest key; (3) each chunk compacts, in column order, the
+//     (key, column) pairs of its valid keys whose bin is >= b1 -- every key
+//     >= T is among them -- into its own slot range; (4) one workgroup per row
+//     runs the exact select over that short, still column-ordered list.  A
+//     chunk with more than kCap such keys (heavy ties) makes step 4 fall back
+//     to reading the full row, so the result is exact in every case.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -26,55 +37,67 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kCap = 1024;      // candidates kept per chunk
+constexpr int kMaxSegs = 256;   // chunks per row in the wide-row path
 
-__device__ __forceinline__ uint32_t order_key(float s) {
-    uint32_t u = __float_as_uint(s);
-    if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;  // NaN -> -inf
-    if (u == 0x80000000u) u = 0u;                           // -0 -> +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Validity and plane row of column c.
-__device__ __forceinline__ bool col_valid(const TopkParams& p, int r, int c, int64_t nv, int32_t& row) {
-    if (p.n_blocks == 0) {
-        row = c;
-        return c < nv;
-    }
-    const int i = c / p.block_rows;
-    const int t = c - i * p.block_rows;
+// Validity of column c of row r.
+__device__ __forceinline__ bool col_valid(const TopkParams& p, int r, int64_t c, int64_t nv) {
+    if (p.n_blocks == 0) return c < nv;
+    const int64_t i = c / p.block_rows;
     const int32_t b = p.cand[(int64_t)r * p.n_blocks + i];
     if (b < 0) return false;
-    const int64_t jr = (int64_t)b * p.block_rows + t;
-    row = (int32_t)jr;
-    return jr < nv;
+    return (int64_t)b * p.block_rows + (c - i * p.block_rows) < nv;
 }
 
-// Block-wide exclusive suffix sum: returns sum of v over threads with a larger index.
-__device__ __forceinline__ uint32_t block_suffix_excl(uint32_t v, uint32_t* wave_tot) {
+// Plane row written to the output for column c (valid columns only).
+__device__ __forceinline__ int32_t col_to_row(const TopkParams& p, int r, int32_t c) {
+    if (p.n_blocks == 0) return c;
+    const int32_t i = c / p.block_rows;
+    return p.cand[(int64_t)r * p.n_blocks + i] * p.block_rows + (c - i * p.block_rows);
+}
+
+struct Lds {
+    uint32_t hist[4096];
+    uint32_t wave_tot[kWaves];
+    uint32_t sel[2];
+    uint32_t flags_cnt[2][2 * kWaves];
+    uint32_t seg_start[kMaxSegs + 1];
+};
+
+// Block-wide exclusive suffix sum (sum of v over threads with a larger index).
+__device__ __forceinline__ uint32_t block_suffix_excl(uint32_t v, Lds& s) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // inclusive suffix scan within the wave (lane l gets sum over lanes >= l)
     uint32_t x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_down(x, o, 64);
+        const uint32_t y = __shfl_down(x, o, 64);
         if (lane + o < 64) x += y;
     }
-    if (lane == 0) wave_tot[wave] = x;
+    if (lane == 0) s.wave_tot[wave] = x;
     __syncthreads();
     uint32_t later = 0;
-    for (int w = wave + 1; w < kWaves; ++w) later += wave_tot[w];
+    for (int w = wave + 1; w < kWaves; ++w) later += s.wave_tot[w];
     __syncthreads();
     return later + x - v;
 }
 
-// Finds the bin b (scanning bins from the top) where the running count first
-// reaches `need`; each thread owns bins [nb_per*t, nb_per*t + nb_per).
-// Returns through LDS: sel[0] = bin, sel[1] = count of keys in higher bins.
-__device__ __forceinline__ void find_bin(const uint32_t* hist, int nbins, uint32_t need, uint32_t* wave_tot,
-                                         uint32_t* sel) {
-    const int per = nbins / kThreads;  // 4 or (for 256 bins) 0 -> handled below
+// Sum of all bins (4096) of s.hist, returned to every thread.
+__device__ __forceinline__ uint32_t hist_total(Lds& s) {
     const int t = threadIdx.x;
-    uint32_t local = 0;
+    const uint32_t local = s.hist[4 * t] + s.hist[4 * t + 1] + s.hist[4 * t + 2] + s.hist[4 * t + 3];
+    const uint32_t later = block_suffix_excl(local, s);
+    if (t == 0) s.sel[0] = later + local;
+    __syncthreads();
+    const uint32_t total = s.sel[0];
+    __syncthreads();
+    return total;
+}
+
+// Scanning bins from the top, the bin where the running count first reaches
+// `need` (>= 1, <= total), and the count in the bins above it.
+__device__ __forceinline__ void find_bin(Lds& s, int nbins, uint32_t need, uint32_t& bin, uint32_t& above_out) {
+    const int per = nbins / kThreads;
+    const int t = threadIdx.x;
     int b0 = 0, b1 = 0;
     if (per > 0) {
         b0 = per * t;
@@ -83,128 +106,133 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int nbins, uint32
         b0 = t;
         b1 = t + 1;
     }
-    for (int b = b0; b < b1; ++b) local += hist[b];
-    uint32_t above = block_suffix_excl(local, wave_tot);
+    uint32_t local = 0;
+    for (int b = b0; b < b1; ++b) local += s.hist[b];
+    uint32_t above = block_suffix_excl(local, s);
     for (int b = b1 - 1; b >= b0; --b) {
-        const uint32_t h = hist[b];
+        const uint32_t h = s.hist[b];
         if (above < need && above + h >= need) {
-            sel[0] = (uint32_t)b;
-            sel[1] = above;
+            s.sel[0] = (uint32_t)b;
+            s.sel[1] = above;
         }
         above += h;
     }
     __syncthreads();
+    bin = s.sel[0];
+    above_out = s.sel[1];
+    __syncthreads();
 }
 
-}  // namespace
+// Positions of the full score row: column i, validity from the row geometry.
+struct RowSrc {
+    const TopkParams* p;
+    const float* srow;
+    int64_t nv;
+    int r;
+    int n;
+    __device__ __forceinline__ bool get(int i, uint32_t& key, int32_t& col) const {
+        col = i;
+        if (!col_valid(*p, r, i, nv)) return false;
+        key = order_key(srow[i]);
+        return true;
+    }
+};
 
-__global__ __launch_bounds__(kThreads) void topk_select_kernel(const TopkParams p) {
-    __shared__ uint32_t hist[4096];
-    __shared__ uint32_t wave_tot[kWaves];
-    __shared__ uint32_t sel[2];
-    __shared__ uint32_t flags_cnt[2][2 * kWaves];
+// Positions of the filtered candidate list: segment-major, column order within.
+struct CandSrc {
+    const uint32_t* keys;      // [nseg][kCap] of this row
+    const int32_t* cols;       // [nseg][kCap]
+    const uint32_t* seg_start; // LDS prefix of the segment counts, [nseg + 1]
+    int nseg;
+    int n;
+    __device__ __forceinline__ bool get(int i, uint32_t& key, int32_t& col) const {
+        int lo = 0, hi = nseg;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if ((int)seg_start[mid] <= i) lo = mid;
+            else hi = mid;
+        }
+        const int j = i - (int)seg_start[lo];
+        key = keys[lo * kCap + j];
+        col = cols[lo * kCap + j];
+        return true;
+    }
+};
 
-    const int r = blockIdx.x;
+template <class Src>
+__device__ __forceinline__ void select_core(const Src& src, const TopkParams& p, int r, Lds& s) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int64_t nv = (p.pos[r] + 1) / p.ratio;
-    const float* srow = p.scores + (int64_t)r * p.width;
     int32_t* orow = p.out + (int64_t)r * p.k;
-    const int ncols = (p.n_blocks == 0) ? (int)(nv < p.width ? nv : p.width) : (int)p.width;
     const uint32_t k = (uint32_t)p.k;
+    const int n = src.n;
 
-    // ---- pass 1: top 12 bits -------------------------------------------------
-    for (int b = tid; b < 4096; b += kThreads) hist[b] = 0;
+    // pass 1: bits [31:20]
+    for (int b = tid; b < 4096; b += kThreads) s.hist[b] = 0;
     __syncthreads();
-    for (int c = tid; c < ncols; c += kThreads) {
-        int32_t row;
-        if (col_valid(p, r, c, nv, row)) atomicAdd(&hist[order_key(srow[c]) >> 20], 1u);
+    for (int i = tid; i < n; i += kThreads) {
+        uint32_t key;
+        int32_t col;
+        if (src.get(i, key, col)) atomicAdd(&s.hist[key >> 20], 1u);
     }
     __syncthreads();
-    // total valid columns
-    {
-        uint32_t local = hist[4 * tid] + hist[4 * tid + 1] + hist[4 * tid + 2] + hist[4 * tid + 3];
-        uint32_t later = block_suffix_excl(local, wave_tot);
-        if (tid == 0) sel[0] = later + local;
-        __syncthreads();
-    }
-    const uint32_t total = sel[0];
-    __syncthreads();
-
-    bool select_all = total <= k;
+    const uint32_t total = hist_total(s);
+    const bool select_all = total <= k;
     uint32_t T = 0, n_gt = 0;
     if (!select_all) {
-        find_bin(hist, 4096, k, wave_tot, sel);
-        const uint32_t b1 = sel[0];
-        const uint32_t above1 = sel[1];
+        uint32_t b1, above1, b2, above2, b3, above3;
+        find_bin(s, 4096, k, b1, above1);
+        // pass 2: bits [19:8] of keys in bin b1
+        for (int b = tid; b < 4096; b += kThreads) s.hist[b] = 0;
         __syncthreads();
-        // ---- pass 2: bits [19:8] among keys with top bits b1 ----------------------
-        for (int b = tid; b < 4096; b += kThreads) hist[b] = 0;
-        __syncthreads();
-        for (int c = tid; c < ncols; c += kThreads) {
-            int32_t row;
-            if (col_valid(p, r, c, nv, row)) {
-                const uint32_t key = order_key(srow[c]);
-                if ((key >> 20) == b1) atomicAdd(&hist[(key >> 8) & 0xfffu], 1u);
-            }
+        for (int i = tid; i < n; i += kThreads) {
+            uint32_t key;
+            int32_t col;
+            if (src.get(i, key, col) && (key >> 20) == b1) atomicAdd(&s.hist[(key >> 8) & 0xfffu], 1u);
         }
         __syncthreads();
-        find_bin(hist, 4096, k - above1, wave_tot, sel);
-        const uint32_t b2 = sel[0];
-        const uint32_t above2 = sel[1];
-        __syncthreads();
-        // ---- pass 3: bits [7:0] among keys with prefix (b1, b2) -------------------
+        find_bin(s, 4096, k - above1, b2, above2);
+        // pass 3: bits [7:0] of keys with prefix (b1, b2)
         const uint32_t pre = (b1 << 12) | b2;
-        for (int b = tid; b < 256; b += kThreads) hist[b] = 0;
+        for (int b = tid; b < 256; b += kThreads) s.hist[b] = 0;
         __syncthreads();
-        for (int c = tid; c < ncols; c += kThreads) {
-            int32_t row;
-            if (col_valid(p, r, c, nv, row)) {
-                const uint32_t key = order_key(srow[c]);
-                if ((key >> 8) == pre) atomicAdd(&hist[key & 0xffu], 1u);
-            }
+        for (int i = tid; i < n; i += kThreads) {
+            uint32_t key;
+            int32_t col;
+            if (src.get(i, key, col) && (key >> 8) == pre) atomicAdd(&s.hist[key & 0xffu], 1u);
         }
         __syncthreads();
-        find_bin(hist, 256, k - above1 - above2, wave_tot, sel);
-        const uint32_t b3 = sel[0];
-        const uint32_t above3 = sel[1];
-        __syncthreads();
+        find_bin(s, 256, k - above1 - above2, b3, above3);
         T = (pre << 8) | b3;
         n_gt = above1 + above2 + above3;
     }
     const uint32_t need = select_all ? 0u : k - n_gt;  // equal keys to take, lowest columns first
     const uint32_t goal = select_all ? total : k;
 
-    // ---- ordered compaction ---------------------------------------------------
+    // ordered compaction
     uint32_t gt_base = 0, eq_base = 0;
     int buf = 0;
-    for (int cs = 0; cs < ncols; cs += kThreads) {
-        const int c = cs + tid;
-        int32_t row = -1;
+    for (int cs = 0; cs < n; cs += kThreads) {
+        const int i = cs + tid;
+        uint32_t key = 0;
+        int32_t col = -1;
         bool gt = false, eq = false;
-        if (c < ncols && col_valid(p, r, c, nv, row)) {
-            if (select_all) {
-                gt = true;
-            } else {
-                const uint32_t key = order_key(srow[c]);
-                gt = key > T;
-                eq = key == T;
-            }
+        if (i < n && src.get(i, key, col)) {
+            gt = select_all || key > T;
+            eq = !select_all && key == T;
         }
         const uint64_t mgt = __ballot(gt);
         const uint64_t meq = __ballot(eq);
-        const uint32_t lo_mask_lo = (uint32_t)(mgt), lo_mask_hi = (uint32_t)(mgt >> 32);
-        const uint32_t gt_lane = __builtin_amdgcn_mbcnt_hi(lo_mask_hi, __builtin_amdgcn_mbcnt_lo(lo_mask_lo, 0u));
-        const uint32_t eq_lane =
-            __builtin_amdgcn_mbcnt_hi((uint32_t)(meq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)meq, 0u));
+        const uint32_t gt_lane = __builtin_amdgcn_mbcnt_hi((uint32_t)(mgt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mgt, 0u));
+        const uint32_t eq_lane = __builtin_amdgcn_mbcnt_hi((uint32_t)(meq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)meq, 0u));
         if (lane == 0) {
-            flags_cnt[buf][wave] = (uint32_t)__builtin_popcountll(mgt);
-            flags_cnt[buf][kWaves + wave] = (uint32_t)__builtin_popcountll(meq);
+            s.flags_cnt[buf][wave] = (uint32_t)__builtin_popcountll(mgt);
+            s.flags_cnt[buf][kWaves + wave] = (uint32_t)__builtin_popcountll(meq);
         }
         __syncthreads();
         uint32_t gt_before = gt_base, eq_before = eq_base, gt_all = 0, eq_all = 0;
         for (int w = 0; w < kWaves; ++w) {
-            const uint32_t a = flags_cnt[buf][w], b = flags_cnt[buf][kWaves + w];
+            const uint32_t a = s.flags_cnt[buf][w], b = s.flags_cnt[buf][kWaves + w];
             if (w < wave) {
                 gt_before += a;
                 eq_before += b;
@@ -214,21 +242,234 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const TopkParams 
         }
         gt_before += gt_lane;
         eq_before += eq_lane;
-        if (gt || (eq && eq_before < need)) {
-            const uint32_t slot = gt_before + (eq_before < need ? eq_before : need);
-            orow[slot] = row;
-        }
+        if (gt || (eq && eq_before < need)) orow[gt_before + (eq_before < need ? eq_before : need)] = col_to_row(p, r, col);
         gt_base += gt_all;
         eq_base += eq_all;
         buf ^= 1;
-        const uint32_t done = gt_base + (eq_base < need ? eq_base : need);
-        if (done >= goal) break;
+        if (gt_base + (eq_base < need ? eq_base : need) >= goal) break;
     }
     for (int i = (int)goal + tid; i < p.k; i += kThreads) orow[i] = -1;
 }
 
-hipError_t launch_topk_select(const TopkParams& p, int rows, hipStream_t stream) {
-    hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+__device__ __forceinline__ RowSrc row_src(const TopkParams& p, int r) {
+    RowSrc src;
+    src.p = &p;
+    src.r = r;
+    src.nv = (p.pos[r] + 1) / p.ratio;
+    src.srow = p.scores + (int64_t)r * p.width;
+    src.n = (p.n_blocks == 0) ? (int)(src.nv < p.width ? src.nv : p.width) : (int)p.width;
+    return src;
+}
+
+}  // namespace
+
+// One workgroup per row over the full score row.
+__global__ __launch_bounds__(kThreads) void topk_select_kernel(const TopkParams p) {
+    __shared__ Lds s;
+    const int r = blockIdx.x;
+    select_core(row_src(p, r), p, r, s);
+}
+
+// ---- wide-row path ----------------------------------------------------------
+
+__global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* buf, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) buf[i] = 0u;
+}
+
+// grid (nseg, rows): 12-bit histogram of one chunk, added into hist[r][4096].
+__global__ __launch_bounds__(kThreads) void topk_hist_kernel(const TopkParams p, uint32_t* hist, int chunk) {
+    __shared__ uint32_t h[4096];
+    const int r = blockIdx.y;
+    const int tid = threadIdx.x;
+    const RowSrc src = row_src(p, r);
+    for (int b = tid; b < 4096; b += kThreads) h[b] = 0;
+    __syncthreads();
+    const int c0 = blockIdx.x * chunk;
+    const int c1 = (c0 + chunk < src.n) ? c0 + chunk : src.n;
+    for (int i = c0 + tid; i < c1; i += kThreads) {
+        uint32_t key;
+        int32_t col;
+        if (src.get(i, key, col)) atomicAdd(&h[key >> 20], 1u);
+    }
+    __syncthreads();
+    uint32_t* g = hist + (int64_t)r * 4096;
+    for (int b = tid; b < 4096; b += kThreads)
+        if (h[b]) atomicAdd(&g[b], h[b]);
+}
+
+// grid rows: bin of the k-th largest key (0 when every valid key is selected).
+__global__ __launch_bounds__(kThreads) void topk_threshold_kernel(const TopkParams p, const uint32_t* hist,
+                                                                  uint32_t* b1_out) {
+    __shared__ Lds s;
+    const int r = blockIdx.x;
+    for (int b = threadIdx.x; b < 4096; b += kThreads) s.hist[b] = hist[(int64_t)r * 4096 + b];
+    __syncthreads();
+    const uint32_t total = hist_total(s);
+    uint32_t b1 = 0, above = 0;
+    if (total > (uint32_t)p.k) find_bin(s, 4096, (uint32_t)p.k, b1, above);
+    if (threadIdx.x == 0) b1_out[r] = b1;
+}
+
+// grid (nseg, rows): ordered compaction of the chunk's keys with bin >= b1.
+// Each sweep covers kSweep columns: wave w owns a contiguous 1024-column slice,
+// lane l holds columns base + 64j + l (j < 16) in registers, so one barrier per
+// sweep (to add up the waves' counts) is the only synchronisation.
+constexpr int kPerLane = 16;
+constexpr int kSweep = kThreads * kPerLane;
+
+__global__ __launch_bounds__(kThreads) void topk_filter_kernel(const TopkParams p, const uint32_t* b1_in,
+                                                               uint32_t* cand_keys, int32_t* cand_cols,
+                                                               uint32_t* seg_count, int chunk, int nseg) {
+    __shared__ uint32_t cnt[2][kWaves];
+    const int r = blockIdx.y, seg = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const RowSrc src = row_src(p, r);
+    const uint32_t b1 = b1_in[r];
+    const int64_t base = ((int64_t)r * nseg + seg) * kCap;
+    const int c0 = seg * chunk;
+    const int c1 = (c0 + chunk < src.n) ? c0 + chunk : src.n;
+    uint32_t n_out = 0;
+    int buf = 0;
+    for (int cs = c0; cs < c1; cs += kSweep) {
+        const int wbase = cs + wave * (kSweep / kWaves);
+        // All loads first (in flight together), then the keys and ballots.
+        float vals[kPerLane];
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) {
+            const int i = wbase + 64 * j + lane;
+            vals[j] = (i < c1) ? src.srow[i] : 0.f;
+        }
+        uint32_t keys[kPerLane];
+        uint64_t masks[kPerLane];
+        uint32_t mine = 0;
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) {
+            const int i = wbase + 64 * j + lane;
+            keys[j] = order_key(vals[j]);
+            const bool take = i < c1 && col_valid(p, r, i, src.nv) && (keys[j] >> 20) >= b1;
+            masks[j] = __ballot(take);
+            mine += (uint32_t)__builtin_popcountll(masks[j]);
+        }
+        if (lane == 0) cnt[buf][wave] = mine;
+        __syncthreads();
+        uint32_t off = n_out, all = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            if (w < wave) off += cnt[buf][w];
+            all += cnt[buf][w];
+        }
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) {
+            const uint64_t m = masks[j];
+            if ((m >> lane) & 1ull) {
+                const uint32_t at = off + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                if (at < (uint32_t)kCap) {
+                    cand_keys[base + at] = keys[j];
+                    cand_cols[base + at] = wbase + 64 * j + lane;
+                }
+            }
+            off += (uint32_t)__builtin_popcountll(m);
+        }
+        n_out += all;
+        buf ^= 1;
+    }
+    if (tid == 0) seg_count[(int64_t)r * nseg + seg] = n_out;
+}
+
+// grid rows: exact select over the candidates (or the full row after an overflow).
+__global__ __launch_bounds__(kThreads) void topk_final_kernel(const TopkParams p, const uint32_t* cand_keys,
+                                                              const int32_t* cand_cols, const uint32_t* seg_count,
+                                                              int nseg) {
+    __shared__ Lds s;
+    const int r = blockIdx.x;
+    if (threadIdx.x == 0) {
+        uint32_t acc = 0, over = 0;
+        for (int g = 0; g < nseg; ++g) {
+            const uint32_t c = seg_count[(int64_t)r * nseg + g];
+            s.seg_start[g] = acc;
+            acc += c;
+            over |= c > (uint32_t)kCap;
+        }
+        s.seg_start[nseg] = acc;
+        s.sel[0] = over;
+    }
+    __syncthreads();
+    const bool overflow = s.sel[0] != 0;
+    const int n = (int)s.seg_start[nseg];
+    __syncthreads();
+    if (overflow) {
+        select_core(row_src(p, r), p, r, s);
+        return;
+    }
+    CandSrc src;
+    src.keys = cand_keys + (int64_t)r * nseg * kCap;
+    src.cols = cand_cols + (int64_t)r * nseg * kCap;
+    src.seg_start = s.seg_start;
+    src.nseg = nseg;
+    src.n = n;
+    select_core(src, p, r, s);
+}
+
+// ---------------------------------------------------------------------------
+// Launch plan for the wide-row path; nseg == 0 means one workgroup per row.
+void topk_plan(int rows, int64_t width, int& chunk, int& nseg) {
+    chunk = 0;
+    nseg = 0;
+    if (rows <= 0 || rows >= 1024 || width < 8192) return;
+    int64_t target = 4096 / rows;
+    if (target < 1) target = 1;
+    int64_t c = (width + target - 1) / target;
+    if (c < 4096) c = 4096;
+    const int64_t min_c = (width + kMaxSegs - 1) / kMaxSegs;
+    if (c < min_c) c = min_c;
+    c = (c + 1023) / 1024 * 1024;
+    chunk = (int)c;
+    nseg = (int)((width + c - 1) / c);
+    if (nseg < 2) chunk = nseg = 0;
+}
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t topk_workspace_bytes(int rows, int64_t width) {
+    int chunk, nseg;
+    topk_plan(rows, width, chunk, nseg);
+    if (nseg == 0) return 0;
+    return align256((size_t)rows * 4096 * 4) + align256((size_t)rows * 4) + align256((size_t)rows * nseg * 4) +
+           2 * align256((size_t)rows * nseg * kCap * 4);
+}
+
+hipError_t launch_topk_select(const TopkParams& p, int rows, void* ws, hipStream_t stream) {
+    int chunk, nseg;
+    topk_plan(rows, p.width, chunk, nseg);
+    if (nseg == 0) {
+        hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+        return hipGetLastError();
+    }
+    char* w = reinterpret_cast<char*>(ws);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(w);
+    w += align256((size_t)rows * 4096 * 4);
+    uint32_t* b1 = reinterpret_cast<uint32_t*>(w);
+    w += align256((size_t)rows * 4);
+    uint32_t* seg_count = reinterpret_cast<uint32_t*>(w);
+    w += align256((size_t)rows * nseg * 4);
+    uint32_t* keys = reinterpret_cast<uint32_t*>(w);
+    w += align256((size_t)rows * nseg * kCap * 4);
+    int32_t* cols = reinterpret_cast<int32_t*>(w);
+
+    const uint32_t* h = p.key_hist;
+    if (h == nullptr) {  // no histogram from the indexer: build it here
+        const int64_t nh = (int64_t)rows * 4096;
+        hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)),
+                           dim3(256), 0, stream, hist, nh);
+        hipLaunchKernelGGL(topk_hist_kernel, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0, stream, p, hist,
+                           chunk);
+        h = hist;
+    }
+    hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, h, b1);
+    hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0, stream, p, b1, keys,
+                       cols, seg_count, chunk, nseg);
+    hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, keys, cols, seg_count,
+                       nseg);
     return hipGetLastError();
 }
 

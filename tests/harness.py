@@ -75,26 +75,41 @@ def index_scale(cfg):
     return 1.0 / (math.sqrt(cfg.idx_dim) * math.sqrt(cfg.idx_heads))
 
 
-def gpu_scores(cfg, x):
+def gpu_scores(cfg, x, key_hist=None):
     import sparse_latent_attention_amd as csa2
     rows = x["pos"].shape[0]
     scores = torch.empty(rows, cfg.width, dtype=torch.float32, device=x["pos"].device)
     kI = x["kI"].reshape(-1, cfg.idx_dim)
     ks = None if x["kI_scale"] is None else x["kI_scale"].reshape(-1)
     csa2.indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, index_scale(cfg), scores,
-                       k_scale=ks, cand=x.get("cand"), block_rows=cfg.block_rows, fp8=cfg.idx_dtype == "fp8")
+                       k_scale=ks, cand=x.get("cand"), block_rows=cfg.block_rows, fp8=cfg.idx_dtype == "fp8",
+                       key_hist=key_hist)
     return scores
 
 
-def gpu_topk(cfg, x, scores, k=None):
+def gpu_topk(cfg, x, scores, k=None, key_hist=None):
     import sparse_latent_attention_amd as csa2
     k = cfg.topk if k is None else k
     out = torch.empty(scores.shape[0], k, dtype=torch.int32, device=scores.device)
-    csa2.topk_select(scores, x["pos"], cfg.ratio, out, cand=x.get("cand"), block_rows=cfg.block_rows)
+    csa2.topk_select(scores, x["pos"], cfg.ratio, out, cand=x.get("cand"), block_rows=cfg.block_rows,
+                     key_hist=key_hist)
     return out
 
 
-def gpu_attention(cfg, x, idx, layer=0, splits=0, out=None):
+def host_key_hist(scores_np, valid):
+    """Histogram of the top 12 bits of the score order key (the definition in include/csa2.h)."""
+    u = scores_np.astype(np.float32).view(np.uint32).copy()
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    u[nan] = 0xFF800000
+    u[u == 0x80000000] = 0
+    key = np.where(u & 0x80000000, ~u, u | 0x80000000).astype(np.uint32)
+    out = np.zeros((scores_np.shape[0], 4096), dtype=np.int64)
+    for r in range(scores_np.shape[0]):
+        np.add.at(out[r], (key[r][valid[r]] >> 20).astype(np.int64), 1)
+    return out
+
+
+def gpu_attention(cfg, x, idx, layer=0, out=None):
     import sparse_latent_attention_amd as csa2
     L = x["layers"][layer]
     q = L["q"]
@@ -108,7 +123,7 @@ def gpu_attention(cfg, x, idx, layer=0, splits=0, out=None):
         swa = x["swa"]
         sws = x["swa_scale"]
         csa2.sparse_attn_decode(q, x["pos"], idx, kv, x["kv_row_base"], swa, L["sink"], freqs, cfg.ratio,
-                                cfg.window, scale, out, kv_scale=kvs, swa_scale=sws, splits=splits, **kw)
+                                cfg.window, scale, out, kv_scale=kvs, swa_scale=sws, **kw)
     else:
         csa2.sparse_attn_prefill(q, x["pos"], idx, kv, L["swa"], x["swa_pos0"], L["sink"], freqs, cfg.ratio,
                                  cfg.window, scale, out, kv_scale=kvs, swa_scale=L["swa_scale"],

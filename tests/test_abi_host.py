@@ -42,8 +42,8 @@ int main(void) {
   printf("csa2_index_args sizeof %zu\n", sizeof(csa2_index_args));
   printf("csa2_topk_args sizeof %zu\n", sizeof(csa2_topk_args));
   printf("csa2_attn_args sizeof %zu\n", sizeof(csa2_attn_args));
-  F(csa2_index_args, width) F(csa2_index_args, q) F(csa2_index_args, cand) F(csa2_index_args, scale) F(csa2_index_args, scores)
-  F(csa2_topk_args, width) F(csa2_topk_args, scores) F(csa2_topk_args, out)
+  F(csa2_index_args, width) F(csa2_index_args, q) F(csa2_index_args, cand) F(csa2_index_args, scale) F(csa2_index_args, scores) F(csa2_index_args, key_hist)
+  F(csa2_topk_args, width) F(csa2_topk_args, scores) F(csa2_topk_args, out) F(csa2_topk_args, key_hist)
   F(csa2_attn_args, swa_rows) F(csa2_attn_args, q) F(csa2_attn_args, rope_inv_freq) F(csa2_attn_args, softmax_scale) F(csa2_attn_args, out)
   return 0;
 }
@@ -135,6 +135,7 @@ def _attn_args(**kw):
 
 @pytest.mark.parametrize("field,value,status", [
     ("window", 100, csa2.ERR_INVALID_ARG), ("topk", 500, csa2.ERR_INVALID_ARG), ("ratio", 4, csa2.ERR_INVALID_ARG),
+    ("window", 2048, csa2.ERR_INVALID_ARG), ("topk", 4096, csa2.ERR_INVALID_ARG),
     ("heads", 32, csa2.ERR_UNSUPPORTED), ("kv_dtype", csa2.FP8_E4M3, csa2.ERR_UNSUPPORTED),
     ("q_dtype", csa2.F32, csa2.ERR_UNSUPPORTED), ("kv_dtype", csa2.FP4_E2M1, csa2.ERR_INVALID_ARG),
     ("softmax_scale", 0.0, csa2.ERR_INVALID_ARG), ("sink", None, csa2.ERR_INVALID_ARG),
@@ -145,12 +146,10 @@ def test_attention_validation(field, value, status):
     assert csa2._lib.csa2_sparse_attn_prefill(ctypes.byref(a), None) == status
 
 
-def test_decode_rejects_small_workspace():
+def test_decode_needs_no_workspace_and_rejects_reserved_field():
+    assert csa2.attn_workspace_size(8, 64, 512, 128, 512, 0) == 0
     a = _attn_args(rows=8, splits=4)
-    need = csa2.attn_workspace_size(8, 64, 512, 128, 512, 4)
-    assert need > 0
-    assert csa2._lib.csa2_sparse_attn_decode(ctypes.byref(a), ctypes.c_void_p(0x1000), need - 1, None) == \
-        csa2.ERR_WORKSPACE
+    assert csa2._lib.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, None) == csa2.ERR_INVALID_ARG
 
 
 def test_status_strings():

@@ -1,0 +1,130 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+Every call goes through the same prepared C ABI calls bench.py uses (the
+library picks chunking and splits from the shapes, so the launches are the
+same).  The oracle checks sampled query rows one by one (scores over the whole
+row, top-k, attention of every layer); properties that hold at any size are
+checked on every row.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import CONFIGS, make_inputs
+
+from harness import (BF16_ATOL, BF16_RTOL, F32_ATOL, F32_RTOL, SCORE_TOL, assert_close, oracle_attention,
+                     oracle_score_bound, oracle_scores, oracle_topk, topk_band_mismatches)
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ["tiny_full_fp32", "full_decode_64k", "prefill_4096_at_128k", "reindex_decode_1m", "lowp_full_decode_1m"]
+
+
+def _run_path(cfg, x):
+    """The path exactly as bench.py launches it."""
+    import sparse_latent_attention_amd as csa2
+    dev = x["pos"].device
+    rows = x["pos"].shape[0]
+    scores = torch.empty(rows, cfg.width, dtype=torch.float32, device=dev)
+    idx = torch.empty(rows, cfg.topk, dtype=torch.int32, device=dev)
+    outs = [torch.empty_like(L["q"]) for L in x["layers"]]
+    freqs = csa2.rope_inv_freq(cfg.rope_dim, cfg.rope_theta, cfg.yarn_factor, cfg.yarn_orig).to(dev)
+    kI = x["kI"].reshape(-1, cfg.idx_dim)
+    kIs = None if x["kI_scale"] is None else x["kI_scale"].reshape(-1)
+    kv = x["main"].reshape(-1, x["main"].shape[-1])
+    kvs = None if x["main_scale"] is None else x["main_scale"].reshape(-1, x["main_scale"].shape[-1])
+    akw = dict(rope_dim=cfg.rope_dim, kv_fp4=cfg.main_dtype == "fp4", swa_fp8=cfg.swa_dtype == "fp8", kv_scale=kvs)
+    key_hist = (torch.empty(rows, 4096, dtype=torch.int32, device=dev)
+                if csa2.topk_uses_key_hist(rows, cfg.width, cfg.topk) else None)
+    calls = [csa2.prepare_indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio,
+                                        1.0 / math.sqrt(cfg.idx_dim * cfg.idx_heads), scores, k_scale=kIs,
+                                        cand=x.get("cand"), block_rows=cfg.block_rows, fp8=cfg.idx_dtype == "fp8",
+                                        key_hist=key_hist),
+             csa2.prepare_topk_select(scores, x["pos"], cfg.ratio, idx, cand=x.get("cand"), block_rows=cfg.block_rows,
+                                      key_hist=key_hist)]
+    tau = 1.0 / math.sqrt(cfg.dim)
+    for li, L in enumerate(x["layers"]):
+        if cfg.phase == "decode":
+            calls.append(csa2.prepare_sparse_attn_decode(L["q"], x["pos"], idx, kv, x["kv_row_base"], x["swa"],
+                                                         L["sink"], freqs, cfg.ratio, cfg.window, tau, outs[li],
+                                                         swa_scale=x["swa_scale"], **akw))
+        else:
+            calls.append(csa2.prepare_sparse_attn_prefill(L["q"], x["pos"], idx, kv, L["swa"], x["swa_pos0"],
+                                                          L["sink"], freqs, cfg.ratio, cfg.window, tau, outs[li],
+                                                          swa_scale=L["swa_scale"], kv_row_base=x["kv_row_base"],
+                                                          **akw))
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    return scores, idx, outs
+
+
+def _sample_rows(cfg):
+    n = cfg.q_tokens
+    if n <= 256:
+        picks = [0, n // 2, n - 1] if n > 64 else [0, n - 1]
+        if cfg.name == "tiny_full_fp32":
+            return np.arange(n)
+        return np.array(sorted(set(picks)))
+    return np.array([0, 1, 1777, n - 2, n - 1])
+
+
+@pytest.fixture(scope="module", params=NAMES)
+def full(request):
+    cfg = CONFIGS[request.param]
+    print(f"\n[full] {cfg.name} seed=2 rows={cfg.q_tokens} width={cfg.width} layers={1 + cfg.reuse_layers}",
+          flush=True)
+    x = make_inputs(cfg, 2, device="cuda")
+    torch.cuda.synchronize()
+    scores, idx, outs = _run_path(cfg, x)
+    yield cfg, x, scores, idx, outs
+    del x, scores, idx, outs
+    torch.cuda.empty_cache()
+
+
+def test_every_row_selection_is_well_formed(full):
+    cfg, x, scores, idx, _ = full
+    ii = idx.cpu().numpy().astype(np.int64)
+    pos = x["pos"].cpu().numpy()
+    nv = (pos + 1) // cfg.ratio
+    for r in range(ii.shape[0]):
+        v = ii[r][ii[r] >= 0]
+        assert np.all(ii[r][len(v):] == -1)
+        assert np.all(np.diff(v) > 0)
+        assert len(v) == min(cfg.topk, nv[r] if cfg.index_mode == "full" else len(v))
+        assert len(v) == 0 or (v[0] >= 0 and v[-1] < nv[r])
+        if cfg.index_mode == "reindex":
+            blocks = set(int(b) for b in x["cand"][r].cpu().numpy() if b >= 0)
+            assert set((v // cfg.block_rows).tolist()) <= blocks
+
+
+def test_every_output_finite(full):
+    cfg, x, scores, idx, outs = full
+    for o in outs:
+        assert torch.isfinite(o.float()).all()
+
+
+def test_sampled_rows_scores_topk_attention(full):
+    cfg, x, scores, idx, outs = full
+    rows = _sample_rows(cfg)
+    s_ref = oracle_scores(cfg, x, rows)
+    bound = oracle_score_bound(cfg, x, rows)
+    got = scores[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    inval = ~np.isfinite(bound)
+    assert np.all(got[inval] == -np.inf) and np.all(s_ref[inval] == -np.inf)
+    ratio = float((np.abs(got[~inval] - s_ref[~inval]) / bound[~inval]).max())
+    print(f"[{cfg.name}] sampled rows {rows.tolist()[:6]}: score max |d|/A = {ratio:.3e}")
+    assert ratio <= SCORE_TOL
+    gi = idx[torch.from_numpy(rows).cuda()].cpu().numpy()
+    assert np.array_equal(gi, oracle_topk(cfg, x, got, rows)), "top-k of the GPU scores is not bit-exact"
+    n_diff, n_bad = topk_band_mismatches(cfg, x, rows, gi, oracle_topk(cfg, x, s_ref, rows), s_ref, bound)
+    print(f"[{cfg.name}] end-to-end index differences {n_diff}, outside the band {n_bad}")
+    assert n_bad == 0
+    atol, rtol = (F32_ATOL, F32_RTOL) if cfg.out_dtype == "f32" else (BF16_ATOL, BF16_RTOL)
+    for layer, o in enumerate(outs):
+        ref = oracle_attention(cfg, x, gi, rows, layer=layer)
+        e = assert_close(o[torch.from_numpy(rows).cuda()], ref, atol, rtol, f"{cfg.name} layer {layer}")
+        print(f"[{cfg.name}] layer {layer} attention max_abs {e:.3e}")
