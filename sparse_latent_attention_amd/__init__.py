@@ -2,8 +2,8 @@
 
 Argument marshalling only: every step of the path runs in the HIP kernels of
 ``libcsa2.so``.  Torch tensors provide device memory and the current HIP
-stream.  The library must have been built (``python -m
-sparse_latent_attention_amd.build``); importing this package without it
+stream.  The library must have been built (``python
+sparse_latent_attention_amd/build.py``); importing this package without it
 raises ``ImportError`` -- there is no CPU fallback.
 
 Entry points (same names as the C ABI in include/csa2.h):
@@ -24,7 +24,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcsa2.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_latent_attention_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python sparse_latent_attention_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 

@@ -1,6 +1,8 @@
 """Builds libcsa2.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m sparse_latent_attention_amd.build
+    python sparse_latent_attention_amd/build.py
+
+(Run it by path: the package itself refuses to import until the library exists.)
 
 Every call recompiles all sources.  hipcc cross-compiles, so no GPU is needed.
 """

@@ -222,50 +222,72 @@ struct RawPair {
     uint32_t valid;  // bit i: row i of the pair exists and is visible
 };
 
+// Loads the 8 elements of chunk x8 of one stored row (`rowp` points at the row;
+// `fsc` at its FP8 scale, `e8` at its E8M0 scales).  Callers point invalid rows
+// at a dummy in-bounds buffer, so the loads need no branches.
 template <int DT, int D>
-__device__ __forceinline__ void raw_load_row(const void* base, const float* fscale, const uint8_t* e8, int64_t row,
-                                             int x8, RawPair& raw, int i) {
+__device__ __forceinline__ void raw_load_row(const uint8_t* rowp, const float* fsc, const uint8_t* e8, int x8,
+                                             RawPair& raw, int i) {
     if (DT == CSA2_BF16) {
-        raw.v[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + row * D + 8 * x8);
+        raw.v[i] = *reinterpret_cast<const u32x4*>(rowp + 16 * x8);
     } else if (DT == CSA2_F32) {
-        const float* pf = reinterpret_cast<const float*>(base) + row * D + 8 * x8;
-        raw.v[i] = *reinterpret_cast<const u32x4*>(pf);
-        raw.v2[i] = *reinterpret_cast<const u32x4*>(pf + 4);
+        raw.v[i] = *reinterpret_cast<const u32x4*>(rowp + 32 * x8);
+        raw.v2[i] = *reinterpret_cast<const u32x4*>(rowp + 32 * x8 + 16);
     } else if (DT == CSA2_FP8_E4M3) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(base) + row * D + 8 * x8);
+        const u32x2 w = *reinterpret_cast<const u32x2*>(rowp + 8 * x8);
         raw.v[i].x = w.x;
         raw.v[i].y = w.y;
-        raw.s[i] = fscale[row];
+        raw.s[i] = *fsc;
     } else {  // FP4-E2M1 with one E8M0 per 32
-        raw.v[i].x = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(base) + row * (D / 2) + 4 * x8);
-        raw.s[i] = e8m0_to_f32(e8[row * (D / 32) + (8 * x8) / 32]);
+        raw.v[i].x = *reinterpret_cast<const uint32_t*>(rowp + 4 * x8);
+        raw.s[i] = e8m0_to_f32(e8[(8 * x8) / 32]);
     }
+}
+
+template <int DT>
+constexpr int row_bytes(int d) {
+    return DT == CSA2_F32 ? 4 * d : DT == CSA2_BF16 ? 2 * d : DT == CSA2_FP8_E4M3 ? d : d / 2;
 }
 
 template <int DT, class CT>
 __device__ __forceinline__ void raw_convert(const RawPair& raw, int i, Pack8<CT>& o) {
-    if (!((raw.valid >> i) & 1u)) {
-        pack_zero<CT>(o);
-        return;
-    }
+    const bool ok = (raw.valid >> i) & 1u;
     if constexpr (DT == CSA2_BF16) {
-        o.w[0] = raw.v[i].x; o.w[1] = raw.v[i].y; o.w[2] = raw.v[i].z; o.w[3] = raw.v[i].w;
+        o.w[0] = ok ? raw.v[i].x : 0u;
+        o.w[1] = ok ? raw.v[i].y : 0u;
+        o.w[2] = ok ? raw.v[i].z : 0u;
+        o.w[3] = ok ? raw.v[i].w : 0u;
     } else if constexpr (DT == CSA2_F32) {
-        o.v[0] = __uint_as_float(raw.v[i].x); o.v[1] = __uint_as_float(raw.v[i].y);
-        o.v[2] = __uint_as_float(raw.v[i].z); o.v[3] = __uint_as_float(raw.v[i].w);
-        o.v[4] = __uint_as_float(raw.v2[i].x); o.v[5] = __uint_as_float(raw.v2[i].y);
-        o.v[6] = __uint_as_float(raw.v2[i].z); o.v[7] = __uint_as_float(raw.v2[i].w);
-    } else if constexpr (DT == CSA2_FP8_E4M3) {
-        const float sc = raw.s[i];
-        const f32x2 a = fp8x2_to_f32<false>(raw.v[i].x), b = fp8x2_to_f32<true>(raw.v[i].x);
-        const f32x2 c = fp8x2_to_f32<false>(raw.v[i].y), d = fp8x2_to_f32<true>(raw.v[i].y);
-        const float f[8] = {a[0] * sc, a[1] * sc, b[0] * sc, b[1] * sc, c[0] * sc, c[1] * sc, d[0] * sc, d[1] * sc};
-        pack_from_floats<CT>(f, o);
-    } else {
-        const float sc = raw.s[i];
+        const uint32_t u[8] = {raw.v[i].x, raw.v[i].y, raw.v[i].z, raw.v[i].w,
+                               raw.v2[i].x, raw.v2[i].y, raw.v2[i].z, raw.v2[i].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o.v[e] = ok ? __uint_as_float(u[e]) : 0.f;
+    } else if constexpr (DT == CSA2_FP4_E2M1 && sizeof(CT) == 2) {
+        // E2M1 pairs straight to bf16 pairs, multiplied by the power-of-two block scale (exact).
         const uint32_t w = raw.v[i].x;
-        const f32x2 a = fp4x2_to_f32<0>(w), b = fp4x2_to_f32<1>(w), c = fp4x2_to_f32<2>(w), d = fp4x2_to_f32<3>(w);
-        const float f[8] = {a[0] * sc, a[1] * sc, b[0] * sc, b[1] * sc, c[0] * sc, c[1] * sc, d[0] * sc, d[1] * sc};
+        const float sc = raw.s[i];
+        const uint32_t b0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+        const uint32_t b1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+        const uint32_t b2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+        const uint32_t b3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+        o.w[0] = ok ? b0 : 0u;
+        o.w[1] = ok ? b1 : 0u;
+        o.w[2] = ok ? b2 : 0u;
+        o.w[3] = ok ? b3 : 0u;
+    } else {
+        float f[8];
+        const float sc = raw.s[i];
+        if constexpr (DT == CSA2_FP8_E4M3) {
+            const f32x2 a = fp8x2_to_f32<false>(raw.v[i].x), b = fp8x2_to_f32<true>(raw.v[i].x);
+            const f32x2 c = fp8x2_to_f32<false>(raw.v[i].y), d = fp8x2_to_f32<true>(raw.v[i].y);
+            f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1]; f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+        } else {
+            const uint32_t w = raw.v[i].x;
+            const f32x2 a = fp4x2_to_f32<0>(w), b = fp4x2_to_f32<1>(w), c = fp4x2_to_f32<2>(w), d = fp4x2_to_f32<3>(w);
+            f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1]; f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = ok ? f[e] * sc : 0.f;
         pack_from_floats<CT>(f, o);
     }
 }
@@ -276,6 +298,7 @@ constexpr int kMaxTopk = 2048;
 // Per-row geometry the gather needs.
 struct RowCtx {
     int64_t pos, nv, kv_base;
+    const uint8_t* dummy;  // in-bounds bytes (this row's q) that invalid entries load from
     int r;
 };
 
@@ -302,7 +325,10 @@ __device__ __forceinline__ void load_pair(const AttnParams& p, const RowCtx& c, 
                 srow = a - p.swa_pos0;
                 valid = a >= 0 && srow >= 0 && srow < p.swa_rows;
             }
-            if (valid) raw_load_row<SWT, D>(p.swa, p.swa_scale, nullptr, srow, x8, raw, i);
+            constexpr int RB = row_bytes<SWT>(D);
+            const uint8_t* rp = valid ? reinterpret_cast<const uint8_t*>(p.swa) + srow * RB : c.dummy;
+            const float* fs = (SWT == CSA2_FP8_E4M3 && valid) ? p.swa_scale + srow : reinterpret_cast<const float*>(c.dummy);
+            raw_load_row<SWT, D>(rp, fs, c.dummy, x8, raw, i);
             raw.valid |= (valid ? 1u : 0u) << i;
         }
     } else {
@@ -311,7 +337,11 @@ __device__ __forceinline__ void load_pair(const AttnParams& p, const RowCtx& c, 
             const int e = tile * 16 + 4 * jb + i;
             const int32_t id = sel[e - W];
             const bool valid = id >= 0 && (int64_t)id < c.nv;  // group-causal mask
-            if (valid) raw_load_row<KVT, D>(p.kv, nullptr, p.kv_scale, c.kv_base + id, x8, raw, i);
+            constexpr int RB = row_bytes<KVT>(D);
+            const int64_t row = c.kv_base + (valid ? id : 0);
+            const uint8_t* rp = valid ? reinterpret_cast<const uint8_t*>(p.kv) + row * RB : c.dummy;
+            const uint8_t* e8 = (KVT == CSA2_FP4_E2M1 && valid) ? p.kv_scale + row * (D / 32) : c.dummy;
+            raw_load_row<KVT, D>(rp, nullptr, e8, x8, raw, i);
             raw.valid |= (valid ? 1u : 0u) << i;
         }
     }
@@ -367,13 +397,15 @@ __device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_
     // Lazy rescaling: m is only a reference point (the result is the same for any
     // m), so it moves -- and acc and l are rescaled -- only when some head's scores
     // exceed it by more than 2^8; the probabilities then stay below 256.
-    if (__ballot(tmax > m + 8.f) != 0ull) {
+    const uint64_t need_rescale = __ballot(tmax > m + 8.f);
+    if (__builtin_expect(__builtin_amdgcn_readfirstlane((uint32_t)(need_rescale | (need_rescale >> 32))) != 0u, 0)) {
         const float m_new = fmaxf(m, tmax);
         const float alpha = exp2f(m - m_new);  // 0 when m was -inf
         l *= alpha;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
         m = m_new;
+        __builtin_amdgcn_sched_barrier(0);
     }
     const float m_use = (m == kNegInf) ? 0.f : m;
     float pr4[4];
@@ -429,6 +461,7 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16)) void attn_rows_kernel(const A
     c.pos = p.pos[c.r];
     c.nv = (c.pos + 1) / p.ratio;
     c.kv_base = p.kv_row_base[c.r];
+    c.dummy = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)c.r * H * D * (QT == CSA2_F32 ? 4 : 2);
     const int n_tiles = (p.window + p.topk) / 16;
 
     if (tid < R / 2) {
@@ -541,6 +574,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
     c.pos = p.pos[c.r];
     c.nv = (c.pos + 1) / p.ratio;
     c.kv_base = p.kv_row_base[c.r];
+    c.dummy = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)c.r * H * D * (QT == CSA2_F32 ? 4 : 2);
     const int n_tiles = (p.window + p.topk) / 16;
 
     if (tid < R / 2) {

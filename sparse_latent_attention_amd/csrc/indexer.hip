@@ -47,6 +47,15 @@ __device__ __forceinline__ bool column_row(const IndexParams& p, int r, int64_t 
     return jr < nv;
 }
 
+// 16-byte load of key-row bytes.  (Non-temporal loads were measured here and
+// rejected: with each 128-byte row read as two 64-byte halves by separate
+// instructions they ran ~12% slower than ordinary loads.)
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+    if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
 // Element-type specific operand loaders.  A "step" covers 32 k-elements for
 // F32/BF16 (one 16x16x32 MFMA) and all 128 for FP8 (one 16x16x128 MFMA).
 template <int KT, int DI>
@@ -57,9 +66,10 @@ struct IdxOps<CSA2_BF16, DI> {
     static constexpr int kSteps = DI / 32;
     typedef bf16x8 Frag;
     // k-group g of step s: elements 32s + 8g .. +8 (64 contiguous bytes per row per step)
+    template <bool NT = false>
     static __device__ __forceinline__ Frag load(const void* base, int64_t row, int s, int g) {
         const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + row * DI + 32 * s + 8 * g;
-        return __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(p));
+        return __builtin_bit_cast(Frag, ld16<NT>(p));
     }
     static __device__ __forceinline__ Frag zero() { return __builtin_bit_cast(Frag, u32x4{0, 0, 0, 0}); }
     static __device__ __forceinline__ f32x4 mma(f32x4 c, Frag a, Frag b) { return Mma<__bf16>::k32(c, a, b); }
@@ -69,11 +79,12 @@ template <int DI>
 struct IdxOps<CSA2_F32, DI> {
     static constexpr int kSteps = DI / 32;
     typedef F32x8 Frag;
+    template <bool NT = false>
     static __device__ __forceinline__ Frag load(const void* base, int64_t row, int s, int g) {
         const float* p = reinterpret_cast<const float*>(base) + row * DI + 32 * s + 8 * g;
         Frag f;
-        f32x4 a = *reinterpret_cast<const f32x4*>(p);
-        f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+        f32x4 a = __builtin_bit_cast(f32x4, ld16<NT>(p));
+        f32x4 b = __builtin_bit_cast(f32x4, ld16<NT>(p + 4));
         f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
         f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
         return f;
@@ -93,10 +104,11 @@ struct IdxOps<CSA2_FP8_E4M3, 128> {
     typedef i32x8 Frag;
     // k-group g holds bytes 16g..16g+15 and 64+16g..64+16g+15 of the row, so each
     // of the two loads covers 64 contiguous bytes per row across the 4 groups.
+    template <bool NT = false>
     static __device__ __forceinline__ Frag load(const void* base, int64_t row, int, int g) {
         const uint8_t* p = reinterpret_cast<const uint8_t*>(base) + row * 128 + 16 * g;
-        u32x4 a = *reinterpret_cast<const u32x4*>(p);
-        u32x4 b = *reinterpret_cast<const u32x4*>(p + 64);
+        u32x4 a = ld16<NT>(p);
+        u32x4 b = ld16<NT>(p + 64);
         Frag f;
         f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
         f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
@@ -108,7 +120,7 @@ struct IdxOps<CSA2_FP8_E4M3, 128> {
 
 }  // namespace
 
-template <int KT, int HI, int DI, bool REINDEX, bool HIST>
+template <int KT, int HI, int DI, bool REINDEX, bool HIST, bool NT>
 __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p) {
     // Per-workgroup histogram of the score keys' top 12 bits (one row per workgroup).
     __shared__ uint32_t hist[HIST ? kKeyBins : 1];
@@ -151,27 +163,39 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p)
         __syncthreads();
     }
 
-    for (int64_t cb = c_begin + 64 * wave; cb < c_end; cb += 256) {
-        const int64_t c_out = cb + lane;
-        if (cb >= c_live) {  // nothing visible in these 64 columns
-            if (c_out < c_end) srow[c_out] = kNegInf;
-            continue;
-        }
-        float v[4];
+    // One step = 64 consecutive columns of this wave: the key rows of 4 tiles of
+    // 16 (B operands) and the output column's scale.  Steps are software
+    // pipelined: the next step's loads are issued before this step's MFMAs.
+    struct Step {
+        Frag kb[4][S];
+        float sc;     // score scale of this lane's output column
+        bool valid;   // this lane's output column is valid
+    };
+    auto issue = [&](int64_t cb, Step& st) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int64_t c = cb + 16 * u + li;
             int64_t prow = 0;
             const bool valid = (c < c_end) && column_row<REINDEX>(p, r, c, nv, base, prow);
-            Frag kb[S];
 #pragma unroll
-            for (int s = 0; s < S; ++s) kb[s] = valid ? Ops::load(p.k, prow, s, g) : Ops::zero();
+            for (int s = 0; s < S; ++s) st.kb[u][s] = valid ? Ops::template load<NT>(p.k, prow, s, g) : Ops::zero();
+        }
+        const int64_t c_out = cb + lane;
+        int64_t prow = 0;
+        st.valid = (c_out < c_end) && column_row<REINDEX>(p, r, c_out, nv, base, prow);
+        st.sc = p.scale;
+        if (KT == CSA2_FP8_E4M3 && st.valid) st.sc *= p.k_scale[prow];
+    };
+    auto finish = [&](int64_t cb, const Step& st) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
             float acc_sum = 0.f;
 #pragma unroll
             for (int t = 0; t < HT; ++t) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < S; ++s) acc = Ops::mma(acc, qa[t][s], kb[s]);
+                for (int s = 0; s < S; ++s) acc = Ops::mma(acc, qa[t][s], st.kb[u][s]);
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) acc_sum += wr[t][rr] * relu_bits(acc[rr]);
             }
@@ -186,22 +210,35 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p)
         k1 += shfl_xor(hi ? v[1] : v[3], 32);
         float kk = mid ? k1 : k0;
         kk += shfl_xor(mid ? k0 : k1, 16);
-
+        const int64_t c_out = cb + lane;
         if (c_out < c_end) {
-            int64_t prow = 0;
-            const bool valid = column_row<REINDEX>(p, r, c_out, nv, base, prow);
-            float sc = p.scale;
-            if (KT == CSA2_FP8_E4M3 && valid) sc *= p.k_scale[prow];
-            const float score = valid ? sc * kk : kNegInf;
+            const float score = st.valid ? st.sc * kk : kNegInf;
             srow[c_out] = score;
-            if (HIST && valid) atomicAdd(&hist[order_key(score) >> 20], 1u);
+            if (HIST && st.valid) atomicAdd(&hist[order_key(score) >> 20], 1u);
         }
+    };
+
+    int64_t cb = c_begin + 64 * wave;
+    Step A, B;
+    if (cb < c_live) issue(cb, A);
+    while (cb < c_live) {
+        if (cb + 256 < c_live) issue(cb + 256, B);
+        finish(cb, A);
+        cb += 256;
+        if (cb >= c_live) break;
+        if (cb + 256 < c_live) issue(cb + 256, A);
+        finish(cb, B);
+        cb += 256;
+    }
+    for (; cb < c_end; cb += 256) {  // nothing visible in these columns
+        const int64_t c_out = cb + lane;
+        if (c_out < c_end) srow[c_out] = kNegInf;
     }
     if (HIST) {
         __syncthreads();
-        uint32_t* g = p.key_hist + (int64_t)r * kKeyBins;
+        uint32_t* gh = p.key_hist + (int64_t)r * kKeyBins;
         for (int b = threadIdx.x; b < kKeyBins; b += 256)
-            if (hist[b]) atomicAdd(&g[b], hist[b]);
+            if (hist[b]) atomicAdd(&gh[b], hist[b]);
     }
 }
 
@@ -214,14 +251,17 @@ template <int KT, int HI, int DI, bool REINDEX>
 static hipError_t launch_one(const IndexParams& p, int rows, hipStream_t stream) {
     const int64_t chunks = (p.width + p.cols_per_wg - 1) / p.cols_per_wg;
     dim3 grid((unsigned)chunks, (unsigned)rows);
-    if (p.key_hist == nullptr) {
-        hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, REINDEX, false>), grid, dim3(256), 0, stream, p);
-        return hipGetLastError();
+    const bool nt = false;  // see ld16
+    if (p.key_hist != nullptr) {
+        const int64_t nh = (int64_t)rows * kKeyBins;
+        hipLaunchKernelGGL(key_hist_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)),
+                           dim3(256), 0, stream, p.key_hist, nh);
+        if (nt) hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, REINDEX, true, true>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, REINDEX, true, false>), grid, dim3(256), 0, stream, p);
+    } else {
+        if (nt) hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, REINDEX, false, true>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, REINDEX, false, false>), grid, dim3(256), 0, stream, p);
     }
-    const int64_t nh = (int64_t)rows * kKeyBins;
-    hipLaunchKernelGGL(key_hist_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)),
-                       dim3(256), 0, stream, p.key_hist, nh);
-    hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, REINDEX, true>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
