@@ -22,9 +22,10 @@ Modules:
 * ``rope``      -- RoPE / YaRN inverse frequencies, rotation and its inverse
 * ``indexer``   -- lightning-indexer scores, FULL and REINDEX
 * ``topk``      -- per-row top-k with the ordering contract
+* ``candidates`` -- the FULL layer's hierarchical candidate pool (8-row block maxima, top-2048)
 * ``attention`` -- single-softmax sink attention over SWA + selected rows
 
 Parity status of each function is stated in its module docstring.
 """
 
-from . import formats, geometry, rope, indexer, topk, attention  # noqa: F401
+from . import formats, geometry, rope, indexer, topk, candidates, attention  # noqa: F401
