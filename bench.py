@@ -29,10 +29,27 @@ DEFAULT_CONFIG = "lowp_full_decode_1m"
 _ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
 
 
-def algorithmic_bytes(cfg, x):
-    """Bytes each kernel of one step must move at least once (reads + writes)."""
+# Dense matrix-core peaks of MI355X by operand type (TFLOP/s, no sparsity).
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0, "f32": 157.3}
+
+
+def _unique_plane_rows(base, rows_read):
+    """Distinct plane rows over query rows: rows_read(r) -> local row ids of row r, offset by its plane base."""
+    import torch
+    seen = [base[r] + rows_read(r) for r in range(base.shape[0])]
+    return int(torch.unique(torch.cat(seen)).numel()) if seen else 0
+
+
+def algorithmic_work(cfg, x, idx_host=None):
+    """Per kernel of one step: the bytes it must move at least once (every distinct input byte read
+    once, every output byte written once) and the multiply-add flops it must do.
+
+    Queries that share one plane (a prefill chunk) read each distinct plane row once; decode rows
+    each own a plane.  Flops count 2 per multiply-add: the indexer's 64 x 128 head dots per scored
+    column, attention's QK^T and PV (2 x H x D multiply-adds per entry row per query)."""
     import torch
     pos = x["pos"].cpu()
+    base = x["kv_row_base"].cpu()
     nv = ((pos + 1) // cfg.ratio).clamp(max=cfg.n_main_rows)
     rows = pos.shape[0]
     idx_row = cfg.idx_dim * _ELEM[cfg.idx_dtype] + (4 if cfg.idx_dtype == "fp8" else 0)
@@ -42,21 +59,52 @@ def algorithmic_bytes(cfg, x):
         cols = cand.repeat_interleave(cfg.block_rows, dim=1) * cfg.block_rows + \
             torch.arange(cfg.block_rows).repeat(cfg.n_blocks)
         valid = (cand.repeat_interleave(cfg.block_rows, dim=1) >= 0) & (cols < nv[:, None])
-        scored_rows = int(valid.sum())
+        scored = int(valid.sum())
+        unique_rows = _unique_plane_rows(base, lambda r: cols[r][valid[r]])
         extra = rows * cfg.n_blocks * 4
     else:
-        scored_rows = int(nv.sum())
+        scored = int(nv.sum())
+        unique_rows = sum(int(nv[base == b].max()) for b in torch.unique(base))
         extra = 0
-    idx_bytes = scored_rows * idx_row + qI + extra + rows * cfg.width * 4
+    idx_bytes = unique_rows * idx_row + qI + extra + rows * cfg.width * 4
+    idx_flops = 2 * scored * cfg.idx_heads * cfg.idx_dim
     topk_bytes = rows * cfg.width * 4 + rows * cfg.topk * 4 + extra
     main_row = cfg.dim // 2 + cfg.dim // 32 if cfg.main_dtype == "fp4" else cfg.dim * _ELEM[cfg.main_dtype]
     swa_row = cfg.dim * _ELEM[cfg.swa_dtype] + (4 if cfg.swa_dtype == "fp8" else 0)
     sel = torch.minimum(nv, torch.tensor(cfg.topk))
     win = torch.minimum(pos + 1, torch.tensor(cfg.window))
+    layers = len(x["layers"])
     qo = rows * cfg.heads * cfg.dim * (_ELEM[cfg.q_dtype] + _ELEM[cfg.out_dtype])
-    attn_bytes = int(sel.sum()) * main_row + int(win.sum()) * swa_row + qo + rows * cfg.topk * 4
-    return {"indexer_score": idx_bytes, "topk_select": topk_bytes, "sparse_attn": attn_bytes,
-            "scored_rows": scored_rows}
+    if cfg.phase == "decode":
+        main_rows, swa_rows = int(sel.sum()), int(win.sum())
+    else:
+        # one chunk: distinct selected rows of the shared plane, and the linear SWA array once
+        ii = idx_host
+        main_rows = int(torch.unique(ii[ii >= 0]).numel()) if ii is not None else int(sel.sum())
+        swa_rows = int(pos.max() - pos.min()) + cfg.window
+    # one launch per layer; each re-reads the selected rows and its own q / SWA
+    attn_bytes = layers * (main_rows * main_row + swa_rows * swa_row + qo + rows * cfg.topk * 4)
+    attn_flops = layers * 4 * cfg.heads * cfg.dim * int((sel + win).sum())
+    attn_dt = "f32" if cfg.q_dtype == "f32" else "bf16"
+    return {"indexer_score": (idx_bytes, idx_flops, cfg.idx_dtype, 1),
+            "topk_select": (topk_bytes, 0, None, 1),
+            "sparse_attn": (attn_bytes, attn_flops, attn_dt, layers),
+            "scored_rows": scored}
+
+
+def roofline_of(work, ms):
+    """Bound (the HBM or matrix-core roof the kernel's intensity puts it under), achieved and fraction."""
+    nbytes, flops, dt, _ = work
+    t = ms * 1e-3
+    if dt is not None and flops > 0:
+        peak_flops = MFMA_PEAK_TFLOPS[dt] * 1e12
+        if flops / nbytes > peak_flops / (HBM_PEAK_GBS * 1e9):
+            achieved = flops / t / 1e12
+            return {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS[dt],
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS[dt], 4)}
+    achieved = nbytes / t / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4)}
 
 
 KERNEL_SOURCES = {
@@ -249,13 +297,14 @@ def main():
     ms_step = wall * 1e3 / args.steps
     kern_ms = {n: sum(a.elapsed_time(b) for a, b in evs[n]) / args.steps for n in names}
 
-    ab = algorithmic_bytes(cfg, x)
+    work = algorithmic_work(cfg, x, idx.cpu() if cfg.phase == "prefill" else None)
     dominant = max(names, key=lambda n: kern_ms[n])
-    achieved = ab[dominant] / (kern_ms[dominant] * 1e-3) / 1e9
-    roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dominant, cfg.name),
-                "algorithmic_bytes_per_launch": ab[dominant], "source_hash": kernel_source_hash(dominant)}
+    roofline = roofline_of(work[dominant], kern_ms[dominant])
+    roofline.update({"kernel": dominant, "traffic": measured_traffic(dominant, cfg.name),
+                     "launches_per_step": work[dominant][3],
+                     "algorithmic_bytes_per_launch": work[dominant][0] // work[dominant][3],
+                     "algorithmic_flops_per_launch": work[dominant][1] // work[dominant][3],
+                     "source_hash": kernel_source_hash(dominant)})
     q_tokens = rows
     line = {
         "metric": METRIC, "value": round(q_tokens / (ms_step * 1e-3), 1), "unit": "query-tokens/s", "n_gpus": 1,
@@ -268,7 +317,7 @@ def main():
                    "index": f"{cfg.index_mode} {cfg.idx_heads}x{cfg.idx_dim} {cfg.idx_dtype}",
                    "main_kv": cfg.main_dtype, "swa": cfg.swa_dtype, "attention_layers": len(x["layers"])},
         "kernels_ms": {n: round(v, 4) for n, v in kern_ms.items()},
-        "kernels_gbs": {n: round(ab[n] / (kern_ms[n] * 1e-3) / 1e9, 1) for n in names},
+        "kernels_roofline": {n: roofline_of(work[n], kern_ms[n]) for n in names},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
