@@ -6,6 +6,8 @@
 A step is one pass of the whole path over one batch of synthetic inputs that
 are already resident in HBM:
   decode  : indexer_score -> topk_select -> sparse_attn_decode
+            (a FULL owner layer that builds the REINDEX candidate pool adds
+            candidate_pool from the block scores the indexer wrote)
   prefill : indexer_score -> topk_select -> sparse_attn_prefill for the FULL
             layer and every REUSE layer (same indices, own q / SWA / sink)
 The default workload is the 1M-context low-precision decode (64 sequences,
@@ -66,7 +68,8 @@ def algorithmic_work(cfg, x, idx_host=None):
         scored = int(nv.sum())
         unique_rows = sum(int(nv[base == b].max()) for b in torch.unique(base))
         extra = 0
-    idx_bytes = unique_rows * idx_row + qI + extra + rows * cfg.width * 4
+    nbm = -(-cfg.width // cfg.block_rows) if cfg.pool_blocks else 0
+    idx_bytes = unique_rows * idx_row + qI + extra + rows * cfg.width * 4 + rows * nbm * 4
     idx_flops = 2 * scored * cfg.idx_heads * cfg.idx_dim
     topk_bytes = rows * cfg.width * 4 + rows * cfg.topk * 4 + extra
     main_row = cfg.dim // 2 + cfg.dim // 32 if cfg.main_dtype == "fp4" else cfg.dim * _ELEM[cfg.main_dtype]
@@ -86,8 +89,11 @@ def algorithmic_work(cfg, x, idx_host=None):
     attn_bytes = layers * (main_rows * main_row + swa_rows * swa_row + qo + rows * cfg.topk * 4)
     attn_flops = layers * 4 * cfg.heads * cfg.dim * int((sel + win).sum())
     attn_dt = "f32" if cfg.q_dtype == "f32" else "bf16"
+    # candidate pool: read the block scores, write the kept blocks
+    pool_bytes = rows * nbm * 4 + rows * cfg.pool_blocks * 4
     return {"indexer_score": (idx_bytes, idx_flops, cfg.idx_dtype, 1),
             "topk_select": (topk_bytes, 0, None, 1),
+            "candidate_pool": (pool_bytes, 0, None, 1),
             "sparse_attn": (attn_bytes, attn_flops, attn_dt, layers),
             "scored_rows": scored}
 
@@ -110,6 +116,7 @@ def roofline_of(work, ms):
 KERNEL_SOURCES = {
     "indexer_score": ["indexer.hip", "common.hpp", "kernels.hpp"],
     "topk_select": ["topk.hip", "common.hpp", "kernels.hpp"],
+    "candidate_pool": ["topk.hip", "pool.hip", "common.hpp", "kernels.hpp"],
     "sparse_attn": ["attention.hip", "common.hpp", "kernels.hpp"],
 }
 
@@ -158,6 +165,8 @@ def cpu_baseline(cfg, x, budget_s=20.0):
         t0 = time.perf_counter()
         s = oracle_scores(sub_cfg, sub, np.array([0]))
         idx = oracle_topk(sub_cfg, sub, s, np.array([0]))
+        if cfg.pool_blocks:
+            oracle.candidates.candidate_pool(s, sub["pos"].numpy(), cfg.ratio, cfg.block_rows, cfg.pool_blocks)
         for layer in range(len(sub["layers"])):
             oracle_attention(sub_cfg, sub, idx, np.array([0]), layer=layer)
         t_total += time.perf_counter() - t0
@@ -165,7 +174,8 @@ def cpu_baseline(cfg, x, budget_s=20.0):
         if t_total >= budget_s:
             break
     return {"value": done / t_total, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {rows} query rows of the {cfg.name} batch, whole path (indexer, top-k, attention"
+            "sample": f"{done} of {rows} query rows of the {cfg.name} batch, whole path (indexer, top-k, "
+                      f"{'candidate pool, ' if cfg.pool_blocks else ''}attention"
                       f"{' x %d layers' % len(x['layers']) if len(x['layers']) > 1 else ''}), float64 NumPy; "
                       f"host copy excluded; {t_total:.1f} s"}
 
@@ -244,15 +254,21 @@ def main():
     akw = dict(rope_dim=cfg.rope_dim, kv_fp4=cfg.main_dtype == "fp4", swa_fp8=cfg.swa_dtype == "fp8", kv_scale=kvs)
     topk_ws = torch.empty(max(csa2.topk_workspace_size(rows, cfg.width, cfg.topk), 1), dtype=torch.uint8, device=dev)
 
-    names = ["indexer_score", "topk_select", "sparse_attn"]
+    names = ["indexer_score", "topk_select"] + (["candidate_pool"] if cfg.pool_blocks else []) + ["sparse_attn"]
     evs = {n: [] for n in names}
     # Arguments are marshalled once; each step only crosses into the library.
     # The indexer also builds the score-key histogram when top-k takes its wide-row path.
     key_hist = (torch.empty(rows, 4096, dtype=torch.int32, device=dev)
                 if csa2.topk_uses_key_hist(rows, cfg.width, cfg.topk) else None)
+    block_max = pool = call_pool = None
+    if cfg.pool_blocks:
+        block_max = torch.empty(rows, -(-cfg.width // cfg.block_rows), dtype=torch.float32, device=dev)
+        pool = torch.empty(rows, cfg.pool_blocks, dtype=torch.int32, device=dev)
+        call_pool = csa2.prepare_candidate_pool(x["pos"], cfg.ratio, pool, block_max=block_max, width=cfg.width,
+                                                block_rows=cfg.block_rows)
     call_idx = csa2.prepare_indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, tau_i, scores,
                                           k_scale=kIs, cand=x.get("cand"), block_rows=cfg.block_rows,
-                                          fp8=cfg.idx_dtype == "fp8", key_hist=key_hist)
+                                          fp8=cfg.idx_dtype == "fp8", key_hist=key_hist, block_max=block_max)
     call_topk = csa2.prepare_topk_select(scores, x["pos"], cfg.ratio, idx, cand=x.get("cand"),
                                          block_rows=cfg.block_rows, workspace=topk_ws, key_hist=key_hist)
     call_attn = []
@@ -276,13 +292,18 @@ def main():
         e1 = ev() if record else None
         call_topk()
         e2 = ev() if record else None
+        if call_pool is not None:
+            call_pool()
+        e2p = ev() if record and call_pool is not None else e2
         for c in call_attn:
             c()
         e3 = ev() if record else None
         if record:
             evs["indexer_score"].append((e0, e1))
             evs["topk_select"].append((e1, e2))
-            evs["sparse_attn"].append((e2, e3))
+            if call_pool is not None:
+                evs["candidate_pool"].append((e2, e2p))
+            evs["sparse_attn"].append((e2p, e3))
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 /* Status codes. */
 #define CSA2_OK 0
@@ -114,7 +114,8 @@ typedef struct csa2_index_args {
     int32_t q_dtype;            /* element type of q */
     int32_t k_dtype;            /* element type of k */
     int32_t n_blocks;           /* REINDEX: candidate blocks per row (ignored for FULL) */
-    int32_t block_rows;         /* REINDEX: rows per candidate block, 1..64 */
+    int32_t block_rows;         /* REINDEX: rows per candidate block, 1..64.  FULL with block_max:
+                                 * rows per pooled block, a power of two in 4..64.  Else ignored. */
     int32_t _pad0;
     int64_t width;              /* columns per score row (FULL: >= every n_visible) */
     const void* q;              /* [rows, heads, dim] */
@@ -133,6 +134,13 @@ typedef struct csa2_index_args {
                                  * (bits | 0x80000000 for scores >= +0, ~bits below, NaN as -inf,
                                  * -0 as +0).  Passing it on to csa2_topk_select saves that call a
                                  * full pass over the scores. */
+    float* block_max;           /* optional out, FULL only: [rows, ceil(width / block_rows)], or NULL.
+                                 * Block b of row r gets the block score csa2_candidate_pool ranks:
+                                 * the largest score over its visible columns, with NaN read as -inf
+                                 * and +-inf clipped to +-FLT_MAX; the block holding the newest
+                                 * visible row ((n_visible - 1) / block_rows) gets +inf; blocks with
+                                 * no visible column get -inf.  Written in the same pass as the
+                                 * scores (no second read of them). */
 } csa2_index_args;
 
 int32_t csa2_indexer_score(const csa2_index_args* args, csa2_stream_t stream);
@@ -176,6 +184,52 @@ size_t csa2_topk_workspace_size(int32_t rows, int64_t width, int32_t k);
 
 int32_t csa2_topk_select(const csa2_topk_args* args, void* workspace, size_t workspace_bytes,
                          csa2_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Hierarchical candidate pool of the FULL owner layer.
+ *
+ * From the FULL layer's own score rows, cut into blocks of block_rows
+ * consecutive rows (8, the index plane's page height, in the pages' model):
+ *
+ *   block score  = max over the block's visible columns of the score, NaN read
+ *                  as -inf and +-inf clipped to +-FLT_MAX;
+ *   newest block = the one holding row (pos + 1) / ratio - 1, pinned to +inf;
+ *   cand[r, :]   = the n_cand best of the ceil(n_visible / block_rows) blocks,
+ *                  by block score descending and the lower block id on ties,
+ *                  written ascending and padded with -1.
+ *
+ * ("DeepSeek-V4.1-Flash 架构解剖", special module "indexer", fig. 3b second
+ * level and fig. 3 candidate blocks; "DeepSeek-V4.1-Flash 结构说明" section 5.2;
+ * "万字长文解析DeekSeekV4.1flash" section 4 and appendix A.11.)  The result is
+ * the cand argument of the REINDEX calls (csa2_indexer_score,
+ * csa2_topk_select) of the layers that share this owner's plane.
+ *
+ * Block scores come either from block_max (what csa2_indexer_score wrote in
+ * the scoring pass; scores may then be NULL) or, when block_max is NULL, are
+ * computed here from scores into the workspace.
+ *
+ * Supported: block_rows a power of two in 4..64; 1 <= n_cand <= 2048;
+ * width < 2^31.
+ */
+typedef struct csa2_pool_args {
+    uint32_t struct_size;       /* sizeof(csa2_pool_args) */
+    int32_t rows;               /* score rows, >= 0 */
+    int32_t ratio;              /* compression ratio m, 1 or 2 */
+    int32_t block_rows;         /* rows per block */
+    int32_t n_cand;             /* blocks kept per row (2048 in the pages' model) */
+    int32_t _pad0;
+    int64_t width;              /* columns per FULL score row */
+    const float* scores;        /* [rows, width] FULL scores, or NULL when block_max is given */
+    const float* block_max;     /* [rows, ceil(width / block_rows)] from csa2_indexer_score, or NULL */
+    const int64_t* pos;         /* [rows] absolute query positions */
+    int32_t* cand;              /* out: [rows, n_cand] block ids */
+} csa2_pool_args;
+
+/* Bytes of workspace csa2_candidate_pool needs (enough with or without block_max). */
+size_t csa2_candidate_pool_workspace_size(int32_t rows, int64_t width, int32_t block_rows, int32_t n_cand);
+
+int32_t csa2_candidate_pool(const csa2_pool_args* args, void* workspace, size_t workspace_bytes,
+                            csa2_stream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Sparse sink attention.

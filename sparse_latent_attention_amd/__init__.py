@@ -42,7 +42,7 @@ class IndexArgs(ctypes.Structure):
         ("struct_size", _u32), ("mode", _i32), ("rows", _i32), ("heads", _i32), ("dim", _i32), ("ratio", _i32),
         ("q_dtype", _i32), ("k_dtype", _i32), ("n_blocks", _i32), ("block_rows", _i32), ("_pad0", _i32),
         ("width", _i64), ("q", _vp), ("w", _vp), ("k", _vp), ("k_scale", _vp), ("row_base", _vp), ("pos", _vp),
-        ("cand", _vp), ("scale", _f32), ("_pad1", _i32), ("scores", _vp), ("key_hist", _vp),
+        ("cand", _vp), ("scale", _f32), ("_pad1", _i32), ("scores", _vp), ("key_hist", _vp), ("block_max", _vp),
     ]
 
 
@@ -51,6 +51,13 @@ class TopkArgs(ctypes.Structure):
         ("struct_size", _u32), ("rows", _i32), ("k", _i32), ("ratio", _i32), ("n_blocks", _i32),
         ("block_rows", _i32), ("width", _i64), ("scores", _vp), ("pos", _vp), ("cand", _vp), ("out", _vp),
         ("key_hist", _vp),
+    ]
+
+
+class PoolArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _u32), ("rows", _i32), ("ratio", _i32), ("block_rows", _i32), ("n_cand", _i32),
+        ("_pad0", _i32), ("width", _i64), ("scores", _vp), ("block_max", _vp), ("pos", _vp), ("cand", _vp),
     ]
 
 
@@ -74,6 +81,10 @@ _lib.csa2_topk_workspace_size.restype = ctypes.c_size_t
 _lib.csa2_topk_workspace_size.argtypes = [_i32, _i64, _i32]
 _lib.csa2_topk_select.restype = _i32
 _lib.csa2_topk_select.argtypes = [ctypes.POINTER(TopkArgs), _vp, ctypes.c_size_t, _vp]
+_lib.csa2_candidate_pool_workspace_size.restype = ctypes.c_size_t
+_lib.csa2_candidate_pool_workspace_size.argtypes = [_i32, _i64, _i32, _i32]
+_lib.csa2_candidate_pool.restype = _i32
+_lib.csa2_candidate_pool.argtypes = [ctypes.POINTER(PoolArgs), _vp, ctypes.c_size_t, _vp]
 _lib.csa2_attn_workspace_size.restype = ctypes.c_size_t
 _lib.csa2_attn_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
 _lib.csa2_sparse_attn_decode.restype = _i32
@@ -85,7 +96,7 @@ _lib.csa2_rope_inv_freq.argtypes = [_i32, ctypes.c_double, ctypes.c_double, _i64
 
 ABI_VERSION = _lib.csa2_abi_version()
 EXPORTED = ("csa2_abi_version", "csa2_status_string", "csa2_indexer_score", "csa2_topk_workspace_size",
-            "csa2_topk_select", "csa2_attn_workspace_size", "csa2_sparse_attn_decode", "csa2_sparse_attn_prefill",
+            "csa2_topk_select", "csa2_candidate_pool_workspace_size", "csa2_candidate_pool", "csa2_attn_workspace_size", "csa2_sparse_attn_decode", "csa2_sparse_attn_prefill",
             "csa2_rope_inv_freq")
 
 
@@ -145,15 +156,17 @@ def rope_inv_freq(rope_dim, theta, yarn_factor=1.0, yarn_orig_len=0):
 
 
 def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None, cand=None, block_rows=8,
-                  fp8=False, key_hist=None, stream=None):
+                  fp8=False, key_hist=None, block_max=None, stream=None):
     """Fills ``scores`` [rows, width] (float32).  REINDEX when ``cand`` is given.
 
     q [rows, H_I, D_I] and k [*, D_I] are float32/bfloat16, or uint8 FP8-E4M3
     codes with ``fp8=True`` (then ``k_scale`` [*] float32 is required and the
     query scales are already folded into w).  ``key_hist`` (int32 [rows, 4096])
     optionally receives the score-key histogram topk_select can reuse.
+    ``block_max`` (FULL only, float32 [rows, ceil(width / block_rows)])
+    optionally receives the candidate pool's block scores.
     """
-    _dev(q, w, k, row_base, pos, scores, k_scale, cand, key_hist)
+    _dev(q, w, k, row_base, pos, scores, k_scale, cand, key_hist, block_max)
     if key_hist is not None and (key_hist.dtype != torch.int32 or tuple(key_hist.shape) != (q.shape[0], 4096)):
         raise ValueError("csa2.indexer_score: key_hist must be int32 [rows, 4096]")
     rows, heads, dim = q.shape
@@ -183,6 +196,13 @@ def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None,
         if cand.shape[0] != rows:
             raise ValueError("csa2.indexer_score: cand rows")
         a.n_blocks, a.block_rows = cand.shape[1], int(block_rows)
+    if block_max is not None:
+        _need(block_max, torch.float32, "block_max")
+        nb = -(-a.width // int(block_rows))
+        if tuple(block_max.shape) != (rows, nb):
+            raise ValueError(f"csa2.indexer_score: block_max must be [rows, {nb}]")
+        a.block_rows = int(block_rows)
+    a.block_max = _ptr(block_max)
     a.q, a.w, a.k, a.k_scale = _ptr(q), _ptr(w), _ptr(k), _ptr(k_scale)
     a.row_base, a.pos, a.cand, a.scores = _ptr(row_base), _ptr(pos), _ptr(cand), _ptr(scores)
     a.key_hist = _ptr(key_hist)
@@ -226,6 +246,49 @@ def topk_select(scores, pos, ratio, out, *, cand=None, block_rows=8, key_hist=No
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("csa2_topk_select", _lib.csa2_topk_select(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
+
+
+def candidate_pool_workspace_size(rows, width, block_rows=8, n_cand=2048):
+    return int(_lib.csa2_candidate_pool_workspace_size(int(rows), int(width), int(block_rows), int(n_cand)))
+
+
+def candidate_pool(pos, ratio, cand, *, scores=None, block_max=None, width=None, block_rows=8, workspace=None,
+                   stream=None):
+    """Fills ``cand`` [rows, n_cand] int32 with the FULL layer's candidate blocks (ascending, -1 padded).
+
+    Block scores come from ``block_max`` (written by indexer_score) when given,
+    else from ``scores`` [rows, width].  ``width`` is the FULL score width
+    (taken from ``scores`` when omitted).
+    """
+    _dev(pos, cand, scores, block_max, workspace)
+    _need(pos, torch.int64, "pos")
+    _need(cand, torch.int32, "cand")
+    rows = cand.shape[0]
+    if width is None:
+        if scores is None:
+            raise ValueError("csa2.candidate_pool: width is needed when scores is not given")
+        width = scores.shape[1]
+    if scores is not None:
+        _need(scores, torch.float32, "scores")
+        if tuple(scores.shape) != (rows, width):
+            raise ValueError("csa2.candidate_pool: scores must be [rows, width]")
+    if block_max is not None:
+        _need(block_max, torch.float32, "block_max")
+        if tuple(block_max.shape) != (rows, -(-int(width) // int(block_rows))):
+            raise ValueError("csa2.candidate_pool: block_max must be [rows, ceil(width / block_rows)]")
+    if pos.shape != (rows,):
+        raise ValueError("csa2.candidate_pool: pos must be [rows]")
+    a = PoolArgs()
+    a.struct_size = ctypes.sizeof(PoolArgs)
+    a.rows, a.ratio, a.block_rows, a.n_cand, a.width = rows, int(ratio), int(block_rows), cand.shape[1], int(width)
+    a.scores, a.block_max, a.pos, a.cand = _ptr(scores), _ptr(block_max), _ptr(pos), _ptr(cand)
+    need = candidate_pool_workspace_size(rows, width, block_rows, a.n_cand)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=pos.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("csa2_candidate_pool", _lib.csa2_candidate_pool(ctypes.byref(a), _ptr(workspace), ws_bytes,
+                                                           _stream(stream)))
+    return cand
 
 
 def _attn_args(q, pos, idx, kv, kv_scale, kv_row_base, swa, swa_scale, sink, inv_freq, ratio, window,
@@ -341,3 +404,14 @@ def prepare_sparse_attn_decode(*args, stream=None, **kw):
 
 def prepare_sparse_attn_prefill(*args, stream=None, **kw):
     return _prepare("csa2_sparse_attn_prefill", lambda: sparse_attn_prefill(*args, stream=stream, **kw), stream)
+
+
+def prepare_candidate_pool(*args, stream=None, **kw):
+    if kw.get("workspace") is None:
+        pos, cand = args[0], args[2]
+        width = kw["scores"].shape[1] if kw.get("scores") is not None else kw["width"]
+        need = candidate_pool_workspace_size(cand.shape[0], width, kw.get("block_rows", 8), cand.shape[1])
+        kw["workspace"] = torch.empty(max(need, 1), dtype=torch.uint8, device=pos.device)
+    p = _prepare("csa2_candidate_pool", lambda: candidate_pool(*args, stream=stream, **kw), stream)
+    p.workspace = kw["workspace"]
+    return p

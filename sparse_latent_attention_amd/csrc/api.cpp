@@ -12,6 +12,11 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Rows per pooled block of the candidate pool: a power of two in 4..64.
+bool pool_block_ok(int32_t b) { return b >= 4 && b <= 64 && (b & (b - 1)) == 0; }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
 size_t elem_bytes(int dtype) {
     switch (dtype) {
         case CSA2_F32: return 4;
@@ -70,13 +75,17 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
     if (reindex) {
         if (a->cand == nullptr || a->n_blocks <= 0 || a->block_rows <= 0 || a->block_rows > 64) return CSA2_ERR_INVALID_ARG;
         if (a->width != (int64_t)a->n_blocks * a->block_rows) return CSA2_ERR_INVALID_ARG;
+        if (a->block_max != nullptr) return CSA2_ERR_INVALID_ARG;
+    } else if (a->block_max != nullptr && !pool_block_ok(a->block_rows)) {
+        return CSA2_ERR_INVALID_ARG;
     }
     if (a->rows == 0 || a->width == 0) return CSA2_OK;
     if (a->q == nullptr || a->w == nullptr || a->k == nullptr || a->row_base == nullptr || a->pos == nullptr ||
         a->scores == nullptr)
         return CSA2_ERR_INVALID_ARG;
     if ((a->k_dtype == CSA2_FP8_E4M3) != (a->k_scale != nullptr)) return CSA2_ERR_INVALID_ARG;
-    if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->scores, 4) || !aligned(a->w, 4))
+    if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->scores, 4) || !aligned(a->w, 4) ||
+        !aligned(a->block_max, 4))
         return CSA2_ERR_INVALID_ARG;
     if (!isfinite(a->scale)) return CSA2_ERR_INVALID_ARG;
 
@@ -85,6 +94,9 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
     p.cand = reindex ? a->cand : nullptr; p.scores = a->scores; p.key_hist = a->key_hist; p.width = a->width;
     p.n_blocks = reindex ? a->n_blocks : 0; p.block_rows = reindex ? a->block_rows : 1; p.ratio = a->ratio;
     p.scale = a->scale;
+    p.block_max = reindex ? nullptr : a->block_max;
+    p.bm_rows = p.block_max != nullptr ? a->block_rows : 4;
+    p.bm_blocks = (a->width + p.bm_rows - 1) / p.bm_rows;
     // Columns per workgroup: multiples of 256 (4 waves x 64), aiming at ~4096 workgroups.
     const int64_t work = a->width * (int64_t)a->rows;
     int64_t per = (work + 256LL * 4096 - 1) / (256LL * 4096);
@@ -122,7 +134,46 @@ int32_t csa2_topk_select(const csa2_topk_args* a, void* workspace, size_t worksp
     p.key_hist = a->key_hist;
     p.width = a->width; p.k = a->k; p.ratio = a->ratio; p.n_blocks = a->n_blocks;
     p.block_rows = a->n_blocks > 0 ? a->block_rows : 1;
+    p.col_group = 1;
     return hip_status(csa2::launch_topk_select(p, a->rows, workspace, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t csa2_candidate_pool_workspace_size(int32_t rows, int64_t width, int32_t block_rows, int32_t n_cand) {
+    (void)n_cand;
+    if (rows <= 0 || width <= 0 || width >= (1LL << 31) || !pool_block_ok(block_rows)) return 0;
+    const int64_t nb = (width + block_rows - 1) / block_rows;
+    return align256((size_t)rows * (size_t)nb * sizeof(float)) + csa2::topk_workspace_bytes(rows, nb);
+}
+
+int32_t csa2_candidate_pool(const csa2_pool_args* a, void* workspace, size_t workspace_bytes, csa2_stream_t stream) {
+    if (a == nullptr || a->struct_size < sizeof(csa2_pool_args)) return CSA2_ERR_INVALID_ARG;
+    if (a->rows < 0 || a->n_cand < 1 || a->n_cand > 2048 || a->width < 0 || a->width >= (1LL << 31))
+        return CSA2_ERR_INVALID_ARG;
+    if ((a->ratio != 1 && a->ratio != 2) || !pool_block_ok(a->block_rows)) return CSA2_ERR_INVALID_ARG;
+    const size_t need = csa2_candidate_pool_workspace_size(a->rows, a->width, a->block_rows, a->n_cand);
+    if (workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 256))) return CSA2_ERR_INVALID_ARG;
+    if (a->rows == 0) return CSA2_OK;
+    if (a->pos == nullptr || a->cand == nullptr) return CSA2_ERR_INVALID_ARG;
+    if (a->width > 0 && a->scores == nullptr && a->block_max == nullptr) return CSA2_ERR_INVALID_ARG;
+    if (!aligned(a->scores, 4) || !aligned(a->block_max, 4)) return CSA2_ERR_INVALID_ARG;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int64_t nb = (a->width + a->block_rows - 1) / a->block_rows;
+    const float* bmax = a->block_max;
+    char* ws = static_cast<char*>(workspace);
+    if (bmax == nullptr && nb > 0) {
+        float* buf = reinterpret_cast<float*>(ws);
+        const hipError_t e = csa2::launch_block_max(a->scores, a->pos, a->ratio, a->width, a->block_rows, a->rows,
+                                                    buf, st);
+        if (e != hipSuccess) return CSA2_ERR_HIP;
+        bmax = buf;
+    }
+    csa2::TopkParams p;
+    p.scores = bmax; p.pos = a->pos; p.cand = nullptr; p.out = a->cand; p.key_hist = nullptr;
+    p.width = nb; p.k = a->n_cand; p.ratio = a->ratio; p.n_blocks = 0; p.block_rows = 1;
+    p.col_group = a->block_rows;
+    void* tws = need > 0 ? ws + align256((size_t)a->rows * (size_t)nb * sizeof(float)) : nullptr;
+    return hip_status(csa2::launch_topk_select(p, a->rows, tws, st));
 }
 
 static int32_t validate_attn(const csa2_attn_args* a, bool decode) {

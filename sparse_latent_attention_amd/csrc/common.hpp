@@ -27,6 +27,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kPosInf = __builtin_huge_valf();
+constexpr float kFltMax = 3.40282346638528859812e+38f;
+
+// A score as the candidate pool ranks it: NaN as -inf, +-inf clipped to +-FLT_MAX.
+__device__ __forceinline__ float pool_value(float x) {
+    return __builtin_isnan(x) ? kNegInf : fminf(fmaxf(x, -kFltMax), kFltMax);
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
 

@@ -47,14 +47,10 @@ __device__ __forceinline__ bool column_row(const IndexParams& p, int r, int64_t 
     return jr < nv;
 }
 
-// 16-byte load of key-row bytes.  (Non-temporal loads were measured here and
+// 16-byte load of key-row bytes.  (Non-temporal loads were measured and
 // rejected: with each 128-byte row read as two 64-byte halves by separate
 // instructions they ran ~12% slower than ordinary loads.)
-template <bool NT>
-__device__ __forceinline__ u32x4 ld16(const void* p) {
-    if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return *reinterpret_cast<const u32x4*>(p);
-}
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // Element-type specific operand loaders.  A "step" covers 32 k-elements for
 // F32/BF16 (one 16x16x32 MFMA) and all 128 for FP8 (one 16x16x128 MFMA).
@@ -66,10 +62,9 @@ struct IdxOps<CSA2_BF16, DI> {
     static constexpr int kSteps = DI / 32;
     typedef bf16x8 Frag;
     // k-group g of step s: elements 32s + 8g .. +8 (64 contiguous bytes per row per step)
-    template <bool NT = false>
     static __device__ __forceinline__ Frag load(const void* base, int64_t row, int s, int g) {
         const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + row * DI + 32 * s + 8 * g;
-        return __builtin_bit_cast(Frag, ld16<NT>(p));
+        return __builtin_bit_cast(Frag, ld16(p));
     }
     static __device__ __forceinline__ Frag zero() { return __builtin_bit_cast(Frag, u32x4{0, 0, 0, 0}); }
     static __device__ __forceinline__ f32x4 mma(f32x4 c, Frag a, Frag b) { return Mma<__bf16>::k32(c, a, b); }
@@ -79,12 +74,11 @@ template <int DI>
 struct IdxOps<CSA2_F32, DI> {
     static constexpr int kSteps = DI / 32;
     typedef F32x8 Frag;
-    template <bool NT = false>
     static __device__ __forceinline__ Frag load(const void* base, int64_t row, int s, int g) {
         const float* p = reinterpret_cast<const float*>(base) + row * DI + 32 * s + 8 * g;
         Frag f;
-        f32x4 a = __builtin_bit_cast(f32x4, ld16<NT>(p));
-        f32x4 b = __builtin_bit_cast(f32x4, ld16<NT>(p + 4));
+        f32x4 a = __builtin_bit_cast(f32x4, ld16(p));
+        f32x4 b = __builtin_bit_cast(f32x4, ld16(p + 4));
         f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
         f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
         return f;
@@ -104,11 +98,10 @@ struct IdxOps<CSA2_FP8_E4M3, 128> {
     typedef i32x8 Frag;
     // k-group g holds bytes 16g..16g+15 and 64+16g..64+16g+15 of the row, so each
     // of the two loads covers 64 contiguous bytes per row across the 4 groups.
-    template <bool NT = false>
     static __device__ __forceinline__ Frag load(const void* base, int64_t row, int, int g) {
         const uint8_t* p = reinterpret_cast<const uint8_t*>(base) + row * 128 + 16 * g;
-        u32x4 a = ld16<NT>(p);
-        u32x4 b = ld16<NT>(p + 64);
+        u32x4 a = ld16(p);
+        u32x4 b = ld16(p + 64);
         Frag f;
         f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
         f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
@@ -120,7 +113,7 @@ struct IdxOps<CSA2_FP8_E4M3, 128> {
 
 }  // namespace
 
-template <int KT, int HI, int DI, bool REINDEX, bool HIST, bool NT>
+template <int KT, int HI, int DI, bool REINDEX, bool HIST, bool BMAX>
 __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p) {
     // Per-workgroup histogram of the score keys' top 12 bits (one row per workgroup).
     __shared__ uint32_t hist[HIST ? kKeyBins : 1];
@@ -178,7 +171,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p)
             int64_t prow = 0;
             const bool valid = (c < c_end) && column_row<REINDEX>(p, r, c, nv, base, prow);
 #pragma unroll
-            for (int s = 0; s < S; ++s) st.kb[u][s] = valid ? Ops::template load<NT>(p.k, prow, s, g) : Ops::zero();
+            for (int s = 0; s < S; ++s) st.kb[u][s] = valid ? Ops::load(p.k, prow, s, g) : Ops::zero();
         }
         const int64_t c_out = cb + lane;
         int64_t prow = 0;
@@ -211,10 +204,21 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p)
         float kk = mid ? k1 : k0;
         kk += shfl_xor(mid ? k0 : k1, 16);
         const int64_t c_out = cb + lane;
+        const float score = st.valid ? st.sc * kk : kNegInf;
         if (c_out < c_end) {
-            const float score = st.valid ? st.sc * kk : kNegInf;
             srow[c_out] = score;
             if (HIST && st.valid) atomicAdd(&hist[order_key(score) >> 20], 1u);
+        }
+        if (BMAX) {
+            // Block score over bm_rows consecutive columns = lanes (blocks never
+            // straddle a 64-column step): NaN as -inf, infinities clipped, invalid
+            // columns -inf; the block of the newest visible row is pinned to +inf.
+            float bm = st.valid ? pool_value(score) : kNegInf;
+            for (int o = 1; o < p.bm_rows; o <<= 1) bm = fmaxf(bm, shfl_xor(bm, o));
+            if ((lane & (p.bm_rows - 1)) == 0 && c_out < c_end) {
+                const int64_t blk = c_out / p.bm_rows;
+                p.block_max[(int64_t)r * p.bm_blocks + blk] = (blk == (nv - 1) / p.bm_rows) ? kPosInf : bm;
+            }
         }
     };
 
@@ -233,6 +237,8 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p)
     for (; cb < c_end; cb += 256) {  // nothing visible in these columns
         const int64_t c_out = cb + lane;
         if (c_out < c_end) srow[c_out] = kNegInf;
+        if (BMAX && (lane & (p.bm_rows - 1)) == 0 && c_out < c_end)
+            p.block_max[(int64_t)r * p.bm_blocks + c_out / p.bm_rows] = kNegInf;
     }
     if (HIST) {
         __syncthreads();
@@ -251,17 +257,22 @@ template <int KT, int HI, int DI, bool REINDEX>
 static hipError_t launch_one(const IndexParams& p, int rows, hipStream_t stream) {
     const int64_t chunks = (p.width + p.cols_per_wg - 1) / p.cols_per_wg;
     dim3 grid((unsigned)chunks, (unsigned)rows);
-    const bool nt = false;  // see ld16
-    if (p.key_hist != nullptr) {
+    const bool hist = p.key_hist != nullptr;
+    const bool bmax = !REINDEX && p.block_max != nullptr;
+    if (hist) {
         const int64_t nh = (int64_t)rows * kKeyBins;
         hipLaunchKernelGGL(key_hist_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)),
                            dim3(256), 0, stream, p.key_hist, nh);
-        if (nt) hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, REINDEX, true, true>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, REINDEX, true, false>), grid, dim3(256), 0, stream, p);
-    } else {
-        if (nt) hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, REINDEX, false, true>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, REINDEX, false, false>), grid, dim3(256), 0, stream, p);
     }
+    if constexpr (!REINDEX) {
+        if (bmax) {
+            if (hist) hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, false, true, true>), grid, dim3(256), 0, stream, p);
+            else hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, false, false, true>), grid, dim3(256), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
+    if (hist) hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, REINDEX, true, false>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((indexer_score_kernel<KT, HI, DI, REINDEX, false, false>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -18,10 +18,13 @@ struct IndexParams {
     const int32_t* cand;
     float* scores;
     uint32_t* key_hist;  // optional [rows, 4096]
+    float* block_max;    // optional [rows, bm_blocks] (FULL only)
     int64_t width;
     int64_t cols_per_wg;
+    int64_t bm_blocks;   // ceil(width / bm_rows)
     int32_t n_blocks;
     int32_t block_rows;
+    int32_t bm_rows;     // rows per pooled block (power of two, 4..64)
     int32_t ratio;
     float scale;
 };
@@ -41,11 +44,16 @@ struct TopkParams {
     int32_t ratio;
     int32_t n_blocks;  // 0: FULL validity
     int32_t block_rows;
+    int32_t col_group;  // FULL validity over groups: column c valid iff c < ceil(n_visible / col_group)
 };
 
 // Bytes of workspace the launch plan for (rows, width) needs (0: one workgroup per row).
 size_t topk_workspace_bytes(int rows, int64_t width);
 hipError_t launch_topk_select(const TopkParams& p, int rows, void* workspace, hipStream_t stream);
+
+// Block scores of the candidate pool from FULL score rows (out: [rows, nb]).
+hipError_t launch_block_max(const float* scores, const int64_t* pos, int ratio, int64_t width, int block_rows,
+                            int rows, float* out, hipStream_t stream);
 
 struct AttnParams {
     const void* q;

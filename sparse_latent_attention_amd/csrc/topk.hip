@@ -256,6 +256,7 @@ __device__ __forceinline__ RowSrc row_src(const TopkParams& p, int r) {
     src.p = &p;
     src.r = r;
     src.nv = (p.pos[r] + 1) / p.ratio;
+    if (p.col_group > 1) src.nv = (src.nv + p.col_group - 1) / p.col_group;
     src.srow = p.scores + (int64_t)r * p.width;
     src.n = (p.n_blocks == 0) ? (int)(src.nv < p.width ? src.nv : p.width) : (int)p.width;
     return src;

@@ -75,7 +75,7 @@ def index_scale(cfg):
     return 1.0 / (math.sqrt(cfg.idx_dim) * math.sqrt(cfg.idx_heads))
 
 
-def gpu_scores(cfg, x, key_hist=None):
+def gpu_scores(cfg, x, key_hist=None, block_max=None):
     import sparse_latent_attention_amd as csa2
     rows = x["pos"].shape[0]
     scores = torch.empty(rows, cfg.width, dtype=torch.float32, device=x["pos"].device)
@@ -83,7 +83,7 @@ def gpu_scores(cfg, x, key_hist=None):
     ks = None if x["kI_scale"] is None else x["kI_scale"].reshape(-1)
     csa2.indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, index_scale(cfg), scores,
                        k_scale=ks, cand=x.get("cand"), block_rows=cfg.block_rows, fp8=cfg.idx_dtype == "fp8",
-                       key_hist=key_hist)
+                       key_hist=key_hist, block_max=block_max)
     return scores
 
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(csa2.EXPORTED)
-    assert csa2.ABI_VERSION == 1
+    assert csa2.ABI_VERSION == 2
 
 
 def test_struct_layouts_match_c_compiler():
@@ -42,7 +42,9 @@ int main(void) {
   printf("csa2_index_args sizeof %zu\n", sizeof(csa2_index_args));
   printf("csa2_topk_args sizeof %zu\n", sizeof(csa2_topk_args));
   printf("csa2_attn_args sizeof %zu\n", sizeof(csa2_attn_args));
-  F(csa2_index_args, width) F(csa2_index_args, q) F(csa2_index_args, cand) F(csa2_index_args, scale) F(csa2_index_args, scores) F(csa2_index_args, key_hist)
+  printf("csa2_pool_args sizeof %zu\n", sizeof(csa2_pool_args));
+  F(csa2_index_args, width) F(csa2_index_args, q) F(csa2_index_args, cand) F(csa2_index_args, scale) F(csa2_index_args, scores) F(csa2_index_args, key_hist) F(csa2_index_args, block_max)
+  F(csa2_pool_args, n_cand) F(csa2_pool_args, width) F(csa2_pool_args, scores) F(csa2_pool_args, block_max) F(csa2_pool_args, pos) F(csa2_pool_args, cand)
   F(csa2_topk_args, width) F(csa2_topk_args, scores) F(csa2_topk_args, out) F(csa2_topk_args, key_hist)
   F(csa2_attn_args, swa_rows) F(csa2_attn_args, q) F(csa2_attn_args, rope_inv_freq) F(csa2_attn_args, softmax_scale) F(csa2_attn_args, out)
   return 0;
@@ -54,7 +56,8 @@ int main(void) {
         open(src, "w").write(prog)
         subprocess.run(["gcc", "-I", os.path.dirname(HEADER), src, "-o", exe], check=True)
         out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
-    cls = {"csa2_index_args": csa2.IndexArgs, "csa2_topk_args": csa2.TopkArgs, "csa2_attn_args": csa2.AttnArgs}
+    cls = {"csa2_index_args": csa2.IndexArgs, "csa2_topk_args": csa2.TopkArgs, "csa2_attn_args": csa2.AttnArgs,
+           "csa2_pool_args": csa2.PoolArgs}
     for line in out.strip().splitlines():
         t, f, v = line.split()
         if f == "sizeof":
@@ -98,6 +101,54 @@ def test_indexer_reindex_width_must_match_pool():
     assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
     a = _index_args(mode=csa2.MODE_REINDEX, cand=None, n_blocks=2048, block_rows=8, width=16384)
     assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+
+
+def test_indexer_block_max_rules():
+    # REINDEX has no block scores; FULL block heights are powers of two in 4..64
+    a = _index_args(mode=csa2.MODE_REINDEX, cand=ctypes.c_void_p(0x1000), n_blocks=4, block_rows=8, width=32,
+                    block_max=ctypes.c_void_p(0x1000))
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+    for b in (0, 2, 6, 128):
+        a = _index_args(block_rows=b, block_max=ctypes.c_void_p(0x1000))
+        assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG, b
+    a = _index_args(block_rows=8, block_max=ctypes.c_void_p(0x1002))
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+
+
+def _pool_args(**kw):
+    a = csa2.PoolArgs()
+    a.struct_size = ctypes.sizeof(csa2.PoolArgs)
+    a.rows, a.ratio, a.block_rows, a.n_cand, a.width = 4, 1, 8, 2048, 1 << 20
+    a.scores = a.pos = a.cand = ctypes.c_void_p(0x1000)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("struct_size", 8, csa2.ERR_INVALID_ARG), ("n_cand", 0, csa2.ERR_INVALID_ARG),
+    ("n_cand", 4096, csa2.ERR_INVALID_ARG), ("block_rows", 6, csa2.ERR_INVALID_ARG),
+    ("block_rows", 2, csa2.ERR_INVALID_ARG), ("block_rows", 128, csa2.ERR_INVALID_ARG),
+    ("ratio", 3, csa2.ERR_INVALID_ARG), ("width", 1 << 31, csa2.ERR_INVALID_ARG),
+    ("scores", None, csa2.ERR_INVALID_ARG), ("cand", None, csa2.ERR_INVALID_ARG),
+])
+def test_candidate_pool_validation(field, value, status):
+    a = _pool_args(**{field: value})
+    ws = csa2.candidate_pool_workspace_size(4, 1 << 20, 8, 2048)
+    # every case is rejected on the host, before any launch
+    assert csa2._lib.csa2_candidate_pool(ctypes.byref(a), ctypes.c_void_p(0x10000), ws, None) == status
+
+
+def test_candidate_pool_workspace_rules():
+    ws = csa2.candidate_pool_workspace_size(4, 1 << 20, 8, 2048)
+    assert ws >= 4 * (1 << 17) * 4                     # room for the block scores it may compute
+    a = _pool_args()
+    assert csa2._lib.csa2_candidate_pool(ctypes.byref(a), ctypes.c_void_p(0x10000), ws - 1, None) == \
+        csa2.ERR_WORKSPACE
+    assert csa2._lib.csa2_candidate_pool(ctypes.byref(a), ctypes.c_void_p(0x10010), ws, None) == \
+        csa2.ERR_INVALID_ARG                            # workspace must be 256-byte aligned
+    a = _pool_args(rows=0)
+    assert csa2._lib.csa2_candidate_pool(ctypes.byref(a), None, 0, None) == csa2.OK
 
 
 def test_empty_calls_launch_nothing():

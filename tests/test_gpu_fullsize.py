@@ -20,7 +20,8 @@ from harness import (BF16_ATOL, BF16_RTOL, F32_ATOL, F32_RTOL, SCORE_TOL, assert
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ["tiny_full_fp32", "full_decode_64k", "prefill_4096_at_128k", "reindex_decode_1m", "lowp_full_decode_1m"]
+NAMES = ["tiny_full_fp32", "full_decode_64k", "prefill_4096_at_128k", "reindex_decode_1m", "lowp_full_decode_1m",
+         "lowp_pool_decode_1m"]
 
 
 def _run_path(cfg, x):
@@ -39,12 +40,19 @@ def _run_path(cfg, x):
     akw = dict(rope_dim=cfg.rope_dim, kv_fp4=cfg.main_dtype == "fp4", swa_fp8=cfg.swa_dtype == "fp8", kv_scale=kvs)
     key_hist = (torch.empty(rows, 4096, dtype=torch.int32, device=dev)
                 if csa2.topk_uses_key_hist(rows, cfg.width, cfg.topk) else None)
+    block_max = pool = None
+    if cfg.pool_blocks:
+        block_max = torch.empty(rows, -(-cfg.width // cfg.block_rows), dtype=torch.float32, device=dev)
+        pool = torch.empty(rows, cfg.pool_blocks, dtype=torch.int32, device=dev)
     calls = [csa2.prepare_indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio,
                                         1.0 / math.sqrt(cfg.idx_dim * cfg.idx_heads), scores, k_scale=kIs,
                                         cand=x.get("cand"), block_rows=cfg.block_rows, fp8=cfg.idx_dtype == "fp8",
-                                        key_hist=key_hist),
+                                        key_hist=key_hist, block_max=block_max),
              csa2.prepare_topk_select(scores, x["pos"], cfg.ratio, idx, cand=x.get("cand"), block_rows=cfg.block_rows,
                                       key_hist=key_hist)]
+    if cfg.pool_blocks:
+        calls.append(csa2.prepare_candidate_pool(x["pos"], cfg.ratio, pool, block_max=block_max, width=cfg.width,
+                                                 block_rows=cfg.block_rows))
     tau = 1.0 / math.sqrt(cfg.dim)
     for li, L in enumerate(x["layers"]):
         if cfg.phase == "decode":
@@ -59,6 +67,7 @@ def _run_path(cfg, x):
     for c in calls:
         c()
     torch.cuda.synchronize()
+    x["_pool"] = pool
     return scores, idx, outs
 
 
@@ -128,3 +137,27 @@ def test_sampled_rows_scores_topk_attention(full):
         ref = oracle_attention(cfg, x, gi, rows, layer=layer)
         e = assert_close(o[torch.from_numpy(rows).cuda()], ref, atol, rtol, f"{cfg.name} layer {layer}")
         print(f"[{cfg.name}] layer {layer} attention max_abs {e:.3e}")
+
+
+def test_candidate_pool(full):
+    """Every row: the pool is well formed, keeps the newest block and every FULL top-k row's block
+    (soundness on the GPU's own scores); sampled rows: bit-exact with the oracle's pool of the GPU scores."""
+    cfg, x, scores, idx, _ = full
+    if not cfg.pool_blocks:
+        pytest.skip("this workload builds no candidate pool")
+    pool = x["_pool"].cpu().numpy()
+    ii = idx.cpu().numpy()
+    pos = x["pos"].cpu().numpy()
+    B = cfg.block_rows
+    for r in range(pool.shape[0]):
+        nv = min((int(pos[r]) + 1) // cfg.ratio, cfg.width)
+        v = pool[r][pool[r] >= 0]
+        assert np.all(pool[r][len(v):] == -1) and np.all(np.diff(v) > 0)
+        assert len(v) == min(cfg.pool_blocks, -(-nv // B))
+        assert (nv - 1) // B in set(v.tolist())
+        kept = set(v.tolist())
+        assert all(int(c) // B in kept for c in ii[r] if c >= 0)
+    rows = _sample_rows(cfg)
+    s_gpu = scores[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    ref = oracle.candidates.candidate_pool(s_gpu, pos[rows], cfg.ratio, B, cfg.pool_blocks)
+    assert np.array_equal(pool[rows], ref)

@@ -39,6 +39,7 @@ class Csa2Config:
     out_dtype: str = "bf16"    # f32 | bf16
     value_scale: str = "unit"  # "unit": N(0,1); "inv_sqrt_d": N(0,1)/sqrt(dim) for q, latent and index vectors
     ragged: bool = False       # decode: per-sequence positions drawn in [window, context-1]
+    pool_blocks: int = 0       # FULL owner layer: candidate blocks it also builds for REINDEX layers (0: none)
 
     @property
     def n_main_rows(self):
@@ -79,10 +80,16 @@ CONFIGS = {
     "lowp_full_decode_1m": Csa2Config(
         name="lowp_full_decode_1m", phase="decode", index_mode="full", batch=64, q_tokens=64, context=1 << 20,
         ratio=1, main_dtype="fp4", swa_dtype="fp8", idx_dtype="fp8", value_scale="inv_sqrt_d", **_COMMON),
+    # The same decode step as the decoder's FULL owner layer runs it: besides its own top-512 it keeps
+    # the 2048 best 8-row blocks as the candidate pool of the REINDEX layers.
+    "lowp_pool_decode_1m": Csa2Config(
+        name="lowp_pool_decode_1m", phase="decode", index_mode="full", batch=64, q_tokens=64, context=1 << 20,
+        ratio=1, main_dtype="fp4", swa_dtype="fp8", idx_dtype="fp8", value_scale="inv_sqrt_d", pool_blocks=2048,
+        **_COMMON),
 }
 
 CONFIG_ORDER = ["tiny_full_fp32", "full_decode_64k", "prefill_4096_at_128k", "reindex_decode_1m",
-                "lowp_full_decode_1m"]
+                "lowp_full_decode_1m", "lowp_pool_decode_1m"]
 
 
 def get_config(name):
