@@ -6,8 +6,10 @@
 A step is one pass of the whole path over one batch of synthetic inputs that
 are already resident in HBM:
   decode  : indexer_score -> topk_select -> sparse_attn_decode
-            (a FULL owner layer that builds the REINDEX candidate pool adds
-            candidate_pool from the block scores the indexer wrote)
+            (wide FULL rows with an FP8 index plane keep their scores on chip:
+            indexer_score(scores=None) -> topk_rescore; a FULL owner layer that
+            builds the REINDEX candidate pool adds candidate_pool from the block
+            scores the indexer wrote)
   prefill : indexer_score -> topk_select -> sparse_attn_prefill for the FULL
             layer and every REUSE layer (same indices, own q / SWA / sink)
 The default workload is the 1M-context low-precision decode (64 sequences,
@@ -42,7 +44,7 @@ def _unique_plane_rows(base, rows_read):
     return int(torch.unique(torch.cat(seen)).numel()) if seen else 0
 
 
-def algorithmic_work(cfg, x, idx_host=None):
+def algorithmic_work(cfg, x, idx_host=None, score_free=False):
     """Per kernel of one step: the bytes it must move at least once (every distinct input byte read
     once, every output byte written once) and the multiply-add flops it must do.
 
@@ -69,9 +71,17 @@ def algorithmic_work(cfg, x, idx_host=None):
         unique_rows = sum(int(nv[base == b].max()) for b in torch.unique(base))
         extra = 0
     nbm = -(-cfg.width // cfg.block_rows) if cfg.pool_blocks else 0
-    idx_bytes = unique_rows * idx_row + qI + extra + rows * cfg.width * 4 + rows * nbm * 4
+    if score_free:
+        # scores stay on chip: the key histogram and the 8-column block keys are written instead
+        nbk = -(-cfg.width // 8)
+        idx_bytes = unique_rows * idx_row + qI + rows * nbm * 4 + rows * (nbk + 4096) * 4
+        # the select reads the histogram and block keys (re-scored candidate rows are not counted:
+        # they are extra work of this route, not bytes the result needs)
+        topk_bytes = rows * (nbk + 4096) * 4 + rows * cfg.topk * 4
+    else:
+        idx_bytes = unique_rows * idx_row + qI + extra + rows * cfg.width * 4 + rows * nbm * 4
+        topk_bytes = rows * cfg.width * 4 + rows * cfg.topk * 4 + extra
     idx_flops = 2 * scored * cfg.idx_heads * cfg.idx_dim
-    topk_bytes = rows * cfg.width * 4 + rows * cfg.topk * 4 + extra
     main_row = cfg.dim // 2 + cfg.dim // 32 if cfg.main_dtype == "fp4" else cfg.dim * _ELEM[cfg.main_dtype]
     swa_row = cfg.dim * _ELEM[cfg.swa_dtype] + (4 if cfg.swa_dtype == "fp8" else 0)
     sel = torch.minimum(nv, torch.tensor(cfg.topk))
@@ -230,8 +240,8 @@ def main():
         sys.exit(2)
 
     import torch
-    import sparse_latent_attention_amd as csa2
     from workloads import CONFIGS, make_inputs
+    from workloads.step import Step
 
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")
@@ -241,69 +251,25 @@ def main():
     torch.cuda.synchronize()
 
     rows = x["pos"].shape[0]
-    scores = torch.empty(rows, cfg.width, dtype=torch.float32, device=dev)
-    idx = torch.empty(rows, cfg.topk, dtype=torch.int32, device=dev)
-    outs = [torch.empty_like(L["q"]) for L in x["layers"]]
-    freqs = csa2.rope_inv_freq(cfg.rope_dim, cfg.rope_theta, cfg.yarn_factor, cfg.yarn_orig).to(dev)
-    kI = x["kI"].reshape(-1, cfg.idx_dim)
-    kIs = None if x["kI_scale"] is None else x["kI_scale"].reshape(-1)
-    kv = x["main"].reshape(-1, x["main"].shape[-1])
-    kvs = None if x["main_scale"] is None else x["main_scale"].reshape(-1, x["main_scale"].shape[-1])
-    tau_i = 1.0 / math.sqrt(cfg.idx_dim * cfg.idx_heads)
-    tau = 1.0 / math.sqrt(cfg.dim)
-    akw = dict(rope_dim=cfg.rope_dim, kv_fp4=cfg.main_dtype == "fp4", swa_fp8=cfg.swa_dtype == "fp8", kv_scale=kvs)
-    topk_ws = torch.empty(max(csa2.topk_workspace_size(rows, cfg.width, cfg.topk), 1), dtype=torch.uint8, device=dev)
-
-    names = ["indexer_score", "topk_select"] + (["candidate_pool"] if cfg.pool_blocks else []) + ["sparse_attn"]
-    evs = {n: [] for n in names}
     # Arguments are marshalled once; each step only crosses into the library.
-    # The indexer also builds the score-key histogram when top-k takes its wide-row path.
-    key_hist = (torch.empty(rows, 4096, dtype=torch.int32, device=dev)
-                if csa2.topk_uses_key_hist(rows, cfg.width, cfg.topk) else None)
-    block_max = pool = call_pool = None
-    if cfg.pool_blocks:
-        block_max = torch.empty(rows, -(-cfg.width // cfg.block_rows), dtype=torch.float32, device=dev)
-        pool = torch.empty(rows, cfg.pool_blocks, dtype=torch.int32, device=dev)
-        call_pool = csa2.prepare_candidate_pool(x["pos"], cfg.ratio, pool, block_max=block_max, width=cfg.width,
-                                                block_rows=cfg.block_rows)
-    call_idx = csa2.prepare_indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, tau_i, scores,
-                                          k_scale=kIs, cand=x.get("cand"), block_rows=cfg.block_rows,
-                                          fp8=cfg.idx_dtype == "fp8", key_hist=key_hist, block_max=block_max)
-    call_topk = csa2.prepare_topk_select(scores, x["pos"], cfg.ratio, idx, cand=x.get("cand"),
-                                         block_rows=cfg.block_rows, workspace=topk_ws, key_hist=key_hist)
-    call_attn = []
-    for li, L in enumerate(x["layers"]):
-        if cfg.phase == "decode":
-            call_attn.append(csa2.prepare_sparse_attn_decode(
-                L["q"], x["pos"], idx, kv, x["kv_row_base"], x["swa"], L["sink"], freqs, cfg.ratio, cfg.window, tau,
-                outs[li], swa_scale=x["swa_scale"], **akw))
-        else:
-            call_attn.append(csa2.prepare_sparse_attn_prefill(
-                L["q"], x["pos"], idx, kv, L["swa"], x["swa_pos0"], L["sink"], freqs, cfg.ratio, cfg.window, tau,
-                outs[li], swa_scale=L["swa_scale"], kv_row_base=x["kv_row_base"], **akw))
+    step_calls = Step(cfg, x)
+    names = list(step_calls.groups)
+    evs = {n: [] for n in names}
 
     def step(record):
-        def ev():
+        if not record:
+            step_calls()
+            return
+        marks = []
+
+        def mark(name):
             e = torch.cuda.Event(enable_timing=True)
             e.record()
-            return e
-        e0 = ev() if record else None
-        call_idx()
-        e1 = ev() if record else None
-        call_topk()
-        e2 = ev() if record else None
-        if call_pool is not None:
-            call_pool()
-        e2p = ev() if record and call_pool is not None else e2
-        for c in call_attn:
-            c()
-        e3 = ev() if record else None
-        if record:
-            evs["indexer_score"].append((e0, e1))
-            evs["topk_select"].append((e1, e2))
-            if call_pool is not None:
-                evs["candidate_pool"].append((e2, e2p))
-            evs["sparse_attn"].append((e2p, e3))
+            marks.append((name, e))
+
+        step_calls(mark)
+        for (name, a), (_, b) in zip(marks[:-1], marks[1:]):
+            evs[name].append((a, b))
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -318,7 +284,7 @@ def main():
     ms_step = wall * 1e3 / args.steps
     kern_ms = {n: sum(a.elapsed_time(b) for a, b in evs[n]) / args.steps for n in names}
 
-    work = algorithmic_work(cfg, x, idx.cpu() if cfg.phase == "prefill" else None)
+    work = algorithmic_work(cfg, x, step_calls.idx.cpu() if cfg.phase == "prefill" else None, step_calls.score_free)
     dominant = max(names, key=lambda n: kern_ms[n])
     roofline = roofline_of(work[dominant], kern_ms[dominant])
     roofline.update({"kernel": dominant, "traffic": measured_traffic(dominant, cfg.name),
@@ -336,7 +302,8 @@ def main():
         "config": {"workload": cfg.name, "sequences": cfg.batch, "query_rows": rows, "context": cfg.context,
                    "ratio": cfg.ratio, "heads": cfg.heads, "dim": cfg.dim, "topk": cfg.topk, "window": cfg.window,
                    "index": f"{cfg.index_mode} {cfg.idx_heads}x{cfg.idx_dim} {cfg.idx_dtype}",
-                   "main_kv": cfg.main_dtype, "swa": cfg.swa_dtype, "attention_layers": len(x["layers"])},
+                   "main_kv": cfg.main_dtype, "swa": cfg.swa_dtype, "attention_layers": len(x["layers"]),
+                   "topk_route": "score-free (topk_rescore)" if step_calls.score_free else "scores + topk_select"},
         "kernels_ms": {n: round(v, 4) for n, v in kern_ms.items()},
         "kernels_roofline": {n: roofline_of(work[n], kern_ms[n]) for n in names},
         "roofline": roofline,

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 2
+#define CSA2_ABI_VERSION 3
 
 /* Status codes. */
 #define CSA2_OK 0
@@ -127,7 +127,8 @@ typedef struct csa2_index_args {
     const int32_t* cand;        /* REINDEX: [rows, n_blocks] block ids, ascending, -1 padded; else NULL */
     float scale;                /* score scale (dim^-1/2 * heads^-1/2 in the pages' model) */
     int32_t _pad1;
-    float* scores;              /* out: [rows, width] float32 */
+    float* scores;              /* out: [rows, width] float32; NULL selects score-free mode (see
+                                 * csa2_topk_rescore) */
     uint32_t* key_hist;         /* optional out: [rows, 4096], or NULL.  The call zeroes it, then
                                  * counts every valid score of row r in bin key(score) >> 20, where
                                  * key is the order-preserving 32-bit key csa2_topk_select ranks by
@@ -141,9 +142,38 @@ typedef struct csa2_index_args {
                                  * visible row ((n_visible - 1) / block_rows) gets +inf; blocks with
                                  * no visible column get -inf.  Written in the same pass as the
                                  * scores (no second read of them). */
+    uint32_t* block_keys;       /* score-free mode only (scores == NULL), out: [rows, ceil(width / 8)].
+                                 * Entry b holds the largest order key (as for key_hist) of the
+                                 * valid columns 8b .. 8b+7, or 0 when none is valid. */
 } csa2_index_args;
 
 int32_t csa2_indexer_score(const csa2_index_args* args, csa2_stream_t stream);
+
+/* Score-free FULL top-k.
+ *
+ * Writing a [rows, width] score matrix only to read it back for the top-k
+ * costs more than the scoring itself reads when rows are 1M columns wide.  In
+ * score-free mode (csa2_indexer_score with scores == NULL, which requires FULL
+ * mode, key_hist and block_keys) the scores stay on chip: the call writes the
+ * key histogram and the per-8-column block keys only.  csa2_topk_rescore then
+ * takes the same arguments and returns the top-k: from the histogram it finds
+ * the bin holding each row's k-th largest key, re-scores exactly the blocks
+ * whose block key reaches that bin (every selected column lies in one), with
+ * the same arithmetic as the scoring pass, and runs the exact select of
+ * csa2_topk_select over those columns.  The result is bit-identical to
+ * csa2_topk_select over the scores csa2_indexer_score would have written.
+ *
+ * args: as given to the score-free csa2_indexer_score call (key_hist and
+ * block_keys are now inputs; scores and block_max are ignored).
+ * out: [rows, k] int32, ascending plane rows, -1 padded.
+ * Supported: FP8-E4M3 q and k with (heads, dim) = (64, 128); 1 <= k <= 2048;
+ * width < 2^24 and wide enough that csa2_topk_select would split its rows
+ * (csa2_topk_workspace_size(rows, width, k) > 0), else CSA2_ERR_UNSUPPORTED.
+ */
+size_t csa2_topk_rescore_workspace_size(int32_t rows, int64_t width, int32_t k);
+
+int32_t csa2_topk_rescore(const csa2_index_args* args, int32_t k, int32_t* out, void* workspace,
+                          size_t workspace_bytes, csa2_stream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Per-row top-k of indexer scores.

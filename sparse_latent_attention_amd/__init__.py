@@ -43,6 +43,7 @@ class IndexArgs(ctypes.Structure):
         ("q_dtype", _i32), ("k_dtype", _i32), ("n_blocks", _i32), ("block_rows", _i32), ("_pad0", _i32),
         ("width", _i64), ("q", _vp), ("w", _vp), ("k", _vp), ("k_scale", _vp), ("row_base", _vp), ("pos", _vp),
         ("cand", _vp), ("scale", _f32), ("_pad1", _i32), ("scores", _vp), ("key_hist", _vp), ("block_max", _vp),
+        ("block_keys", _vp),
     ]
 
 
@@ -81,6 +82,10 @@ _lib.csa2_topk_workspace_size.restype = ctypes.c_size_t
 _lib.csa2_topk_workspace_size.argtypes = [_i32, _i64, _i32]
 _lib.csa2_topk_select.restype = _i32
 _lib.csa2_topk_select.argtypes = [ctypes.POINTER(TopkArgs), _vp, ctypes.c_size_t, _vp]
+_lib.csa2_topk_rescore_workspace_size.restype = ctypes.c_size_t
+_lib.csa2_topk_rescore_workspace_size.argtypes = [_i32, _i64, _i32]
+_lib.csa2_topk_rescore.restype = _i32
+_lib.csa2_topk_rescore.argtypes = [ctypes.POINTER(IndexArgs), _i32, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.csa2_candidate_pool_workspace_size.restype = ctypes.c_size_t
 _lib.csa2_candidate_pool_workspace_size.argtypes = [_i32, _i64, _i32, _i32]
 _lib.csa2_candidate_pool.restype = _i32
@@ -96,7 +101,8 @@ _lib.csa2_rope_inv_freq.argtypes = [_i32, ctypes.c_double, ctypes.c_double, _i64
 
 ABI_VERSION = _lib.csa2_abi_version()
 EXPORTED = ("csa2_abi_version", "csa2_status_string", "csa2_indexer_score", "csa2_topk_workspace_size",
-            "csa2_topk_select", "csa2_candidate_pool_workspace_size", "csa2_candidate_pool", "csa2_attn_workspace_size", "csa2_sparse_attn_decode", "csa2_sparse_attn_prefill",
+            "csa2_topk_select", "csa2_topk_rescore_workspace_size", "csa2_topk_rescore",
+            "csa2_candidate_pool_workspace_size", "csa2_candidate_pool", "csa2_attn_workspace_size", "csa2_sparse_attn_decode", "csa2_sparse_attn_prefill",
             "csa2_rope_inv_freq")
 
 
@@ -155,18 +161,9 @@ def rope_inv_freq(rope_dim, theta, yarn_factor=1.0, yarn_orig_len=0):
     return torch.tensor(list(out), dtype=torch.float64)
 
 
-def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None, cand=None, block_rows=8,
-                  fp8=False, key_hist=None, block_max=None, stream=None):
-    """Fills ``scores`` [rows, width] (float32).  REINDEX when ``cand`` is given.
-
-    q [rows, H_I, D_I] and k [*, D_I] are float32/bfloat16, or uint8 FP8-E4M3
-    codes with ``fp8=True`` (then ``k_scale`` [*] float32 is required and the
-    query scales are already folded into w).  ``key_hist`` (int32 [rows, 4096])
-    optionally receives the score-key histogram topk_select can reuse.
-    ``block_max`` (FULL only, float32 [rows, ceil(width / block_rows)])
-    optionally receives the candidate pool's block scores.
-    """
-    _dev(q, w, k, row_base, pos, scores, k_scale, cand, key_hist, block_max)
+def _index_args(q, w, k, row_base, pos, ratio, scale, scores, width, k_scale, cand, block_rows, fp8, key_hist,
+                block_max, block_keys):
+    _dev(q, w, k, row_base, pos, scores, k_scale, cand, key_hist, block_max, block_keys)
     if key_hist is not None and (key_hist.dtype != torch.int32 or tuple(key_hist.shape) != (q.shape[0], 4096)):
         raise ValueError("csa2.indexer_score: key_hist must be int32 [rows, 4096]")
     rows, heads, dim = q.shape
@@ -179,18 +176,21 @@ def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None,
         if k.dtype != q.dtype:
             raise ValueError("csa2: q and k must share a dtype")
     _need(w, torch.float32, "w")
-    _need(scores, torch.float32, "scores")
     _need(row_base, torch.int64, "row_base")
     _need(pos, torch.int64, "pos")
-    if w.shape != (rows, heads) or k.shape[-1] != dim or scores.shape[0] != rows or row_base.shape != (rows,) \
-            or pos.shape != (rows,):
+    if scores is not None:
+        _need(scores, torch.float32, "scores")
+        if scores.shape[0] != rows:
+            raise ValueError("csa2.indexer_score: scores rows")
+        width = scores.shape[1]
+    if w.shape != (rows, heads) or k.shape[-1] != dim or row_base.shape != (rows,) or pos.shape != (rows,):
         raise ValueError("csa2.indexer_score: inconsistent shapes")
     a = IndexArgs()
     a.struct_size = ctypes.sizeof(IndexArgs)
     a.mode = MODE_REINDEX if cand is not None else MODE_FULL
     a.rows, a.heads, a.dim, a.ratio = rows, heads, dim, int(ratio)
     a.q_dtype = a.k_dtype = code
-    a.width = scores.shape[1]
+    a.width = int(width)
     if cand is not None:
         _need(cand, torch.int32, "cand")
         if cand.shape[0] != rows:
@@ -202,13 +202,63 @@ def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None,
         if tuple(block_max.shape) != (rows, nb):
             raise ValueError(f"csa2.indexer_score: block_max must be [rows, {nb}]")
         a.block_rows = int(block_rows)
-    a.block_max = _ptr(block_max)
+    if block_keys is not None:
+        _need(block_keys, torch.int32, "block_keys")
+        if tuple(block_keys.shape) != (rows, -(-a.width // 8)):
+            raise ValueError("csa2.indexer_score: block_keys must be int32 [rows, ceil(width / 8)]")
+    a.block_max, a.block_keys = _ptr(block_max), _ptr(block_keys)
     a.q, a.w, a.k, a.k_scale = _ptr(q), _ptr(w), _ptr(k), _ptr(k_scale)
     a.row_base, a.pos, a.cand, a.scores = _ptr(row_base), _ptr(pos), _ptr(cand), _ptr(scores)
     a.key_hist = _ptr(key_hist)
     a.scale = float(scale)
+    return a
+
+
+def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None, cand=None, block_rows=8,
+                  fp8=False, key_hist=None, block_max=None, block_keys=None, width=None, stream=None):
+    """Fills ``scores`` [rows, width] (float32).  REINDEX when ``cand`` is given.
+
+    q [rows, H_I, D_I] and k [*, D_I] are float32/bfloat16, or uint8 FP8-E4M3
+    codes with ``fp8=True`` (then ``k_scale`` [*] float32 is required and the
+    query scales are already folded into w).  ``key_hist`` (int32 [rows, 4096])
+    optionally receives the score-key histogram topk_select can reuse.
+    ``block_max`` (FULL only, float32 [rows, ceil(width / block_rows)])
+    optionally receives the candidate pool's block scores.  ``scores=None``
+    (with ``width``, ``key_hist`` and ``block_keys`` int32 [rows, ceil(width / 8)])
+    selects the score-free mode whose top-k ``topk_rescore`` takes.
+    """
+    a = _index_args(q, w, k, row_base, pos, ratio, scale, scores, width, k_scale, cand, block_rows, fp8, key_hist,
+                    block_max, block_keys)
     _check("csa2_indexer_score", _lib.csa2_indexer_score(ctypes.byref(a), _stream(stream)))
     return scores
+
+
+def topk_rescore_workspace_size(rows, width, k):
+    return int(_lib.csa2_topk_rescore_workspace_size(int(rows), int(width), int(k)))
+
+
+def topk_rescore_supported(rows, width, k, heads=64, dim=128, fp8=True):
+    """Whether the score-free FULL path (indexer_score(scores=None) + topk_rescore) takes these sizes."""
+    return fp8 and heads == 64 and dim == 128 and 1 <= k <= 2048 and topk_rescore_workspace_size(rows, width, k) > 0
+
+
+def topk_rescore(q, w, k, row_base, pos, ratio, scale, out, key_hist, block_keys, width, *, k_scale=None,
+                 workspace=None, stream=None):
+    """Top-k ``out`` [rows, k] int32 of the scores a score-free indexer_score call with these arguments kept on
+    chip (its ``key_hist`` and ``block_keys``); bit-identical to topk_select over the written scores."""
+    _dev(out)
+    _need(out, torch.int32, "out")
+    a = _index_args(q, w, k, row_base, pos, ratio, scale, None, width, k_scale, None, 8, True, key_hist, None,
+                    block_keys)
+    if out.shape[0] != a.rows:
+        raise ValueError("csa2.topk_rescore: out rows")
+    need = topk_rescore_workspace_size(a.rows, a.width, out.shape[1])
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=out.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("csa2_topk_rescore", _lib.csa2_topk_rescore(ctypes.byref(a), out.shape[1], _ptr(out), _ptr(workspace),
+                                                       ws_bytes, _stream(stream)))
+    return out
 
 
 def topk_workspace_size(rows, width, k):
@@ -413,5 +463,15 @@ def prepare_candidate_pool(*args, stream=None, **kw):
         need = candidate_pool_workspace_size(cand.shape[0], width, kw.get("block_rows", 8), cand.shape[1])
         kw["workspace"] = torch.empty(max(need, 1), dtype=torch.uint8, device=pos.device)
     p = _prepare("csa2_candidate_pool", lambda: candidate_pool(*args, stream=stream, **kw), stream)
+    p.workspace = kw["workspace"]
+    return p
+
+
+def prepare_topk_rescore(*args, stream=None, **kw):
+    if kw.get("workspace") is None:
+        out, width = args[7], args[10]
+        need = topk_rescore_workspace_size(out.shape[0], width, out.shape[1])
+        kw["workspace"] = torch.empty(max(need, 1), dtype=torch.uint8, device=out.device)
+    p = _prepare("csa2_topk_rescore", lambda: topk_rescore(*args, stream=stream, **kw), stream)
     p.workspace = kw["workspace"]
     return p

@@ -79,9 +79,18 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
     } else if (a->block_max != nullptr && !pool_block_ok(a->block_rows)) {
         return CSA2_ERR_INVALID_ARG;
     }
+    // Score-free mode: FULL FP8 rows keep their scores on chip and leave the key
+    // histogram and block keys for csa2_topk_rescore.
+    const bool score_free = a->scores == nullptr;
+    if (a->block_keys != nullptr && !score_free) return CSA2_ERR_INVALID_ARG;
+    if (score_free) {
+        if (reindex || a->key_hist == nullptr || a->block_keys == nullptr) return CSA2_ERR_INVALID_ARG;
+        if (!csa2::indexer_rescore_supported(a->heads, a->dim, a->k_dtype)) return CSA2_ERR_UNSUPPORTED;
+        if (a->width >= (1LL << 24)) return CSA2_ERR_UNSUPPORTED;
+        if (!aligned(a->block_keys, 4)) return CSA2_ERR_INVALID_ARG;
+    }
     if (a->rows == 0 || a->width == 0) return CSA2_OK;
-    if (a->q == nullptr || a->w == nullptr || a->k == nullptr || a->row_base == nullptr || a->pos == nullptr ||
-        a->scores == nullptr)
+    if (a->q == nullptr || a->w == nullptr || a->k == nullptr || a->row_base == nullptr || a->pos == nullptr)
         return CSA2_ERR_INVALID_ARG;
     if ((a->k_dtype == CSA2_FP8_E4M3) != (a->k_scale != nullptr)) return CSA2_ERR_INVALID_ARG;
     if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->scores, 4) || !aligned(a->w, 4) ||
@@ -95,6 +104,7 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
     p.n_blocks = reindex ? a->n_blocks : 0; p.block_rows = reindex ? a->block_rows : 1; p.ratio = a->ratio;
     p.scale = a->scale;
     p.block_max = reindex ? nullptr : a->block_max;
+    p.block_keys = score_free ? a->block_keys : nullptr;
     p.bm_rows = p.block_max != nullptr ? a->block_rows : 4;
     p.bm_blocks = (a->width + p.bm_rows - 1) / p.bm_rows;
     // Columns per workgroup: multiples of 256 (4 waves x 64), aiming at ~4096 workgroups.
@@ -107,6 +117,67 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
     p.cols_per_wg = 256 * per;
     return hip_status(csa2::launch_indexer_score(p, a->rows, a->heads, a->dim, a->k_dtype, reindex,
                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
+// Wide-row plan of the score-free select, or nseg == 0 if these sizes have none.
+static void rescore_plan(int32_t rows, int64_t width, int& chunk, int& nseg) {
+    chunk = nseg = 0;
+    if (rows <= 0 || width <= 0 || width >= (1LL << 24)) return;
+    csa2::topk_plan(rows, width, chunk, nseg);
+}
+
+size_t csa2_topk_rescore_workspace_size(int32_t rows, int64_t width, int32_t k) {
+    (void)k;
+    int chunk, nseg;
+    rescore_plan(rows, width, chunk, nseg);
+    if (nseg == 0) return 0;
+    const size_t lists = (size_t)rows * nseg * chunk;
+    return align256((size_t)rows * 4) + align256((size_t)rows * nseg * 4) + 2 * align256(lists * 4);
+}
+
+int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, void* workspace, size_t workspace_bytes,
+                          csa2_stream_t stream) {
+    if (a == nullptr || a->struct_size < sizeof(csa2_index_args)) return CSA2_ERR_INVALID_ARG;
+    if (a->mode != CSA2_MODE_FULL || a->rows < 0 || a->width < 0 || (a->ratio != 1 && a->ratio != 2))
+        return CSA2_ERR_INVALID_ARG;
+    if (k < 1 || k > 2048) return CSA2_ERR_INVALID_ARG;
+    if (a->q_dtype != a->k_dtype || !csa2::indexer_rescore_supported(a->heads, a->dim, a->k_dtype))
+        return CSA2_ERR_UNSUPPORTED;
+    if (a->rows == 0) return CSA2_OK;
+    int chunk, nseg;
+    rescore_plan(a->rows, a->width, chunk, nseg);
+    if (nseg == 0) return CSA2_ERR_UNSUPPORTED;  // narrow rows: score, then csa2_topk_select
+    const size_t need = csa2_topk_rescore_workspace_size(a->rows, a->width, k);
+    if (workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+    if (workspace == nullptr || !aligned(workspace, 256)) return CSA2_ERR_INVALID_ARG;
+    if (a->q == nullptr || a->w == nullptr || a->k == nullptr || a->k_scale == nullptr || a->row_base == nullptr ||
+        a->pos == nullptr || a->key_hist == nullptr || a->block_keys == nullptr || out == nullptr)
+        return CSA2_ERR_INVALID_ARG;
+    if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->w, 4) || !isfinite(a->scale))
+        return CSA2_ERR_INVALID_ARG;
+
+    csa2::IndexParams ip;
+    ip.q = a->q; ip.w = a->w; ip.k = a->k; ip.k_scale = a->k_scale; ip.row_base = a->row_base; ip.pos = a->pos;
+    ip.cand = nullptr; ip.scores = nullptr; ip.key_hist = a->key_hist; ip.block_max = nullptr;
+    ip.block_keys = a->block_keys; ip.width = a->width; ip.cols_per_wg = 0; ip.bm_blocks = 0; ip.n_blocks = 0;
+    ip.block_rows = 1; ip.bm_rows = 4; ip.ratio = a->ratio; ip.scale = a->scale;
+    csa2::TopkParams tp;
+    tp.scores = nullptr; tp.pos = a->pos; tp.cand = nullptr; tp.out = out; tp.key_hist = a->key_hist;
+    tp.width = a->width; tp.k = k; tp.ratio = a->ratio; tp.n_blocks = 0; tp.block_rows = 1; tp.col_group = 1;
+
+    char* w = static_cast<char*>(workspace);
+    uint32_t* b1 = reinterpret_cast<uint32_t*>(w);
+    w += align256((size_t)a->rows * 4);
+    uint32_t* seg_count = reinterpret_cast<uint32_t*>(w);
+    w += align256((size_t)a->rows * nseg * 4);
+    uint32_t* keys = reinterpret_cast<uint32_t*>(w);
+    w += align256((size_t)a->rows * nseg * chunk * 4);
+    int32_t* cols = reinterpret_cast<int32_t*>(w);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = csa2::launch_topk_threshold(tp, a->rows, a->key_hist, b1, st);
+    if (e == hipSuccess) e = csa2::launch_indexer_rescore(ip, a->rows, b1, chunk, nseg, keys, cols, seg_count, st);
+    if (e == hipSuccess) e = csa2::launch_topk_final(tp, a->rows, keys, cols, seg_count, nseg, chunk, st);
+    return hip_status(e);
 }
 
 size_t csa2_topk_workspace_size(int32_t rows, int64_t width, int32_t k) {

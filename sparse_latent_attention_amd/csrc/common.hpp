@@ -79,6 +79,11 @@ constexpr int kKeyBins = 4096;  // bins of the top 12 key bits
 
 // Wave-level lane exchange (ds_bpermute based).
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ uint32_t shfl_xor(uint32_t v, int m) { return (uint32_t)__shfl_xor((int)v, m, 64); }
+
+// Columns per entry of the block-key summary the scoring pass can write
+// instead of the scores (the largest order key of each 8 consecutive columns).
+constexpr int kKeyBlock = 8;
 
 // ---------------------------------------------------------------------------
 // MFMA wrappers.  Compute element type CT is __bf16 or float.

@@ -124,10 +124,14 @@ struct IdxOps<CSA2_FP8_E4M3, 128> {
 // column 16u + n.  A reduce-scatter over the 4 lane groups leaves lane l with
 // column cb + l, which is scaled, stored (one coalesced 256-byte store), and
 // optionally counted into the LDS key histogram and folded into block scores.
-template <bool HIST, bool BMAX>
-__device__ __forceinline__ void store_step(const IndexParams& p, int r, int64_t nv, int64_t cb, int64_t c_end,
-                                           int lane, const float (&v)[4], float sc, bool valid, float* srow,
-                                           uint32_t* hist) {
+//
+// SCORES = false keeps the scores on chip; BKEYS then records, in the
+// workgroup's LDS array bkl, the largest order key of every kKeyBlock columns
+// (0 when none is valid), relative to the workgroup's first column c0.
+// Reduce over the 4 lane groups and scatter: lane l ends with column l of the
+// step.  Every column's sum is formed as (g0 + g2) + (g1 + g3) up to the order of
+// single additions, so the rounding does not depend on the column's position.
+__device__ __forceinline__ float reduce_scatter(const float (&v)[4], int lane) {
     const bool hi = (lane & 32) != 0;
     const bool mid = (lane & 16) != 0;
     float k0 = hi ? v[2] : v[0];
@@ -136,11 +140,25 @@ __device__ __forceinline__ void store_step(const IndexParams& p, int r, int64_t 
     k1 += shfl_xor(hi ? v[1] : v[3], 32);
     float kk = mid ? k1 : k0;
     kk += shfl_xor(mid ? k0 : k1, 16);
+    return kk;
+}
+
+template <bool HIST, bool BMAX, bool SCORES = true, bool BKEYS = false>
+__device__ __forceinline__ void store_step(const IndexParams& p, int r, int64_t nv, int64_t cb, int64_t c_end,
+                                           int lane, const float (&v)[4], float sc, bool valid, float* srow,
+                                           uint32_t* hist, uint32_t* bkl = nullptr, int64_t c0 = 0) {
+    const float kk = reduce_scatter(v, lane);
     const int64_t c_out = cb + lane;
     const float score = valid ? sc * kk : kNegInf;
     if (c_out < c_end) {
-        srow[c_out] = score;
+        if (SCORES) srow[c_out] = score;
         if (HIST && valid) atomicAdd(&hist[order_key(score) >> 20], 1u);
+    }
+    if (BKEYS) {
+        uint32_t bk = valid ? order_key(score) : 0u;
+#pragma unroll
+        for (int o = 1; o < kKeyBlock; o <<= 1) bk = max(bk, shfl_xor(bk, o));
+        if ((lane & (kKeyBlock - 1)) == 0 && c_out < c_end) bkl[(c_out - c0) / kKeyBlock] = bk;
     }
     if (BMAX) {
         // Block score over bm_rows consecutive columns = lanes (blocks never
@@ -155,12 +173,14 @@ __device__ __forceinline__ void store_step(const IndexParams& p, int r, int64_t 
     }
 }
 
-// Columns of a workgroup beyond the visible prefix: -inf scores, -inf block scores.
-template <bool BMAX>
+// Columns of a workgroup beyond the visible prefix: -inf scores, -inf block
+// scores, empty (0) block keys.
+template <bool BMAX, bool SCORES = true, bool BKEYS = false>
 __device__ __forceinline__ void store_invisible(const IndexParams& p, int r, int64_t cb, int64_t c_end, int lane,
-                                                float* srow) {
+                                                float* srow, uint32_t* bkl = nullptr, int64_t c0 = 0) {
     const int64_t c_out = cb + lane;
-    if (c_out < c_end) srow[c_out] = kNegInf;
+    if (SCORES && c_out < c_end) srow[c_out] = kNegInf;
+    if (BKEYS && (lane & (kKeyBlock - 1)) == 0 && c_out < c_end) bkl[(c_out - c0) / kKeyBlock] = 0u;
     if (BMAX && (lane & (p.bm_rows - 1)) == 0 && c_out < c_end)
         p.block_max[(int64_t)r * p.bm_blocks + c_out / p.bm_rows] = kNegInf;
 }
@@ -277,6 +297,57 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p)
 constexpr int kFp8Depth = 2;
 constexpr int kFp8MaxSteps = 16;
 
+// ---- FP8 64-key steps staged through LDS (shared by scoring and re-scoring) ----
+//
+// Lane l's 8 loads cover keys 8j + (l >> 3), 16-byte chunk l & 7, of a 64-key
+// step.  In LDS, chunk c of key kk sits at position c ^ ((kk >> 1) & 7) of the
+// key's 128-byte row: writes and MFMA-layout reads are free of bank conflicts.
+__device__ __forceinline__ void fp8_stage_put(uint8_t* my, const u32x4 (&v)[8], int ksub, int kchunk) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int kk = 8 * j + ksub;
+        *reinterpret_cast<u32x4*>(my + kk * 128 + 16 * (kchunk ^ ((kk >> 1) & 7))) = v[j];
+    }
+}
+
+// v[u] (lane (g, n)): sum over heads 4g..4g+3 of every 16-head tile t of
+// w * ReLU(q . k) for key 16u + n of the staged step.
+__device__ __forceinline__ void fp8_step_sums(const uint8_t* my, const i32x8 (&qa)[4], const float (&wr)[4][4],
+                                              int g, int li, float (&v)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int kk = 16 * u + li;
+        const int sw = (kk >> 1) & 7;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(my + kk * 128 + 16 * (g ^ sw));
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(my + kk * 128 + 16 * ((g + 4) ^ sw));
+        i32x8 kb;
+        kb[0] = a0[0]; kb[1] = a0[1]; kb[2] = a0[2]; kb[3] = a0[3];
+        kb[4] = a1[0]; kb[5] = a1[1]; kb[6] = a1[2]; kb[7] = a1[3];
+        float acc_sum = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const f32x4 acc = mma_fp8_k128(f32x4{0.f, 0.f, 0.f, 0.f}, qa[t], kb);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) acc_sum = fmaf(wr[t][rr], relu_bits(acc[rr]), acc_sum);
+        }
+        v[u] = acc_sum;
+    }
+}
+
+// Query fragments (A operands: heads as rows, 16 per tile) and head weights of query row r.
+__device__ __forceinline__ void fp8_load_query(const IndexParams& p, int r, int g, int li, i32x8 (&qa)[4],
+                                               float (&wr)[4][4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        qa[t] = IdxOps<CSA2_FP8_E4M3, 128>::load(p.q, (int64_t)r * 64 + 16 * t + li, 0, g);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) wr[t][rr] = p.w[(int64_t)r * 64 + 16 * t + 4 * g + rr];
+    }
+}
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, gfx9-family descriptor
+constexpr int kNT = 2;                  // non-temporal cache policy of a buffer load
+
 // FP8 FULL scoring with coalesced, non-temporal key-row loads.
 //
 // A FULL row's key rows are contiguous in the plane, so a wave's 64-key step is
@@ -294,15 +365,11 @@ constexpr int kFp8MaxSteps = 16;
 // guards a load.  The per-lane offset is fixed for the whole launch and the
 // step offset is a scalar.  DEPTH steps of loads are in flight per wave while
 // the matrix cores work on the step in LDS.
-template <bool HIST, bool BMAX, int DEPTH>
+template <bool HIST, bool BMAX, int DEPTH, bool SCORES, bool BKEYS>
 __global__ __launch_bounds__(256) void indexer_fp8_full_kernel(const IndexParams p) {
     __shared__ uint32_t hist[HIST ? kKeyBins : 1];
     __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * 128];
-    typedef IdxOps<CSA2_FP8_E4M3, 128> Ops;
-    typedef Ops::Frag Frag;
-    constexpr int HI = 64, HT = 4;
-    constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, gfx9-family descriptor
-    constexpr int kNT = 2;                  // non-temporal cache policy
+    __shared__ __attribute__((aligned(16))) uint32_t bkl[BKEYS ? 256 * kFp8MaxSteps / kKeyBlock : 1];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -318,14 +385,9 @@ __global__ __launch_bounds__(256) void indexer_fp8_full_kernel(const IndexParams
     float* srow = p.scores + (int64_t)r * p.width;
     uint8_t* my = stage[wave];
 
-    Frag qa[HT];
-    float wr[HT][4];
-#pragma unroll
-    for (int t = 0; t < HT; ++t) {
-        qa[t] = Ops::load(p.q, (int64_t)r * HI + 16 * t + li, 0, g);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) wr[t][rr] = p.w[(int64_t)r * HI + 16 * t + 4 * g + rr];
-    }
+    i32x8 qa[4];
+    float wr[4][4];
+    fp8_load_query(p, r, g, li, qa, wr);
     if (HIST) {
         for (int b = threadIdx.x; b < kKeyBins; b += 256) hist[b] = 0u;
         __syncthreads();
@@ -353,36 +415,15 @@ __global__ __launch_bounds__(256) void indexer_fp8_full_kernel(const IndexParams
         b.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, lane * 4, (int)(cb - c_begin) * 4, 0));
     };
     auto step = [&](int64_t cb, Buf& b) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int kk = 8 * j + ksub;
-            *reinterpret_cast<u32x4*>(my + kk * 128 + 16 * (kchunk ^ ((kk >> 1) & 7))) = b.v[j];
-        }
+        fp8_stage_put(my, b.v, ksub, kchunk);
         const float sc = p.scale * b.sc;
         const bool valid = cb + lane < c_live;
         // Unconditional: past the visible rows the descriptor turns the loads into zeros
         // (a conditional issue would make the compiler drain every load at the join).
         issue(cb + 256 * DEPTH, b);
         float v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int kk = 16 * u + li;
-            const int sw = (kk >> 1) & 7;
-            const u32x4 a0 = *reinterpret_cast<const u32x4*>(my + kk * 128 + 16 * (g ^ sw));
-            const u32x4 a1 = *reinterpret_cast<const u32x4*>(my + kk * 128 + 16 * ((g + 4) ^ sw));
-            Frag kb;
-            kb[0] = a0[0]; kb[1] = a0[1]; kb[2] = a0[2]; kb[3] = a0[3];
-            kb[4] = a1[0]; kb[5] = a1[1]; kb[6] = a1[2]; kb[7] = a1[3];
-            float acc_sum = 0.f;
-#pragma unroll
-            for (int t = 0; t < HT; ++t) {
-                const f32x4 acc = Ops::mma(f32x4{0.f, 0.f, 0.f, 0.f}, qa[t], kb);
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) acc_sum += wr[t][rr] * relu_bits(acc[rr]);
-            }
-            v[u] = acc_sum;
-        }
-        store_step<HIST, BMAX>(p, r, nv, cb, c_end, lane, v, sc, valid, srow, hist);
+        fp8_step_sums(my, qa, wr, g, li, v);
+        store_step<HIST, BMAX, SCORES, BKEYS>(p, r, nv, cb, c_end, lane, v, sc, valid, srow, hist, bkl, c_begin);
     };
 
     // At most kFp8MaxSteps steps per wave (cols_per_wg <= 256 * kFp8MaxSteps): the step
@@ -400,13 +441,147 @@ __global__ __launch_bounds__(256) void indexer_fp8_full_kernel(const IndexParams
     }
     int64_t cb = cb0;
     if (c_live > cb0) cb += 256 * ((c_live - cb0 + 255) / 256);
-    for (; cb < c_end; cb += 256) store_invisible<BMAX>(p, r, cb, c_end, lane, srow);
+    for (; cb < c_end; cb += 256) store_invisible<BMAX, SCORES, BKEYS>(p, r, cb, c_end, lane, srow, bkl, c_begin);
+    if (BKEYS) {  // the workgroup's block keys in one contiguous burst
+        __syncthreads();
+        const int nbk = (int)((c_end - c_begin + kKeyBlock - 1) / kKeyBlock);
+        uint32_t* gk = p.block_keys + (int64_t)r * ((p.width + kKeyBlock - 1) / kKeyBlock) + c_begin / kKeyBlock;
+        for (int i = threadIdx.x; i < nbk; i += 256) gk[i] = bkl[i];
+    }
     if (HIST) {
         __syncthreads();
         uint32_t* gh = p.key_hist + (int64_t)r * kKeyBins;
         for (int b = threadIdx.x; b < kKeyBins; b += 256)
             if (hist[b]) atomicAdd(&gh[b], hist[b]);
     }
+}
+
+// Re-scoring for the top-k of FP8 FULL scores that were never written.
+//
+// grid (nseg, rows).  Segment seg of row r covers columns [seg * chunk,
+// (seg + 1) * chunk).  b1[r] is the histogram bin holding the row's k-th
+// largest key, so every selected column has a key in bin >= b1, and so has the
+// largest key of its kKeyBlock-column block.  The workgroup collects, in column
+// order, the blocks of its segment whose block key (from the scoring pass)
+// reaches bin b1, re-scores their columns with exactly the scoring pass's
+// arithmetic (8 blocks = one 64-key step per wave), and appends the (key,
+// column) pairs of valid columns in bins >= b1, in column order, to the
+// segment's list (capacity cap = chunk, so it never overflows); seg_count gets
+// the list length.  Blocks are processed in sub-ranges of kRescoreSub.
+constexpr int kRescoreSub = 2048;
+
+__global__ __launch_bounds__(256) void indexer_fp8_rescore_kernel(const IndexParams p, const uint32_t* b1_in,
+                                                                  int chunk, int nseg, uint32_t* cand_keys,
+                                                                  int32_t* cand_cols, uint32_t* seg_count) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * 128];
+    __shared__ int32_t blist[kRescoreSub];
+    __shared__ uint32_t wcnt[4];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, li = lane & 15;
+    const int ksub = lane >> 3, kchunk = lane & 7;
+    const int r = blockIdx.y, seg = blockIdx.x;
+
+    const int64_t nv = uniform64((p.pos[r] + 1) / p.ratio);
+    const int64_t base = uniform64(p.row_base[r]);
+    const int64_t n_valid = nv < p.width ? nv : p.width;
+    const uint32_t b1 = __builtin_amdgcn_readfirstlane(b1_in[r]);
+    const int64_t c_lo = (int64_t)seg * chunk;
+    const int64_t c_hi = c_lo + chunk < n_valid ? c_lo + chunk : n_valid;
+    const int64_t nbk_row = (p.width + kKeyBlock - 1) / kKeyBlock;
+    const uint32_t* bkeys = p.block_keys + (int64_t)r * nbk_row;
+    uint32_t* okeys = cand_keys + ((int64_t)r * nseg + seg) * chunk;
+    int32_t* ocols = cand_cols + ((int64_t)r * nseg + seg) * chunk;
+    uint8_t* my = stage[wave];
+
+    i32x8 qa[4];
+    float wr[4][4];
+    fp8_load_query(p, r, g, li, qa, wr);
+    // the row's visible key rows and their scales; loads beyond them return zeros
+    const int n_rows = (int)(n_valid > 0 ? n_valid : 0);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.k) + base * 128), (short)0, n_rows * 128,
+        kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(p.k_scale + base), (short)0, n_rows * 4, kRsrcWord3);
+
+    uint32_t n_out = 0;
+    if (c_hi > c_lo) {
+        const int64_t blk_lo = c_lo / kKeyBlock, blk_hi = (c_hi + kKeyBlock - 1) / kKeyBlock;
+        for (int64_t sub = blk_lo; sub < blk_hi; sub += kRescoreSub) {
+            const int64_t sub_hi = sub + kRescoreSub < blk_hi ? sub + kRescoreSub : blk_hi;
+            // (a) candidate blocks of the sub-range, in order
+            uint32_t nbl = 0;
+            for (int64_t i0 = sub; i0 < sub_hi; i0 += 256) {
+                const int64_t i = i0 + threadIdx.x;
+                const uint32_t bk = i < sub_hi ? bkeys[i] : 0u;
+                const bool take = bk != 0u && (bk >> 20) >= b1;
+                const uint64_t m = __ballot(take);
+                if (lane == 0) wcnt[wave] = (uint32_t)__builtin_popcountll(m);
+                __syncthreads();
+                uint32_t before = nbl, all = 0;
+                for (int w = 0; w < 4; ++w) {
+                    if (w < wave) before += wcnt[w];
+                    all += wcnt[w];
+                }
+                if (take)
+                    blist[before + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = (int32_t)i;
+                nbl += all;
+                __syncthreads();
+            }
+            // (b) re-score 8 blocks per wave and round, append in order
+            for (uint32_t first0 = 0; first0 < nbl; first0 += 4 * 8) {
+                const int first = (int)first0 + 8 * wave;
+                const int cnt = (int)nbl - first;  // blocks of this wave's step (<= 0: idle)
+                u32x4 buf[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    // rows of block j; past the list: an offset beyond the descriptor -> zeros
+                    const int row = j < cnt ? blist[first + j] * kKeyBlock + ksub : n_rows;
+                    buf[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, row * 128 + 16 * kchunk,
+                                                                                             0, kNT));
+                }
+                const int my_blk = lane / kKeyBlock;
+                const int64_t col = my_blk < cnt ? (int64_t)blist[first + my_blk] * kKeyBlock + (lane % kKeyBlock)
+                                                 : n_valid;
+                const float ksc = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(col < n_valid ? col : n_valid) * 4, 0, 0));
+                fp8_stage_put(my, buf, ksub, kchunk);
+                float v[4];
+                fp8_step_sums(my, qa, wr, g, li, v);
+                const float kk = reduce_scatter(v, lane);
+                const bool valid = col < n_valid;
+                const float sc = p.scale * ksc;
+                const uint32_t key = order_key(sc * kk);
+                const bool take = valid && (key >> 20) >= b1;
+                const uint64_t m = __ballot(take);
+                if (lane == 0) wcnt[wave] = (uint32_t)__builtin_popcountll(m);
+                __syncthreads();
+                uint32_t before = n_out, all = 0;
+                for (int w = 0; w < 4; ++w) {
+                    if (w < wave) before += wcnt[w];
+                    all += wcnt[w];
+                }
+                if (take) {
+                    const uint32_t at = before + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    okeys[at] = key;
+                    ocols[at] = (int32_t)col;
+                }
+                n_out += all;
+                __syncthreads();
+            }
+        }
+    }
+    if (threadIdx.x == 0) seg_count[(int64_t)r * nseg + seg] = n_out;
+}
+
+hipError_t launch_indexer_rescore(const IndexParams& p, int rows, const uint32_t* b1, int chunk, int nseg,
+                                  uint32_t* cand_keys, int32_t* cand_cols, uint32_t* seg_count, hipStream_t stream) {
+    hipLaunchKernelGGL(indexer_fp8_rescore_kernel, dim3((unsigned)nseg, (unsigned)rows), dim3(256), 0, stream, p, b1,
+                       chunk, nseg, cand_keys, cand_cols, seg_count);
+    return hipGetLastError();
 }
 
 __global__ __launch_bounds__(256) void key_hist_zero_kernel(uint32_t* h, int64_t n) {
@@ -448,12 +623,18 @@ static hipError_t launch_fp8_full(const IndexParams& p, int rows, hipStream_t st
                            dim3(256), 0, stream, p.key_hist, nh);
     }
     constexpr int D = kFp8Depth;
-    if (p.block_max != nullptr) {
-        if (hist) hipLaunchKernelGGL((indexer_fp8_full_kernel<true, true, D>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((indexer_fp8_full_kernel<false, true, D>), grid, dim3(256), 0, stream, p);
+    if (p.scores == nullptr) {
+        // scores kept on chip: histogram and block keys only (validated by the caller)
+        if (p.block_max != nullptr)
+            hipLaunchKernelGGL((indexer_fp8_full_kernel<true, true, D, false, true>), grid, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((indexer_fp8_full_kernel<true, false, D, false, true>), grid, dim3(256), 0, stream, p);
+    } else if (p.block_max != nullptr) {
+        if (hist) hipLaunchKernelGGL((indexer_fp8_full_kernel<true, true, D, true, false>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((indexer_fp8_full_kernel<false, true, D, true, false>), grid, dim3(256), 0, stream, p);
     } else {
-        if (hist) hipLaunchKernelGGL((indexer_fp8_full_kernel<true, false, D>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((indexer_fp8_full_kernel<false, false, D>), grid, dim3(256), 0, stream, p);
+        if (hist) hipLaunchKernelGGL((indexer_fp8_full_kernel<true, false, D, true, false>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((indexer_fp8_full_kernel<false, false, D, true, false>), grid, dim3(256), 0, stream, p);
     }
     return hipGetLastError();
 }
@@ -475,6 +656,10 @@ hipError_t launch_indexer_score(const IndexParams& p, int rows, int heads, int d
                                                : launch_one<CSA2_BF16, 4, 32, false>(p, rows, stream);
     }
     return hipErrorInvalidValue;
+}
+
+bool indexer_rescore_supported(int heads, int dim, int dtype) {
+    return heads == 64 && dim == 128 && dtype == CSA2_FP8_E4M3;
 }
 
 bool indexer_supported(int heads, int dim, int dtype) {

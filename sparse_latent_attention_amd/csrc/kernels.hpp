@@ -19,6 +19,7 @@ struct IndexParams {
     float* scores;
     uint32_t* key_hist;  // optional [rows, 4096]
     float* block_max;    // optional [rows, bm_blocks] (FULL only)
+    uint32_t* block_keys;  // optional [rows, ceil(width / kKeyBlock)] (FULL only)
     int64_t width;
     int64_t cols_per_wg;
     int64_t bm_blocks;   // ceil(width / bm_rows)
@@ -50,6 +51,20 @@ struct TopkParams {
 // Bytes of workspace the launch plan for (rows, width) needs (0: one workgroup per row).
 size_t topk_workspace_bytes(int rows, int64_t width);
 hipError_t launch_topk_select(const TopkParams& p, int rows, void* workspace, hipStream_t stream);
+
+// Pieces of the wide-row select used by the score-free path: the threshold bin
+// of the k-th key from a key histogram, and the exact select over per-segment
+// (key, column) lists of capacity cap (a longer list falls back to p.scores).
+void topk_plan(int rows, int64_t width, int& chunk, int& nseg);
+hipError_t launch_topk_threshold(const TopkParams& p, int rows, const uint32_t* key_hist, uint32_t* b1,
+                                 hipStream_t stream);
+hipError_t launch_topk_final(const TopkParams& p, int rows, const uint32_t* cand_keys, const int32_t* cand_cols,
+                             const uint32_t* seg_count, int nseg, int cap, hipStream_t stream);
+
+// Re-scoring of candidate blocks for the score-free FP8 FULL path.
+bool indexer_rescore_supported(int heads, int dim, int dtype);
+hipError_t launch_indexer_rescore(const IndexParams& p, int rows, const uint32_t* b1, int chunk, int nseg,
+                                  uint32_t* cand_keys, int32_t* cand_cols, uint32_t* seg_count, hipStream_t stream);
 
 // Block scores of the candidate pool from FULL score rows (out: [rows, nb]).
 hipError_t launch_block_max(const float* scores, const int64_t* pos, int ratio, int64_t width, int block_rows,

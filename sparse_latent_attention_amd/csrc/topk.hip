@@ -140,10 +140,11 @@ struct RowSrc {
 
 // Positions of the filtered candidate list: segment-major, column order within.
 struct CandSrc {
-    const uint32_t* keys;      // [nseg][kCap] of this row
-    const int32_t* cols;       // [nseg][kCap]
+    const uint32_t* keys;      // [nseg][cap] of this row
+    const int32_t* cols;       // [nseg][cap]
     const uint32_t* seg_start; // LDS prefix of the segment counts, [nseg + 1]
     int nseg;
+    int cap;
     int n;
     __device__ __forceinline__ bool get(int i, uint32_t& key, int32_t& col) const {
         int lo = 0, hi = nseg;
@@ -153,8 +154,8 @@ struct CandSrc {
             else hi = mid;
         }
         const int j = i - (int)seg_start[lo];
-        key = keys[lo * kCap + j];
-        col = cols[lo * kCap + j];
+        key = keys[(int64_t)lo * cap + j];
+        col = cols[(int64_t)lo * cap + j];
         return true;
     }
 };
@@ -377,10 +378,11 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const TopkParams 
     if (tid == 0) seg_count[(int64_t)r * nseg + seg] = n_out;
 }
 
-// grid rows: exact select over the candidates (or the full row after an overflow).
+// grid rows: exact select over the candidates (or the full row after an overflow:
+// a list longer than its capacity `cap`).
 __global__ __launch_bounds__(kThreads) void topk_final_kernel(const TopkParams p, const uint32_t* cand_keys,
                                                               const int32_t* cand_cols, const uint32_t* seg_count,
-                                                              int nseg) {
+                                                              int nseg, int cap) {
     __shared__ Lds s;
     const int r = blockIdx.x;
     if (threadIdx.x == 0) {
@@ -389,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const TopkParams p
             const uint32_t c = seg_count[(int64_t)r * nseg + g];
             s.seg_start[g] = acc;
             acc += c;
-            over |= c > (uint32_t)kCap;
+            over |= c > (uint32_t)cap;
         }
         s.seg_start[nseg] = acc;
         s.sel[0] = over;
@@ -403,10 +405,11 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const TopkParams p
         return;
     }
     CandSrc src;
-    src.keys = cand_keys + (int64_t)r * nseg * kCap;
-    src.cols = cand_cols + (int64_t)r * nseg * kCap;
+    src.keys = cand_keys + (int64_t)r * nseg * cap;
+    src.cols = cand_cols + (int64_t)r * nseg * cap;
     src.seg_start = s.seg_start;
     src.nseg = nseg;
+    src.cap = cap;
     src.n = n;
     select_core(src, p, r, s);
 }
@@ -470,7 +473,20 @@ hipError_t launch_topk_select(const TopkParams& p, int rows, void* ws, hipStream
     hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0, stream, p, b1, keys,
                        cols, seg_count, chunk, nseg);
     hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, keys, cols, seg_count,
-                       nseg);
+                       nseg, kCap);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_threshold(const TopkParams& p, int rows, const uint32_t* key_hist, uint32_t* b1,
+                                 hipStream_t stream) {
+    hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, key_hist, b1);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_final(const TopkParams& p, int rows, const uint32_t* cand_keys, const int32_t* cand_cols,
+                             const uint32_t* seg_count, int nseg, int cap, hipStream_t stream) {
+    hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, cand_keys, cand_cols,
+                       seg_count, nseg, cap);
     return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(csa2.EXPORTED)
-    assert csa2.ABI_VERSION == 2
+    assert csa2.ABI_VERSION == 3
 
 
 def test_struct_layouts_match_c_compiler():
@@ -43,7 +43,7 @@ int main(void) {
   printf("csa2_topk_args sizeof %zu\n", sizeof(csa2_topk_args));
   printf("csa2_attn_args sizeof %zu\n", sizeof(csa2_attn_args));
   printf("csa2_pool_args sizeof %zu\n", sizeof(csa2_pool_args));
-  F(csa2_index_args, width) F(csa2_index_args, q) F(csa2_index_args, cand) F(csa2_index_args, scale) F(csa2_index_args, scores) F(csa2_index_args, key_hist) F(csa2_index_args, block_max)
+  F(csa2_index_args, width) F(csa2_index_args, q) F(csa2_index_args, cand) F(csa2_index_args, scale) F(csa2_index_args, scores) F(csa2_index_args, key_hist) F(csa2_index_args, block_max) F(csa2_index_args, block_keys)
   F(csa2_pool_args, n_cand) F(csa2_pool_args, width) F(csa2_pool_args, scores) F(csa2_pool_args, block_max) F(csa2_pool_args, pos) F(csa2_pool_args, cand)
   F(csa2_topk_args, width) F(csa2_topk_args, scores) F(csa2_topk_args, out) F(csa2_topk_args, key_hist)
   F(csa2_attn_args, swa_rows) F(csa2_attn_args, q) F(csa2_attn_args, rope_inv_freq) F(csa2_attn_args, softmax_scale) F(csa2_attn_args, out)
@@ -113,6 +113,59 @@ def test_indexer_block_max_rules():
         assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG, b
     a = _index_args(block_rows=8, block_max=ctypes.c_void_p(0x1002))
     assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+
+
+def test_score_free_mode_rules():
+    ptr = ctypes.c_void_p(0x1000)
+    fp8 = dict(q_dtype=csa2.FP8_E4M3, k_dtype=csa2.FP8_E4M3, k_scale=ptr, width=1 << 20)
+    # score-free needs FULL, key_hist and block_keys, and the FP8 64 x 128 kernel
+    a = _index_args(scores=None, key_hist=ptr, **fp8)
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+    a = _index_args(scores=None, block_keys=ptr, **fp8)
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+    a = _index_args(scores=None, key_hist=ptr, block_keys=ptr, mode=csa2.MODE_REINDEX, cand=ptr, n_blocks=2048,
+                    block_rows=8, **dict(fp8, width=16384))
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+    a = _index_args(scores=None, key_hist=ptr, block_keys=ptr, width=1 << 20)     # bf16
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_UNSUPPORTED
+    a = _index_args(scores=None, key_hist=ptr, block_keys=ptr, **dict(fp8, width=1 << 24))
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_UNSUPPORTED
+    # block keys are only written in score-free mode
+    a = _index_args(block_keys=ptr, key_hist=ptr, **fp8)
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,k,status", [
+    (dict(), 0, csa2.ERR_INVALID_ARG), (dict(), 4096, csa2.ERR_INVALID_ARG),
+    (dict(q_dtype=csa2.BF16, k_dtype=csa2.BF16), 512, csa2.ERR_UNSUPPORTED),
+    (dict(width=4000), 512, csa2.ERR_UNSUPPORTED),          # narrow rows: no wide-row plan
+    (dict(rows=2000), 512, csa2.ERR_UNSUPPORTED),           # many rows: one workgroup per row instead
+    (dict(mode=csa2.MODE_REINDEX), 512, csa2.ERR_INVALID_ARG),
+    (dict(key_hist=None), 512, csa2.ERR_INVALID_ARG),
+    (dict(block_keys=None), 512, csa2.ERR_INVALID_ARG),
+])
+def test_topk_rescore_validation(kw, k, status):
+    ptr = ctypes.c_void_p(0x1000)
+    base = dict(q_dtype=csa2.FP8_E4M3, k_dtype=csa2.FP8_E4M3, k_scale=ptr, width=1 << 20, scores=None, key_hist=ptr,
+                block_keys=ptr)
+    base.update(kw)
+    a = _index_args(**base)
+    ws = csa2.topk_rescore_workspace_size(a.rows, a.width, 512)
+    # every case is rejected on the host, before any launch
+    assert csa2._lib.csa2_topk_rescore(ctypes.byref(a), k, ptr, ctypes.c_void_p(0x10000), ws, None) == status
+
+
+def test_topk_rescore_workspace_rules():
+    ptr = ctypes.c_void_p(0x1000)
+    a = _index_args(q_dtype=csa2.FP8_E4M3, k_dtype=csa2.FP8_E4M3, k_scale=ptr, width=1 << 20, scores=None,
+                    key_hist=ptr, block_keys=ptr)
+    ws = csa2.topk_rescore_workspace_size(4, 1 << 20, 512)
+    assert ws >= 2 * 4 * (1 << 20) * 4                      # full-capacity candidate lists
+    assert csa2._lib.csa2_topk_rescore(ctypes.byref(a), 512, ptr, ctypes.c_void_p(0x10000), ws - 1, None) == \
+        csa2.ERR_WORKSPACE
+    assert csa2._lib.csa2_topk_rescore(ctypes.byref(a), 512, ptr, ctypes.c_void_p(0x10040), ws, None) == \
+        csa2.ERR_INVALID_ARG
+    assert csa2.topk_rescore_workspace_size(4, 4000, 512) == 0
 
 
 def _pool_args(**kw):

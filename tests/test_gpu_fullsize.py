@@ -6,8 +6,6 @@ same).  The oracle checks sampled query rows one by one (scores over the whole
 row, top-k, attention of every layer); properties that hold at any size are
 checked on every row.
 """
-import math
-
 import numpy as np
 import pytest
 import torch
@@ -25,50 +23,24 @@ NAMES = ["tiny_full_fp32", "full_decode_64k", "prefill_4096_at_128k", "reindex_d
 
 
 def _run_path(cfg, x):
-    """The path exactly as bench.py launches it."""
-    import sparse_latent_attention_amd as csa2
-    dev = x["pos"].device
-    rows = x["pos"].shape[0]
-    scores = torch.empty(rows, cfg.width, dtype=torch.float32, device=dev)
-    idx = torch.empty(rows, cfg.topk, dtype=torch.int32, device=dev)
-    outs = [torch.empty_like(L["q"]) for L in x["layers"]]
-    freqs = csa2.rope_inv_freq(cfg.rope_dim, cfg.rope_theta, cfg.yarn_factor, cfg.yarn_orig).to(dev)
-    kI = x["kI"].reshape(-1, cfg.idx_dim)
-    kIs = None if x["kI_scale"] is None else x["kI_scale"].reshape(-1)
-    kv = x["main"].reshape(-1, x["main"].shape[-1])
-    kvs = None if x["main_scale"] is None else x["main_scale"].reshape(-1, x["main_scale"].shape[-1])
-    akw = dict(rope_dim=cfg.rope_dim, kv_fp4=cfg.main_dtype == "fp4", swa_fp8=cfg.swa_dtype == "fp8", kv_scale=kvs)
-    key_hist = (torch.empty(rows, 4096, dtype=torch.int32, device=dev)
-                if csa2.topk_uses_key_hist(rows, cfg.width, cfg.topk) else None)
-    block_max = pool = None
-    if cfg.pool_blocks:
-        block_max = torch.empty(rows, -(-cfg.width // cfg.block_rows), dtype=torch.float32, device=dev)
-        pool = torch.empty(rows, cfg.pool_blocks, dtype=torch.int32, device=dev)
-    calls = [csa2.prepare_indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio,
-                                        1.0 / math.sqrt(cfg.idx_dim * cfg.idx_heads), scores, k_scale=kIs,
-                                        cand=x.get("cand"), block_rows=cfg.block_rows, fp8=cfg.idx_dtype == "fp8",
-                                        key_hist=key_hist, block_max=block_max),
-             csa2.prepare_topk_select(scores, x["pos"], cfg.ratio, idx, cand=x.get("cand"), block_rows=cfg.block_rows,
-                                      key_hist=key_hist)]
-    if cfg.pool_blocks:
-        calls.append(csa2.prepare_candidate_pool(x["pos"], cfg.ratio, pool, block_max=block_max, width=cfg.width,
-                                                 block_rows=cfg.block_rows))
-    tau = 1.0 / math.sqrt(cfg.dim)
-    for li, L in enumerate(x["layers"]):
-        if cfg.phase == "decode":
-            calls.append(csa2.prepare_sparse_attn_decode(L["q"], x["pos"], idx, kv, x["kv_row_base"], x["swa"],
-                                                         L["sink"], freqs, cfg.ratio, cfg.window, tau, outs[li],
-                                                         swa_scale=x["swa_scale"], **akw))
-        else:
-            calls.append(csa2.prepare_sparse_attn_prefill(L["q"], x["pos"], idx, kv, L["swa"], x["swa_pos0"],
-                                                          L["sink"], freqs, cfg.ratio, cfg.window, tau, outs[li],
-                                                          swa_scale=L["swa_scale"], kv_row_base=x["kv_row_base"],
-                                                          **akw))
-    for c in calls:
-        c()
+    """The path exactly as bench.py launches it.  When it keeps the scores on chip, the scores are
+    also written by a separate call for the checks, and the score-free top-k must equal topk_select
+    over them on every row."""
+    from workloads.step import Step
+    from harness import gpu_scores, gpu_topk
+    step = Step(cfg, x)
+    step()
     torch.cuda.synchronize()
-    x["_pool"] = pool
-    return scores, idx, outs
+    x["_pool"] = step.pool
+    if step.score_free:
+        scores = gpu_scores(cfg, x)
+        ref = gpu_topk(cfg, x, scores)
+        torch.cuda.synchronize()
+        assert torch.equal(step.idx, ref), "score-free top-k differs from topk_select over the written scores"
+        print(f"[{cfg.name}] score-free top-k == topk_select(written scores) on all {cfg.q_tokens} rows")
+    else:
+        scores = step.scores
+    return scores, step.idx, step.outs
 
 
 def _sample_rows(cfg):

@@ -1,0 +1,110 @@
+"""GPU parity of the score-free FULL top-k (indexer_score with scores=None, then topk_rescore).
+
+The score-free path must return exactly what topk_select returns over the
+scores indexer_score writes, so every check here is bit-exact against that
+materialised path on the same inputs, which in turn is checked against the
+oracle (tests/test_gpu_parity.py, tests/test_gpu_fullsize.py):
+  * the key histogram equals a host recount of the written scores;
+  * each block key equals the largest order key of its 8 written scores;
+  * the top-k equals topk_select of the written scores, and the oracle's top-k
+    of them.
+Inputs include ragged histories (rows with fewer visible rows than k, a row
+at position 0), duplicated key rows (exact score ties across blocks), and
+the full 1M-row width.
+"""
+import numpy as np
+import pytest
+import torch
+
+from workloads import CONFIGS, make_inputs
+
+from harness import gpu_scores, gpu_topk, host_key_hist, index_scale, oracle_score_bound, oracle_topk
+
+pytestmark = pytest.mark.gpu
+
+
+def _order_keys(s):
+    u = s.astype(np.float32).view(np.uint32).copy()
+    u[(u & 0x7FFFFFFF) > 0x7F800000] = 0xFF800000
+    u[u == 0x80000000] = 0
+    return np.where(u & 0x80000000, ~u, u | 0x80000000).astype(np.uint32)
+
+
+def _score_free(cfg, x, k):
+    import sparse_latent_attention_amd as csa2
+    rows = x["pos"].shape[0]
+    dev = x["pos"].device
+    hist = torch.full((rows, 4096), 7, dtype=torch.int32, device=dev)          # the call must zero it
+    bkeys = torch.full((rows, -(-cfg.width // 8)), 12345, dtype=torch.int32, device=dev)
+    kI = x["kI"].reshape(-1, cfg.idx_dim)
+    ks = x["kI_scale"].reshape(-1)
+    csa2.indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, index_scale(cfg), None,
+                       width=cfg.width, k_scale=ks, fp8=True, key_hist=hist, block_keys=bkeys)
+    out = torch.full((rows, k), -7, dtype=torch.int32, device=dev)
+    csa2.topk_rescore(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, index_scale(cfg), out, hist, bkeys,
+                      cfg.width, k_scale=ks)
+    torch.cuda.synchronize()
+    return hist, bkeys, out
+
+
+CASES = {
+    "ragged_100k": (CONFIGS["lowp_full_decode_1m"].replace(batch=6, q_tokens=6, context=100003, ragged=True), 512),
+    "short_rows": (CONFIGS["lowp_full_decode_1m"].replace(batch=5, q_tokens=5, context=30000, ragged=True), 512),
+    "k2048": (CONFIGS["lowp_full_decode_1m"].replace(batch=3, q_tokens=3, context=50000), 2048),
+    "ratio2": (CONFIGS["lowp_full_decode_1m"].replace(batch=4, q_tokens=4, context=80001, ratio=2, ragged=True), 512),
+    "ties": (CONFIGS["lowp_full_decode_1m"].replace(batch=4, q_tokens=4, context=40000), 512),
+    "full_1m": (CONFIGS["lowp_full_decode_1m"].replace(batch=3, q_tokens=3), 512),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_score_free_matches_written_scores(name):
+    import sparse_latent_attention_amd as csa2
+    cfg, k = CASES[name]
+    print(f"\n[rescore] {name} rows={cfg.q_tokens} width={cfg.width} k={k}", flush=True)
+    x = make_inputs(cfg, 51, device="cuda")
+    rows = cfg.q_tokens
+    if name == "short_rows":
+        x["pos"][0] = 0
+        x["pos"][1] = 300              # fewer visible rows than k
+        x["pos"][2] = 8 * 64 + 2
+    if name == "ties":
+        # every 40th key row (and its scale) is a copy of row 17: equal scores across blocks
+        kI = x["kI"].view(rows, -1, cfg.idx_dim)
+        kI[:, ::40] = kI[:, 17:18]
+        sc = x["kI_scale"].view(rows, -1)
+        sc[:, ::40] = sc[:, 17:18]
+    assert csa2.topk_rescore_supported(rows, cfg.width, k)
+    hist, bkeys, out = _score_free(cfg, x, k)
+
+    scores = gpu_scores(cfg, x)
+    ref_idx = gpu_topk(cfg, x, scores, k=k)
+    s_np = scores.cpu().numpy()
+    valid = np.isfinite(oracle_score_bound(cfg, x, np.arange(rows)))
+    assert np.array_equal(hist.cpu().numpy().astype(np.int64), host_key_hist(s_np, valid))
+    keys = np.where(valid, _order_keys(s_np), 0).astype(np.uint32)
+    pad = (-cfg.width) % 8
+    want_bk = np.pad(keys, ((0, 0), (0, pad))).reshape(rows, -1, 8).max(axis=2)
+    assert np.array_equal(bkeys.cpu().numpy().view(np.uint32), want_bk)
+    got = out.cpu().numpy()
+    assert np.array_equal(got, ref_idx.cpu().numpy()), "score-free top-k differs from topk_select of written scores"
+    assert np.array_equal(got, oracle_topk(cfg, x, s_np.astype(np.float64), np.arange(rows), k=k))
+
+
+def test_score_free_with_pool_block_scores():
+    """The pool's block scores from a score-free pass equal those of the writing pass."""
+    import sparse_latent_attention_amd as csa2
+    cfg = CONFIGS["lowp_pool_decode_1m"].replace(batch=4, q_tokens=4, context=70001, ragged=True)
+    x = make_inputs(cfg, 53, device="cuda")
+    rows, nb = cfg.q_tokens, -(-cfg.width // 8)
+    bm_a = torch.empty(rows, nb, dtype=torch.float32, device="cuda")
+    bm_b = torch.empty(rows, nb, dtype=torch.float32, device="cuda")
+    gpu_scores(cfg, x, block_max=bm_a)
+    hist = torch.empty(rows, 4096, dtype=torch.int32, device="cuda")
+    bkeys = torch.empty(rows, nb, dtype=torch.int32, device="cuda")
+    kI = x["kI"].reshape(-1, cfg.idx_dim)
+    csa2.indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, index_scale(cfg), None,
+                       width=cfg.width, k_scale=x["kI_scale"].reshape(-1), fp8=True, key_hist=hist,
+                       block_keys=bkeys, block_max=bm_b)
+    torch.cuda.synchronize()
+    assert torch.equal(bm_a, bm_b)

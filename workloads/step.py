@@ -1,0 +1,94 @@
+"""One step of the hot path for a workload: output buffers plus the C ABI calls, marshalled once.
+
+A step is the whole path over one batch (see bench.py): the indexer scores,
+the top-k, the candidate pool when the workload's FULL layer builds one, and
+sparse attention for every layer that uses the selection.  Wide FULL rows with
+an FP8 index plane take the score-free route (indexer_score with scores=None,
+then topk_rescore) whenever the library supports the shape; everything else
+writes the scores and runs topk_select.  bench.py times these calls and the
+full-size parity tests run exactly the same ones.
+"""
+
+import math
+
+import torch
+
+
+class Step:
+    """Buffers and prepared calls of one step, grouped by kernel: ``groups`` maps
+    "indexer_score" / "topk_select" / "candidate_pool" / "sparse_attn" to lists of calls."""
+
+    def __init__(self, cfg, x, score_free=None):
+        import sparse_latent_attention_amd as csa2
+        self.cfg = cfg
+        dev = x["pos"].device
+        rows = x["pos"].shape[0]
+        self.rows = rows
+        kI = x["kI"].reshape(-1, cfg.idx_dim)
+        kIs = None if x["kI_scale"] is None else x["kI_scale"].reshape(-1)
+        kv = x["main"].reshape(-1, x["main"].shape[-1])
+        kvs = None if x["main_scale"] is None else x["main_scale"].reshape(-1, x["main_scale"].shape[-1])
+        tau_i = 1.0 / math.sqrt(cfg.idx_dim * cfg.idx_heads)
+        tau = 1.0 / math.sqrt(cfg.dim)
+        fp8 = cfg.idx_dtype == "fp8"
+        if score_free is None:
+            score_free = (cfg.index_mode == "full" and fp8 and
+                          csa2.topk_rescore_supported(rows, cfg.width, cfg.topk, cfg.idx_heads, cfg.idx_dim, fp8))
+        self.score_free = score_free
+        self.idx = torch.empty(rows, cfg.topk, dtype=torch.int32, device=dev)
+        self.outs = [torch.empty_like(L["q"]) for L in x["layers"]]
+        self.block_max = self.pool = None
+        if cfg.pool_blocks:
+            self.block_max = torch.empty(rows, -(-cfg.width // cfg.block_rows), dtype=torch.float32, device=dev)
+            self.pool = torch.empty(rows, cfg.pool_blocks, dtype=torch.int32, device=dev)
+        freqs = csa2.rope_inv_freq(cfg.rope_dim, cfg.rope_theta, cfg.yarn_factor, cfg.yarn_orig).to(dev)
+        self.freqs = freqs
+
+        idx_common = (x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, tau_i)
+        if score_free:
+            self.scores = None
+            self.key_hist = torch.empty(rows, 4096, dtype=torch.int32, device=dev)
+            self.block_keys = torch.empty(rows, -(-cfg.width // 8), dtype=torch.int32, device=dev)
+            call_idx = csa2.prepare_indexer_score(*idx_common, None, width=cfg.width, k_scale=kIs, fp8=True,
+                                                  key_hist=self.key_hist, block_keys=self.block_keys,
+                                                  block_max=self.block_max, block_rows=cfg.block_rows)
+            call_topk = csa2.prepare_topk_rescore(*idx_common, self.idx, self.key_hist, self.block_keys, cfg.width,
+                                                  k_scale=kIs)
+        else:
+            self.scores = torch.empty(rows, cfg.width, dtype=torch.float32, device=dev)
+            # the indexer also builds the score-key histogram when top-k takes its wide-row path
+            self.key_hist = (torch.empty(rows, 4096, dtype=torch.int32, device=dev)
+                             if csa2.topk_uses_key_hist(rows, cfg.width, cfg.topk) else None)
+            self.block_keys = None
+            call_idx = csa2.prepare_indexer_score(*idx_common, self.scores, k_scale=kIs, cand=x.get("cand"),
+                                                  block_rows=cfg.block_rows, fp8=fp8, key_hist=self.key_hist,
+                                                  block_max=self.block_max)
+            call_topk = csa2.prepare_topk_select(self.scores, x["pos"], cfg.ratio, self.idx, cand=x.get("cand"),
+                                                 block_rows=cfg.block_rows, key_hist=self.key_hist)
+        self.groups = {"indexer_score": [call_idx], "topk_select": [call_topk]}
+        if cfg.pool_blocks:
+            self.groups["candidate_pool"] = [csa2.prepare_candidate_pool(
+                x["pos"], cfg.ratio, self.pool, block_max=self.block_max, width=cfg.width, block_rows=cfg.block_rows)]
+        akw = dict(rope_dim=cfg.rope_dim, kv_fp4=cfg.main_dtype == "fp4", swa_fp8=cfg.swa_dtype == "fp8",
+                   kv_scale=kvs)
+        attn = []
+        for li, L in enumerate(x["layers"]):
+            if cfg.phase == "decode":
+                attn.append(csa2.prepare_sparse_attn_decode(
+                    L["q"], x["pos"], self.idx, kv, x["kv_row_base"], x["swa"], L["sink"], freqs, cfg.ratio,
+                    cfg.window, tau, self.outs[li], swa_scale=x["swa_scale"], **akw))
+            else:
+                attn.append(csa2.prepare_sparse_attn_prefill(
+                    L["q"], x["pos"], self.idx, kv, L["swa"], x["swa_pos0"], L["sink"], freqs, cfg.ratio,
+                    cfg.window, tau, self.outs[li], swa_scale=L["swa_scale"], kv_row_base=x["kv_row_base"], **akw))
+        self.groups["sparse_attn"] = attn
+
+    def __call__(self, on_group=None):
+        """Runs every call in order; ``on_group(name)`` is called before each group and once more at the end."""
+        for name, calls in self.groups.items():
+            if on_group is not None:
+                on_group(name)
+            for c in calls:
+                c()
+        if on_group is not None:
+            on_group(None)
