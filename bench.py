@@ -74,7 +74,8 @@ def algorithmic_work(cfg, x, idx_host=None, score_free=False):
     if score_free:
         # scores stay on chip: the key histogram and the 8-column block keys are written instead
         nbk = -(-cfg.width // 8)
-        idx_bytes = unique_rows * idx_row + qI + rows * nbm * 4 + rows * (nbk + 4096) * 4
+        idx_bytes = unique_rows * idx_row + qI + rows * (nbk + 4096) * 4
+        nbm = nbk  # the pool ranks the same block keys
         # the select reads the histogram and block keys (re-scored candidate rows are not counted:
         # they are extra work of this route, not bytes the result needs)
         topk_bytes = rows * (nbk + 4096) * 4 + rows * cfg.topk * 4

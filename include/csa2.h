@@ -143,8 +143,10 @@ typedef struct csa2_index_args {
                                  * no visible column get -inf.  Written in the same pass as the
                                  * scores (no second read of them). */
     uint32_t* block_keys;       /* score-free mode only (scores == NULL), out: [rows, ceil(width / 8)].
-                                 * Entry b holds the largest order key (as for key_hist) of the
-                                 * valid columns 8b .. 8b+7, or 0 when none is valid. */
+                                 * Entry b holds the largest key of the valid columns 8b .. 8b+7,
+                                 * or 0 when none is valid; a column's key is its order key (as for
+                                 * key_hist), except that a NaN score counts as 0x007FFFFE, just
+                                 * below -inf (so the candidate pool can still tell NaN from -inf). */
 } csa2_index_args;
 
 int32_t csa2_indexer_score(const csa2_index_args* args, csa2_stream_t stream);
@@ -234,9 +236,9 @@ int32_t csa2_topk_select(const csa2_topk_args* args, void* workspace, size_t wor
  * the cand argument of the REINDEX calls (csa2_indexer_score,
  * csa2_topk_select) of the layers that share this owner's plane.
  *
- * Block scores come either from block_max (what csa2_indexer_score wrote in
- * the scoring pass; scores may then be NULL) or, when block_max is NULL, are
- * computed here from scores into the workspace.
+ * Block scores come from block_keys (written by a score-free
+ * csa2_indexer_score pass), else from block_max (what csa2_indexer_score wrote
+ * in the scoring pass), else are computed here from scores into the workspace.
  *
  * Supported: block_rows a power of two in 4..64; 1 <= n_cand <= 2048;
  * width < 2^31.
@@ -253,6 +255,9 @@ typedef struct csa2_pool_args {
     const float* block_max;     /* [rows, ceil(width / block_rows)] from csa2_indexer_score, or NULL */
     const int64_t* pos;         /* [rows] absolute query positions */
     int32_t* cand;              /* out: [rows, n_cand] block ids */
+    const uint32_t* block_keys; /* [rows, ceil(width / 8)] from a score-free csa2_indexer_score, or NULL;
+                                 * when given (block_rows must be 8) the block scores are derived
+                                 * from it and scores / block_max are ignored */
 } csa2_pool_args;
 
 /* Bytes of workspace csa2_candidate_pool needs (enough with or without block_max). */

@@ -59,6 +59,7 @@ class PoolArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", _u32), ("rows", _i32), ("ratio", _i32), ("block_rows", _i32), ("n_cand", _i32),
         ("_pad0", _i32), ("width", _i64), ("scores", _vp), ("block_max", _vp), ("pos", _vp), ("cand", _vp),
+        ("block_keys", _vp),
     ]
 
 
@@ -302,15 +303,16 @@ def candidate_pool_workspace_size(rows, width, block_rows=8, n_cand=2048):
     return int(_lib.csa2_candidate_pool_workspace_size(int(rows), int(width), int(block_rows), int(n_cand)))
 
 
-def candidate_pool(pos, ratio, cand, *, scores=None, block_max=None, width=None, block_rows=8, workspace=None,
-                   stream=None):
+def candidate_pool(pos, ratio, cand, *, scores=None, block_max=None, block_keys=None, width=None, block_rows=8,
+                   workspace=None, stream=None):
     """Fills ``cand`` [rows, n_cand] int32 with the FULL layer's candidate blocks (ascending, -1 padded).
 
-    Block scores come from ``block_max`` (written by indexer_score) when given,
-    else from ``scores`` [rows, width].  ``width`` is the FULL score width
-    (taken from ``scores`` when omitted).
+    Block scores come from ``block_keys`` (int32 [rows, ceil(width / 8)] from a
+    score-free indexer_score) or ``block_max`` (written by indexer_score) when
+    given, else from ``scores`` [rows, width].  ``width`` is the FULL score
+    width (taken from ``scores`` when omitted).
     """
-    _dev(pos, cand, scores, block_max, workspace)
+    _dev(pos, cand, scores, block_max, block_keys, workspace)
     _need(pos, torch.int64, "pos")
     _need(cand, torch.int32, "cand")
     rows = cand.shape[0]
@@ -326,12 +328,17 @@ def candidate_pool(pos, ratio, cand, *, scores=None, block_max=None, width=None,
         _need(block_max, torch.float32, "block_max")
         if tuple(block_max.shape) != (rows, -(-int(width) // int(block_rows))):
             raise ValueError("csa2.candidate_pool: block_max must be [rows, ceil(width / block_rows)]")
+    if block_keys is not None:
+        _need(block_keys, torch.int32, "block_keys")
+        if tuple(block_keys.shape) != (rows, -(-int(width) // 8)):
+            raise ValueError("csa2.candidate_pool: block_keys must be [rows, ceil(width / 8)]")
     if pos.shape != (rows,):
         raise ValueError("csa2.candidate_pool: pos must be [rows]")
     a = PoolArgs()
     a.struct_size = ctypes.sizeof(PoolArgs)
     a.rows, a.ratio, a.block_rows, a.n_cand, a.width = rows, int(ratio), int(block_rows), cand.shape[1], int(width)
     a.scores, a.block_max, a.pos, a.cand = _ptr(scores), _ptr(block_max), _ptr(pos), _ptr(cand)
+    a.block_keys = _ptr(block_keys)
     need = candidate_pool_workspace_size(rows, width, block_rows, a.n_cand)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=pos.device)

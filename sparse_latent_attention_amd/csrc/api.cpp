@@ -164,6 +164,7 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
     csa2::TopkParams tp;
     tp.scores = nullptr; tp.pos = a->pos; tp.cand = nullptr; tp.out = out; tp.key_hist = a->key_hist;
     tp.width = a->width; tp.k = k; tp.ratio = a->ratio; tp.n_blocks = 0; tp.block_rows = 1; tp.col_group = 1;
+    tp.pool_keys = nullptr;
 
     char* w = static_cast<char*>(workspace);
     uint32_t* b1 = reinterpret_cast<uint32_t*>(w);
@@ -206,6 +207,7 @@ int32_t csa2_topk_select(const csa2_topk_args* a, void* workspace, size_t worksp
     p.width = a->width; p.k = a->k; p.ratio = a->ratio; p.n_blocks = a->n_blocks;
     p.block_rows = a->n_blocks > 0 ? a->block_rows : 1;
     p.col_group = 1;
+    p.pool_keys = nullptr;
     return hip_status(csa2::launch_topk_select(p, a->rows, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -226,13 +228,15 @@ int32_t csa2_candidate_pool(const csa2_pool_args* a, void* workspace, size_t wor
     if (need > 0 && (workspace == nullptr || !aligned(workspace, 256))) return CSA2_ERR_INVALID_ARG;
     if (a->rows == 0) return CSA2_OK;
     if (a->pos == nullptr || a->cand == nullptr) return CSA2_ERR_INVALID_ARG;
-    if (a->width > 0 && a->scores == nullptr && a->block_max == nullptr) return CSA2_ERR_INVALID_ARG;
-    if (!aligned(a->scores, 4) || !aligned(a->block_max, 4)) return CSA2_ERR_INVALID_ARG;
+    if (a->width > 0 && a->scores == nullptr && a->block_max == nullptr && a->block_keys == nullptr)
+        return CSA2_ERR_INVALID_ARG;
+    if (a->block_keys != nullptr && a->block_rows != 8) return CSA2_ERR_INVALID_ARG;
+    if (!aligned(a->scores, 4) || !aligned(a->block_max, 4) || !aligned(a->block_keys, 4)) return CSA2_ERR_INVALID_ARG;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int64_t nb = (a->width + a->block_rows - 1) / a->block_rows;
     const float* bmax = a->block_max;
     char* ws = static_cast<char*>(workspace);
-    if (bmax == nullptr && nb > 0) {
+    if (a->block_keys == nullptr && bmax == nullptr && nb > 0) {
         float* buf = reinterpret_cast<float*>(ws);
         const hipError_t e = csa2::launch_block_max(a->scores, a->pos, a->ratio, a->width, a->block_rows, a->rows,
                                                     buf, st);
@@ -243,6 +247,8 @@ int32_t csa2_candidate_pool(const csa2_pool_args* a, void* workspace, size_t wor
     p.scores = bmax; p.pos = a->pos; p.cand = nullptr; p.out = a->cand; p.key_hist = nullptr;
     p.width = nb; p.k = a->n_cand; p.ratio = a->ratio; p.n_blocks = 0; p.block_rows = 1;
     p.col_group = a->block_rows;
+    p.pool_keys = a->block_keys;
+    if (a->block_keys != nullptr) p.scores = nullptr;
     void* tws = need > 0 ? ws + align256((size_t)a->rows * (size_t)nb * sizeof(float)) : nullptr;
     return hip_status(csa2::launch_topk_select(p, a->rows, tws, st));
 }

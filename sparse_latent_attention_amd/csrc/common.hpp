@@ -82,8 +82,24 @@ __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v,
 __device__ __forceinline__ uint32_t shfl_xor(uint32_t v, int m) { return (uint32_t)__shfl_xor((int)v, m, 64); }
 
 // Columns per entry of the block-key summary the scoring pass can write
-// instead of the scores (the largest order key of each 8 consecutive columns).
+// instead of the scores (the largest block key of each 8 consecutive columns).
 constexpr int kKeyBlock = 8;
+
+// Block key of a score: its order key, except that a NaN gets 0x007FFFFE, just
+// below key(-inf) = 0x007FFFFF and in the same histogram bin (no other score
+// has this key).  Block keys thus still tell an all-NaN block (pool score
+// -inf) from one holding -inf (pool score -FLT_MAX).  0 = no valid column.
+constexpr uint32_t kNanBlockKey = 0x007ffffeu;
+__device__ __forceinline__ uint32_t block_key(float s) {
+    return __builtin_isnan(s) ? kNanBlockKey : order_key(s);
+}
+
+// The candidate pool's block score from a block key (before pinning).
+__device__ __forceinline__ float pool_value_of_block_key(uint32_t bk) {
+    if (bk == kNanBlockKey) return kNegInf;
+    const uint32_t bits = (bk & 0x80000000u) ? (bk & 0x7fffffffu) : ~bk;
+    return pool_value(__uint_as_float(bits));
+}
 
 // ---------------------------------------------------------------------------
 // MFMA wrappers.  Compute element type CT is __bf16 or float.

@@ -155,7 +155,7 @@ __device__ __forceinline__ void store_step(const IndexParams& p, int r, int64_t 
         if (HIST && valid) atomicAdd(&hist[order_key(score) >> 20], 1u);
     }
     if (BKEYS) {
-        uint32_t bk = valid ? order_key(score) : 0u;
+        uint32_t bk = valid ? block_key(score) : 0u;
 #pragma unroll
         for (int o = 1; o < kKeyBlock; o <<= 1) bk = max(bk, shfl_xor(bk, o));
         if ((lane & (kKeyBlock - 1)) == 0 && c_out < c_end) bkl[(c_out - c0) / kKeyBlock] = bk;
@@ -510,26 +510,36 @@ __global__ __launch_bounds__(256) void indexer_fp8_rescore_kernel(const IndexPar
         const int64_t blk_lo = c_lo / kKeyBlock, blk_hi = (c_hi + kKeyBlock - 1) / kKeyBlock;
         for (int64_t sub = blk_lo; sub < blk_hi; sub += kRescoreSub) {
             const int64_t sub_hi = sub + kRescoreSub < blk_hi ? sub + kRescoreSub : blk_hi;
-            // (a) candidate blocks of the sub-range, in order
-            uint32_t nbl = 0;
-            for (int64_t i0 = sub; i0 < sub_hi; i0 += 256) {
-                const int64_t i = i0 + threadIdx.x;
-                const uint32_t bk = i < sub_hi ? bkeys[i] : 0u;
-                const bool take = bk != 0u && (bk >> 20) >= b1;
-                const uint64_t m = __ballot(take);
-                if (lane == 0) wcnt[wave] = (uint32_t)__builtin_popcountll(m);
-                __syncthreads();
-                uint32_t before = nbl, all = 0;
-                for (int w = 0; w < 4; ++w) {
-                    if (w < wave) before += wcnt[w];
-                    all += wcnt[w];
-                }
-                if (take)
-                    blist[before + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] = (int32_t)i;
-                nbl += all;
-                __syncthreads();
+            // (a) candidate blocks of the sub-range, in order: thread t owns blocks
+            // sub + 8t .. sub + 8t + 7 (all loads issued at once), then a block-wide scan
+            constexpr int kPer = kRescoreSub / 256;
+            uint32_t bk[kPer];
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) {
+                const int64_t i = sub + kPer * threadIdx.x + e;
+                bk[e] = i < sub_hi ? bkeys[i] : 0u;
             }
+            uint32_t mine = 0;
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) mine |= (uint32_t)(bk[e] != 0u && (bk[e] >> 20) >= b1) << e;
+            const uint32_t cnt = (uint32_t)__builtin_popcount(mine);
+            uint32_t incl = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
+                if (lane >= o) incl += y;
+            }
+            if (lane == 63) wcnt[wave] = incl;
+            __syncthreads();
+            uint32_t at = incl - cnt, nbl = 0;
+            for (int w = 0; w < 4; ++w) {
+                if (w < wave) at += wcnt[w];
+                nbl += wcnt[w];
+            }
+#pragma unroll
+            for (int e = 0; e < kPer; ++e)
+                if ((mine >> e) & 1u) blist[at++] = (int32_t)(sub + kPer * threadIdx.x + e);
+            __syncthreads();
             // (b) re-score 8 blocks per wave and round, append in order
             for (uint32_t first0 = 0; first0 < nbl; first0 += 4 * 8) {
                 const int first = (int)first0 + 8 * wave;

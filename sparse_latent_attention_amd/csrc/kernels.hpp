@@ -46,6 +46,10 @@ struct TopkParams {
     int32_t n_blocks;  // 0: FULL validity
     int32_t block_rows;
     int32_t col_group;  // FULL validity over groups: column c valid iff c < ceil(n_visible / col_group)
+    // Candidate pool from block keys: when set, column c of row r ranks by the pool's
+    // block score of pool_keys[r * width + c] (the newest valid column pinned to +inf)
+    // instead of scores.
+    const uint32_t* pool_keys;
 };
 
 // Bytes of workspace the launch plan for (rows, width) needs (0: one workgroup per row).

@@ -123,17 +123,28 @@ __device__ __forceinline__ void find_bin(Lds& s, int nbins, uint32_t need, uint3
     __syncthreads();
 }
 
+// Rank key of a pool column from its block key (the newest column pinned to +inf).
+__device__ __forceinline__ uint32_t pool_rank_key(uint32_t bk, bool newest) {
+    return newest ? 0xff800000u : order_key(pool_value_of_block_key(bk));
+}
+
 // Positions of the full score row: column i, validity from the row geometry.
 struct RowSrc {
     const TopkParams* p;
     const float* srow;
+    const uint32_t* krow;  // pool block keys instead of scores, or null
     int64_t nv;
     int r;
     int n;
+    // the 32-bit word of column i (score bits or block key)
+    __device__ __forceinline__ uint32_t raw(int i) const { return krow ? krow[i] : __float_as_uint(srow[i]); }
+    __device__ __forceinline__ uint32_t key_of(uint32_t w, int i) const {
+        return krow ? pool_rank_key(w, i == nv - 1) : order_key(__uint_as_float(w));
+    }
     __device__ __forceinline__ bool get(int i, uint32_t& key, int32_t& col) const {
         col = i;
         if (!col_valid(*p, r, i, nv)) return false;
-        key = order_key(srow[i]);
+        key = key_of(raw(i), i);
         return true;
     }
 };
@@ -259,6 +270,7 @@ __device__ __forceinline__ RowSrc row_src(const TopkParams& p, int r) {
     src.nv = (p.pos[r] + 1) / p.ratio;
     if (p.col_group > 1) src.nv = (src.nv + p.col_group - 1) / p.col_group;
     src.srow = p.scores + (int64_t)r * p.width;
+    src.krow = p.pool_keys ? p.pool_keys + (int64_t)r * p.width : nullptr;
     src.n = (p.n_blocks == 0) ? (int)(src.nv < p.width ? src.nv : p.width) : (int)p.width;
     return src;
 }
@@ -335,11 +347,11 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const TopkParams 
     for (int cs = c0; cs < c1; cs += kSweep) {
         const int wbase = cs + wave * (kSweep / kWaves);
         // All loads first (in flight together), then the keys and ballots.
-        float vals[kPerLane];
+        uint32_t vals[kPerLane];
 #pragma unroll
         for (int j = 0; j < kPerLane; ++j) {
             const int i = wbase + 64 * j + lane;
-            vals[j] = (i < c1) ? src.srow[i] : 0.f;
+            vals[j] = (i < c1) ? src.raw(i) : 0u;
         }
         uint32_t keys[kPerLane];
         uint64_t masks[kPerLane];
@@ -347,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const TopkParams 
 #pragma unroll
         for (int j = 0; j < kPerLane; ++j) {
             const int i = wbase + 64 * j + lane;
-            keys[j] = order_key(vals[j]);
+            keys[j] = src.key_of(vals[j], i);
             const bool take = i < c1 && col_valid(p, r, i, src.nv) && (keys[j] >> 20) >= b1;
             masks[j] = __ballot(take);
             mine += (uint32_t)__builtin_popcountll(masks[j]);
@@ -385,15 +397,19 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const TopkParams p
                                                               int nseg, int cap) {
     __shared__ Lds s;
     const int r = blockIdx.x;
-    if (threadIdx.x == 0) {
-        uint32_t acc = 0, over = 0;
-        for (int g = 0; g < nseg; ++g) {
-            const uint32_t c = seg_count[(int64_t)r * nseg + g];
-            s.seg_start[g] = acc;
-            acc += c;
-            over |= c > (uint32_t)cap;
-        }
-        s.seg_start[nseg] = acc;
+    // segment starts: one count per thread (nseg <= kMaxSegs < kThreads), block-wide scan
+    const int t = threadIdx.x;
+    const uint32_t c = t < nseg ? seg_count[(int64_t)r * nseg + t] : 0u;
+    const uint64_t over_m = __ballot(c > (uint32_t)cap);
+    if ((threadIdx.x & 63) == 0) s.flags_cnt[0][threadIdx.x >> 6] = over_m != 0;
+    const uint32_t later = block_suffix_excl(c, s);  // counts of segments after t
+    if (t == 0) s.sel[1] = later + c;                // total
+    __syncthreads();
+    const uint32_t total = s.sel[1];
+    if (t <= nseg) s.seg_start[t] = total - later - c;
+    if (t == 0) {
+        uint32_t over = 0;
+        for (int w = 0; w < kWaves; ++w) over |= s.flags_cnt[0][w];
         s.sel[0] = over;
     }
     __syncthreads();

@@ -44,7 +44,7 @@ int main(void) {
   printf("csa2_attn_args sizeof %zu\n", sizeof(csa2_attn_args));
   printf("csa2_pool_args sizeof %zu\n", sizeof(csa2_pool_args));
   F(csa2_index_args, width) F(csa2_index_args, q) F(csa2_index_args, cand) F(csa2_index_args, scale) F(csa2_index_args, scores) F(csa2_index_args, key_hist) F(csa2_index_args, block_max) F(csa2_index_args, block_keys)
-  F(csa2_pool_args, n_cand) F(csa2_pool_args, width) F(csa2_pool_args, scores) F(csa2_pool_args, block_max) F(csa2_pool_args, pos) F(csa2_pool_args, cand)
+  F(csa2_pool_args, n_cand) F(csa2_pool_args, width) F(csa2_pool_args, scores) F(csa2_pool_args, block_max) F(csa2_pool_args, pos) F(csa2_pool_args, cand) F(csa2_pool_args, block_keys)
   F(csa2_topk_args, width) F(csa2_topk_args, scores) F(csa2_topk_args, out) F(csa2_topk_args, key_hist)
   F(csa2_attn_args, swa_rows) F(csa2_attn_args, q) F(csa2_attn_args, rope_inv_freq) F(csa2_attn_args, softmax_scale) F(csa2_attn_args, out)
   return 0;

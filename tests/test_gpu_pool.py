@@ -158,3 +158,42 @@ def test_pool_end_to_end_band():
         band = 2 * SCORE_TOL * float(np.max(bound[r][np.isfinite(bound[r])]))
         assert all(abs(m[b] - cut) <= band for b in diff), f"row {r}"
     print(f"[pool end to end] block differences {n_diff}")
+
+
+def _host_block_keys(s, n_vis, width):
+    """Block keys by their definition: the largest key of each 8 valid columns, a NaN counting as
+    0x007FFFFE (just below -inf), 0 for a block without valid columns."""
+    u = s.astype(np.float32).view(np.uint32).copy()
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    u[u == 0x80000000] = 0
+    key = np.where(u & 0x80000000, ~u, u | 0x80000000).astype(np.uint32)
+    key[nan] = 0x007FFFFE
+    key[:, :] = np.where(np.arange(width)[None, :] < n_vis[:, None], key, 0)
+    pad = (-width) % 8
+    return np.pad(key, ((0, 0), (0, pad))).reshape(s.shape[0], -1, 8).max(axis=2).astype(np.uint32)
+
+
+@pytest.mark.parametrize("width,n_cand,kind", [(3001, 100, "special"), (1 << 20, 2048, "normal"),
+                                               (200003, 2048, "special"), (50000, 700, "ties")])
+def test_pool_from_block_keys(width, n_cand, kind):
+    """Pool ranking from block keys (score-free route) == the oracle pool of the same scores, with NaN,
+    +-inf, FLT_MAX and ties in the scores."""
+    rows = 5
+    rng = np.random.default_rng(width + n_cand)
+    s = rng.standard_normal((rows, width)).astype(np.float32)
+    pos = np.full(rows, width - 1, dtype=np.int64)
+    if kind == "special":
+        s[0, rng.random(width) < 0.3] = np.nan
+        s[1, rng.random(width) < 0.002] = np.inf
+        s[1, rng.random(width) < 0.002] = np.float32(3.4028235e38)
+        s[2] = -np.inf
+        s[2, ::3] = np.nan                       # blocks of NaN and -inf: NaN ranks below -inf
+        s[3, :] = np.nan
+        pos[4] = 777
+    if kind == "ties":
+        s = rng.integers(0, 3, (rows, width)).astype(np.float32)
+    n_vis = np.minimum(pos + 1, width)
+    bk = torch.from_numpy(_host_block_keys(s, n_vis, width).view(np.int32)).cuda()
+    got = _pool(torch.from_numpy(pos).cuda(), 1, n_cand, block_keys=bk, width=width, block_rows=8).cpu().numpy()
+    ref = oracle.candidates.candidate_pool(s.astype(np.float64), pos, 1, 8, n_cand)
+    assert np.array_equal(got, ref)

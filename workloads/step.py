@@ -49,9 +49,10 @@ class Step:
             self.scores = None
             self.key_hist = torch.empty(rows, 4096, dtype=torch.int32, device=dev)
             self.block_keys = torch.empty(rows, -(-cfg.width // 8), dtype=torch.int32, device=dev)
+            # the pool's block scores come from the block keys: no block_max pass
+            self.block_max = None
             call_idx = csa2.prepare_indexer_score(*idx_common, None, width=cfg.width, k_scale=kIs, fp8=True,
-                                                  key_hist=self.key_hist, block_keys=self.block_keys,
-                                                  block_max=self.block_max, block_rows=cfg.block_rows)
+                                                  key_hist=self.key_hist, block_keys=self.block_keys)
             call_topk = csa2.prepare_topk_rescore(*idx_common, self.idx, self.key_hist, self.block_keys, cfg.width,
                                                   k_scale=kIs)
         else:
@@ -67,8 +68,9 @@ class Step:
                                                  block_rows=cfg.block_rows, key_hist=self.key_hist)
         self.groups = {"indexer_score": [call_idx], "topk_select": [call_topk]}
         if cfg.pool_blocks:
+            src = dict(block_keys=self.block_keys) if score_free else dict(block_max=self.block_max)
             self.groups["candidate_pool"] = [csa2.prepare_candidate_pool(
-                x["pos"], cfg.ratio, self.pool, block_max=self.block_max, width=cfg.width, block_rows=cfg.block_rows)]
+                x["pos"], cfg.ratio, self.pool, width=cfg.width, block_rows=cfg.block_rows, **src)]
         akw = dict(rope_dim=cfg.rope_dim, kv_fp4=cfg.main_dtype == "fp4", swa_fp8=cfg.swa_dtype == "fp8",
                    kv_scale=kvs)
         attn = []
