@@ -169,8 +169,8 @@ int32_t csa2_indexer_score(const csa2_index_args* args, csa2_stream_t stream);
  * block_keys are now inputs; scores and block_max are ignored).
  * out: [rows, k] int32, ascending plane rows, -1 padded.
  * Supported: FP8-E4M3 q and k with (heads, dim) = (64, 128); 1 <= k <= 2048;
- * width < 2^24 and wide enough that csa2_topk_select would split its rows
- * (csa2_topk_workspace_size(rows, width, k) > 0), else CSA2_ERR_UNSUPPORTED.
+ * rows < 1024 and 8192 <= width < 2^24 (exactly when
+ * csa2_topk_rescore_workspace_size(rows, width, k) > 0), else CSA2_ERR_UNSUPPORTED.
  */
 size_t csa2_topk_rescore_workspace_size(int32_t rows, int64_t width, int32_t k);
 

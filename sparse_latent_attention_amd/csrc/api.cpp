@@ -123,7 +123,7 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
 static void rescore_plan(int32_t rows, int64_t width, int& chunk, int& nseg) {
     chunk = nseg = 0;
     if (rows <= 0 || width <= 0 || width >= (1LL << 24)) return;
-    csa2::topk_plan(rows, width, chunk, nseg);
+    csa2::topk_plan(rows, width, chunk, nseg, 4096);
 }
 
 size_t csa2_topk_rescore_workspace_size(int32_t rows, int64_t width, int32_t k) {

@@ -59,7 +59,7 @@ hipError_t launch_topk_select(const TopkParams& p, int rows, void* workspace, hi
 // Pieces of the wide-row select used by the score-free path: the threshold bin
 // of the k-th key from a key histogram, and the exact select over per-segment
 // (key, column) lists of capacity cap (a longer list falls back to p.scores).
-void topk_plan(int rows, int64_t width, int& chunk, int& nseg);
+void topk_plan(int rows, int64_t width, int& chunk, int& nseg, int min_chunk);
 hipError_t launch_topk_threshold(const TopkParams& p, int rows, const uint32_t* key_hist, uint32_t* b1,
                                  hipStream_t stream);
 hipError_t launch_topk_final(const TopkParams& p, int rows, const uint32_t* cand_keys, const int32_t* cand_cols,

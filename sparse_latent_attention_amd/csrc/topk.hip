@@ -431,15 +431,17 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const TopkParams p
 }
 
 // ---------------------------------------------------------------------------
-// Launch plan for the wide-row path; nseg == 0 means one workgroup per row.
-void topk_plan(int rows, int64_t width, int& chunk, int& nseg) {
+// Launch plan for the wide-row path; nseg == 0 means one workgroup per row.  A
+// chunk is at least min_chunk columns (the filter pass sweeps kSweep columns
+// per workgroup at a time, so smaller chunks would leave most lanes idle).
+void topk_plan(int rows, int64_t width, int& chunk, int& nseg, int min_chunk) {
     chunk = 0;
     nseg = 0;
     if (rows <= 0 || rows >= 1024 || width < 8192) return;
     int64_t target = 4096 / rows;
     if (target < 1) target = 1;
     int64_t c = (width + target - 1) / target;
-    if (c < 4096) c = 4096;
+    if (c < min_chunk) c = min_chunk;
     const int64_t min_c = (width + kMaxSegs - 1) / kMaxSegs;
     if (c < min_c) c = min_c;
     c = (c + 1023) / 1024 * 1024;
@@ -452,7 +454,7 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 size_t topk_workspace_bytes(int rows, int64_t width) {
     int chunk, nseg;
-    topk_plan(rows, width, chunk, nseg);
+    topk_plan(rows, width, chunk, nseg, kSweep);
     if (nseg == 0) return 0;
     return align256((size_t)rows * 4096 * 4) + align256((size_t)rows * 4) + align256((size_t)rows * nseg * 4) +
            2 * align256((size_t)rows * nseg * kCap * 4);
@@ -460,7 +462,7 @@ size_t topk_workspace_bytes(int rows, int64_t width) {
 
 hipError_t launch_topk_select(const TopkParams& p, int rows, void* ws, hipStream_t stream) {
     int chunk, nseg;
-    topk_plan(rows, p.width, chunk, nseg);
+    topk_plan(rows, p.width, chunk, nseg, kSweep);
     if (nseg == 0) {
         hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
         return hipGetLastError();
