@@ -218,7 +218,8 @@ __device__ __forceinline__ void rope_angle(int64_t pos, double f, float& c, floa
 struct RawPair {
     u32x4 v[4];    // BF16: 16 B per row; F32: elements 0..3; FP8: .x .y; FP4: .x
     u32x4 v2[4];   // F32: elements 4..7
-    float s[4];    // FP8 row scale or FP4 block scale
+    float s[4];    // FP8 row scale
+    uint32_t sb[4];  // FP4: E8M0 block-scale byte (decoded at conversion, so no load waits on it)
     uint32_t valid;  // bit i: row i of the pair exists and is visible
 };
 
@@ -240,7 +241,7 @@ __device__ __forceinline__ void raw_load_row(const uint8_t* rowp, const float* f
         raw.s[i] = *fsc;
     } else {  // FP4-E2M1 with one E8M0 per 32
         raw.v[i].x = *reinterpret_cast<const uint32_t*>(rowp + 4 * x8);
-        raw.s[i] = e8m0_to_f32(e8[(8 * x8) / 32]);
+        raw.sb[i] = e8[(8 * x8) / 32];
     }
 }
 
@@ -265,7 +266,7 @@ __device__ __forceinline__ void raw_convert(const RawPair& raw, int i, Pack8<CT>
     } else if constexpr (DT == CSA2_FP4_E2M1 && sizeof(CT) == 2) {
         // E2M1 pairs straight to bf16 pairs, multiplied by the power-of-two block scale (exact).
         const uint32_t w = raw.v[i].x;
-        const float sc = raw.s[i];
+        const float sc = e8m0_to_f32(raw.sb[i]);
         const uint32_t b0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
         const uint32_t b1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
         const uint32_t b2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
@@ -276,7 +277,7 @@ __device__ __forceinline__ void raw_convert(const RawPair& raw, int i, Pack8<CT>
         o.w[3] = ok ? b3 : 0u;
     } else {
         float f[8];
-        const float sc = raw.s[i];
+        const float sc = DT == CSA2_FP4_E2M1 ? e8m0_to_f32(raw.sb[i]) : raw.s[i];
         if constexpr (DT == CSA2_FP8_E4M3) {
             const f32x2 a = fp8x2_to_f32<false>(raw.v[i].x), b = fp8x2_to_f32<true>(raw.v[i].x);
             const f32x2 c = fp8x2_to_f32<false>(raw.v[i].y), d = fp8x2_to_f32<true>(raw.v[i].y);
@@ -332,10 +333,11 @@ __device__ __forceinline__ void load_pair(const AttnParams& p, const RowCtx& c, 
             raw.valid |= (valid ? 1u : 0u) << i;
         }
     } else {
+        // the pair's 4 selected indices with one 16-byte LDS read (W and 16 * tile are multiples of 16)
+        const i32x4 ids = *reinterpret_cast<const i32x4*>(sel + tile * 16 + 4 * jb - W);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int e = tile * 16 + 4 * jb + i;
-            const int32_t id = sel[e - W];
+            const int32_t id = ids[i];
             const bool valid = id >= 0 && (int64_t)id < c.nv;  // group-causal mask
             constexpr int RB = row_bytes<KVT>(D);
             const int64_t row = c.kv_base + (valid ? id : 0);
@@ -452,7 +454,7 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16)) void attn_rows_kernel(const A
     __shared__ __attribute__((aligned(16))) CT tiles[2][G::K_ELEMS + G::V_ELEMS];
     __shared__ float rope_cs[R];
     __shared__ uint32_t vmask[kMaxTiles];  // validity bits of each tile's 16 entries, written once
-    __shared__ int32_t sel[kMaxTopk];      // this row's selected indices
+    __shared__ __attribute__((aligned(16))) int32_t sel[kMaxTopk];  // this row's selected indices
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
@@ -559,7 +561,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
     __shared__ float rope_cs[R];
     __shared__ float ml[4][2][16];
-    __shared__ int32_t sel[kMaxTopk];  // this row's selected indices
+    __shared__ __attribute__((aligned(16))) int32_t sel[kMaxTopk];  // this row's selected indices
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, li = lane & 15;

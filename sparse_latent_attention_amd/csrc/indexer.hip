@@ -458,29 +458,30 @@ __global__ __launch_bounds__(256) void indexer_fp8_full_kernel(const IndexParams
 
 // Re-scoring for the top-k of FP8 FULL scores that were never written.
 //
-// grid (nseg, rows).  Segment seg of row r covers columns [seg * chunk,
-// (seg + 1) * chunk).  b1[r] is the histogram bin holding the row's k-th
-// largest key, so every selected column has a key in bin >= b1, and so has the
-// largest key of its kKeyBlock-column block.  The workgroup collects, in column
-// order, the blocks of its segment whose block key (from the scoring pass)
-// reaches bin b1, re-scores their columns with exactly the scoring pass's
-// arithmetic (8 blocks = one 64-key step per wave), and appends the (key,
-// column) pairs of valid columns in bins >= b1, in column order, to the
-// segment's list (capacity cap = chunk, so it never overflows); seg_count gets
-// the list length.  Blocks are processed in sub-ranges of kRescoreSub.
-constexpr int kRescoreSub = 2048;
+// Segment seg of row r covers columns [seg * chunk, (seg + 1) * chunk).  b1[r]
+// is the histogram bin holding the row's k-th largest key, so every selected
+// column has a key in bin >= b1, and so has the largest key of its
+// kKeyBlock-column block.  One wave handles one segment on its own (no
+// barriers): it loads the segment's block keys (32 per lane at a time), queues
+// in column order the blocks whose key reaches bin b1 in a small LDS ring, and
+// whenever 8 are queued re-scores their columns as one 64-key step with exactly
+// the scoring pass's arithmetic, appending the (key, column) pairs of valid
+// columns in bins >= b1, in column order, to the segment's list (capacity
+// chunk, so it never overflows).  seg_count gets the list length.
+constexpr int kRescoreRing = 128;  // > 7 pending + 64 appended at once
 
 __global__ __launch_bounds__(256) void indexer_fp8_rescore_kernel(const IndexParams p, const uint32_t* b1_in,
                                                                   int chunk, int nseg, uint32_t* cand_keys,
                                                                   int32_t* cand_cols, uint32_t* seg_count) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * 128];
-    __shared__ int32_t blist[kRescoreSub];
-    __shared__ uint32_t wcnt[4];
+    __shared__ int32_t ring[4][kRescoreRing];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, li = lane & 15;
     const int ksub = lane >> 3, kchunk = lane & 7;
-    const int r = blockIdx.y, seg = blockIdx.x;
+    const int r = blockIdx.y;
+    const int seg = 4 * blockIdx.x + wave;
+    if (seg >= nseg) return;  // no barriers in this kernel: waves are independent
 
     const int64_t nv = uniform64((p.pos[r] + 1) / p.ratio);
     const int64_t base = uniform64(p.row_base[r]);
@@ -493,6 +494,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_rescore_kernel(const IndexPar
     uint32_t* okeys = cand_keys + ((int64_t)r * nseg + seg) * chunk;
     int32_t* ocols = cand_cols + ((int64_t)r * nseg + seg) * chunk;
     uint8_t* my = stage[wave];
+    int32_t* q8 = ring[wave];
 
     i32x8 qa[4];
     float wr[4][4];
@@ -506,91 +508,72 @@ __global__ __launch_bounds__(256) void indexer_fp8_rescore_kernel(const IndexPar
         const_cast<float*>(p.k_scale + base), (short)0, n_rows * 4, kRsrcWord3);
 
     uint32_t n_out = 0;
+    int head = 0, tail = 0;  // wave-uniform ring indices (entries head..tail-1 pending)
+    // Re-scores the first cnt (1..8) queued blocks as one step and appends its candidates.
+    auto rescore = [&](int cnt) {
+        u32x4 buf[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            // rows of block j; past the queue: an offset beyond the descriptor -> zeros
+            const int row = j < cnt ? q8[(head + j) % kRescoreRing] * kKeyBlock + ksub : n_rows;
+            buf[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, row * 128 + 16 * kchunk, 0,
+                                                                                     kNT));
+        }
+        const int my_blk = lane / kKeyBlock;
+        const int64_t col = my_blk < cnt
+            ? (int64_t)q8[(head + my_blk) % kRescoreRing] * kKeyBlock + (lane % kKeyBlock) : n_valid;
+        const float ksc = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(col < n_valid ? col : n_valid) * 4, 0, 0));
+        fp8_stage_put(my, buf, ksub, kchunk);
+        float v[4];
+        fp8_step_sums(my, qa, wr, g, li, v);
+        const float kk = reduce_scatter(v, lane);
+        const bool valid = col < n_valid;
+        const float sc = p.scale * ksc;
+        const uint32_t key = order_key(sc * kk);
+        const bool take = valid && (key >> 20) >= b1;
+        const uint64_t m = __ballot(take);
+        if (take) {
+            const uint32_t at = n_out + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            okeys[at] = key;
+            ocols[at] = (int32_t)col;
+        }
+        n_out += (uint32_t)__builtin_popcountll(m);
+        head += cnt;
+    };
+
     if (c_hi > c_lo) {
         const int64_t blk_lo = c_lo / kKeyBlock, blk_hi = (c_hi + kKeyBlock - 1) / kKeyBlock;
-        for (int64_t sub = blk_lo; sub < blk_hi; sub += kRescoreSub) {
-            const int64_t sub_hi = sub + kRescoreSub < blk_hi ? sub + kRescoreSub : blk_hi;
-            // (a) candidate blocks of the sub-range, in order: thread t owns blocks
-            // sub + 8t .. sub + 8t + 7 (all loads issued at once), then a block-wide scan
-            constexpr int kPer = kRescoreSub / 256;
-            uint32_t bk[kPer];
+        constexpr int kBatch = 32;  // block keys per lane per batch, loaded at once
+        for (int64_t b0 = blk_lo; b0 < blk_hi; b0 += 64 * kBatch) {
+            uint32_t bk[kBatch];
 #pragma unroll
-            for (int e = 0; e < kPer; ++e) {
-                const int64_t i = sub + kPer * threadIdx.x + e;
-                bk[e] = i < sub_hi ? bkeys[i] : 0u;
-            }
-            uint32_t mine = 0;
-#pragma unroll
-            for (int e = 0; e < kPer; ++e) mine |= (uint32_t)(bk[e] != 0u && (bk[e] >> 20) >= b1) << e;
-            const uint32_t cnt = (uint32_t)__builtin_popcount(mine);
-            uint32_t incl = cnt;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
-                if (lane >= o) incl += y;
-            }
-            if (lane == 63) wcnt[wave] = incl;
-            __syncthreads();
-            uint32_t at = incl - cnt, nbl = 0;
-            for (int w = 0; w < 4; ++w) {
-                if (w < wave) at += wcnt[w];
-                nbl += wcnt[w];
+            for (int i = 0; i < kBatch; ++i) {
+                const int64_t b = b0 + 64 * i + lane;
+                bk[i] = b < blk_hi ? bkeys[b] : 0u;
             }
 #pragma unroll
-            for (int e = 0; e < kPer; ++e)
-                if ((mine >> e) & 1u) blist[at++] = (int32_t)(sub + kPer * threadIdx.x + e);
-            __syncthreads();
-            // (b) re-score 8 blocks per wave and round, append in order
-            for (uint32_t first0 = 0; first0 < nbl; first0 += 4 * 8) {
-                const int first = (int)first0 + 8 * wave;
-                const int cnt = (int)nbl - first;  // blocks of this wave's step (<= 0: idle)
-                u32x4 buf[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    // rows of block j; past the list: an offset beyond the descriptor -> zeros
-                    const int row = j < cnt ? blist[first + j] * kKeyBlock + ksub : n_rows;
-                    buf[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, row * 128 + 16 * kchunk,
-                                                                                             0, kNT));
-                }
-                const int my_blk = lane / kKeyBlock;
-                const int64_t col = my_blk < cnt ? (int64_t)blist[first + my_blk] * kKeyBlock + (lane % kKeyBlock)
-                                                 : n_valid;
-                const float ksc = __builtin_bit_cast(
-                    float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(col < n_valid ? col : n_valid) * 4, 0, 0));
-                fp8_stage_put(my, buf, ksub, kchunk);
-                float v[4];
-                fp8_step_sums(my, qa, wr, g, li, v);
-                const float kk = reduce_scatter(v, lane);
-                const bool valid = col < n_valid;
-                const float sc = p.scale * ksc;
-                const uint32_t key = order_key(sc * kk);
-                const bool take = valid && (key >> 20) >= b1;
+            for (int i = 0; i < kBatch; ++i) {
+                const bool take = bk[i] != 0u && (bk[i] >> 20) >= b1;
                 const uint64_t m = __ballot(take);
-                if (lane == 0) wcnt[wave] = (uint32_t)__builtin_popcountll(m);
-                __syncthreads();
-                uint32_t before = n_out, all = 0;
-                for (int w = 0; w < 4; ++w) {
-                    if (w < wave) before += wcnt[w];
-                    all += wcnt[w];
-                }
-                if (take) {
-                    const uint32_t at = before + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                    okeys[at] = key;
-                    ocols[at] = (int32_t)col;
-                }
-                n_out += all;
-                __syncthreads();
+                if (take)
+                    q8[(tail + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))) %
+                       kRescoreRing] = (int32_t)(b0 + 64 * i + lane);
+                tail += __builtin_popcountll(m);
+                while (tail - head >= 8) rescore(8);
             }
         }
+        if (tail > head) rescore(tail - head);
     }
-    if (threadIdx.x == 0) seg_count[(int64_t)r * nseg + seg] = n_out;
+    if (lane == 0) seg_count[(int64_t)r * nseg + seg] = n_out;
 }
 
 hipError_t launch_indexer_rescore(const IndexParams& p, int rows, const uint32_t* b1, int chunk, int nseg,
                                   uint32_t* cand_keys, int32_t* cand_cols, uint32_t* seg_count, hipStream_t stream) {
-    hipLaunchKernelGGL(indexer_fp8_rescore_kernel, dim3((unsigned)nseg, (unsigned)rows), dim3(256), 0, stream, p, b1,
-                       chunk, nseg, cand_keys, cand_cols, seg_count);
+    hipLaunchKernelGGL(indexer_fp8_rescore_kernel, dim3((unsigned)((nseg + 3) / 4), (unsigned)rows), dim3(256), 0,
+                       stream, p, b1, chunk, nseg, cand_keys, cand_cols, seg_count);
     return hipGetLastError();
 }
 

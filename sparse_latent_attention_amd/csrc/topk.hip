@@ -129,17 +129,19 @@ __device__ __forceinline__ uint32_t pool_rank_key(uint32_t bk, bool newest) {
 }
 
 // Positions of the full score row: column i, validity from the row geometry.
+// POOL: the row holds candidate-pool block keys instead of scores.
+template <bool POOL>
 struct RowSrc {
     const TopkParams* p;
     const float* srow;
-    const uint32_t* krow;  // pool block keys instead of scores, or null
+    const uint32_t* krow;
     int64_t nv;
     int r;
     int n;
     // the 32-bit word of column i (score bits or block key)
-    __device__ __forceinline__ uint32_t raw(int i) const { return krow ? krow[i] : __float_as_uint(srow[i]); }
+    __device__ __forceinline__ uint32_t raw(int i) const { return POOL ? krow[i] : __float_as_uint(srow[i]); }
     __device__ __forceinline__ uint32_t key_of(uint32_t w, int i) const {
-        return krow ? pool_rank_key(w, i == nv - 1) : order_key(__uint_as_float(w));
+        return POOL ? pool_rank_key(w, i == nv - 1) : order_key(__uint_as_float(w));
     }
     __device__ __forceinline__ bool get(int i, uint32_t& key, int32_t& col) const {
         col = i;
@@ -167,6 +169,19 @@ struct CandSrc {
         const int j = i - (int)seg_start[lo];
         key = keys[(int64_t)lo * cap + j];
         col = cols[(int64_t)lo * cap + j];
+        return true;
+    }
+};
+
+// Candidates copied into LDS: a dense, column-ordered list.
+constexpr int kLdsCand = 4096;
+struct LdsCandSrc {
+    const uint32_t* keys;
+    const int32_t* cols;
+    int n;
+    __device__ __forceinline__ bool get(int i, uint32_t& key, int32_t& col) const {
+        key = keys[i];
+        col = cols[i];
         return true;
     }
 };
@@ -263,14 +278,15 @@ __device__ __forceinline__ void select_core(const Src& src, const TopkParams& p,
     for (int i = (int)goal + tid; i < p.k; i += kThreads) orow[i] = -1;
 }
 
-__device__ __forceinline__ RowSrc row_src(const TopkParams& p, int r) {
-    RowSrc src;
+template <bool POOL>
+__device__ __forceinline__ RowSrc<POOL> row_src(const TopkParams& p, int r) {
+    RowSrc<POOL> src;
     src.p = &p;
     src.r = r;
     src.nv = (p.pos[r] + 1) / p.ratio;
     if (p.col_group > 1) src.nv = (src.nv + p.col_group - 1) / p.col_group;
     src.srow = p.scores + (int64_t)r * p.width;
-    src.krow = p.pool_keys ? p.pool_keys + (int64_t)r * p.width : nullptr;
+    src.krow = POOL ? p.pool_keys + (int64_t)r * p.width : nullptr;
     src.n = (p.n_blocks == 0) ? (int)(src.nv < p.width ? src.nv : p.width) : (int)p.width;
     return src;
 }
@@ -278,10 +294,11 @@ __device__ __forceinline__ RowSrc row_src(const TopkParams& p, int r) {
 }  // namespace
 
 // One workgroup per row over the full score row.
+template <bool POOL>
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(const TopkParams p) {
     __shared__ Lds s;
     const int r = blockIdx.x;
-    select_core(row_src(p, r), p, r, s);
+    select_core(row_src<POOL>(p, r), p, r, s);
 }
 
 // ---- wide-row path ----------------------------------------------------------
@@ -291,11 +308,12 @@ __global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* buf, int64_t n
 }
 
 // grid (nseg, rows): 12-bit histogram of one chunk, added into hist[r][4096].
+template <bool POOL>
 __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const TopkParams p, uint32_t* hist, int chunk) {
     __shared__ uint32_t h[4096];
     const int r = blockIdx.y;
     const int tid = threadIdx.x;
-    const RowSrc src = row_src(p, r);
+    const RowSrc<POOL> src = row_src<POOL>(p, r);
     for (int b = tid; b < 4096; b += kThreads) h[b] = 0;
     __syncthreads();
     const int c0 = blockIdx.x * chunk;
@@ -331,13 +349,14 @@ __global__ __launch_bounds__(kThreads) void topk_threshold_kernel(const TopkPara
 constexpr int kPerLane = 16;
 constexpr int kSweep = kThreads * kPerLane;
 
+template <bool POOL>
 __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const TopkParams p, const uint32_t* b1_in,
                                                                uint32_t* cand_keys, int32_t* cand_cols,
                                                                uint32_t* seg_count, int chunk, int nseg) {
     __shared__ uint32_t cnt[2][kWaves];
     const int r = blockIdx.y, seg = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const RowSrc src = row_src(p, r);
+    const RowSrc<POOL> src = row_src<POOL>(p, r);
     const uint32_t b1 = b1_in[r];
     const int64_t base = ((int64_t)r * nseg + seg) * kCap;
     const int c0 = seg * chunk;
@@ -392,10 +411,13 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const TopkParams 
 
 // grid rows: exact select over the candidates (or the full row after an overflow:
 // a list longer than its capacity `cap`).
+template <bool POOL>
 __global__ __launch_bounds__(kThreads) void topk_final_kernel(const TopkParams p, const uint32_t* cand_keys,
                                                               const int32_t* cand_cols, const uint32_t* seg_count,
                                                               int nseg, int cap) {
     __shared__ Lds s;
+    __shared__ uint32_t lkeys[kLdsCand];
+    __shared__ int32_t lcols[kLdsCand];
     const int r = blockIdx.x;
     // segment starts: one count per thread (nseg <= kMaxSegs < kThreads), block-wide scan
     const int t = threadIdx.x;
@@ -417,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const TopkParams p
     const int n = (int)s.seg_start[nseg];
     __syncthreads();
     if (overflow) {
-        select_core(row_src(p, r), p, r, s);
+        select_core(row_src<POOL>(p, r), p, r, s);
         return;
     }
     CandSrc src;
@@ -427,13 +449,31 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const TopkParams p
     src.nseg = nseg;
     src.cap = cap;
     src.n = n;
-    select_core(src, p, r, s);
+    if (n > kLdsCand) {
+        select_core(src, p, r, s);
+        return;
+    }
+    // the usual case: few candidates, read once into LDS and selected from there
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+        uint32_t key;
+        int32_t col;
+        src.get(i, key, col);
+        lkeys[i] = key;
+        lcols[i] = col;
+    }
+    __syncthreads();
+    LdsCandSrc lsrc;
+    lsrc.keys = lkeys;
+    lsrc.cols = lcols;
+    lsrc.n = n;
+    select_core(lsrc, p, r, s);
 }
 
 // ---------------------------------------------------------------------------
 // Launch plan for the wide-row path; nseg == 0 means one workgroup per row.  A
-// chunk is at least min_chunk columns (the filter pass sweeps kSweep columns
-// per workgroup at a time, so smaller chunks would leave most lanes idle).
+// chunk is at least 4096 columns, and min_chunk when that still leaves >= 512
+// workgroups (the filter pass sweeps kSweep columns per workgroup at a time, so
+// smaller chunks leave lanes idle).
 void topk_plan(int rows, int64_t width, int& chunk, int& nseg, int min_chunk) {
     chunk = 0;
     nseg = 0;
@@ -441,7 +481,9 @@ void topk_plan(int rows, int64_t width, int& chunk, int& nseg, int min_chunk) {
     int64_t target = 4096 / rows;
     if (target < 1) target = 1;
     int64_t c = (width + target - 1) / target;
-    if (c < min_chunk) c = min_chunk;
+    if (c < 4096) c = 4096;
+    // full sweeps when that still leaves >= 512 workgroups
+    if (c < min_chunk && (int64_t)rows * ((width + min_chunk - 1) / min_chunk) >= 512) c = min_chunk;
     const int64_t min_c = (width + kMaxSegs - 1) / kMaxSegs;
     if (c < min_c) c = min_c;
     c = (c + 1023) / 1024 * 1024;
@@ -461,10 +503,12 @@ size_t topk_workspace_bytes(int rows, int64_t width) {
 }
 
 hipError_t launch_topk_select(const TopkParams& p, int rows, void* ws, hipStream_t stream) {
+    const bool pool = p.pool_keys != nullptr;
     int chunk, nseg;
     topk_plan(rows, p.width, chunk, nseg, kSweep);
     if (nseg == 0) {
-        hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+        if (pool) hipLaunchKernelGGL(topk_select_kernel<true>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+        else hipLaunchKernelGGL(topk_select_kernel<false>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
         return hipGetLastError();
     }
     char* w = reinterpret_cast<char*>(ws);
@@ -483,15 +527,24 @@ hipError_t launch_topk_select(const TopkParams& p, int rows, void* ws, hipStream
         const int64_t nh = (int64_t)rows * 4096;
         hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)),
                            dim3(256), 0, stream, hist, nh);
-        hipLaunchKernelGGL(topk_hist_kernel, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0, stream, p, hist,
-                           chunk);
+        if (pool) hipLaunchKernelGGL(topk_hist_kernel<true>, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0,
+                                     stream, p, hist, chunk);
+        else hipLaunchKernelGGL(topk_hist_kernel<false>, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0,
+                                stream, p, hist, chunk);
         h = hist;
     }
     hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, h, b1);
-    hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0, stream, p, b1, keys,
-                       cols, seg_count, chunk, nseg);
-    hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, keys, cols, seg_count,
-                       nseg, kCap);
+    if (pool) {
+        hipLaunchKernelGGL(topk_filter_kernel<true>, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0, stream, p,
+                           b1, keys, cols, seg_count, chunk, nseg);
+        hipLaunchKernelGGL(topk_final_kernel<true>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, keys, cols,
+                           seg_count, nseg, kCap);
+    } else {
+        hipLaunchKernelGGL(topk_filter_kernel<false>, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0, stream,
+                           p, b1, keys, cols, seg_count, chunk, nseg);
+        hipLaunchKernelGGL(topk_final_kernel<false>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, keys, cols,
+                           seg_count, nseg, kCap);
+    }
     return hipGetLastError();
 }
 
@@ -503,8 +556,8 @@ hipError_t launch_topk_threshold(const TopkParams& p, int rows, const uint32_t* 
 
 hipError_t launch_topk_final(const TopkParams& p, int rows, const uint32_t* cand_keys, const int32_t* cand_cols,
                              const uint32_t* seg_count, int nseg, int cap, hipStream_t stream) {
-    hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, cand_keys, cand_cols,
-                       seg_count, nseg, cap);
+    hipLaunchKernelGGL(topk_final_kernel<false>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, cand_keys,
+                       cand_cols, seg_count, nseg, cap);
     return hipGetLastError();
 }
 

@@ -208,7 +208,7 @@ def test_topk_wide_rows(rows, width, k, kind):
 @pytest.mark.parametrize("name,kw", [
     ("lowp_full_decode_1m", dict(batch=6, q_tokens=6, context=100003, ragged=True)),
     ("full_decode_64k", dict(batch=5, q_tokens=5, context=40000, ragged=True)),
-    ("reindex_decode_1m", dict(batch=5, q_tokens=5, context=300000, ragged=True)),
+    ("reindex_decode_1m", dict(batch=5, q_tokens=5, context=300000, ragged=True, n_blocks=8192)),
 ])
 def test_key_hist_path(name, kw):
     """Indexer-built key histogram == host recount of the GPU scores; top-k through it is exact."""
