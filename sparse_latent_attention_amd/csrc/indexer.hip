@@ -462,19 +462,20 @@ __global__ __launch_bounds__(256) void indexer_fp8_full_kernel(const IndexParams
 // is the histogram bin holding the row's k-th largest key, so every selected
 // column has a key in bin >= b1, and so has the largest key of its
 // kKeyBlock-column block.  One wave handles one segment on its own (no
-// barriers): it loads the segment's block keys (32 per lane at a time), queues
-// in column order the blocks whose key reaches bin b1 in a small LDS ring, and
-// whenever 8 are queued re-scores their columns as one 64-key step with exactly
-// the scoring pass's arithmetic, appending the (key, column) pairs of valid
-// columns in bins >= b1, in column order, to the segment's list (capacity
-// chunk, so it never overflows).  seg_count gets the list length.
-constexpr int kRescoreRing = 128;  // > 7 pending + 64 appended at once
+// barriers): per batch of 2048 blocks it loads the block keys (32 per lane, at
+// once), queues in column order the blocks whose key reaches bin b1 in an LDS
+// list, then re-scores the queue 8 blocks (one 64-key step) at a time with
+// exactly the scoring pass's arithmetic, appending the (key, column) pairs of
+// valid columns in bins >= b1, in column order, to the segment's list
+// (capacity chunk, so it never overflows).  seg_count gets the list length.
+constexpr int kRescoreBatch = 16;                  // block keys per lane per batch
+constexpr int kRescoreQueue = 64 * kRescoreBatch;  // blocks per batch
 
 __global__ __launch_bounds__(256) void indexer_fp8_rescore_kernel(const IndexParams p, const uint32_t* b1_in,
                                                                   int chunk, int nseg, uint32_t* cand_keys,
                                                                   int32_t* cand_cols, uint32_t* seg_count) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * 128];
-    __shared__ int32_t ring[4][kRescoreRing];
+    __shared__ int32_t queue[4][kRescoreQueue];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, li = lane & 15;
@@ -494,7 +495,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_rescore_kernel(const IndexPar
     uint32_t* okeys = cand_keys + ((int64_t)r * nseg + seg) * chunk;
     int32_t* ocols = cand_cols + ((int64_t)r * nseg + seg) * chunk;
     uint8_t* my = stage[wave];
-    int32_t* q8 = ring[wave];
+    int32_t* q8 = queue[wave];
 
     i32x8 qa[4];
     float wr[4][4];
@@ -508,20 +509,19 @@ __global__ __launch_bounds__(256) void indexer_fp8_rescore_kernel(const IndexPar
         const_cast<float*>(p.k_scale + base), (short)0, n_rows * 4, kRsrcWord3);
 
     uint32_t n_out = 0;
-    int head = 0, tail = 0;  // wave-uniform ring indices (entries head..tail-1 pending)
-    // Re-scores the first cnt (1..8) queued blocks as one step and appends its candidates.
-    auto rescore = [&](int cnt) {
+    // Re-scores queued blocks head .. head+cnt-1 (cnt 1..8) as one step and appends their candidates.
+    auto rescore = [&](int head, int cnt) {
         u32x4 buf[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             // rows of block j; past the queue: an offset beyond the descriptor -> zeros
-            const int row = j < cnt ? q8[(head + j) % kRescoreRing] * kKeyBlock + ksub : n_rows;
+            const int row = j < cnt ? q8[head + j] * kKeyBlock + ksub : n_rows;
             buf[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, row * 128 + 16 * kchunk, 0,
                                                                                      kNT));
         }
         const int my_blk = lane / kKeyBlock;
         const int64_t col = my_blk < cnt
-            ? (int64_t)q8[(head + my_blk) % kRescoreRing] * kKeyBlock + (lane % kKeyBlock) : n_valid;
+            ? (int64_t)q8[head + my_blk] * kKeyBlock + (lane % kKeyBlock) : n_valid;
         const float ksc = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(col < n_valid ? col : n_valid) * 4, 0, 0));
         fp8_stage_put(my, buf, ksub, kchunk);
@@ -540,32 +540,30 @@ __global__ __launch_bounds__(256) void indexer_fp8_rescore_kernel(const IndexPar
             ocols[at] = (int32_t)col;
         }
         n_out += (uint32_t)__builtin_popcountll(m);
-        head += cnt;
     };
 
     if (c_hi > c_lo) {
         const int64_t blk_lo = c_lo / kKeyBlock, blk_hi = (c_hi + kKeyBlock - 1) / kKeyBlock;
-        constexpr int kBatch = 32;  // block keys per lane per batch, loaded at once
-        for (int64_t b0 = blk_lo; b0 < blk_hi; b0 += 64 * kBatch) {
-            uint32_t bk[kBatch];
+        for (int64_t b0 = blk_lo; b0 < blk_hi; b0 += kRescoreQueue) {
+            uint32_t bk[kRescoreBatch];
 #pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
+            for (int i = 0; i < kRescoreBatch; ++i) {
                 const int64_t b = b0 + 64 * i + lane;
                 bk[i] = b < blk_hi ? bkeys[b] : 0u;
             }
+            int n_q = 0;  // wave-uniform queue length
 #pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
+            for (int i = 0; i < kRescoreBatch; ++i) {
                 const bool take = bk[i] != 0u && (bk[i] >> 20) >= b1;
                 const uint64_t m = __ballot(take);
                 if (take)
-                    q8[(tail + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))) %
-                       kRescoreRing] = (int32_t)(b0 + 64 * i + lane);
-                tail += __builtin_popcountll(m);
-                while (tail - head >= 8) rescore(8);
+                    q8[n_q + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
+                        (int32_t)(b0 + 64 * i + lane);
+                n_q += __builtin_popcountll(m);
             }
+            for (int h = 0; h < n_q; h += 8) rescore(h, n_q - h < 8 ? n_q - h : 8);
         }
-        if (tail > head) rescore(tail - head);
     }
     if (lane == 0) seg_count[(int64_t)r * nseg + seg] = n_out;
 }
