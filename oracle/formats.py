@@ -20,7 +20,17 @@ Layouts decoded here are the ones the stored planes use:
   FP8 SWA ring uses the same per-row form).
 * FP4 rows: ``packed[N, D/2]`` uint8, element 2i in the low nibble and 2i+1 in
   the high nibble, with one E8M0 byte per 32 consecutive elements in
-  ``scales[N, D/32]`` (MXFP4 block size 32).
+  ``scales[N, D/32]`` (MXFP4 block size 32).  The pages' FP4 index plane
+  (68 B per row: 64 bytes of E2M1 plus one E8M0 per 32, "DeepSeek-V4.1-Flash
+  结构说明" §5.3; "万字长文解析DeekSeekV4.1flash" §10.6) and FP4 indexer query
+  are this format.
+* Packed FP4 main rows of the pages' 890 B/token configuration: 288 bytes per
+  512-element row, the 256 bytes of E2M1 (packed as above) followed by 32
+  E4M3 scales, one per 16 consecutive elements, with no second-level scale
+  ("DeepSeek-V4.1-Flash 架构解剖", "换成 packed FP4 主池"; the essay §10.7).
+* FP8 SWA rows of that configuration: 528 bytes per 512-element row, 512
+  E4M3 codes followed by 16 E8M0 scales, one per 32 elements (the anatomy
+  page, same section).
 
 Pins (tests/test_oracle_formats.py): every FP8 code against torch's
 independent float8_e4m3fn conversion and against spot values fixed by the
@@ -120,3 +130,42 @@ def decode_fp4_rows(packed, scales):
     sc = e8m0_to_f64(scales)  # [..., N, D/32]
     assert sc.shape[-1] * 32 == d and sc.shape[-2] == n
     return vals * np.repeat(sc, 32, axis=-1)
+
+
+def _unpack_e2m1(packed):
+    """Packed E2M1 bytes [..., B] -> codes [..., 2B] (element 2i = low nibble of byte i)."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    codes = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.uint8)
+    codes[..., 0::2] = packed & 0x0F
+    codes[..., 1::2] = packed >> 4
+    return codes
+
+
+def decode_nvfp4_rows(rows):
+    """288-byte-per-512 rows: packed E2M1 then one E4M3 scale per 16 elements -> float64 [..., D]."""
+    global _E2M1, _E4M3
+    if _E2M1 is None:
+        _E2M1 = e2m1_table()
+    if _E4M3 is None:
+        _E4M3 = e4m3fn_table()
+    rows = np.asarray(rows, dtype=np.uint8)
+    nb = rows.shape[-1]
+    assert (nb * 16) % 9 == 0
+    d = nb * 16 // 9                       # D/2 value bytes + D/16 scale bytes
+    vals = _E2M1[_unpack_e2m1(rows[..., : d // 2])]
+    scales = _E4M3[rows[..., d // 2: d // 2 + d // 16]]
+    return vals * np.repeat(scales, 16, axis=-1)
+
+
+def decode_fp8_e8m0_rows(rows):
+    """528-byte-per-512 rows: E4M3 codes then one E8M0 scale per 32 elements -> float64 [..., D]."""
+    global _E4M3
+    if _E4M3 is None:
+        _E4M3 = e4m3fn_table()
+    rows = np.asarray(rows, dtype=np.uint8)
+    nb = rows.shape[-1]
+    assert (nb * 32) % 33 == 0
+    d = nb * 32 // 33                      # D value bytes + D/32 scale bytes
+    vals = _E4M3[rows[..., :d]]
+    scales = e8m0_to_f64(rows[..., d: d + d // 32])
+    return vals * np.repeat(scales, 32, axis=-1)

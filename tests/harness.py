@@ -41,6 +41,10 @@ def to_numpy_f64(t, fmt, scale=None):
         return formats.decode_fp8_rows(t.numpy(), scale.detach().cpu().numpy())
     if fmt == "fp4":
         return formats.decode_fp4_rows(t.numpy(), scale.detach().cpu().numpy())
+    if fmt == "nvfp4":
+        return formats.decode_nvfp4_rows(t.numpy())
+    if fmt == "fp8mx":
+        return formats.decode_fp8_e8m0_rows(t.numpy())
     raise ValueError(fmt)
 
 
@@ -148,7 +152,8 @@ def oracle_planes(cfg, x):
 
 
 def oracle_index_inputs(cfg, x, rows):
-    q = to_numpy_f64(x["qI"][rows], "fp8" if cfg.idx_dtype == "fp8" else cfg.idx_dtype)
+    qs = None if x.get("qI_scale") is None else x["qI_scale"][rows]
+    q = to_numpy_f64(x["qI"][rows], cfg.idx_dtype, qs)
     w = x["w"][rows].detach().cpu().numpy().astype(np.float64)
     return q, w
 

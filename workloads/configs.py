@@ -32,9 +32,9 @@ class Csa2Config:
     n_blocks: int = 0      # REINDEX candidate blocks per query
     block_rows: int = 8    # rows per candidate block
     reuse_layers: int = 0  # prefill: REUSE layers that attend with the FULL layer's indices
-    main_dtype: str = "bf16"   # f32 | bf16 | fp4
-    swa_dtype: str = "bf16"    # f32 | bf16 | fp8
-    idx_dtype: str = "bf16"    # f32 | bf16 | fp8 (index plane and indexer query)
+    main_dtype: str = "bf16"   # f32 | bf16 | fp4 (E8M0 / 32, planar) | nvfp4 (288 B rows: E4M3 / 16 inline)
+    swa_dtype: str = "bf16"    # f32 | bf16 | fp8 (row scale) | fp8mx (528 B rows: E8M0 / 32 inline)
+    idx_dtype: str = "bf16"    # f32 | bf16 | fp8 | fp4 (MXFP4) -- index plane and indexer query
     q_dtype: str = "bf16"      # f32 | bf16
     out_dtype: str = "bf16"    # f32 | bf16
     value_scale: str = "unit"  # "unit": N(0,1); "inv_sqrt_d": N(0,1)/sqrt(dim) for q, latent and index vectors
@@ -86,10 +86,16 @@ CONFIGS = {
         name="lowp_pool_decode_1m", phase="decode", index_mode="full", batch=64, q_tokens=64, context=1 << 20,
         ratio=1, main_dtype="fp4", swa_dtype="fp8", idx_dtype="fp8", value_scale="inv_sqrt_d", pool_blocks=2048,
         **_COMMON),
+    # The pages' own byte formats (the 890 B/token pool): packed FP4 main rows with an E4M3 scale per 16
+    # (288 B), FP8 SWA rows with an E8M0 scale per 32 (528 B), an MXFP4 index plane (64 + 4 B per row) and
+    # an MXFP4 indexer query; unit-scale values, like the post-RMSNorm latents the pages quantize.
+    "pages_fp4_decode_1m": Csa2Config(
+        name="pages_fp4_decode_1m", phase="decode", index_mode="full", batch=64, q_tokens=64, context=1 << 20,
+        ratio=1, main_dtype="nvfp4", swa_dtype="fp8mx", idx_dtype="fp4", value_scale="unit", **_COMMON),
 }
 
 CONFIG_ORDER = ["tiny_full_fp32", "full_decode_64k", "prefill_4096_at_128k", "reindex_decode_1m",
-                "lowp_full_decode_1m", "lowp_pool_decode_1m"]
+                "lowp_full_decode_1m", "lowp_pool_decode_1m", "pages_fp4_decode_1m"]
 
 
 def get_config(name):

@@ -21,7 +21,13 @@ Recipe (all draws from one torch.Generator seeded with ``seed`` on ``device``):
   figure describes.
 * FP4-E2M1 rows: one E8M0 scale per 32 elements, 2^ceil(log2(amax/6)); the
   scaled values are rounded to the nearest E2M1 magnitude (ties to the even
-  code) and packed two per byte, element 2i in the low nibble.
+  code) and packed two per byte, element 2i in the low nibble.  The FP4 index
+  plane and FP4 indexer query use this format (no scale folded into w).
+* Packed FP4 main rows (288 B per 512): E2M1 as above with one E4M3 scale per
+  16 elements, the scale being amax/6 rounded to E4M3 (at least 2^-9); values
+  beyond 6 after scaling saturate.
+* FP8 rows with E8M0 block scales (528 B per 512): one scale per 32 elements,
+  2^ceil(log2(amax/448)); values cast with float8_e4m3fn.
 
 Nothing here scores, selects, normalises or rotates.
 """
@@ -58,6 +64,43 @@ def encode_fp8_rows(x):
     return codes.contiguous(), scale.to(torch.float32).contiguous()
 
 
+def _e2m1_codes(y):
+    """float32 -> E2M1 codes (nearest magnitude, ties to the even code, saturating at 6)."""
+    mag = y.abs().clamp(max=6.0)
+    grid = torch.tensor(_E2M1_MAG, device=y.device, dtype=torch.float32)
+    mids = (grid[1:] + grid[:-1]) * 0.5
+    code = torch.bucketize(mag, mids, right=False)            # ties go to the lower magnitude
+    tie = mag == mids[code.clamp(max=6)]
+    code = torch.where(tie & (code % 2 == 1), code + 1, code)  # ... unless that code is odd
+    return code.to(torch.uint8) | ((y < 0).to(torch.uint8) << 3)
+
+
+def encode_nvfp4_rows(x):
+    """x float32 [..., D] -> rows uint8 [..., D/2 + D/16]: packed E2M1, then one E4M3 scale per 16."""
+    shp = x.shape
+    d = shp[-1]
+    assert d % 16 == 0
+    xb = x.reshape(*shp[:-1], d // 16, 16)
+    amax = xb.abs().amax(dim=-1)
+    sc = (amax / 6.0).clamp(min=2.0 ** -9, max=448.0).to(torch.float8_e4m3fn)
+    y = xb / sc.to(torch.float32).unsqueeze(-1)
+    code = _e2m1_codes(y).reshape(*shp[:-1], d)
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return torch.cat([packed, sc.view(torch.uint8)], dim=-1).contiguous()
+
+
+def encode_fp8_e8m0_rows(x):
+    """x float32 [..., D] -> rows uint8 [..., D + D/32]: E4M3 codes, then one E8M0 scale per 32."""
+    shp = x.shape
+    d = shp[-1]
+    assert d % 32 == 0
+    xb = x.reshape(*shp[:-1], d // 32, 32)
+    amax = xb.abs().amax(dim=-1)
+    e = torch.where(amax > 0, torch.ceil(torch.log2(amax / 448.0)), torch.full_like(amax, -127.0)).clamp_(-127.0, 127.0)
+    codes = (xb / torch.exp2(e).unsqueeze(-1)).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return torch.cat([codes.reshape(*shp[:-1], d), (e + 127.0).to(torch.uint8)], dim=-1).contiguous()
+
+
 def encode_fp4_rows(x):
     """x float32 [..., D] -> (packed uint8 [..., D/2], E8M0 scales uint8 [..., D/32])."""
     shp = x.shape
@@ -68,14 +111,7 @@ def encode_fp4_rows(x):
     e = torch.where(amax > 0, torch.ceil(torch.log2(amax / 6.0)), torch.full_like(amax, -127.0))
     e = e.clamp_(-127.0, 127.0)
     y = xb / torch.exp2(e).unsqueeze(-1)
-    mag = y.abs().clamp_(max=6.0)
-    grid = torch.tensor(_E2M1_MAG, device=x.device, dtype=torch.float32)
-    mids = (grid[1:] + grid[:-1]) * 0.5
-    code = torch.bucketize(mag, mids, right=False)            # ties go to the lower magnitude
-    tie = mag == mids[code.clamp(max=6)]
-    code = torch.where(tie & (code % 2 == 1), code + 1, code)  # ... unless that code is odd
-    code = code.to(torch.uint8) | ((y < 0).to(torch.uint8) << 3)
-    code = code.reshape(*shp[:-1], d)
+    code = _e2m1_codes(y).reshape(*shp[:-1], d)
     packed = (code[..., 0::2] | (code[..., 1::2] << 4)).contiguous()
     scale = (e + 127.0).to(torch.uint8).reshape(*shp[:-1], d // 32).contiguous()
     return packed, scale
@@ -108,6 +144,15 @@ def _store_rows(g, shape, device, std, dtype, chunk_leading=False):
             return {"data": packed, "scale": scale}
         packed, scale = encode_fp4_rows(_normal(g, shape, device, std))
         return {"data": packed, "scale": scale}
+    if dtype in ("nvfp4", "fp8mx"):
+        enc = encode_nvfp4_rows if dtype == "nvfp4" else encode_fp8_e8m0_rows
+        row_bytes = shape[-1] // 2 + shape[-1] // 16 if dtype == "nvfp4" else shape[-1] + shape[-1] // 32
+        if chunk_leading and len(shape) == 3:
+            rows = torch.empty(shape[:-1] + (row_bytes,), device=device, dtype=torch.uint8)
+            for b in range(shape[0]):
+                rows[b] = enc(_normal(g, shape[1:], device, std))
+            return {"data": rows}
+        return {"data": enc(_normal(g, shape, device, std))}
     raise ValueError(dtype)
 
 
@@ -193,11 +238,15 @@ def make_inputs(cfg: Csa2Config, seed: int, device="cpu"):
         rows = T
     # indexer query and weights (the FULL / REINDEX layer's own)
     w = _normal(g, (rows, HI), device, 1.0)
+    out["qI_scale"] = None
     if cfg.idx_dtype == "fp8":
         qraw = _normal(g, (rows, HI, DI), device, std)
         codes, qscale = encode_fp8_rows(qraw)
         out["qI"] = codes
         out["w"] = (w * qscale).contiguous()
+    elif cfg.idx_dtype == "fp4":
+        out["qI"], out["qI_scale"] = encode_fp4_rows(_normal(g, (rows, HI, DI), device, std))
+        out["w"] = w.contiguous()
     else:
         out["qI"] = store_dense(_normal(g, (rows, HI, DI), device, std), cfg.idx_dtype)
         out["w"] = w.contiguous()
