@@ -6,7 +6,7 @@
 A step is one pass of the whole path over one batch of synthetic inputs that
 are already resident in HBM:
   decode  : indexer_score -> topk_select -> sparse_attn_decode
-            (wide FULL rows with an FP8 index plane keep their scores on chip:
+            (wide FULL rows with an FP8 or MXFP4 index plane keep their scores on chip:
             indexer_score(scores=None) -> topk_rescore; a FULL owner layer that
             builds the REINDEX candidate pool adds candidate_pool from the block
             scores the indexer wrote)
@@ -34,7 +34,13 @@ _ELEM = {"f32": 4, "bf16": 2, "fp8": 1}
 
 
 # Dense matrix-core peaks of MI355X by operand type (TFLOP/s, no sparsity).
-MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0, "f32": 157.3}
+MFMA_PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0, "f32": 157.3}
+
+
+def _row_bytes(dtype, d):
+    """Stored bytes of one d-element row, scales included."""
+    return {"f32": 4 * d, "bf16": 2 * d, "fp8": d + 4, "fp4": d // 2 + d // 32, "nvfp4": d // 2 + d // 16,
+            "fp8mx": d + d // 32}[dtype]
 
 
 def _unique_plane_rows(base, rows_read):
@@ -56,8 +62,10 @@ def algorithmic_work(cfg, x, idx_host=None, score_free=False):
     base = x["kv_row_base"].cpu()
     nv = ((pos + 1) // cfg.ratio).clamp(max=cfg.n_main_rows)
     rows = pos.shape[0]
-    idx_row = cfg.idx_dim * _ELEM[cfg.idx_dtype] + (4 if cfg.idx_dtype == "fp8" else 0)
-    qI = rows * cfg.idx_heads * cfg.idx_dim * _ELEM[cfg.idx_dtype] + rows * cfg.idx_heads * 4
+    idx_row = _row_bytes(cfg.idx_dtype, cfg.idx_dim)
+    # the query (FP8: no scale, it is folded into w) and the head weights
+    q_row = cfg.idx_dim if cfg.idx_dtype == "fp8" else _row_bytes(cfg.idx_dtype, cfg.idx_dim)
+    qI = rows * cfg.idx_heads * q_row + rows * cfg.idx_heads * 4
     if cfg.index_mode == "reindex":
         cand = x["cand"].cpu().long()
         cols = cand.repeat_interleave(cfg.block_rows, dim=1) * cfg.block_rows + \
@@ -75,7 +83,7 @@ def algorithmic_work(cfg, x, idx_host=None, score_free=False):
         # scores stay on chip: the key histogram and the 8-column block keys are written instead
         nbk = -(-cfg.width // 8)
         idx_bytes = unique_rows * idx_row + qI + rows * (nbk + 4096) * 4
-        nbm = nbk  # the pool ranks the same block keys
+        nbm = nbk if cfg.pool_blocks else 0  # the pool ranks the same block keys
         # the select reads the histogram and block keys (re-scored candidate rows are not counted:
         # they are extra work of this route, not bytes the result needs)
         topk_bytes = rows * (nbk + 4096) * 4 + rows * cfg.topk * 4
@@ -83,8 +91,8 @@ def algorithmic_work(cfg, x, idx_host=None, score_free=False):
         idx_bytes = unique_rows * idx_row + qI + extra + rows * cfg.width * 4 + rows * nbm * 4
         topk_bytes = rows * cfg.width * 4 + rows * cfg.topk * 4 + extra
     idx_flops = 2 * scored * cfg.idx_heads * cfg.idx_dim
-    main_row = cfg.dim // 2 + cfg.dim // 32 if cfg.main_dtype == "fp4" else cfg.dim * _ELEM[cfg.main_dtype]
-    swa_row = cfg.dim * _ELEM[cfg.swa_dtype] + (4 if cfg.swa_dtype == "fp8" else 0)
+    main_row = _row_bytes(cfg.main_dtype, cfg.dim)
+    swa_row = _row_bytes(cfg.swa_dtype, cfg.dim)
     sel = torch.minimum(nv, torch.tensor(cfg.topk))
     win = torch.minimum(pos + 1, torch.tensor(cfg.window))
     layers = len(x["layers"])
@@ -216,6 +224,7 @@ def _host_slice(cfg, x, r):
         out["layers"] = [{"q": cpu(L["q"][r:r + 1]), "swa": cpu(L["swa"]), "swa_scale": cpu(L["swa_scale"]),
                           "sink": cpu(L["sink"])} for L in x["layers"]]
     out["qI"] = cpu(x["qI"][r:r + 1])
+    out["qI_scale"] = cpu(None if x.get("qI_scale") is None else x["qI_scale"][r:r + 1])
     out["w"] = cpu(x["w"][r:r + 1])
     if "cand" in x:
         out["cand"] = cpu(x["cand"][r:r + 1])
@@ -298,7 +307,7 @@ def main():
         "metric": METRIC, "value": round(q_tokens / (ms_step * 1e-3), 1), "unit": "query-tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": {"fp8": "fp8+bf16", "bf16": "bf16", "f32": "f32"}[cfg.idx_dtype],
+        "dtype": {"fp4": "fp4+bf16", "fp8": "fp8+bf16", "bf16": "bf16", "f32": "f32"}[cfg.idx_dtype],
         "data": "synthetic (seeded; stored formats drawn as in workloads/gen.py)",
         "config": {"workload": cfg.name, "sequences": cfg.batch, "query_rows": rows, "context": cfg.context,
                    "ratio": cfg.ratio, "heads": cfg.heads, "dim": cfg.dim, "topk": cfg.topk, "window": cfg.window,

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 3
+#define CSA2_ABI_VERSION 4
 
 /* Status codes. */
 #define CSA2_OK 0
@@ -66,6 +66,14 @@ extern "C" {
 #define CSA2_BF16 1     /* bfloat16 */
 #define CSA2_FP8_E4M3 2 /* OCP FP8 E4M3 "FN" (bias 7, S.1111.111 = NaN), one byte per element */
 #define CSA2_FP4_E2M1 3 /* OCP FP4 E2M1, two per byte (element 2i in the low nibble) */
+/* Rows with their scales inline (the pages' 890 B/token pool, "DeepSeek-V4.1-Flash 架构解剖",
+ * "换成 packed FP4 主池"):
+ *   CSA2_FP4_E2M1_E4M3G16: D/2 bytes of packed E2M1, then D/16 E4M3 scales, one per 16
+ *                          elements (288 B per 512-element row);
+ *   CSA2_FP8_E4M3_E8M0G32: D bytes of FP8-E4M3, then D/32 E8M0 scales, one per 32
+ *                          elements (528 B per 512-element row). */
+#define CSA2_FP4_E2M1_E4M3G16 4
+#define CSA2_FP8_E4M3_E8M0G32 5
 
 /* Indexer modes. */
 #define CSA2_MODE_FULL 0
@@ -101,8 +109,18 @@ const char* csa2_status_string(int32_t status);
  * query's per-(row, head) scale is folded into w by the caller (anatomy page,
  * fig. 3b: the FP32 scale is folded into w, not passed separately).
  *
+ * MXFP4 (k_dtype == q_dtype == CSA2_FP4_E2M1): q is [rows, heads, dim / 2]
+ * packed E2M1 with E8M0 block scales q_scale_e8m0 [rows, heads, dim / 32], k is
+ * [*, dim / 2] with k_scale_e8m0 [*, dim / 32] (one E8M0 byte per 32 elements,
+ * a power of two; "DeepSeek-V4.1-Flash 结构说明" §5.3: the indexer keys and, at
+ * inference, the indexer query are FP4 with one E8M0 scale per 32 channels;
+ * "万字长文解析DeekSeekV4.1flash" §10.6: 64 + 4 bytes per key row).  Each
+ * dot product is the sum over 32-element blocks of (q block . k block) times
+ * both blocks' scales; k_scale is NULL.  FULL mode with (heads, dim) =
+ * (64, 128) only.
+ *
  * Supported: (heads, dim) in {(4, 32), (64, 128)}; q_dtype == k_dtype in
- * {F32, BF16, FP8_E4M3}.  rows * width fits in int64.
+ * {F32, BF16, FP8_E4M3}, or FP4_E2M1 as above.  rows * width fits in int64.
  */
 typedef struct csa2_index_args {
     uint32_t struct_size;       /* sizeof(csa2_index_args) */
@@ -147,6 +165,9 @@ typedef struct csa2_index_args {
                                  * or 0 when none is valid; a column's key is its order key (as for
                                  * key_hist), except that a NaN score counts as 0x007FFFFE, just
                                  * below -inf (so the candidate pool can still tell NaN from -inf). */
+    const uint8_t* q_scale_e8m0; /* MXFP4: [rows, heads, dim / 32] E8M0 block scales of q; else NULL */
+    const uint8_t* k_scale_e8m0; /* MXFP4: [*, dim / 32] E8M0 block scales of k, same row numbering as
+                                  * k; else NULL */
 } csa2_index_args;
 
 int32_t csa2_indexer_score(const csa2_index_args* args, csa2_stream_t stream);
@@ -168,7 +189,7 @@ int32_t csa2_indexer_score(const csa2_index_args* args, csa2_stream_t stream);
  * args: as given to the score-free csa2_indexer_score call (key_hist and
  * block_keys are now inputs; scores and block_max are ignored).
  * out: [rows, k] int32, ascending plane rows, -1 padded.
- * Supported: FP8-E4M3 q and k with (heads, dim) = (64, 128); 1 <= k <= 2048;
+ * Supported: FP8-E4M3 or MXFP4 q and k with (heads, dim) = (64, 128); 1 <= k <= 2048;
  * rows < 1024 and 8192 <= width < 2^24 (exactly when
  * csa2_topk_rescore_workspace_size(rows, width, k) > 0), else CSA2_ERR_UNSUPPORTED.
  */
@@ -295,12 +316,15 @@ int32_t csa2_candidate_pool(const csa2_pool_args* args, void* workspace, size_t 
  * [*, dim], or FP4_E2M1 packed [*, dim/2] bytes with kv_scale = E8M0 bytes
  * [*, dim/32] (one power-of-two scale per 32 elements).  swa is F32 or BF16,
  * or FP8_E4M3 with swa_scale = float32 per swa row ([rows, window] in decode,
- * [swa_rows] in prefill).
+ * [swa_rows] in prefill).  With the inline-scale types kv rows are
+ * dim/2 + dim/16 bytes (FP4_E2M1_E4M3G16) and swa rows dim + dim/32 bytes
+ * (FP8_E4M3_E8M0G32); the shapes above then count bytes in their last axis.
  *
  * Supported: (heads, dim, rope_dim) in {(4, 64, 16), (64, 512, 64)}; window
  * a multiple of 16 in [16, 1024] and topk a multiple of 16 in [0, 2048]; F32 only together with F32 everywhere (the
  * (4, 64, 16) shape); otherwise BF16 q/out with kv BF16 or FP4 and swa BF16
- * or FP8.  rope_inv_freq holds rope_dim/2 float64 frequencies in device
+ * or FP8, or kv FP4_E2M1_E4M3G16 with swa FP8_E4M3_E8M0G32 (scales inline:
+ * kv_scale and swa_scale NULL).  rope_inv_freq holds rope_dim/2 float64 frequencies in device
  * memory (see csa2_rope_inv_freq).
  *
  * Decode with few rows gives each (row, 16-head group) its own workgroup and

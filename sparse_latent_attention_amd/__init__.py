@@ -29,7 +29,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # Element types and modes (include/csa2.h).
-F32, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
+F32, BF16, FP8_E4M3, FP4_E2M1, FP4_E2M1_E4M3G16, FP8_E4M3_E8M0G32 = 0, 1, 2, 3, 4, 5
 MODE_FULL, MODE_REINDEX = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
@@ -43,7 +43,7 @@ class IndexArgs(ctypes.Structure):
         ("q_dtype", _i32), ("k_dtype", _i32), ("n_blocks", _i32), ("block_rows", _i32), ("_pad0", _i32),
         ("width", _i64), ("q", _vp), ("w", _vp), ("k", _vp), ("k_scale", _vp), ("row_base", _vp), ("pos", _vp),
         ("cand", _vp), ("scale", _f32), ("_pad1", _i32), ("scores", _vp), ("key_hist", _vp), ("block_max", _vp),
-        ("block_keys", _vp),
+        ("block_keys", _vp), ("q_scale_e8m0", _vp), ("k_scale_e8m0", _vp),
     ]
 
 
@@ -163,12 +163,25 @@ def rope_inv_freq(rope_dim, theta, yarn_factor=1.0, yarn_orig_len=0):
 
 
 def _index_args(q, w, k, row_base, pos, ratio, scale, scores, width, k_scale, cand, block_rows, fp8, key_hist,
-                block_max, block_keys):
-    _dev(q, w, k, row_base, pos, scores, k_scale, cand, key_hist, block_max, block_keys)
+                block_max, block_keys, fp4=False, q_scale=None):
+    _dev(q, w, k, row_base, pos, scores, k_scale, cand, key_hist, block_max, block_keys, q_scale)
     if key_hist is not None and (key_hist.dtype != torch.int32 or tuple(key_hist.shape) != (q.shape[0], 4096)):
         raise ValueError("csa2.indexer_score: key_hist must be int32 [rows, 4096]")
     rows, heads, dim = q.shape
-    if fp8:
+    if fp8 and fp4:
+        raise ValueError("csa2.indexer_score: fp8 and fp4 exclude each other")
+    if fp4:
+        # packed E2M1: q [rows, heads, dim / 2], k [*, dim / 2]; E8M0 scales per 32 elements
+        _need(q, torch.uint8, "q")
+        _need(k, torch.uint8, "k")
+        _need(q_scale, torch.uint8, "q_scale")
+        _need(k_scale, torch.uint8, "k_scale")
+        code = FP4_E2M1
+        if tuple(q_scale.shape) != (rows, heads, dim // 16) or k_scale.shape[-1] != dim // 16:
+            raise ValueError("csa2.indexer_score: fp4 scales must be [rows, heads, dim / 32] and [*, dim / 32]")
+    elif q_scale is not None:
+        raise ValueError("csa2.indexer_score: q_scale is for fp4 only")
+    elif fp8:
         _need(q, torch.uint8, "q")
         _need(k, torch.uint8, "k")
         code = FP8_E4M3
@@ -189,7 +202,7 @@ def _index_args(q, w, k, row_base, pos, ratio, scale, scores, width, k_scale, ca
     a = IndexArgs()
     a.struct_size = ctypes.sizeof(IndexArgs)
     a.mode = MODE_REINDEX if cand is not None else MODE_FULL
-    a.rows, a.heads, a.dim, a.ratio = rows, heads, dim, int(ratio)
+    a.rows, a.heads, a.dim, a.ratio = rows, heads, 2 * dim if fp4 else dim, int(ratio)
     a.q_dtype = a.k_dtype = code
     a.width = int(width)
     if cand is not None:
@@ -208,7 +221,11 @@ def _index_args(q, w, k, row_base, pos, ratio, scale, scores, width, k_scale, ca
         if tuple(block_keys.shape) != (rows, -(-a.width // 8)):
             raise ValueError("csa2.indexer_score: block_keys must be int32 [rows, ceil(width / 8)]")
     a.block_max, a.block_keys = _ptr(block_max), _ptr(block_keys)
-    a.q, a.w, a.k, a.k_scale = _ptr(q), _ptr(w), _ptr(k), _ptr(k_scale)
+    if fp4:
+        a.q_scale_e8m0, a.k_scale_e8m0 = _ptr(q_scale), _ptr(k_scale)
+        a.q, a.w, a.k = _ptr(q), _ptr(w), _ptr(k)
+    else:
+        a.q, a.w, a.k, a.k_scale = _ptr(q), _ptr(w), _ptr(k), _ptr(k_scale)
     a.row_base, a.pos, a.cand, a.scores = _ptr(row_base), _ptr(pos), _ptr(cand), _ptr(scores)
     a.key_hist = _ptr(key_hist)
     a.scale = float(scale)
@@ -216,12 +233,16 @@ def _index_args(q, w, k, row_base, pos, ratio, scale, scores, width, k_scale, ca
 
 
 def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None, cand=None, block_rows=8,
-                  fp8=False, key_hist=None, block_max=None, block_keys=None, width=None, stream=None):
+                  fp8=False, fp4=False, q_scale=None, key_hist=None, block_max=None, block_keys=None, width=None,
+                  stream=None):
     """Fills ``scores`` [rows, width] (float32).  REINDEX when ``cand`` is given.
 
     q [rows, H_I, D_I] and k [*, D_I] are float32/bfloat16, or uint8 FP8-E4M3
     codes with ``fp8=True`` (then ``k_scale`` [*] float32 is required and the
-    query scales are already folded into w).  ``key_hist`` (int32 [rows, 4096])
+    query scales are already folded into w), or MXFP4 with ``fp4=True``: packed
+    E2M1 q [rows, H_I, D_I / 2] and k [*, D_I / 2] with E8M0 block scales
+    ``q_scale`` [rows, H_I, D_I / 32] and ``k_scale`` [*, D_I / 32] (uint8;
+    FULL only).  ``key_hist`` (int32 [rows, 4096])
     optionally receives the score-key histogram topk_select can reuse.
     ``block_max`` (FULL only, float32 [rows, ceil(width / block_rows)])
     optionally receives the candidate pool's block scores.  ``scores=None``
@@ -229,7 +250,7 @@ def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None,
     selects the score-free mode whose top-k ``topk_rescore`` takes.
     """
     a = _index_args(q, w, k, row_base, pos, ratio, scale, scores, width, k_scale, cand, block_rows, fp8, key_hist,
-                    block_max, block_keys)
+                    block_max, block_keys, fp4, q_scale)
     _check("csa2_indexer_score", _lib.csa2_indexer_score(ctypes.byref(a), _stream(stream)))
     return scores
 
@@ -238,19 +259,22 @@ def topk_rescore_workspace_size(rows, width, k):
     return int(_lib.csa2_topk_rescore_workspace_size(int(rows), int(width), int(k)))
 
 
-def topk_rescore_supported(rows, width, k, heads=64, dim=128, fp8=True):
-    """Whether the score-free FULL path (indexer_score(scores=None) + topk_rescore) takes these sizes."""
-    return fp8 and heads == 64 and dim == 128 and 1 <= k <= 2048 and topk_rescore_workspace_size(rows, width, k) > 0
+def topk_rescore_supported(rows, width, k, heads=64, dim=128, fp8=True, fp4=False):
+    """Whether the score-free FULL path (indexer_score(scores=None) + topk_rescore) takes these sizes
+    (FP8-E4M3 or MXFP4 index planes)."""
+    return ((fp8 or fp4) and heads == 64 and dim == 128 and 1 <= k <= 2048 and
+            topk_rescore_workspace_size(rows, width, k) > 0)
 
 
 def topk_rescore(q, w, k, row_base, pos, ratio, scale, out, key_hist, block_keys, width, *, k_scale=None,
-                 workspace=None, stream=None):
+                 fp4=False, q_scale=None, workspace=None, stream=None):
     """Top-k ``out`` [rows, k] int32 of the scores a score-free indexer_score call with these arguments kept on
-    chip (its ``key_hist`` and ``block_keys``); bit-identical to topk_select over the written scores."""
+    chip (its ``key_hist`` and ``block_keys``); bit-identical to topk_select over the written scores.  FP8
+    index planes by default, MXFP4 ones with ``fp4=True`` (and ``q_scale``, as for indexer_score)."""
     _dev(out)
     _need(out, torch.int32, "out")
-    a = _index_args(q, w, k, row_base, pos, ratio, scale, None, width, k_scale, None, 8, True, key_hist, None,
-                    block_keys)
+    a = _index_args(q, w, k, row_base, pos, ratio, scale, None, width, k_scale, None, 8, not fp4, key_hist, None,
+                    block_keys, fp4, q_scale)
     if out.shape[0] != a.rows:
         raise ValueError("csa2.topk_rescore: out rows")
     need = topk_rescore_workspace_size(a.rows, a.width, out.shape[1])
@@ -349,7 +373,7 @@ def candidate_pool(pos, ratio, cand, *, scores=None, block_max=None, block_keys=
 
 
 def _attn_args(q, pos, idx, kv, kv_scale, kv_row_base, swa, swa_scale, sink, inv_freq, ratio, window,
-               softmax_scale, out, rope_dim, kv_fp4, swa_fp8):
+               softmax_scale, out, rope_dim, kv_fp4, swa_fp8, kv_nvfp4=False, swa_fp8mx=False):
     _dev(q, pos, idx, kv, kv_scale, kv_row_base, swa, swa_scale, sink, inv_freq, out)
     rows, heads, dim = q.shape
     _need(pos, torch.int64, "pos")
@@ -363,6 +387,15 @@ def _attn_args(q, pos, idx, kv, kv_scale, kv_row_base, swa, swa_scale, sink, inv
     if swa_fp8:
         _need(swa, torch.uint8, "swa")
         _need(swa_scale, torch.float32, "swa_scale")
+    if kv_nvfp4 or swa_fp8mx:
+        # rows with inline scales: E2M1 + E4M3 per 16 (dim/2 + dim/16 bytes) and
+        # FP8 + E8M0 per 32 (dim + dim/32 bytes); the two go together
+        if not (kv_nvfp4 and swa_fp8mx) or kv_fp4 or swa_fp8 or kv_scale is not None or swa_scale is not None:
+            raise ValueError("csa2.sparse_attn: kv_nvfp4 goes with swa_fp8mx, without separate scales")
+        _need(kv, torch.uint8, "kv")
+        _need(swa, torch.uint8, "swa")
+        if kv.shape[-1] != dim // 2 + dim // 16:
+            raise ValueError(f"csa2.sparse_attn: kv rows must be {dim // 2 + dim // 16} bytes")
     if out.shape != q.shape or idx.shape[0] != rows or pos.shape != (rows,) or sink.shape != (heads,) \
             or inv_freq.shape != (rope_dim // 2,) or kv_row_base.shape != (rows,):
         raise ValueError("csa2.sparse_attn: inconsistent shapes")
@@ -371,8 +404,8 @@ def _attn_args(q, pos, idx, kv, kv_scale, kv_row_base, swa, swa_scale, sink, inv
     a.rows, a.heads, a.dim, a.rope_dim, a.topk = rows, heads, dim, int(rope_dim), idx.shape[1]
     a.ratio, a.window = int(ratio), int(window)
     a.q_dtype, a.out_dtype = _dense_code(q, "q"), _dense_code(out, "out")
-    a.kv_dtype = FP4_E2M1 if kv_fp4 else _dense_code(kv, "kv")
-    a.swa_dtype = FP8_E4M3 if swa_fp8 else _dense_code(swa, "swa")
+    a.kv_dtype = FP4_E2M1 if kv_fp4 else FP4_E2M1_E4M3G16 if kv_nvfp4 else _dense_code(kv, "kv")
+    a.swa_dtype = FP8_E4M3 if swa_fp8 else FP8_E4M3_E8M0G32 if swa_fp8mx else _dense_code(swa, "swa")
     a.q, a.pos, a.idx, a.kv, a.kv_scale = _ptr(q), _ptr(pos), _ptr(idx), _ptr(kv), _ptr(kv_scale)
     a.kv_row_base, a.swa, a.swa_scale, a.sink = _ptr(kv_row_base), _ptr(swa), _ptr(swa_scale), _ptr(sink)
     a.rope_inv_freq, a.softmax_scale, a.out = _ptr(inv_freq), float(softmax_scale), _ptr(out)
@@ -383,12 +416,21 @@ def attn_workspace_size(rows, heads, dim, window, topk, splits=0):
     return int(_lib.csa2_attn_workspace_size(int(rows), int(heads), int(dim), int(window), int(topk), int(splits)))
 
 
+def _swa_row_len(dim, swa_fp8mx):
+    return dim + dim // 32 if swa_fp8mx else dim
+
+
 def sparse_attn_decode(q, pos, idx, kv, kv_row_base, swa, sink, inv_freq, ratio, window, softmax_scale, out, *,
-                       rope_dim=64, kv_scale=None, swa_scale=None, kv_fp4=False, swa_fp8=False, stream=None):
-    """Decode attention: ``swa`` is one ring [rows, window, D] per query row."""
+                       rope_dim=64, kv_scale=None, swa_scale=None, kv_fp4=False, swa_fp8=False, kv_nvfp4=False,
+                       swa_fp8mx=False, stream=None):
+    """Decode attention: ``swa`` is one ring [rows, window, D] per query row.
+
+    ``kv_nvfp4`` with ``swa_fp8mx`` selects rows with inline scales: kv
+    [*, D/2 + D/16] bytes (E2M1, then one E4M3 per 16) and swa
+    [rows, window, D + D/32] bytes (FP8-E4M3, then one E8M0 per 32)."""
     a = _attn_args(q, pos, idx, kv, kv_scale, kv_row_base, swa, swa_scale, sink, inv_freq, ratio, window,
-                   softmax_scale, out, rope_dim, kv_fp4, swa_fp8)
-    if tuple(swa.shape) != (a.rows, a.window, a.dim):
+                   softmax_scale, out, rope_dim, kv_fp4, swa_fp8, kv_nvfp4, swa_fp8mx)
+    if tuple(swa.shape) != (a.rows, a.window, _swa_row_len(a.dim, swa_fp8mx)):
         raise ValueError("csa2.sparse_attn_decode: swa must be [rows, window, dim]")
     if swa_fp8 and tuple(swa_scale.shape) != (a.rows, a.window):
         raise ValueError("csa2.sparse_attn_decode: swa_scale must be [rows, window]")
@@ -398,13 +440,15 @@ def sparse_attn_decode(q, pos, idx, kv, kv_row_base, swa, sink, inv_freq, ratio,
 
 def sparse_attn_prefill(q, pos, idx, kv, swa, swa_pos0, sink, inv_freq, ratio, window, softmax_scale, out, *,
                         rope_dim=64, kv_row_base=None, kv_scale=None, swa_scale=None, kv_fp4=False, swa_fp8=False,
-                        stream=None):
-    """Prefill attention: ``swa`` is one linear array [swa_rows, D]; row t holds position swa_pos0 + t."""
+                        kv_nvfp4=False, swa_fp8mx=False, stream=None):
+    """Prefill attention: ``swa`` is one linear array [swa_rows, D]; row t holds position swa_pos0 + t.
+    Storage flags as for sparse_attn_decode."""
     if kv_row_base is None:
         kv_row_base = torch.zeros(q.shape[0], dtype=torch.int64, device=q.device)
     a = _attn_args(q, pos, idx, kv, kv_scale, kv_row_base, swa, swa_scale, sink, inv_freq, ratio, window,
-                   softmax_scale, out, rope_dim, kv_fp4, swa_fp8)
-    if swa.dim() != 2 or swa.shape[1] != a.dim or (swa_fp8 and tuple(swa_scale.shape) != (swa.shape[0],)):
+                   softmax_scale, out, rope_dim, kv_fp4, swa_fp8, kv_nvfp4, swa_fp8mx)
+    if swa.dim() != 2 or swa.shape[1] != _swa_row_len(a.dim, swa_fp8mx) or \
+            (swa_fp8 and tuple(swa_scale.shape) != (swa.shape[0],)):
         raise ValueError("csa2.sparse_attn_prefill: swa must be [swa_rows, dim] (and swa_scale [swa_rows])")
     a.swa_rows, a.swa_pos0 = swa.shape[0], int(swa_pos0)
     _check("csa2_sparse_attn_prefill", _lib.csa2_sparse_attn_prefill(ctypes.byref(a), _stream(stream)))

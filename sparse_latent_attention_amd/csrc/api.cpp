@@ -22,11 +22,20 @@ size_t elem_bytes(int dtype) {
         case CSA2_F32: return 4;
         case CSA2_BF16: return 2;
         case CSA2_FP8_E4M3: return 1;
+        case CSA2_FP4_E2M1: return 1;  // two elements per byte; rows are dim / 2 bytes
         default: return 0;
     }
 }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
+
+// Scale operands match the element type: FP8 takes k_scale, MXFP4 takes both
+// E8M0 planes, the other types take none.
+bool index_scales_ok(const csa2_index_args* a) {
+    const bool fp8 = a->k_dtype == CSA2_FP8_E4M3, fp4 = a->k_dtype == CSA2_FP4_E2M1;
+    return fp8 == (a->k_scale != nullptr) && fp4 == (a->q_scale_e8m0 != nullptr) &&
+           fp4 == (a->k_scale_e8m0 != nullptr) && aligned(a->k_scale_e8m0, 4);
+}
 
 
 }  // namespace
@@ -72,6 +81,7 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
     if (a->q_dtype != a->k_dtype || elem_bytes(a->k_dtype) == 0) return CSA2_ERR_UNSUPPORTED;
     if (!csa2::indexer_supported(a->heads, a->dim, a->k_dtype)) return CSA2_ERR_UNSUPPORTED;
     const bool reindex = a->mode == CSA2_MODE_REINDEX;
+    if (a->k_dtype == CSA2_FP4_E2M1 && reindex) return CSA2_ERR_UNSUPPORTED;
     if (reindex) {
         if (a->cand == nullptr || a->n_blocks <= 0 || a->block_rows <= 0 || a->block_rows > 64) return CSA2_ERR_INVALID_ARG;
         if (a->width != (int64_t)a->n_blocks * a->block_rows) return CSA2_ERR_INVALID_ARG;
@@ -92,7 +102,7 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
     if (a->rows == 0 || a->width == 0) return CSA2_OK;
     if (a->q == nullptr || a->w == nullptr || a->k == nullptr || a->row_base == nullptr || a->pos == nullptr)
         return CSA2_ERR_INVALID_ARG;
-    if ((a->k_dtype == CSA2_FP8_E4M3) != (a->k_scale != nullptr)) return CSA2_ERR_INVALID_ARG;
+    if (!index_scales_ok(a)) return CSA2_ERR_INVALID_ARG;
     if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->scores, 4) || !aligned(a->w, 4) ||
         !aligned(a->block_max, 4))
         return CSA2_ERR_INVALID_ARG;
@@ -100,6 +110,7 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
 
     csa2::IndexParams p;
     p.q = a->q; p.w = a->w; p.k = a->k; p.k_scale = a->k_scale; p.row_base = a->row_base; p.pos = a->pos;
+    p.q_e8 = a->q_scale_e8m0; p.k_e8 = a->k_scale_e8m0;
     p.cand = reindex ? a->cand : nullptr; p.scores = a->scores; p.key_hist = a->key_hist; p.width = a->width;
     p.n_blocks = reindex ? a->n_blocks : 0; p.block_rows = reindex ? a->block_rows : 1; p.ratio = a->ratio;
     p.scale = a->scale;
@@ -150,14 +161,15 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
     const size_t need = csa2_topk_rescore_workspace_size(a->rows, a->width, k);
     if (workspace_bytes < need) return CSA2_ERR_WORKSPACE;
     if (workspace == nullptr || !aligned(workspace, 256)) return CSA2_ERR_INVALID_ARG;
-    if (a->q == nullptr || a->w == nullptr || a->k == nullptr || a->k_scale == nullptr || a->row_base == nullptr ||
-        a->pos == nullptr || a->key_hist == nullptr || a->block_keys == nullptr || out == nullptr)
+    if (a->q == nullptr || a->w == nullptr || a->k == nullptr || a->row_base == nullptr || a->pos == nullptr ||
+        a->key_hist == nullptr || a->block_keys == nullptr || out == nullptr || !index_scales_ok(a))
         return CSA2_ERR_INVALID_ARG;
     if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->w, 4) || !isfinite(a->scale))
         return CSA2_ERR_INVALID_ARG;
 
     csa2::IndexParams ip;
     ip.q = a->q; ip.w = a->w; ip.k = a->k; ip.k_scale = a->k_scale; ip.row_base = a->row_base; ip.pos = a->pos;
+    ip.q_e8 = a->q_scale_e8m0; ip.k_e8 = a->k_scale_e8m0;
     ip.cand = nullptr; ip.scores = nullptr; ip.key_hist = a->key_hist; ip.block_max = nullptr;
     ip.block_keys = a->block_keys; ip.width = a->width; ip.cols_per_wg = 0; ip.bm_blocks = 0; ip.n_blocks = 0;
     ip.block_rows = 1; ip.bm_rows = 4; ip.ratio = a->ratio; ip.scale = a->scale;
@@ -176,7 +188,8 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
     int32_t* cols = reinterpret_cast<int32_t*>(w);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = csa2::launch_topk_threshold(tp, a->rows, a->key_hist, b1, st);
-    if (e == hipSuccess) e = csa2::launch_indexer_rescore(ip, a->rows, b1, chunk, nseg, keys, cols, seg_count, st);
+    if (e == hipSuccess)
+        e = csa2::launch_indexer_rescore(ip, a->rows, a->k_dtype, b1, chunk, nseg, keys, cols, seg_count, st);
     if (e == hipSuccess) e = csa2::launch_topk_final(tp, a->rows, keys, cols, seg_count, nseg, chunk, st);
     return hip_status(e);
 }

@@ -239,15 +239,24 @@ __device__ __forceinline__ void raw_load_row(const uint8_t* rowp, const float* f
         raw.v[i].x = w.x;
         raw.v[i].y = w.y;
         raw.s[i] = *fsc;
-    } else {  // FP4-E2M1 with one E8M0 per 32
+    } else if (DT == CSA2_FP4_E2M1) {  // FP4-E2M1 with one E8M0 per 32 (planar scales)
         raw.v[i].x = *reinterpret_cast<const uint32_t*>(rowp + 4 * x8);
         raw.sb[i] = e8[(8 * x8) / 32];
+    } else if (DT == CSA2_FP4_E2M1_E4M3G16) {  // FP4-E2M1, then one E4M3 scale per 16, inline
+        raw.v[i].x = *reinterpret_cast<const uint32_t*>(rowp + 4 * x8);
+        raw.sb[i] = rowp[D / 2 + (8 * x8) / 16];
+    } else {  // CSA2_FP8_E4M3_E8M0G32: FP8-E4M3, then one E8M0 scale per 32, inline
+        const u32x2 w = *reinterpret_cast<const u32x2*>(rowp + 8 * x8);
+        raw.v[i].x = w.x;
+        raw.v[i].y = w.y;
+        raw.sb[i] = rowp[D + (8 * x8) / 32];
     }
 }
 
 template <int DT>
 constexpr int row_bytes(int d) {
-    return DT == CSA2_F32 ? 4 * d : DT == CSA2_BF16 ? 2 * d : DT == CSA2_FP8_E4M3 ? d : d / 2;
+    return DT == CSA2_F32 ? 4 * d : DT == CSA2_BF16 ? 2 * d : DT == CSA2_FP8_E4M3 ? d
+         : DT == CSA2_FP4_E2M1_E4M3G16 ? d / 2 + d / 16 : DT == CSA2_FP8_E4M3_E8M0G32 ? d + d / 32 : d / 2;
 }
 
 template <int DT, class CT>
@@ -276,9 +285,14 @@ __device__ __forceinline__ void raw_convert(const RawPair& raw, int i, Pack8<CT>
         o.w[2] = ok ? b2 : 0u;
         o.w[3] = ok ? b3 : 0u;
     } else {
+        // Exact in every case: an FP8 or FP4 value times a power of two, or an E2M1 value
+        // (<= 2 significant bits) times an E4M3 scale (<= 4), fits bf16's 8 bits.
         float f[8];
-        const float sc = DT == CSA2_FP4_E2M1 ? e8m0_to_f32(raw.sb[i]) : raw.s[i];
-        if constexpr (DT == CSA2_FP8_E4M3) {
+        float sc;
+        if constexpr (DT == CSA2_FP4_E2M1 || DT == CSA2_FP8_E4M3_E8M0G32) sc = e8m0_to_f32(raw.sb[i]);
+        else if constexpr (DT == CSA2_FP4_E2M1_E4M3G16) sc = fp8x2_to_f32<false>(raw.sb[i])[0];
+        else sc = raw.s[i];
+        if constexpr (DT == CSA2_FP8_E4M3 || DT == CSA2_FP8_E4M3_E8M0G32) {
             const f32x2 a = fp8x2_to_f32<false>(raw.v[i].x), b = fp8x2_to_f32<true>(raw.v[i].x);
             const f32x2 c = fp8x2_to_f32<false>(raw.v[i].y), d = fp8x2_to_f32<true>(raw.v[i].y);
             f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1]; f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
@@ -697,8 +711,9 @@ bool attn_supported(const AttnShape& s) {
         return s.q_dtype == CSA2_F32 && s.kv_dtype == CSA2_F32 && s.swa_dtype == CSA2_F32 && s.out_dtype == CSA2_F32;
     if (s.heads == 64 && s.dim == 512 && s.rope_dim == 64)
         return s.q_dtype == CSA2_BF16 && s.out_dtype == CSA2_BF16 &&
-               (s.kv_dtype == CSA2_BF16 || s.kv_dtype == CSA2_FP4_E2M1) &&
-               (s.swa_dtype == CSA2_BF16 || s.swa_dtype == CSA2_FP8_E4M3);
+               (((s.kv_dtype == CSA2_BF16 || s.kv_dtype == CSA2_FP4_E2M1) &&
+                 (s.swa_dtype == CSA2_BF16 || s.swa_dtype == CSA2_FP8_E4M3)) ||
+                (s.kv_dtype == CSA2_FP4_E2M1_E4M3G16 && s.swa_dtype == CSA2_FP8_E4M3_E8M0G32));
     return false;
 }
 
@@ -714,6 +729,9 @@ hipError_t launch_sparse_attn(const AttnParams& p, const AttnShape& s, bool deco
             return launch_attn<64, 512, 64, __bf16, CSA2_BF16, CSA2_FP4_E2M1, CSA2_BF16, CSA2_BF16>(p, decode, stream);
         if (s.kv_dtype == CSA2_BF16 && s.swa_dtype == CSA2_FP8_E4M3)
             return launch_attn<64, 512, 64, __bf16, CSA2_BF16, CSA2_BF16, CSA2_FP8_E4M3, CSA2_BF16>(p, decode, stream);
+        if (s.kv_dtype == CSA2_FP4_E2M1_E4M3G16 && s.swa_dtype == CSA2_FP8_E4M3_E8M0G32)
+            return launch_attn<64, 512, 64, __bf16, CSA2_BF16, CSA2_FP4_E2M1_E4M3G16, CSA2_FP8_E4M3_E8M0G32, CSA2_BF16>(
+                p, decode, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -292,41 +292,112 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p)
     }
 }
 
-// Steps of key-row loads each wave keeps in flight in the FP8 FULL kernel, and
-// the most 64-column steps one wave makes (a workgroup covers <= 4096 columns).
-constexpr int kFp8Depth = 2;
-constexpr int kFp8MaxSteps = 16;
+// Steps of key-row loads each wave keeps in flight in the streaming FULL
+// kernels, and the most 64-column steps one wave makes (a workgroup covers
+// <= 4096 columns).
+constexpr int kStreamDepth = 2;
+constexpr int kStreamMaxSteps = 16;
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, gfx9-family descriptor
+constexpr int kNT = 2;                  // non-temporal cache policy of a buffer load
 
-// ---- FP8 64-key steps staged through LDS (shared by scoring and re-scoring) ----
+// ---- 64-key steps of a quantised index plane, staged through LDS ---------------
 //
-// Lane l's 8 loads cover keys 8j + (l >> 3), 16-byte chunk l & 7, of a 64-key
-// step.  In LDS, chunk c of key kk sits at position c ^ ((kk >> 1) & 7) of the
-// key's 128-byte row: writes and MFMA-layout reads are free of bank conflicts.
-__device__ __forceinline__ void fp8_stage_put(uint8_t* my, const u32x4 (&v)[8], int ksub, int kchunk) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int kk = 8 * j + ksub;
-        *reinterpret_cast<u32x4*>(my + kk * 128 + 16 * (kchunk ^ ((kk >> 1) & 7))) = v[j];
+// A step is 64 consecutive key rows.  Lane l's 16-byte load j covers key
+// j * (64 / kLoads) + l / kChunks, chunk l % kChunks, so one load instruction
+// reads 1 KiB of whole rows.  In LDS, chunk c of key kk sits at position
+// c ^ swz(kk) of the key's row, which keeps both the writes and the MFMA-layout
+// reads free of bank conflicts.  Each lane also loads the 32-bit scale word of
+// key (step start + lane).  The same code serves the scoring pass and the
+// re-scoring of candidates, so both compute a column's score identically.
+
+// FP8-E4M3 keys: 128-byte rows, one float32 scale per key that multiplies the
+// score (scales are positive and ReLU commutes with a positive factor).  The
+// FP8 query's per-(row, head) scale is folded into w by the caller.  One
+// 16x16x128 MFMA with unit block scales per 16 keys x 16 heads; lane (g, n)
+// holds bytes 16g..16g+15 and 64+16g..64+16g+15 of its row (the query
+// fragments use the same k order).
+struct Fp8Keys {
+    static constexpr int kRowBytes = 128, kChunks = 8, kLoads = 8;
+    static constexpr bool kScaleInScore = true;
+    static __device__ __forceinline__ int swz(int kk) { return (kk >> 1) & 7; }
+    static __device__ __forceinline__ void frag(const uint8_t* my, const uint32_t*, int kk, int g, i32x8& kb,
+                                                uint32_t& ksc) {
+        const int sw = swz(kk);
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(my + kk * 128 + 16 * (g ^ sw));
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(my + kk * 128 + 16 * ((g + 4) ^ sw));
+        kb[0] = a0[0]; kb[1] = a0[1]; kb[2] = a0[2]; kb[3] = a0[3];
+        kb[4] = a1[0]; kb[5] = a1[1]; kb[6] = a1[2]; kb[7] = a1[3];
+        ksc = 127u;
     }
+    static __device__ __forceinline__ f32x4 mma(const i32x8& qa, uint32_t, const i32x8& kb, uint32_t) {
+        return mma_fp8_k128(f32x4{0.f, 0.f, 0.f, 0.f}, qa, kb);
+    }
+    static __device__ __forceinline__ void query(const IndexParams& p, int64_t head, int g, i32x8& qa, uint32_t& qs) {
+        qa = IdxOps<CSA2_FP8_E4M3, 128>::load(p.q, head, 0, g);
+        qs = 127u;
+    }
+    static __device__ __forceinline__ const void* scale_base(const IndexParams& p, int64_t row) {
+        return p.k_scale + row;
+    }
+};
+
+// MXFP4 keys and query (E2M1 with one E8M0 scale per 32 elements): 64-byte
+// rows plus a 4-byte word of block scales per row.  The MFMA takes FP4
+// operands with their block scales directly: lane (g, n) holds elements
+// 32g..32g+31 (16 bytes, operand dwords 0-3) of row n and that block's scale
+// byte.
+struct Fp4Keys {
+    static constexpr int kRowBytes = 64, kChunks = 4, kLoads = 4;
+    static constexpr bool kScaleInScore = false;
+    static __device__ __forceinline__ int swz(int kk) { return (kk >> 2) & 3; }
+    static __device__ __forceinline__ void frag(const uint8_t* my, const uint32_t* scl, int kk, int g, i32x8& kb,
+                                                uint32_t& ksc) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(my + kk * 64 + 16 * (g ^ swz(kk)));
+        kb[0] = a[0]; kb[1] = a[1]; kb[2] = a[2]; kb[3] = a[3];
+        kb[4] = 0; kb[5] = 0; kb[6] = 0; kb[7] = 0;
+        ksc = (scl[kk] >> (8 * g)) & 0xffu;
+    }
+    static __device__ __forceinline__ f32x4 mma(const i32x8& qa, uint32_t qs, const i32x8& kb, uint32_t ksc) {
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, kb, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, (int)qs,
+                                                                0, (int)ksc);
+    }
+    static __device__ __forceinline__ void query(const IndexParams& p, int64_t head, int g, i32x8& qa, uint32_t& qs) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.q) + head * 64 + 16 * g);
+        qa[0] = a[0]; qa[1] = a[1]; qa[2] = a[2]; qa[3] = a[3];
+        qa[4] = 0; qa[5] = 0; qa[6] = 0; qa[7] = 0;
+        qs = p.q_e8[head * 4 + g];
+    }
+    static __device__ __forceinline__ const void* scale_base(const IndexParams& p, int64_t row) {
+        return p.k_e8 + 4 * row;
+    }
+};
+
+template <class KF>
+__device__ __forceinline__ void stage_put(uint8_t* my, uint32_t* scl, const u32x4 (&v)[KF::kLoads], uint32_t sw,
+                                          int lane) {
+#pragma unroll
+    for (int j = 0; j < KF::kLoads; ++j) {
+        const int kk = j * (64 / KF::kLoads) + lane / KF::kChunks;
+        *reinterpret_cast<u32x4*>(my + kk * KF::kRowBytes + 16 * ((lane % KF::kChunks) ^ KF::swz(kk))) = v[j];
+    }
+    if (!KF::kScaleInScore) scl[lane] = sw;
 }
 
 // v[u] (lane (g, n)): sum over heads 4g..4g+3 of every 16-head tile t of
 // w * ReLU(q . k) for key 16u + n of the staged step.
-__device__ __forceinline__ void fp8_step_sums(const uint8_t* my, const i32x8 (&qa)[4], const float (&wr)[4][4],
-                                              int g, int li, float (&v)[4]) {
+template <class KF>
+__device__ __forceinline__ void step_sums(const uint8_t* my, const uint32_t* scl, const i32x8 (&qa)[4],
+                                          const uint32_t (&qs)[4], const float (&wr)[4][4], int g, int li,
+                                          float (&v)[4]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int kk = 16 * u + li;
-        const int sw = (kk >> 1) & 7;
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(my + kk * 128 + 16 * (g ^ sw));
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(my + kk * 128 + 16 * ((g + 4) ^ sw));
         i32x8 kb;
-        kb[0] = a0[0]; kb[1] = a0[1]; kb[2] = a0[2]; kb[3] = a0[3];
-        kb[4] = a1[0]; kb[5] = a1[1]; kb[6] = a1[2]; kb[7] = a1[3];
+        uint32_t ksc;
+        KF::frag(my, scl, 16 * u + li, g, kb, ksc);
         float acc_sum = 0.f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const f32x4 acc = mma_fp8_k128(f32x4{0.f, 0.f, 0.f, 0.f}, qa[t], kb);
+            const f32x4 acc = KF::mma(qa[t], qs[t], kb, ksc);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) acc_sum = fmaf(wr[t][rr], relu_bits(acc[rr]), acc_sum);
         }
@@ -334,42 +405,38 @@ __device__ __forceinline__ void fp8_step_sums(const uint8_t* my, const i32x8 (&q
     }
 }
 
-// Query fragments (A operands: heads as rows, 16 per tile) and head weights of query row r.
-__device__ __forceinline__ void fp8_load_query(const IndexParams& p, int r, int g, int li, i32x8 (&qa)[4],
-                                               float (&wr)[4][4]) {
+// Query fragments (A operands: heads as rows, 16 per tile), their block scales
+// and the head weights of query row r (64 heads).
+template <class KF>
+__device__ __forceinline__ void load_query(const IndexParams& p, int r, int g, int li, i32x8 (&qa)[4],
+                                           uint32_t (&qs)[4], float (&wr)[4][4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        qa[t] = IdxOps<CSA2_FP8_E4M3, 128>::load(p.q, (int64_t)r * 64 + 16 * t + li, 0, g);
+        KF::query(p, (int64_t)r * 64 + 16 * t + li, g, qa[t], qs[t]);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) wr[t][rr] = p.w[(int64_t)r * 64 + 16 * t + 4 * g + rr];
     }
 }
 
-constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, gfx9-family descriptor
-constexpr int kNT = 2;                  // non-temporal cache policy of a buffer load
-
-// FP8 FULL scoring with coalesced, non-temporal key-row loads.
+// FULL scoring of a quantised plane (64 heads x 128) with coalesced,
+// non-temporal key-row loads.
 //
 // A FULL row's key rows are contiguous in the plane, so a wave's 64-key step is
-// one 8 KiB span.  Each lane loads 8 x 16 B of it (instruction j covers keys
-// 8j..8j+7 completely: whole 128-byte lines, non-temporal, since each byte is
-// read once), writes them to its wave's LDS slot and reads them back in the
-// MFMA B-operand layout (lane (g, n) of tile u: key 16u + n, bytes 16g and
-// 64 + 16g -- the k order of the query fragments).  Chunk c of key kk sits at
-// position c ^ ((kk >> 1) & 7) of its 128-byte LDS row, which keeps both the
-// writes and the reads free of bank conflicts.
-//
-// Loads go through buffer descriptors that cover exactly the workgroup's
-// visible key rows (and their scales): a load past the visible prefix returns
-// zeros instead of touching memory, so no address is clamped and no branch
-// guards a load.  The per-lane offset is fixed for the whole launch and the
-// step offset is a scalar.  DEPTH steps of loads are in flight per wave while
-// the matrix cores work on the step in LDS.
-template <bool HIST, bool BMAX, int DEPTH, bool SCORES, bool BKEYS>
-__global__ __launch_bounds__(256) void indexer_fp8_full_kernel(const IndexParams p) {
+// one contiguous span (8 KiB FP8, 4 KiB MXFP4), loaded as whole 128-byte lines
+// (non-temporal: each byte is read once), staged in the wave's LDS slot and
+// read back in the MFMA operand layout.  Loads go through buffer descriptors
+// that cover exactly the workgroup's visible key rows and their scales: a load
+// past the visible prefix returns zeros instead of touching memory, so no
+// address is clamped and no branch guards a load (a branch there made the
+// compiler drain every outstanding load at the join).  The per-lane offset is
+// fixed for the launch and the step offset is a scalar.  DEPTH steps of loads
+// are in flight per wave while the matrix cores work on the step in LDS.
+template <class KF, bool HIST, bool BMAX, int DEPTH, bool SCORES, bool BKEYS>
+__global__ __launch_bounds__(256) void indexer_stream_kernel(const IndexParams p) {
     __shared__ uint32_t hist[HIST ? kKeyBins : 1];
-    __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * 128];
-    __shared__ __attribute__((aligned(16))) uint32_t bkl[BKEYS ? 256 * kFp8MaxSteps / kKeyBlock : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * KF::kRowBytes];
+    __shared__ uint32_t scl_all[4][KF::kScaleInScore ? 1 : 64];
+    __shared__ __attribute__((aligned(16))) uint32_t bkl[BKEYS ? 256 * kStreamMaxSteps / kKeyBlock : 1];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -384,10 +451,12 @@ __global__ __launch_bounds__(256) void indexer_fp8_full_kernel(const IndexParams
     const int64_t c_live = nv < c_end ? nv : c_end;
     float* srow = p.scores + (int64_t)r * p.width;
     uint8_t* my = stage[wave];
+    uint32_t* scl = scl_all[wave];
 
     i32x8 qa[4];
+    uint32_t qs[4];
     float wr[4][4];
-    fp8_load_query(p, r, g, li, qa, wr);
+    load_query<KF>(p, r, g, li, qa, qs, wr);
     if (HIST) {
         for (int b = threadIdx.x; b < kKeyBins; b += 256) hist[b] = 0u;
         __syncthreads();
@@ -396,45 +465,43 @@ __global__ __launch_bounds__(256) void indexer_fp8_full_kernel(const IndexParams
     // Descriptors over this workgroup's visible rows [c_begin, c_live).
     const int n_live = c_live > c_begin ? (int)(c_live - c_begin) : 0;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.k) + (base + c_begin) * 128), (short)0, n_live * 128,
-        kRsrcWord3);
+        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.k) + (base + c_begin) * KF::kRowBytes), (short)0,
+        n_live * KF::kRowBytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(p.k_scale + base + c_begin), (short)0, n_live * 4, kRsrcWord3);
-    const int ksub = lane >> 3, kchunk = lane & 7;
-    const int voff = ksub * 128 + kchunk * 16;
+        const_cast<void*>(KF::scale_base(p, base + c_begin)), (short)0, n_live * 4, kRsrcWord3);
+    const int voff = (lane / KF::kChunks) * KF::kRowBytes + (lane % KF::kChunks) * 16;
 
     struct Buf {
-        u32x4 v[8];
-        float sc;
+        u32x4 v[KF::kLoads];
+        uint32_t sw;  // scale word of key (step start + lane)
     };
     auto issue = [&](int64_t cb, Buf& b) {
-        const int so = (int)(cb - c_begin) * 128;
+        const int so = (int)(cb - c_begin) * KF::kRowBytes;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < KF::kLoads; ++j)
             b.v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff, so + 1024 * j, kNT));
-        b.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, lane * 4, (int)(cb - c_begin) * 4, 0));
+        b.sw = __builtin_amdgcn_raw_buffer_load_b32(srs, lane * 4, (int)(cb - c_begin) * 4, 0);
     };
     auto step = [&](int64_t cb, Buf& b) {
-        fp8_stage_put(my, b.v, ksub, kchunk);
-        const float sc = p.scale * b.sc;
+        stage_put<KF>(my, scl, b.v, b.sw, lane);
+        const float sc = KF::kScaleInScore ? p.scale * __uint_as_float(b.sw) : p.scale;
         const bool valid = cb + lane < c_live;
-        // Unconditional: past the visible rows the descriptor turns the loads into zeros
-        // (a conditional issue would make the compiler drain every load at the join).
+        // Unconditional: past the visible rows the descriptor turns the loads into zeros.
         issue(cb + 256 * DEPTH, b);
         float v[4];
-        fp8_step_sums(my, qa, wr, g, li, v);
+        step_sums<KF>(my, scl, qa, qs, wr, g, li, v);
         store_step<HIST, BMAX, SCORES, BKEYS>(p, r, nv, cb, c_end, lane, v, sc, valid, srow, hist, bkl, c_begin);
     };
 
-    // At most kFp8MaxSteps steps per wave (cols_per_wg <= 256 * kFp8MaxSteps): the step
-    // loop is unrolled completely, so the compiler's memory-counter waits see the
-    // loads in flight exactly instead of draining them at a loop back edge.
+    // At most kStreamMaxSteps steps per wave: the step loop is unrolled
+    // completely, so the compiler's memory-counter waits see the loads in
+    // flight exactly instead of draining them at a loop back edge.
     const int64_t cb0 = c_begin + 64 * wave;
     Buf bufs[DEPTH];
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) issue(cb0 + 256 * d, bufs[d]);
 #pragma unroll
-    for (int it = 0; it < kFp8MaxSteps; ++it) {
+    for (int it = 0; it < kStreamMaxSteps; ++it) {
         const int64_t cb = cb0 + 256 * it;
         if (cb >= c_live) break;
         step(cb, bufs[it % DEPTH]);
@@ -456,13 +523,13 @@ __global__ __launch_bounds__(256) void indexer_fp8_full_kernel(const IndexParams
     }
 }
 
-// Re-scoring for the top-k of FP8 FULL scores that were never written.
+// Re-scoring for the top-k of FULL scores that were never written.
 //
 // Segment seg of row r covers columns [seg * chunk, (seg + 1) * chunk).  b1[r]
 // is the histogram bin holding the row's k-th largest key, so every selected
 // column has a key in bin >= b1, and so has the largest key of its
 // kKeyBlock-column block.  One wave handles one segment on its own (no
-// barriers): per batch of 2048 blocks it loads the block keys (32 per lane, at
+// barriers): per batch of 1024 blocks it loads the block keys (16 per lane, at
 // once), queues in column order the blocks whose key reaches bin b1 in an LDS
 // list, then re-scores the queue 8 blocks (one 64-key step) at a time with
 // exactly the scoring pass's arithmetic, appending the (key, column) pairs of
@@ -471,15 +538,16 @@ __global__ __launch_bounds__(256) void indexer_fp8_full_kernel(const IndexParams
 constexpr int kRescoreBatch = 16;                  // block keys per lane per batch
 constexpr int kRescoreQueue = 64 * kRescoreBatch;  // blocks per batch
 
-__global__ __launch_bounds__(256) void indexer_fp8_rescore_kernel(const IndexParams p, const uint32_t* b1_in,
-                                                                  int chunk, int nseg, uint32_t* cand_keys,
-                                                                  int32_t* cand_cols, uint32_t* seg_count) {
-    __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * 128];
+template <class KF>
+__global__ __launch_bounds__(256) void indexer_rescore_kernel(const IndexParams p, const uint32_t* b1_in, int chunk,
+                                                              int nseg, uint32_t* cand_keys, int32_t* cand_cols,
+                                                              uint32_t* seg_count) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * KF::kRowBytes];
+    __shared__ uint32_t scl_all[4][KF::kScaleInScore ? 1 : 64];
     __shared__ int32_t queue[4][kRescoreQueue];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, li = lane & 15;
-    const int ksub = lane >> 3, kchunk = lane & 7;
     const int r = blockIdx.y;
     const int seg = 4 * blockIdx.x + wave;
     if (seg >= nseg) return;  // no barriers in this kernel: waves are independent
@@ -495,41 +563,45 @@ __global__ __launch_bounds__(256) void indexer_fp8_rescore_kernel(const IndexPar
     uint32_t* okeys = cand_keys + ((int64_t)r * nseg + seg) * chunk;
     int32_t* ocols = cand_cols + ((int64_t)r * nseg + seg) * chunk;
     uint8_t* my = stage[wave];
+    uint32_t* scl = scl_all[wave];
     int32_t* q8 = queue[wave];
 
     i32x8 qa[4];
+    uint32_t qs[4];
     float wr[4][4];
-    fp8_load_query(p, r, g, li, qa, wr);
+    load_query<KF>(p, r, g, li, qa, qs, wr);
     // the row's visible key rows and their scales; loads beyond them return zeros
     const int n_rows = (int)(n_valid > 0 ? n_valid : 0);
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.k) + base * 128), (short)0, n_rows * 128,
-        kRsrcWord3);
+        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.k) + base * KF::kRowBytes), (short)0,
+        n_rows * KF::kRowBytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(p.k_scale + base), (short)0, n_rows * 4, kRsrcWord3);
+        const_cast<void*>(KF::scale_base(p, base)), (short)0, n_rows * 4, kRsrcWord3);
 
     uint32_t n_out = 0;
     // Re-scores queued blocks head .. head+cnt-1 (cnt 1..8) as one step and appends their candidates.
     auto rescore = [&](int head, int cnt) {
-        u32x4 buf[8];
+        u32x4 buf[KF::kLoads];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            // rows of block j; past the queue: an offset beyond the descriptor -> zeros
-            const int row = j < cnt ? q8[head + j] * kKeyBlock + ksub : n_rows;
-            buf[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, row * 128 + 16 * kchunk, 0,
-                                                                                     kNT));
+        for (int j = 0; j < KF::kLoads; ++j) {
+            // key kk of the step = row kk % 8 of queued block kk / 8; past the queue: an
+            // offset beyond the descriptor -> zeros
+            const int kk = j * (64 / KF::kLoads) + lane / KF::kChunks;
+            const int blk = kk >> 3;
+            const int row = blk < cnt ? q8[head + blk] * kKeyBlock + (kk & 7) : n_rows;
+            buf[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   krs, row * KF::kRowBytes + 16 * (lane % KF::kChunks), 0, kNT));
         }
         const int my_blk = lane / kKeyBlock;
         const int64_t col = my_blk < cnt
             ? (int64_t)q8[head + my_blk] * kKeyBlock + (lane % kKeyBlock) : n_valid;
-        const float ksc = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(col < n_valid ? col : n_valid) * 4, 0, 0));
-        fp8_stage_put(my, buf, ksub, kchunk);
+        const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(col < n_valid ? col : n_valid) * 4, 0, 0);
+        stage_put<KF>(my, scl, buf, sw, lane);
         float v[4];
-        fp8_step_sums(my, qa, wr, g, li, v);
+        step_sums<KF>(my, scl, qa, qs, wr, g, li, v);
         const float kk = reduce_scatter(v, lane);
         const bool valid = col < n_valid;
-        const float sc = p.scale * ksc;
+        const float sc = KF::kScaleInScore ? p.scale * __uint_as_float(sw) : p.scale;
         const uint32_t key = order_key(sc * kk);
         const bool take = valid && (key >> 20) >= b1;
         const uint64_t m = __ballot(take);
@@ -568,10 +640,15 @@ __global__ __launch_bounds__(256) void indexer_fp8_rescore_kernel(const IndexPar
     if (lane == 0) seg_count[(int64_t)r * nseg + seg] = n_out;
 }
 
-hipError_t launch_indexer_rescore(const IndexParams& p, int rows, const uint32_t* b1, int chunk, int nseg,
+hipError_t launch_indexer_rescore(const IndexParams& p, int rows, int dtype, const uint32_t* b1, int chunk, int nseg,
                                   uint32_t* cand_keys, int32_t* cand_cols, uint32_t* seg_count, hipStream_t stream) {
-    hipLaunchKernelGGL(indexer_fp8_rescore_kernel, dim3((unsigned)((nseg + 3) / 4), (unsigned)rows), dim3(256), 0,
-                       stream, p, b1, chunk, nseg, cand_keys, cand_cols, seg_count);
+    const dim3 grid((unsigned)((nseg + 3) / 4), (unsigned)rows);
+    if (dtype == CSA2_FP4_E2M1)
+        hipLaunchKernelGGL(indexer_rescore_kernel<Fp4Keys>, grid, dim3(256), 0, stream, p, b1, chunk, nseg, cand_keys,
+                           cand_cols, seg_count);
+    else
+        hipLaunchKernelGGL(indexer_rescore_kernel<Fp8Keys>, grid, dim3(256), 0, stream, p, b1, chunk, nseg, cand_keys,
+                           cand_cols, seg_count);
     return hipGetLastError();
 }
 
@@ -603,8 +680,9 @@ static hipError_t launch_one(const IndexParams& p, int rows, hipStream_t stream)
     return hipGetLastError();
 }
 
-static hipError_t launch_fp8_full(const IndexParams& p, int rows, hipStream_t stream) {
-    if (p.cols_per_wg > 256 * kFp8MaxSteps || p.cols_per_wg % 256 != 0) return hipErrorInvalidValue;
+template <class KF>
+static hipError_t launch_stream_full(const IndexParams& p, int rows, hipStream_t stream) {
+    if (p.cols_per_wg > 256 * kStreamMaxSteps || p.cols_per_wg % 256 != 0) return hipErrorInvalidValue;
     const int64_t chunks = (p.width + p.cols_per_wg - 1) / p.cols_per_wg;
     dim3 grid((unsigned)chunks, (unsigned)rows);
     const bool hist = p.key_hist != nullptr;
@@ -613,19 +691,19 @@ static hipError_t launch_fp8_full(const IndexParams& p, int rows, hipStream_t st
         hipLaunchKernelGGL(key_hist_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)),
                            dim3(256), 0, stream, p.key_hist, nh);
     }
-    constexpr int D = kFp8Depth;
+    constexpr int D = kStreamDepth;
     if (p.scores == nullptr) {
         // scores kept on chip: histogram and block keys only (validated by the caller)
         if (p.block_max != nullptr)
-            hipLaunchKernelGGL((indexer_fp8_full_kernel<true, true, D, false, true>), grid, dim3(256), 0, stream, p);
+            hipLaunchKernelGGL((indexer_stream_kernel<KF, true, true, D, false, true>), grid, dim3(256), 0, stream, p);
         else
-            hipLaunchKernelGGL((indexer_fp8_full_kernel<true, false, D, false, true>), grid, dim3(256), 0, stream, p);
+            hipLaunchKernelGGL((indexer_stream_kernel<KF, true, false, D, false, true>), grid, dim3(256), 0, stream, p);
     } else if (p.block_max != nullptr) {
-        if (hist) hipLaunchKernelGGL((indexer_fp8_full_kernel<true, true, D, true, false>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((indexer_fp8_full_kernel<false, true, D, true, false>), grid, dim3(256), 0, stream, p);
+        if (hist) hipLaunchKernelGGL((indexer_stream_kernel<KF, true, true, D, true, false>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((indexer_stream_kernel<KF, false, true, D, true, false>), grid, dim3(256), 0, stream, p);
     } else {
-        if (hist) hipLaunchKernelGGL((indexer_fp8_full_kernel<true, false, D, true, false>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((indexer_fp8_full_kernel<false, false, D, true, false>), grid, dim3(256), 0, stream, p);
+        if (hist) hipLaunchKernelGGL((indexer_stream_kernel<KF, true, false, D, true, false>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((indexer_stream_kernel<KF, false, false, D, true, false>), grid, dim3(256), 0, stream, p);
     }
     return hipGetLastError();
 }
@@ -636,7 +714,8 @@ hipError_t launch_indexer_score(const IndexParams& p, int rows, int heads, int d
         if (dtype == CSA2_BF16) return reindex ? launch_one<CSA2_BF16, 64, 128, true>(p, rows, stream)
                                                : launch_one<CSA2_BF16, 64, 128, false>(p, rows, stream);
         if (dtype == CSA2_FP8_E4M3) return reindex ? launch_one<CSA2_FP8_E4M3, 64, 128, true>(p, rows, stream)
-                                                   : launch_fp8_full(p, rows, stream);
+                                                   : launch_stream_full<Fp8Keys>(p, rows, stream);
+        if (dtype == CSA2_FP4_E2M1) return reindex ? hipErrorInvalidValue : launch_stream_full<Fp4Keys>(p, rows, stream);
         if (dtype == CSA2_F32) return reindex ? launch_one<CSA2_F32, 64, 128, true>(p, rows, stream)
                                               : launch_one<CSA2_F32, 64, 128, false>(p, rows, stream);
     }
@@ -650,11 +729,12 @@ hipError_t launch_indexer_score(const IndexParams& p, int rows, int heads, int d
 }
 
 bool indexer_rescore_supported(int heads, int dim, int dtype) {
-    return heads == 64 && dim == 128 && dtype == CSA2_FP8_E4M3;
+    return heads == 64 && dim == 128 && (dtype == CSA2_FP8_E4M3 || dtype == CSA2_FP4_E2M1);
 }
 
 bool indexer_supported(int heads, int dim, int dtype) {
-    if (heads == 64 && dim == 128) return dtype == CSA2_BF16 || dtype == CSA2_FP8_E4M3 || dtype == CSA2_F32;
+    if (heads == 64 && dim == 128)
+        return dtype == CSA2_BF16 || dtype == CSA2_FP8_E4M3 || dtype == CSA2_F32 || dtype == CSA2_FP4_E2M1;
     if (heads == 4 && dim == 32) return dtype == CSA2_F32 || dtype == CSA2_BF16;
     return false;
 }

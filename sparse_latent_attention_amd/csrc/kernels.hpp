@@ -20,6 +20,8 @@ struct IndexParams {
     uint32_t* key_hist;  // optional [rows, 4096]
     float* block_max;    // optional [rows, bm_blocks] (FULL only)
     uint32_t* block_keys;  // optional [rows, ceil(width / kKeyBlock)] (FULL only)
+    const uint8_t* q_e8;   // MXFP4 query: E8M0 [rows, heads, dim / 32]
+    const uint8_t* k_e8;   // MXFP4 keys: E8M0 [*, dim / 32]
     int64_t width;
     int64_t cols_per_wg;
     int64_t bm_blocks;   // ceil(width / bm_rows)
@@ -67,7 +69,7 @@ hipError_t launch_topk_final(const TopkParams& p, int rows, const uint32_t* cand
 
 // Re-scoring of candidate blocks for the score-free FP8 FULL path.
 bool indexer_rescore_supported(int heads, int dim, int dtype);
-hipError_t launch_indexer_rescore(const IndexParams& p, int rows, const uint32_t* b1, int chunk, int nseg,
+hipError_t launch_indexer_rescore(const IndexParams& p, int rows, int dtype, const uint32_t* b1, int chunk, int nseg,
                                   uint32_t* cand_keys, int32_t* cand_cols, uint32_t* seg_count, hipStream_t stream);
 
 // Block scores of the candidate pool from FULL score rows (out: [rows, nb]).

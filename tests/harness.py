@@ -14,6 +14,7 @@ import torch
 
 import oracle
 from oracle import formats
+from workloads.step import attn_storage_args, index_plane_args
 
 # Tolerances.
 # Indexer scores: |gpu - oracle| <= SCORE_TOL * A, A = tau_I sum_h |w_h| sum_d |q_hd k_d|.
@@ -83,11 +84,9 @@ def gpu_scores(cfg, x, key_hist=None, block_max=None):
     import sparse_latent_attention_amd as csa2
     rows = x["pos"].shape[0]
     scores = torch.empty(rows, cfg.width, dtype=torch.float32, device=x["pos"].device)
-    kI = x["kI"].reshape(-1, cfg.idx_dim)
-    ks = None if x["kI_scale"] is None else x["kI_scale"].reshape(-1)
+    kI, ikw = index_plane_args(cfg, x)
     csa2.indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, index_scale(cfg), scores,
-                       k_scale=ks, cand=x.get("cand"), block_rows=cfg.block_rows, fp8=cfg.idx_dtype == "fp8",
-                       key_hist=key_hist, block_max=block_max)
+                       cand=x.get("cand"), block_rows=cfg.block_rows, key_hist=key_hist, block_max=block_max, **ikw)
     return scores
 
 
@@ -118,19 +117,17 @@ def gpu_attention(cfg, x, idx, layer=0, out=None):
     L = x["layers"][layer]
     q = L["q"]
     out = torch.empty_like(q) if out is None else out
-    kw = dict(rope_dim=cfg.rope_dim, kv_fp4=cfg.main_dtype == "fp4", swa_fp8=cfg.swa_dtype == "fp8")
-    kv = x["main"].reshape(-1, x["main"].shape[-1])
-    kvs = None if x["main_scale"] is None else x["main_scale"].reshape(-1, x["main_scale"].shape[-1])
+    kv, kw = attn_storage_args(cfg, x)
     freqs = inv_freq_device(cfg, q.device)
     scale = 1.0 / math.sqrt(cfg.dim)
     if cfg.phase == "decode":
         swa = x["swa"]
         sws = x["swa_scale"]
         csa2.sparse_attn_decode(q, x["pos"], idx, kv, x["kv_row_base"], swa, L["sink"], freqs, cfg.ratio,
-                                cfg.window, scale, out, kv_scale=kvs, swa_scale=sws, **kw)
+                                cfg.window, scale, out, swa_scale=sws, **kw)
     else:
         csa2.sparse_attn_prefill(q, x["pos"], idx, kv, L["swa"], x["swa_pos0"], L["sink"], freqs, cfg.ratio,
-                                 cfg.window, scale, out, kv_scale=kvs, swa_scale=L["swa_scale"],
+                                 cfg.window, scale, out, swa_scale=L["swa_scale"],
                                  kv_row_base=x["kv_row_base"], **kw)
     return out
 

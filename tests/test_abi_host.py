@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(csa2.EXPORTED)
-    assert csa2.ABI_VERSION == 3
+    assert csa2.ABI_VERSION == 4
 
 
 def test_struct_layouts_match_c_compiler():
@@ -43,7 +43,7 @@ int main(void) {
   printf("csa2_topk_args sizeof %zu\n", sizeof(csa2_topk_args));
   printf("csa2_attn_args sizeof %zu\n", sizeof(csa2_attn_args));
   printf("csa2_pool_args sizeof %zu\n", sizeof(csa2_pool_args));
-  F(csa2_index_args, width) F(csa2_index_args, q) F(csa2_index_args, cand) F(csa2_index_args, scale) F(csa2_index_args, scores) F(csa2_index_args, key_hist) F(csa2_index_args, block_max) F(csa2_index_args, block_keys)
+  F(csa2_index_args, width) F(csa2_index_args, q) F(csa2_index_args, cand) F(csa2_index_args, scale) F(csa2_index_args, scores) F(csa2_index_args, key_hist) F(csa2_index_args, block_max) F(csa2_index_args, block_keys) F(csa2_index_args, q_scale_e8m0) F(csa2_index_args, k_scale_e8m0)
   F(csa2_pool_args, n_cand) F(csa2_pool_args, width) F(csa2_pool_args, scores) F(csa2_pool_args, block_max) F(csa2_pool_args, pos) F(csa2_pool_args, cand) F(csa2_pool_args, block_keys)
   F(csa2_topk_args, width) F(csa2_topk_args, scores) F(csa2_topk_args, out) F(csa2_topk_args, key_hist)
   F(csa2_attn_args, swa_rows) F(csa2_attn_args, q) F(csa2_attn_args, rope_inv_freq) F(csa2_attn_args, softmax_scale) F(csa2_attn_args, out)
@@ -133,6 +133,35 @@ def test_score_free_mode_rules():
     # block keys are only written in score-free mode
     a = _index_args(block_keys=ptr, key_hist=ptr, **fp8)
     assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+
+
+def test_mxfp4_indexer_rules():
+    """MXFP4 q and k take both E8M0 planes (4-byte aligned for k) and no float scale; FULL 64 x 128 only."""
+    ptr = ctypes.c_void_p(0x1000)
+    fp4 = dict(q_dtype=csa2.FP4_E2M1, k_dtype=csa2.FP4_E2M1, q_scale_e8m0=ptr, k_scale_e8m0=ptr, width=1 << 20)
+    call = lambda **kw: csa2._lib.csa2_indexer_score(ctypes.byref(_index_args(**dict(fp4, **kw))), None)
+    assert call(rows=0) == csa2.OK                                      # accepted shape, nothing to do
+    assert call(q_scale_e8m0=None) == csa2.ERR_INVALID_ARG
+    assert call(k_scale_e8m0=None) == csa2.ERR_INVALID_ARG
+    assert call(k_scale_e8m0=ctypes.c_void_p(0x1002)) == csa2.ERR_INVALID_ARG
+    assert call(k_scale=ptr) == csa2.ERR_INVALID_ARG
+    assert call(heads=4, dim=32) == csa2.ERR_UNSUPPORTED
+    assert call(mode=csa2.MODE_REINDEX, cand=ptr, n_blocks=2048, block_rows=8, width=16384) == csa2.ERR_UNSUPPORTED
+    # the E8M0 planes belong to MXFP4 only
+    a = _index_args(q_scale_e8m0=ptr, k_scale_e8m0=ptr)
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+    a = _index_args(q_dtype=csa2.FP8_E4M3, k_dtype=csa2.FP8_E4M3, k_scale=ptr, q_scale_e8m0=ptr)
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+    # score-free mode and the re-scoring select take MXFP4 like FP8
+    a = _index_args(scores=None, key_hist=ptr, block_keys=ptr, rows=0, **fp4)
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.OK
+    a = _index_args(scores=None, key_hist=ptr, block_keys=ptr, **fp4)
+    ws = csa2.topk_rescore_workspace_size(a.rows, a.width, 512)
+    assert csa2._lib.csa2_topk_rescore(ctypes.byref(a), 512, ptr, ctypes.c_void_p(0x10000), ws - 1, None) == \
+        csa2.ERR_WORKSPACE
+    a = _index_args(scores=None, key_hist=ptr, block_keys=ptr, **dict(fp4, k_scale_e8m0=None))
+    assert csa2._lib.csa2_topk_rescore(ctypes.byref(a), 512, ptr, ctypes.c_void_p(0x10000), ws, None) == \
+        csa2.ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("kw,k,status", [
@@ -248,6 +277,19 @@ def _attn_args(**kw):
 def test_attention_validation(field, value, status):
     a = _attn_args(**{field: value})
     assert csa2._lib.csa2_sparse_attn_prefill(ctypes.byref(a), None) == status
+
+
+def test_attention_inline_scale_rows():
+    """E2M1 + E4M3/16 kv goes with FP8 + E8M0/32 swa and takes no separate scale arrays."""
+    ptr = ctypes.c_void_p(0x1000)
+    g = dict(kv_dtype=csa2.FP4_E2M1_E4M3G16, swa_dtype=csa2.FP8_E4M3_E8M0G32)
+    run = lambda **kw: csa2._lib.csa2_sparse_attn_prefill(ctypes.byref(_attn_args(**kw)), None)
+    assert run(rows=0, **g) == csa2.OK
+    assert run(kv_scale=ptr, **g) == csa2.ERR_INVALID_ARG
+    assert run(swa_scale=ptr, **g) == csa2.ERR_INVALID_ARG
+    assert run(kv_dtype=csa2.FP4_E2M1_E4M3G16) == csa2.ERR_UNSUPPORTED            # with bf16 swa
+    assert run(swa_dtype=csa2.FP8_E4M3_E8M0G32) == csa2.ERR_UNSUPPORTED           # with bf16 kv
+    assert run(kv_dtype=csa2.FP4_E2M1, kv_scale=ptr, swa_dtype=csa2.FP8_E4M3_E8M0G32) == csa2.ERR_UNSUPPORTED
 
 
 def test_decode_needs_no_workspace_and_rejects_reserved_field():

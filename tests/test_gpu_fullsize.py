@@ -19,7 +19,7 @@ from harness import (BF16_ATOL, BF16_RTOL, F32_ATOL, F32_RTOL, SCORE_TOL, assert
 pytestmark = pytest.mark.gpu
 
 NAMES = ["tiny_full_fp32", "full_decode_64k", "prefill_4096_at_128k", "reindex_decode_1m", "lowp_full_decode_1m",
-         "lowp_pool_decode_1m"]
+         "lowp_pool_decode_1m", "pages_fp4_decode_1m"]
 
 
 def _run_path(cfg, x):

@@ -28,6 +28,7 @@ SMALL = {
     "reindex_small": CONFIGS["reindex_decode_1m"].replace(batch=7, q_tokens=7, context=40001, n_blocks=200,
                                                           ragged=True),
     "lowp_small": CONFIGS["lowp_full_decode_1m"].replace(batch=7, q_tokens=7, context=5003, ragged=True),
+    "pages_fp4_small": CONFIGS["pages_fp4_decode_1m"].replace(batch=7, q_tokens=7, context=5003, ragged=True),
     "prefill_small": CONFIGS["prefill_4096_at_128k"].replace(q_tokens=300, context=2000, reuse_layers=2),
 }
 

@@ -10,7 +10,7 @@ oracle (tests/test_gpu_parity.py, tests/test_gpu_fullsize.py):
     of them.
 Inputs include ragged histories (rows with fewer visible rows than k, a row
 at position 0), duplicated key rows (exact score ties across blocks), and
-the full 1M-row width.
+the full 1M-row width, for FP8 and for MXFP4 index planes.
 """
 import numpy as np
 import pytest
@@ -19,6 +19,7 @@ import torch
 from workloads import CONFIGS, make_inputs
 
 from harness import gpu_scores, gpu_topk, host_key_hist, index_scale, oracle_score_bound, oracle_topk
+from workloads.step import index_plane_args
 
 pytestmark = pytest.mark.gpu
 
@@ -36,17 +37,18 @@ def _score_free(cfg, x, k):
     dev = x["pos"].device
     hist = torch.full((rows, 4096), 7, dtype=torch.int32, device=dev)          # the call must zero it
     bkeys = torch.full((rows, -(-cfg.width // 8)), 12345, dtype=torch.int32, device=dev)
-    kI = x["kI"].reshape(-1, cfg.idx_dim)
-    ks = x["kI_scale"].reshape(-1)
+    kI, ikw = index_plane_args(cfg, x)
     csa2.indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, index_scale(cfg), None,
-                       width=cfg.width, k_scale=ks, fp8=True, key_hist=hist, block_keys=bkeys)
+                       width=cfg.width, key_hist=hist, block_keys=bkeys, **ikw)
     out = torch.full((rows, k), -7, dtype=torch.int32, device=dev)
+    ikw.pop("fp8", None)
     csa2.topk_rescore(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, index_scale(cfg), out, hist, bkeys,
-                      cfg.width, k_scale=ks)
+                      cfg.width, **ikw)
     torch.cuda.synchronize()
     return hist, bkeys, out
 
 
+_MX = CONFIGS["pages_fp4_decode_1m"]
 CASES = {
     "ragged_100k": (CONFIGS["lowp_full_decode_1m"].replace(batch=6, q_tokens=6, context=100003, ragged=True), 512),
     "short_rows": (CONFIGS["lowp_full_decode_1m"].replace(batch=5, q_tokens=5, context=30000, ragged=True), 512),
@@ -54,6 +56,12 @@ CASES = {
     "ratio2": (CONFIGS["lowp_full_decode_1m"].replace(batch=4, q_tokens=4, context=80001, ratio=2, ragged=True), 512),
     "ties": (CONFIGS["lowp_full_decode_1m"].replace(batch=4, q_tokens=4, context=40000), 512),
     "full_1m": (CONFIGS["lowp_full_decode_1m"].replace(batch=3, q_tokens=3), 512),
+    # MXFP4 index plane and query
+    "mx_ragged_100k": (_MX.replace(batch=6, q_tokens=6, context=100003, ragged=True), 512),
+    "mx_short_rows": (_MX.replace(batch=5, q_tokens=5, context=30000, ragged=True), 512),
+    "mx_k2048_ratio2": (_MX.replace(batch=4, q_tokens=4, context=80001, ratio=2), 2048),
+    "mx_ties": (_MX.replace(batch=4, q_tokens=4, context=40000), 512),
+    "mx_full_1m": (_MX.replace(batch=3, q_tokens=3), 512),
 }
 
 
@@ -64,17 +72,17 @@ def test_score_free_matches_written_scores(name):
     print(f"\n[rescore] {name} rows={cfg.q_tokens} width={cfg.width} k={k}", flush=True)
     x = make_inputs(cfg, 51, device="cuda")
     rows = cfg.q_tokens
-    if name == "short_rows":
+    if name.endswith("short_rows"):
         x["pos"][0] = 0
         x["pos"][1] = 300              # fewer visible rows than k
         x["pos"][2] = 8 * 64 + 2
-    if name == "ties":
-        # every 40th key row (and its scale) is a copy of row 17: equal scores across blocks
-        kI = x["kI"].view(rows, -1, cfg.idx_dim)
+    if name.endswith("ties"):
+        # every 40th key row (and its scales) is a copy of row 17: equal scores across blocks
+        kI = x["kI"].view(rows, -1, x["kI"].shape[-1])
         kI[:, ::40] = kI[:, 17:18]
-        sc = x["kI_scale"].view(rows, -1)
+        sc = x["kI_scale"].view(rows, -1, *x["kI_scale"].shape[2:])
         sc[:, ::40] = sc[:, 17:18]
-    assert csa2.topk_rescore_supported(rows, cfg.width, k)
+    assert csa2.topk_rescore_supported(rows, cfg.width, k, fp8=cfg.idx_dtype == "fp8", fp4=cfg.idx_dtype == "fp4")
     hist, bkeys, out = _score_free(cfg, x, k)
 
     scores = gpu_scores(cfg, x)

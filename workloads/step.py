@@ -3,7 +3,7 @@
 A step is the whole path over one batch (see bench.py): the indexer scores,
 the top-k, the candidate pool when the workload's FULL layer builds one, and
 sparse attention for every layer that uses the selection.  Wide FULL rows with
-an FP8 index plane take the score-free route (indexer_score with scores=None,
+an FP8 or MXFP4 index plane take the score-free route (indexer_score with scores=None,
 then topk_rescore) whenever the library supports the shape; everything else
 writes the scores and runs topk_select.  bench.py times these calls and the
 full-size parity tests run exactly the same ones.
@@ -12,6 +12,25 @@ full-size parity tests run exactly the same ones.
 import math
 
 import torch
+
+
+def index_plane_args(cfg, x):
+    """(k, keyword arguments) of indexer_score / topk_rescore for the workload's index plane: the plane as
+    [*, row elements or bytes] and its scale operands and format flags."""
+    if cfg.idx_dtype == "fp4":
+        kI = x["kI"].reshape(-1, cfg.idx_dim // 2)
+        return kI, dict(fp4=True, k_scale=x["kI_scale"].reshape(-1, cfg.idx_dim // 32), q_scale=x["qI_scale"])
+    kI = x["kI"].reshape(-1, cfg.idx_dim)
+    kIs = None if x["kI_scale"] is None else x["kI_scale"].reshape(-1)
+    return kI, dict(fp8=cfg.idx_dtype == "fp8", k_scale=kIs)
+
+
+def attn_storage_args(cfg, x):
+    """(kv, keyword arguments) of the sparse attention calls for the workload's main and SWA storage."""
+    kv = x["main"].reshape(-1, x["main"].shape[-1])
+    kvs = None if x["main_scale"] is None else x["main_scale"].reshape(-1, x["main_scale"].shape[-1])
+    return kv, dict(rope_dim=cfg.rope_dim, kv_fp4=cfg.main_dtype == "fp4", swa_fp8=cfg.swa_dtype == "fp8",
+                    kv_nvfp4=cfg.main_dtype == "nvfp4", swa_fp8mx=cfg.swa_dtype == "fp8mx", kv_scale=kvs)
 
 
 class Step:
@@ -24,16 +43,15 @@ class Step:
         dev = x["pos"].device
         rows = x["pos"].shape[0]
         self.rows = rows
-        kI = x["kI"].reshape(-1, cfg.idx_dim)
-        kIs = None if x["kI_scale"] is None else x["kI_scale"].reshape(-1)
-        kv = x["main"].reshape(-1, x["main"].shape[-1])
-        kvs = None if x["main_scale"] is None else x["main_scale"].reshape(-1, x["main_scale"].shape[-1])
+        kI, ikw = index_plane_args(cfg, x)
+        kv, akw = attn_storage_args(cfg, x)
         tau_i = 1.0 / math.sqrt(cfg.idx_dim * cfg.idx_heads)
         tau = 1.0 / math.sqrt(cfg.dim)
-        fp8 = cfg.idx_dtype == "fp8"
+        quantised = cfg.idx_dtype in ("fp8", "fp4")
         if score_free is None:
-            score_free = (cfg.index_mode == "full" and fp8 and
-                          csa2.topk_rescore_supported(rows, cfg.width, cfg.topk, cfg.idx_heads, cfg.idx_dim, fp8))
+            score_free = (cfg.index_mode == "full" and quantised and
+                          csa2.topk_rescore_supported(rows, cfg.width, cfg.topk, cfg.idx_heads, cfg.idx_dim,
+                                                      fp8=cfg.idx_dtype == "fp8", fp4=cfg.idx_dtype == "fp4"))
         self.score_free = score_free
         self.idx = torch.empty(rows, cfg.topk, dtype=torch.int32, device=dev)
         self.outs = [torch.empty_like(L["q"]) for L in x["layers"]]
@@ -51,19 +69,21 @@ class Step:
             self.block_keys = torch.empty(rows, -(-cfg.width // 8), dtype=torch.int32, device=dev)
             # the pool's block scores come from the block keys: no block_max pass
             self.block_max = None
-            call_idx = csa2.prepare_indexer_score(*idx_common, None, width=cfg.width, k_scale=kIs, fp8=True,
-                                                  key_hist=self.key_hist, block_keys=self.block_keys)
+            call_idx = csa2.prepare_indexer_score(*idx_common, None, width=cfg.width, key_hist=self.key_hist,
+                                                  block_keys=self.block_keys, **ikw)
+            rkw = dict(ikw)
+            rkw.pop("fp8", None)
             call_topk = csa2.prepare_topk_rescore(*idx_common, self.idx, self.key_hist, self.block_keys, cfg.width,
-                                                  k_scale=kIs)
+                                                  **rkw)
         else:
             self.scores = torch.empty(rows, cfg.width, dtype=torch.float32, device=dev)
             # the indexer also builds the score-key histogram when top-k takes its wide-row path
             self.key_hist = (torch.empty(rows, 4096, dtype=torch.int32, device=dev)
                              if csa2.topk_uses_key_hist(rows, cfg.width, cfg.topk) else None)
             self.block_keys = None
-            call_idx = csa2.prepare_indexer_score(*idx_common, self.scores, k_scale=kIs, cand=x.get("cand"),
-                                                  block_rows=cfg.block_rows, fp8=fp8, key_hist=self.key_hist,
-                                                  block_max=self.block_max)
+            call_idx = csa2.prepare_indexer_score(*idx_common, self.scores, cand=x.get("cand"),
+                                                  block_rows=cfg.block_rows, key_hist=self.key_hist,
+                                                  block_max=self.block_max, **ikw)
             call_topk = csa2.prepare_topk_select(self.scores, x["pos"], cfg.ratio, self.idx, cand=x.get("cand"),
                                                  block_rows=cfg.block_rows, key_hist=self.key_hist)
         self.groups = {"indexer_score": [call_idx], "topk_select": [call_topk]}
@@ -71,8 +91,6 @@ class Step:
             src = dict(block_keys=self.block_keys) if score_free else dict(block_max=self.block_max)
             self.groups["candidate_pool"] = [csa2.prepare_candidate_pool(
                 x["pos"], cfg.ratio, self.pool, width=cfg.width, block_rows=cfg.block_rows, **src)]
-        akw = dict(rope_dim=cfg.rope_dim, kv_fp4=cfg.main_dtype == "fp4", swa_fp8=cfg.swa_dtype == "fp8",
-                   kv_scale=kvs)
         attn = []
         for li, L in enumerate(x["layers"]):
             if cfg.phase == "decode":
