@@ -152,7 +152,9 @@ typedef struct csa2_index_args {
                                  * key is the order-preserving 32-bit key csa2_topk_select ranks by
                                  * (bits | 0x80000000 for scores >= +0, ~bits below, NaN as -inf,
                                  * -0 as +0).  Passing it on to csa2_topk_select saves that call a
-                                 * full pass over the scores. */
+                                 * full pass over the scores.  In score-free mode it counts instead,
+                                 * per 8-column block with a valid column, the bin block_keys[b] >> 20
+                                 * of its block key (below). */
     float* block_max;           /* optional out, FULL only: [rows, ceil(width / block_rows)], or NULL.
                                  * Block b of row r gets the block score csa2_candidate_pool ranks:
                                  * the largest score over its visible columns, with NaN read as -inf
@@ -179,11 +181,13 @@ int32_t csa2_indexer_score(const csa2_index_args* args, csa2_stream_t stream);
  * score-free mode (csa2_indexer_score with scores == NULL, which requires FULL
  * mode, key_hist and block_keys) the scores stay on chip: the call writes the
  * key histogram and the per-8-column block keys only.  csa2_topk_rescore then
- * takes the same arguments and returns the top-k: from the histogram it finds
- * the bin holding each row's k-th largest key, re-scores exactly the blocks
- * whose block key reaches that bin (every selected column lies in one), with
- * the same arithmetic as the scoring pass, and runs the exact select of
- * csa2_topk_select over those columns.  The result is bit-identical to
+ * takes the same arguments and returns the top-k: from the block-key histogram
+ * it finds the bin b1 holding each row's k-th largest block key (the k blocks
+ * with the largest keys hold k columns with keys in bins >= b1, so every
+ * selected column has a key in a bin >= b1), re-scores exactly the blocks
+ * whose block key reaches b1 (every selected column lies in one), with the
+ * same arithmetic as the scoring pass, and runs the exact select of
+ * csa2_topk_select over their columns in bins >= b1.  The result is bit-identical to
  * csa2_topk_select over the scores csa2_indexer_score would have written.
  *
  * args: as given to the score-free csa2_indexer_score call (key_hist and

@@ -152,13 +152,18 @@ __device__ __forceinline__ void store_step(const IndexParams& p, int r, int64_t 
     const float score = valid ? sc * kk : kNegInf;
     if (c_out < c_end) {
         if (SCORES) srow[c_out] = score;
-        if (HIST && valid) atomicAdd(&hist[order_key(score) >> 20], 1u);
+        if (HIST && !BKEYS && valid) atomicAdd(&hist[order_key(score) >> 20], 1u);
     }
     if (BKEYS) {
+        // Score-free mode: the histogram counts block keys (one LDS atomic per 8
+        // columns instead of per column); a block without valid columns has key 0.
         uint32_t bk = valid ? block_key(score) : 0u;
 #pragma unroll
         for (int o = 1; o < kKeyBlock; o <<= 1) bk = max(bk, shfl_xor(bk, o));
-        if ((lane & (kKeyBlock - 1)) == 0 && c_out < c_end) bkl[(c_out - c0) / kKeyBlock] = bk;
+        if ((lane & (kKeyBlock - 1)) == 0 && c_out < c_end) {
+            bkl[(c_out - c0) / kKeyBlock] = bk;
+            if (HIST && bk != 0u) atomicAdd(&hist[bk >> 20], 1u);
+        }
     }
     if (BMAX) {
         // Block score over bm_rows consecutive columns = lanes (blocks never
@@ -526,9 +531,11 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(const IndexParams p
 // Re-scoring for the top-k of FULL scores that were never written.
 //
 // Segment seg of row r covers columns [seg * chunk, (seg + 1) * chunk).  b1[r]
-// is the histogram bin holding the row's k-th largest key, so every selected
-// column has a key in bin >= b1, and so has the largest key of its
-// kKeyBlock-column block.  One wave handles one segment on its own (no
+// is the bin holding the row's k-th largest block key (the score-free pass
+// counts block keys).  The k blocks with the largest keys hold k distinct
+// columns with keys in bins >= b1, so the row's k-th largest column key is in
+// a bin >= b1 too: every selected column has a key in bin >= b1, and so has
+// the largest key of its kKeyBlock-column block.  One wave handles one segment on its own (no
 // barriers): per batch of 1024 blocks it loads the block keys (16 per lane, at
 // once), queues in column order the blocks whose key reaches bin b1 in an LDS
 // list, then re-scores the queue 8 blocks (one 64-key step) at a time with
