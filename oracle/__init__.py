@@ -24,8 +24,10 @@ Modules:
 * ``topk``      -- per-row top-k with the ordering contract
 * ``candidates`` -- the FULL layer's hierarchical candidate pool (8-row block maxima, top-2048)
 * ``attention`` -- single-softmax sink attention over SWA + selected rows
+* ``compressor`` -- the FULL layer's write path: pooled latent, main row, index key
+* ``quantize``  -- float32 rows to the planes' FP8 / FP4 byte formats
 
 Parity status of each function is stated in its module docstring.
 """
 
-from . import formats, geometry, rope, indexer, topk, candidates, attention  # noqa: F401
+from . import formats, geometry, rope, indexer, topk, candidates, attention, compressor, quantize  # noqa: F401
