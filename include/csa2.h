@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 4
+#define CSA2_ABI_VERSION 5
 
 /* Status codes. */
 #define CSA2_OK 0
@@ -376,6 +376,90 @@ int32_t csa2_sparse_attn_decode(const csa2_attn_args* args, void* workspace, siz
                                 csa2_stream_t stream);
 
 int32_t csa2_sparse_attn_prefill(const csa2_attn_args* args, csa2_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* The FULL layer's write path: compressor, main row and index key.
+ *
+ * For the token rows of one call (rows of one sequence consecutive, at
+ * consecutive positions), with D = 512 latent channels and a 128-wide key:
+ *   kv[r] = wkv . x[r]; at ratio 2 also score[r] = wgate . x[r]  (FP32)
+ *   group j covers positions [j*ratio, j*ratio + ratio - 1] (no overlap);
+ *   latent_j = RMSNorm(pooled) * norm_w, where pooled is, per channel, the
+ *              softmax over the group's positions of score weighting kv
+ *              (ratio 1: kv itself);
+ *   main row j  = latent_j with its last 64 dims rotated at position j*ratio
+ *                 (adjacent pairs, angles pos * rope_inv_freq[i]);
+ *   index key j = RMSNorm(wk . latent_j) * knorm_w, with its last 64 dims
+ *                 rotated the same way.
+ * Row j of both planes is written at plane row row_base[r] + j by the token
+ * row r that completes group j.  ("万字长文解析DeekSeekV4.1flash" appendix
+ * A.15.1 and §6.2; "DeepSeek-V4.1-Flash 架构解剖", special module
+ * "compressor": FP32 pooling, non-overlapping groups, rotation before the
+ * write, the indexer's wk reads the latent before rotation; special module
+ * "indexer", key side: wk -> k_norm -> rotation -> the index plane;
+ * "DeepSeek-V4.1-Flash 结构说明" §4: the rotation position of a compressed
+ * entry is its group's first token.)  k_norm is an RMSNorm with a learned
+ * weight.
+ *
+ * Ratio 2 tail state: a token at an even position whose group partner is not
+ * the next row of the call leaves its kv and score in tail_kv / tail_score
+ * [slot[r]]; a token at an odd position whose partner is not the previous row
+ * of the call pools with the tail state of its slot, which must hold position
+ * pos - 1 (the caller's contract).  Tail state read and written in one call
+ * is consistent (reads see the state the call started with).
+ *
+ * Storage of the written rows (plane row n):
+ *   main_dtype  F32 / BF16 [n, 512]; FP4_E2M1 packed [n, 256] + E8M0
+ *               main_scale_out [n, 16] (one scale per 32: 2^ceil(log2(amax/6)));
+ *               FP4_E2M1_E4M3G16 [n, 288] inline (E4M3 scale per 16 =
+ *               E4M3(amax/6) clamped to [2^-9, 448]).
+ *   idx_dtype   F32 / BF16 [n, 128]; FP8_E4M3 [n, 128] + float32 idx_scale_out
+ *               [n] (amax/448, 1 for a zero row); FP4_E2M1 packed [n, 64] +
+ *               E8M0 idx_scale_out [n, 4].
+ * E4M3 and E2M1 round to nearest even and saturate (448, 6); the scaled
+ * values are formed in float32 with IEEE division.
+ *
+ * Supported: dim 512, idx_dim 128, rope_dim 64, ratio 1 or 2, d_in a positive
+ * multiple of 64.  x and the weights are bf16; x, wkv, wgate and wk 16-byte
+ * aligned.  wgate, tail_kv and tail_score are required at ratio 2 and NULL at
+ * ratio 1.  workspace: csa2_compress_workspace_size bytes, 256-byte aligned.
+ * All pointers are device memory owned by the caller.
+ */
+typedef struct csa2_compress_args {
+    uint32_t struct_size;       /* sizeof(csa2_compress_args) */
+    int32_t rows;               /* token rows R, >= 0 */
+    int32_t d_in;               /* hidden width of x and the projections' inputs */
+    int32_t ratio;              /* 1 or 2 */
+    int32_t dim;                /* latent width, 512 */
+    int32_t idx_dim;            /* index key width, 128 */
+    int32_t rope_dim;           /* rotated tail, 64 */
+    int32_t main_dtype;         /* see above */
+    int32_t idx_dtype;          /* see above */
+    int32_t _pad0;
+    const void* x;              /* [R, d_in] bf16 hidden rows */
+    const int64_t* pos;         /* [R] absolute positions, >= 0 */
+    const int32_t* slot;        /* [R] tail-state slot of the row's sequence, >= 0 */
+    const int64_t* row_base;    /* [R] first plane row of the row's sequence */
+    const void* wkv;            /* [dim, d_in] bf16 */
+    const void* wgate;          /* ratio 2: [dim, d_in] bf16; else NULL */
+    const float* norm_w;        /* [dim] */
+    const void* wk;             /* [idx_dim, dim] bf16 */
+    const float* knorm_w;       /* [idx_dim] */
+    const double* rope_inv_freq;/* [rope_dim / 2] (see csa2_rope_inv_freq) */
+    float eps;                  /* RMSNorm epsilon of the latent, >= 0 */
+    float k_eps;                /* RMSNorm epsilon of the key, >= 0 */
+    float* tail_kv;             /* ratio 2: [slots, dim] in/out; else NULL */
+    float* tail_score;          /* ratio 2: [slots, dim] in/out; else NULL */
+    void* main_out;             /* main plane */
+    void* main_scale_out;       /* FP4_E2M1: E8M0 [*, dim / 32]; else NULL */
+    void* idx_out;              /* index plane */
+    void* idx_scale_out;        /* FP8: float32 [*]; FP4_E2M1: E8M0 [*, idx_dim / 32]; else NULL */
+} csa2_compress_args;
+
+size_t csa2_compress_workspace_size(int32_t rows, int32_t d_in, int32_t ratio);
+
+int32_t csa2_compress(const csa2_compress_args* args, void* workspace, size_t workspace_bytes,
+                      csa2_stream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Host helper: RoPE frequencies in float64, written to HOST memory.

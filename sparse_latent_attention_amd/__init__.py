@@ -74,6 +74,16 @@ class AttnArgs(ctypes.Structure):
     ]
 
 
+class CompressArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", _u32), ("rows", _i32), ("d_in", _i32), ("ratio", _i32), ("dim", _i32), ("idx_dim", _i32),
+        ("rope_dim", _i32), ("main_dtype", _i32), ("idx_dtype", _i32), ("_pad0", _i32), ("x", _vp), ("pos", _vp),
+        ("slot", _vp), ("row_base", _vp), ("wkv", _vp), ("wgate", _vp), ("norm_w", _vp), ("wk", _vp),
+        ("knorm_w", _vp), ("rope_inv_freq", _vp), ("eps", _f32), ("k_eps", _f32), ("tail_kv", _vp),
+        ("tail_score", _vp), ("main_out", _vp), ("main_scale_out", _vp), ("idx_out", _vp), ("idx_scale_out", _vp),
+    ]
+
+
 _lib.csa2_abi_version.restype = _i32
 _lib.csa2_status_string.restype = ctypes.c_char_p
 _lib.csa2_status_string.argtypes = [_i32]
@@ -97,6 +107,10 @@ _lib.csa2_sparse_attn_decode.restype = _i32
 _lib.csa2_sparse_attn_decode.argtypes = [ctypes.POINTER(AttnArgs), _vp, ctypes.c_size_t, _vp]
 _lib.csa2_sparse_attn_prefill.restype = _i32
 _lib.csa2_sparse_attn_prefill.argtypes = [ctypes.POINTER(AttnArgs), _vp]
+_lib.csa2_compress_workspace_size.restype = ctypes.c_size_t
+_lib.csa2_compress_workspace_size.argtypes = [_i32, _i32, _i32]
+_lib.csa2_compress.restype = _i32
+_lib.csa2_compress.argtypes = [ctypes.POINTER(CompressArgs), _vp, ctypes.c_size_t, _vp]
 _lib.csa2_rope_inv_freq.restype = _i32
 _lib.csa2_rope_inv_freq.argtypes = [_i32, ctypes.c_double, ctypes.c_double, _i64, ctypes.POINTER(ctypes.c_double)]
 
@@ -104,7 +118,7 @@ ABI_VERSION = _lib.csa2_abi_version()
 EXPORTED = ("csa2_abi_version", "csa2_status_string", "csa2_indexer_score", "csa2_topk_workspace_size",
             "csa2_topk_select", "csa2_topk_rescore_workspace_size", "csa2_topk_rescore",
             "csa2_candidate_pool_workspace_size", "csa2_candidate_pool", "csa2_attn_workspace_size", "csa2_sparse_attn_decode", "csa2_sparse_attn_prefill",
-            "csa2_rope_inv_freq")
+            "csa2_compress_workspace_size", "csa2_compress", "csa2_rope_inv_freq")
 
 
 class Csa2Error(RuntimeError):
@@ -455,6 +469,69 @@ def sparse_attn_prefill(q, pos, idx, kv, swa, swa_pos0, sink, inv_freq, ratio, w
     return out
 
 
+# Plane formats of csa2_compress, by name: main rows and index keys.
+_MAIN_FORMATS = {"f32": F32, "bf16": BF16, "fp4": FP4_E2M1, "nvfp4": FP4_E2M1_E4M3G16}
+_IDX_FORMATS = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp4": FP4_E2M1}
+
+
+def compress_workspace_size(rows, d_in, ratio):
+    return int(_lib.csa2_compress_workspace_size(int(rows), int(d_in), int(ratio)))
+
+
+def compress(x, pos, slot, row_base, wkv, norm_w, wk, knorm_w, inv_freq, main_out, idx_out, *, ratio, wgate=None,
+             eps=1e-6, k_eps=1e-6, tail_kv=None, tail_score=None, main_format="bf16", idx_format="fp8",
+             main_scale=None, idx_scale=None, workspace=None, stream=None):
+    """The FULL layer's write path (csa2_compress): pools the token rows x [R, d_in] (bf16) into latent
+    rows, writes the rotated main rows into ``main_out`` and the index keys into ``idx_out`` at plane row
+    row_base[r] + pos[r] // ratio for each row r that completes a group.
+
+    Weights: wkv / wgate [512, d_in] bf16, wk [128, 512] bf16, norm_w [512] and knorm_w [128] float32;
+    inv_freq: the float64 rope table on the device.  Ratio 2 needs wgate and the tail state
+    tail_kv / tail_score [slots, 512] float32 (rows of sequence s use slot[r] = s).
+    main_format: "f32" | "bf16" | "fp4" (with main_scale, E8M0 [*, 16]) | "nvfp4" (288-byte rows);
+    idx_format: "f32" | "bf16" | "fp8" (with idx_scale, float32 [*]) | "fp4" (with idx_scale, E8M0 [*, 4]).
+    """
+    _dev(x, pos, slot, row_base, wkv, wgate, norm_w, wk, knorm_w, inv_freq, main_out, idx_out, tail_kv, tail_score,
+         main_scale, idx_scale, workspace)
+    _need(x, torch.bfloat16, "x")
+    _need(wkv, torch.bfloat16, "wkv")
+    _need(wk, torch.bfloat16, "wk")
+    _need(norm_w, torch.float32, "norm_w")
+    _need(knorm_w, torch.float32, "knorm_w")
+    _need(inv_freq, torch.float64, "rope_inv_freq")
+    _need(pos, torch.int64, "pos")
+    _need(slot, torch.int32, "slot")
+    _need(row_base, torch.int64, "row_base")
+    if wgate is not None:
+        _need(wgate, torch.bfloat16, "wgate")
+    for t, n in ((tail_kv, "tail_kv"), (tail_score, "tail_score")):
+        if t is not None:
+            _need(t, torch.float32, n)
+            if t.dim() != 2 or t.shape[1] != 512:
+                raise ValueError(f"csa2.compress: {n} must be [slots, 512]")
+    rows, d_in = x.shape
+    if pos.shape != (rows,) or slot.shape != (rows,) or row_base.shape != (rows,) or wkv.shape != (512, d_in) \
+            or (wgate is not None and wgate.shape != (512, d_in)) or wk.shape != (128, 512):
+        raise ValueError("csa2.compress: inconsistent shapes")
+    if main_format not in _MAIN_FORMATS or idx_format not in _IDX_FORMATS:
+        raise ValueError("csa2.compress: unknown plane format")
+    a = CompressArgs()
+    a.struct_size = ctypes.sizeof(CompressArgs)
+    a.rows, a.d_in, a.ratio, a.dim, a.idx_dim, a.rope_dim = rows, d_in, int(ratio), 512, 128, 64
+    a.main_dtype, a.idx_dtype = _MAIN_FORMATS[main_format], _IDX_FORMATS[idx_format]
+    a.x, a.pos, a.slot, a.row_base = _ptr(x), _ptr(pos), _ptr(slot), _ptr(row_base)
+    a.wkv, a.wgate, a.norm_w, a.wk, a.knorm_w = _ptr(wkv), _ptr(wgate), _ptr(norm_w), _ptr(wk), _ptr(knorm_w)
+    a.rope_inv_freq, a.eps, a.k_eps = _ptr(inv_freq), float(eps), float(k_eps)
+    a.tail_kv, a.tail_score = _ptr(tail_kv), _ptr(tail_score)
+    a.main_out, a.main_scale_out, a.idx_out, a.idx_scale_out = _ptr(main_out), _ptr(main_scale), _ptr(idx_out), \
+        _ptr(idx_scale)
+    need = compress_workspace_size(rows, d_in, ratio)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("csa2_compress", _lib.csa2_compress(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 class Prepared:
     """A C ABI call with its arguments marshalled once: ``call()`` only crosses into the library.
 
@@ -514,6 +591,15 @@ def prepare_candidate_pool(*args, stream=None, **kw):
         need = candidate_pool_workspace_size(cand.shape[0], width, kw.get("block_rows", 8), cand.shape[1])
         kw["workspace"] = torch.empty(max(need, 1), dtype=torch.uint8, device=pos.device)
     p = _prepare("csa2_candidate_pool", lambda: candidate_pool(*args, stream=stream, **kw), stream)
+    p.workspace = kw["workspace"]
+    return p
+
+
+def prepare_compress(x, *args, stream=None, **kw):
+    if kw.get("workspace") is None:
+        need = compress_workspace_size(x.shape[0], x.shape[1], kw["ratio"])
+        kw["workspace"] = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    p = _prepare("csa2_compress", lambda: compress(x, *args, stream=stream, **kw), stream)
     p.workspace = kw["workspace"]
     return p
 

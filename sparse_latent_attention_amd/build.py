@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa2.so")
 
-SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "pool.hip", "attention.hip"]
+SOURCES = ["api.cpp", "indexer.hip", "topk.hip", "pool.hip", "attention.hip", "compress.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

@@ -194,6 +194,59 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
     return hip_status(e);
 }
 
+// Split of the projections' K range: enough workgroups to stream the weights
+// when rows are few, with d_in / ksplit a multiple of 64.
+static int compress_ksplit(int32_t rows, int32_t d_in, int32_t ratio) {
+    const int64_t tiles = (int64_t)((rows + 63) / 64) * (ratio == 2 ? 16 : 8);
+    int ks = 1;
+    while (tiles * ks < 1024 && ks < 16 && (d_in / 64) % (2 * ks) == 0) ks *= 2;
+    return ks;
+}
+
+size_t csa2_compress_workspace_size(int32_t rows, int32_t d_in, int32_t ratio) {
+    if (rows <= 0 || d_in <= 0 || d_in % 64 != 0 || (ratio != 1 && ratio != 2)) return 0;
+    return align256((size_t)compress_ksplit(rows, d_in, ratio) * rows * (ratio == 2 ? 1024 : 512) * 4);
+}
+
+int32_t csa2_compress(const csa2_compress_args* a, void* workspace, size_t workspace_bytes, csa2_stream_t stream) {
+    if (a == nullptr || a->struct_size < sizeof(csa2_compress_args)) return CSA2_ERR_INVALID_ARG;
+    if (a->rows < 0 || a->rows > (1 << 24) || a->d_in <= 0 || (a->ratio != 1 && a->ratio != 2))
+        return CSA2_ERR_INVALID_ARG;
+    if (a->dim != 512 || a->idx_dim != 128 || a->rope_dim != 64 || a->d_in % 64 != 0) return CSA2_ERR_UNSUPPORTED;
+    if (!csa2::compress_supported(a->main_dtype, a->idx_dtype)) return CSA2_ERR_UNSUPPORTED;
+    if (!(a->eps >= 0.f) || !(a->k_eps >= 0.f) || !isfinite(a->eps) || !isfinite(a->k_eps)) return CSA2_ERR_INVALID_ARG;
+    const bool r2 = a->ratio == 2;
+    if ((a->wgate != nullptr) != r2 || (a->tail_kv != nullptr) != r2 || (a->tail_score != nullptr) != r2)
+        return CSA2_ERR_INVALID_ARG;
+    const bool main_scale = a->main_dtype == CSA2_FP4_E2M1;
+    const bool idx_scale = a->idx_dtype == CSA2_FP8_E4M3 || a->idx_dtype == CSA2_FP4_E2M1;
+    if ((a->main_scale_out != nullptr) != main_scale || (a->idx_scale_out != nullptr) != idx_scale)
+        return CSA2_ERR_INVALID_ARG;
+    if (a->rows == 0) return CSA2_OK;
+    const size_t need = csa2_compress_workspace_size(a->rows, a->d_in, a->ratio);
+    if (workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+    if (workspace == nullptr || !aligned(workspace, 256)) return CSA2_ERR_INVALID_ARG;
+    if (a->x == nullptr || a->pos == nullptr || a->slot == nullptr || a->row_base == nullptr || a->wkv == nullptr ||
+        a->norm_w == nullptr || a->wk == nullptr || a->knorm_w == nullptr || a->rope_inv_freq == nullptr ||
+        a->main_out == nullptr || a->idx_out == nullptr)
+        return CSA2_ERR_INVALID_ARG;
+    if (!aligned(a->x, 16) || !aligned(a->wkv, 16) || !aligned(a->wgate, 16) || !aligned(a->wk, 16) ||
+        !aligned(a->main_out, 8) || !aligned(a->idx_out, 8) || !aligned(a->idx_scale_out, 4) ||
+        !aligned(a->tail_kv, 8) || !aligned(a->tail_score, 8))
+        return CSA2_ERR_INVALID_ARG;
+    csa2::CompressParams p;
+    p.x = static_cast<const uint16_t*>(a->x); p.pos = a->pos; p.slot = a->slot; p.row_base = a->row_base;
+    p.wkv = static_cast<const uint16_t*>(a->wkv); p.wgate = static_cast<const uint16_t*>(a->wgate);
+    p.norm_w = a->norm_w; p.wk = static_cast<const uint16_t*>(a->wk); p.knorm_w = a->knorm_w;
+    p.inv_freq = a->rope_inv_freq; p.tail_kv = a->tail_kv; p.tail_score = a->tail_score;
+    p.main_out = a->main_out; p.main_scale_out = a->main_scale_out; p.idx_out = a->idx_out;
+    p.idx_scale_out = a->idx_scale_out; p.partial = static_cast<float*>(workspace);
+    p.eps = a->eps; p.k_eps = a->k_eps; p.rows = a->rows; p.d_in = a->d_in; p.nproj = r2 ? 1024 : 512;
+    p.ksplit = compress_ksplit(a->rows, a->d_in, a->ratio);
+    return hip_status(csa2::launch_compress(p, a->ratio, a->main_dtype, a->idx_dtype,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t csa2_topk_workspace_size(int32_t rows, int64_t width, int32_t k) {
     (void)k;
     if (rows <= 0 || width <= 0 || width >= (1LL << 31)) return 0;

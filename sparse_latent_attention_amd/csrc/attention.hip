@@ -205,13 +205,6 @@ __device__ __forceinline__ void store_out4<CSA2_F32>(void* out, int64_t off, flo
     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off) = f32x4{a, b, c, d};
 }
 
-// cos/sin of pos * inv_freq[i] in float64, returned as float.
-__device__ __forceinline__ void rope_angle(int64_t pos, double f, float& c, float& s) {
-    double sd, cd;
-    sincos((double)pos * f, &sd, &cd);
-    c = (float)cd;
-    s = (float)sd;
-}
 
 
 // Raw bytes of one pair (4 rows x 8 elements) of a tile, as loaded from HBM.

@@ -48,6 +48,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
+// cos/sin of pos * inv_freq in float64 (an fp32 angle at positions near 10^6
+// would be off by up to ~0.06 rad), returned as float.
+__device__ __forceinline__ void rope_angle(int64_t pos, double f, float& c, float& s) {
+    double sd, cd;
+    sincos((double)pos * f, &sd, &cd);
+    c = (float)cd;
+    s = (float)sd;
+}
+
 // Value of an E8M0 scale byte: 2^(e-127), e = 255 is NaN.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
     if (e == 255u) return __builtin_nanf("");

@@ -105,4 +105,30 @@ struct AttnShape {
 bool attn_supported(const AttnShape& s);
 hipError_t launch_sparse_attn(const AttnParams& p, const AttnShape& s, bool decode, hipStream_t stream);
 
+// The FULL layer's write path (compress.hip).
+struct CompressParams {
+    const uint16_t* x;       // [rows, d_in] bf16
+    const int64_t* pos;      // [rows]
+    const int32_t* slot;     // [rows] tail-state slot
+    const int64_t* row_base; // [rows]
+    const uint16_t* wkv;     // [512, d_in] bf16
+    const uint16_t* wgate;   // [512, d_in] bf16 (ratio 2)
+    const float* norm_w;     // [512]
+    const uint16_t* wk;      // [128, 512] bf16
+    const float* knorm_w;    // [128]
+    const double* inv_freq;  // [32]
+    float* tail_kv;          // [slots, 512] (ratio 2)
+    float* tail_score;       // [slots, 512] (ratio 2)
+    void* main_out;
+    void* main_scale_out;
+    void* idx_out;
+    void* idx_scale_out;
+    float* partial;          // workspace [ksplit, rows, nproj]
+    float eps, k_eps;
+    int rows, d_in, nproj, ksplit;
+};
+
+bool compress_supported(int main_dtype, int idx_dtype);
+hipError_t launch_compress(const CompressParams& p, int ratio, int main_dtype, int idx_dtype, hipStream_t stream);
+
 }  // namespace csa2

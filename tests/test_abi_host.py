@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(csa2.EXPORTED)
-    assert csa2.ABI_VERSION == 4
+    assert csa2.ABI_VERSION == 5
 
 
 def test_struct_layouts_match_c_compiler():
@@ -43,6 +43,8 @@ int main(void) {
   printf("csa2_topk_args sizeof %zu\n", sizeof(csa2_topk_args));
   printf("csa2_attn_args sizeof %zu\n", sizeof(csa2_attn_args));
   printf("csa2_pool_args sizeof %zu\n", sizeof(csa2_pool_args));
+  printf("csa2_compress_args sizeof %zu\n", sizeof(csa2_compress_args));
+  F(csa2_compress_args, x) F(csa2_compress_args, rope_inv_freq) F(csa2_compress_args, eps) F(csa2_compress_args, k_eps) F(csa2_compress_args, tail_kv) F(csa2_compress_args, idx_scale_out)
   F(csa2_index_args, width) F(csa2_index_args, q) F(csa2_index_args, cand) F(csa2_index_args, scale) F(csa2_index_args, scores) F(csa2_index_args, key_hist) F(csa2_index_args, block_max) F(csa2_index_args, block_keys) F(csa2_index_args, q_scale_e8m0) F(csa2_index_args, k_scale_e8m0)
   F(csa2_pool_args, n_cand) F(csa2_pool_args, width) F(csa2_pool_args, scores) F(csa2_pool_args, block_max) F(csa2_pool_args, pos) F(csa2_pool_args, cand) F(csa2_pool_args, block_keys)
   F(csa2_topk_args, width) F(csa2_topk_args, scores) F(csa2_topk_args, out) F(csa2_topk_args, key_hist)
@@ -57,7 +59,7 @@ int main(void) {
         subprocess.run(["gcc", "-I", os.path.dirname(HEADER), src, "-o", exe], check=True)
         out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
     cls = {"csa2_index_args": csa2.IndexArgs, "csa2_topk_args": csa2.TopkArgs, "csa2_attn_args": csa2.AttnArgs,
-           "csa2_pool_args": csa2.PoolArgs}
+           "csa2_pool_args": csa2.PoolArgs, "csa2_compress_args": csa2.CompressArgs}
     for line in out.strip().splitlines():
         t, f, v = line.split()
         if f == "sizeof":
@@ -318,3 +320,48 @@ def test_rope_table_rejects_bad_args():
     assert csa2._lib.csa2_rope_inv_freq(15, 1e4, 1.0, 0, out) == csa2.ERR_INVALID_ARG
     assert csa2._lib.csa2_rope_inv_freq(16, 0.5, 1.0, 0, out) == csa2.ERR_INVALID_ARG
     assert csa2._lib.csa2_rope_inv_freq(16, 1e4, 1.0, 0, None) == csa2.ERR_INVALID_ARG
+
+
+def _compress_args(**kw):
+    a = csa2.CompressArgs()
+    a.struct_size = ctypes.sizeof(csa2.CompressArgs)
+    a.rows, a.d_in, a.ratio, a.dim, a.idx_dim, a.rope_dim = 4, 5120, 2, 512, 128, 64
+    a.main_dtype, a.idx_dtype = csa2.FP4_E2M1, csa2.FP8_E4M3
+    for f in ("x", "pos", "slot", "row_base", "wkv", "wgate", "norm_w", "wk", "knorm_w", "rope_inv_freq", "tail_kv",
+              "tail_score", "main_out", "main_scale_out", "idx_out", "idx_scale_out"):
+        setattr(a, f, ctypes.c_void_p(0x1000))
+    a.eps = a.k_eps = 1e-6
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(struct_size=8), csa2.ERR_INVALID_ARG), (dict(ratio=3), csa2.ERR_INVALID_ARG),
+    (dict(rows=-1), csa2.ERR_INVALID_ARG), (dict(dim=256), csa2.ERR_UNSUPPORTED),
+    (dict(idx_dim=64), csa2.ERR_UNSUPPORTED), (dict(d_in=100), csa2.ERR_UNSUPPORTED),
+    (dict(main_dtype=csa2.FP8_E4M3), csa2.ERR_UNSUPPORTED), (dict(idx_dtype=csa2.FP4_E2M1_E4M3G16), csa2.ERR_UNSUPPORTED),
+    (dict(wgate=None), csa2.ERR_INVALID_ARG), (dict(tail_kv=None), csa2.ERR_INVALID_ARG),
+    (dict(ratio=1), csa2.ERR_INVALID_ARG),                       # ratio 1 takes no gate and no tail state
+    (dict(main_scale_out=None), csa2.ERR_INVALID_ARG), (dict(idx_scale_out=None), csa2.ERR_INVALID_ARG),
+    (dict(main_dtype=csa2.BF16), csa2.ERR_INVALID_ARG),          # bf16 rows take no scale array
+    (dict(eps=float("nan")), csa2.ERR_INVALID_ARG), (dict(k_eps=-1.0), csa2.ERR_INVALID_ARG),
+    (dict(x=ctypes.c_void_p(0x1008)), csa2.ERR_INVALID_ARG), (dict(x=None), csa2.ERR_INVALID_ARG),
+])
+def test_compress_validation(kw, status):
+    a = _compress_args(**kw)
+    ws = max(csa2.compress_workspace_size(4, 5120, 2), 256)
+    assert csa2._lib.csa2_compress(ctypes.byref(a), ctypes.c_void_p(0x10000), ws, None) == status
+
+
+def test_compress_workspace_rules():
+    # decode shapes split the 5120-wide reduction; the workspace holds every partial tile
+    assert csa2.compress_workspace_size(64, 5120, 2) == 16 * 64 * 1024 * 4
+    assert csa2.compress_workspace_size(4096, 5120, 2) == 4096 * 1024 * 4
+    assert csa2.compress_workspace_size(64, 5120, 1) == 16 * 64 * 512 * 4
+    assert csa2.compress_workspace_size(0, 5120, 2) == 0 and csa2.compress_workspace_size(4, 100, 2) == 0
+    a = _compress_args()
+    need = csa2.compress_workspace_size(4, 5120, 2)
+    assert csa2._lib.csa2_compress(ctypes.byref(a), ctypes.c_void_p(0x10000), need - 1, None) == csa2.ERR_WORKSPACE
+    a = _compress_args(rows=0)
+    assert csa2._lib.csa2_compress(ctypes.byref(a), None, 0, None) == csa2.OK

@@ -1,0 +1,203 @@
+"""GPU parity of the FULL layer's write path (csa2_compress) against the oracle.
+
+* Float32 planes: every written main row and index key against
+  oracle.compressor (float64 from the same bf16 inputs), the tail state the
+  call leaves, and plane rows no group completes left untouched.  Decode
+  shapes (one token per sequence, odd and even positions, tail state in and
+  out) and prefill chunks (several sequences per call, groups straddling the
+  call's start and end), at ratio 2 and ratio 1.
+* Quantised planes: the bytes equal oracle.quantize applied to the GPU's own
+  float32 rows of the same call (both sides decide every code from the same
+  float32 values), for every main and index format.
+* Full size (d_in 5120) in the launch configuration of the workload, on
+  sampled rows.
+
+Tolerance for float32 rows: |gpu - oracle| <= 1e-5 * (1 + |oracle|).  The
+inputs are bf16 (exact in both) and products are exact in float32; a float32
+sum of n unit-scale terms carries an error of about sqrt(n) * 2^-24 relative
+to the sum of their magnitudes, i.e. ~1e-6 of a unit-scale result for the
+5120-term projections and the 512-term key projection, and the softmax, the
+two RMSNorms and the rotation add a few ulps.  Measured: <= 2.3e-6 (printed).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import formats, quantize
+from workloads.gen import make_compress_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+ROPE = (64, 160000.0, 16.0, 65536)
+
+
+def _freqs():
+    import sparse_latent_attention_amd as csa2
+    return csa2.rope_inv_freq(*ROPE).cuda()
+
+
+def _f64(t):
+    return None if t is None else t.detach().cpu().double().numpy()
+
+
+_MAIN_SHAPES = {"f32": (512, torch.float32), "bf16": (512, torch.bfloat16), "fp4": (256, torch.uint8),
+                "nvfp4": (288, torch.uint8)}
+_IDX_SHAPES = {"f32": (128, torch.float32), "bf16": (128, torch.bfloat16), "fp8": (128, torch.uint8),
+               "fp4": (64, torch.uint8)}
+
+
+def _planes(n, main_format, idx_format):
+    mw, mdt = _MAIN_SHAPES[main_format]
+    iw, idt = _IDX_SHAPES[idx_format]
+    main = torch.full((n, mw), 0, dtype=mdt, device="cuda")
+    idx = torch.full((n, iw), 0, dtype=idt, device="cuda")
+    if mdt == torch.uint8:
+        main.fill_(0xA5)
+    else:
+        main.fill_(float("nan"))
+    if idt == torch.uint8:
+        idx.fill_(0xA5)
+    else:
+        idx.fill_(float("nan"))
+    ms = torch.full((n, 16), 0xA5, dtype=torch.uint8, device="cuda") if main_format == "fp4" else None
+    isc = {"fp8": torch.full((n,), float("nan"), dtype=torch.float32, device="cuda"),
+           "fp4": torch.full((n, 4), 0xA5, dtype=torch.uint8, device="cuda")}.get(idx_format)
+    return main, ms, idx, isc
+
+
+def _gpu(x, ratio, main_format="f32", idx_format="f32", n_plane=None):
+    import sparse_latent_attention_amd as csa2
+    n_plane = n_plane or int(x["row_base"].max()) + x["plane_rows"]
+    main, ms, idx, isc = _planes(n_plane, main_format, idx_format)
+    tk = None if x["tail_kv"] is None else x["tail_kv"].clone()
+    ts = None if x["tail_score"] is None else x["tail_score"].clone()
+    csa2.compress(x["x"], x["pos"], x["slot"], x["row_base"], x["wkv"], x["norm_w"], x["wk"], x["knorm_w"],
+                  _freqs(), main, idx, ratio=ratio, wgate=x["wgate"], tail_kv=tk, tail_score=ts,
+                  main_format=main_format, idx_format=idx_format, main_scale=ms, idx_scale=isc)
+    torch.cuda.synchronize()
+    return dict(main=main, main_scale=ms, idx=idx, idx_scale=isc, tail_kv=tk, tail_score=ts)
+
+
+def _oracle(x, ratio, rows=None):
+    """Oracle rows; ``rows`` restricts the call to those row indices (kept in order)."""
+    sel = slice(None) if rows is None else torch.as_tensor(rows, device=x["x"].device)
+    freqs = oracle.rope.inv_freq(*ROPE)
+    return oracle.compressor.compress_call(
+        _f64(x["x"][sel]), x["pos"][sel].cpu().numpy(), x["slot"][sel].cpu().numpy(), ratio, _f64(x["wkv"]),
+        _f64(x["wgate"]), _f64(x["norm_w"]), 1e-6, _f64(x["wk"]), _f64(x["knorm_w"]), 1e-6, freqs,
+        _f64(x["tail_kv"]), _f64(x["tail_score"]))
+
+
+def _err(got, want):
+    return float(np.max(np.abs(got - want) / (1.0 + np.abs(want))))
+
+
+CASES = {
+    "decode_r2": dict(rows=37, d_in=512, ratio=2, seqs=None, pos0=0, span=120, plane_rows=64),
+    "decode_r1": dict(rows=37, d_in=512, ratio=1, seqs=None, pos0=3, span=60, plane_rows=64),
+    # starts at an odd position (pools with the tail state), ends at an even one (leaves a tail)
+    "prefill_r2": dict(rows=301, d_in=256, ratio=2, seqs=3, pos0=1001, span=0, plane_rows=640),
+    "prefill_r1": dict(rows=150, d_in=320, ratio=1, seqs=2, pos0=0, span=0, plane_rows=128),
+    "single_r2": dict(rows=1, d_in=64, ratio=2, seqs=None, pos0=0, span=1, plane_rows=8),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_float32_rows_match_oracle(name):
+    c = CASES[name]
+    print(f"\n[compress f32] {name} {c}", flush=True)
+    x = make_compress_inputs(c["rows"], c["d_in"], c["ratio"], 7, device="cuda", seqs=c["seqs"], pos0=c["pos0"],
+                             span=max(c["span"], 1), plane_rows=c["plane_rows"])
+    if name == "single_r2":
+        x["pos"][0] = 11                      # odd: pools with the tail state
+    out = _gpu(x, c["ratio"])
+    rows, tk, ts = _oracle(x, c["ratio"])
+    main = out["main"].cpu().numpy().astype(np.float64)
+    idx = out["idx"].cpu().numpy().astype(np.float64)
+    base = x["row_base"].cpu().numpy()
+    written = set()
+    e_main = e_idx = 0.0
+    for r, (j, m, k, _) in rows.items():
+        n = int(base[r] + j)
+        written.add(n)
+        e_main = max(e_main, _err(main[n], m))
+        e_idx = max(e_idx, _err(idx[n], k))
+    print(f"[compress f32] {name}: {len(rows)} rows, max err main {e_main:.2e} index {e_idx:.2e}")
+    assert e_main <= TOL and e_idx <= TOL
+    others = np.array(sorted(set(range(main.shape[0])) - written))
+    assert np.all(np.isnan(main[others])) and np.all(np.isnan(idx[others])), "rows no group completes stay"
+    if c["ratio"] == 2:
+        tk0, ts0 = _f64(x["tail_kv"]), _f64(x["tail_score"])
+        gk, gs = _f64(out["tail_kv"]), _f64(out["tail_score"])
+        for s in range(tk0.shape[0]):
+            if np.array_equal(tk[s], tk0[s]):
+                assert np.array_equal(gk[s], tk0[s]) and np.array_equal(gs[s], ts0[s]), f"slot {s} untouched"
+            else:
+                assert _err(gk[s], tk[s]) <= TOL and _err(gs[s], ts[s]) <= TOL, f"slot {s} tail"
+
+
+@pytest.mark.parametrize("main_format,idx_format", [("bf16", "fp8"), ("fp4", "fp8"), ("nvfp4", "fp4"),
+                                                    ("fp4", "bf16")])
+@pytest.mark.parametrize("ratio", [1, 2])
+def test_quantised_planes_encode_the_gpu_float32_rows(main_format, idx_format, ratio):
+    print(f"\n[compress quant] ratio {ratio} main {main_format} idx {idx_format}", flush=True)
+    x = make_compress_inputs(96, 256, ratio, 11, device="cuda", seqs=3, pos0=77, plane_rows=256)
+    ref = _gpu(x, ratio)
+    got = _gpu(x, ratio, main_format, idx_format)
+    rows, _, _ = _oracle(x, ratio)
+    base = x["row_base"].cpu().numpy()
+    n = np.array(sorted(int(base[r] + j) for r, (j, *_rest) in rows.items()))
+    fm = ref["main"][n].cpu().numpy()
+    fi = ref["idx"][n].cpu().numpy()
+    gm = got["main"][n].cpu()
+    gi = got["idx"][n].cpu()
+    if main_format == "bf16":
+        assert torch.equal(gm, torch.from_numpy(fm).to(torch.bfloat16))
+    elif main_format == "fp4":
+        p, e = quantize.fp4_e8m0_rows(fm)
+        assert np.array_equal(gm.numpy(), p) and np.array_equal(got["main_scale"][n].cpu().numpy(), e)
+    else:
+        assert np.array_equal(gm.numpy(), quantize.nvfp4_rows(fm))
+    if idx_format == "fp8":
+        c, s = quantize.fp8_rows(fi)
+        assert np.array_equal(gi.numpy(), c) and np.array_equal(got["idx_scale"][n].cpu().numpy(), s)
+    elif idx_format == "fp4":
+        p, e = quantize.fp4_e8m0_rows(fi)
+        assert np.array_equal(gi.numpy(), p) and np.array_equal(got["idx_scale"][n].cpu().numpy(), e)
+    else:
+        assert torch.equal(gi, torch.from_numpy(fi).to(torch.bfloat16))
+    # and the decoded planes stay within the formats' rounding of the oracle rows
+    if idx_format == "fp8":
+        dec = formats.decode_fp8_rows(gi.numpy(), got["idx_scale"][n].cpu().numpy())
+        want = np.stack([rows[r][2] for r in sorted(rows, key=lambda r: int(base[r] + rows[r][0]))])
+        amax = np.max(np.abs(want), axis=1, keepdims=True)
+        slack = TOL * (1 + np.abs(want))
+        assert np.all(np.abs(dec - want) <= np.maximum(np.abs(want) * 2 ** -4, amax / 448 * 2 ** -10) + 2 * slack)
+
+
+@pytest.mark.parametrize("ratio,rows,seqs", [(2, 64, None), (1, 64, None), (2, 4096, 1), (1, 1024, 4)])
+def test_full_size_sampled_rows(ratio, rows, seqs):
+    """d_in 5120, the model's hidden width, in the launch configuration bench.py times; the oracle checks a
+    sample of the rows (each from its own group's rows, which gives the same result as the whole call)."""
+    print(f"\n[compress full] ratio {ratio} rows {rows} seqs {seqs}", flush=True)
+    x = make_compress_inputs(rows, 5120, ratio, 13, device="cuda", seqs=seqs, pos0=126975,
+                             plane_rows=131072 + 8192)
+    out = _gpu(x, ratio, "f32", "f32")
+    pos = x["pos"].cpu().numpy()
+    slot = x["slot"].cpu().numpy()
+    base = x["row_base"].cpu().numpy()
+    emit = [r for r in range(rows) if ratio == 1 or pos[r] % 2 == 1]
+    rng = np.random.default_rng(0)
+    pick = sorted(set(rng.choice(emit, size=min(48, len(emit)), replace=False).tolist()) | {emit[0], emit[-1]})
+    e_main = e_idx = 0.0
+    for r in pick:
+        sub = [r - 1, r] if (ratio == 2 and r > 0 and slot[r - 1] == slot[r] and pos[r - 1] == pos[r] - 1) else [r]
+        got_rows, _, _ = _oracle(x, ratio, sub)
+        j, m, k, _ = got_rows[len(sub) - 1]
+        n = int(base[r] + j)
+        e_main = max(e_main, _err(out["main"][n].cpu().numpy().astype(np.float64), m))
+        e_idx = max(e_idx, _err(out["idx"][n].cpu().numpy().astype(np.float64), k))
+    print(f"[compress full] {len(pick)} sampled rows: max err main {e_main:.2e} index {e_idx:.2e}")
+    assert e_main <= TOL and e_idx <= TOL

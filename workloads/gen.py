@@ -253,3 +253,41 @@ def make_inputs(cfg: Csa2Config, seed: int, device="cpu"):
     if cfg.index_mode == "reindex":
         out["cand"] = make_candidates(cfg, pos, g, device)
     return out
+
+
+def make_compress_inputs(rows, d_in, ratio, seed, device="cpu", seqs=None, pos0=0, slots=None, span=4096,
+                         plane_rows=8192):
+    """Inputs of the FULL layer's write path: bf16 hidden rows and bf16 weights, float32 norm weights and
+    tail state, positions and sequence slots.
+
+    ``seqs``: None gives one token per sequence (decode: row r is sequence r at a random position in
+    [pos0, pos0 + span)); an int n splits the rows into n consecutive chunks, sequence s covering
+    positions pos0 + 17 s ... (prefill chunks).  Weights are scaled so projections are O(1): wkv,
+    wgate ~ N(0, 1/d_in), wk ~ N(0, 1/512), norm weights 1 + N(0, 0.01).  Sequence s's plane rows
+    start at plane_rows * s (they must hold its rows pos // ratio).
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    bf = lambda shape, std: _normal(g, shape, device, std).to(torch.bfloat16)
+    out = {"x": bf((rows, d_in), 1.0), "wkv": bf((512, d_in), d_in ** -0.5), "wk": bf((128, 512), 512 ** -0.5),
+           "norm_w": 1.0 + _normal(g, (512,), device, 0.1), "knorm_w": 1.0 + _normal(g, (128,), device, 0.1)}
+    out["wgate"] = bf((512, d_in), d_in ** -0.5) if ratio == 2 else None
+    if seqs is None:
+        slot = torch.arange(rows, dtype=torch.int32, device=device)
+        pos = pos0 + torch.randint(0, span, (rows,), generator=g, device=device, dtype=torch.int64)
+    else:
+        bounds = torch.linspace(0, rows, seqs + 1).round().to(torch.int64).tolist()
+        slot = torch.empty(rows, dtype=torch.int32, device=device)
+        pos = torch.empty(rows, dtype=torch.int64, device=device)
+        for s in range(seqs):
+            a, b = bounds[s], bounds[s + 1]
+            slot[a:b] = s
+            pos[a:b] = pos0 + 17 * s + torch.arange(b - a, device=device)
+    n_slots = int(slot.max()) + 1 if slots is None else slots
+    out.update(pos=pos, slot=slot, row_base=slot.to(torch.int64) * plane_rows, plane_rows=plane_rows)
+    if ratio == 2:
+        out["tail_kv"] = _normal(g, (n_slots, 512), device, 1.0)
+        out["tail_score"] = _normal(g, (n_slots, 512), device, 1.0)
+    else:
+        out["tail_kv"] = out["tail_score"] = None
+    return out
