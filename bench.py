@@ -110,7 +110,17 @@ def algorithmic_work(cfg, x, idx_host=None, score_free=False):
     attn_dt = "f32" if cfg.q_dtype == "f32" else "bf16"
     # candidate pool: read the block scores, write the kept blocks
     pool_bytes = rows * nbm * 4 + rows * cfg.pool_blocks * 4
-    return {"indexer_score": (idx_bytes, idx_flops, cfg.idx_dtype, 1),
+    # write path (owner layers): the hidden rows and the weights once, the new rows of both planes, the
+    # tail state; flops of the projections (kv [+ gate]) and of the index-key projection of each new row
+    comp = (0, 0, None, 1)
+    if cfg.d_model:
+        nproj = 512 * cfg.ratio
+        emitted = rows if cfg.ratio == 1 else int((pos % 2 == 1).sum())
+        comp_bytes = (rows * cfg.d_model * 2 + nproj * cfg.d_model * 2 + 128 * 512 * 2 + (512 + 128) * 4
+                      + emitted * (main_row + idx_row) + rows * 8 * 2 + (rows * 512 * 8 if cfg.ratio == 2 else 0))
+        comp = (comp_bytes, 2 * rows * cfg.d_model * nproj + 2 * emitted * 512 * 128, "bf16", 1)
+    return {"compress": comp,
+            "indexer_score": (idx_bytes, idx_flops, cfg.idx_dtype, 1),
             "topk_select": (topk_bytes, 0, None, 1),
             "candidate_pool": (pool_bytes, 0, None, 1),
             "sparse_attn": (attn_bytes, attn_flops, attn_dt, layers),
@@ -136,6 +146,7 @@ KERNEL_SOURCES = {
     "indexer_score": ["indexer.hip", "common.hpp", "kernels.hpp"],
     "topk_select": ["topk.hip", "common.hpp", "kernels.hpp"],
     "candidate_pool": ["topk.hip", "pool.hip", "common.hpp", "kernels.hpp"],
+    "compress": ["compress.hip", "common.hpp", "kernels.hpp"],
     "sparse_attn": ["attention.hip", "common.hpp", "kernels.hpp"],
 }
 
@@ -182,6 +193,8 @@ def cpu_baseline(cfg, x, budget_s=20.0):
         sub = _host_slice(cfg, x, r)
         sub_cfg = cfg.replace(batch=1, q_tokens=1)
         t0 = time.perf_counter()
+        if cfg.d_model:
+            oracle.compressor.compress_call(*sub["compress_args"])
         s = oracle_scores(sub_cfg, sub, np.array([0]))
         idx = oracle_topk(sub_cfg, sub, s, np.array([0]))
         if cfg.pool_blocks:
@@ -193,14 +206,21 @@ def cpu_baseline(cfg, x, budget_s=20.0):
         if t_total >= budget_s:
             break
     return {"value": done / t_total, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {rows} query rows of the {cfg.name} batch, whole path (indexer, top-k, "
+            "sample": f"{done} of {rows} query rows of the {cfg.name} batch, whole path ("
+                      f"{'write path of the row, ' if cfg.d_model else ''}indexer, top-k, "
                       f"{'candidate pool, ' if cfg.pool_blocks else ''}attention"
                       f"{' x %d layers' % len(x['layers']) if len(x['layers']) > 1 else ''}), float64 NumPy; "
                       f"host copy excluded; {t_total:.1f} s"}
 
 
+def oracle_rope_freqs(cfg):
+    import oracle
+    return oracle.rope.inv_freq(cfg.rope_dim, cfg.rope_theta, cfg.yarn_factor, cfg.yarn_orig)
+
+
 def _host_slice(cfg, x, r):
     """Inputs of query row r alone, on the host (decode: its sequence; prefill: the shared planes)."""
+    import numpy as np
     import torch
     out = {"cfg": cfg}
     cpu = lambda t: None if t is None else t.detach().cpu()
@@ -223,6 +243,16 @@ def _host_slice(cfg, x, r):
         out["swa_pos0"] = x["swa_pos0"]
         out["layers"] = [{"q": cpu(L["q"][r:r + 1]), "swa": cpu(L["swa"]), "swa_scale": cpu(L["swa_scale"]),
                           "sink": cpu(L["sink"])} for L in x["layers"]]
+    if cfg.d_model:
+        # the write path's work for this row's token (with its group partner at ratio 2), float64 host arrays
+        c = x["compress"]
+        f64 = lambda t: None if t is None else t.detach().cpu().double().numpy()
+        rs = [r - 1, r] if cfg.ratio == 2 and r > 0 and int(c["pos"][r]) % 2 == 1 else [r]
+        freqs = oracle_rope_freqs(cfg)
+        out["compress_args"] = (f64(c["x"][rs]), c["pos"][rs].cpu().numpy(), np.zeros(len(rs), dtype=np.int64),
+                                cfg.ratio, f64(c["wkv"]), f64(c["wgate"]), f64(c["norm_w"]), 1e-6, f64(c["wk"]),
+                                f64(c["knorm_w"]), 1e-6, freqs, None if c["tail_kv"] is None else f64(c["tail_kv"][:1]),
+                                None if c["tail_score"] is None else f64(c["tail_score"][:1]))
     out["qI"] = cpu(x["qI"][r:r + 1])
     out["qI_scale"] = cpu(None if x.get("qI_scale") is None else x["qI_scale"][r:r + 1])
     out["w"] = cpu(x["w"][r:r + 1])
@@ -313,7 +343,8 @@ def main():
                    "ratio": cfg.ratio, "heads": cfg.heads, "dim": cfg.dim, "topk": cfg.topk, "window": cfg.window,
                    "index": f"{cfg.index_mode} {cfg.idx_heads}x{cfg.idx_dim} {cfg.idx_dtype}",
                    "main_kv": cfg.main_dtype, "swa": cfg.swa_dtype, "attention_layers": len(x["layers"]),
-                   "topk_route": "score-free (topk_rescore)" if step_calls.score_free else "scores + topk_select"},
+                   "topk_route": "score-free (topk_rescore)" if step_calls.score_free else "scores + topk_select",
+                   "write_path": f"d_in {cfg.d_model}, ratio {cfg.ratio}" if cfg.d_model else None},
         "kernels_ms": {n: round(v, 4) for n, v in kern_ms.items()},
         "kernels_roofline": {n: roofline_of(work[n], kern_ms[n]) for n in names},
         "roofline": roofline,

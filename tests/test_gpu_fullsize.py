@@ -19,7 +19,7 @@ from harness import (BF16_ATOL, BF16_RTOL, F32_ATOL, F32_RTOL, SCORE_TOL, assert
 pytestmark = pytest.mark.gpu
 
 NAMES = ["tiny_full_fp32", "full_decode_64k", "prefill_4096_at_128k", "reindex_decode_1m", "lowp_full_decode_1m",
-         "lowp_pool_decode_1m", "pages_fp4_decode_1m"]
+         "lowp_pool_decode_1m", "pages_fp4_decode_1m", "lowp_owner_decode_1m", "prefill_owner_4096_at_128k"]
 
 
 def _run_path(cfg, x):
@@ -133,3 +133,59 @@ def test_candidate_pool(full):
     s_gpu = scores[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
     ref = oracle.candidates.candidate_pool(s_gpu, pos[rows], cfg.ratio, B, cfg.pool_blocks)
     assert np.array_equal(pool[rows], ref)
+
+
+def _row_error_bound(fmt, ref, scales):
+    """Largest error the plane format's rounding allows per element of the float64 rows ``ref``
+    (scales: the decoded per-element scale, for the block-scaled formats)."""
+    if fmt == "bf16":
+        return np.abs(ref) * 2.0 ** -8
+    if fmt == "fp8":   # E4M3: half a step is <= 2^-4 relative for normals, 2^-10 * scale below
+        return np.maximum(np.abs(ref) * 2.0 ** -4, scales * 2.0 ** -10)
+    return scales * 1.0    # E2M1: steps of at most 2 (between 4 and 6) times the block scale
+
+
+def test_owner_rows_written(full):
+    """The write path of an owner layer: the compressed rows it appended for sampled query rows, decoded from
+    the planes, equal the oracle's rows within the formats' rounding (plus the float32 tolerance)."""
+    cfg, x, *_ = full
+    if not cfg.d_model:
+        pytest.skip("this workload appends no rows")
+    from harness import to_numpy_f64
+    c = x["compress"]
+    rows = _sample_rows(cfg)
+    if cfg.ratio == 2:
+        rows = np.array(sorted({int(r) | 1 for r in rows if (int(r) | 1) < cfg.q_tokens}))  # rows that emit
+    f64 = lambda t: None if t is None else t.detach().cpu().double().numpy()
+    freqs = oracle.rope.inv_freq(cfg.rope_dim, cfg.rope_theta, cfg.yarn_factor, cfg.yarn_orig)
+    pos = c["pos"].cpu().numpy()
+    for r in rows:
+        sub = [r - 1, r] if cfg.ratio == 2 else [r]
+        tk = None if c["tail_kv"] is None else f64(c["tail_kv"])
+        ts = None if c["tail_score"] is None else f64(c["tail_score"])
+        got_rows, _, _ = oracle.compressor.compress_call(
+            f64(c["x"][sub]), pos[sub], np.zeros(len(sub), dtype=np.int64), cfg.ratio, f64(c["wkv"]), f64(c["wgate"]),
+            f64(c["norm_w"]), 1e-6, f64(c["wk"]), f64(c["knorm_w"]), 1e-6, freqs, tk, ts)
+        j, m_ref, k_ref, _ = got_rows[len(sub) - 1]
+        n = int(c["row_base"][r]) + j
+        main = x["main"].reshape(-1, x["main"].shape[-1])[n:n + 1]
+        ms = None if x["main_scale"] is None else x["main_scale"].reshape(-1, x["main_scale"].shape[-1])[n:n + 1]
+        kI = x["kI"].reshape(-1, x["kI"].shape[-1])[n:n + 1]
+        ks = None if x["kI_scale"] is None else (x["kI_scale"].reshape(-1)[n:n + 1] if cfg.idx_dtype == "fp8"
+                                                 else x["kI_scale"].reshape(-1, x["kI_scale"].shape[-1])[n:n + 1])
+        m_got = to_numpy_f64(main, cfg.main_dtype, ms)[0]
+        k_got = to_numpy_f64(kI, cfg.idx_dtype, ks)[0]
+        # per-element scales of the block formats, from the stored scale bytes
+        if cfg.main_dtype == "fp4":
+            m_sc = np.repeat(oracle.formats.e8m0_to_f64(ms.cpu().numpy()[0]), 32)
+        elif cfg.main_dtype == "nvfp4":
+            m_sc = np.repeat(oracle.formats.decode_fp8_values(main.cpu().numpy()[0, 256:]), 16)
+        else:
+            m_sc = None
+        k_sc = (np.full(128, float(ks.cpu()[0])) if cfg.idx_dtype == "fp8" else
+                np.repeat(oracle.formats.e8m0_to_f64(ks.cpu().numpy()[0]), 32) if cfg.idx_dtype == "fp4" else None)
+        slack_m = 1e-5 * (1 + np.abs(m_ref))
+        slack_k = 1e-5 * (1 + np.abs(k_ref))
+        assert np.all(np.abs(m_got - m_ref) <= _row_error_bound(cfg.main_dtype, m_ref, m_sc) + slack_m), f"row {r}"
+        assert np.all(np.abs(k_got - k_ref) <= _row_error_bound(cfg.idx_dtype, k_ref, k_sc) + slack_k), f"row {r}"
+    print(f"[{cfg.name}] appended rows of {len(rows)} sampled query rows within the formats' rounding")

@@ -40,6 +40,8 @@ class Csa2Config:
     value_scale: str = "unit"  # "unit": N(0,1); "inv_sqrt_d": N(0,1)/sqrt(dim) for q, latent and index vectors
     ragged: bool = False       # decode: per-sequence positions drawn in [window, context-1]
     pool_blocks: int = 0       # FULL owner layer: candidate blocks it also builds for REINDEX layers (0: none)
+    d_model: int = 0           # FULL owner layer: hidden width of the write path that first appends the step's
+                               # compressed rows (compressor, main row, index key); 0: planes given as they are
 
     @property
     def n_main_rows(self):
@@ -92,10 +94,22 @@ CONFIGS = {
     "pages_fp4_decode_1m": Csa2Config(
         name="pages_fp4_decode_1m", phase="decode", index_mode="full", batch=64, q_tokens=64, context=1 << 20,
         ratio=1, main_dtype="nvfp4", swa_dtype="fp8mx", idx_dtype="fp4", value_scale="unit", **_COMMON),
+    # The decoder's FULL owner layer as one step: the write path (5120-wide hidden rows -> the new
+    # compressed row of each sequence, m = 1), then the same scoring, selection and attention.
+    "lowp_owner_decode_1m": Csa2Config(
+        name="lowp_owner_decode_1m", phase="decode", index_mode="full", batch=64, q_tokens=64, context=1 << 20,
+        ratio=1, main_dtype="fp4", swa_dtype="fp8", idx_dtype="fp8", value_scale="inv_sqrt_d", d_model=5120,
+        **_COMMON),
+    # An encoder FULL owner layer's prefill chunk: the write path pools the chunk's 4096 tokens into 2048
+    # rows (m = 2) before the FULL layer scores them; then the 5 REUSE layers.
+    "prefill_owner_4096_at_128k": Csa2Config(
+        name="prefill_owner_4096_at_128k", phase="prefill", index_mode="full", batch=1, q_tokens=4096,
+        context=131072, ratio=2, reuse_layers=5, value_scale="unit", d_model=5120, **_COMMON),
 }
 
 CONFIG_ORDER = ["tiny_full_fp32", "full_decode_64k", "prefill_4096_at_128k", "reindex_decode_1m",
-                "lowp_full_decode_1m", "lowp_pool_decode_1m", "pages_fp4_decode_1m"]
+                "lowp_full_decode_1m", "lowp_pool_decode_1m", "pages_fp4_decode_1m", "lowp_owner_decode_1m",
+                "prefill_owner_4096_at_128k"]
 
 
 def get_config(name):

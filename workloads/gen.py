@@ -252,6 +252,18 @@ def make_inputs(cfg: Csa2Config, seed: int, device="cpu"):
         out["w"] = w.contiguous()
     if cfg.index_mode == "reindex":
         out["cand"] = make_candidates(cfg, pos, g, device)
+    if cfg.d_model:
+        # the write path's inputs: one hidden row per query token (its own sequence's newest token in
+        # decode, the chunk's tokens in prefill), the owner layer's weights and the tail state
+        c = make_compress_inputs(rows, cfg.d_model, cfg.ratio, int(seed) + 7919, device=device, seqs=1)
+        slot = torch.arange(rows, dtype=torch.int32, device=device) if cfg.phase == "decode" else \
+            torch.zeros(rows, dtype=torch.int32, device=device)
+        n_slots = rows if cfg.phase == "decode" else 1
+        c.update(pos=pos, slot=slot, row_base=out["kv_row_base"])
+        if cfg.ratio == 2:
+            c["tail_kv"] = _normal(g, (n_slots, 512), device, 1.0)
+            c["tail_score"] = _normal(g, (n_slots, 512), device, 1.0)
+        out["compress"] = c
     return out
 
 

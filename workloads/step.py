@@ -1,6 +1,7 @@
 """One step of the hot path for a workload: output buffers plus the C ABI calls, marshalled once.
 
-A step is the whole path over one batch (see bench.py): the indexer scores,
+A step is the whole path over one batch (see bench.py): for a FULL owner layer
+the write path that appends the step's compressed rows, the indexer scores,
 the top-k, the candidate pool when the workload's FULL layer builds one, and
 sparse attention for every layer that uses the selection.  Wide FULL rows with
 an FP8 or MXFP4 index plane take the score-free route (indexer_score with scores=None,
@@ -33,9 +34,29 @@ def attn_storage_args(cfg, x):
                     kv_nvfp4=cfg.main_dtype == "nvfp4", swa_fp8mx=cfg.swa_dtype == "fp8mx", kv_scale=kvs)
 
 
+_MAIN_FORMAT = {"f32": "f32", "bf16": "bf16", "fp4": "fp4", "nvfp4": "nvfp4"}
+_IDX_FORMAT = {"f32": "f32", "bf16": "bf16", "fp8": "fp8", "fp4": "fp4"}
+
+
+def compress_plane_args(cfg, x):
+    """Keyword arguments of csa2.compress writing into the workload's main and index planes."""
+    main = x["main"].reshape(-1, x["main"].shape[-1])
+    idx = x["kI"].reshape(-1, x["kI"].shape[-1])
+    ms = None if x["main_scale"] is None else x["main_scale"].reshape(-1, x["main_scale"].shape[-1])
+    if x["kI_scale"] is None:
+        isc = None
+    elif cfg.idx_dtype == "fp8":
+        isc = x["kI_scale"].reshape(-1)
+    else:
+        isc = x["kI_scale"].reshape(-1, x["kI_scale"].shape[-1])
+    return main, idx, dict(main_format=_MAIN_FORMAT[cfg.main_dtype], idx_format=_IDX_FORMAT[cfg.idx_dtype],
+                           main_scale=ms, idx_scale=isc)
+
+
 class Step:
     """Buffers and prepared calls of one step, grouped by kernel: ``groups`` maps
-    "indexer_score" / "topk_select" / "candidate_pool" / "sparse_attn" to lists of calls."""
+    "compress" (owner layers) / "indexer_score" / "topk_select" / "candidate_pool" / "sparse_attn" to lists
+    of calls, in launch order."""
 
     def __init__(self, cfg, x, score_free=None):
         import sparse_latent_attention_amd as csa2
@@ -86,7 +107,17 @@ class Step:
                                                   block_max=self.block_max, **ikw)
             call_topk = csa2.prepare_topk_select(self.scores, x["pos"], cfg.ratio, self.idx, cand=x.get("cand"),
                                                  block_rows=cfg.block_rows, key_hist=self.key_hist)
-        self.groups = {"indexer_score": [call_idx], "topk_select": [call_topk]}
+        self.groups = {}
+        if cfg.d_model:
+            # the FULL owner layer first appends the step's compressed rows to its planes
+            c = x["compress"]
+            main, idx, pkw = compress_plane_args(cfg, x)
+            self.groups["compress"] = [csa2.prepare_compress(
+                c["x"], c["pos"], c["slot"], c["row_base"], c["wkv"], c["norm_w"], c["wk"], c["knorm_w"], freqs,
+                main, idx, ratio=cfg.ratio, wgate=c["wgate"], tail_kv=c["tail_kv"], tail_score=c["tail_score"],
+                **pkw)]
+        self.groups["indexer_score"] = [call_idx]
+        self.groups["topk_select"] = [call_topk]
         if cfg.pool_blocks:
             src = dict(block_keys=self.block_keys) if score_free else dict(block_max=self.block_max)
             self.groups["candidate_pool"] = [csa2.prepare_candidate_pool(
