@@ -194,8 +194,10 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
     return hip_status(e);
 }
 
-// Split of the projections' K range: enough workgroups to stream the weights
-// when rows are few, with d_in / ksplit a multiple of 64.
+// Split of the projections' K range when rows are few (decode): enough
+// workgroups to stream the weights, up to 16 splits (each adds a rows x nproj
+// float32 partial tile that the finish kernel reads back), d_in / ksplit a
+// multiple of 64.
 static int compress_ksplit(int32_t rows, int32_t d_in, int32_t ratio) {
     const int64_t tiles = (int64_t)((rows + 63) / 64) * (ratio == 2 ? 16 : 8);
     int ks = 1;

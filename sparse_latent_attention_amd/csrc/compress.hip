@@ -19,7 +19,9 @@
 //    consecutive k of row n: 16 contiguous bytes).  With few rows (decode) the
 //    K range is split over workgroups so the weights, the dominant bytes, are
 //    streamed by enough of them; partial tiles go to a workspace and are added
-//    in a fixed order, so the result does not depend on scheduling.
+//    in a fixed order, so the result does not depend on scheduling.  (At
+//    prefill sizes the operands are re-read by every tile from L2; an
+//    LDS-staged 128 x 128 tiling is the next step for this kernel.)
 //  * compress_finish_kernel: one workgroup per token row: pooling with its
 //    group partner (the previous row of the call, or the tail state), the two
 //    RMSNorms, the 128 x 512 index-key projection (thread pairs split each
@@ -153,7 +155,9 @@ __device__ __forceinline__ void store_pair(void* out, void* scale_out, int64_t r
 
 }  // namespace
 
-// grid (nproj / 64, ceil(rows / 64), ksplit), 256 threads.
+// grid (nproj / 64, ceil(rows / 64), ksplit), 256 threads.  (Loading the next
+// k step ahead of the matrix cores measured no faster at prefill sizes and
+// slower at decode sizes.)
 __global__ __launch_bounds__(256) void compress_project_kernel(const CompressParams p, int k_per_split) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -174,8 +178,8 @@ __global__ __launch_bounds__(256) void compress_project_kernel(const CompressPar
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int k = k0; k < k0 + k_per_split; k += 64) {  // k_per_split is a multiple of 64
-        bf16x8 b0 = *reinterpret_cast<const bf16x8*>(wrow + k);
-        bf16x8 b1 = *reinterpret_cast<const bf16x8*>(wrow + k + 32);
+        const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(wrow + k);
+        const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(wrow + k + 32);
         bf16x8 a0[4], a1[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -198,115 +202,184 @@ __global__ __launch_bounds__(256) void compress_project_kernel(const CompressPar
         }
 }
 
-// grid rows, 256 threads: thread t owns latent channels 2t, 2t+1 and (t < 64)
-// key elements 2t, 2t+1.
-template <int RATIO, int MT, int KT>
+namespace {
+
+// Columns (col, col + 1) of one row's projections: the split-K partial tiles
+// added in the order k = 0, 1, ... (eight loads in flight at a time).  The
+// finish and tail kernels both use it, so a tail holds exactly the values
+// the row's own group would have used.
+__device__ __forceinline__ f32x2 proj2(const CompressParams& p, int row, int col) {
+    const float* base = p.partial + (int64_t)row * p.nproj + col;
+    if (p.ksplit == 1) return *reinterpret_cast<const f32x2*>(base);
+    const int64_t stride = (int64_t)p.rows * p.nproj;
+    f32x2 acc{0.f, 0.f};
+    for (int k0 = 0; k0 < p.ksplit; k0 += 8) {
+        f32x2 v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int k = k0 + e < p.ksplit ? k0 + e : p.ksplit - 1;  // in bounds; not added below
+            v[e] = *reinterpret_cast<const f32x2*>(base + k * stride);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (k0 + e < p.ksplit) acc += v[e];
+    }
+    return acc;
+}
+
+}  // namespace
+
+// grid ceil(rows / RPB), 256 threads: RPB consecutive token rows per workgroup
+// (the index-key weights are read once for all of them).  Thread t owns latent
+// channels 2t, 2t+1 and (t < 64) key elements 2t, 2t+1.
+template <int RATIO, int MT, int KT, int RPB>
 __global__ __launch_bounds__(256) void compress_finish_kernel(const CompressParams p) {
-    __shared__ float lat[kLatent];
-    __shared__ float key[kKey];
+    __shared__ float lat[RPB][kLatent];
+    __shared__ float key[RPB][kKey];
     __shared__ float red[4];
     const int t = threadIdx.x;
-    const int r = blockIdx.x;
-    const int64_t pos = p.pos[r];
-    const int s = p.slot[r];
-    const int nk = p.ksplit;
-    // projections: the split-K partial tiles added in a fixed order (the tail
-    // kernel adds them the same way, so a tail holds exactly these values)
-    auto proj = [&](int row, int col) {
-        float v = 0.f;
-        for (int k = 0; k < nk; ++k) v += p.partial[((int64_t)k * p.rows + row) * p.nproj + col];
-        return v;
-    };
     const int c = 2 * t;
-    float v0, v1;
-    int64_t j;
-    if (RATIO == 1) {
-        v0 = proj(r, c);
-        v1 = proj(r, c + 1);
-        j = pos;
-    } else {
-        const float kv0 = proj(r, c), kv1 = proj(r, c + 1);
-        const float s0 = proj(r, kLatent + c), s1 = proj(r, kLatent + c + 1);
-        if ((pos & 1) == 0) return;  // first token of its group (uniform over the workgroup)
-        float pk0, pk1, ps0, ps1;
-        if (r > 0 && p.slot[r - 1] == s && p.pos[r - 1] == pos - 1) {
-            pk0 = proj(r - 1, c);
-            pk1 = proj(r - 1, c + 1);
-            ps0 = proj(r - 1, kLatent + c);
-            ps1 = proj(r - 1, kLatent + c + 1);
-        } else {
-            const f32x2 tk = *reinterpret_cast<const f32x2*>(p.tail_kv + (int64_t)s * kLatent + c);
-            const f32x2 ts = *reinterpret_cast<const f32x2*>(p.tail_score + (int64_t)s * kLatent + c);
-            pk0 = tk[0];
-            pk1 = tk[1];
-            ps0 = ts[0];
-            ps1 = ts[1];
-        }
-        // per channel, softmax over the group's two positions (first: partner)
-        const float m0 = fmaxf(ps0, s0), m1 = fmaxf(ps1, s1);
-        const float a0 = expf(ps0 - m0), b0 = expf(s0 - m0);
-        const float a1 = expf(ps1 - m1), b1 = expf(s1 - m1);
-        v0 = (a0 * pk0 + b0 * kv0) / (a0 + b0);
-        v1 = (a1 * pk1 + b1 * kv1) / (a1 + b1);
-        j = pos / 2;
+    const int r0 = blockIdx.x * RPB;
+    // Loads that depend on nothing are issued first, so their latency overlaps
+    // the partial sums: the norm weights, the rotation frequencies and, with one
+    // row per workgroup (the latency-bound decode shape), this thread's 512 bytes
+    // of index-key weights.
+    const int ki = t >> 1, kh = t & 1;
+    const uint16_t* wr = p.wk + (int64_t)ki * kLatent + 256 * kh;
+    constexpr int kPre = RPB == 1 ? 32 : 1;
+    u32x4 wv[kPre];
+    if constexpr (RPB == 1) {
+#pragma unroll
+        for (int q = 0; q < kPre; ++q) wv[q] = *reinterpret_cast<const u32x4*>(wr + 8 * q);
     }
-    // RMSNorm of the latent
-    const float ss = block_sum(v0 * v0 + v1 * v1, red);
-    const float inv = 1.0f / sqrtf(ss / (float)kLatent + p.eps);
-    v0 = v0 * inv * p.norm_w[c];
-    v1 = v1 * inv * p.norm_w[c + 1];
-    lat[c] = v0;
-    lat[c + 1] = v1;
+    // (with several rows per workgroup these stay at their uses: registers there buy occupancy)
+    f32x2 nw_pre{0.f, 0.f}, knw_pre{0.f, 0.f};
+    double fm_pre = 0.0, fk_pre = 0.0;
+    if constexpr (RPB == 1) {
+        nw_pre = *reinterpret_cast<const f32x2*>(p.norm_w + c);
+        if (t < kKey / 2) knw_pre = *reinterpret_cast<const f32x2*>(p.knorm_w + 2 * t);
+        if (c >= kLatent - kRope) fm_pre = p.inv_freq[(c - (kLatent - kRope)) / 2];
+        if (t < kKey / 2 && 2 * t >= kKey - kRope) fk_pre = p.inv_freq[(2 * t - (kKey - kRope)) / 2];
+    }
+    auto nw = [&](int e) { return RPB == 1 ? nw_pre[e] : p.norm_w[c + e]; };
+    auto knw = [&](int e) { return RPB == 1 ? knw_pre[e] : p.knorm_w[2 * t + e]; };
+    auto fm = [&]() { return RPB == 1 ? fm_pre : p.inv_freq[(c - (kLatent - kRope)) / 2]; };
+    auto fk = [&]() { return RPB == 1 ? fk_pre : p.inv_freq[(2 * t - (kKey - kRope)) / 2]; };
+    float lv[RPB][2];
+    bool emit[RPB];
+    int64_t jj[RPB];
+#pragma unroll
+    for (int rr = 0; rr < RPB; ++rr) {
+        const int r = r0 + rr;
+        emit[rr] = false;
+        jj[rr] = 0;
+        lv[rr][0] = lv[rr][1] = 0.f;
+        if (r >= p.rows) continue;  // uniform over the workgroup, as every condition on r below
+        const int64_t pos = p.pos[r];
+        if (RATIO == 2 && (pos & 1) == 0) continue;  // first token of its group: no row yet
+        emit[rr] = true;
+        float v0, v1;
+        if (RATIO == 1) {
+            const f32x2 kv = proj2(p, r, c);
+            v0 = kv[0];
+            v1 = kv[1];
+            jj[rr] = pos;
+        } else {
+            const int s = p.slot[r];
+            const f32x2 kv = proj2(p, r, c), sc = proj2(p, r, kLatent + c);
+            f32x2 pk, ps;
+            if (r > 0 && p.slot[r - 1] == s && p.pos[r - 1] == pos - 1) {
+                pk = proj2(p, r - 1, c);
+                ps = proj2(p, r - 1, kLatent + c);
+            } else {
+                pk = *reinterpret_cast<const f32x2*>(p.tail_kv + (int64_t)s * kLatent + c);
+                ps = *reinterpret_cast<const f32x2*>(p.tail_score + (int64_t)s * kLatent + c);
+            }
+            // per channel, softmax over the group's two positions (first: partner)
+            const float m0 = fmaxf(ps[0], sc[0]), m1 = fmaxf(ps[1], sc[1]);
+            const float a0 = expf(ps[0] - m0), b0 = expf(sc[0] - m0);
+            const float a1 = expf(ps[1] - m1), b1 = expf(sc[1] - m1);
+            v0 = (a0 * pk[0] + b0 * kv[0]) / (a0 + b0);
+            v1 = (a1 * pk[1] + b1 * kv[1]) / (a1 + b1);
+            jj[rr] = pos / 2;
+        }
+        // RMSNorm of the latent
+        const float ss = block_sum(v0 * v0 + v1 * v1, red);
+        const float inv = 1.0f / sqrtf(ss / (float)kLatent + p.eps);
+        lv[rr][0] = v0 * inv * nw(0);
+        lv[rr][1] = v1 * inv * nw(1);
+        lat[rr][c] = lv[rr][0];
+        lat[rr][c + 1] = lv[rr][1];
+    }
     __syncthreads();
-    // index key: output i = t / 2, channels [256 h, 256 h + 256) of half h = t % 2
+    // index keys: output i = t / 2 over channels [256 h, 256 h + 256) of half h = t % 2
     {
-        const int i = t >> 1, h = t & 1;
-        const uint16_t* wr = p.wk + (int64_t)i * kLatent + 256 * h;
-        const float* lr = lat + 256 * h;
-        float acc = 0.f;
-#pragma unroll 4
-        for (int q = 0; q < 256; q += 8) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(wr + q);
+        const int h = kh;
+        float acc[RPB];
+#pragma unroll
+        for (int rr = 0; rr < RPB; ++rr) acc[rr] = 0.f;
+        auto fma8 = [&](const u32x4& w, int q) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc = fmaf(bf16_bits_to_f32(w[e] & 0xffffu), lr[q + 2 * e], acc);
-                acc = fmaf(bf16_bits_to_f32(w[e] >> 16), lr[q + 2 * e + 1], acc);
+                const float w0 = bf16_bits_to_f32(w[e] & 0xffffu), w1 = bf16_bits_to_f32(w[e] >> 16);
+#pragma unroll
+                for (int rr = 0; rr < RPB; ++rr) {
+                    if (!emit[rr]) continue;
+                    acc[rr] = fmaf(w0, lat[rr][256 * h + q + 2 * e], acc[rr]);
+                    acc[rr] = fmaf(w1, lat[rr][256 * h + q + 2 * e + 1], acc[rr]);
+                }
             }
+        };
+        if constexpr (RPB == 1) {
+#pragma unroll
+            for (int q8 = 0; q8 < kPre; ++q8) fma8(wv[q8], 8 * q8);
+        } else {
+#pragma unroll 4
+            for (int q = 0; q < 256; q += 8) fma8(*reinterpret_cast<const u32x4*>(wr + q), q);
         }
-        acc += __shfl_xor(acc, 1, 64);
-        if (h == 0) key[i] = acc;
+#pragma unroll
+        for (int rr = 0; rr < RPB; ++rr) {
+            acc[rr] += __shfl_xor(acc[rr], 1, 64);
+            if (h == 0) key[rr][ki] = acc[rr];
+        }
     }
     __syncthreads();
-    float k0 = 0.f, k1 = 0.f;
-    if (t < kKey / 2) {
-        k0 = key[2 * t];
-        k1 = key[2 * t + 1];
+#pragma unroll
+    for (int rr = 0; rr < RPB; ++rr) {
+        if (!emit[rr]) continue;
+        const int r = r0 + rr;
+        float k0 = 0.f, k1 = 0.f;
+        if (t < kKey / 2) {
+            k0 = key[rr][2 * t];
+            k1 = key[rr][2 * t + 1];
+        }
+        const float kss = block_sum(k0 * k0 + k1 * k1, red);
+        const float kinv = 1.0f / sqrtf(kss / (float)kKey + p.k_eps);
+        if (t < kKey / 2) {
+            k0 = k0 * kinv * knw(0);
+            k1 = k1 * kinv * knw(1);
+        }
+        // rotation of the last 64 dims at the group's first position
+        const int64_t rp = jj[rr] * RATIO;
+        float v0 = lv[rr][0], v1 = lv[rr][1];
+        if (c >= kLatent - kRope) {
+            float cs, sn;
+            rope_angle(rp, fm(), cs, sn);
+            const float x0 = v0, x1 = v1;
+            v0 = x0 * cs - x1 * sn;
+            v1 = x0 * sn + x1 * cs;
+        }
+        if (t < kKey / 2 && 2 * t >= kKey - kRope) {
+            float cs, sn;
+            rope_angle(rp, fk(), cs, sn);
+            const float x0 = k0, x1 = k1;
+            k0 = x0 * cs - x1 * sn;
+            k1 = x0 * sn + x1 * cs;
+        }
+        const int64_t row = p.row_base[r] + jj[rr];
+        store_pair<MT>(p.main_out, p.main_scale_out, row, kLatent, t, v0, v1);
+        if (t < kKey / 2) store_pair<KT>(p.idx_out, p.idx_scale_out, row, kKey, t, k0, k1);
     }
-    const float kss = block_sum(k0 * k0 + k1 * k1, red);
-    const float kinv = 1.0f / sqrtf(kss / (float)kKey + p.k_eps);
-    if (t < kKey / 2) {
-        k0 = k0 * kinv * p.knorm_w[2 * t];
-        k1 = k1 * kinv * p.knorm_w[2 * t + 1];
-    }
-    // rotation of the last 64 dims at the group's first position
-    const int64_t rp = j * RATIO;
-    if (c >= kLatent - kRope) {
-        float cs, sn;
-        rope_angle(rp, p.inv_freq[(c - (kLatent - kRope)) / 2], cs, sn);
-        const float x0 = v0, x1 = v1;
-        v0 = x0 * cs - x1 * sn;
-        v1 = x0 * sn + x1 * cs;
-    }
-    if (t < kKey / 2 && 2 * t >= kKey - kRope) {
-        float cs, sn;
-        rope_angle(rp, p.inv_freq[(2 * t - (kKey - kRope)) / 2], cs, sn);
-        const float x0 = k0, x1 = k1;
-        k0 = x0 * cs - x1 * sn;
-        k1 = x0 * sn + x1 * cs;
-    }
-    const int64_t row = p.row_base[r] + j;
-    store_pair<MT>(p.main_out, p.main_scale_out, row, kLatent, t, v0, v1);
-    if (t < kKey / 2) store_pair<KT>(p.idx_out, p.idx_scale_out, row, kKey, t, k0, k1);
 }
 
 // grid rows, 256 threads: the first token of a group that no later row of the
@@ -318,14 +391,8 @@ __global__ __launch_bounds__(256) void compress_tail_kernel(const CompressParams
     const int s = p.slot[r];
     if ((p.pos[r] & 1) != 0 || (r + 1 < p.rows && p.slot[r + 1] == s)) return;
     const int c = 2 * threadIdx.x;
-    f32x2 kv{0.f, 0.f}, sc{0.f, 0.f};
-    for (int k = 0; k < p.ksplit; ++k) {
-        const float* pr = p.partial + ((int64_t)k * p.rows + r) * p.nproj;
-        kv += *reinterpret_cast<const f32x2*>(pr + c);
-        sc += *reinterpret_cast<const f32x2*>(pr + kLatent + c);
-    }
-    *reinterpret_cast<f32x2*>(p.tail_kv + (int64_t)s * kLatent + c) = kv;
-    *reinterpret_cast<f32x2*>(p.tail_score + (int64_t)s * kLatent + c) = sc;
+    *reinterpret_cast<f32x2*>(p.tail_kv + (int64_t)s * kLatent + c) = proj2(p, r, c);
+    *reinterpret_cast<f32x2*>(p.tail_score + (int64_t)s * kLatent + c) = proj2(p, r, kLatent + c);
 }
 
 bool compress_supported(int main_dtype, int idx_dtype) {
@@ -336,29 +403,41 @@ bool compress_supported(int main_dtype, int idx_dtype) {
     return m && k;
 }
 
-template <int RATIO, int MT>
+template <int RATIO, int MT, int RPB>
 static void launch_finish_k(const CompressParams& p, int idx_dtype, hipStream_t st) {
-    const dim3 grid((unsigned)p.rows);
+    const dim3 grid((unsigned)((p.rows + RPB - 1) / RPB));
     switch (idx_dtype) {
-        case CSA2_F32: hipLaunchKernelGGL((compress_finish_kernel<RATIO, MT, CSA2_F32>), grid, dim3(256), 0, st, p); break;
-        case CSA2_BF16: hipLaunchKernelGGL((compress_finish_kernel<RATIO, MT, CSA2_BF16>), grid, dim3(256), 0, st, p); break;
+        case CSA2_F32:
+            hipLaunchKernelGGL((compress_finish_kernel<RATIO, MT, CSA2_F32, RPB>), grid, dim3(256), 0, st, p);
+            break;
+        case CSA2_BF16:
+            hipLaunchKernelGGL((compress_finish_kernel<RATIO, MT, CSA2_BF16, RPB>), grid, dim3(256), 0, st, p);
+            break;
         case CSA2_FP8_E4M3:
-            hipLaunchKernelGGL((compress_finish_kernel<RATIO, MT, CSA2_FP8_E4M3>), grid, dim3(256), 0, st, p);
+            hipLaunchKernelGGL((compress_finish_kernel<RATIO, MT, CSA2_FP8_E4M3, RPB>), grid, dim3(256), 0, st, p);
             break;
         default:
-            hipLaunchKernelGGL((compress_finish_kernel<RATIO, MT, CSA2_FP4_E2M1>), grid, dim3(256), 0, st, p);
+            hipLaunchKernelGGL((compress_finish_kernel<RATIO, MT, CSA2_FP4_E2M1, RPB>), grid, dim3(256), 0, st, p);
             break;
     }
 }
 
-template <int RATIO>
+template <int RATIO, int RPB>
 static void launch_finish_m(const CompressParams& p, int main_dtype, int idx_dtype, hipStream_t st) {
     switch (main_dtype) {
-        case CSA2_F32: launch_finish_k<RATIO, CSA2_F32>(p, idx_dtype, st); break;
-        case CSA2_BF16: launch_finish_k<RATIO, CSA2_BF16>(p, idx_dtype, st); break;
-        case CSA2_FP4_E2M1: launch_finish_k<RATIO, CSA2_FP4_E2M1>(p, idx_dtype, st); break;
-        default: launch_finish_k<RATIO, CSA2_FP4_E2M1_E4M3G16>(p, idx_dtype, st); break;
+        case CSA2_F32: launch_finish_k<RATIO, CSA2_F32, RPB>(p, idx_dtype, st); break;
+        case CSA2_BF16: launch_finish_k<RATIO, CSA2_BF16, RPB>(p, idx_dtype, st); break;
+        case CSA2_FP4_E2M1: launch_finish_k<RATIO, CSA2_FP4_E2M1, RPB>(p, idx_dtype, st); break;
+        default: launch_finish_k<RATIO, CSA2_FP4_E2M1_E4M3G16, RPB>(p, idx_dtype, st); break;
     }
+}
+
+// Rows per finish workgroup: several when there are many rows (the index-key
+// weights are then read once per group of rows), one otherwise.
+template <int RATIO>
+static void launch_finish(const CompressParams& p, int main_dtype, int idx_dtype, hipStream_t st) {
+    if (p.rows >= 1024) launch_finish_m<RATIO, 4>(p, main_dtype, idx_dtype, st);
+    else launch_finish_m<RATIO, 1>(p, main_dtype, idx_dtype, st);
 }
 
 hipError_t launch_compress(const CompressParams& p, int ratio, int main_dtype, int idx_dtype, hipStream_t stream) {
@@ -368,9 +447,9 @@ hipError_t launch_compress(const CompressParams& p, int ratio, int main_dtype, i
     const dim3 grid((unsigned)(p.nproj / 64), (unsigned)((p.rows + 63) / 64), (unsigned)p.ksplit);
     hipLaunchKernelGGL(compress_project_kernel, grid, dim3(256), 0, stream, p, k_per_split);
     if (ratio == 1) {
-        launch_finish_m<1>(p, main_dtype, idx_dtype, stream);
+        launch_finish<1>(p, main_dtype, idx_dtype, stream);
     } else {
-        launch_finish_m<2>(p, main_dtype, idx_dtype, stream);
+        launch_finish<2>(p, main_dtype, idx_dtype, stream);
         hipLaunchKernelGGL(compress_tail_kernel, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
     }
     return hipGetLastError();

@@ -359,6 +359,7 @@ def test_compress_workspace_rules():
     assert csa2.compress_workspace_size(64, 5120, 2) == 16 * 64 * 1024 * 4
     assert csa2.compress_workspace_size(4096, 5120, 2) == 4096 * 1024 * 4
     assert csa2.compress_workspace_size(64, 5120, 1) == 16 * 64 * 512 * 4
+    assert csa2.compress_workspace_size(1024, 5120, 1) == 8 * 1024 * 512 * 4
     assert csa2.compress_workspace_size(0, 5120, 2) == 0 and csa2.compress_workspace_size(4, 100, 2) == 0
     a = _compress_args()
     need = csa2.compress_workspace_size(4, 5120, 2)
