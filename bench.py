@@ -80,13 +80,13 @@ def algorithmic_work(cfg, x, idx_host=None, score_free=False):
         extra = 0
     nbm = -(-cfg.width // cfg.block_rows) if cfg.pool_blocks else 0
     if score_free:
-        # scores stay on chip: the key histogram and the 8-column block keys are written instead
+        # scores stay on chip: only the 8-column block keys are written
         nbk = -(-cfg.width // 8)
-        idx_bytes = unique_rows * idx_row + qI + rows * (nbk + 4096) * 4
+        idx_bytes = unique_rows * idx_row + qI + rows * nbk * 4
         nbm = nbk if cfg.pool_blocks else 0  # the pool ranks the same block keys
-        # the select reads the histogram and block keys (re-scored candidate rows are not counted:
-        # they are extra work of this route, not bytes the result needs)
-        topk_bytes = rows * (nbk + 4096) * 4 + rows * cfg.topk * 4
+        # the select reads the block keys (re-scored candidate rows and the second look at the block
+        # keys are not counted: they are extra work of this route, not bytes the result needs)
+        topk_bytes = rows * nbk * 4 + rows * cfg.topk * 4
     else:
         idx_bytes = unique_rows * idx_row + qI + extra + rows * cfg.width * 4 + rows * nbm * 4
         topk_bytes = rows * cfg.width * 4 + rows * cfg.topk * 4 + extra

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 5
+#define CSA2_ABI_VERSION 6
 
 /* Status codes. */
 #define CSA2_OK 0
@@ -146,15 +146,14 @@ typedef struct csa2_index_args {
     float scale;                /* score scale (dim^-1/2 * heads^-1/2 in the pages' model) */
     int32_t _pad1;
     float* scores;              /* out: [rows, width] float32; NULL selects score-free mode (see
-                                 * csa2_topk_rescore) */
+                                 * csa2_topk_rescore; FULL, FP8 or MXFP4 64 x 128, block_keys
+                                 * required, key_hist NULL) */
     uint32_t* key_hist;         /* optional out: [rows, 4096], or NULL.  The call zeroes it, then
                                  * counts every valid score of row r in bin key(score) >> 20, where
                                  * key is the order-preserving 32-bit key csa2_topk_select ranks by
                                  * (bits | 0x80000000 for scores >= +0, ~bits below, NaN as -inf,
                                  * -0 as +0).  Passing it on to csa2_topk_select saves that call a
-                                 * full pass over the scores.  In score-free mode it counts instead,
-                                 * per 8-column block with a valid column, the bin block_keys[b] >> 20
-                                 * of its block key (below). */
+                                 * full pass over the scores.  NULL in score-free mode. */
     float* block_max;           /* optional out, FULL only: [rows, ceil(width / block_rows)], or NULL.
                                  * Block b of row r gets the block score csa2_candidate_pool ranks:
                                  * the largest score over its visible columns, with NaN read as -inf
@@ -179,19 +178,19 @@ int32_t csa2_indexer_score(const csa2_index_args* args, csa2_stream_t stream);
  * Writing a [rows, width] score matrix only to read it back for the top-k
  * costs more than the scoring itself reads when rows are 1M columns wide.  In
  * score-free mode (csa2_indexer_score with scores == NULL, which requires FULL
- * mode, key_hist and block_keys) the scores stay on chip: the call writes the
- * key histogram and the per-8-column block keys only.  csa2_topk_rescore then
- * takes the same arguments and returns the top-k: from the block-key histogram
- * it finds the bin b1 holding each row's k-th largest block key (the k blocks
- * with the largest keys hold k columns with keys in bins >= b1, so every
- * selected column has a key in a bin >= b1), re-scores exactly the blocks
- * whose block key reaches b1 (every selected column lies in one), with the
- * same arithmetic as the scoring pass, and runs the exact select of
+ * mode and block_keys, and key_hist NULL) the scores stay on chip: the call
+ * writes the per-8-column block keys only.  csa2_topk_rescore then takes the
+ * same arguments and returns the top-k: it counts the block keys' top 12 bits
+ * per row and finds the bin b1 holding each row's k-th largest block key (the
+ * k blocks with the largest keys hold k columns with keys in bins >= b1, so
+ * every selected column has a key in a bin >= b1), re-scores exactly the
+ * blocks whose block key reaches b1 (every selected column lies in one), with
+ * the same arithmetic as the scoring pass, and runs the exact select of
  * csa2_topk_select over their columns in bins >= b1.  The result is bit-identical to
  * csa2_topk_select over the scores csa2_indexer_score would have written.
  *
- * args: as given to the score-free csa2_indexer_score call (key_hist and
- * block_keys are now inputs; scores and block_max are ignored).
+ * args: as given to the score-free csa2_indexer_score call (block_keys is now
+ * an input; key_hist NULL; scores and block_max are ignored).
  * out: [rows, k] int32, ascending plane rows, -1 padded.
  * Supported: FP8-E4M3 or MXFP4 q and k with (heads, dim) = (64, 128); 1 <= k <= 2048;
  * rows < 1024 and 8192 <= width < 2^24 (exactly when

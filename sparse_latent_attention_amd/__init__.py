@@ -260,8 +260,8 @@ def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None,
     optionally receives the score-key histogram topk_select can reuse.
     ``block_max`` (FULL only, float32 [rows, ceil(width / block_rows)])
     optionally receives the candidate pool's block scores.  ``scores=None``
-    (with ``width``, ``key_hist`` and ``block_keys`` int32 [rows, ceil(width / 8)])
-    selects the score-free mode whose top-k ``topk_rescore`` takes.
+    (with ``width`` and ``block_keys`` int32 [rows, ceil(width / 8)], no
+    ``key_hist``) selects the score-free mode whose top-k ``topk_rescore`` takes.
     """
     a = _index_args(q, w, k, row_base, pos, ratio, scale, scores, width, k_scale, cand, block_rows, fp8, key_hist,
                     block_max, block_keys, fp4, q_scale)
@@ -280,14 +280,14 @@ def topk_rescore_supported(rows, width, k, heads=64, dim=128, fp8=True, fp4=Fals
             topk_rescore_workspace_size(rows, width, k) > 0)
 
 
-def topk_rescore(q, w, k, row_base, pos, ratio, scale, out, key_hist, block_keys, width, *, k_scale=None,
+def topk_rescore(q, w, k, row_base, pos, ratio, scale, out, block_keys, width, *, k_scale=None,
                  fp4=False, q_scale=None, workspace=None, stream=None):
     """Top-k ``out`` [rows, k] int32 of the scores a score-free indexer_score call with these arguments kept on
-    chip (its ``key_hist`` and ``block_keys``); bit-identical to topk_select over the written scores.  FP8
-    index planes by default, MXFP4 ones with ``fp4=True`` (and ``q_scale``, as for indexer_score)."""
+    chip (its ``block_keys``); bit-identical to topk_select over the written scores.  FP8 index planes by
+    default, MXFP4 ones with ``fp4=True`` (and ``q_scale``, as for indexer_score)."""
     _dev(out)
     _need(out, torch.int32, "out")
-    a = _index_args(q, w, k, row_base, pos, ratio, scale, None, width, k_scale, None, 8, not fp4, key_hist, None,
+    a = _index_args(q, w, k, row_base, pos, ratio, scale, None, width, k_scale, None, 8, not fp4, None, None,
                     block_keys, fp4, q_scale)
     if out.shape[0] != a.rows:
         raise ValueError("csa2.topk_rescore: out rows")
@@ -606,7 +606,7 @@ def prepare_compress(x, *args, stream=None, **kw):
 
 def prepare_topk_rescore(*args, stream=None, **kw):
     if kw.get("workspace") is None:
-        out, width = args[7], args[10]
+        out, width = args[7], args[9]
         need = topk_rescore_workspace_size(out.shape[0], width, out.shape[1])
         kw["workspace"] = torch.empty(max(need, 1), dtype=torch.uint8, device=out.device)
     p = _prepare("csa2_topk_rescore", lambda: topk_rescore(*args, stream=stream, **kw), stream)

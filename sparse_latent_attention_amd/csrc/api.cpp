@@ -89,12 +89,12 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
     } else if (a->block_max != nullptr && !pool_block_ok(a->block_rows)) {
         return CSA2_ERR_INVALID_ARG;
     }
-    // Score-free mode: FULL FP8 rows keep their scores on chip and leave the key
-    // histogram and block keys for csa2_topk_rescore.
+    // Score-free mode: FULL rows of a quantised plane keep their scores on chip and
+    // leave the block keys for csa2_topk_rescore.
     const bool score_free = a->scores == nullptr;
     if (a->block_keys != nullptr && !score_free) return CSA2_ERR_INVALID_ARG;
     if (score_free) {
-        if (reindex || a->key_hist == nullptr || a->block_keys == nullptr) return CSA2_ERR_INVALID_ARG;
+        if (reindex || a->key_hist != nullptr || a->block_keys == nullptr) return CSA2_ERR_INVALID_ARG;
         if (!csa2::indexer_rescore_supported(a->heads, a->dim, a->k_dtype)) return CSA2_ERR_UNSUPPORTED;
         if (a->width >= (1LL << 24)) return CSA2_ERR_UNSUPPORTED;
         if (!aligned(a->block_keys, 4)) return CSA2_ERR_INVALID_ARG;
@@ -143,7 +143,8 @@ size_t csa2_topk_rescore_workspace_size(int32_t rows, int64_t width, int32_t k) 
     rescore_plan(rows, width, chunk, nseg);
     if (nseg == 0) return 0;
     const size_t lists = (size_t)rows * nseg * chunk;
-    return align256((size_t)rows * 4) + align256((size_t)rows * nseg * 4) + 2 * align256(lists * 4);
+    return align256((size_t)rows * 4) + align256((size_t)rows * nseg * 4) + 2 * align256(lists * 4) +
+           align256((size_t)rows * 4096 * 4);
 }
 
 int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, void* workspace, size_t workspace_bytes,
@@ -162,7 +163,7 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
     if (workspace_bytes < need) return CSA2_ERR_WORKSPACE;
     if (workspace == nullptr || !aligned(workspace, 256)) return CSA2_ERR_INVALID_ARG;
     if (a->q == nullptr || a->w == nullptr || a->k == nullptr || a->row_base == nullptr || a->pos == nullptr ||
-        a->key_hist == nullptr || a->block_keys == nullptr || out == nullptr || !index_scales_ok(a))
+        a->key_hist != nullptr || a->block_keys == nullptr || out == nullptr || !index_scales_ok(a))
         return CSA2_ERR_INVALID_ARG;
     if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->w, 4) || !isfinite(a->scale))
         return CSA2_ERR_INVALID_ARG;
@@ -170,11 +171,11 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
     csa2::IndexParams ip;
     ip.q = a->q; ip.w = a->w; ip.k = a->k; ip.k_scale = a->k_scale; ip.row_base = a->row_base; ip.pos = a->pos;
     ip.q_e8 = a->q_scale_e8m0; ip.k_e8 = a->k_scale_e8m0;
-    ip.cand = nullptr; ip.scores = nullptr; ip.key_hist = a->key_hist; ip.block_max = nullptr;
+    ip.cand = nullptr; ip.scores = nullptr; ip.key_hist = nullptr; ip.block_max = nullptr;
     ip.block_keys = a->block_keys; ip.width = a->width; ip.cols_per_wg = 0; ip.bm_blocks = 0; ip.n_blocks = 0;
     ip.block_rows = 1; ip.bm_rows = 4; ip.ratio = a->ratio; ip.scale = a->scale;
     csa2::TopkParams tp;
-    tp.scores = nullptr; tp.pos = a->pos; tp.cand = nullptr; tp.out = out; tp.key_hist = a->key_hist;
+    tp.scores = nullptr; tp.pos = a->pos; tp.cand = nullptr; tp.out = out; tp.key_hist = nullptr;
     tp.width = a->width; tp.k = k; tp.ratio = a->ratio; tp.n_blocks = 0; tp.block_rows = 1; tp.col_group = 1;
     tp.pool_keys = nullptr;
 
@@ -186,8 +187,11 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
     uint32_t* keys = reinterpret_cast<uint32_t*>(w);
     w += align256((size_t)a->rows * nseg * chunk * 4);
     int32_t* cols = reinterpret_cast<int32_t*>(w);
+    w += align256((size_t)a->rows * nseg * chunk * 4);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(w);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = csa2::launch_topk_threshold(tp, a->rows, a->key_hist, b1, st);
+    hipError_t e = csa2::launch_block_key_hist(a->block_keys, (a->width + 7) / 8, a->rows, hist, st);
+    if (e == hipSuccess) e = csa2::launch_topk_threshold(tp, a->rows, hist, b1, st);
     if (e == hipSuccess)
         e = csa2::launch_indexer_rescore(ip, a->rows, a->k_dtype, b1, chunk, nseg, keys, cols, seg_count, st);
     if (e == hipSuccess) e = csa2::launch_topk_final(tp, a->rows, keys, cols, seg_count, nseg, chunk, st);

@@ -152,18 +152,15 @@ __device__ __forceinline__ void store_step(const IndexParams& p, int r, int64_t 
     const float score = valid ? sc * kk : kNegInf;
     if (c_out < c_end) {
         if (SCORES) srow[c_out] = score;
-        if (HIST && !BKEYS && valid) atomicAdd(&hist[order_key(score) >> 20], 1u);
+        if (HIST && valid) atomicAdd(&hist[order_key(score) >> 20], 1u);
     }
     if (BKEYS) {
-        // Score-free mode: the histogram counts block keys (one LDS atomic per 8
-        // columns instead of per column); a block without valid columns has key 0.
+        // Score-free mode: block keys only (the select counts them); a block
+        // without valid columns has key 0.
         uint32_t bk = valid ? block_key(score) : 0u;
 #pragma unroll
         for (int o = 1; o < kKeyBlock; o <<= 1) bk = max(bk, shfl_xor(bk, o));
-        if ((lane & (kKeyBlock - 1)) == 0 && c_out < c_end) {
-            bkl[(c_out - c0) / kKeyBlock] = bk;
-            if (HIST && bk != 0u) atomicAdd(&hist[bk >> 20], 1u);
-        }
+        if ((lane & (kKeyBlock - 1)) == 0 && c_out < c_end) bkl[(c_out - c0) / kKeyBlock] = bk;
     }
     if (BMAX) {
         // Block score over bm_rows consecutive columns = lanes (blocks never
@@ -518,7 +515,7 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(const IndexParams p
         __syncthreads();
         const int nbk = (int)((c_end - c_begin + kKeyBlock - 1) / kKeyBlock);
         uint32_t* gk = p.block_keys + (int64_t)r * ((p.width + kKeyBlock - 1) / kKeyBlock) + c_begin / kKeyBlock;
-        for (int i = threadIdx.x; i < nbk; i += 256) gk[i] = bkl[i];
+        for (int i = threadIdx.x; i < nbk; i += 256) __builtin_nontemporal_store(bkl[i], gk + i);
     }
     if (HIST) {
         __syncthreads();
@@ -531,8 +528,8 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(const IndexParams p
 // Re-scoring for the top-k of FULL scores that were never written.
 //
 // Segment seg of row r covers columns [seg * chunk, (seg + 1) * chunk).  b1[r]
-// is the bin holding the row's k-th largest block key (the score-free pass
-// counts block keys).  The k blocks with the largest keys hold k distinct
+// is the bin holding the row's k-th largest block key (the select counts the
+// block keys the score-free pass wrote).  The k blocks with the largest keys hold k distinct
 // columns with keys in bins >= b1, so the row's k-th largest column key is in
 // a bin >= b1 too: every selected column has a key in bin >= b1, and so has
 // the largest key of its kKeyBlock-column block.  One wave handles one segment on its own (no
@@ -700,11 +697,11 @@ static hipError_t launch_stream_full(const IndexParams& p, int rows, hipStream_t
     }
     constexpr int D = kStreamDepth;
     if (p.scores == nullptr) {
-        // scores kept on chip: histogram and block keys only (validated by the caller)
+        // scores kept on chip: block keys only (validated by the caller); the select counts them itself
         if (p.block_max != nullptr)
-            hipLaunchKernelGGL((indexer_stream_kernel<KF, true, true, D, false, true>), grid, dim3(256), 0, stream, p);
+            hipLaunchKernelGGL((indexer_stream_kernel<KF, false, true, D, false, true>), grid, dim3(256), 0, stream, p);
         else
-            hipLaunchKernelGGL((indexer_stream_kernel<KF, true, false, D, false, true>), grid, dim3(256), 0, stream, p);
+            hipLaunchKernelGGL((indexer_stream_kernel<KF, false, false, D, false, true>), grid, dim3(256), 0, stream, p);
     } else if (p.block_max != nullptr) {
         if (hist) hipLaunchKernelGGL((indexer_stream_kernel<KF, true, true, D, true, false>), grid, dim3(256), 0, stream, p);
         else hipLaunchKernelGGL((indexer_stream_kernel<KF, false, true, D, true, false>), grid, dim3(256), 0, stream, p);

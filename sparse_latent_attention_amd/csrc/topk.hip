@@ -548,6 +548,43 @@ hipError_t launch_topk_select(const TopkParams& p, int rows, void* ws, hipStream
     return hipGetLastError();
 }
 
+// grid (nseg, rows): histogram of the block keys' top 12 bits, per row.  Each
+// workgroup counts seg_len consecutive keys of its row in LDS and adds its
+// non-empty bins to the row's histogram (zeroed beforehand); keys of 0 (blocks
+// without a valid column) are not counted.
+__global__ __launch_bounds__(kThreads) void block_key_hist_kernel(const uint32_t* bkeys, int64_t nbk_row, int seg_len,
+                                                                  uint32_t* hist) {
+    __shared__ uint32_t h[4096];
+    const int r = blockIdx.y;
+    for (int b = threadIdx.x; b < 4096; b += kThreads) h[b] = 0u;
+    __syncthreads();
+    const int64_t i0 = (int64_t)blockIdx.x * seg_len;
+    const int64_t i1 = i0 + seg_len < nbk_row ? i0 + seg_len : nbk_row;
+    const uint32_t* row = bkeys + (int64_t)r * nbk_row;
+    for (int64_t i = i0 + threadIdx.x; i < i1; i += kThreads) {
+        const uint32_t k = row[i];
+        if (k != 0u) atomicAdd(&h[k >> 20], 1u);
+    }
+    __syncthreads();
+    uint32_t* g = hist + (int64_t)r * 4096;
+    for (int b = threadIdx.x; b < 4096; b += kThreads)
+        if (h[b]) atomicAdd(&g[b], h[b]);
+}
+
+__global__ __launch_bounds__(256) void hist_zero_kernel(uint32_t* h, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) h[i] = 0u;
+}
+
+hipError_t launch_block_key_hist(const uint32_t* bkeys, int64_t nbk_row, int rows, uint32_t* hist, hipStream_t stream) {
+    const int64_t nh = (int64_t)rows * 4096;
+    hipLaunchKernelGGL(hist_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)), dim3(256),
+                       0, stream, hist, nh);
+    const int seg_len = 4096;
+    const dim3 grid((unsigned)((nbk_row + seg_len - 1) / seg_len), (unsigned)rows);
+    hipLaunchKernelGGL(block_key_hist_kernel, grid, dim3(kThreads), 0, stream, bkeys, nbk_row, seg_len, hist);
+    return hipGetLastError();
+}
+
 hipError_t launch_topk_threshold(const TopkParams& p, int rows, const uint32_t* key_hist, uint32_t* b1,
                                  hipStream_t stream) {
     hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, key_hist, b1);

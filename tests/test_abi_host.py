@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(csa2.EXPORTED)
-    assert csa2.ABI_VERSION == 5
+    assert csa2.ABI_VERSION == 6
 
 
 def test_struct_layouts_match_c_compiler():
@@ -120,17 +120,20 @@ def test_indexer_block_max_rules():
 def test_score_free_mode_rules():
     ptr = ctypes.c_void_p(0x1000)
     fp8 = dict(q_dtype=csa2.FP8_E4M3, k_dtype=csa2.FP8_E4M3, k_scale=ptr, width=1 << 20)
-    # score-free needs FULL, key_hist and block_keys, and the FP8 64 x 128 kernel
-    a = _index_args(scores=None, key_hist=ptr, **fp8)
+    # score-free needs FULL and block_keys (and no key_hist: the select counts the block keys), and a
+    # quantised 64 x 128 plane
+    a = _index_args(scores=None, **fp8)
     assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
-    a = _index_args(scores=None, block_keys=ptr, **fp8)
+    a = _index_args(scores=None, key_hist=ptr, block_keys=ptr, **fp8)
     assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
-    a = _index_args(scores=None, key_hist=ptr, block_keys=ptr, mode=csa2.MODE_REINDEX, cand=ptr, n_blocks=2048,
+    a = _index_args(scores=None, block_keys=ptr, rows=0, **fp8)
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.OK
+    a = _index_args(scores=None, block_keys=ptr, mode=csa2.MODE_REINDEX, cand=ptr, n_blocks=2048,
                     block_rows=8, **dict(fp8, width=16384))
     assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
-    a = _index_args(scores=None, key_hist=ptr, block_keys=ptr, width=1 << 20)     # bf16
+    a = _index_args(scores=None, block_keys=ptr, width=1 << 20)     # bf16
     assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_UNSUPPORTED
-    a = _index_args(scores=None, key_hist=ptr, block_keys=ptr, **dict(fp8, width=1 << 24))
+    a = _index_args(scores=None, block_keys=ptr, **dict(fp8, width=1 << 24))
     assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_UNSUPPORTED
     # block keys are only written in score-free mode
     a = _index_args(block_keys=ptr, key_hist=ptr, **fp8)
@@ -155,13 +158,13 @@ def test_mxfp4_indexer_rules():
     a = _index_args(q_dtype=csa2.FP8_E4M3, k_dtype=csa2.FP8_E4M3, k_scale=ptr, q_scale_e8m0=ptr)
     assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
     # score-free mode and the re-scoring select take MXFP4 like FP8
-    a = _index_args(scores=None, key_hist=ptr, block_keys=ptr, rows=0, **fp4)
+    a = _index_args(scores=None, block_keys=ptr, rows=0, **fp4)
     assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.OK
-    a = _index_args(scores=None, key_hist=ptr, block_keys=ptr, **fp4)
+    a = _index_args(scores=None, block_keys=ptr, **fp4)
     ws = csa2.topk_rescore_workspace_size(a.rows, a.width, 512)
     assert csa2._lib.csa2_topk_rescore(ctypes.byref(a), 512, ptr, ctypes.c_void_p(0x10000), ws - 1, None) == \
         csa2.ERR_WORKSPACE
-    a = _index_args(scores=None, key_hist=ptr, block_keys=ptr, **dict(fp4, k_scale_e8m0=None))
+    a = _index_args(scores=None, block_keys=ptr, **dict(fp4, k_scale_e8m0=None))
     assert csa2._lib.csa2_topk_rescore(ctypes.byref(a), 512, ptr, ctypes.c_void_p(0x10000), ws, None) == \
         csa2.ERR_INVALID_ARG
 
@@ -172,12 +175,12 @@ def test_mxfp4_indexer_rules():
     (dict(width=4000), 512, csa2.ERR_UNSUPPORTED),          # narrow rows: no wide-row plan
     (dict(rows=2000), 512, csa2.ERR_UNSUPPORTED),           # many rows: one workgroup per row instead
     (dict(mode=csa2.MODE_REINDEX), 512, csa2.ERR_INVALID_ARG),
-    (dict(key_hist=None), 512, csa2.ERR_INVALID_ARG),
+    (dict(key_hist=ctypes.c_void_p(0x1000)), 512, csa2.ERR_INVALID_ARG),
     (dict(block_keys=None), 512, csa2.ERR_INVALID_ARG),
 ])
 def test_topk_rescore_validation(kw, k, status):
     ptr = ctypes.c_void_p(0x1000)
-    base = dict(q_dtype=csa2.FP8_E4M3, k_dtype=csa2.FP8_E4M3, k_scale=ptr, width=1 << 20, scores=None, key_hist=ptr,
+    base = dict(q_dtype=csa2.FP8_E4M3, k_dtype=csa2.FP8_E4M3, k_scale=ptr, width=1 << 20, scores=None,
                 block_keys=ptr)
     base.update(kw)
     a = _index_args(**base)
@@ -189,7 +192,7 @@ def test_topk_rescore_validation(kw, k, status):
 def test_topk_rescore_workspace_rules():
     ptr = ctypes.c_void_p(0x1000)
     a = _index_args(q_dtype=csa2.FP8_E4M3, k_dtype=csa2.FP8_E4M3, k_scale=ptr, width=1 << 20, scores=None,
-                    key_hist=ptr, block_keys=ptr)
+                    block_keys=ptr)
     ws = csa2.topk_rescore_workspace_size(4, 1 << 20, 512)
     assert ws >= 2 * 4 * (1 << 20) * 4                      # full-capacity candidate lists
     assert csa2._lib.csa2_topk_rescore(ctypes.byref(a), 512, ptr, ctypes.c_void_p(0x10000), ws - 1, None) == \

@@ -86,16 +86,15 @@ class Step:
         idx_common = (x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, tau_i)
         if score_free:
             self.scores = None
-            self.key_hist = torch.empty(rows, 4096, dtype=torch.int32, device=dev)
+            self.key_hist = None
             self.block_keys = torch.empty(rows, -(-cfg.width // 8), dtype=torch.int32, device=dev)
             # the pool's block scores come from the block keys: no block_max pass
             self.block_max = None
-            call_idx = csa2.prepare_indexer_score(*idx_common, None, width=cfg.width, key_hist=self.key_hist,
-                                                  block_keys=self.block_keys, **ikw)
+            call_idx = csa2.prepare_indexer_score(*idx_common, None, width=cfg.width, block_keys=self.block_keys,
+                                                  **ikw)
             rkw = dict(ikw)
             rkw.pop("fp8", None)
-            call_topk = csa2.prepare_topk_rescore(*idx_common, self.idx, self.key_hist, self.block_keys, cfg.width,
-                                                  **rkw)
+            call_topk = csa2.prepare_topk_rescore(*idx_common, self.idx, self.block_keys, cfg.width, **rkw)
         else:
             self.scores = torch.empty(rows, cfg.width, dtype=torch.float32, device=dev)
             # the indexer also builds the score-key histogram when top-k takes its wide-row path
