@@ -143,8 +143,9 @@ size_t csa2_topk_rescore_workspace_size(int32_t rows, int64_t width, int32_t k) 
     rescore_plan(rows, width, chunk, nseg);
     if (nseg == 0) return 0;
     const size_t lists = (size_t)rows * nseg * chunk;
+    const size_t parts = (size_t)csa2::block_key_hist_parts((width + 7) / 8);
     return align256((size_t)rows * 4) + align256((size_t)rows * nseg * 4) + 2 * align256(lists * 4) +
-           align256((size_t)rows * 4096 * 4);
+           align256((size_t)rows * parts * 4096 * 4);
 }
 
 int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, void* workspace, size_t workspace_bytes,
@@ -191,7 +192,8 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
     uint32_t* hist = reinterpret_cast<uint32_t*>(w);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = csa2::launch_block_key_hist(a->block_keys, (a->width + 7) / 8, a->rows, hist, st);
-    if (e == hipSuccess) e = csa2::launch_topk_threshold(tp, a->rows, hist, b1, st);
+    if (e == hipSuccess)
+        e = csa2::launch_topk_threshold(tp, a->rows, hist, csa2::block_key_hist_parts((a->width + 7) / 8), b1, st);
     if (e == hipSuccess)
         e = csa2::launch_indexer_rescore(ip, a->rows, a->k_dtype, b1, chunk, nseg, keys, cols, seg_count, st);
     if (e == hipSuccess) e = csa2::launch_topk_final(tp, a->rows, keys, cols, seg_count, nseg, chunk, st);

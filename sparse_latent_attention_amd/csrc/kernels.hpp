@@ -62,8 +62,11 @@ hipError_t launch_topk_select(const TopkParams& p, int rows, void* workspace, hi
 // of the k-th key from a key histogram, and the exact select over per-segment
 // (key, column) lists of capacity cap (a longer list falls back to p.scores).
 void topk_plan(int rows, int64_t width, int& chunk, int& nseg, int min_chunk);
+// Per-row histograms of block keys' top 12 bits as [rows, parts, 4096] partial
+// counts (parts = block_key_hist_parts(nbk_row)).
+int block_key_hist_parts(int64_t nbk_row);
 hipError_t launch_block_key_hist(const uint32_t* bkeys, int64_t nbk_row, int rows, uint32_t* hist, hipStream_t stream);
-hipError_t launch_topk_threshold(const TopkParams& p, int rows, const uint32_t* key_hist, uint32_t* b1,
+hipError_t launch_topk_threshold(const TopkParams& p, int rows, const uint32_t* key_hist, int parts, uint32_t* b1,
                                  hipStream_t stream);
 hipError_t launch_topk_final(const TopkParams& p, int rows, const uint32_t* cand_keys, const int32_t* cand_cols,
                              const uint32_t* seg_count, int nseg, int cap, hipStream_t stream);

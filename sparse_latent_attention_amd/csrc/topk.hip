@@ -330,11 +330,18 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const TopkParams p,
 }
 
 // grid rows: bin of the k-th largest key (0 when every valid key is selected).
+// hist holds `parts` histograms per row ([rows, parts, 4096]); they are added
+// in order.
 __global__ __launch_bounds__(kThreads) void topk_threshold_kernel(const TopkParams p, const uint32_t* hist,
-                                                                  uint32_t* b1_out) {
+                                                                  uint32_t* b1_out, int parts) {
     __shared__ Lds s;
     const int r = blockIdx.x;
-    for (int b = threadIdx.x; b < 4096; b += kThreads) s.hist[b] = hist[(int64_t)r * 4096 + b];
+    for (int b = threadIdx.x; b < 4096; b += kThreads) {
+        const uint32_t* hr = hist + (int64_t)r * parts * 4096 + b;
+        uint32_t v = 0u;
+        for (int q = 0; q < parts; ++q) v += hr[(int64_t)q * 4096];
+        s.hist[b] = v;
+    }
     __syncthreads();
     const uint32_t total = hist_total(s);
     uint32_t b1 = 0, above = 0;
@@ -533,7 +540,7 @@ hipError_t launch_topk_select(const TopkParams& p, int rows, void* ws, hipStream
                                 stream, p, hist, chunk);
         h = hist;
     }
-    hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, h, b1);
+    hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, h, b1, 1);
     if (pool) {
         hipLaunchKernelGGL(topk_filter_kernel<true>, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0, stream, p,
                            b1, keys, cols, seg_count, chunk, nseg);
@@ -549,45 +556,57 @@ hipError_t launch_topk_select(const TopkParams& p, int rows, void* ws, hipStream
 }
 
 // grid (nseg, rows): histogram of the block keys' top 12 bits, per row.  Each
-// workgroup counts seg_len consecutive keys of its row in LDS and adds its
-// non-empty bins to the row's histogram (zeroed beforehand); keys of 0 (blocks
-// without a valid column) are not counted.
-__global__ __launch_bounds__(kThreads) void block_key_hist_kernel(const uint32_t* bkeys, int64_t nbk_row, int seg_len,
-                                                                  uint32_t* hist) {
+// workgroup counts seg_len consecutive keys of its row in LDS and writes all
+// 4096 bins to its own slot hist[(r * nseg + seg) * 4096 ...] (no atomics, no
+// zeroing; topk_threshold_kernel adds the slots).  Keys of 0 (blocks without a
+// valid column) are not counted.
+template <int NT, bool VEC>
+__global__ __launch_bounds__(NT) void block_key_hist_kernel(const uint32_t* bkeys, int64_t nbk_row, int seg_len,
+                                                            uint32_t* hist) {
     __shared__ uint32_t h[4096];
     const int r = blockIdx.y;
-    for (int b = threadIdx.x; b < 4096; b += kThreads) h[b] = 0u;
+    for (int b = threadIdx.x; b < 4096; b += NT) h[b] = 0u;
     __syncthreads();
     const int64_t i0 = (int64_t)blockIdx.x * seg_len;
     const int64_t i1 = i0 + seg_len < nbk_row ? i0 + seg_len : nbk_row;
     const uint32_t* row = bkeys + (int64_t)r * nbk_row;
-    for (int64_t i = i0 + threadIdx.x; i < i1; i += kThreads) {
-        const uint32_t k = row[i];
-        if (k != 0u) atomicAdd(&h[k >> 20], 1u);
+    if (VEC) {  // 16-byte loads: the segment and the row are multiples of 4 keys, 16-byte aligned
+        for (int64_t i = i0 + 4 * threadIdx.x; i < i1; i += 4 * NT) {
+            const u32x4 k = *reinterpret_cast<const u32x4*>(row + i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (k[e] != 0u) atomicAdd(&h[k[e] >> 20], 1u);
+        }
+    } else {
+        for (int64_t i = i0 + threadIdx.x; i < i1; i += NT) {
+            const uint32_t k = row[i];
+            if (k != 0u) atomicAdd(&h[k >> 20], 1u);
+        }
     }
     __syncthreads();
-    uint32_t* g = hist + (int64_t)r * 4096;
-    for (int b = threadIdx.x; b < 4096; b += kThreads)
-        if (h[b]) atomicAdd(&g[b], h[b]);
+    uint32_t* g = hist + ((int64_t)r * gridDim.x + blockIdx.x) * 4096;
+    for (int b = threadIdx.x; b < 4096; b += NT) g[b] = h[b];
 }
 
-__global__ __launch_bounds__(256) void hist_zero_kernel(uint32_t* h, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) h[i] = 0u;
-}
+constexpr int kBkhThreads = 1024;
+constexpr int kBkhSeg = 16384;
+
+int block_key_hist_parts(int64_t nbk_row) { return (int)((nbk_row + kBkhSeg - 1) / kBkhSeg); }
 
 hipError_t launch_block_key_hist(const uint32_t* bkeys, int64_t nbk_row, int rows, uint32_t* hist, hipStream_t stream) {
-    const int64_t nh = (int64_t)rows * 4096;
-    hipLaunchKernelGGL(hist_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)), dim3(256),
-                       0, stream, hist, nh);
-    const int seg_len = 4096;
-    const dim3 grid((unsigned)((nbk_row + seg_len - 1) / seg_len), (unsigned)rows);
-    hipLaunchKernelGGL(block_key_hist_kernel, grid, dim3(kThreads), 0, stream, bkeys, nbk_row, seg_len, hist);
+    const dim3 grid((unsigned)((nbk_row + kBkhSeg - 1) / kBkhSeg), (unsigned)rows);
+    if (nbk_row % 4 == 0 && reinterpret_cast<uintptr_t>(bkeys) % 16 == 0)
+        hipLaunchKernelGGL((block_key_hist_kernel<kBkhThreads, true>), grid, dim3(kBkhThreads), 0, stream, bkeys, nbk_row,
+                           kBkhSeg, hist);
+    else
+        hipLaunchKernelGGL((block_key_hist_kernel<kBkhThreads, false>), grid, dim3(kBkhThreads), 0, stream, bkeys,
+                           nbk_row, kBkhSeg, hist);
     return hipGetLastError();
 }
 
-hipError_t launch_topk_threshold(const TopkParams& p, int rows, const uint32_t* key_hist, uint32_t* b1,
+hipError_t launch_topk_threshold(const TopkParams& p, int rows, const uint32_t* key_hist, int parts, uint32_t* b1,
                                  hipStream_t stream) {
-    hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, key_hist, b1);
+    hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, key_hist, b1, parts);
     return hipGetLastError();
 }
 
