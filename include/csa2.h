@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 6
+#define CSA2_ABI_VERSION 7
 
 /* Status codes. */
 #define CSA2_OK 0
@@ -121,7 +121,16 @@ const char* csa2_status_string(int32_t status);
  *
  * Supported: (heads, dim) in {(4, 32), (64, 128)}; q_dtype == k_dtype in
  * {F32, BF16, FP8_E4M3}, or FP4_E2M1 as above.  rows * width fits in int64.
+ *
+ * flags: CSA2_INDEX_SHARED_PLANE (FULL only) is the caller's statement that
+ * row_base holds one value in every row (the query tokens of a prefill chunk
+ * of one sequence all index that sequence's compressed rows).  The library
+ * may then read row_base[0] only and stage each key tile once for several
+ * query rows (BF16 planes of 64 x 128 without key_hist or block_max); the
+ * scores are bit-identical to those of the same call without the flag.
+ * Other bits must be 0.
  */
+#define CSA2_INDEX_SHARED_PLANE 1
 typedef struct csa2_index_args {
     uint32_t struct_size;       /* sizeof(csa2_index_args) */
     int32_t mode;               /* CSA2_MODE_FULL | CSA2_MODE_REINDEX */
@@ -134,7 +143,7 @@ typedef struct csa2_index_args {
     int32_t n_blocks;           /* REINDEX: candidate blocks per row (ignored for FULL) */
     int32_t block_rows;         /* REINDEX: rows per candidate block, 1..64.  FULL with block_max:
                                  * rows per pooled block, a power of two in 4..64.  Else ignored. */
-    int32_t _pad0;
+    int32_t flags;              /* CSA2_INDEX_SHARED_PLANE or 0 */
     int64_t width;              /* columns per score row (FULL: >= every n_visible) */
     const void* q;              /* [rows, heads, dim] */
     const float* w;             /* [rows, heads] effective head weights */

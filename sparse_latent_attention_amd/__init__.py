@@ -40,7 +40,7 @@ _i32, _i64, _u32, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes
 class IndexArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", _u32), ("mode", _i32), ("rows", _i32), ("heads", _i32), ("dim", _i32), ("ratio", _i32),
-        ("q_dtype", _i32), ("k_dtype", _i32), ("n_blocks", _i32), ("block_rows", _i32), ("_pad0", _i32),
+        ("q_dtype", _i32), ("k_dtype", _i32), ("n_blocks", _i32), ("block_rows", _i32), ("flags", _i32),
         ("width", _i64), ("q", _vp), ("w", _vp), ("k", _vp), ("k_scale", _vp), ("row_base", _vp), ("pos", _vp),
         ("cand", _vp), ("scale", _f32), ("_pad1", _i32), ("scores", _vp), ("key_hist", _vp), ("block_max", _vp),
         ("block_keys", _vp), ("q_scale_e8m0", _vp), ("k_scale_e8m0", _vp),
@@ -246,9 +246,12 @@ def _index_args(q, w, k, row_base, pos, ratio, scale, scores, width, k_scale, ca
     return a
 
 
+INDEX_SHARED_PLANE = 1
+
+
 def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None, cand=None, block_rows=8,
                   fp8=False, fp4=False, q_scale=None, key_hist=None, block_max=None, block_keys=None, width=None,
-                  stream=None):
+                  shared_plane=False, stream=None):
     """Fills ``scores`` [rows, width] (float32).  REINDEX when ``cand`` is given.
 
     q [rows, H_I, D_I] and k [*, D_I] are float32/bfloat16, or uint8 FP8-E4M3
@@ -262,9 +265,13 @@ def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None,
     optionally receives the candidate pool's block scores.  ``scores=None``
     (with ``width`` and ``block_keys`` int32 [rows, ceil(width / 8)], no
     ``key_hist``) selects the score-free mode whose top-k ``topk_rescore`` takes.
+    ``shared_plane=True`` (FULL only) states that every row reads the plane rows of
+    ``row_base[0]`` (a prefill chunk of one sequence); the library may then stage
+    key tiles once for several rows (same results).
     """
     a = _index_args(q, w, k, row_base, pos, ratio, scale, scores, width, k_scale, cand, block_rows, fp8, key_hist,
                     block_max, block_keys, fp4, q_scale)
+    a.flags = INDEX_SHARED_PLANE if shared_plane else 0
     _check("csa2_indexer_score", _lib.csa2_indexer_score(ctypes.byref(a), _stream(stream)))
     return scores
 

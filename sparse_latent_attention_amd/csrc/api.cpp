@@ -81,6 +81,7 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
     if (a->q_dtype != a->k_dtype || elem_bytes(a->k_dtype) == 0) return CSA2_ERR_UNSUPPORTED;
     if (!csa2::indexer_supported(a->heads, a->dim, a->k_dtype)) return CSA2_ERR_UNSUPPORTED;
     const bool reindex = a->mode == CSA2_MODE_REINDEX;
+    if ((a->flags & ~CSA2_INDEX_SHARED_PLANE) != 0 || (reindex && a->flags != 0)) return CSA2_ERR_INVALID_ARG;
     if (a->k_dtype == CSA2_FP4_E2M1 && reindex) return CSA2_ERR_UNSUPPORTED;
     if (reindex) {
         if (a->cand == nullptr || a->n_blocks <= 0 || a->block_rows <= 0 || a->block_rows > 64) return CSA2_ERR_INVALID_ARG;
@@ -114,6 +115,7 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
     p.cand = reindex ? a->cand : nullptr; p.scores = a->scores; p.key_hist = a->key_hist; p.width = a->width;
     p.n_blocks = reindex ? a->n_blocks : 0; p.block_rows = reindex ? a->block_rows : 1; p.ratio = a->ratio;
     p.scale = a->scale;
+    p.shared_plane = (a->flags & CSA2_INDEX_SHARED_PLANE) != 0;
     p.block_max = reindex ? nullptr : a->block_max;
     p.block_keys = score_free ? a->block_keys : nullptr;
     p.bm_rows = p.block_max != nullptr ? a->block_rows : 4;
@@ -153,7 +155,7 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
     if (a == nullptr || a->struct_size < sizeof(csa2_index_args)) return CSA2_ERR_INVALID_ARG;
     if (a->mode != CSA2_MODE_FULL || a->rows < 0 || a->width < 0 || (a->ratio != 1 && a->ratio != 2))
         return CSA2_ERR_INVALID_ARG;
-    if (k < 1 || k > 2048) return CSA2_ERR_INVALID_ARG;
+    if (k < 1 || k > 2048 || (a->flags & ~CSA2_INDEX_SHARED_PLANE) != 0) return CSA2_ERR_INVALID_ARG;
     if (a->q_dtype != a->k_dtype || !csa2::indexer_rescore_supported(a->heads, a->dim, a->k_dtype))
         return CSA2_ERR_UNSUPPORTED;
     if (a->rows == 0) return CSA2_OK;
@@ -174,7 +176,7 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
     ip.q_e8 = a->q_scale_e8m0; ip.k_e8 = a->k_scale_e8m0;
     ip.cand = nullptr; ip.scores = nullptr; ip.key_hist = nullptr; ip.block_max = nullptr;
     ip.block_keys = a->block_keys; ip.width = a->width; ip.cols_per_wg = 0; ip.bm_blocks = 0; ip.n_blocks = 0;
-    ip.block_rows = 1; ip.bm_rows = 4; ip.ratio = a->ratio; ip.scale = a->scale;
+    ip.block_rows = 1; ip.bm_rows = 4; ip.ratio = a->ratio; ip.scale = a->scale; ip.shared_plane = false;
     csa2::TopkParams tp;
     tp.scores = nullptr; tp.pos = a->pos; tp.cand = nullptr; tp.out = out; tp.key_hist = nullptr;
     tp.width = a->width; tp.k = k; tp.ratio = a->ratio; tp.n_blocks = 0; tp.block_rows = 1; tp.col_group = 1;

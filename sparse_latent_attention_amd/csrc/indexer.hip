@@ -294,6 +294,118 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// FULL rows that share one BF16 plane (64 heads x 128), as in a prefill chunk.
+// Every row reads the same key rows, so a workgroup of 8 waves takes 8 query
+// rows -- one per wave, its 64 heads x 128 held in registers as A operands as
+// in indexer_score_kernel -- and streams its column range through LDS in
+// stages of 64 key rows: each stage is read from memory once and feeds all 8
+// rows (indexer_score_kernel re-reads every key row for every query row).
+// Consecutive workgroup ids take consecutive row groups of one column range,
+// so the workgroups resident together share that range's key rows in L2.
+// Per column the arithmetic is that of indexer_score_kernel (the same MFMA
+// chains and head reduction), so the scores are identical.
+constexpr int kChunkRows = 8;       // query rows per workgroup, one per wave
+constexpr int kChunkKeys = 64;      // key rows per LDS stage
+constexpr int kChunkStride = 272;   // LDS bytes per staged key row (256 + 16: the 16 rows a B-operand read
+                                    // touches start in distinct bank groups)
+
+__global__ __launch_bounds__(512) void indexer_chunk_kernel(const IndexParams p, int rows) {
+    typedef IdxOps<CSA2_BF16, 128> Ops;
+    typedef Ops::Frag Frag;
+    constexpr int HT = 4, S = Ops::kSteps;
+    __shared__ __attribute__((aligned(16))) uint8_t tile[2][kChunkKeys * kChunkStride];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, li = lane & 15;
+    const int r0 = blockIdx.x * kChunkRows;
+    const int r = r0 + wave;
+    const bool live = r < rows;
+    const int rq = live ? r : rows - 1;  // an idle wave (past the last row) still stages tiles
+    const int64_t base = p.row_base[0];
+    const int64_t nv = (p.pos[rq] + 1) / p.ratio;
+    int64_t nvg = 0;  // columns some row of the group sees
+    for (int j = 0; j < kChunkRows; ++j) {
+        const int64_t v = (p.pos[min(r0 + j, rows - 1)] + 1) / p.ratio;
+        nvg = v > nvg ? v : nvg;
+    }
+    const int64_t c0 = (int64_t)blockIdx.y * p.cols_per_wg;
+    const int64_t c1 = c0 + p.cols_per_wg < p.width ? c0 + p.cols_per_wg : p.width;
+    const int64_t c_live = nvg < c1 ? nvg : c1;
+    float* srow = p.scores + (int64_t)rq * p.width;
+
+    Frag qa[HT][S];
+    float wr[HT][4];
+#pragma unroll
+    for (int t = 0; t < HT; ++t) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) qa[t][s] = Ops::load(p.q, (int64_t)rq * 64 + 16 * t + li, s, g);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) wr[t][rr] = p.w[(int64_t)rq * 64 + 16 * t + 4 * g + rr];
+    }
+
+    // Staging: thread i copies bytes 32 (i % 8) .. +31 of key row i / 8 of the stage
+    // (zeros past the visible columns).
+    const int lk = threadIdx.x >> 3, lp = threadIdx.x & 7;
+    auto fetch = [&](int64_t cs, u32x4& x0, u32x4& x1) {
+        const int64_t c = cs + lk;
+        x0 = x1 = u32x4{0u, 0u, 0u, 0u};
+        if (c < c_live) {
+            const uint8_t* src = reinterpret_cast<const uint8_t*>(p.k) + (base + c) * 256 + 32 * lp;
+            x0 = ld16(src);
+            x1 = ld16(src + 16);
+        }
+    };
+    auto put = [&](int b, const u32x4& x0, const u32x4& x1) {
+        uint8_t* dst = tile[b] + lk * kChunkStride + 32 * lp;
+        *reinterpret_cast<u32x4*>(dst) = x0;
+        *reinterpret_cast<u32x4*>(dst + 16) = x1;
+    };
+
+    int64_t cs = c0;
+    int b = 0;
+    if (cs < c_live) {
+        u32x4 x0, x1;
+        fetch(cs, x0, x1);
+        put(0, x0, x1);
+    }
+    __syncthreads();
+    for (; cs < c_live; cs += kChunkKeys) {
+        // the next stage's loads are in flight while this stage is computed
+        const bool more = cs + kChunkKeys < c_live;
+        u32x4 x0, x1;
+        if (more) fetch(cs + kChunkKeys, x0, x1);
+        if (live) {
+            const uint8_t* tb = tile[b];
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                Frag kb[S];
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+                    kb[s] = __builtin_bit_cast(
+                        Frag, *reinterpret_cast<const u32x4*>(tb + (16 * u + li) * kChunkStride + 64 * s + 16 * g));
+                float acc_sum = 0.f;
+#pragma unroll
+                for (int t = 0; t < HT; ++t) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < S; ++s) acc = Ops::mma(acc, qa[t][s], kb[s]);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) acc_sum += wr[t][rr] * relu_bits(acc[rr]);
+                }
+                v[u] = acc_sum;
+            }
+            const int64_t c_out = cs + lane;
+            store_step<false, false>(p, rq, nv, cs, c1, lane, v, p.scale, c_out < c1 && c_out < nv, srow, nullptr);
+        }
+        if (more) put(b ^ 1, x0, x1);
+        __syncthreads();
+        b ^= 1;
+    }
+    if (live)
+        for (; cs < c1; cs += 64) store_invisible<false>(p, rq, cs, c1, lane, srow);  // nothing visible here
+}
+
 // Steps of key-row loads each wave keeps in flight in the streaming FULL
 // kernels, and the most 64-column steps one wave makes (a workgroup covers
 // <= 4096 columns).
@@ -712,8 +824,26 @@ static hipError_t launch_stream_full(const IndexParams& p, int rows, hipStream_t
     return hipGetLastError();
 }
 
+// Rows sharing one BF16 plane, scores only (no histogram, no block scores).
+static bool chunk_path(const IndexParams& p, int rows, int heads, int dim, int dtype, bool reindex) {
+    return p.shared_plane && !reindex && heads == 64 && dim == 128 && dtype == CSA2_BF16 && rows >= kChunkRows &&
+           p.scores != nullptr && p.key_hist == nullptr && p.block_max == nullptr && p.block_keys == nullptr;
+}
+
+static hipError_t launch_chunk(IndexParams p, int rows, hipStream_t stream) {
+    // 8192 columns per workgroup, more when the grid's second dimension (<= 65535) needs it
+    int64_t cw = 8192;
+    const int64_t need = (p.width + 65534) / 65535;
+    if (need > cw) cw = (need + kChunkKeys - 1) / kChunkKeys * kChunkKeys;
+    p.cols_per_wg = cw;
+    const dim3 grid((unsigned)((rows + kChunkRows - 1) / kChunkRows), (unsigned)((p.width + cw - 1) / cw));
+    hipLaunchKernelGGL(indexer_chunk_kernel, grid, dim3(64 * kChunkRows), 0, stream, p, rows);
+    return hipGetLastError();
+}
+
 hipError_t launch_indexer_score(const IndexParams& p, int rows, int heads, int dim, int dtype, bool reindex,
                                 hipStream_t stream) {
+    if (chunk_path(p, rows, heads, dim, dtype, reindex)) return launch_chunk(p, rows, stream);
     if (heads == 64 && dim == 128) {
         if (dtype == CSA2_BF16) return reindex ? launch_one<CSA2_BF16, 64, 128, true>(p, rows, stream)
                                                : launch_one<CSA2_BF16, 64, 128, false>(p, rows, stream);

@@ -30,6 +30,7 @@ struct IndexParams {
     int32_t bm_rows;     // rows per pooled block (power of two, 4..64)
     int32_t ratio;
     float scale;
+    bool shared_plane;   // every row reads the plane rows of row_base[0]
 };
 
 hipError_t launch_indexer_score(const IndexParams& p, int rows, int heads, int dim, int dtype, bool reindex,

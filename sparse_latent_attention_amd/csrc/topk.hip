@@ -334,19 +334,45 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const TopkParams p,
 // in order.
 __global__ __launch_bounds__(kThreads) void topk_threshold_kernel(const TopkParams p, const uint32_t* hist,
                                                                   uint32_t* b1_out, int parts) {
+    static_assert(4 * kThreads == 4096, "four bins per thread");
     __shared__ Lds s;
-    const int r = blockIdx.x;
-    for (int b = threadIdx.x; b < 4096; b += kThreads) {
-        const uint32_t* hr = hist + (int64_t)r * parts * 4096 + b;
-        uint32_t v = 0u;
-        for (int q = 0; q < parts; ++q) v += hr[(int64_t)q * 4096];
-        s.hist[b] = v;
+    const int r = blockIdx.x, t = threadIdx.x;
+    // Thread t adds bins t + 1024e (e < 4) over the parts, eight parts' loads in
+    // flight at once (a part index past the end re-reads the last part, whose
+    // values are then dropped).
+    const uint32_t* hr = hist + (int64_t)r * parts * 4096 + t;
+    uint32_t acc[4] = {0u, 0u, 0u, 0u};
+    for (int q0 = 0; q0 < parts; q0 += 8) {
+        uint32_t v[8][4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t q = q0 + j < parts ? q0 + j : parts - 1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[j][e] = hr[q * 4096 + e * kThreads];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += q0 + j < parts ? v[j][e] : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s.hist[e * kThreads + t] = acc[e];
+    __syncthreads();
+    // One suffix scan over the threads' four-bin groups gives both the total
+    // and, for the group that holds it, the bin where the count from the top
+    // reaches k.
+    const uint32_t need = (uint32_t)p.k;
+    const uint32_t h0 = s.hist[4 * t], h1 = s.hist[4 * t + 1], h2 = s.hist[4 * t + 2], h3 = s.hist[4 * t + 3];
+    uint32_t above = block_suffix_excl(h0 + h1 + h2 + h3, s);
+    if (t == 0) s.sel[1] = above + h0 + h1 + h2 + h3;
+    const uint32_t hv[4] = {h0, h1, h2, h3};
+#pragma unroll
+    for (int b = 3; b >= 0; --b) {
+        if (above < need && above + hv[b] >= need) s.sel[0] = (uint32_t)(4 * t + b);
+        above += hv[b];
     }
     __syncthreads();
-    const uint32_t total = hist_total(s);
-    uint32_t b1 = 0, above = 0;
-    if (total > (uint32_t)p.k) find_bin(s, 4096, (uint32_t)p.k, b1, above);
-    if (threadIdx.x == 0) b1_out[r] = b1;
+    if (t == 0) b1_out[r] = s.sel[1] > need ? s.sel[0] : 0u;
 }
 
 // grid (nseg, rows): ordered compaction of the chunk's keys with bin >= b1.

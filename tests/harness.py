@@ -85,8 +85,10 @@ def gpu_scores(cfg, x, key_hist=None, block_max=None):
     rows = x["pos"].shape[0]
     scores = torch.empty(rows, cfg.width, dtype=torch.float32, device=x["pos"].device)
     kI, ikw = index_plane_args(cfg, x)
+    # a prefill chunk's rows share one plane (row_base is 0 for every row)
     csa2.indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, index_scale(cfg), scores,
-                       cand=x.get("cand"), block_rows=cfg.block_rows, key_hist=key_hist, block_max=block_max, **ikw)
+                       cand=x.get("cand"), block_rows=cfg.block_rows, key_hist=key_hist, block_max=block_max,
+                       shared_plane=cfg.phase == "prefill", **ikw)
     return scores
 
 

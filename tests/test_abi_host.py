@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(csa2.EXPORTED)
-    assert csa2.ABI_VERSION == 6
+    assert csa2.ABI_VERSION == 7
 
 
 def test_struct_layouts_match_c_compiler():
@@ -92,6 +92,8 @@ def _index_args(**kw):
     ("q", None, csa2.ERR_INVALID_ARG),
     ("k_scale", ctypes.c_void_p(0x1000), csa2.ERR_INVALID_ARG),
     ("scale", float("nan"), csa2.ERR_INVALID_ARG),
+    ("flags", 2, csa2.ERR_INVALID_ARG),
+    ("flags", -1, csa2.ERR_INVALID_ARG),
 ])
 def test_indexer_validation(field, value, status):
     a = _index_args(**{field: value})
@@ -102,6 +104,15 @@ def test_indexer_reindex_width_must_match_pool():
     a = _index_args(mode=csa2.MODE_REINDEX, cand=ctypes.c_void_p(0x1000), n_blocks=2048, block_rows=8, width=100)
     assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
     a = _index_args(mode=csa2.MODE_REINDEX, cand=None, n_blocks=2048, block_rows=8, width=16384)
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+
+
+def test_indexer_shared_plane_flag_rules():
+    # FULL only; with rows == 0 a valid call returns OK before touching memory
+    a = _index_args(flags=csa2.INDEX_SHARED_PLANE, rows=0)
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.OK
+    a = _index_args(flags=csa2.INDEX_SHARED_PLANE, mode=csa2.MODE_REINDEX, cand=ctypes.c_void_p(0x1000),
+                    n_blocks=4, block_rows=8, width=32)
     assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
 
 

@@ -247,3 +247,44 @@ def test_attention_large_logit_spread(name, kw):
     rows = np.unique(np.linspace(0, cfg.q_tokens - 1, min(cfg.q_tokens, 16)).astype(int))
     ref = oracle_attention(cfg, x, idx.cpu().numpy()[rows], rows)
     assert_close(out[torch.from_numpy(rows).cuda()], ref, BF16_ATOL, BF16_RTOL, f"spread {name}")
+
+
+@pytest.mark.parametrize("rows,width,base", [(37, 9000, 100), (8, 64, 0), (300, 20000, 5), (13, 8300, 0)])
+def test_shared_plane_scores_equal_per_row_path(rows, width, base):
+    """Rows that share one plane (the staged-key-tile path for BF16 64 x 128): bit-identical scores to the
+    per-row path, over ragged row groups (rows not a multiple of 8), ragged column ranges and stages
+    (width not a multiple of 8192 or 64), rows that see nothing (position 0 at ratio 2) and rows that see
+    every column."""
+    import sparse_latent_attention_amd as csa2
+    g = torch.Generator(device="cuda")
+    g.manual_seed(rows * 7 + width)
+    k = (torch.randn(base + width, 128, generator=g, device="cuda") * 0.1).to(torch.bfloat16)
+    q = (torch.randn(rows, 64, 128, generator=g, device="cuda") * 0.1).to(torch.bfloat16)
+    w = torch.randn(rows, 64, generator=g, device="cuda")
+    pos = torch.randint(0, 2 * width + 10, (rows,), generator=g, device="cuda")
+    pos[0] = 0
+    pos[-1] = 2 * width + 5
+    rb = torch.full((rows,), base, dtype=torch.int64, device="cuda")
+    out = {}
+    for shared in (True, False):
+        s = torch.full((rows, width), float("nan"), dtype=torch.float32, device="cuda")
+        csa2.indexer_score(q, w, k, rb, pos, 2, 0.01, s, shared_plane=shared)
+        out[shared] = s
+    torch.cuda.synchronize()
+    assert not torch.isnan(out[True]).any()
+    assert torch.equal(out[True], out[False])
+    nv = ((pos + 1) // 2).clamp(max=width).cpu().numpy()
+    got = out[True].cpu().numpy()
+    for r in range(rows):
+        assert np.all(got[r, nv[r]:] == -np.inf) and np.all(np.isfinite(got[r, :nv[r]]))
+    # spot check against the oracle on a few rows
+    tau = 0.01
+    for r in sorted({0, rows // 2, rows - 1}):
+        n = int(nv[r])
+        if n == 0:
+            continue
+        kk = k[base:base + n].double().cpu().numpy()
+        ref = oracle.indexer.scores_full(q[r:r + 1].double().cpu().numpy(), w[r:r + 1].double().cpu().numpy(),
+                                         lambda i: kk, np.array([2 * n - 1]), 2, tau, n)[0]
+        bound = oracle.indexer.score_abs_bound(q[r].double().cpu().numpy(), w[r].double().cpu().numpy(), kk, tau)
+        assert np.all(np.abs(got[r, :n] - ref) <= SCORE_TOL * bound)

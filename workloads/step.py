@@ -101,9 +101,11 @@ class Step:
             self.key_hist = (torch.empty(rows, 4096, dtype=torch.int32, device=dev)
                              if csa2.topk_uses_key_hist(rows, cfg.width, cfg.topk) else None)
             self.block_keys = None
+            # a prefill chunk's rows all read the sequence's one plane
             call_idx = csa2.prepare_indexer_score(*idx_common, self.scores, cand=x.get("cand"),
                                                   block_rows=cfg.block_rows, key_hist=self.key_hist,
-                                                  block_max=self.block_max, **ikw)
+                                                  block_max=self.block_max, shared_plane=cfg.phase == "prefill",
+                                                  **ikw)
             call_topk = csa2.prepare_topk_select(self.scores, x["pos"], cfg.ratio, self.idx, cand=x.get("cand"),
                                                  block_rows=cfg.block_rows, key_hist=self.key_hist)
         self.groups = {}
