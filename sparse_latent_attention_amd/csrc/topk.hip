@@ -293,13 +293,6 @@ __device__ __forceinline__ RowSrc<POOL> row_src(const TopkParams& p, int r) {
 
 }  // namespace
 
-// One workgroup per row over the full score row.
-template <bool POOL>
-__global__ __launch_bounds__(kThreads) void topk_select_kernel(const TopkParams p) {
-    __shared__ Lds s;
-    const int r = blockIdx.x;
-    select_core(row_src<POOL>(p, r), p, r, s);
-}
 
 // ---- wide-row path ----------------------------------------------------------
 
@@ -381,6 +374,102 @@ __global__ __launch_bounds__(kThreads) void topk_threshold_kernel(const TopkPara
 // sweep (to add up the waves' counts) is the only synchronisation.
 constexpr int kPerLane = 16;
 constexpr int kSweep = kThreads * kPerLane;
+
+// One workgroup per row over the full score row, in two passes over memory.
+// The first counts the valid keys' top 12 bits, which gives the bin b1 of the
+// k-th largest key; the second copies the valid keys in bins >= b1 (in column
+// order) into LDS, where select_core finishes without touching memory again.
+// A row with more than kLdsCand such keys (heavy ties) is selected from
+// memory instead.  Sweeps as in topk_filter_kernel: wave w owns a contiguous
+// 1024-column slice and lane l its columns base + 64j + l (j < 16), whose
+// loads are all in flight before any is used.
+template <bool POOL>
+__global__ __launch_bounds__(kThreads) void topk_select_kernel(const TopkParams p) {
+    __shared__ Lds s;
+    __shared__ uint32_t lkeys[kLdsCand];
+    __shared__ int32_t lcols[kLdsCand];
+    __shared__ uint32_t cnt[2][kWaves];
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const RowSrc<POOL> src = row_src<POOL>(p, r);
+    const int n = src.n;
+    const uint32_t k = (uint32_t)p.k;
+
+    for (int b = tid; b < 4096; b += kThreads) s.hist[b] = 0u;
+    __syncthreads();
+    for (int cs = 0; cs < n; cs += kSweep) {
+        const int wbase = cs + wave * (kSweep / kWaves);
+        uint32_t vals[kPerLane];
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) {
+            const int i = wbase + 64 * j + lane;
+            vals[j] = (i < n) ? src.raw(i) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) {
+            const int i = wbase + 64 * j + lane;
+            if (i < n && col_valid(p, r, i, src.nv)) atomicAdd(&s.hist[src.key_of(vals[j], i) >> 20], 1u);
+        }
+    }
+    __syncthreads();
+    const uint32_t total = hist_total(s);
+    uint32_t b1 = 0, above = 0;
+    if (total > k) find_bin(s, 4096, k, b1, above);
+    const uint32_t n_cand = total > k ? above + s.hist[b1] : total;  // valid keys with bin >= b1
+    __syncthreads();  // every thread has read the histogram
+    if (n_cand > (uint32_t)kLdsCand) {
+        select_core(src, p, r, s);
+        return;
+    }
+    uint32_t n_out = 0;
+    int buf = 0;
+    for (int cs = 0; cs < n && n_out < n_cand; cs += kSweep) {
+        const int wbase = cs + wave * (kSweep / kWaves);
+        uint32_t vals[kPerLane];
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) {
+            const int i = wbase + 64 * j + lane;
+            vals[j] = (i < n) ? src.raw(i) : 0u;
+        }
+        uint32_t keys[kPerLane];
+        uint64_t masks[kPerLane];
+        uint32_t mine = 0;
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) {
+            const int i = wbase + 64 * j + lane;
+            keys[j] = src.key_of(vals[j], i);
+            const bool take = i < n && col_valid(p, r, i, src.nv) && (keys[j] >> 20) >= b1;
+            masks[j] = __ballot(take);
+            mine += (uint32_t)__builtin_popcountll(masks[j]);
+        }
+        if (lane == 0) cnt[buf][wave] = mine;
+        __syncthreads();
+        uint32_t off = n_out, all = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            if (w < wave) off += cnt[buf][w];
+            all += cnt[buf][w];
+        }
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) {
+            const uint64_t m = masks[j];
+            if ((m >> lane) & 1ull) {
+                const uint32_t at = off + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                lkeys[at] = keys[j];
+                lcols[at] = wbase + 64 * j + lane;
+            }
+            off += (uint32_t)__builtin_popcountll(m);
+        }
+        n_out += all;
+        buf ^= 1;
+    }
+    __syncthreads();
+    LdsCandSrc lsrc;
+    lsrc.keys = lkeys;
+    lsrc.cols = lcols;
+    lsrc.n = (int)n_cand;
+    select_core(lsrc, p, r, s);
+}
 
 template <bool POOL>
 __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const TopkParams p, const uint32_t* b1_in,

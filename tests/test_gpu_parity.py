@@ -153,6 +153,31 @@ def test_topk_crafted_scores():
     assert np.array_equal(out.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("rows,width,kind", [
+    (3, 8000, "ties"),       # one workgroup per row; > 4096 keys at the threshold bin: read from memory
+    (1100, 9000, "normal"),  # many rows: one workgroup per row, candidates in LDS
+    (1030, 9000, "mixed"),   # many rows, some all-tied (fallback) and some short
+])
+def test_topk_row_kernel(rows, width, kind):
+    import sparse_latent_attention_amd as csa2
+    print(f"\n[topk rows] rows={rows} width={width} kind={kind}", flush=True)
+    rng = np.random.default_rng(rows + width)
+    s = rng.standard_normal((rows, width)).astype(np.float32)
+    pos = np.full(rows, width - 1, dtype=np.int64)
+    if kind == "ties":
+        s[:] = 2.5
+        s[1, ::7] = 3.0
+    if kind == "mixed":
+        s[::5] = 1.0
+        pos[1::7] = rng.integers(0, 600, len(pos[1::7]))
+    sc = torch.from_numpy(s).cuda()
+    pt = torch.from_numpy(pos).cuda()
+    out = torch.empty(rows, 512, dtype=torch.int32, device="cuda")
+    csa2.topk_select(sc, pt, 1, out)
+    ref = oracle.topk.topk_full(s.astype(np.float64), pos, 1, 512)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
 def test_deterministic():
     cfg = SMALL["reindex_small"]
     x = make_inputs(cfg, 8, device="cuda")
