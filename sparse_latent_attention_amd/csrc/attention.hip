@@ -379,9 +379,12 @@ struct TileGeom {
 };
 
 // One wave's work on one tile for its 16 heads: scores, online softmax, PV.
-template <int D, class CT, int KS, int VS>
+// The wave accumulates output columns 16 dt0 .. 16 (dt0 + NACC) - 1 (all of D
+// by default); the scores and the softmax state always cover the whole row.
+template <int D, class CT, int KS, int VS, int NACC = D / 16>
 __device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_t vm, const typename Mma<CT>::Frag8* qf,
-                                             float scale_log2, int g, int li, float& m, float& l, f32x4* acc) {
+                                             float scale_log2, int g, int li, float& m, float& l, f32x4* acc,
+                                             int dt0 = 0) {
     typedef Mma<CT> M;
     constexpr int NS = D / 32, NDT = D / 16;
     // Four independent accumulation chains keep the matrix cores busy.
@@ -412,7 +415,7 @@ __device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_
         const float alpha = exp2f(m - m_new);  // 0 when m was -inf
         l *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+        for (int dt = 0; dt < NACC; ++dt) acc[dt] *= alpha;
         m = m_new;
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -427,7 +430,8 @@ __device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_
     l += psum;
     const typename M::Frag4 pb = p_frag<CT>(pr4);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[dt] = M::k16(acc[dt], lds_frag4<CT>(Vt + g * VS + vcol(16 * dt + li)), pb);
+    for (int dt = 0; dt < NACC; ++dt)
+        acc[dt] = M::k16(acc[dt], lds_frag4<CT>(Vt + g * VS + vcol(16 * (dt0 + dt) + li)), pb);
 }
 
 // Normalises, rotates the rope tail back and stores 4 consecutive elements.
@@ -448,13 +452,17 @@ __device__ __forceinline__ void emit4(void* out, int64_t off, int d0, f32x4 a, f
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// One workgroup per query row; wave w owns heads 16w .. 16w+15; shared tiles.
-template <int H, int D, int R, class CT, int QT, int KVT, int SWT, int OT, bool DECODE>
-__global__ __launch_bounds__(64 * ((H + 15) / 16)) void attn_rows_kernel(const AttnParams p) {
-    constexpr int NW = (H + 15) / 16;
+// One workgroup per query row, all waves on the same tiles.  Each 16-head
+// group has DS waves: each computes the group's scores and softmax state over
+// the whole row (identical in all DS waves) and accumulates 1/DS of the output
+// columns.  DS = 2 halves the accumulator registers, so two waves fit on each
+// SIMD and one wave's LDS reads and waits overlap the other's matrix work.
+template <int H, int D, int R, class CT, int QT, int KVT, int SWT, int OT, bool DECODE, int DS>
+__global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(const AttnParams p) {
+    constexpr int NW = (H + 15) / 16 * DS;
     constexpr int NT = 64 * NW;
     typedef TileGeom<CT, D> G;
-    constexpr int NS = D / 32, NDT = D / 16;
+    constexpr int NS = D / 32, NDT = D / 16 / DS;
     constexpr int PAIRS = 4 * (D / 8);
     constexpr int PPT = (PAIRS + NT - 1) / NT;  // pairs per thread
 
@@ -482,7 +490,8 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16)) void attn_rows_kernel(const A
     for (int i = tid; i < n_tiles; i += NT) vmask[i] = 0u;
     for (int i = tid; i < p.topk; i += NT) sel[i] = p.idx[(int64_t)c.r * p.topk + i];
 
-    const int h = 16 * wave + li;
+    const int h = 16 * (wave / DS) + li;
+    const int dt0 = (wave % DS) * NDT;  // this wave's first 16-column output block
     typename Mma<CT>::Frag8 qf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
@@ -531,7 +540,7 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16)) void attn_rows_kernel(const A
         const int b = t & 1;
         const CT* Kt = tiles[b];
         const CT* Vt = tiles[b] + G::K_ELEMS;
-        tile_compute<D, CT, G::KS, G::VS>(Kt, Vt, vmask[t], qf, p.scale_log2, g, li, m, l, acc);
+        tile_compute<D, CT, G::KS, G::VS, NDT>(Kt, Vt, vmask[t], qf, p.scale_log2, g, li, m, l, acc, dt0);
         if (t + 1 < n_tiles) {
             store_tile(t + 1, b ^ 1);
             if (t + 2 < n_tiles) load_tile(t + 2);
@@ -546,7 +555,7 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16)) void attn_rows_kernel(const A
     const int64_t obase = ((int64_t)c.r * H + h) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-        const int d0 = 16 * dt + 4 * g;
+        const int d0 = 16 * (dt0 + dt) + 4 * g;
         emit4<D, R, OT>(p.out, obase + d0, d0, acc[dt], inv, rope_cs);
     }
 }
@@ -690,12 +699,14 @@ static hipError_t launch_attn(const AttnParams& p, bool decode, hipStream_t stre
                            stream, p);
         return hipGetLastError();
     }
+    // the 64-head shapes split each head group's output columns over two waves
+    constexpr int DS = (H == 64 && D == 512) ? 2 : 1;
     if (decode)
-        hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, true>), dim3((unsigned)p.rows), dim3(NT), 0,
-                           stream, p);
+        hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, true, DS>), dim3((unsigned)p.rows),
+                           dim3(NT * DS), 0, stream, p);
     else
-        hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, false>), dim3((unsigned)p.rows), dim3(NT), 0,
-                           stream, p);
+        hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, false, DS>), dim3((unsigned)p.rows),
+                           dim3(NT * DS), 0, stream, p);
     return hipGetLastError();
 }
 
