@@ -84,21 +84,34 @@ __device__ __forceinline__ void store_k(CT* Kt, int j, int x8, const Pack8<CT>& 
 template <class CT, int D, int VS>
 __device__ __forceinline__ void store_v4(CT* Vt, int jb, int x8, const Pack8<CT> (&v)[4]);
 
+// Tile layouts in LDS (element offsets).  D = 512 (BF16): Kt rows of 512
+// elements whose 8-element (16-byte) chunks are XOR-ed with the row's low 4
+// bits, and the PV copy's column d at 4 (d ^ ((d >> 3) & 7)): both measured
+// free of bank conflicts for the MFMA operand reads with rocprofv3
+// (SQ_LDS_BANK_CONFLICT), where rows padded by 16 bytes (2.7 conflict cycles
+// per LDS cycle) and columns with a gap after every 8 (1.3) were not.
+// D = 64 (F32): rows padded to 68 elements, column d at 4d + 4(d/8).
+template <int D>
+__device__ __forceinline__ int kpos(int j, int c8) {
+    return D == 512 ? j * 512 + 8 * (c8 ^ (j & 15)) : j * 68 + 8 * c8;
+}
+template <int D>
+__device__ __forceinline__ int vcol(int d) {
+    return D == 512 ? 4 * (d ^ ((d >> 3) & 7)) : 4 * d + 4 * (d >> 3);
+}
+
 template <>
-__device__ __forceinline__ void store_k<__bf16, 512, 520>(__bf16* Kt, int j, int x8, const Pack8<__bf16>& v) {
-    *reinterpret_cast<u32x4*>(Kt + j * 520 + 8 * x8) = u32x4{v.w[0], v.w[1], v.w[2], v.w[3]};
+__device__ __forceinline__ void store_k<__bf16, 512, 512>(__bf16* Kt, int j, int x8, const Pack8<__bf16>& v) {
+    *reinterpret_cast<u32x4*>(Kt + kpos<512>(j, x8)) = u32x4{v.w[0], v.w[1], v.w[2], v.w[3]};
 }
 template <>
 __device__ __forceinline__ void store_k<float, 64, 68>(float* Kt, int j, int x8, const Pack8<float>& v) {
-    float* p = Kt + j * 68 + 8 * x8;
+    float* p = Kt + kpos<64>(j, x8);
     *reinterpret_cast<f32x4*>(p) = f32x4{v.v[0], v.v[1], v.v[2], v.v[3]};
     *reinterpret_cast<f32x4*>(p + 4) = f32x4{v.v[4], v.v[5], v.v[6], v.v[7]};
 }
 
-// Vt layout: Vt[jb * VS + vcol(d) + i] holds entry 4*jb + i, element d, where
-// vcol(d) = 4d + 4(d/8) leaves a 4-element gap after every 8 columns so the
-// lanes of a store (8 columns apart) spread over the LDS banks.
-__device__ __forceinline__ int vcol(int d) { return 4 * d + 4 * (d >> 3); }
+// Vt layout: Vt[jb * VS + vcol<D>(d) + i] holds entry 4*jb + i, element d.
 template <>
 __device__ __forceinline__ void store_v4<__bf16, 512, 2368>(__bf16* Vt, int jb, int x8,
                                                                    const Pack8<__bf16> (&v)[4]) {
@@ -110,8 +123,8 @@ __device__ __forceinline__ void store_v4<__bf16, 512, 2368>(__bf16* Vt, int jb, 
         const uint32_t hi01 = (v[0].w[q] >> 16) | (v[1].w[q] & 0xffff0000u);
         const uint32_t hi23 = (v[2].w[q] >> 16) | (v[3].w[q] & 0xffff0000u);
         const int d = 8 * x8 + 2 * q;
-        *reinterpret_cast<u32x2*>(Vt + jb * 2368 + vcol(d)) = u32x2{lo01, lo23};
-        *reinterpret_cast<u32x2*>(Vt + jb * 2368 + vcol(d + 1)) = u32x2{hi01, hi23};
+        *reinterpret_cast<u32x2*>(Vt + jb * 2368 + vcol<512>(d)) = u32x2{lo01, lo23};
+        *reinterpret_cast<u32x2*>(Vt + jb * 2368 + vcol<512>(d + 1)) = u32x2{hi01, hi23};
     }
 }
 template <>
@@ -120,7 +133,7 @@ __device__ __forceinline__ void store_v4<float, 64, 304>(float* Vt, int jb, int 
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int d = 8 * x8 + e;
-        *reinterpret_cast<f32x4*>(Vt + jb * 304 + vcol(d)) = f32x4{v[0].v[e], v[1].v[e], v[2].v[e], v[3].v[e]};
+        *reinterpret_cast<f32x4*>(Vt + jb * 304 + vcol<64>(d)) = f32x4{v[0].v[e], v[1].v[e], v[2].v[e], v[3].v[e]};
     }
 }
 
@@ -371,7 +384,7 @@ __device__ __forceinline__ void store_pair(const RawPair& raw, bool swa_tile, CT
 
 template <class CT, int D>
 struct TileGeom {
-    static constexpr int KS = (D == 512) ? 520 : 68;                // Kt row stride (elements)
+    static constexpr int KS = (D == 512) ? 512 : 68;                // Kt row stride (elements)
     static constexpr int VS = (D == 512) ? 2368 : 304;  // Vt block stride (elements): 4D + D/2 + padding
     static constexpr int K_ELEMS = 16 * KS;
     static constexpr int V_ELEMS = 4 * VS;
@@ -392,8 +405,22 @@ __device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_
     f32x4 part[NC];
 #pragma unroll
     for (int k = 0; k < NC; ++k) part[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Operand addresses.  With the D = 512 layouts the lane-dependent part of
+    // kpos(li, 4s + g) takes 4 values (by s mod 4) and that of the PV column
+    // 16 (dt0 + dt) + li another 4 (by dt mod 4, dt0 a multiple of 8); the
+    // rest is a compile-time offset.
+    int ko[4], vo[4];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) part[s % NC] = M::k32(part[s % NC], lds_frag8<CT>(Kt + li * KS + 32 * s + 8 * g), qf[s]);
+    for (int b = 0; b < 4; ++b) {
+        ko[b] = (D == 512) ? li * 512 + 32 * (b ^ (li >> 2)) + 8 * (g ^ (li & 3)) : kpos<D>(li, 4 * b + g);
+        vo[b] = (D == 512) ? g * VS + 64 * dt0 + 4 * (16 * b + (li & 8) + ((li & 7) ^ ((2 * b + (li >> 3)) & 7)))
+                           : g * VS + vcol<D>(16 * (dt0 + b) + li);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int k_off = (D == 512) ? ko[s & 3] + 128 * (s >> 2) : kpos<D>(li, 4 * s + g);
+        part[s % NC] = M::k32(part[s % NC], lds_frag8<CT>(Kt + k_off), qf[s]);
+    }
     f32x4 st = part[0];
 #pragma unroll
     for (int k = 1; k < NC; ++k) st += part[k];
@@ -430,8 +457,10 @@ __device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_
     l += psum;
     const typename M::Frag4 pb = p_frag<CT>(pr4);
 #pragma unroll
-    for (int dt = 0; dt < NACC; ++dt)
-        acc[dt] = M::k16(acc[dt], lds_frag4<CT>(Vt + g * VS + vcol(16 * (dt0 + dt) + li)), pb);
+    for (int dt = 0; dt < NACC; ++dt) {
+        const int v_off = (D == 512) ? vo[dt & 3] + 256 * (dt >> 2) : g * VS + vcol<D>(16 * (dt0 + dt) + li);
+        acc[dt] = M::k16(acc[dt], lds_frag4<CT>(Vt + v_off), pb);
+    }
 }
 
 // Normalises, rotates the rope tail back and stores 4 consecutive elements.
