@@ -399,7 +399,7 @@ __device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_
                                              float scale_log2, int g, int li, float& m, float& l, f32x4* acc,
                                              int dt0 = 0) {
     typedef Mma<CT> M;
-    constexpr int NS = D / 32, NDT = D / 16;
+    constexpr int NS = D / 32;
     // Four independent accumulation chains keep the matrix cores busy.
     constexpr int NC = NS >= 4 ? 4 : NS;
     f32x4 part[NC];
