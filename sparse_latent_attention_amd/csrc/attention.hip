@@ -590,14 +590,21 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup per (query row, 16-head group); 4 waves take interleaved tiles.
-template <int H, int D, int R, class CT, int QT, int KVT, int SWT, int OT>
-__global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
+// One workgroup per (query row, 16-head group).  Its waves form 4 groups of DS
+// waves; group w takes tiles w, w + 4, ... into its own LDS tile buffer.  The
+// DS waves of a group split each tile's gather and decode, compute the group's
+// scores and softmax state (identical in each) and accumulate 1/DS of the
+// output columns each: DS = 2 halves the per-wave decode work and the
+// accumulator, so two waves fit on each SIMD.  The groups' softmax states
+// merge through LDS at the end -- no partial results leave the chip.
+template <int H, int D, int R, class CT, int QT, int KVT, int SWT, int OT, int DS>
+__global__ __launch_bounds__(256 * DS) void attn_decode_kernel(const AttnParams p) {
     constexpr int NHG = (H + 15) / 16;  // head groups per row
     typedef TileGeom<CT, D> G;
-    constexpr int NS = D / 32, NDT = D / 16;
+    constexpr int NS = D / 32, NDT = D / 16 / DS;  // NDT: 16-column output blocks per wave
     constexpr int PAIRS = 4 * (D / 8);
-    constexpr int PPL = (PAIRS + 63) / 64;          // pairs per lane (each wave gathers its own tile)
+    constexpr int GL = 64 * DS;                     // lanes of a tile group
+    constexpr int PPL = (PAIRS + GL - 1) / GL;      // pairs per lane
     constexpr int ACC_STRIDE = D + 4;               // merge slice row stride (floats)
     constexpr int TILE_BYTES = G::BYTES;
     constexpr int MERGE_BYTES = 4 * 16 * ACC_STRIDE * 4;
@@ -610,6 +617,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
+    const int grp = wave / DS, dh = wave % DS;
+    const int gl = 64 * dh + lane;  // lane within the tile group
 
     // Workgroups of one row share an XCD: ids are dispatched round-robin over 8 XCDs.
     const int id = blockIdx.x;
@@ -632,13 +641,14 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
     }
 
     const int h = 16 * hg + li;
+    const int dt0 = dh * NDT;
     typename Mma<CT>::Frag8 qf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
         qf[s] = (h < H) ? load_q_frag<QT, CT, D>(p.q, ((int64_t)c.r * H + h) * D, s, g) : zero_frag8<CT>();
-    // Wave 0 carries the sink (max = sink, sum = 1); the others start empty.
+    // Group 0 carries the sink (max = sink, sum = 1); the others start empty.
     float m = kNegInf, l = 0.f;
-    if (wave == 0 && h < H) {
+    if (grp == 0 && h < H) {
         m = p.sink[h] * kLog2e;
         l = (g == 0) ? 1.f : 0.f;
     }
@@ -646,48 +656,60 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    CT* Kt = reinterpret_cast<CT*>(smem + wave * TILE_BYTES);
+    CT* Kt = reinterpret_cast<CT*>(smem + grp * TILE_BYTES);
     CT* Vt = Kt + G::K_ELEMS;
     RawPair raw[PPL];
     auto load_tile = [&](int tile) {
 #pragma unroll
         for (int k = 0; k < PPL; ++k) {
-            const int pr = lane + 64 * k;
+            const int pr = gl + GL * k;
             if (pr < PAIRS) load_pair<D, KVT, SWT, true>(p, c, sel, tile, pr / (D / 8), pr % (D / 8), raw[k]);
         }
     };
+    // Validity of a tile's 16 entries (as load_pair decides it): lane e < 16 tests entry e.
+    auto tile_mask = [&](int tile) {
+        const int e = tile * 16 + li;
+        bool v;
+        if (tile * 16 < p.window) {
+            v = e <= c.pos;  // ring slot e was written
+        } else {
+            const int32_t ix = sel[e - p.window];
+            v = ix >= 0 && (int64_t)ix < c.nv;
+        }
+        return (uint32_t)__ballot(lane < 16 && v) & 0xffffu;
+    };
 
-    for (int i = tid; i < p.topk; i += 256) sel[i] = p.idx[(int64_t)c.r * p.topk + i];
+    for (int i = tid; i < p.topk; i += 256 * DS) sel[i] = p.idx[(int64_t)c.r * p.topk + i];
     __syncthreads();  // sel and rope_cs complete
-    int t = wave;
+    const int rounds = (n_tiles + 3) / 4;
+    int t = grp;
     if (t < n_tiles) load_tile(t);
-    for (; t < n_tiles; t += 4) {
-        uint32_t vm = 0;
+    for (int rd = 0; rd < rounds; ++rd, t += 4) {
+        const bool mine = t < n_tiles;  // the same for every wave of the group
+        if (mine) {
 #pragma unroll
-        for (int k = 0; k < PPL; ++k) {
-            const int pr = lane + 64 * k;
-            if (pr < PAIRS) {
-                const int jb = pr / (D / 8), x8 = pr % (D / 8);
-                store_pair<D, CT, G::KS, G::VS, KVT, SWT>(raw[k], t * 16 < p.window, Kt, Vt, jb, x8);
-                if (x8 == 0) vm |= raw[k].valid << (4 * jb);
+            for (int k = 0; k < PPL; ++k) {
+                const int pr = gl + GL * k;
+                if (pr < PAIRS)
+                    store_pair<D, CT, G::KS, G::VS, KVT, SWT>(raw[k], t * 16 < p.window, Kt, Vt, pr / (D / 8),
+                                                              pr % (D / 8));
             }
         }
-        // validity of the tile's 16 entries: OR of what the x8 == 0 lanes hold
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) vm |= (uint32_t)__shfl_xor((int)vm, o, 64);
-        if (t + 4 < n_tiles) load_tile(t + 4);  // next tile's bytes in flight during this tile
-        wave_lds_fence();
-        tile_compute<D, CT, G::KS, G::VS>(Kt, Vt, vm, qf, p.scale_log2, g, li, m, l, acc);
-        wave_lds_fence();
+        __syncthreads();  // every group's tile is in LDS
+        if (t + 4 < n_tiles) load_tile(t + 4);  // next round's bytes in flight during this round
+        if (mine) {
+            const uint32_t vm = tile_mask(t);
+            tile_compute<D, CT, G::KS, G::VS, NDT>(Kt, Vt, vm, qf, p.scale_log2, g, li, m, l, acc, dt0);
+        }
+        __syncthreads();  // tile buffers free for the next round
     }
 
-    // ---- merge the 4 waves' softmax states ------------------------------------
+    // ---- merge the 4 groups' softmax states -----------------------------------
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
-    __syncthreads();  // every wave is done with its tile buffer; rope_cs is complete
-    if (g == 0) {
-        ml[wave][0][li] = m;
-        ml[wave][1][li] = l;
+    if (dh == 0 && g == 0) {
+        ml[grp][0][li] = m;
+        ml[grp][1][li] = l;
     }
     __syncthreads();
     float mx = kNegInf;
@@ -697,17 +719,17 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const AttnParams p) {
     float L = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) L += ml[w][1][li] * exp2f(ml[w][0][li] - mu);
-    const float mine = exp2f(m - mu);
-    float* slice = reinterpret_cast<float*>(smem) + wave * 16 * ACC_STRIDE;
+    const float mine_w = exp2f(m - mu);
+    float* slice = reinterpret_cast<float*>(smem) + grp * 16 * ACC_STRIDE;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
-        *reinterpret_cast<f32x4*>(slice + li * ACC_STRIDE + 16 * dt + 4 * g) = acc[dt] * mine;
+        *reinterpret_cast<f32x4*>(slice + li * ACC_STRIDE + 16 * (dt0 + dt) + 4 * g) = acc[dt] * mine_w;
     __syncthreads();
     if (h >= H) return;
     const float inv = L > 0.f ? 1.f / L : 0.f;
     const float* base = reinterpret_cast<const float*>(smem);
     const int64_t obase = ((int64_t)c.r * H + h) * D;
-    for (int dt = wave; dt < NDT; dt += 4) {
+    for (int dt = wave; dt < D / 16; dt += 4 * DS) {
         const int off = li * ACC_STRIDE + 16 * dt + 4 * g;
         f32x4 sum = *reinterpret_cast<const f32x4*>(base + off);
 #pragma unroll
@@ -722,14 +744,14 @@ template <int H, int D, int R, class CT, int QT, int KVT, int SWT, int OT>
 static hipError_t launch_attn(const AttnParams& p, bool decode, hipStream_t stream) {
     constexpr int NHG = (H + 15) / 16;
     constexpr int NT = 64 * NHG;
-    if (decode && p.rows * NHG < 1024) {
-        const int blocks = ((p.rows + 7) / 8) * 8 * NHG;
-        hipLaunchKernelGGL((attn_decode_kernel<H, D, R, CT, QT, KVT, SWT, OT>), dim3((unsigned)blocks), dim3(256), 0,
-                           stream, p);
-        return hipGetLastError();
-    }
     // the 64-head shapes split each head group's output columns over two waves
     constexpr int DS = (H == 64 && D == 512) ? 2 : 1;
+    if (decode && p.rows * NHG < 1024) {
+        const int blocks = ((p.rows + 7) / 8) * 8 * NHG;
+        hipLaunchKernelGGL((attn_decode_kernel<H, D, R, CT, QT, KVT, SWT, OT, DS>), dim3((unsigned)blocks),
+                           dim3(256 * DS), 0, stream, p);
+        return hipGetLastError();
+    }
     if (decode)
         hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, true, DS>), dim3((unsigned)p.rows),
                            dim3(NT * DS), 0, stream, p);
