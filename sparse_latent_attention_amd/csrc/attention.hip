@@ -493,15 +493,20 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     typedef TileGeom<CT, D> G;
     constexpr int NS = D / 32, NDT = D / 16 / DS;
     constexpr int PAIRS = 4 * (D / 8);
-    constexpr int PPT = (PAIRS + NT - 1) / NT;  // pairs per thread
+    // DS tiles per round: thread group ts (NT / DS threads) gathers tile DS*round + ts, so every
+    // thread takes part in the gather; each wave then computes the round's DS tiles.
+    constexpr int TPR = DS;
+    constexpr int TT = NT / TPR;                // threads per tile
+    constexpr int PPT = (PAIRS + TT - 1) / TT;  // pairs per thread
 
-    __shared__ __attribute__((aligned(16))) CT tiles[2][G::K_ELEMS + G::V_ELEMS];
+    __shared__ __attribute__((aligned(16))) CT tiles[2 * TPR][G::K_ELEMS + G::V_ELEMS];
     __shared__ float rope_cs[R];
     __shared__ uint32_t vmask[kMaxTiles];  // validity bits of each tile's 16 entries, written once
     __shared__ __attribute__((aligned(16))) int32_t sel[kMaxTopk];  // this row's selected indices
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
+    const int ts = tid / TT, tl = tid % TT;  // this thread's tile of a round, and its index there
     RowCtx c;
     c.r = blockIdx.x;
     c.pos = p.pos[c.r];
@@ -538,7 +543,7 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     auto load_tile = [&](int tile) {
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
-            const int pr = tid + k * NT;
+            const int pr = tl + k * TT;
             if (pr < PAIRS) load_pair<D, KVT, SWT, DECODE>(p, c, sel, tile, pr / (D / 8), pr % (D / 8), raw[k]);
         }
     };
@@ -548,7 +553,7 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
         uint32_t bits = 0;
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
-            const int pr = tid + k * NT;
+            const int pr = tl + k * TT;
             if (pr < PAIRS) {
                 const int jb = pr / (D / 8), x8 = pr % (D / 8);
                 store_pair<D, CT, G::KS, G::VS, KVT, SWT>(raw[k], tile * 16 < p.window, Kt, Vt, jb, x8);
@@ -559,20 +564,27 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     };
 
     __syncthreads();  // rope table and vmask reset visible
-    if (n_tiles > 0) {
-        load_tile(0);
-        store_tile(0, 0);
-        if (n_tiles > 1) load_tile(1);
+    const int n_rounds = (n_tiles + TPR - 1) / TPR;
+    if (ts < n_tiles) {
+        load_tile(ts);
+        store_tile(ts, ts);
     }
+    if (TPR + ts < n_tiles) load_tile(TPR + ts);
     __syncthreads();
-    for (int t = 0; t < n_tiles; ++t) {
-        const int b = t & 1;
-        const CT* Kt = tiles[b];
-        const CT* Vt = tiles[b] + G::K_ELEMS;
-        tile_compute<D, CT, G::KS, G::VS, NDT>(Kt, Vt, vmask[t], qf, p.scale_log2, g, li, m, l, acc, dt0);
-        if (t + 1 < n_tiles) {
-            store_tile(t + 1, b ^ 1);
-            if (t + 2 < n_tiles) load_tile(t + 2);
+    for (int rd = 0; rd < n_rounds; ++rd) {
+        const int bs = (rd & 1) * TPR;
+#pragma unroll
+        for (int jt = 0; jt < TPR; ++jt) {
+            const int t = rd * TPR + jt;
+            if (t < n_tiles)
+                tile_compute<D, CT, G::KS, G::VS, NDT>(tiles[bs + jt], tiles[bs + jt] + G::K_ELEMS, vmask[t], qf,
+                                                       p.scale_log2, g, li, m, l, acc, dt0);
+        }
+        // the next round's tiles go into the other buffer set; its loads were issued a round ago
+        const int tn = (rd + 1) * TPR + ts;
+        if (tn < n_tiles) {
+            store_tile(tn, (bs ^ TPR) + ts);
+            if (tn + TPR < n_tiles) load_tile(tn + TPR);
         }
         __syncthreads();
     }
