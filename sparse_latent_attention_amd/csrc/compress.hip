@@ -440,12 +440,111 @@ static void launch_finish(const CompressParams& p, int main_dtype, int idx_dtype
     else launch_finish_m<RATIO, 1>(p, main_dtype, idx_dtype, st);
 }
 
+// Projection for many rows (a prefill chunk): one workgroup per 128 x 128 tile
+// of the [rows, nproj] product, its 4 waves 64 x 64 each.  The x and weight
+// rows of a 128-column slice of the reduction are staged in LDS once per
+// workgroup (double-buffered; 256-byte rows whose 16-byte chunks are XOR-ed
+// with the row's low 4 bits, so the MFMA operand reads hit distinct banks) and
+// each operand fragment read from LDS feeds 4 MFMAs; compress_project_kernel
+// instead reads every fragment from memory for every wave.  One partial slice
+// (no split of the reduction), in the layout the finish kernel reads.
+constexpr int kGemmTile = 128;
+__device__ __forceinline__ int gemm_off(int row, int c) { return 256 * row + 16 * (c ^ (row & 15)); }
+
+__global__ __launch_bounds__(256) void compress_gemm_kernel(const CompressParams p) {
+    __shared__ __attribute__((aligned(16))) uint8_t sa[2][kGemmTile * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t sb[2][kGemmTile * 256];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, li = lane & 15;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = blockIdx.y * kGemmTile, n0 = blockIdx.x * kGemmTile;
+
+    // Staging: chunk i = tid + 256 j (j < 8) of a 128 x 128 operand slice is 16-byte chunk
+    // i % 16 of row i / 16 (consecutive threads read consecutive bytes of a row).
+    const uint16_t* arow[8];
+    const uint16_t* brow[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int ci = tid + 256 * j, r = ci / 16, c = ci % 16;
+        int m = m0 + r;
+        if (m >= p.rows) m = p.rows - 1;  // in bounds; such rows' results are not stored
+        const int n = n0 + r;
+        arow[j] = p.x + (int64_t)m * p.d_in + 8 * c;
+        brow[j] = (n < kLatent ? p.wkv + (int64_t)n * p.d_in : p.wgate + (int64_t)(n - kLatent) * p.d_in) + 8 * c;
+    }
+    auto fetch = [&](int k, u32x4 (&xa)[8], u32x4 (&xb)[8]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            xa[j] = *reinterpret_cast<const u32x4*>(arow[j] + k);
+            xb[j] = *reinterpret_cast<const u32x4*>(brow[j] + k);
+        }
+    };
+    auto put = [&](int b, const u32x4 (&xa)[8], const u32x4 (&xb)[8]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int ci = tid + 256 * j;
+            *reinterpret_cast<u32x4*>(sa[b] + gemm_off(ci / 16, ci % 16)) = xa[j];
+            *reinterpret_cast<u32x4*>(sb[b] + gemm_off(ci / 16, ci % 16)) = xb[j];
+        }
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+        u32x4 xa[8], xb[8];
+        fetch(0, xa, xb);
+        put(0, xa, xb);
+    }
+    __syncthreads();
+    int b = 0;
+    for (int k = 0; k < p.d_in; k += kGemmTile) {
+        const bool more = k + kGemmTile < p.d_in;
+        u32x4 xa[8], xb[8];
+        if (more) fetch(k + kGemmTile, xa, xb);  // in flight during this slice's MFMAs
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 fa[4], fb[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                fa[t] = *reinterpret_cast<const bf16x8*>(sa[b] + gemm_off(64 * wm + 16 * t + li, 4 * s + g));
+                fb[t] = *reinterpret_cast<const bf16x8*>(sb[b] + gemm_off(64 * wn + 16 * t + li, 4 * s + g));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = Mma<__bf16>::k32(acc[i][j], fa[i], fb[j]);
+        }
+        if (more) put(b ^ 1, xa, xb);
+        __syncthreads();
+        b ^= 1;
+    }
+    // D[4g + rr][li] of tile (i, j): row m0 + 64 wm + 16 i + 4g + rr, column n0 + 64 wn + 16 j + li
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int m = m0 + 64 * wm + 16 * i + 4 * g + rr;
+            if (m < p.rows) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) p.partial[(int64_t)m * p.nproj + n0 + 64 * wn + 16 * j + li] = acc[i][j][rr];
+            }
+        }
+}
+
 hipError_t launch_compress(const CompressParams& p, int ratio, int main_dtype, int idx_dtype, hipStream_t stream) {
     if (p.rows <= 0) return hipSuccess;
     const int k_per_split = p.d_in / p.ksplit;
     if (k_per_split % 64 != 0 || p.nproj % 64 != 0) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(p.nproj / 64), (unsigned)((p.rows + 63) / 64), (unsigned)p.ksplit);
-    hipLaunchKernelGGL(compress_project_kernel, grid, dim3(256), 0, stream, p, k_per_split);
+    if (p.ksplit == 1 && p.rows >= 1024 && p.d_in % kGemmTile == 0 && p.nproj % kGemmTile == 0) {
+        const dim3 grid((unsigned)(p.nproj / kGemmTile), (unsigned)((p.rows + kGemmTile - 1) / kGemmTile));
+        hipLaunchKernelGGL(compress_gemm_kernel, grid, dim3(256), 0, stream, p);
+    } else {
+        const dim3 grid((unsigned)(p.nproj / 64), (unsigned)((p.rows + 63) / 64), (unsigned)p.ksplit);
+        hipLaunchKernelGGL(compress_project_kernel, grid, dim3(256), 0, stream, p, k_per_split);
+    }
     if (ratio == 1) {
         launch_finish<1>(p, main_dtype, idx_dtype, stream);
     } else {
