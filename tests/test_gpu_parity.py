@@ -104,6 +104,26 @@ def test_decode_kernels_agree(rows):
     assert_close(out[torch.from_numpy(sample).cuda()], ref, BF16_ATOL, BF16_RTOL, f"decode rows={rows}")
 
 
+@pytest.mark.parametrize("window,topk", [(16, 16), (48, 32), (16, 96), (128, 48)])
+@pytest.mark.parametrize("base,rows", [("full_decode_small", 5), ("full_decode_small", 300), ("lowp_small", 7),
+                                       ("prefill_small", None)])
+def test_attention_ragged_tile_counts(base, rows, window, topk):
+    """(window + topk) / 16 = 2, 5, 7, 11 tiles: the decode kernel's four tile groups and the rows kernel's
+    two-tile rounds then end with idle groups / a half round."""
+    cfg = SMALL[base].replace(window=window, topk=topk)
+    if rows is not None:
+        cfg = cfg.replace(batch=rows, q_tokens=rows)
+    else:
+        cfg = cfg.replace(reuse_layers=0)
+    print(f"\n[ragged tiles] {base} rows={cfg.q_tokens} window={window} topk={topk}", flush=True)
+    x = make_inputs(cfg, 9, device="cuda")
+    idx = gpu_topk(cfg, x, gpu_scores(cfg, x))
+    out = gpu_attention(cfg, x, idx)
+    sample = np.unique(np.linspace(0, cfg.q_tokens - 1, min(cfg.q_tokens, 10)).astype(int))
+    ref = oracle_attention(cfg, x, idx.cpu().numpy()[sample], sample)
+    assert_close(out[torch.from_numpy(sample).cuda()], ref, BF16_ATOL, BF16_RTOL, f"{base} W={window} k={topk}")
+
+
 def test_injected_indices_and_masks():
     # -1 padding, duplicates, rows the group-causal mask hides, far out-of-range rows
     cfg = SMALL["lowp_small"]
