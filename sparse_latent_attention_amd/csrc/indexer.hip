@@ -385,6 +385,14 @@ __global__ __launch_bounds__(64 * ROWS) void indexer_chunk_kernel(const IndexPar
         if (more) fetch(cs + KEYS, x);
         if (live) {
             const uint8_t* tb = tile[b];
+            // B operands of the next 16 keys are read from LDS while this 16 keys' MFMAs run
+            auto read_kb = [&](int kk, Frag (&kb)[S]) {
+#pragma unroll
+                for (int s = 0; s < S; ++s)
+                    kb[s] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(tb + stage_off(kk + li, 4 * s + g)));
+            };
+            Frag kn[S];
+            read_kb(0, kn);
 #pragma unroll
             for (int st = 0; st < KEYS / 64; ++st) {
                 float v[4];
@@ -392,9 +400,8 @@ __global__ __launch_bounds__(64 * ROWS) void indexer_chunk_kernel(const IndexPar
                 for (int u = 0; u < 4; ++u) {
                     Frag kb[S];
 #pragma unroll
-                    for (int s = 0; s < S; ++s)
-                        kb[s] = __builtin_bit_cast(
-                            Frag, *reinterpret_cast<const u32x4*>(tb + stage_off(64 * st + 16 * u + li, 4 * s + g)));
+                    for (int s = 0; s < S; ++s) kb[s] = kn[s];
+                    if (64 * st + 16 * u + 16 < KEYS) read_kb(64 * st + 16 * u + 16, kn);
                     float acc_sum = 0.f;
 #pragma unroll
                     for (int t = 0; t < HT; ++t) {
