@@ -24,13 +24,18 @@
 // probability 0.  The raw bytes of the next tile are loaded into registers
 // while the current tile is computed.
 //
+// For the 64-head shape a 16-head group has two waves: both compute the
+// group's scores and softmax state (identical) and each accumulates half of
+// the 512 output columns, which halves the accumulator registers so that two
+// waves fit on each SIMD.
+//
 // Two kernels share that machinery:
 //   * attn_rows_kernel (prefill, and decode with many rows): one workgroup per
-//     query row, one wave per 16-head group, all waves on the same tile;
-//     two LDS tile buffers so one barrier per tile suffices.
+//     query row, all waves on the same tiles, two tiles per round (each half
+//     of the threads gathers one) in two buffer sets, one barrier per round.
 //   * attn_decode_kernel (decode with few rows): one workgroup per (row,
-//     16-head group) so small batches still fill the chip; its 4 waves take
-//     interleaved tiles with private LDS buffers and merge their softmax
+//     16-head group) so small batches still fill the chip; 4 groups of waves
+//     take interleaved tiles into private LDS buffers and merge their softmax
 //     states through LDS at the end -- no partial results leave the chip.
 //     The workgroups of one row sit on the same XCD, so the 4x re-gather of
 //     that row's entries is served by one L2.

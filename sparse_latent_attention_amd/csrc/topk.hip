@@ -18,7 +18,10 @@
 //
 // Two ways to feed that select:
 //   * narrow rows or many rows: one 1024-thread workgroup per row reads the
-//     score row directly (4 passes over a row that stays in L2);
+//     score row twice -- a histogram of the keys' top 12 bits gives the bin b1
+//     of the k-th largest key, then the keys in bins >= b1 are compacted in
+//     column order into LDS, where the select runs (more than kLdsCand such
+//     keys, i.e. heavy ties: the select reads the row from memory instead);
 //   * wide rows (the 1M-column decode): the row is cut into chunks handled by
 //     separate workgroups.  (1) each chunk adds its 12-bit histogram into a
 //     per-row global histogram; (2) one workgroup per row finds the bin b1 of
