@@ -430,20 +430,22 @@ __device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_
 #pragma unroll
     for (int k = 1; k < NC; ++k) st += part[k];
     float x[4];
-    float tmax = kNegInf;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        x[rr] = ((vm >> (4 * g + rr)) & 1u) ? st[rr] * scale_log2 : kNegInf;
-        tmax = fmaxf(tmax, x[rr]);
+    for (int rr = 0; rr < 4; ++rr) x[rr] = st[rr] * scale_log2;
+    if (vm != 0xffffu) {  // the same for the whole wave: most tiles have 16 valid entries
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) x[rr] = ((vm >> (4 * g + rr)) & 1u) ? x[rr] : kNegInf;
     }
-    tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+    const float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    float tmax_all = tmax;
+    tmax_all = fmaxf(tmax_all, shfl_xor(tmax_all, 16));
+    tmax_all = fmaxf(tmax_all, shfl_xor(tmax_all, 32));
     // Lazy rescaling: m is only a reference point (the result is the same for any
     // m), so it moves -- and acc and l are rescaled -- only when some head's scores
     // exceed it by more than 2^8; the probabilities then stay below 256.
-    const uint64_t need_rescale = __ballot(tmax > m + 8.f);
+    const uint64_t need_rescale = __ballot(tmax_all > m + 8.f);
     if (__builtin_expect(__builtin_amdgcn_readfirstlane((uint32_t)(need_rescale | (need_rescale >> 32))) != 0u, 0)) {
-        const float m_new = fmaxf(m, tmax);
+        const float m_new = fmaxf(m, tmax_all);
         const float alpha = exp2f(m - m_new);  // 0 when m was -inf
         l *= alpha;
 #pragma unroll
@@ -456,7 +458,9 @@ __device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_
     float psum = 0.f;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-        pr4[rr] = exp2f(x[rr] - m_use);
+        // x - m_use <= 8 (lazy rescaling) and -inf for masked entries: the hardware exp2 (v_exp_f32,
+        // -inf -> 0) needs none of exp2f's range handling
+        pr4[rr] = __builtin_amdgcn_exp2f(x[rr] - m_use);
         psum += pr4[rr];
     }
     l += psum;
