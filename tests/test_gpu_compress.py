@@ -177,10 +177,13 @@ def test_quantised_planes_encode_the_gpu_float32_rows(main_format, idx_format, r
         assert np.all(np.abs(dec - want) <= np.maximum(np.abs(want) * 2 ** -4, amax / 448 * 2 ** -10) + 2 * slack)
 
 
-@pytest.mark.parametrize("ratio,rows,seqs", [(2, 64, None), (1, 64, None), (2, 4096, 1), (1, 1024, 4)])
+@pytest.mark.parametrize("ratio,rows,seqs", [(2, 64, None), (1, 64, None), (2, 4096, 1), (1, 1024, 4),
+                                             (2, 4100, 3), (1, 8192, 2)])
 def test_full_size_sampled_rows(ratio, rows, seqs):
     """d_in 5120, the model's hidden width, in the launch configuration bench.py times; the oracle checks a
-    sample of the rows (each from its own group's rows, which gives the same result as the whole call)."""
+    sample of the rows (each from its own group's rows, which gives the same result as the whole call).
+    4096 / 4100 rows at ratio 2 and 8192 rows at ratio 1 take the LDS-tiled projection (4100: a ragged
+    last 128-row tile); 64 and 1024 rows the split reduction."""
     print(f"\n[compress full] ratio {ratio} rows {rows} seqs {seqs}", flush=True)
     x = make_compress_inputs(rows, 5120, ratio, 13, device="cuda", seqs=seqs, pos0=126975,
                              plane_rows=131072 + 8192)
