@@ -90,6 +90,9 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
     } else if (a->block_max != nullptr && !pool_block_ok(a->block_rows)) {
         return CSA2_ERR_INVALID_ARG;
     }
+    // Nothing to compute (an empty output may come with a null pointer, which would
+    // otherwise read as score-free mode).
+    if (a->rows == 0 || a->width == 0) return CSA2_OK;
     // Score-free mode: FULL rows of a quantised plane keep their scores on chip and
     // leave the block keys for csa2_topk_rescore.
     const bool score_free = a->scores == nullptr;
@@ -100,7 +103,6 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
         if (a->width >= (1LL << 24)) return CSA2_ERR_UNSUPPORTED;
         if (!aligned(a->block_keys, 4)) return CSA2_ERR_INVALID_ARG;
     }
-    if (a->rows == 0 || a->width == 0) return CSA2_OK;
     if (a->q == nullptr || a->w == nullptr || a->k == nullptr || a->row_base == nullptr || a->pos == nullptr)
         return CSA2_ERR_INVALID_ARG;
     if (!index_scales_ok(a)) return CSA2_ERR_INVALID_ARG;

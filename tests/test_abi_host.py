@@ -107,6 +107,14 @@ def test_indexer_reindex_width_must_match_pool():
     assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
 
 
+def test_indexer_empty_calls_do_nothing():
+    # no rows or no columns: OK even with a null score pointer (an empty tensor's), which otherwise selects
+    # score-free mode
+    for kw in (dict(rows=0), dict(width=0)):
+        a = _index_args(scores=None, **kw)
+        assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.OK, kw
+
+
 def test_indexer_shared_plane_flag_rules():
     # FULL only; with rows == 0 a valid call returns OK before touching memory
     a = _index_args(flags=csa2.INDEX_SHARED_PLANE, rows=0)

@@ -333,3 +333,39 @@ def test_shared_plane_scores_equal_per_row_path(rows, width, base):
                                          lambda i: kk, np.array([2 * n - 1]), 2, tau, n)[0]
         bound = oracle.indexer.score_abs_bound(q[r].double().cpu().numpy(), w[r].double().cpu().numpy(), kk, tau)
         assert np.all(np.abs(got[r, :n] - ref) <= SCORE_TOL * bound)
+
+
+def test_empty_inputs():
+    """Zero query rows through every entry point (device tensors with no elements), and zero-width rows in
+    top-k (no valid column: all -1)."""
+    import sparse_latent_attention_amd as csa2
+    dev = "cuda"
+    e64 = torch.empty(0, dtype=torch.int64, device=dev)
+    bf = lambda *s: torch.zeros(*s, dtype=torch.bfloat16, device=dev)
+    # indexer: no rows, and rows over an empty width
+    csa2.indexer_score(bf(0, 64, 128), torch.zeros(0, 64, device=dev), bf(16, 128), e64, e64, 2, 0.01,
+                       torch.empty(0, 100, device=dev))
+    csa2.indexer_score(bf(3, 64, 128), torch.zeros(3, 64, device=dev), bf(16, 128),
+                       torch.zeros(3, dtype=torch.int64, device=dev), torch.full((3,), 5, dtype=torch.int64, device=dev),
+                       2, 0.01, torch.empty(3, 0, device=dev))
+    # top-k: no rows; rows of width 0 give only -1
+    csa2.topk_select(torch.empty(0, 50, device=dev), e64, 1, torch.empty(0, 16, dtype=torch.int32, device=dev))
+    out = torch.zeros(4, 16, dtype=torch.int32, device=dev)
+    csa2.topk_select(torch.empty(4, 0, device=dev), torch.full((4,), 9, dtype=torch.int64, device=dev), 1, out)
+    torch.cuda.synchronize()
+    assert bool((out == -1).all())
+    # attention, decode and prefill: no rows
+    freqs = csa2.rope_inv_freq(64, 160000.0, 16.0, 65536).to(dev)
+    sink = torch.zeros(64, device=dev)
+    csa2.sparse_attn_decode(bf(0, 64, 512), e64, torch.empty(0, 16, dtype=torch.int32, device=dev), bf(8, 512), e64,
+                            bf(0, 128, 512), sink, freqs, 1, 128, 0.04, bf(0, 64, 512))
+    csa2.sparse_attn_prefill(bf(0, 64, 512), e64, torch.empty(0, 16, dtype=torch.int32, device=dev), bf(8, 512),
+                             bf(8, 512), 0, sink, freqs, 1, 128, 0.04, bf(0, 64, 512))
+    # candidate pool and write path: no rows
+    csa2.candidate_pool(e64, 1, torch.empty(0, 16, dtype=torch.int32, device=dev),
+                        scores=torch.empty(0, 100, device=dev))
+    csa2.compress(bf(0, 256), e64, torch.empty(0, dtype=torch.int32, device=dev), e64, bf(512, 256),
+                  torch.ones(512, device=dev), bf(128, 512), torch.ones(128, device=dev), freqs,
+                  torch.zeros(8, 512, device=dev), torch.zeros(8, 128, device=dev), ratio=1, main_format="f32",
+                  idx_format="f32")
+    torch.cuda.synchronize()
