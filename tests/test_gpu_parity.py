@@ -104,12 +104,13 @@ def test_decode_kernels_agree(rows):
     assert_close(out[torch.from_numpy(sample).cuda()], ref, BF16_ATOL, BF16_RTOL, f"decode rows={rows}")
 
 
-@pytest.mark.parametrize("window,topk", [(16, 16), (48, 32), (16, 96), (128, 48)])
+@pytest.mark.parametrize("window,topk", [(16, 16), (48, 32), (16, 96), (128, 48), (1024, 2048)])
 @pytest.mark.parametrize("base,rows", [("full_decode_small", 5), ("full_decode_small", 300), ("lowp_small", 7),
                                        ("prefill_small", None)])
 def test_attention_ragged_tile_counts(base, rows, window, topk):
     """(window + topk) / 16 = 2, 5, 7, 11 tiles: the decode kernel's four tile groups and the rows kernel's
-    two-tile rounds then end with idle groups / a half round."""
+    two-tile rounds then end with idle groups / a half round; and the largest window and top-k the library
+    takes (1024 + 2048: 192 tiles, the per-row index and validity buffers full)."""
     cfg = SMALL[base].replace(window=window, topk=topk)
     if rows is not None:
         cfg = cfg.replace(batch=rows, q_tokens=rows)
