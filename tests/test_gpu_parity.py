@@ -174,14 +174,16 @@ def test_topk_crafted_scores():
     assert np.array_equal(out.cpu().numpy(), ref)
 
 
-@pytest.mark.parametrize("rows,width,kind", [
-    (3, 8000, "ties"),       # one workgroup per row; > 4096 keys at the threshold bin: read from memory
-    (1100, 9000, "normal"),  # many rows: one workgroup per row, candidates in LDS
-    (1030, 9000, "mixed"),   # many rows, some all-tied (fallback) and some short
+@pytest.mark.parametrize("rows,width,kind,k", [
+    (3, 8000, "ties", 512),       # one workgroup per row; > 4096 keys at the threshold bin: read from memory
+    (1100, 9000, "normal", 512),  # many rows: one workgroup per row, candidates in LDS
+    (1030, 9000, "mixed", 512),   # many rows, some all-tied (fallback) and some short
+    (1030, 9000, "mixed", 1),     # the smallest k
+    (5, 3000, "ties", 1),
 ])
-def test_topk_row_kernel(rows, width, kind):
+def test_topk_row_kernel(rows, width, kind, k):
     import sparse_latent_attention_amd as csa2
-    print(f"\n[topk rows] rows={rows} width={width} kind={kind}", flush=True)
+    print(f"\n[topk rows] rows={rows} width={width} kind={kind} k={k}", flush=True)
     rng = np.random.default_rng(rows + width)
     s = rng.standard_normal((rows, width)).astype(np.float32)
     pos = np.full(rows, width - 1, dtype=np.int64)
@@ -193,9 +195,9 @@ def test_topk_row_kernel(rows, width, kind):
         pos[1::7] = rng.integers(0, 600, len(pos[1::7]))
     sc = torch.from_numpy(s).cuda()
     pt = torch.from_numpy(pos).cuda()
-    out = torch.empty(rows, 512, dtype=torch.int32, device="cuda")
+    out = torch.empty(rows, k, dtype=torch.int32, device="cuda")
     csa2.topk_select(sc, pt, 1, out)
-    ref = oracle.topk.topk_full(s.astype(np.float64), pos, 1, 512)
+    ref = oracle.topk.topk_full(s.astype(np.float64), pos, 1, k)
     assert np.array_equal(out.cpu().numpy(), ref)
 
 
@@ -219,6 +221,7 @@ def test_deterministic():
     (2, 20000, 2048, "normal"),      # largest k
     (3, 30000, 512, "short"),        # fewer valid columns than k in one row
     (3, 200000, 512, "quantized"),   # ~100 copies of each value: ties at the threshold inside the candidates
+    (4, 100003, 1, "quantized"),     # the smallest k on the wide path
 ])
 def test_topk_wide_rows(rows, width, k, kind):
     import sparse_latent_attention_amd as csa2
@@ -295,8 +298,9 @@ def test_attention_large_logit_spread(name, kw):
     assert_close(out[torch.from_numpy(rows).cuda()], ref, BF16_ATOL, BF16_RTOL, f"spread {name}")
 
 
-@pytest.mark.parametrize("rows,width,base", [(37, 9000, 100), (8, 64, 0), (300, 20000, 5), (13, 8300, 0)])
-def test_shared_plane_scores_equal_per_row_path(rows, width, base):
+@pytest.mark.parametrize("rows,width,base,ratio", [(37, 9000, 100, 2), (8, 64, 0, 2), (300, 20000, 5, 2),
+                                                   (13, 8300, 0, 2), (40, 9000, 7, 1)])
+def test_shared_plane_scores_equal_per_row_path(rows, width, base, ratio):
     """Rows that share one plane (the staged-key-tile path for BF16 64 x 128): bit-identical scores to the
     per-row path, over ragged row groups (rows not a multiple of 8), ragged column ranges and stages
     (width not a multiple of 8192 or 64), rows that see nothing (position 0 at ratio 2) and rows that see
@@ -307,19 +311,19 @@ def test_shared_plane_scores_equal_per_row_path(rows, width, base):
     k = (torch.randn(base + width, 128, generator=g, device="cuda") * 0.1).to(torch.bfloat16)
     q = (torch.randn(rows, 64, 128, generator=g, device="cuda") * 0.1).to(torch.bfloat16)
     w = torch.randn(rows, 64, generator=g, device="cuda")
-    pos = torch.randint(0, 2 * width + 10, (rows,), generator=g, device="cuda")
+    pos = torch.randint(0, ratio * width + 10, (rows,), generator=g, device="cuda")
     pos[0] = 0
-    pos[-1] = 2 * width + 5
+    pos[-1] = ratio * width + 5
     rb = torch.full((rows,), base, dtype=torch.int64, device="cuda")
     out = {}
     for shared in (True, False):
         s = torch.full((rows, width), float("nan"), dtype=torch.float32, device="cuda")
-        csa2.indexer_score(q, w, k, rb, pos, 2, 0.01, s, shared_plane=shared)
+        csa2.indexer_score(q, w, k, rb, pos, ratio, 0.01, s, shared_plane=shared)
         out[shared] = s
     torch.cuda.synchronize()
     assert not torch.isnan(out[True]).any()
     assert torch.equal(out[True], out[False])
-    nv = ((pos + 1) // 2).clamp(max=width).cpu().numpy()
+    nv = ((pos + 1) // ratio).clamp(max=width).cpu().numpy()
     got = out[True].cpu().numpy()
     for r in range(rows):
         assert np.all(got[r, nv[r]:] == -np.inf) and np.all(np.isfinite(got[r, :nv[r]]))
@@ -331,7 +335,7 @@ def test_shared_plane_scores_equal_per_row_path(rows, width, base):
             continue
         kk = k[base:base + n].double().cpu().numpy()
         ref = oracle.indexer.scores_full(q[r:r + 1].double().cpu().numpy(), w[r:r + 1].double().cpu().numpy(),
-                                         lambda i: kk, np.array([2 * n - 1]), 2, tau, n)[0]
+                                         lambda i: kk, np.array([ratio * n - 1]), ratio, tau, n)[0]
         bound = oracle.indexer.score_abs_bound(q[r].double().cpu().numpy(), w[r].double().cpu().numpy(), kk, tau)
         assert np.all(np.abs(got[r, :n] - ref) <= SCORE_TOL * bound)
 

@@ -56,12 +56,14 @@ CASES = {
     "ratio2": (CONFIGS["lowp_full_decode_1m"].replace(batch=4, q_tokens=4, context=80001, ratio=2, ragged=True), 512),
     "ties": (CONFIGS["lowp_full_decode_1m"].replace(batch=4, q_tokens=4, context=40000), 512),
     "full_1m": (CONFIGS["lowp_full_decode_1m"].replace(batch=3, q_tokens=3), 512),
+    "k1_short_rows": (CONFIGS["lowp_full_decode_1m"].replace(batch=5, q_tokens=5, context=60000, ragged=True), 1),
     # MXFP4 index plane and query
     "mx_ragged_100k": (_MX.replace(batch=6, q_tokens=6, context=100003, ragged=True), 512),
     "mx_short_rows": (_MX.replace(batch=5, q_tokens=5, context=30000, ragged=True), 512),
     "mx_k2048_ratio2": (_MX.replace(batch=4, q_tokens=4, context=80001, ratio=2), 2048),
     "mx_ties": (_MX.replace(batch=4, q_tokens=4, context=40000), 512),
     "mx_full_1m": (_MX.replace(batch=3, q_tokens=3), 512),
+    "mx_k1": (_MX.replace(batch=4, q_tokens=4, context=200001, ragged=True), 1),
 }
 
 
