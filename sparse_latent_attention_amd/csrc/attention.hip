@@ -387,6 +387,40 @@ __device__ __forceinline__ void store_pair(const RawPair& raw, bool swa_tile, CT
     store_v4<CT, D, VS>(Vt, jb, x8, v);
 }
 
+// Tile pairs (BF16, D = 512): the two tiles of a pair share one PV copy in
+// which column d of entries 4jb .. 4jb + 3 holds the first tile's 4 values
+// and then the second tile's, so one 16-byte read gives a lane both halves
+// of its 16x16x32 operand.  Block jb starts at jb * kPairVS; column d sits at
+// 8 (d ^ ((d >> 3) & 7)) within it, which spreads a wave's 8-byte stores (one
+// column per lane, 8 columns apart) over the banks, while 8 lanes reading 8
+// consecutive columns still read 128 contiguous bytes.  The 64-element pad
+// shifts consecutive blocks by half a bank row.
+constexpr int kPairVS = 512 * 8 + 64;
+__device__ __forceinline__ int pair_vcol(int d) { return 8 * (d ^ ((d >> 3) & 7)); }
+
+template <int KVT, int SWT>
+__device__ __forceinline__ void store_pair_paired(const RawPair& raw, bool swa_tile, __bf16* Kt, __bf16* V01,
+                                                  int tip, int jb, int x8) {
+    Pack8<__bf16> v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (swa_tile) raw_convert<SWT, __bf16>(raw, i, v[i]);
+        else raw_convert<KVT, __bf16>(raw, i, v[i]);
+        store_k<__bf16, 512, 512>(Kt, 4 * jb + i, x8, v[i]);
+    }
+    __bf16* vb = V01 + jb * kPairVS + 4 * tip;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t lo01 = (v[0].w[q] & 0xffffu) | (v[1].w[q] << 16);
+        const uint32_t lo23 = (v[2].w[q] & 0xffffu) | (v[3].w[q] << 16);
+        const uint32_t hi01 = (v[0].w[q] >> 16) | (v[1].w[q] & 0xffff0000u);
+        const uint32_t hi23 = (v[2].w[q] >> 16) | (v[3].w[q] & 0xffff0000u);
+        const int d = 8 * x8 + 2 * q;
+        *reinterpret_cast<u32x2*>(vb + pair_vcol(d)) = u32x2{lo01, lo23};
+        *reinterpret_cast<u32x2*>(vb + pair_vcol(d + 1)) = u32x2{hi01, hi23};
+    }
+}
+
 template <class CT, int D>
 struct TileGeom {
     static constexpr int KS = (D == 512) ? 512 : 68;                // Kt row stride (elements)
@@ -472,6 +506,90 @@ __device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_
     }
 }
 
+// Two tiles at once (BF16, D = 512): the scores of both, one softmax update
+// over their 32 entries, and PV as 16x16x32 MFMAs.  Slot 8g + i of such an
+// MFMA's 32-long reduction is entry 4g + i of tile 0 for i < 4 and entry
+// 4g + i - 4 of tile 1 otherwise, in both operands: a lane's P^T fragment is
+// then its 4 probabilities of each tile side by side, and its V^T fragment the
+// same 4 entries' column from each tile's PV copy.  On gfx950 a 16x16x32 MFMA
+// takes about as long as a 16x16x16 one (measured: 1.44 against 0.81 PFLOP/s
+// sustained), so this halves the PV matrix time.  Two score chains per tile.
+template <int NACC>
+__device__ __forceinline__ void tile_pair_compute(const __bf16* Kt0, const __bf16* Kt1, const __bf16* V01,
+                                                  uint32_t vm0, uint32_t vm1, const bf16x8* qf, float scale_log2,
+                                                  int g, int li, float& m, float& l, f32x4* acc, int dt0) {
+    constexpr int NS = 512 / 32;
+    // Operand offsets: the lane-dependent part takes 4 values (by s mod 4 for K, by dt mod 4 for
+    // the PV copy: pair_vcol(16 (dt0 + dt) + li) with dt0 a multiple of 8); the rest is constant.
+    int ko[4], vo[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        ko[b] = li * 512 + 32 * (b ^ (li >> 2)) + 8 * (g ^ (li & 3));
+        vo[b] = g * kPairVS + 128 * dt0 + 8 * (16 * b + (li & 8) + ((li & 7) ^ ((2 * b + (li >> 3)) & 7)));
+    }
+    f32x4 part[4];  // chains 0, 1: tile 0; chains 2, 3: tile 1
+#pragma unroll
+    for (int k = 0; k < 4; ++k) part[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int k_off = ko[s & 3] + 128 * (s >> 2);
+        part[s & 1] = Mma<__bf16>::k32(part[s & 1], lds_frag8<__bf16>(Kt0 + k_off), qf[s]);
+        part[2 + (s & 1)] = Mma<__bf16>::k32(part[2 + (s & 1)], lds_frag8<__bf16>(Kt1 + k_off), qf[s]);
+    }
+    // Keep QK_AHEAD operand reads in flight ahead of the matrix instructions.
+    constexpr int QK_AHEAD = 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, QK_AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NS - QK_AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, QK_AHEAD, 0);
+    const f32x4 st0 = part[0] + part[1], st1 = part[2] + part[3];
+    float x[8];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        x[rr] = st0[rr] * scale_log2;
+        x[4 + rr] = st1[rr] * scale_log2;
+    }
+    if ((vm0 & vm1) != 0xffffu) {  // the same for the whole wave
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            x[rr] = ((vm0 >> (4 * g + rr)) & 1u) ? x[rr] : kNegInf;
+            x[4 + rr] = ((vm1 >> (4 * g + rr)) & 1u) ? x[4 + rr] : kNegInf;
+        }
+    }
+    float tmax_all = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    tmax_all = fmaxf(tmax_all, shfl_xor(tmax_all, 16));
+    tmax_all = fmaxf(tmax_all, shfl_xor(tmax_all, 32));
+    // lazy rescaling, as in tile_compute
+    const uint64_t need_rescale = __ballot(tmax_all > m + 8.f);
+    if (__builtin_expect(__builtin_amdgcn_readfirstlane((uint32_t)(need_rescale | (need_rescale >> 32))) != 0u, 0)) {
+        const float m_new = fmaxf(m, tmax_all);
+        const float alpha = exp2f(m - m_new);  // 0 when m was -inf
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NACC; ++dt) acc[dt] *= alpha;
+        m = m_new;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const float m_use = (m == kNegInf) ? 0.f : m;
+    float pr[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        pr[e] = __builtin_amdgcn_exp2f(x[e] - m_use);  // x - m_use <= 8; -inf -> 0
+        psum += pr[e];
+    }
+    l += psum;
+    const bf16x8 pb = __builtin_bit_cast(
+        bf16x8, u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]), pack_bf16x2(pr[4], pr[5]),
+                      pack_bf16x2(pr[6], pr[7])});
+#pragma unroll
+    for (int dt = 0; dt < NACC; ++dt)
+        acc[dt] = Mma<__bf16>::k32(acc[dt], lds_frag8<__bf16>(V01 + vo[dt & 3] + 512 * (dt >> 2)), pb);
+}
+
 // Normalises, rotates the rope tail back and stores 4 consecutive elements.
 template <int D, int R, int OT>
 __device__ __forceinline__ void emit4(void* out, int64_t off, int d0, f32x4 a, float inv, const float* rope_cs) {
@@ -508,9 +626,13 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     constexpr int TT = NT / TPR;                // threads per tile
     constexpr int PPT = (PAIRS + TT - 1) / TT;  // pairs per thread
 
-    __shared__ __attribute__((aligned(16))) CT tiles[2 * TPR][G::K_ELEMS + G::V_ELEMS];
+    // Tile pairs (see kPairVS) for the BF16 512-wide shape with two tiles per round.
+    constexpr bool PAIRED = TPR == 2 && D == 512 && sizeof(CT) == 2;
+    // One buffer set per round parity: TPR tiles (paired: two K tiles, then their shared PV copy).
+    constexpr int SET_ELEMS = PAIRED ? 2 * G::K_ELEMS + 4 * kPairVS : TPR * (G::K_ELEMS + G::V_ELEMS);
+    __shared__ __attribute__((aligned(16))) CT tiles[2][SET_ELEMS];
     __shared__ float rope_cs[R];
-    __shared__ uint32_t vmask[kMaxTiles];  // validity bits of each tile's 16 entries, written once
+    __shared__ uint32_t vmask[kMaxTiles + 1];  // validity bits of each tile's 16 entries, written once
     __shared__ __attribute__((aligned(16))) int32_t sel[kMaxTopk];  // this row's selected indices
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -538,9 +660,10 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     typename Mma<CT>::Frag8 qf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-        qf[s] = (h < H) ? load_q_frag<QT, CT, D>(p.q, ((int64_t)c.r * H + h) * D, s, g) : zero_frag8<CT>();
+        qf[s] = (H % 16 == 0 || h < H) ? load_q_frag<QT, CT, D>(p.q, ((int64_t)c.r * H + h) * D, s, g)
+                                       : zero_frag8<CT>();
     float m = kNegInf, l = 0.f;
-    if (h < H) {
+    if (H % 16 == 0 || h < H) {
         m = p.sink[h] * kLog2e;  // the sink is the initial state: max = sink, sum = 1
         l = (g == 0) ? 1.f : 0.f;
     }
@@ -556,20 +679,43 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
             if (pr < PAIRS) load_pair<D, KVT, SWT, DECODE>(p, c, sel, tile, pr / (D / 8), pr % (D / 8), raw[k]);
         }
     };
+    // Tile buffer b = TPR * set + i: its K tile, and its PV copy (paired: the set's shared one).
+    auto kbuf = [&](int b) -> CT* {
+        return tiles[b / TPR] + (b % TPR) * (PAIRED ? G::K_ELEMS : G::K_ELEMS + G::V_ELEMS);
+    };
+    auto vbuf = [&](int b) -> CT* {
+        return PAIRED ? tiles[b / TPR] + 2 * G::K_ELEMS : kbuf(b) + G::K_ELEMS;
+    };
     auto store_tile = [&](int tile, int b) {  // tile into buffer b
-        CT* Kt = tiles[b];
-        CT* Vt = tiles[b] + G::K_ELEMS;
+        CT* Kt = kbuf(b);
+        CT* Vt = vbuf(b);
         uint32_t bits = 0;
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
             const int pr = tl + k * TT;
             if (pr < PAIRS) {
                 const int jb = pr / (D / 8), x8 = pr % (D / 8);
-                store_pair<D, CT, G::KS, G::VS, KVT, SWT>(raw[k], tile * 16 < p.window, Kt, Vt, jb, x8);
+                if constexpr (PAIRED)
+                    store_pair_paired<KVT, SWT>(raw[k], tile * 16 < p.window, Kt, Vt, b % TPR, jb, x8);
+                else
+                    store_pair<D, CT, G::KS, G::VS, KVT, SWT>(raw[k], tile * 16 < p.window, Kt, Vt, jb, x8);
                 if (x8 == 0) bits |= raw[k].valid << (4 * jb);
             }
         }
         if (bits) atomicOr(&vmask[tile], bits);
+    };
+    // With tile pairs, an odd tile count leaves the last pair's second buffer without a tile:
+    // it is zero-filled (its mask is empty, so it adds exactly nothing).
+    auto zero_tile = [&](int b) {
+        if constexpr (PAIRED) {
+            RawPair z;
+            z.valid = 0u;  // every row invalid: the stores write zeros
+#pragma unroll
+            for (int k = 0; k < PPT; ++k) {
+                const int pr = tl + k * TT;
+                if (pr < PAIRS) store_pair_paired<KVT, SWT>(z, false, kbuf(b), vbuf(b), b % TPR, pr / 64, pr % 64);
+            }
+        }
     };
 
     __syncthreads();  // rope table and vmask reset visible
@@ -577,23 +723,34 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     if (ts < n_tiles) {
         load_tile(ts);
         store_tile(ts, ts);
+    } else if (PAIRED && ts == n_tiles) {
+        zero_tile(ts);
     }
     if (TPR + ts < n_tiles) load_tile(TPR + ts);
     __syncthreads();
     for (int rd = 0; rd < n_rounds; ++rd) {
         const int bs = (rd & 1) * TPR;
+        if constexpr (PAIRED) {
+            // (an odd last tile is paired with the zero-filled buffer, under an empty mask)
+            const int t = 2 * rd;
+            tile_pair_compute<NDT>(kbuf(bs), kbuf(bs + 1), vbuf(bs), vmask[t], t + 1 < n_tiles ? vmask[t + 1] : 0u,
+                                   qf, p.scale_log2, g, li, m, l, acc, dt0);
+        } else {
 #pragma unroll
-        for (int jt = 0; jt < TPR; ++jt) {
-            const int t = rd * TPR + jt;
-            if (t < n_tiles)
-                tile_compute<D, CT, G::KS, G::VS, NDT>(tiles[bs + jt], tiles[bs + jt] + G::K_ELEMS, vmask[t], qf,
-                                                       p.scale_log2, g, li, m, l, acc, dt0);
+            for (int jt = 0; jt < TPR; ++jt) {
+                const int t = rd * TPR + jt;
+                if (t < n_tiles)
+                    tile_compute<D, CT, G::KS, G::VS, NDT>(kbuf(bs + jt), vbuf(bs + jt), vmask[t], qf, p.scale_log2,
+                                                           g, li, m, l, acc, dt0);
+            }
         }
         // the next round's tiles go into the other buffer set; its loads were issued a round ago
         const int tn = (rd + 1) * TPR + ts;
         if (tn < n_tiles) {
             store_tile(tn, (bs ^ TPR) + ts);
             if (tn + TPR < n_tiles) load_tile(tn + TPR);
+        } else if (PAIRED && tn == n_tiles && (n_tiles & 1)) {
+            zero_tile((bs ^ TPR) + ts);
         }
         __syncthreads();
     }
