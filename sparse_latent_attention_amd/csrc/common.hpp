@@ -156,6 +156,15 @@ __device__ __forceinline__ f32x4 mma_fp8_k128(f32x4 c, i32x8 a, i32x8 b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// s_waitcnt vmcnt(0): every vector-memory load of this wave has returned.
+// Issued after loads made before a loop that loads again, it keeps the
+// compiler's wait insertion -- which cannot order conditional loads across
+// the loop's back edge -- from making the first use of those earlier values
+// inside the loop wait for the loop's own loads still in flight.
+__device__ __forceinline__ void wait_vmem_all() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0; expcnt 7 and lgkmcnt 15: no wait
+}
+
 // Keeps the compiler from moving LDS accesses of one wave across this point.
 __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");

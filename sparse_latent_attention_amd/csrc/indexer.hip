@@ -350,6 +350,7 @@ __global__ __launch_bounds__(64 * ROWS) void indexer_chunk_kernel(const IndexPar
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) wr[t][rr] = p.w[(int64_t)rq * 64 + 16 * t + 4 * g + rr];
     }
+    wait_vmem_all();  // q and w are in registers before the staging loop starts loading
 
     // Staging: chunk i = thread + NT j of the stage is 16-byte chunk i % 16 of key row i / 16
     // (consecutive threads read consecutive bytes; zeros past the visible columns).
@@ -379,10 +380,12 @@ __global__ __launch_bounds__(64 * ROWS) void indexer_chunk_kernel(const IndexPar
     }
     __syncthreads();
     for (; cs < c_live; cs += KEYS) {
-        // the next stage's loads are in flight while this stage is computed
-        const bool more = cs + KEYS < c_live;
+        // The next stage's loads are in flight while this stage is computed.  After the last
+        // stage this fetches nothing and stages zeros: unconditional, so the compiler's wait
+        // insertion sees every staged value consumed before the next fetch.
         u32x4 x[NCH];
-        if (more) fetch(cs + KEYS, x);
+        fetch(cs + KEYS, x);
+        float vlast[4];  // the stage's last 64 scores, stored after the staging writes (below)
         if (live) {
             const uint8_t* tb = tile[b];
             // B operands of the next 16 keys are read from LDS while this 16 keys' MFMAs run
@@ -413,12 +416,25 @@ __global__ __launch_bounds__(64 * ROWS) void indexer_chunk_kernel(const IndexPar
                     }
                     v[u] = acc_sum;
                 }
-                const int64_t cb = cs + 64 * st;
-                const int64_t c_out = cb + lane;
-                store_step<false, false>(p, rq, nv, cb, c1, lane, v, p.scale, c_out < c1 && c_out < nv, srow, nullptr);
+                if (st + 1 < KEYS / 64) {
+                    const int64_t cb = cs + 64 * st;
+                    const int64_t c_out = cb + lane;
+                    store_step<false, false>(p, rq, nv, cb, c1, lane, v, p.scale, c_out < c1 && c_out < nv, srow,
+                                             nullptr);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) vlast[u] = v[u];
+                }
             }
         }
-        if (more) put(b ^ 1, x);
+        // The staging writes wait for the next stage's loads; the score stores issued after them
+        // (the stage's last step) are then not waited for before the barrier.
+        put(b ^ 1, x);
+        if (live) {
+            const int64_t cb = cs + KEYS - 64;
+            const int64_t c_out = cb + lane;
+            store_step<false, false>(p, rq, nv, cb, c1, lane, vlast, p.scale, c_out < c1 && c_out < nv, srow, nullptr);
+        }
         __syncthreads();
         b ^= 1;
     }
