@@ -516,22 +516,24 @@ __device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_
 // sustained), so this halves the PV matrix time.  Two score chains per tile.
 template <int NACC>
 __device__ __forceinline__ void tile_pair_compute(const __bf16* Kt0, const __bf16* Kt1, const __bf16* V01,
-                                                  uint32_t vm0, uint32_t vm1, const bf16x8* qf, float scale_log2,
-                                                  int g, int li, float& m, float& l, f32x4* acc, int dt0) {
-    constexpr int NS = 512 / 32;
+                                                  uint32_t vm0, uint32_t vm1, const bf16x8* qf, int half,
+                                                  f32x4* xch_mine, const f32x4* xch_partner, float scale_log2,
+                                                  int g, int li, int lane, float& m, float& l, f32x4* acc, int dt0) {
+    constexpr int NS = 512 / 32, NH = NS / 2;
     // Operand offsets: the lane-dependent part takes 4 values (by s mod 4 for K, by dt mod 4 for
     // the PV copy: pair_vcol(16 (dt0 + dt) + li) with dt0 a multiple of 8); the rest is constant.
+    // This wave's half of the reduction is k-steps NH * half .. NH * half + NH - 1 (256 elements on).
     int ko[4], vo[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        ko[b] = li * 512 + 32 * (b ^ (li >> 2)) + 8 * (g ^ (li & 3));
+        ko[b] = li * 512 + 32 * (b ^ (li >> 2)) + 8 * (g ^ (li & 3)) + 256 * half;
         vo[b] = g * kPairVS + 128 * dt0 + 8 * (16 * b + (li & 8) + ((li & 7) ^ ((2 * b + (li >> 3)) & 7)));
     }
     f32x4 part[4];  // chains 0, 1: tile 0; chains 2, 3: tile 1
 #pragma unroll
     for (int k = 0; k < 4; ++k) part[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
+    for (int s = 0; s < NH; ++s) {
         const int k_off = ko[s & 3] + 128 * (s >> 2);
         part[s & 1] = Mma<__bf16>::k32(part[s & 1], lds_frag8<__bf16>(Kt0 + k_off), qf[s]);
         part[2 + (s & 1)] = Mma<__bf16>::k32(part[2 + (s & 1)], lds_frag8<__bf16>(Kt1 + k_off), qf[s]);
@@ -540,12 +542,19 @@ __device__ __forceinline__ void tile_pair_compute(const __bf16* Kt0, const __bf1
     constexpr int QK_AHEAD = 4;
     __builtin_amdgcn_sched_group_barrier(0x100, QK_AHEAD, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * NS - QK_AHEAD; ++i) {
+    for (int i = 0; i < 2 * NH - QK_AHEAD; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, QK_AHEAD, 0);
-    const f32x4 st0 = part[0] + part[1], st1 = part[2] + part[3];
+    // The two waves of a head group exchange their halves through LDS; a + b == b + a exactly,
+    // so both form bit-identical scores and softmax states.
+    f32x4 st0 = part[0] + part[1], st1 = part[2] + part[3];
+    xch_mine[lane] = st0;
+    xch_mine[64 + lane] = st1;
+    __syncthreads();
+    st0 = st0 + xch_partner[lane];
+    st1 = st1 + xch_partner[64 + lane];
     float x[8];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -631,6 +640,8 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     // One buffer set per round parity: TPR tiles (paired: two K tiles, then their shared PV copy).
     constexpr int SET_ELEMS = PAIRED ? 2 * G::K_ELEMS + 4 * kPairVS : TPR * (G::K_ELEMS + G::V_ELEMS);
     __shared__ __attribute__((aligned(16))) CT tiles[2][SET_ELEMS];
+    // Paired: per wave, the partial scores of its half of the reduction (2 tiles x 64 lanes).
+    __shared__ f32x4 xch[PAIRED ? 128 * NW : 1];
     __shared__ float rope_cs[R];
     __shared__ uint32_t vmask[kMaxTiles + 1];  // validity bits of each tile's 16 entries, written once
     __shared__ __attribute__((aligned(16))) int32_t sel[kMaxTopk];  // this row's selected indices
@@ -657,10 +668,13 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
 
     const int h = 16 * (wave / DS) + li;
     const int dt0 = (wave % DS) * NDT;  // this wave's first 16-column output block
-    typename Mma<CT>::Frag8 qf[NS];
+    // Paired: the two waves of a head group each hold and reduce over half of the query.
+    constexpr int NQ = PAIRED ? NS / 2 : NS;
+    const int s0 = PAIRED ? (wave % 2) * NQ : 0;
+    typename Mma<CT>::Frag8 qf[NQ];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-        qf[s] = (H % 16 == 0 || h < H) ? load_q_frag<QT, CT, D>(p.q, ((int64_t)c.r * H + h) * D, s, g)
+    for (int s = 0; s < NQ; ++s)
+        qf[s] = (H % 16 == 0 || h < H) ? load_q_frag<QT, CT, D>(p.q, ((int64_t)c.r * H + h) * D, s0 + s, g)
                                        : zero_frag8<CT>();
     float m = kNegInf, l = 0.f;
     if (H % 16 == 0 || h < H) {
@@ -734,7 +748,8 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
             // (an odd last tile is paired with the zero-filled buffer, under an empty mask)
             const int t = 2 * rd;
             tile_pair_compute<NDT>(kbuf(bs), kbuf(bs + 1), vbuf(bs), vmask[t], t + 1 < n_tiles ? vmask[t + 1] : 0u,
-                                   qf, p.scale_log2, g, li, m, l, acc, dt0);
+                                   qf, wave % 2, xch + 128 * wave, xch + 128 * (wave ^ 1), p.scale_log2, g, li,
+                                   lane, m, l, acc, dt0);
         } else {
 #pragma unroll
             for (int jt = 0; jt < TPR; ++jt) {
