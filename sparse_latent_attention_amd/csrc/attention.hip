@@ -460,6 +460,16 @@ __device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_
         const int k_off = (D == 512) ? ko[s & 3] + 128 * (s >> 2) : kpos<D>(li, 4 * s + g);
         part[s % NC] = M::k32(part[s % NC], lds_frag8<CT>(Kt + k_off), qf[s]);
     }
+    if constexpr (sizeof(CT) == 2) {
+        // keep 4 operand reads in flight ahead of the matrix instructions
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < NS - 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
     f32x4 st = part[0];
 #pragma unroll
     for (int k = 1; k < NC; ++k) st += part[k];
@@ -845,6 +855,7 @@ __global__ __launch_bounds__(256 * DS) void attn_decode_kernel(const AttnParams 
         m = p.sink[h] * kLog2e;
         l = (g == 0) ? 1.f : 0.f;
     }
+    wait_vmem_all();  // q and the sink in registers before the tile loop starts gathering
     f32x4 acc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
