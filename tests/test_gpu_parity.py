@@ -125,6 +125,26 @@ def test_attention_ragged_tile_counts(base, rows, window, topk):
     assert_close(out[torch.from_numpy(sample).cuda()], ref, BF16_ATOL, BF16_RTOL, f"{base} W={window} k={topk}")
 
 
+@pytest.mark.parametrize("window", [16, 48])
+@pytest.mark.parametrize("base,rows", [("full_decode_small", 5), ("full_decode_small", 300), ("lowp_small", 7),
+                                       ("prefill_small", None)])
+def test_attention_window_only(base, rows, window):
+    """No selected rows (top-k 0): 1 or 3 tiles, all from the window.  One tile leaves the rows kernel's
+    first tile pair with only its zero-filled partner."""
+    cfg = SMALL[base].replace(window=window, topk=0)
+    if rows is not None:
+        cfg = cfg.replace(batch=rows, q_tokens=rows)
+    else:
+        cfg = cfg.replace(reuse_layers=0)
+    print(f"\n[window only] {base} rows={cfg.q_tokens} window={window}", flush=True)
+    x = make_inputs(cfg, 10, device="cuda")
+    idx = torch.empty(cfg.q_tokens, 0, dtype=torch.int32, device="cuda")
+    out = gpu_attention(cfg, x, idx)
+    sample = np.unique(np.linspace(0, cfg.q_tokens - 1, min(cfg.q_tokens, 10)).astype(int))
+    ref = oracle_attention(cfg, x, idx.cpu().numpy()[sample], sample)
+    assert_close(out[torch.from_numpy(sample).cuda()], ref, BF16_ATOL, BF16_RTOL, f"{base} W={window} k=0")
+
+
 def test_injected_indices_and_masks():
     # -1 padding, duplicates, rows the group-causal mask hides, far out-of-range rows
     cfg = SMALL["lowp_small"]
