@@ -732,8 +732,7 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     // it is zero-filled (its mask is empty, so it adds exactly nothing).
     auto zero_tile = [&](int b) {
         if constexpr (PAIRED) {
-            RawPair z;
-            z.valid = 0u;  // every row invalid: the stores write zeros
+            RawPair z = {};  // every row invalid (valid == 0): the stores write zeros
 #pragma unroll
             for (int k = 0; k < PPT; ++k) {
                 const int pr = tl + k * TT;
