@@ -430,31 +430,24 @@ struct TileGeom {
     static constexpr int BYTES = (K_ELEMS + V_ELEMS) * (int)sizeof(CT);
 };
 
-// One wave's work on one tile for its 16 heads: scores, online softmax, PV.
-// The wave accumulates output columns 16 dt0 .. 16 (dt0 + NACC) - 1 (all of D
-// by default); the scores and the softmax state always cover the whole row.
-template <int D, class CT, int KS, int VS, int NACC = D / 16>
-__device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_t vm, const typename Mma<CT>::Frag8* qf,
-                                             float scale_log2, int g, int li, float& m, float& l, f32x4* acc,
-                                             int dt0 = 0) {
+// Scores S^T of one tile for the wave's 16 heads over NSQ of the D / 32 k-steps,
+// starting koff elements into each row (all of them by default).
+template <int D, class CT, int KS, int NSQ = D / 32>
+__device__ __forceinline__ f32x4 tile_scores(const CT* Kt, const typename Mma<CT>::Frag8* qf, int g, int li,
+                                             int koff = 0) {
     typedef Mma<CT> M;
-    constexpr int NS = D / 32;
+    constexpr int NS = NSQ;
     // Four independent accumulation chains keep the matrix cores busy.
     constexpr int NC = NS >= 4 ? 4 : NS;
     f32x4 part[NC];
 #pragma unroll
     for (int k = 0; k < NC; ++k) part[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Operand addresses.  With the D = 512 layouts the lane-dependent part of
-    // kpos(li, 4s + g) takes 4 values (by s mod 4) and that of the PV column
-    // 16 (dt0 + dt) + li another 4 (by dt mod 4, dt0 a multiple of 8); the
-    // rest is a compile-time offset.
-    int ko[4], vo[4];
+    // Operand addresses.  With the D = 512 layout the lane-dependent part of
+    // kpos(li, 4s + g) takes 4 values (by s mod 4); the rest is a compile-time offset.
+    int ko[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        ko[b] = (D == 512) ? li * 512 + 32 * (b ^ (li >> 2)) + 8 * (g ^ (li & 3)) : kpos<D>(li, 4 * b + g);
-        vo[b] = (D == 512) ? g * VS + 64 * dt0 + 4 * (16 * b + (li & 8) + ((li & 7) ^ ((2 * b + (li >> 3)) & 7)))
-                           : g * VS + vcol<D>(16 * (dt0 + b) + li);
-    }
+    for (int b = 0; b < 4; ++b)
+        ko[b] = (D == 512) ? li * 512 + 32 * (b ^ (li >> 2)) + 8 * (g ^ (li & 3)) + koff : kpos<D>(li, 4 * b + g);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int k_off = (D == 512) ? ko[s & 3] + 128 * (s >> 2) : kpos<D>(li, 4 * s + g);
@@ -473,6 +466,19 @@ __device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_
     f32x4 st = part[0];
 #pragma unroll
     for (int k = 1; k < NC; ++k) st += part[k];
+    return st;
+}
+
+// The online-softmax update and PV of one tile, given its full scores st.
+template <int D, class CT, int VS, int NACC = D / 16>
+__device__ __forceinline__ void tile_update(f32x4 st, const CT* Vt, uint32_t vm, float scale_log2, int g, int li,
+                                            float& m, float& l, f32x4* acc, int dt0 = 0) {
+    typedef Mma<CT> M;
+    int vo[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        vo[b] = (D == 512) ? g * VS + 64 * dt0 + 4 * (16 * b + (li & 8) + ((li & 7) ^ ((2 * b + (li >> 3)) & 7)))
+                           : g * VS + vcol<D>(16 * (dt0 + b) + li);
     float x[4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) x[rr] = st[rr] * scale_log2;
@@ -514,6 +520,16 @@ __device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_
         const int v_off = (D == 512) ? vo[dt & 3] + 256 * (dt >> 2) : g * VS + vcol<D>(16 * (dt0 + dt) + li);
         acc[dt] = M::k16(acc[dt], lds_frag4<CT>(Vt + v_off), pb);
     }
+}
+
+// One wave's work on one tile for its 16 heads: scores, online softmax, PV.
+// The wave accumulates output columns 16 dt0 .. 16 (dt0 + NACC) - 1 (all of D
+// by default); the scores and the softmax state always cover the whole row.
+template <int D, class CT, int KS, int VS, int NACC = D / 16>
+__device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_t vm, const typename Mma<CT>::Frag8* qf,
+                                             float scale_log2, int g, int li, float& m, float& l, f32x4* acc,
+                                             int dt0 = 0) {
+    tile_update<D, CT, VS, NACC>(tile_scores<D, CT, KS>(Kt, qf, g, li), Vt, vm, scale_log2, g, li, m, l, acc, dt0);
 }
 
 // Two tiles at once (BF16, D = 512): the scores of both, one softmax update
@@ -816,6 +832,10 @@ __global__ __launch_bounds__(256 * DS) void attn_decode_kernel(const AttnParams 
     __shared__ float rope_cs[R];
     __shared__ float ml[4][2][16];
     __shared__ __attribute__((aligned(16))) int32_t sel[kMaxTopk];  // this row's selected indices
+    // BF16 512-wide with wave pairs: the two waves of a group each reduce the scores over half of
+    // the 512 dimensions and exchange the halves here (a + b == b + a: identical scores in both).
+    constexpr bool SPLIT = DS == 2 && D == 512 && sizeof(CT) == 2;
+    __shared__ f32x4 xch[SPLIT ? 64 * 4 * DS : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
@@ -844,10 +864,12 @@ __global__ __launch_bounds__(256 * DS) void attn_decode_kernel(const AttnParams 
 
     const int h = 16 * hg + li;
     const int dt0 = dh * NDT;
-    typename Mma<CT>::Frag8 qf[NS];
+    constexpr int NQ = SPLIT ? NS / 2 : NS;
+    typename Mma<CT>::Frag8 qf[NQ];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-        qf[s] = (h < H) ? load_q_frag<QT, CT, D>(p.q, ((int64_t)c.r * H + h) * D, s, g) : zero_frag8<CT>();
+    for (int s = 0; s < NQ; ++s)
+        qf[s] = (h < H) ? load_q_frag<QT, CT, D>(p.q, ((int64_t)c.r * H + h) * D, (SPLIT ? dh * NQ : 0) + s, g)
+                        : zero_frag8<CT>();
     // Group 0 carries the sink (max = sink, sum = 1); the others start empty.
     float m = kNegInf, l = 0.f;
     if (grp == 0 && h < H) {
@@ -900,7 +922,15 @@ __global__ __launch_bounds__(256 * DS) void attn_decode_kernel(const AttnParams 
         }
         __syncthreads();  // every group's tile is in LDS
         if (t + 4 < n_tiles) load_tile(t + 4);  // next round's bytes in flight during this round
-        if (mine) {
+        if constexpr (SPLIT) {
+            f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (mine) st = tile_scores<D, CT, G::KS, NQ>(Kt, qf, g, li, 256 * dh);
+            xch[64 * wave + lane] = st;
+            __syncthreads();  // both halves of every group's scores written
+            if (mine)
+                tile_update<D, CT, G::VS, NDT>(st + xch[64 * (wave ^ 1) + lane], Vt, tile_mask(t), p.scale_log2, g,
+                                               li, m, l, acc, dt0);
+        } else if (mine) {
             const uint32_t vm = tile_mask(t);
             tile_compute<D, CT, G::KS, G::VS, NDT>(Kt, Vt, vm, qf, p.scale_log2, g, li, m, l, acc, dt0);
         }
