@@ -683,6 +683,9 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     c.dummy = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)c.r * H * D * (QT == CSA2_F32 ? 4 : 2);
     const int n_tiles = (p.window + p.topk) / 16;
 
+    // The first selected index of each thread is loaded before the float64 rope angles are
+    // computed, so that latency and the angles overlap.
+    const int32_t idx0 = tid < p.topk ? p.idx[(int64_t)c.r * p.topk + tid] : 0;
     if (tid < R / 2) {
         float cs, sn;
         rope_angle(c.pos, p.inv_freq[tid], cs, sn);
@@ -690,7 +693,8 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
         rope_cs[2 * tid + 1] = sn;
     }
     for (int i = tid; i < n_tiles; i += NT) vmask[i] = 0u;
-    for (int i = tid; i < p.topk; i += NT) sel[i] = p.idx[(int64_t)c.r * p.topk + i];
+    if (tid < p.topk) sel[tid] = idx0;
+    for (int i = tid + NT; i < p.topk; i += NT) sel[i] = p.idx[(int64_t)c.r * p.topk + i];
 
     const int h = 16 * (wave / DS) + li;
     const int dt0 = (wave % DS) * NDT;  // this wave's first 16-column output block
@@ -855,13 +859,6 @@ __global__ __launch_bounds__(256 * DS) void attn_decode_kernel(const AttnParams 
     c.dummy = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)c.r * H * D * (QT == CSA2_F32 ? 4 : 2);
     const int n_tiles = (p.window + p.topk) / 16;
 
-    if (tid < R / 2) {
-        float cs, sn;
-        rope_angle(c.pos, p.inv_freq[tid], cs, sn);
-        rope_cs[2 * tid] = cs;
-        rope_cs[2 * tid + 1] = sn;
-    }
-
     const int h = 16 * hg + li;
     const int dt0 = dh * NDT;
     constexpr int NQ = SPLIT ? NS / 2 : NS;
@@ -876,7 +873,15 @@ __global__ __launch_bounds__(256 * DS) void attn_decode_kernel(const AttnParams 
         m = p.sink[h] * kLog2e;
         l = (g == 0) ? 1.f : 0.f;
     }
-    wait_vmem_all();  // q and the sink in registers before the tile loop starts gathering
+    // The float64 rope angles are computed while the query, sink and first index loads are in flight.
+    const int32_t idx0 = tid < p.topk ? p.idx[(int64_t)c.r * p.topk + tid] : 0;
+    if (tid < R / 2) {
+        float cs, sn;
+        rope_angle(c.pos, p.inv_freq[tid], cs, sn);
+        rope_cs[2 * tid] = cs;
+        rope_cs[2 * tid + 1] = sn;
+    }
+    wait_vmem_all();  // q, the sink and idx0 in registers before the tile loop starts gathering
     f32x4 acc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -904,7 +909,8 @@ __global__ __launch_bounds__(256 * DS) void attn_decode_kernel(const AttnParams 
         return (uint32_t)__ballot(lane < 16 && v) & 0xffffu;
     };
 
-    for (int i = tid; i < p.topk; i += 256 * DS) sel[i] = p.idx[(int64_t)c.r * p.topk + i];
+    if (tid < p.topk) sel[tid] = idx0;
+    for (int i = tid + 256 * DS; i < p.topk; i += 256 * DS) sel[i] = p.idx[(int64_t)c.r * p.topk + i];
     __syncthreads();  // sel and rope_cs complete
     const int rounds = (n_tiles + 3) / 4;
     int t = grp;
