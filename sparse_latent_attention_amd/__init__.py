@@ -8,11 +8,18 @@ raises ``ImportError`` -- there is no CPU fallback.
 
 Entry points (same names as the C ABI in include/csa2.h):
 
-* ``indexer_score``        lightning-indexer scores, FULL or REINDEX
-* ``topk_select``          per-row top-k of the scores
+* ``indexer_score``        lightning-indexer scores, FULL or REINDEX (or, with
+                           ``scores=None``, only the block keys ``topk_rescore`` needs)
+* ``topk_select``          per-row top-k of written scores
+* ``topk_rescore``         top-k of FULL scores that were kept on chip
+* ``candidate_pool``       the FULL owner layer's 2048 x 8 REINDEX candidate blocks
 * ``sparse_attn_decode``   sink attention, SWA ring per query row
 * ``sparse_attn_prefill``  sink attention, one linear SWA array
+* ``compress``             the FULL owner layer's write path (compressor, main row, index key)
 * ``rope_inv_freq``        float64 RoPE / YaRN frequency table (host)
+
+``prepare_*`` variants marshal a call's arguments once and return a callable
+that only crosses into the library (what bench.py times).
 """
 
 import ctypes
@@ -168,6 +175,16 @@ def _need(t, dtype, name):
         raise ValueError(f"csa2: {name} must be {dtype}, got {t.dtype}")
 
 
+def _scratch(nbytes, device, stream):
+    """A workspace the call allocates itself.  It is allocated on torch's current stream; when the
+    call runs on another stream, the caching allocator is told so (record_stream), so the block is
+    not handed out again before that stream's kernels are done with it."""
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(ws.device):
+        ws.record_stream(stream)
+    return ws
+
+
 def rope_inv_freq(rope_dim, theta, yarn_factor=1.0, yarn_orig_len=0):
     """float64 frequency table computed by the library on the host (CPU tensor)."""
     out = (ctypes.c_double * (rope_dim // 2))()
@@ -300,7 +317,7 @@ def topk_rescore(q, w, k, row_base, pos, ratio, scale, out, block_keys, width, *
         raise ValueError("csa2.topk_rescore: out rows")
     need = topk_rescore_workspace_size(a.rows, a.width, out.shape[1])
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=out.device)
+        workspace = _scratch(need, out.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("csa2_topk_rescore", _lib.csa2_topk_rescore(ctypes.byref(a), out.shape[1], _ptr(out), _ptr(workspace),
                                                        ws_bytes, _stream(stream)))
@@ -338,7 +355,7 @@ def topk_select(scores, pos, ratio, out, *, cand=None, block_rows=8, key_hist=No
     a.key_hist = _ptr(key_hist)
     need = topk_workspace_size(rows, width, a.k)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+        workspace = _scratch(need, scores.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("csa2_topk_select", _lib.csa2_topk_select(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
@@ -386,7 +403,7 @@ def candidate_pool(pos, ratio, cand, *, scores=None, block_max=None, block_keys=
     a.block_keys = _ptr(block_keys)
     need = candidate_pool_workspace_size(rows, width, block_rows, a.n_cand)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=pos.device)
+        workspace = _scratch(need, pos.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("csa2_candidate_pool", _lib.csa2_candidate_pool(ctypes.byref(a), _ptr(workspace), ws_bytes,
                                                            _stream(stream)))
@@ -534,7 +551,7 @@ def compress(x, pos, slot, row_base, wkv, norm_w, wk, knorm_w, inv_freq, main_ou
         _ptr(idx_scale)
     need = compress_workspace_size(rows, d_in, ratio)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = _scratch(need, x.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("csa2_compress", _lib.csa2_compress(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)))
 

@@ -285,16 +285,20 @@ __device__ __forceinline__ void raw_convert(const RawPair& raw, int i, Pack8<CT>
         for (int e = 0; e < 8; ++e) o.v[e] = ok ? __uint_as_float(u[e]) : 0.f;
     } else if constexpr (DT == CSA2_FP4_E2M1 && sizeof(CT) == 2) {
         // E2M1 pairs straight to bf16 pairs, multiplied by the power-of-two block scale (exact).
+        // E8M0 byte 255 is NaN: every element of its block decodes to NaN (0 x NaN included),
+        // set explicitly rather than left to the convert's handling of a NaN scale.
         const uint32_t w = raw.v[i].x;
         const float sc = e8m0_to_f32(raw.sb[i]);
+        const bool nan_blk = raw.sb[i] == 255u;
+        constexpr uint32_t kNanPair = 0x7fc07fc0u;
         const uint32_t b0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
         const uint32_t b1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
         const uint32_t b2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
         const uint32_t b3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
-        o.w[0] = ok ? b0 : 0u;
-        o.w[1] = ok ? b1 : 0u;
-        o.w[2] = ok ? b2 : 0u;
-        o.w[3] = ok ? b3 : 0u;
+        o.w[0] = ok ? (nan_blk ? kNanPair : b0) : 0u;
+        o.w[1] = ok ? (nan_blk ? kNanPair : b1) : 0u;
+        o.w[2] = ok ? (nan_blk ? kNanPair : b2) : 0u;
+        o.w[3] = ok ? (nan_blk ? kNanPair : b3) : 0u;
     } else {
         // Exact in every case: an FP8 or FP4 value times a power of two, or an E2M1 value
         // (<= 2 significant bits) times an E4M3 scale (<= 4), fits bf16's 8 bits.

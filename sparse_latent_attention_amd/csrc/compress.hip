@@ -19,9 +19,10 @@
 //    consecutive k of row n: 16 contiguous bytes).  With few rows (decode) the
 //    K range is split over workgroups so the weights, the dominant bytes, are
 //    streamed by enough of them; partial tiles go to a workspace and are added
-//    in a fixed order, so the result does not depend on scheduling.  (At
-//    prefill sizes the operands are re-read by every tile from L2; an
-//    LDS-staged 128 x 128 tiling is the next step for this kernel.)
+//    in a fixed order, so the result does not depend on scheduling.  At
+//    prefill sizes (many rows, no split) compress_gemm_kernel takes the
+//    projections instead: 128 x 128 output tiles with both operands staged
+//    through LDS, so each fragment read feeds several MFMAs.
 //  * compress_finish_kernel: one workgroup per token row: pooling with its
 //    group partner (the previous row of the call, or the tail state), the two
 //    RMSNorms, the 128 x 512 index-key projection (thread pairs split each

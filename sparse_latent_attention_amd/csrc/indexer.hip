@@ -24,10 +24,47 @@ namespace csa2 {
 
 namespace {
 
-// ReLU as an integer max on the float's bits: every negative float and -0 has
-// a negative signed pattern and becomes +0; +0, positive values and +inf are
-// unchanged.  One instruction, where fmaxf would also canonicalise NaNs.
+// NaN rule: a NaN dot stays NaN through the per-head ReLU, so a score with
+// one is NaN (and ranks as -inf).  A NaN can only come from the inputs: a key
+// row holding a NaN makes its dot with every head NaN, a NaN in the query
+// makes every dot of that head NaN.  Both cases are carried without a NaN
+// test per dot:
+//   * relu_bits: ReLU as an integer max on the float's bits (one
+//     instruction): negative values, -0 and -inf become +0; positive values,
+//     +inf and NaNs with the sign bit clear pass unchanged;
+//   * nan_guard: each lane's weighted head sum starts from 0 x (its first raw
+//     dot), which is +-0, or NaN when that dot is NaN -- a NaN key row thus
+//     makes every column sum NaN, whatever the sign bits of its NaN dots;
+//   * a query row holding a NaN is found once per row (frag_has_nan) and its
+//     scores are set to NaN.
+// (Dots beyond the float32 range are outside the inputs the path takes.)
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+__device__ __forceinline__ float nan_guard(float raw_dot) { return raw_dot * 0.f; }
+
+// Whether a query operand fragment holds a NaN element.
+__device__ __forceinline__ bool frag_has_nan(const bf16x8& f) {
+    const u32x4 d = __builtin_bit_cast(u32x4, f);
+    uint32_t m = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m |= ((d[e] & 0x7fff7fffu) + 0x007f007fu) & 0x80008000u;  // |half| > 0x7f80
+    return m != 0u;
+}
+__device__ __forceinline__ bool frag_has_nan(const F32x8& f) {
+    bool n = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) n |= f.v[e] != f.v[e];
+    return n;
+}
+// FP8-E4M3 codes: a byte is NaN iff its low 7 bits are all ones (zero-byte test on the complement).
+__device__ __forceinline__ bool frag_has_nan(const i32x8& f) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t v = ~(uint32_t)f[e] & 0x7f7f7f7fu;
+        m |= (v - 0x01010101u) & ~v & 0x80808080u;
+    }
+    return m != 0u;
+}
 
 // Plane row of column c and whether it is valid.
 template <bool REINDEX>
@@ -226,6 +263,12 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p)
             wr[t][rr] = (hw < HI) ? p.w[(int64_t)r * HI + hw] : 0.f;
         }
     }
+    bool qn = false;
+#pragma unroll
+    for (int t = 0; t < HT; ++t)
+#pragma unroll
+        for (int s = 0; s < S; ++s) qn |= frag_has_nan(qa[t][s]);
+    const float row_scale = __ballot(qn) != 0ull ? __builtin_nanf("") : p.scale;  // NaN query: NaN scores
 
     if (HIST) {
         for (int b = threadIdx.x; b < kKeyBins; b += 256) hist[b] = 0u;
@@ -252,7 +295,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p)
         const int64_t c_out = cb + lane;
         int64_t prow = 0;
         st.valid = (c_out < c_end) && column_row<REINDEX>(p, r, c_out, nv, base, prow);
-        st.sc = p.scale;
+        st.sc = row_scale;
         if (KT == CSA2_FP8_E4M3 && st.valid) st.sc *= p.k_scale[prow];
     };
     auto finish = [&](int64_t cb, const Step& st) {
@@ -265,6 +308,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(const IndexParams p)
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < S; ++s) acc = Ops::mma(acc, qa[t][s], st.kb[u][s]);
+                if (t == 0) acc_sum = nan_guard(acc[0]);
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) acc_sum += wr[t][rr] * relu_bits(acc[rr]);
             }
@@ -351,6 +395,12 @@ __global__ __launch_bounds__(64 * ROWS) void indexer_chunk_kernel(const IndexPar
         for (int rr = 0; rr < 4; ++rr) wr[t][rr] = p.w[(int64_t)rq * 64 + 16 * t + 4 * g + rr];
     }
     wait_vmem_all();  // q and w are in registers before the staging loop starts loading
+    bool qn = false;
+#pragma unroll
+    for (int t = 0; t < HT; ++t)
+#pragma unroll
+        for (int s = 0; s < S; ++s) qn |= frag_has_nan(qa[t][s]);
+    const float row_scale = __ballot(qn) != 0ull ? __builtin_nanf("") : p.scale;  // NaN query: NaN scores
 
     // Staging: chunk i = thread + NT j of the stage is 16-byte chunk i % 16 of key row i / 16
     // (consecutive threads read consecutive bytes; zeros past the visible columns).
@@ -411,6 +461,7 @@ __global__ __launch_bounds__(64 * ROWS) void indexer_chunk_kernel(const IndexPar
                         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int s = 0; s < S; ++s) acc = Ops::mma(acc, qa[t][s], kb[s]);
+                        if (t == 0) acc_sum = nan_guard(acc[0]);
 #pragma unroll
                         for (int rr = 0; rr < 4; ++rr) acc_sum += wr[t][rr] * relu_bits(acc[rr]);
                     }
@@ -419,7 +470,7 @@ __global__ __launch_bounds__(64 * ROWS) void indexer_chunk_kernel(const IndexPar
                 if (st + 1 < KEYS / 64) {
                     const int64_t cb = cs + 64 * st;
                     const int64_t c_out = cb + lane;
-                    store_step<false, false>(p, rq, nv, cb, c1, lane, v, p.scale, c_out < c1 && c_out < nv, srow,
+                    store_step<false, false>(p, rq, nv, cb, c1, lane, v, row_scale, c_out < c1 && c_out < nv, srow,
                                              nullptr);
                 } else {
 #pragma unroll
@@ -433,7 +484,7 @@ __global__ __launch_bounds__(64 * ROWS) void indexer_chunk_kernel(const IndexPar
         if (live) {
             const int64_t cb = cs + KEYS - 64;
             const int64_t c_out = cb + lane;
-            store_step<false, false>(p, rq, nv, cb, c1, lane, vlast, p.scale, c_out < c1 && c_out < nv, srow, nullptr);
+            store_step<false, false>(p, rq, nv, cb, c1, lane, vlast, row_scale, c_out < c1 && c_out < nv, srow, nullptr);
         }
         __syncthreads();
         b ^= 1;
@@ -489,6 +540,16 @@ struct Fp8Keys {
     static __device__ __forceinline__ const void* scale_base(const IndexParams& p, int64_t row) {
         return p.k_scale + row;
     }
+    // Factor of the output column's score: the key row's float32 scale (a NaN scale makes the
+    // score NaN, as the decoded row is NaN).
+    static __device__ __forceinline__ float score_scale(float scale, uint32_t sw, bool q_nan) {
+        return q_nan ? __builtin_nanf("") : scale * __uint_as_float(sw);
+    }
+    // Whether the query row holds an E4M3 NaN code (the lanes together hold all of it).
+    static __device__ __forceinline__ bool query_nan(const i32x8 (&qa)[4], const uint32_t (&)[4]) {
+        return __ballot(frag_has_nan(qa[0]) || frag_has_nan(qa[1]) || frag_has_nan(qa[2]) ||
+                        frag_has_nan(qa[3])) != 0ull;
+    }
 };
 
 // MXFP4 keys and query (E2M1 with one E8M0 scale per 32 elements): 64-byte
@@ -520,6 +581,18 @@ struct Fp4Keys {
     static __device__ __forceinline__ const void* scale_base(const IndexParams& p, int64_t row) {
         return p.k_e8 + 4 * row;
     }
+    // E8M0 byte 255 encodes NaN: a key with a NaN block scale has a NaN dot with every head, and
+    // a query with one has a NaN dot in that head for every key, so the score is NaN either
+    // way.  Set here explicitly rather than left to how the matrix core treats a NaN scale.
+    static __device__ __forceinline__ float score_scale(float scale, uint32_t sw, bool q_nan) {
+        const uint32_t ff = ~sw;  // a byte of sw is 0xff iff that byte of ff is zero
+        const bool k_nan = ((ff - 0x01010101u) & ~ff & 0x80808080u) != 0u;
+        return (k_nan || q_nan) ? __builtin_nanf("") : scale;
+    }
+    // Whether any E8M0 scale of the query row is 255 (the lanes together hold all of them).
+    static __device__ __forceinline__ bool query_nan(const i32x8 (&)[4], const uint32_t (&qs)[4]) {
+        return __ballot(qs[0] == 255u || qs[1] == 255u || qs[2] == 255u || qs[3] == 255u) != 0ull;
+    }
 };
 
 template <class KF>
@@ -548,6 +621,7 @@ __device__ __forceinline__ void step_sums(const uint8_t* my, const uint32_t* scl
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const f32x4 acc = KF::mma(qa[t], qs[t], kb, ksc);
+            if (t == 0) acc_sum = nan_guard(acc[0]);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) acc_sum = fmaf(wr[t][rr], relu_bits(acc[rr]), acc_sum);
         }
@@ -607,6 +681,7 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(const IndexParams p
     uint32_t qs[4];
     float wr[4][4];
     load_query<KF>(p, r, g, li, qa, qs, wr);
+    const bool q_nan = KF::query_nan(qa, qs);
     if (HIST) {
         for (int b = threadIdx.x; b < kKeyBins; b += 256) hist[b] = 0u;
         __syncthreads();
@@ -634,7 +709,7 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(const IndexParams p
     };
     auto step = [&](int64_t cb, Buf& b) {
         stage_put<KF>(my, scl, b.v, b.sw, lane);
-        const float sc = KF::kScaleInScore ? p.scale * __uint_as_float(b.sw) : p.scale;
+        const float sc = KF::score_scale(p.scale, b.sw, q_nan);
         const bool valid = cb + lane < c_live;
         // Unconditional: past the visible rows the descriptor turns the loads into zeros.
         issue(cb + 256 * DEPTH, b);
@@ -722,6 +797,7 @@ __global__ __launch_bounds__(256) void indexer_rescore_kernel(const IndexParams 
     uint32_t qs[4];
     float wr[4][4];
     load_query<KF>(p, r, g, li, qa, qs, wr);
+    const bool q_nan = KF::query_nan(qa, qs);
     // the row's visible key rows and their scales; loads beyond them return zeros
     const int n_rows = (int)(n_valid > 0 ? n_valid : 0);
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
@@ -753,7 +829,7 @@ __global__ __launch_bounds__(256) void indexer_rescore_kernel(const IndexParams 
         step_sums<KF>(my, scl, qa, qs, wr, g, li, v);
         const float kk = reduce_scatter(v, lane);
         const bool valid = col < n_valid;
-        const float sc = KF::kScaleInScore ? p.scale * __uint_as_float(sw) : p.scale;
+        const float sc = KF::score_scale(p.scale, sw, q_nan);
         const uint32_t key = order_key(sc * kk);
         const bool take = valid && (key >> 20) >= b1;
         const uint64_t m = __ballot(take);

@@ -223,15 +223,33 @@ def oracle_attention(cfg, x, idx_np, rows, layer=0):
     return out
 
 
+def close_mask(g, ref, atol, rtol):
+    """Elements that agree: both NaN, the same infinity, or finite with |g - o| <= atol + rtol |o|.
+    Anything else fails, including a NaN or an infinity on one side only."""
+    g = np.asarray(g, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    both_nan = np.isnan(g) & np.isnan(ref)
+    same_inf = np.isinf(g) & np.isinf(ref) & (g == ref)
+    fin = np.isfinite(g) & np.isfinite(ref)
+    with np.errstate(invalid="ignore"):
+        ok_fin = np.abs(g - ref) <= atol + rtol * np.abs(ref)
+    return both_nan | same_inf | (fin & ok_fin)
+
+
 def assert_close(gpu, ref, atol, rtol, what):
-    g = gpu.detach().float().cpu().numpy().astype(np.float64) if torch.is_tensor(gpu) else gpu
-    err = np.abs(g - ref)
-    lim = atol + rtol * np.abs(ref)
-    bad = err > lim
+    g = gpu.detach().float().cpu().numpy().astype(np.float64) if torch.is_tensor(gpu) else np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert g.shape == ref.shape, f"{what}: shape {g.shape} != {ref.shape}"
+    ok = close_mask(g, ref, atol, rtol)
+    fin = np.isfinite(g) & np.isfinite(ref)
+    err = np.where(fin, np.abs(g - ref), 0.0)
     max_abs = float(err.max()) if err.size else 0.0
-    rel = err / np.maximum(np.abs(ref), 1e-30)
-    info = f"{what}: max_abs={max_abs:.3e} max_rel(|o|>1e-3)={float(rel[np.abs(ref) > 1e-3].max()) if (np.abs(ref) > 1e-3).any() else 0:.3e}"
-    assert not bad.any(), info + f" ; {int(bad.sum())} elements outside {atol}+{rtol}|o|"
+    big = fin & (np.abs(ref) > 1e-3)
+    max_rel = float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0
+    info = f"{what}: max_abs={max_abs:.3e} max_rel(|o|>1e-3)={max_rel:.3e}"
+    n_bad = int((~ok).sum())
+    n_nf = int((~fin & ~ok).sum())
+    assert n_bad == 0, info + f" ; {n_bad} elements outside {atol}+{rtol}|o| ({n_nf} of them non-finite on one side)"
     return max_abs
 
 

@@ -18,8 +18,16 @@ from harness import (BF16_ATOL, BF16_RTOL, F32_ATOL, F32_RTOL, SCORE_TOL, assert
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ["tiny_full_fp32", "full_decode_64k", "prefill_4096_at_128k", "reindex_decode_1m", "lowp_full_decode_1m",
-         "lowp_pool_decode_1m", "pages_fp4_decode_1m", "lowp_owner_decode_1m", "prefill_owner_4096_at_128k"]
+# (workload, seed, ragged positions).  The two 1M decodes the measurements name run seeds 0, 1 and 2
+# plus a ragged-position batch; the 64K decode runs a ragged batch as well.
+CASES = [("tiny_full_fp32", 2, False), ("full_decode_64k", 2, False), ("full_decode_64k", 1, True),
+         ("prefill_4096_at_128k", 2, False),
+         ("reindex_decode_1m", 0, False), ("reindex_decode_1m", 1, False), ("reindex_decode_1m", 2, False),
+         ("reindex_decode_1m", 3, True),
+         ("lowp_full_decode_1m", 0, False), ("lowp_full_decode_1m", 1, False), ("lowp_full_decode_1m", 2, False),
+         ("lowp_full_decode_1m", 3, True),
+         ("lowp_pool_decode_1m", 2, False), ("pages_fp4_decode_1m", 2, False), ("lowp_owner_decode_1m", 2, False),
+         ("prefill_owner_4096_at_128k", 2, False)]
 
 
 def _run_path(cfg, x):
@@ -43,22 +51,28 @@ def _run_path(cfg, x):
     return scores, step.idx, step.outs
 
 
-def _sample_rows(cfg):
+def _sample_rows(cfg, seed):
+    """Rows the oracle checks one by one: every row of the tiny workload and of the 32-sequence decodes;
+    8 rows (first, last and 6 seeded others) of the 64-sequence decodes; 8 rows of a prefill chunk."""
     n = cfg.q_tokens
-    if n <= 256:
-        picks = [0, n // 2, n - 1] if n > 64 else [0, n - 1]
-        if cfg.name == "tiny_full_fp32":
-            return np.arange(n)
-        return np.array(sorted(set(picks)))
-    return np.array([0, 1, 1777, n - 2, n - 1])
+    if n <= 32 or cfg.name == "tiny_full_fp32":
+        return np.arange(n)
+    rng = np.random.default_rng(1000 + seed)
+    inner = rng.choice(np.arange(2, n - 2), size=4 if n > 256 else 6, replace=False)
+    picks = {0, n - 1} | set(int(v) for v in inner)
+    if n > 256:
+        picks |= {1, 1777, n - 2}
+    return np.array(sorted(picks))
 
 
-@pytest.fixture(scope="module", params=NAMES)
+@pytest.fixture(scope="module", params=CASES, ids=[f"{n}-s{s}{'-ragged' if r else ''}" for n, s, r in CASES])
 def full(request):
-    cfg = CONFIGS[request.param]
-    print(f"\n[full] {cfg.name} seed=2 rows={cfg.q_tokens} width={cfg.width} layers={1 + cfg.reuse_layers}",
-          flush=True)
-    x = make_inputs(cfg, 2, device="cuda")
+    name, seed, ragged = request.param
+    cfg = CONFIGS[name].replace(ragged=ragged)
+    print(f"\n[full] {cfg.name} seed={seed} ragged={ragged} rows={cfg.q_tokens} width={cfg.width} "
+          f"layers={1 + cfg.reuse_layers}", flush=True)
+    x = make_inputs(cfg, seed, device="cuda")
+    x["_seed"] = seed
     torch.cuda.synchronize()
     scores, idx, outs = _run_path(cfg, x)
     yield cfg, x, scores, idx, outs
@@ -90,7 +104,7 @@ def test_every_output_finite(full):
 
 def test_sampled_rows_scores_topk_attention(full):
     cfg, x, scores, idx, outs = full
-    rows = _sample_rows(cfg)
+    rows = _sample_rows(cfg, x["_seed"])
     s_ref = oracle_scores(cfg, x, rows)
     bound = oracle_score_bound(cfg, x, rows)
     got = scores[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
@@ -129,7 +143,7 @@ def test_candidate_pool(full):
         assert (nv - 1) // B in set(v.tolist())
         kept = set(v.tolist())
         assert all(int(c) // B in kept for c in ii[r] if c >= 0)
-    rows = _sample_rows(cfg)
+    rows = _sample_rows(cfg, x["_seed"])
     s_gpu = scores[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
     ref = oracle.candidates.candidate_pool(s_gpu, pos[rows], cfg.ratio, B, cfg.pool_blocks)
     assert np.array_equal(pool[rows], ref)
@@ -153,7 +167,7 @@ def test_owner_rows_written(full):
         pytest.skip("this workload appends no rows")
     from harness import to_numpy_f64
     c = x["compress"]
-    rows = _sample_rows(cfg)
+    rows = _sample_rows(cfg, x["_seed"])
     if cfg.ratio == 2:
         rows = np.array(sorted({int(r) | 1 for r in rows if (int(r) | 1) < cfg.q_tokens}))  # rows that emit
     f64 = lambda t: None if t is None else t.detach().cpu().double().numpy()

@@ -146,3 +146,29 @@ def test_constant_stored_row_comes_back_unrotated():
     s = 0.5 * q @ stored
     psink = np.exp(sink) / (np.exp(sink) + 3 * np.exp(s))
     assert np.allclose(out, (1 - psink)[:, None] * c[None], atol=1e-13)
+
+
+def test_nan_entry_row_gives_nan_output():
+    """An entry row holding a NaN scores NaN against every head; one softmax over all entries then
+    makes every output element NaN.  A NaN in a ring slot outside the window changes nothing."""
+    rng = np.random.default_rng(21)
+    H, D, W = 2, 8, 4
+    q = rng.standard_normal((H, D))
+    sink = rng.standard_normal(H)
+    ring = rng.standard_normal((W, D))
+    plane = rng.standard_normal((6, D))
+    freqs = rope.inv_freq(4, 10000.0)
+    idx = np.array([0, 2, -1])
+    pos = 5   # ring slots hold positions 4, 5, 2, 3: all valid
+    base = attention.attend(q, pos, attention.entries_decode(pos, idx, plane, ring, 1), sink, 0.3, freqs)
+    assert np.all(np.isfinite(base))
+    bad = plane.copy()
+    bad[2, 5] = np.nan
+    out = attention.attend(q, pos, attention.entries_decode(pos, idx, bad, ring, 1), sink, 0.3, freqs)
+    assert np.all(np.isnan(out))
+    # position 1: slots 2 and 3 were never written (positions -2, -1); a NaN there is not an entry
+    ring2 = ring.copy()
+    ring2[3, 0] = np.nan
+    a = attention.attend(q, 1, attention.entries_decode(1, idx, plane, ring, 1), sink, 0.3, freqs)
+    b = attention.attend(q, 1, attention.entries_decode(1, idx, plane, ring2, 1), sink, 0.3, freqs)
+    assert np.array_equal(a, b) and np.all(np.isfinite(b))

@@ -85,3 +85,31 @@ def test_abs_bound_dominates_score():
     s = indexer.score_rows(q, w, k, 0.1)
     a = indexer.score_abs_bound(q, w, k, 0.1)
     assert np.all(np.abs(s) <= a + 1e-15)
+
+
+@pytest.mark.parametrize("nan_sign", [1.0, -1.0])
+def test_nan_key_gives_nan_score(nan_sign):
+    """A NaN dot stays NaN through the per-head ReLU (of either sign bit), so the score is NaN; the
+    loop form (ReLU as 'd < 0 -> 0', false for NaN) agrees.  Other columns are unaffected."""
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, 3, 4))
+    w = rng.standard_normal((1, 3))
+    plane = rng.standard_normal((5, 4))
+    plane[2, 1] = np.copysign(np.nan, nan_sign)
+    s = indexer.scores_full(q, w, lambda r: plane, np.array([4]), 1, 0.5, 5)
+    assert np.isnan(s[0, 2])
+    assert math.isnan(_loop_score(q[0], w[0], plane[2], 0.5))
+    for c in (0, 1, 3, 4):
+        assert math.isclose(s[0, c], _loop_score(q[0], w[0], plane[c], 0.5), rel_tol=1e-12, abs_tol=1e-12)
+
+
+def test_nan_query_head_gives_nan_row():
+    """A NaN in one head of the query makes that head's dot NaN for every key: every valid score is
+    NaN, invalid columns stay -inf."""
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((1, 3, 4))
+    q[0, 1, 3] = np.nan
+    w = rng.standard_normal((1, 3))
+    plane = rng.standard_normal((6, 4))
+    s = indexer.scores_full(q, w, lambda r: plane, np.array([3]), 1, 0.5, 6)
+    assert np.all(np.isnan(s[0, :4])) and np.all(s[0, 4:] == -np.inf)
