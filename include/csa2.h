@@ -18,7 +18,9 @@
  *   - All tensor pointers are DEVICE memory owned by the caller.  The library
  *     keeps no state between calls, never frees caller memory, and allocates
  *     nothing: scratch space comes in through an explicit workspace argument
- *     whose size the matching *_workspace_size() call reports.
+ *     whose size the matching *_workspace_size() call reports.  (The one
+ *     exception, csa2_topk_select_noalloc, uses a fixed array in the library's
+ *     own device memory instead.)
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream); the
  *     call returns after the launches, without synchronising.  Calls are
  *     re-entrant; two calls on different streams must not share a workspace.
@@ -249,6 +251,29 @@ size_t csa2_topk_workspace_size(int32_t rows, int64_t width, int32_t k);
 
 int32_t csa2_topk_select(const csa2_topk_args* args, void* workspace, size_t workspace_bytes,
                          csa2_stream_t stream);
+
+/* The same top-k for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the workspace is a
+ * fixed array of CSA2_TOPK_NOALLOC_SCRATCH_BYTES in the library's own device memory, one per
+ * GPU, held until the process ends.  Results are identical to csa2_topk_select's.
+ *
+ *   - No hipMalloc / hipFree or allocating library call is made.  The first call on a
+ *     device looks up that device's array (hipGetSymbolAddress, with the device current);
+ *     the call uses the current device, which must be the stream's.
+ *   - Sizes whose csa2_topk_workspace_size exceeds CSA2_TOPK_NOALLOC_SCRATCH_BYTES return
+ *     CSA2_ERR_WORKSPACE before anything is launched (40 MiB covers, e.g., 256 rows of
+ *     2^20 columns; rows >= 1024 and widths < 8192 need no workspace at all).
+ *   - Every call on one GPU shares that GPU's array and leaves its contents behind; the
+ *     call's own kernels initialise everything they read, so nothing needs clearing.
+ *     Calls that overlap on one GPU (concurrent streams, several host threads) race on
+ *     the array: serialise them.
+ * Other arguments, validation and status codes as for csa2_topk_select.
+ */
+#define CSA2_TOPK_NOALLOC_SCRATCH_BYTES (40u << 20)
+
+size_t csa2_topk_noalloc_scratch_bytes(void);
+
+int32_t csa2_topk_select_noalloc(const csa2_topk_args* args, csa2_stream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Hierarchical candidate pool of the FULL owner layer.

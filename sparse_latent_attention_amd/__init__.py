@@ -118,6 +118,10 @@ _lib.csa2_compress_workspace_size.restype = ctypes.c_size_t
 _lib.csa2_compress_workspace_size.argtypes = [_i32, _i32, _i32]
 _lib.csa2_compress.restype = _i32
 _lib.csa2_compress.argtypes = [ctypes.POINTER(CompressArgs), _vp, ctypes.c_size_t, _vp]
+_lib.csa2_topk_noalloc_scratch_bytes.restype = ctypes.c_size_t
+_lib.csa2_topk_noalloc_scratch_bytes.argtypes = []
+_lib.csa2_topk_select_noalloc.restype = _i32
+_lib.csa2_topk_select_noalloc.argtypes = [ctypes.POINTER(TopkArgs), _vp]
 _lib.csa2_rope_inv_freq.restype = _i32
 _lib.csa2_rope_inv_freq.argtypes = [_i32, ctypes.c_double, ctypes.c_double, _i64, ctypes.POINTER(ctypes.c_double)]
 
@@ -125,7 +129,8 @@ ABI_VERSION = _lib.csa2_abi_version()
 EXPORTED = ("csa2_abi_version", "csa2_status_string", "csa2_indexer_score", "csa2_topk_workspace_size",
             "csa2_topk_select", "csa2_topk_rescore_workspace_size", "csa2_topk_rescore",
             "csa2_candidate_pool_workspace_size", "csa2_candidate_pool", "csa2_attn_workspace_size", "csa2_sparse_attn_decode", "csa2_sparse_attn_prefill",
-            "csa2_compress_workspace_size", "csa2_compress", "csa2_rope_inv_freq")
+            "csa2_compress_workspace_size", "csa2_compress", "csa2_rope_inv_freq", "csa2_topk_noalloc_scratch_bytes",
+            "csa2_topk_select_noalloc")
 
 
 class Csa2Error(RuntimeError):
@@ -338,7 +343,19 @@ def topk_select(scores, pos, ratio, out, *, cand=None, block_rows=8, key_hist=No
 
     ``key_hist`` is the histogram indexer_score wrote for these scores, if any.
     """
-    _dev(scores, pos, out, cand, workspace, key_hist)
+    _dev(workspace)
+    a = _topk_args(scores, pos, ratio, out, cand, block_rows, key_hist)
+    rows, width = a.rows, a.width
+    need = topk_workspace_size(rows, width, a.k)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = _scratch(need, scores.device, stream)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("csa2_topk_select", _lib.csa2_topk_select(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def _topk_args(scores, pos, ratio, out, cand, block_rows, key_hist):
+    _dev(scores, pos, out, cand, key_hist)
     _need(scores, torch.float32, "scores")
     _need(pos, torch.int64, "pos")
     _need(out, torch.int32, "out")
@@ -353,11 +370,17 @@ def topk_select(scores, pos, ratio, out, *, cand=None, block_rows=8, key_hist=No
         a.n_blocks, a.block_rows = cand.shape[1], int(block_rows)
     a.scores, a.pos, a.cand, a.out = _ptr(scores), _ptr(pos), _ptr(cand), _ptr(out)
     a.key_hist = _ptr(key_hist)
-    need = topk_workspace_size(rows, width, a.k)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = _scratch(need, scores.device, stream)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("csa2_topk_select", _lib.csa2_topk_select(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream)))
+    return a
+
+
+NOALLOC_SCRATCH_BYTES = int(_lib.csa2_topk_noalloc_scratch_bytes())
+
+
+def topk_select_noalloc(scores, pos, ratio, out, *, cand=None, block_rows=8, key_hist=None, stream=None):
+    """topk_select without any allocation: the library's fixed per-GPU scratch array is the workspace
+    (for callers that cannot allocate).  Calls that overlap on one GPU race on that array."""
+    a = _topk_args(scores, pos, ratio, out, cand, block_rows, key_hist)
+    _check("csa2_topk_select_noalloc", _lib.csa2_topk_select_noalloc(ctypes.byref(a), _stream(stream)))
     return out
 
 

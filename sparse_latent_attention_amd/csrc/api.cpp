@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/csa2.h"
@@ -269,7 +271,8 @@ size_t csa2_topk_workspace_size(int32_t rows, int64_t width, int32_t k) {
     return csa2::topk_workspace_bytes(rows, width);
 }
 
-int32_t csa2_topk_select(const csa2_topk_args* a, void* workspace, size_t workspace_bytes, csa2_stream_t stream) {
+// Host-side checks of csa2_topk_select's arguments that do not involve the workspace.
+static int32_t validate_topk(const csa2_topk_args* a) {
     if (a == nullptr || a->struct_size < sizeof(csa2_topk_args)) return CSA2_ERR_INVALID_ARG;
     if (a->rows < 0 || a->k < 1 || a->k > 2048 || a->width < 0 || a->width >= (1LL << 31)) return CSA2_ERR_INVALID_ARG;
     if (a->ratio != 1 && a->ratio != 2) return CSA2_ERR_INVALID_ARG;
@@ -278,6 +281,12 @@ int32_t csa2_topk_select(const csa2_topk_args* a, void* workspace, size_t worksp
         if (a->cand == nullptr || a->block_rows <= 0 || a->block_rows > 64) return CSA2_ERR_INVALID_ARG;
         if (a->width != (int64_t)a->n_blocks * a->block_rows) return CSA2_ERR_INVALID_ARG;
     }
+    return CSA2_OK;
+}
+
+int32_t csa2_topk_select(const csa2_topk_args* a, void* workspace, size_t workspace_bytes, csa2_stream_t stream) {
+    const int32_t st = validate_topk(a);
+    if (st != CSA2_OK) return st;
     const size_t need = csa2_topk_workspace_size(a->rows, a->width, a->k);
     if (workspace_bytes < need) return CSA2_ERR_WORKSPACE;
     if (need > 0 && (workspace == nullptr || !aligned(workspace, 256))) return CSA2_ERR_INVALID_ARG;
@@ -389,6 +398,48 @@ int32_t csa2_sparse_attn_prefill(const csa2_attn_args* a, csa2_stream_t stream) 
     csa2::AttnParams p = attn_params(a);
     csa2::AttnShape s{a->heads, a->dim, a->rope_dim, a->q_dtype, a->kv_dtype, a->swa_dtype, a->out_dtype};
     return hip_status(csa2::launch_sparse_attn(p, s, false, reinterpret_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// csa2_topk_select_noalloc: csa2_topk_select with its workspace in a fixed device array.
+//
+// The array lives in this library's code object on every GPU it runs on, for the life of the
+// process.  Host code never uses its name as an address (it is a host-side stand-in there):
+// the device address comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that pointer is passed to kernels.
+static __device__ __align__(256) uint8_t csa2_topk_scratch[CSA2_TOPK_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of this device's scratch array, or nullptr on a HIP error.
+static void* topk_scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(csa2_topk_scratch)) != hipSuccess || p == nullptr) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+size_t csa2_topk_noalloc_scratch_bytes(void) { return CSA2_TOPK_NOALLOC_SCRATCH_BYTES; }
+
+int32_t csa2_topk_select_noalloc(const csa2_topk_args* a, csa2_stream_t stream) {
+    const int32_t st = validate_topk(a);
+    if (st != CSA2_OK) return st;
+    const size_t need = csa2_topk_workspace_size(a->rows, a->width, a->k);
+    if (need > (size_t)CSA2_TOPK_NOALLOC_SCRATCH_BYTES) return CSA2_ERR_WORKSPACE;
+    if (a->rows == 0) return CSA2_OK;
+    void* ws = nullptr;
+    if (need > 0) {
+        ws = topk_scratch_for_current_device();
+        if (ws == nullptr) return CSA2_ERR_HIP;
+    }
+    return csa2_topk_select(a, ws, need, stream);
 }
 
 }  // extern "C"

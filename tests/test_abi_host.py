@@ -277,6 +277,35 @@ def test_topk_validation(field, value, status):
     assert csa2._lib.csa2_topk_select(ctypes.byref(t), None, 0, None) == status
 
 
+@pytest.mark.parametrize("field,value,status", [
+    ("k", 0, csa2.ERR_INVALID_ARG), ("k", 4096, csa2.ERR_INVALID_ARG), ("ratio", 0, csa2.ERR_INVALID_ARG),
+    ("width", 1 << 31, csa2.ERR_INVALID_ARG), ("n_blocks", 3, csa2.ERR_INVALID_ARG),
+])
+def test_topk_noalloc_validation(field, value, status):
+    t = csa2.TopkArgs()
+    t.struct_size, t.rows, t.k, t.ratio, t.width = ctypes.sizeof(csa2.TopkArgs), 2, 512, 1, 1000
+    t.scores = t.pos = t.out = ctypes.c_void_p(0x1000)
+    setattr(t, field, value)
+    assert csa2._lib.csa2_topk_select_noalloc(ctypes.byref(t), None) == status
+
+
+def test_topk_noalloc_rejects_sizes_beyond_its_scratch():
+    """Shapes whose workspace is larger than the fixed scratch are refused before any HIP call; the
+    decode shapes fit; empty calls do nothing."""
+    cap = csa2.NOALLOC_SCRATCH_BYTES
+    assert cap == 40 << 20
+    t = csa2.TopkArgs()
+    t.struct_size, t.k, t.ratio = ctypes.sizeof(csa2.TopkArgs), 512, 1
+    t.scores = t.pos = t.out = ctypes.c_void_p(0x1000)
+    t.rows, t.width = 1023, 65536
+    assert csa2.topk_workspace_size(1023, 65536, 512) > cap
+    assert csa2._lib.csa2_topk_select_noalloc(ctypes.byref(t), None) == csa2.ERR_WORKSPACE
+    for rows, width in ((32, 32768), (64, 1 << 20), (256, 1 << 20)):
+        assert 0 < csa2.topk_workspace_size(rows, width, 512) <= cap
+    t.rows = 0
+    assert csa2._lib.csa2_topk_select_noalloc(ctypes.byref(t), None) == csa2.OK
+
+
 def _attn_args(**kw):
     a = csa2.AttnArgs()
     a.struct_size = ctypes.sizeof(csa2.AttnArgs)
