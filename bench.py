@@ -27,6 +27,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sparse-attn query-tokens/s + achieved HBM GB/s, decode at 1M context, 1 MI355X"
+# Workloads whose bytes (157-289 MiB) are about the size of the 256 MB last-level cache (MALL): reading a
+# 512 MiB buffer between timed steps evicts their planes, so each step reads them from HBM.  (A read, not a
+# write: a write leaves ~256 MB of dirty lines whose write-back would land inside the next step's kernels.)
+FLUSH_DEFAULT = {"full_decode_64k", "reindex_decode_1m", "reindex_fp8_decode_1m", "reindex_pages_decode_1m"}
+FLUSH_BYTES = 512 << 20
 HBM_PEAK_GBS = 8000.0
 DEFAULT_CONFIG = "lowp_full_decode_1m"
 
@@ -270,6 +275,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--flush", choices=["auto", "on", "off"], default="auto",
+                    help="read 512 MiB between timed steps (outside the timed events) so the planes come from HBM; "
+                         "auto: on for the workloads about the size of the MALL (64K decode, 1M REINDEX decodes)")
     ap.add_argument("--calibrate", action="store_true",
                     help="after the bench, run a plain 1 GiB float32 copy kernel 3 times (the reference for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE scaling: 1 GiB read + 1 GiB written per launch)")
@@ -315,13 +323,30 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    flush = args.flush == "on" or (args.flush == "auto" and cfg.name in FLUSH_DEFAULT)
+    flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if flush else None
+    step_evs = []
+    print(f"[bench] timing {args.steps} steps{' (L2/MALL flushed between steps)' if flush else ''}",
+          file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
+        if flush:
+            flush_buf.sum()  # evicts the planes (a 512 MiB read); outside the step's events
+            a = torch.cuda.Event(enable_timing=True)
+            a.record()
         step(True)
+        if flush:
+            b = torch.cuda.Event(enable_timing=True)
+            b.record()
+            step_evs.append((a, b))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
+    if flush:
+        # with a flush between steps the wall clock includes it: the step time is the events' span
+        ms_step = sum(a.elapsed_time(b) for a, b in step_evs) / args.steps
+    else:
+        ms_step = wall * 1e3 / args.steps
     kern_ms = {n: sum(a.elapsed_time(b) for a, b in evs[n]) / args.steps for n in names}
 
     work = algorithmic_work(cfg, x, step_calls.idx.cpu() if cfg.phase == "prefill" else None, step_calls.score_free)
@@ -345,6 +370,9 @@ def main():
                    "main_kv": cfg.main_dtype, "swa": cfg.swa_dtype, "attention_layers": len(x["layers"]),
                    "topk_route": "score-free (topk_rescore)" if step_calls.score_free else "scores + topk_select",
                    "write_path": f"d_in {cfg.d_model}, ratio {cfg.ratio}" if cfg.d_model else None},
+        "timing": ("HIP events around each step; 512 MiB read between steps (L2/MALL flush, not timed); "
+                   f"wall clock incl. flush {wall * 1e3 / args.steps:.4f} ms/step") if flush else
+                  "wall clock over the timed steps (synchronized before and after)",
         "kernels_ms": {n: round(v, 4) for n, v in kern_ms.items()},
         "kernels_roofline": {n: roofline_of(work[n], kern_ms[n]) for n in names},
         "roofline": roofline,

@@ -118,8 +118,13 @@ const char* csa2_status_string(int32_t status);
  * inference, the indexer query are FP4 with one E8M0 scale per 32 channels;
  * "万字长文解析DeekSeekV4.1flash" §10.6: 64 + 4 bytes per key row).  Each
  * dot product is the sum over 32-element blocks of (q block . k block) times
- * both blocks' scales; k_scale is NULL.  FULL mode with (heads, dim) =
- * (64, 128) only.
+ * both blocks' scales; k_scale is NULL.  (heads, dim) = (64, 128), FULL, or
+ * REINDEX with block_rows 8.
+ *
+ * REINDEX with block_rows 8 (the pages' 2048 x 8 pool) and (heads, dim) =
+ * (64, 128) gathers whole candidate blocks for BF16, FP8 and MXFP4 planes and
+ * computes every column with the FULL pass's arithmetic, so its scores are
+ * bit-identical to the FULL scores of the same plane rows.
  *
  * Supported: (heads, dim) in {(4, 32), (64, 128)}; q_dtype == k_dtype in
  * {F32, BF16, FP8_E4M3}, or FP4_E2M1 as above.  rows * width fits in int64.

@@ -84,7 +84,7 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
     if (!csa2::indexer_supported(a->heads, a->dim, a->k_dtype)) return CSA2_ERR_UNSUPPORTED;
     const bool reindex = a->mode == CSA2_MODE_REINDEX;
     if ((a->flags & ~CSA2_INDEX_SHARED_PLANE) != 0 || (reindex && a->flags != 0)) return CSA2_ERR_INVALID_ARG;
-    if (a->k_dtype == CSA2_FP4_E2M1 && reindex) return CSA2_ERR_UNSUPPORTED;
+    if (a->k_dtype == CSA2_FP4_E2M1 && reindex && a->block_rows != 8) return CSA2_ERR_UNSUPPORTED;
     if (reindex) {
         if (a->cand == nullptr || a->n_blocks <= 0 || a->block_rows <= 0 || a->block_rows > 64) return CSA2_ERR_INVALID_ARG;
         if (a->width != (int64_t)a->n_blocks * a->block_rows) return CSA2_ERR_INVALID_ARG;

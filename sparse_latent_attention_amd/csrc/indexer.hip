@@ -17,6 +17,8 @@
 // holds 4 heads x 1 column per lane, so the head reduction is 16 in-lane
 // multiply-adds plus a 3-shuffle reduce-scatter across the 4 lane groups that
 // leaves lane l with column l of the 64 -- one coalesced 256-byte store.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -520,6 +522,7 @@ constexpr int kNT = 2;                  // non-temporal cache policy of a buffer
 struct Fp8Keys {
     static constexpr int kRowBytes = 128, kChunks = 8, kLoads = 8;
     static constexpr bool kScaleInScore = true;
+    static constexpr bool kDense = false;
     static __device__ __forceinline__ int swz(int kk) { return (kk >> 1) & 7; }
     static __device__ __forceinline__ void frag(const uint8_t* my, const uint32_t*, int kk, int g, i32x8& kb,
                                                 uint32_t& ksc) {
@@ -560,6 +563,7 @@ struct Fp8Keys {
 struct Fp4Keys {
     static constexpr int kRowBytes = 64, kChunks = 4, kLoads = 4;
     static constexpr bool kScaleInScore = false;
+    static constexpr bool kDense = false;
     static __device__ __forceinline__ int swz(int kk) { return (kk >> 2) & 3; }
     static __device__ __forceinline__ void frag(const uint8_t* my, const uint32_t* scl, int kk, int g, i32x8& kb,
                                                 uint32_t& ksc) {
@@ -880,6 +884,220 @@ hipError_t launch_indexer_rescore(const IndexParams& p, int rows, int dtype, con
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// REINDEX scoring over 8-row candidate blocks (64 heads x 128; BF16, FP8 or
+// MXFP4 index planes).
+//
+// Column c = 8 i + t of a row is plane row cand[r, i] * 8 + t
+// ("DeepSeek-V4.1-Flash 架构解剖", fig. 2c REINDEX: only the 2048 x 8 candidate
+// rows are scored).  A 64-column step is 8 consecutive candidate blocks, i.e.
+// 8 runs of 8 consecutive key rows (2 KiB each in BF16), so the gather reads
+// whole blocks: one load instruction covers whole key rows of one block (BF16:
+// 4 rows, FP8: 8 rows) or of two (MXFP4: 16 rows of 64 B).  Each wave loads
+// the candidate ids of all its steps up front (lane 8 i' + k holds slot k of
+// its step i') and moves each step's 8 ids to scalar registers, so no load
+// address waits on an id load inside the step loop.  The rows go through the
+// wave's LDS slot into the MFMA operand layout as in the FULL streaming
+// kernel, DEPTH steps of loads in flight.  Rows that are not valid (slot -1,
+// or past the visible prefix) load a valid row of the same plane instead --
+// the plane's first row, or the block's first -- and their columns get -inf.
+
+// BF16 key rows: 256 bytes, sixteen 16-byte chunks, chunk c of key kk at
+// position c ^ (kk & 15) (conflict-free for both the staging writes and the
+// B-operand reads); no per-row scale.
+struct Bf16Keys {
+    static constexpr int kRowBytes = 256, kChunks = 16, kLoads = 16;
+    static constexpr bool kScaleInScore = true;  // no scale word is staged
+    static constexpr bool kDense = true;
+    static __device__ __forceinline__ int swz(int kk) { return kk & 15; }
+};
+
+// v[u] (lane (g, n)) for BF16 keys: the per-row kernel's arithmetic (four
+// 16x16x32 MFMAs per head tile, the NaN guard, integer-max ReLU).
+__device__ __forceinline__ void step_sums_bf16(const uint8_t* my, const bf16x8 (&qa)[4][4], const float (&wr)[4][4],
+                                               int g, int li, float (&v)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int kk = 16 * u + li;
+        bf16x8 kb[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            kb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(my + kk * 256 + 16 * ((4 * s + g) ^ (kk & 15))));
+        // the four head tiles' chains interleaved (independent accumulators between dependent MFMAs)
+        f32x4 acc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[t] = Mma<__bf16>::k32(acc[t], qa[t][s], kb[s]);
+        float acc_sum = nan_guard(acc[0][0]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) acc_sum += wr[t][rr] * relu_bits(acc[t][rr]);
+        v[u] = acc_sum;
+    }
+}
+
+constexpr int kReindexMaxSteps = 8;  // 64-column steps per wave at most (the step loop is unrolled)
+
+#ifndef CSA2_REINDEX_MIN_WG
+#define CSA2_REINDEX_MIN_WG 1
+#endif
+template <class KF, bool HIST, int DEPTH>
+__global__ __launch_bounds__(256, CSA2_REINDEX_MIN_WG) void indexer_reindex_kernel(const IndexParams p, int steps_per_wave) {
+    __shared__ uint32_t hist[HIST ? kKeyBins : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * KF::kRowBytes];
+    __shared__ uint32_t scl_all[4][KF::kScaleInScore ? 1 : 64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, li = lane & 15;
+    const int r = blockIdx.y;
+    const int64_t nv = uniform64((p.pos[r] + 1) / p.ratio);
+    const int64_t base = uniform64(p.row_base[r]);
+    const int nb = p.n_blocks;
+    const int n_steps = (nb + 7) / 8;
+    const int step0 = blockIdx.x * 4 * steps_per_wave + wave;  // this wave's steps: step0 + 4 i
+    float* srow = p.scores + (int64_t)r * p.width;
+    uint8_t* my = stage[wave];
+    uint32_t* scl = scl_all[wave];
+    const uint8_t* plane = reinterpret_cast<const uint8_t*>(p.k) + base * KF::kRowBytes;
+
+    // Candidate ids of this wave's steps first (every load address depends on them): creg[h] in
+    // lane 8 i' + k holds slot k of step 8 h + i' (-1 past the row's slots; the last register
+    // serves the loads issued past the last step).
+    const int32_t* crow = p.cand + (int64_t)r * nb;
+    int32_t creg[kReindexMaxSteps / 8 + 1];
+#pragma unroll
+    for (int h = 0; h < kReindexMaxSteps / 8; ++h) {
+        const int i = 8 * h + (lane >> 3);
+        const int slot = 8 * (step0 + 4 * i) + (lane & 7);
+        creg[h] = (i < steps_per_wave && slot < nb) ? crow[slot] : -1;
+    }
+    creg[kReindexMaxSteps / 8] = -1;
+
+    // Query fragments and head weights of row r (in flight while the first steps' loads are issued).
+    typedef typename std::conditional<KF::kDense, bf16x8[4][4], i32x8[4]>::type QFrags;
+    QFrags qa;
+    uint32_t qs[4];
+    float wr[4][4];
+    if constexpr (KF::kDense) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) qa[t][s] = IdxOps<CSA2_BF16, 128>::load(p.q, (int64_t)r * 64 + 16 * t + li, s, g);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) wr[t][rr] = p.w[(int64_t)r * 64 + 16 * t + 4 * g + rr];
+            qs[t] = 0u;
+        }
+    } else {
+        load_query<KF>(p, r, g, li, qa, qs, wr);
+    }
+
+    if (HIST) {
+        for (int b = threadIdx.x; b < kKeyBins; b += 256) hist[b] = 0u;
+        __syncthreads();
+    }
+
+    // Set once the query is in: a NaN in it makes every score NaN.
+    bool q_nan = false;
+    float row_scale = p.scale;
+
+    struct Buf {
+        u32x4 v[KF::kLoads];
+        uint32_t sw;  // scale word of this lane's column (FP8: float bits; MXFP4: 4 E8M0 bytes)
+        bool ok;      // this lane's column is valid
+    };
+    auto issue = [&](int i, Buf& b) {
+        // Per slot: the block's first row and how many of its rows are visible (uniform).
+        const uint8_t* bp[8];
+        int lim[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int32_t c = __builtin_amdgcn_readlane(creg[i >> 3], ((i & 7) << 3) + k);
+            const int64_t rem = nv - (int64_t)c * 8;
+            const int l = c < 0 ? 0 : (rem >= 8 ? 8 : (rem <= 0 ? 0 : (int)rem));
+            lim[k] = l;
+            bp[k] = l > 0 ? plane + (int64_t)c * 8 * KF::kRowBytes : plane;
+        }
+        constexpr int per = 64 / KF::kLoads;  // keys per load instruction
+#pragma unroll
+        for (int j = 0; j < KF::kLoads; ++j) {
+            const int kk = j * per + lane / KF::kChunks;
+            const int kA = (j * per) / 8, kB = (j * per + per - 1) / 8;
+            const bool second = kA != kB && (kk >> 3) != kA;
+            const uint8_t* q = second ? bp[kB] : bp[kA];
+            const int l = second ? lim[kB] : lim[kA];
+            const int t = kk & 7;
+            // non-temporal: each block is read once (measured ~10 % faster than ordinary loads here)
+            b.v[j] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(q + ((t < l ? t * KF::kRowBytes : 0) + 16 * (lane % KF::kChunks))));
+        }
+        const int32_t c = __shfl(creg[i >> 3], ((i & 7) << 3) + (lane >> 3), 64);
+        const int t = lane & 7;
+        b.ok = c >= 0 && (int64_t)c * 8 + t < nv;
+        if constexpr (!KF::kDense) {
+            const int64_t row = b.ok ? base + (int64_t)c * 8 + t : base;
+            b.sw = *reinterpret_cast<const uint32_t*>(KF::scale_base(p, row));
+        } else {
+            b.sw = 0u;
+        }
+    };
+    auto step = [&](int i, Buf& b) {
+        stage_put<KF>(my, scl, b.v, b.sw, lane);
+        float sc;
+        if constexpr (KF::kDense) sc = row_scale;
+        else sc = KF::score_scale(p.scale, b.sw, q_nan);
+        const bool valid = b.ok;
+        // Unconditional: past the wave's last step the ids are -1 and the loads read the plane's
+        // first row.
+        issue(i + DEPTH, b);
+        // Scheduling fence: the compiler would otherwise pull the next step's staging (and the
+        // wait for its loads) into this step's MFMA chains, stalling them on memory.
+        __builtin_amdgcn_sched_barrier(0);
+        float v[4];
+        if constexpr (KF::kDense) step_sums_bf16(my, qa, wr, g, li, v);
+        else step_sums<KF>(my, scl, qa, qs, wr, g, li, v);
+        const float kk = reduce_scatter(v, lane);
+        const int64_t c_out = (int64_t)(step0 + 4 * i) * 64 + lane;
+        const float score = valid ? sc * kk : kNegInf;
+        if (c_out < p.width) {
+            srow[c_out] = score;
+            if (HIST && valid) atomicAdd(&hist[order_key(score) >> 20], 1u);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // steps this wave makes (wave-uniform)
+    const int n_mine = step0 < n_steps ? min(steps_per_wave, (n_steps - step0 + 3) / 4) : 0;
+    Buf bufs[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) issue(d, bufs[d]);
+    if constexpr (KF::kDense) {
+        bool qn = false;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) qn |= frag_has_nan(qa[t][s]);
+        q_nan = __ballot(qn) != 0ull;
+    } else {
+        q_nan = KF::query_nan(qa, qs);
+    }
+    row_scale = q_nan ? __builtin_nanf("") : p.scale;
+#pragma unroll
+    for (int it = 0; it < kReindexMaxSteps; ++it) {
+        if (it >= n_mine) break;
+        step(it, bufs[it % DEPTH]);
+    }
+    if (HIST) {
+        __syncthreads();
+        uint32_t* gh = p.key_hist + (int64_t)r * kKeyBins;
+        for (int b = threadIdx.x; b < kKeyBins; b += 256)
+            if (hist[b]) atomicAdd(&gh[b], hist[b]);
+    }
+}
+
 __global__ __launch_bounds__(256) void key_hist_zero_kernel(uint32_t* h, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) h[i] = 0u;
 }
@@ -936,6 +1154,42 @@ static hipError_t launch_stream_full(const IndexParams& p, int rows, hipStream_t
     return hipGetLastError();
 }
 
+// Steps of loads in flight per wave and waves per launch of the REINDEX kernel (BF16 rows, quantised
+// rows); build-time constants so launch shapes can be swept.
+#ifndef CSA2_REINDEX_DEPTH
+#define CSA2_REINDEX_DEPTH 1
+#endif
+#ifndef CSA2_REINDEX_WAVES_BF16
+#define CSA2_REINDEX_WAVES_BF16 1024
+#endif
+#ifndef CSA2_REINDEX_WAVES_Q
+#define CSA2_REINDEX_WAVES_Q 2048
+#endif
+constexpr int kReindexDepth = CSA2_REINDEX_DEPTH;
+
+// REINDEX over 8-row blocks: as many waves as fit the chip in one round (BF16: ~300 registers,
+// one wave per SIMD; FP8 / MXFP4: two), each taking up to kReindexMaxSteps steps of its row.
+template <class KF>
+static hipError_t launch_reindex(const IndexParams& p, int rows, hipStream_t stream) {
+    const int n_steps = (p.n_blocks + 7) / 8;
+    const int64_t total = (int64_t)n_steps * rows;
+    const int64_t waves = KF::kDense ? CSA2_REINDEX_WAVES_BF16 : CSA2_REINDEX_WAVES_Q;
+    int64_t spw = (total + waves - 1) / waves;
+    if (spw < 1) spw = 1;
+    if (spw > kReindexMaxSteps) spw = kReindexMaxSteps;
+    const int per_wg = 4 * (int)spw;
+    const dim3 grid((unsigned)((n_steps + per_wg - 1) / per_wg), (unsigned)rows);
+    if (p.key_hist != nullptr) {
+        const int64_t nh = (int64_t)rows * kKeyBins;
+        hipLaunchKernelGGL(key_hist_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)),
+                           dim3(256), 0, stream, p.key_hist, nh);
+        hipLaunchKernelGGL((indexer_reindex_kernel<KF, true, kReindexDepth>), grid, dim3(256), 0, stream, p, (int)spw);
+    } else {
+        hipLaunchKernelGGL((indexer_reindex_kernel<KF, false, kReindexDepth>), grid, dim3(256), 0, stream, p, (int)spw);
+    }
+    return hipGetLastError();
+}
+
 // Rows sharing one BF16 plane, scores only (no histogram, no block scores).
 static bool chunk_path(const IndexParams& p, int rows, int heads, int dim, int dtype, bool reindex) {
     return p.shared_plane && !reindex && heads == 64 && dim == 128 && dtype == CSA2_BF16 && rows >= kChunkRows &&
@@ -957,11 +1211,15 @@ hipError_t launch_indexer_score(const IndexParams& p, int rows, int heads, int d
                                 hipStream_t stream) {
     if (chunk_path(p, rows, heads, dim, dtype, reindex)) return launch_chunk(p, rows, stream);
     if (heads == 64 && dim == 128) {
-        if (dtype == CSA2_BF16) return reindex ? launch_one<CSA2_BF16, 64, 128, true>(p, rows, stream)
+        const bool blocks8 = reindex && p.block_rows == 8;  // the pages' 8-row candidate blocks
+        if (dtype == CSA2_BF16) return blocks8 ? launch_reindex<Bf16Keys>(p, rows, stream)
+                                     : reindex ? launch_one<CSA2_BF16, 64, 128, true>(p, rows, stream)
                                                : launch_one<CSA2_BF16, 64, 128, false>(p, rows, stream);
-        if (dtype == CSA2_FP8_E4M3) return reindex ? launch_one<CSA2_FP8_E4M3, 64, 128, true>(p, rows, stream)
+        if (dtype == CSA2_FP8_E4M3) return blocks8 ? launch_reindex<Fp8Keys>(p, rows, stream)
+                                         : reindex ? launch_one<CSA2_FP8_E4M3, 64, 128, true>(p, rows, stream)
                                                    : launch_stream_full<Fp8Keys>(p, rows, stream);
-        if (dtype == CSA2_FP4_E2M1) return reindex ? hipErrorInvalidValue : launch_stream_full<Fp4Keys>(p, rows, stream);
+        if (dtype == CSA2_FP4_E2M1) return blocks8 ? launch_reindex<Fp4Keys>(p, rows, stream)
+                                         : reindex ? hipErrorInvalidValue : launch_stream_full<Fp4Keys>(p, rows, stream);
         if (dtype == CSA2_F32) return reindex ? launch_one<CSA2_F32, 64, 128, true>(p, rows, stream)
                                               : launch_one<CSA2_F32, 64, 128, false>(p, rows, stream);
     }

@@ -599,10 +599,13 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const TopkParams p
 // chunk is at least 4096 columns, and min_chunk when that still leaves >= 512
 // workgroups (the filter pass sweeps kSweep columns per workgroup at a time, so
 // smaller chunks leave lanes idle).
+#ifndef CSA2_TOPK_WIDE_MIN
+#define CSA2_TOPK_WIDE_MIN 8192
+#endif
 void topk_plan(int rows, int64_t width, int& chunk, int& nseg, int min_chunk) {
     chunk = 0;
     nseg = 0;
-    if (rows <= 0 || rows >= 1024 || width < 8192) return;
+    if (rows <= 0 || rows >= 1024 || width < CSA2_TOPK_WIDE_MIN) return;
     int64_t target = 4096 / rows;
     if (target < 1) target = 1;
     int64_t c = (width + target - 1) / target;

@@ -160,7 +160,8 @@ def test_score_free_mode_rules():
 
 
 def test_mxfp4_indexer_rules():
-    """MXFP4 q and k take both E8M0 planes (4-byte aligned for k) and no float scale; FULL 64 x 128 only."""
+    """MXFP4 q and k take both E8M0 planes (4-byte aligned for k) and no float scale; 64 x 128, FULL or
+    REINDEX over 8-row blocks."""
     ptr = ctypes.c_void_p(0x1000)
     fp4 = dict(q_dtype=csa2.FP4_E2M1, k_dtype=csa2.FP4_E2M1, q_scale_e8m0=ptr, k_scale_e8m0=ptr, width=1 << 20)
     call = lambda **kw: csa2._lib.csa2_indexer_score(ctypes.byref(_index_args(**dict(fp4, **kw))), None)
@@ -170,7 +171,9 @@ def test_mxfp4_indexer_rules():
     assert call(k_scale_e8m0=ctypes.c_void_p(0x1002)) == csa2.ERR_INVALID_ARG
     assert call(k_scale=ptr) == csa2.ERR_INVALID_ARG
     assert call(heads=4, dim=32) == csa2.ERR_UNSUPPORTED
-    assert call(mode=csa2.MODE_REINDEX, cand=ptr, n_blocks=2048, block_rows=8, width=16384) == csa2.ERR_UNSUPPORTED
+    # MXFP4 REINDEX: the 8-row candidate blocks of the pages' pool only
+    assert call(mode=csa2.MODE_REINDEX, cand=ptr, n_blocks=2048, block_rows=16, width=32768) == csa2.ERR_UNSUPPORTED
+    assert call(mode=csa2.MODE_REINDEX, cand=ptr, n_blocks=0, block_rows=8, width=0) == csa2.ERR_INVALID_ARG
     # the E8M0 planes belong to MXFP4 only
     a = _index_args(q_scale_e8m0=ptr, k_scale_e8m0=ptr)
     assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG

@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 CASES = [("tiny_full_fp32", 2, False), ("full_decode_64k", 2, False), ("full_decode_64k", 1, True),
          ("prefill_4096_at_128k", 2, False),
          ("reindex_decode_1m", 0, False), ("reindex_decode_1m", 1, False), ("reindex_decode_1m", 2, False),
-         ("reindex_decode_1m", 3, True),
+         ("reindex_decode_1m", 3, True), ("reindex_fp8_decode_1m", 2, False), ("reindex_pages_decode_1m", 2, False),
          ("lowp_full_decode_1m", 0, False), ("lowp_full_decode_1m", 1, False), ("lowp_full_decode_1m", 2, False),
          ("lowp_full_decode_1m", 3, True),
          ("lowp_pool_decode_1m", 2, False), ("pages_fp4_decode_1m", 2, False), ("lowp_owner_decode_1m", 2, False),

@@ -27,6 +27,13 @@ SMALL = {
                                                                  value_scale="unit"),
     "reindex_small": CONFIGS["reindex_decode_1m"].replace(batch=7, q_tokens=7, context=40001, n_blocks=200,
                                                           ragged=True),
+    "reindex_fp8_small": CONFIGS["reindex_fp8_decode_1m"].replace(batch=7, q_tokens=7, context=40001, n_blocks=203,
+                                                                  ragged=True),
+    "reindex_pages_small": CONFIGS["reindex_pages_decode_1m"].replace(batch=7, q_tokens=7, context=40001,
+                                                                      n_blocks=197, ragged=True),
+    # blocks of 5 rows: the generic REINDEX kernel (the 8-row one serves block_rows == 8)
+    "reindex_b5_small": CONFIGS["reindex_decode_1m"].replace(batch=5, q_tokens=5, context=20011, n_blocks=150,
+                                                             block_rows=5, ragged=True),
     "lowp_small": CONFIGS["lowp_full_decode_1m"].replace(batch=7, q_tokens=7, context=5003, ragged=True),
     "pages_fp4_small": CONFIGS["pages_fp4_decode_1m"].replace(batch=7, q_tokens=7, context=5003, ragged=True),
     "prefill_small": CONFIGS["prefill_4096_at_128k"].replace(q_tokens=300, context=2000, reuse_layers=2),
@@ -275,10 +282,35 @@ def test_topk_wide_rows(rows, width, k, kind):
     assert np.array_equal(out.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("name", ["reindex_decode_1m", "reindex_fp8_decode_1m", "reindex_pages_decode_1m"])
+def test_reindex_equals_full_then_gather(name):
+    """REINDEX over 8-row blocks computes each column with the FULL pass's arithmetic, so its scores are
+    bit-identical to the FULL scores of the same plane rows (and -inf where the slot is -1 or the row is
+    past the visible prefix): ragged positions, rows that see fewer blocks than the pool, -1 slots
+    inside the id list's tail, a partially visible newest block, and a last step of fewer than 8 slots."""
+    cfg = CONFIGS[name].replace(batch=6, q_tokens=6, context=60001, n_blocks=317, ragged=True)
+    x = make_inputs(cfg, 23, device="cuda")
+    x["pos"][2] = 9                                   # 10 visible rows: 2 blocks, the newest partial
+    x["cand"][2] = -1
+    x["cand"][2, :2] = torch.tensor([0, 1], dtype=torch.int32)
+    full_cfg = cfg.replace(index_mode="full", n_blocks=0)
+    re_s = gpu_scores(cfg, x).cpu().numpy()
+    full_s = gpu_scores(full_cfg, {k: v for k, v in x.items() if k != "cand"}).cpu().numpy()
+    cand = x["cand"].cpu().numpy().astype(np.int64)
+    pos = x["pos"].cpu().numpy()
+    for r in range(cfg.q_tokens):
+        nv = (int(pos[r]) + 1) // cfg.ratio
+        rows, valid = oracle.indexer.reindex_rows(cand[r], 8, nv)
+        want = np.where(valid, full_s[r][np.where(valid, rows, 0)], -np.inf).astype(np.float32)
+        assert np.array_equal(re_s[r].view(np.uint32), want.view(np.uint32)), f"row {r}"
+
+
 @pytest.mark.parametrize("name,kw", [
     ("lowp_full_decode_1m", dict(batch=6, q_tokens=6, context=100003, ragged=True)),
     ("full_decode_64k", dict(batch=5, q_tokens=5, context=40000, ragged=True)),
     ("reindex_decode_1m", dict(batch=5, q_tokens=5, context=300000, ragged=True, n_blocks=8192)),
+    ("reindex_fp8_decode_1m", dict(batch=5, q_tokens=5, context=300000, ragged=True, n_blocks=8192)),
+    ("reindex_pages_decode_1m", dict(batch=5, q_tokens=5, context=300000, ragged=True, n_blocks=8192)),
 ])
 def test_key_hist_path(name, kw):
     """Indexer-built key histogram == host recount of the GPU scores; top-k through it is exact."""

@@ -78,6 +78,18 @@ CONFIGS = {
     "reindex_decode_1m": Csa2Config(
         name="reindex_decode_1m", phase="decode", index_mode="reindex", batch=32, q_tokens=32, context=1 << 20,
         ratio=1, n_blocks=2048, block_rows=8, value_scale="inv_sqrt_d", **_COMMON),
+    # The same REINDEX decode over quantised planes: FP8 index plane (128 B + float32 scale per row) with
+    # an FP8 indexer query, FP4 main plane (E8M0 / 32), FP8 SWA ring.
+    "reindex_fp8_decode_1m": Csa2Config(
+        name="reindex_fp8_decode_1m", phase="decode", index_mode="reindex", batch=32, q_tokens=32,
+        context=1 << 20, ratio=1, n_blocks=2048, block_rows=8, main_dtype="fp4", swa_dtype="fp8", idx_dtype="fp8",
+        value_scale="inv_sqrt_d", **_COMMON),
+    # ... and in the pages' 890 B/token formats: MXFP4 index plane (64 + 4 B per row) and query, packed FP4
+    # main rows with E4M3 / 16 (288 B), FP8 SWA rows with E8M0 / 32 (528 B); unit-scale values.
+    "reindex_pages_decode_1m": Csa2Config(
+        name="reindex_pages_decode_1m", phase="decode", index_mode="reindex", batch=32, q_tokens=32,
+        context=1 << 20, ratio=1, n_blocks=2048, block_rows=8, main_dtype="nvfp4", swa_dtype="fp8mx",
+        idx_dtype="fp4", value_scale="unit", **_COMMON),
     # 64 sequences at position 1048575; FP4 main plane, FP8 SWA ring, FP8 index plane and indexer query.
     "lowp_full_decode_1m": Csa2Config(
         name="lowp_full_decode_1m", phase="decode", index_mode="full", batch=64, q_tokens=64, context=1 << 20,
@@ -108,7 +120,7 @@ CONFIGS = {
 }
 
 CONFIG_ORDER = ["tiny_full_fp32", "full_decode_64k", "prefill_4096_at_128k", "reindex_decode_1m",
-                "lowp_full_decode_1m", "lowp_pool_decode_1m", "pages_fp4_decode_1m", "lowp_owner_decode_1m",
+                "reindex_fp8_decode_1m", "reindex_pages_decode_1m", "lowp_full_decode_1m", "lowp_pool_decode_1m", "pages_fp4_decode_1m", "lowp_owner_decode_1m",
                 "prefill_owner_4096_at_128k"]
 
 
