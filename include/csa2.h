@@ -162,8 +162,8 @@ typedef struct csa2_index_args {
     float scale;                /* score scale (dim^-1/2 * heads^-1/2 in the pages' model) */
     int32_t _pad1;
     float* scores;              /* out: [rows, width] float32; NULL selects score-free mode (see
-                                 * csa2_topk_rescore; FULL, FP8 or MXFP4 64 x 128, block_keys
-                                 * required, key_hist NULL) */
+                                 * csa2_topk_rescore; FULL, FP8 or MXFP4 64 x 128, or BF16 64 x 128
+                                 * with CSA2_INDEX_SHARED_PLANE; block_keys required, key_hist NULL) */
     uint32_t* key_hist;         /* optional out: [rows, 4096], or NULL.  The call zeroes it, then
                                  * counts every valid score of row r in bin key(score) >> 20, where
                                  * key is the order-preserving 32-bit key csa2_topk_select ranks by
@@ -205,12 +205,24 @@ int32_t csa2_indexer_score(const csa2_index_args* args, csa2_stream_t stream);
  * csa2_topk_select over their columns in bins >= b1.  The result is bit-identical to
  * csa2_topk_select over the scores csa2_indexer_score would have written.
  *
+ * BF16 planes whose rows share one plane (CSA2_INDEX_SHARED_PLANE: a prefill
+ * chunk, whose score matrix would be rows x width floats) take another route
+ * to the same result: the k best blocks by block key (ties to the lower
+ * block) are chosen, their 8 k columns re-scored with the FULL pass's
+ * arithmetic (the REINDEX kernel), and the exact select runs over those.
+ * Every selected column lies in a chosen block: its score is at least T, the
+ * k-th largest block key, so its block's key is too; all blocks with a key
+ * above T are chosen, and if the k-th largest score equals T, the
+ * lowest-numbered columns with score T lie in the lowest-numbered blocks with
+ * key T, as many of which are chosen as the k slots leave.
+ *
  * args: as given to the score-free csa2_indexer_score call (block_keys is now
  * an input; key_hist NULL; scores and block_max are ignored).
  * out: [rows, k] int32, ascending plane rows, -1 padded.
- * Supported: FP8-E4M3 or MXFP4 q and k with (heads, dim) = (64, 128); 1 <= k <= 2048;
- * rows < 1024 and 8192 <= width < 2^24 (exactly when
- * csa2_topk_rescore_workspace_size(rows, width, k) > 0), else CSA2_ERR_UNSUPPORTED.
+ * Supported: FP8-E4M3 or MXFP4 q and k with (heads, dim) = (64, 128), rows <
+ * 1024 and 8192 <= width < 2^24; or BF16 q and k with (heads, dim) = (64, 128)
+ * and CSA2_INDEX_SHARED_PLANE, any rows and width < 2^31; 1 <= k <= 2048; else
+ * CSA2_ERR_UNSUPPORTED.  The workspace size covers either route.
  */
 size_t csa2_topk_rescore_workspace_size(int32_t rows, int64_t width, int32_t k);
 

@@ -302,22 +302,33 @@ def topk_rescore_workspace_size(rows, width, k):
     return int(_lib.csa2_topk_rescore_workspace_size(int(rows), int(width), int(k)))
 
 
-def topk_rescore_supported(rows, width, k, heads=64, dim=128, fp8=True, fp4=False):
-    """Whether the score-free FULL path (indexer_score(scores=None) + topk_rescore) takes these sizes
-    (FP8-E4M3 or MXFP4 index planes)."""
-    return ((fp8 or fp4) and heads == 64 and dim == 128 and 1 <= k <= 2048 and
-            topk_rescore_workspace_size(rows, width, k) > 0)
+def topk_rescore_supported(rows, width, k, heads=64, dim=128, fp8=True, fp4=False, shared_plane=False):
+    """Whether the score-free FULL path (indexer_score(scores=None) + topk_rescore) takes these sizes:
+    FP8-E4M3 or MXFP4 index planes (wide rows), or a BF16 plane whose rows share it (``shared_plane``,
+    a prefill chunk; ``fp8`` and ``fp4`` False)."""
+    if heads != 64 or dim != 128 or not 1 <= k <= 2048 or rows < 1:
+        return False
+    if not (fp8 or fp4):
+        return bool(shared_plane) and width < (1 << 31)
+    return topk_rescore_workspace_size(rows, width, k) > 0 and _quant_rescore_plan(rows, width)
+
+
+def _quant_rescore_plan(rows, width):
+    # the wide-row plan the quantised planes' select uses: fewer than 1024 rows, 8192 <= width < 2^24
+    return rows < 1024 and 8192 <= width < (1 << 24)
 
 
 def topk_rescore(q, w, k, row_base, pos, ratio, scale, out, block_keys, width, *, k_scale=None,
-                 fp4=False, q_scale=None, workspace=None, stream=None):
+                 fp4=False, q_scale=None, dense=False, shared_plane=False, workspace=None, stream=None):
     """Top-k ``out`` [rows, k] int32 of the scores a score-free indexer_score call with these arguments kept on
     chip (its ``block_keys``); bit-identical to topk_select over the written scores.  FP8 index planes by
-    default, MXFP4 ones with ``fp4=True`` (and ``q_scale``, as for indexer_score)."""
+    default, MXFP4 ones with ``fp4=True`` (and ``q_scale``, as for indexer_score), BF16 ones with
+    ``dense=True`` and ``shared_plane=True`` (rows of one prefill chunk)."""
     _dev(out)
     _need(out, torch.int32, "out")
-    a = _index_args(q, w, k, row_base, pos, ratio, scale, None, width, k_scale, None, 8, not fp4, None, None,
-                    block_keys, fp4, q_scale)
+    a = _index_args(q, w, k, row_base, pos, ratio, scale, None, width, k_scale, None, 8, not (fp4 or dense), None,
+                    None, block_keys, fp4, q_scale)
+    a.flags = INDEX_SHARED_PLANE if shared_plane else 0
     if out.shape[0] != a.rows:
         raise ValueError("csa2.topk_rescore: out rows")
     need = topk_rescore_workspace_size(a.rows, a.width, out.shape[1])

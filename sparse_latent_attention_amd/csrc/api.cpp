@@ -40,6 +40,21 @@ bool index_scales_ok(const csa2_index_args* a) {
 }
 
 
+// Score-free mode over a BF16 plane: rows that share one plane (a prefill chunk), 64 x 128.
+bool dense_score_free(const csa2_index_args* a) {
+    return a->k_dtype == CSA2_BF16 && a->q_dtype == CSA2_BF16 && a->heads == 64 && a->dim == 128 &&
+           (a->flags & CSA2_INDEX_SHARED_PLANE) != 0 && a->width < (1LL << 31);
+}
+
+// Workspace of the BF16 score-free select: the chosen blocks [rows, k], their re-computed scores
+// [rows, 8 k], and the larger of the two selects' own workspaces.
+size_t dense_rescore_bytes(int32_t rows, int64_t width, int32_t k) {
+    if (rows <= 0 || width <= 0 || width >= (1LL << 31) || k < 1 || k > 2048) return 0;
+    const int64_t nbk = (width + 7) / 8;
+    const size_t t1 = csa2::topk_workspace_bytes(rows, nbk), t2 = csa2::topk_workspace_bytes(rows, 8 * (int64_t)k);
+    return align256((size_t)rows * k * 4) + align256((size_t)rows * 8 * k * 4) + align256(t1 > t2 ? t1 : t2);
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,8 +116,9 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
     if (a->block_keys != nullptr && !score_free) return CSA2_ERR_INVALID_ARG;
     if (score_free) {
         if (reindex || a->key_hist != nullptr || a->block_keys == nullptr) return CSA2_ERR_INVALID_ARG;
-        if (!csa2::indexer_rescore_supported(a->heads, a->dim, a->k_dtype)) return CSA2_ERR_UNSUPPORTED;
-        if (a->width >= (1LL << 24)) return CSA2_ERR_UNSUPPORTED;
+        if (!csa2::indexer_rescore_supported(a->heads, a->dim, a->k_dtype) && !dense_score_free(a))
+            return CSA2_ERR_UNSUPPORTED;
+        if (a->width >= (1LL << 24) && !dense_score_free(a)) return CSA2_ERR_UNSUPPORTED;
         if (!aligned(a->block_keys, 4)) return CSA2_ERR_INVALID_ARG;
     }
     if (a->q == nullptr || a->w == nullptr || a->k == nullptr || a->row_base == nullptr || a->pos == nullptr)
@@ -147,8 +163,8 @@ static void rescore_plan(int32_t rows, int64_t width, int& chunk, int& nseg) {
     csa2::topk_plan(rows, width, chunk, nseg, 4096);
 }
 
-size_t csa2_topk_rescore_workspace_size(int32_t rows, int64_t width, int32_t k) {
-    (void)k;
+// Workspace of the quantised-plane score-free select (0: these sizes have no plan).
+static size_t quant_rescore_bytes(int32_t rows, int64_t width) {
     int chunk, nseg;
     rescore_plan(rows, width, chunk, nseg);
     if (nseg == 0) return 0;
@@ -158,18 +174,64 @@ size_t csa2_topk_rescore_workspace_size(int32_t rows, int64_t width, int32_t k) 
            align256((size_t)rows * parts * 4096 * 4);
 }
 
+size_t csa2_topk_rescore_workspace_size(int32_t rows, int64_t width, int32_t k) {
+    const size_t a = quant_rescore_bytes(rows, width), b = dense_rescore_bytes(rows, width, k);
+    return a > b ? a : b;
+}
+
+// BF16 plane: the k best 8-column blocks by block key (ties to the lower block), re-scored with the FULL
+// pass's arithmetic through the REINDEX kernel, then the exact select over their columns.  The top-k of
+// the row lies in those blocks: a column with one of the k largest scores has a score >= T, the k-th
+// largest block key, so its block's key is >= T; every block with a key > T is chosen, and if the k-th
+// largest score equals T, the lowest-numbered columns with score T lie in the lowest-numbered blocks with
+// key T (each such block holds at least one), of which the k - #(keys > T) lowest are chosen.
+static int32_t dense_rescore(const csa2_index_args* a, int32_t k, int32_t* out, void* workspace, hipStream_t st) {
+    const int rows = a->rows;
+    const int64_t nbk = (a->width + 7) / 8;
+    char* w = static_cast<char*>(workspace);
+    int32_t* cand = reinterpret_cast<int32_t*>(w);
+    w += align256((size_t)rows * k * 4);
+    float* sc = reinterpret_cast<float*>(w);
+    w += align256((size_t)rows * 8 * k * 4);
+    void* tws = w;
+
+    csa2::TopkParams bp;  // best k blocks
+    bp.scores = nullptr; bp.pos = a->pos; bp.cand = nullptr; bp.out = cand; bp.key_hist = nullptr;
+    bp.width = nbk; bp.k = k; bp.ratio = a->ratio; bp.n_blocks = 0; bp.block_rows = 1; bp.col_group = 8;
+    bp.pool_keys = a->block_keys; bp.plain_keys = true;
+    hipError_t e = csa2::launch_topk_select(bp, rows, tws, st);
+
+    csa2::IndexParams ip;  // their columns, re-scored
+    ip.q = a->q; ip.w = a->w; ip.k = a->k; ip.k_scale = nullptr; ip.row_base = a->row_base; ip.pos = a->pos;
+    ip.q_e8 = nullptr; ip.k_e8 = nullptr; ip.cand = cand; ip.scores = sc; ip.key_hist = nullptr;
+    ip.block_max = nullptr; ip.block_keys = nullptr; ip.width = 8 * (int64_t)k; ip.cols_per_wg = 0;
+    ip.bm_blocks = 0; ip.n_blocks = k; ip.block_rows = 8; ip.bm_rows = 4; ip.ratio = a->ratio; ip.scale = a->scale;
+    ip.shared_plane = false;
+    if (e == hipSuccess) e = csa2::launch_indexer_score(ip, rows, 64, 128, CSA2_BF16, true, st);
+
+    csa2::TopkParams fp;  // the exact select over them
+    fp.scores = sc; fp.pos = a->pos; fp.cand = cand; fp.out = out; fp.key_hist = nullptr;
+    fp.width = 8 * (int64_t)k; fp.k = k; fp.ratio = a->ratio; fp.n_blocks = k; fp.block_rows = 8; fp.col_group = 1;
+    fp.pool_keys = nullptr; fp.plain_keys = false;
+    if (e == hipSuccess) e = csa2::launch_topk_select(fp, rows, tws, st);
+    return hip_status(e);
+}
+
 int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, void* workspace, size_t workspace_bytes,
                           csa2_stream_t stream) {
     if (a == nullptr || a->struct_size < sizeof(csa2_index_args)) return CSA2_ERR_INVALID_ARG;
     if (a->mode != CSA2_MODE_FULL || a->rows < 0 || a->width < 0 || (a->ratio != 1 && a->ratio != 2))
         return CSA2_ERR_INVALID_ARG;
     if (k < 1 || k > 2048 || (a->flags & ~CSA2_INDEX_SHARED_PLANE) != 0) return CSA2_ERR_INVALID_ARG;
-    if (a->q_dtype != a->k_dtype || !csa2::indexer_rescore_supported(a->heads, a->dim, a->k_dtype))
+    const bool dense = a->q_dtype == a->k_dtype && dense_score_free(a);
+    if (!dense && (a->q_dtype != a->k_dtype || !csa2::indexer_rescore_supported(a->heads, a->dim, a->k_dtype)))
         return CSA2_ERR_UNSUPPORTED;
     if (a->rows == 0) return CSA2_OK;
-    int chunk, nseg;
-    rescore_plan(a->rows, a->width, chunk, nseg);
-    if (nseg == 0) return CSA2_ERR_UNSUPPORTED;  // narrow rows: score, then csa2_topk_select
+    int chunk = 0, nseg = 0;
+    if (!dense) {
+        rescore_plan(a->rows, a->width, chunk, nseg);
+        if (nseg == 0) return CSA2_ERR_UNSUPPORTED;  // narrow rows: score, then csa2_topk_select
+    }
     const size_t need = csa2_topk_rescore_workspace_size(a->rows, a->width, k);
     if (workspace_bytes < need) return CSA2_ERR_WORKSPACE;
     if (workspace == nullptr || !aligned(workspace, 256)) return CSA2_ERR_INVALID_ARG;
@@ -178,6 +240,7 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
         return CSA2_ERR_INVALID_ARG;
     if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->w, 4) || !isfinite(a->scale))
         return CSA2_ERR_INVALID_ARG;
+    if (dense) return dense_rescore(a, k, out, workspace, reinterpret_cast<hipStream_t>(stream));
 
     csa2::IndexParams ip;
     ip.q = a->q; ip.w = a->w; ip.k = a->k; ip.k_scale = a->k_scale; ip.row_base = a->row_base; ip.pos = a->pos;
@@ -188,7 +251,7 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
     csa2::TopkParams tp;
     tp.scores = nullptr; tp.pos = a->pos; tp.cand = nullptr; tp.out = out; tp.key_hist = nullptr;
     tp.width = a->width; tp.k = k; tp.ratio = a->ratio; tp.n_blocks = 0; tp.block_rows = 1; tp.col_group = 1;
-    tp.pool_keys = nullptr;
+    tp.pool_keys = nullptr; tp.plain_keys = false;
 
     char* w = static_cast<char*>(workspace);
     uint32_t* b1 = reinterpret_cast<uint32_t*>(w);
@@ -298,7 +361,7 @@ int32_t csa2_topk_select(const csa2_topk_args* a, void* workspace, size_t worksp
     p.width = a->width; p.k = a->k; p.ratio = a->ratio; p.n_blocks = a->n_blocks;
     p.block_rows = a->n_blocks > 0 ? a->block_rows : 1;
     p.col_group = 1;
-    p.pool_keys = nullptr;
+    p.pool_keys = nullptr; p.plain_keys = false;
     return hip_status(csa2::launch_topk_select(p, a->rows, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -338,7 +401,7 @@ int32_t csa2_candidate_pool(const csa2_pool_args* a, void* workspace, size_t wor
     p.scores = bmax; p.pos = a->pos; p.cand = nullptr; p.out = a->cand; p.key_hist = nullptr;
     p.width = nb; p.k = a->n_cand; p.ratio = a->ratio; p.n_blocks = 0; p.block_rows = 1;
     p.col_group = a->block_rows;
-    p.pool_keys = a->block_keys;
+    p.pool_keys = a->block_keys; p.plain_keys = false;
     if (a->block_keys != nullptr) p.scores = nullptr;
     void* tws = need > 0 ? ws + align256((size_t)a->rows * (size_t)nb * sizeof(float)) : nullptr;
     return hip_status(csa2::launch_topk_select(p, a->rows, tws, st));

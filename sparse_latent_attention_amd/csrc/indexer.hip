@@ -360,7 +360,38 @@ constexpr int kChunkKeys = 128;     // key rows per LDS stage (64 measured ~3 % 
 // 272 bytes) measured 2.7 conflict cycles per LDS cycle with rocprofv3.
 __device__ __forceinline__ int stage_off(int k, int c) { return 256 * k + 16 * (c ^ (k & 15)); }
 
-template <int ROWS, int KEYS>
+// Output of one 64-column step of the chunk kernel: the scores, or (BK, score-free mode) only the block
+// key of each 8 columns -- the largest order key of the valid ones, NaN as kNanBlockKey, 0 for none.
+template <bool BK>
+__device__ __forceinline__ void chunk_store(const IndexParams& p, int r, int64_t nv, int64_t cb, int64_t c_end,
+                                            int lane, const float (&v)[4], float sc, bool valid, float* srow) {
+    if constexpr (!BK) {
+        store_step<false, false>(p, r, nv, cb, c_end, lane, v, sc, valid, srow, nullptr);
+    } else {
+        const float kk = reduce_scatter(v, lane);
+        const float score = valid ? sc * kk : kNegInf;
+        uint32_t bk = valid ? block_key(score) : 0u;
+#pragma unroll
+        for (int o = 1; o < kKeyBlock; o <<= 1) bk = max(bk, shfl_xor(bk, o));
+        const int64_t c_out = cb + lane;
+        if ((lane & (kKeyBlock - 1)) == 0 && c_out < c_end)
+            p.block_keys[(int64_t)r * ((p.width + kKeyBlock - 1) / kKeyBlock) + c_out / kKeyBlock] = bk;
+    }
+}
+
+template <bool BK>
+__device__ __forceinline__ void chunk_store_invisible(const IndexParams& p, int r, int64_t cb, int64_t c_end, int lane,
+                                                      float* srow) {
+    if constexpr (!BK) {
+        store_invisible<false>(p, r, cb, c_end, lane, srow);
+    } else {
+        const int64_t c_out = cb + lane;
+        if ((lane & (kKeyBlock - 1)) == 0 && c_out < c_end)
+            p.block_keys[(int64_t)r * ((p.width + kKeyBlock - 1) / kKeyBlock) + c_out / kKeyBlock] = 0u;
+    }
+}
+
+template <int ROWS, int KEYS, bool BK>
 __global__ __launch_bounds__(64 * ROWS) void indexer_chunk_kernel(const IndexParams p, int rows) {
     typedef IdxOps<CSA2_BF16, 128> Ops;
     typedef Ops::Frag Frag;
@@ -385,7 +416,7 @@ __global__ __launch_bounds__(64 * ROWS) void indexer_chunk_kernel(const IndexPar
     const int64_t c0 = (int64_t)blockIdx.y * p.cols_per_wg;
     const int64_t c1 = c0 + p.cols_per_wg < p.width ? c0 + p.cols_per_wg : p.width;
     const int64_t c_live = nvg < c1 ? nvg : c1;
-    float* srow = p.scores + (int64_t)rq * p.width;
+    float* srow = BK ? nullptr : p.scores + (int64_t)rq * p.width;
 
     Frag qa[HT][S];
     float wr[HT][4];
@@ -472,8 +503,7 @@ __global__ __launch_bounds__(64 * ROWS) void indexer_chunk_kernel(const IndexPar
                 if (st + 1 < KEYS / 64) {
                     const int64_t cb = cs + 64 * st;
                     const int64_t c_out = cb + lane;
-                    store_step<false, false>(p, rq, nv, cb, c1, lane, v, row_scale, c_out < c1 && c_out < nv, srow,
-                                             nullptr);
+                    chunk_store<BK>(p, rq, nv, cb, c1, lane, v, row_scale, c_out < c1 && c_out < nv, srow);
                 } else {
 #pragma unroll
                     for (int u = 0; u < 4; ++u) vlast[u] = v[u];
@@ -486,13 +516,13 @@ __global__ __launch_bounds__(64 * ROWS) void indexer_chunk_kernel(const IndexPar
         if (live) {
             const int64_t cb = cs + KEYS - 64;
             const int64_t c_out = cb + lane;
-            store_step<false, false>(p, rq, nv, cb, c1, lane, vlast, row_scale, c_out < c1 && c_out < nv, srow, nullptr);
+            chunk_store<BK>(p, rq, nv, cb, c1, lane, vlast, row_scale, c_out < c1 && c_out < nv, srow);
         }
         __syncthreads();
         b ^= 1;
     }
     if (live)
-        for (; cs < c1; cs += 64) store_invisible<false>(p, rq, cs, c1, lane, srow);  // nothing visible here
+        for (; cs < c1; cs += 64) chunk_store_invisible<BK>(p, rq, cs, c1, lane, srow);  // nothing visible here
 }
 
 // Steps of key-row loads each wave keeps in flight in the streaming FULL
@@ -1190,10 +1220,13 @@ static hipError_t launch_reindex(const IndexParams& p, int rows, hipStream_t str
     return hipGetLastError();
 }
 
-// Rows sharing one BF16 plane, scores only (no histogram, no block scores).
+// Rows sharing one BF16 plane: scores only (no histogram, no block scores), or in score-free mode
+// (scores == NULL) the block keys only.
 static bool chunk_path(const IndexParams& p, int rows, int heads, int dim, int dtype, bool reindex) {
-    return p.shared_plane && !reindex && heads == 64 && dim == 128 && dtype == CSA2_BF16 && rows >= kChunkRows &&
-           p.scores != nullptr && p.key_hist == nullptr && p.block_max == nullptr && p.block_keys == nullptr;
+    if (!p.shared_plane || reindex || heads != 64 || dim != 128 || dtype != CSA2_BF16) return false;
+    if (p.key_hist != nullptr || p.block_max != nullptr) return false;
+    if (p.scores == nullptr) return p.block_keys != nullptr;  // score-free: any number of rows
+    return rows >= kChunkRows && p.block_keys == nullptr;
 }
 
 static hipError_t launch_chunk(IndexParams p, int rows, hipStream_t stream) {
@@ -1203,7 +1236,12 @@ static hipError_t launch_chunk(IndexParams p, int rows, hipStream_t stream) {
     if (need > cw) cw = (need + kChunkKeys - 1) / kChunkKeys * kChunkKeys;
     p.cols_per_wg = cw;
     const dim3 grid((unsigned)((rows + kChunkRows - 1) / kChunkRows), (unsigned)((p.width + cw - 1) / cw));
-    hipLaunchKernelGGL((indexer_chunk_kernel<kChunkRows, kChunkKeys>), grid, dim3(64 * kChunkRows), 0, stream, p, rows);
+    if (p.scores == nullptr)
+        hipLaunchKernelGGL((indexer_chunk_kernel<kChunkRows, kChunkKeys, true>), grid, dim3(64 * kChunkRows), 0, stream, p,
+                           rows);
+    else
+        hipLaunchKernelGGL((indexer_chunk_kernel<kChunkRows, kChunkKeys, false>), grid, dim3(64 * kChunkRows), 0, stream,
+                           p, rows);
     return hipGetLastError();
 }
 

@@ -53,6 +53,9 @@ struct TopkParams {
     // block score of pool_keys[r * width + c] (the newest valid column pinned to +inf)
     // instead of scores.
     const uint32_t* pool_keys;
+    // With pool_keys: rank column c by the plain block key pool_keys[r * width + c] instead (the
+    // largest score of an 8-column block, NaN as -inf; no pinning): the best blocks of a score row.
+    bool plain_keys;
 };
 
 // Bytes of workspace the launch plan for (rows, width) needs (0: one workgroup per row).

@@ -131,9 +131,12 @@ __device__ __forceinline__ uint32_t pool_rank_key(uint32_t bk, bool newest) {
     return newest ? 0xff800000u : order_key(pool_value_of_block_key(bk));
 }
 
-// Positions of the full score row: column i, validity from the row geometry.
-// POOL: the row holds candidate-pool block keys instead of scores.
-template <bool POOL>
+// What a row holds: scores, candidate-pool block keys (ranked by the pool's block score, the
+// newest block pinned) or plain block keys (ranked as the largest score of the block, NaN as -inf).
+constexpr int kSrcScores = 0, kSrcPool = 1, kSrcKeys = 2;
+
+// Positions of the full row: column i, validity from the row geometry.
+template <int SRC>
 struct RowSrc {
     const TopkParams* p;
     const float* srow;
@@ -142,9 +145,13 @@ struct RowSrc {
     int r;
     int n;
     // the 32-bit word of column i (score bits or block key)
-    __device__ __forceinline__ uint32_t raw(int i) const { return POOL ? krow[i] : __float_as_uint(srow[i]); }
+    __device__ __forceinline__ uint32_t raw(int i) const {
+        return SRC == kSrcScores ? __float_as_uint(srow[i]) : krow[i];
+    }
     __device__ __forceinline__ uint32_t key_of(uint32_t w, int i) const {
-        return POOL ? pool_rank_key(w, i == nv - 1) : order_key(__uint_as_float(w));
+        if (SRC == kSrcPool) return pool_rank_key(w, i == nv - 1);
+        if (SRC == kSrcKeys) return w == kNanBlockKey ? 0x007fffffu : w;  // a NaN block ranks as -inf
+        return order_key(__uint_as_float(w));
     }
     __device__ __forceinline__ bool get(int i, uint32_t& key, int32_t& col) const {
         col = i;
@@ -281,15 +288,15 @@ __device__ __forceinline__ void select_core(const Src& src, const TopkParams& p,
     for (int i = (int)goal + tid; i < p.k; i += kThreads) orow[i] = -1;
 }
 
-template <bool POOL>
-__device__ __forceinline__ RowSrc<POOL> row_src(const TopkParams& p, int r) {
-    RowSrc<POOL> src;
+template <int SRC>
+__device__ __forceinline__ RowSrc<SRC> row_src(const TopkParams& p, int r) {
+    RowSrc<SRC> src;
     src.p = &p;
     src.r = r;
     src.nv = (p.pos[r] + 1) / p.ratio;
     if (p.col_group > 1) src.nv = (src.nv + p.col_group - 1) / p.col_group;
     src.srow = p.scores + (int64_t)r * p.width;
-    src.krow = POOL ? p.pool_keys + (int64_t)r * p.width : nullptr;
+    src.krow = SRC != kSrcScores ? p.pool_keys + (int64_t)r * p.width : nullptr;
     src.n = (p.n_blocks == 0) ? (int)(src.nv < p.width ? src.nv : p.width) : (int)p.width;
     return src;
 }
@@ -304,12 +311,12 @@ __global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t* buf, int64_t n
 }
 
 // grid (nseg, rows): 12-bit histogram of one chunk, added into hist[r][4096].
-template <bool POOL>
+template <int SRC>
 __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const TopkParams p, uint32_t* hist, int chunk) {
     __shared__ uint32_t h[4096];
     const int r = blockIdx.y;
     const int tid = threadIdx.x;
-    const RowSrc<POOL> src = row_src<POOL>(p, r);
+    const RowSrc<SRC> src = row_src<SRC>(p, r);
     for (int b = tid; b < 4096; b += kThreads) h[b] = 0;
     __syncthreads();
     const int c0 = blockIdx.x * chunk;
@@ -386,7 +393,7 @@ constexpr int kSweep = kThreads * kPerLane;
 // memory instead.  Sweeps as in topk_filter_kernel: wave w owns a contiguous
 // 1024-column slice and lane l its columns base + 64j + l (j < 16), whose
 // loads are all in flight before any is used.
-template <bool POOL>
+template <int SRC>
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(const TopkParams p) {
     __shared__ Lds s;
     __shared__ uint32_t lkeys[kLdsCand];
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const TopkParams 
     __shared__ uint32_t cnt[2][kWaves];
     const int r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const RowSrc<POOL> src = row_src<POOL>(p, r);
+    const RowSrc<SRC> src = row_src<SRC>(p, r);
     const int n = src.n;
     const uint32_t k = (uint32_t)p.k;
 
@@ -474,14 +481,14 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const TopkParams 
     select_core(lsrc, p, r, s);
 }
 
-template <bool POOL>
+template <int SRC>
 __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const TopkParams p, const uint32_t* b1_in,
                                                                uint32_t* cand_keys, int32_t* cand_cols,
                                                                uint32_t* seg_count, int chunk, int nseg) {
     __shared__ uint32_t cnt[2][kWaves];
     const int r = blockIdx.y, seg = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const RowSrc<POOL> src = row_src<POOL>(p, r);
+    const RowSrc<SRC> src = row_src<SRC>(p, r);
     const uint32_t b1 = b1_in[r];
     const int64_t base = ((int64_t)r * nseg + seg) * kCap;
     const int c0 = seg * chunk;
@@ -536,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const TopkParams 
 
 // grid rows: exact select over the candidates (or the full row after an overflow:
 // a list longer than its capacity `cap`).
-template <bool POOL>
+template <int SRC>
 __global__ __launch_bounds__(kThreads) void topk_final_kernel(const TopkParams p, const uint32_t* cand_keys,
                                                               const int32_t* cand_cols, const uint32_t* seg_count,
                                                               int nseg, int cap) {
@@ -564,7 +571,7 @@ __global__ __launch_bounds__(kThreads) void topk_final_kernel(const TopkParams p
     const int n = (int)s.seg_start[nseg];
     __syncthreads();
     if (overflow) {
-        select_core(row_src<POOL>(p, r), p, r, s);
+        select_core(row_src<SRC>(p, r), p, r, s);
         return;
     }
     CandSrc src;
@@ -630,13 +637,12 @@ size_t topk_workspace_bytes(int rows, int64_t width) {
            2 * align256((size_t)rows * nseg * kCap * 4);
 }
 
-hipError_t launch_topk_select(const TopkParams& p, int rows, void* ws, hipStream_t stream) {
-    const bool pool = p.pool_keys != nullptr;
+template <int SRC>
+static hipError_t launch_topk_src(const TopkParams& p, int rows, void* ws, hipStream_t stream) {
     int chunk, nseg;
     topk_plan(rows, p.width, chunk, nseg, kSweep);
     if (nseg == 0) {
-        if (pool) hipLaunchKernelGGL(topk_select_kernel<true>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
-        else hipLaunchKernelGGL(topk_select_kernel<false>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL(topk_select_kernel<SRC>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
         return hipGetLastError();
     }
     char* w = reinterpret_cast<char*>(ws);
@@ -655,25 +661,22 @@ hipError_t launch_topk_select(const TopkParams& p, int rows, void* ws, hipStream
         const int64_t nh = (int64_t)rows * 4096;
         hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)),
                            dim3(256), 0, stream, hist, nh);
-        if (pool) hipLaunchKernelGGL(topk_hist_kernel<true>, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0,
-                                     stream, p, hist, chunk);
-        else hipLaunchKernelGGL(topk_hist_kernel<false>, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0,
-                                stream, p, hist, chunk);
+        hipLaunchKernelGGL(topk_hist_kernel<SRC>, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0, stream, p,
+                           hist, chunk);
         h = hist;
     }
     hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, h, b1, 1);
-    if (pool) {
-        hipLaunchKernelGGL(topk_filter_kernel<true>, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0, stream, p,
-                           b1, keys, cols, seg_count, chunk, nseg);
-        hipLaunchKernelGGL(topk_final_kernel<true>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, keys, cols,
-                           seg_count, nseg, kCap);
-    } else {
-        hipLaunchKernelGGL(topk_filter_kernel<false>, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0, stream,
-                           p, b1, keys, cols, seg_count, chunk, nseg);
-        hipLaunchKernelGGL(topk_final_kernel<false>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, keys, cols,
-                           seg_count, nseg, kCap);
-    }
+    hipLaunchKernelGGL(topk_filter_kernel<SRC>, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0, stream, p, b1,
+                       keys, cols, seg_count, chunk, nseg);
+    hipLaunchKernelGGL(topk_final_kernel<SRC>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, keys, cols,
+                       seg_count, nseg, kCap);
     return hipGetLastError();
+}
+
+hipError_t launch_topk_select(const TopkParams& p, int rows, void* ws, hipStream_t stream) {
+    if (p.pool_keys == nullptr) return launch_topk_src<kSrcScores>(p, rows, ws, stream);
+    if (p.plain_keys) return launch_topk_src<kSrcKeys>(p, rows, ws, stream);
+    return launch_topk_src<kSrcPool>(p, rows, ws, stream);
 }
 
 // grid (nseg, rows): histogram of the block keys' top 12 bits, per row.  Each
@@ -733,7 +736,7 @@ hipError_t launch_topk_threshold(const TopkParams& p, int rows, const uint32_t* 
 
 hipError_t launch_topk_final(const TopkParams& p, int rows, const uint32_t* cand_keys, const int32_t* cand_cols,
                              const uint32_t* seg_count, int nseg, int cap, hipStream_t stream) {
-    hipLaunchKernelGGL(topk_final_kernel<false>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, cand_keys,
+    hipLaunchKernelGGL(topk_final_kernel<kSrcScores>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, cand_keys,
                        cand_cols, seg_count, nseg, cap);
     return hipGetLastError();
 }

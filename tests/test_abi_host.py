@@ -221,7 +221,29 @@ def test_topk_rescore_workspace_rules():
         csa2.ERR_WORKSPACE
     assert csa2._lib.csa2_topk_rescore(ctypes.byref(a), 512, ptr, ctypes.c_void_p(0x10040), ws, None) == \
         csa2.ERR_INVALID_ARG
-    assert csa2.topk_rescore_workspace_size(4, 4000, 512) == 0
+    # narrow rows: no quantised plan, but the BF16 shared-plane plan (the chosen blocks and their re-computed
+    # scores) sizes the workspace
+    assert csa2.topk_rescore_workspace_size(4, 4000, 512) >= 4 * 512 * 4 + 4 * 4096 * 4
+
+
+def test_topk_rescore_bf16_shared_plane_rules():
+    """BF16 score-free rows must state that they share one plane; then any width and row count is taken."""
+    ptr = ctypes.c_void_p(0x1000)
+    base = dict(q_dtype=csa2.BF16, k_dtype=csa2.BF16, width=70000, scores=None, block_keys=ptr, rows=4096)
+    a = _index_args(**base)
+    assert csa2._lib.csa2_topk_rescore(ctypes.byref(a), 512, ptr, ctypes.c_void_p(0x10000), 1 << 30, None) == \
+        csa2.ERR_UNSUPPORTED
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_UNSUPPORTED
+    a = _index_args(flags=csa2.INDEX_SHARED_PLANE, **base)
+    ws = csa2.topk_rescore_workspace_size(4096, 70000, 512)
+    assert ws >= 4096 * 512 * 4 + 4096 * 4096 * 4
+    assert csa2._lib.csa2_topk_rescore(ctypes.byref(a), 512, ptr, ctypes.c_void_p(0x10000), ws - 1, None) == \
+        csa2.ERR_WORKSPACE
+    assert csa2._lib.csa2_topk_rescore(ctypes.byref(a), 0, ptr, ctypes.c_void_p(0x10000), ws, None) == \
+        csa2.ERR_INVALID_ARG
+    assert csa2.topk_rescore_supported(4096, 65536, 512, fp8=False, fp4=False, shared_plane=True)
+    assert not csa2.topk_rescore_supported(4096, 65536, 512, fp8=False, fp4=False, shared_plane=False)
+    assert not csa2.topk_rescore_supported(4096, 65536, 512, fp8=True)
 
 
 def _pool_args(**kw):

@@ -116,3 +116,52 @@ def test_score_free_with_pool_block_scores():
                        block_max=bm_b)
     torch.cuda.synchronize()
     assert torch.equal(bm_a, bm_b)
+
+
+_PF = CONFIGS["prefill_4096_at_128k"]
+DENSE_CASES = {
+    # rows of one prefill chunk over a shared BF16 plane
+    "bf16_chunk": (_PF.replace(q_tokens=300, context=30000, reuse_layers=0), 512),
+    "bf16_ratio1": (_PF.replace(q_tokens=100, context=20000, ratio=1, reuse_layers=0), 512),
+    "bf16_short_rows": (_PF.replace(q_tokens=200, context=700, reuse_layers=0), 512),   # 250..350 visible rows < k
+    "bf16_k2048": (_PF.replace(q_tokens=64, context=40000, reuse_layers=0), 2048),
+    "bf16_k1": (_PF.replace(q_tokens=33, context=9000, reuse_layers=0), 1),
+    "bf16_few_rows": (_PF.replace(q_tokens=5, context=12000, reuse_layers=0), 512),      # fewer rows than a group
+    "bf16_ties": (_PF.replace(q_tokens=70, context=26000, reuse_layers=0), 512),
+}
+
+
+@pytest.mark.parametrize("name", list(DENSE_CASES))
+def test_score_free_bf16_chunk_matches_written_scores(name):
+    """Prefill rows over one BF16 plane: the chunk kernel's block keys, then the best k blocks re-scored,
+    give exactly topk_select over the written scores (and the oracle's top-k of them)."""
+    import sparse_latent_attention_amd as csa2
+    cfg, k = DENSE_CASES[name]
+    print(f"\n[rescore bf16] {name} rows={cfg.q_tokens} width={cfg.width} k={k}", flush=True)
+    x = make_inputs(cfg, 57, device="cuda")
+    rows = cfg.q_tokens
+    if name.endswith("ties"):
+        kI = x["kI"]
+        kI[::40] = kI[17:18]          # every 40th key row equals row 17: equal scores across blocks
+        kI[5::40] = kI[17:18]
+    assert csa2.topk_rescore_supported(rows, cfg.width, k, fp8=False, fp4=False, shared_plane=True)
+    dev = x["pos"].device
+    bkeys = torch.full((rows, -(-cfg.width // 8)), 12345, dtype=torch.int32, device=dev)
+    kI, ikw = index_plane_args(cfg, x)
+    csa2.indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, index_scale(cfg), None,
+                       width=cfg.width, block_keys=bkeys, shared_plane=True)
+    out = torch.full((rows, k), -7, dtype=torch.int32, device=dev)
+    csa2.topk_rescore(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, index_scale(cfg), out, bkeys,
+                      cfg.width, dense=True, shared_plane=True)
+    scores = gpu_scores(cfg, x)
+    ref_idx = gpu_topk(cfg, x, scores, k=k)
+    torch.cuda.synchronize()
+    s_np = scores.cpu().numpy()
+    valid = np.isfinite(oracle_score_bound(cfg, x, np.arange(rows)))
+    keys = np.where(valid, _order_keys(s_np), 0).astype(np.uint32)
+    pad = (-cfg.width) % 8
+    want_bk = np.pad(keys, ((0, 0), (0, pad))).reshape(rows, -1, 8).max(axis=2)
+    assert np.array_equal(bkeys.cpu().numpy().view(np.uint32), want_bk), "block keys"
+    got = out.cpu().numpy()
+    assert np.array_equal(got, ref_idx.cpu().numpy()), "score-free top-k differs from topk_select of written scores"
+    assert np.array_equal(got, oracle_topk(cfg, x, s_np.astype(np.float64), np.arange(rows), k=k))

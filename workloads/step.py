@@ -69,10 +69,18 @@ class Step:
         tau_i = 1.0 / math.sqrt(cfg.idx_dim * cfg.idx_heads)
         tau = 1.0 / math.sqrt(cfg.dim)
         quantised = cfg.idx_dtype in ("fp8", "fp4")
+        # A prefill chunk's rows share one BF16 plane.  Its score-free route (block keys, the best blocks
+        # re-scored) is exact but measured slower than writing the scores (the chunk kernel is bound by its
+        # matrix work, so the writes cost little, while re-scoring 1/16 of the columns without shared key
+        # tiles costs more than the select saves): it is taken only when asked for (score_free=True).
+        dense = cfg.idx_dtype == "bf16" and cfg.phase == "prefill"
+        if score_free is None and dense:
+            score_free = False
         if score_free is None:
-            score_free = (cfg.index_mode == "full" and quantised and
+            score_free = (cfg.index_mode == "full" and (quantised or dense) and
                           csa2.topk_rescore_supported(rows, cfg.width, cfg.topk, cfg.idx_heads, cfg.idx_dim,
-                                                      fp8=cfg.idx_dtype == "fp8", fp4=cfg.idx_dtype == "fp4"))
+                                                      fp8=cfg.idx_dtype == "fp8", fp4=cfg.idx_dtype == "fp4",
+                                                      shared_plane=dense))
         self.score_free = score_free
         self.idx = torch.empty(rows, cfg.topk, dtype=torch.int32, device=dev)
         self.outs = [torch.empty_like(L["q"]) for L in x["layers"]]
@@ -91,9 +99,11 @@ class Step:
             # the pool's block scores come from the block keys: no block_max pass
             self.block_max = None
             call_idx = csa2.prepare_indexer_score(*idx_common, None, width=cfg.width, block_keys=self.block_keys,
-                                                  **ikw)
+                                                  shared_plane=dense, **ikw)
             rkw = dict(ikw)
             rkw.pop("fp8", None)
+            if dense:
+                rkw.update(dense=True, shared_plane=True)
             call_topk = csa2.prepare_topk_rescore(*idx_common, self.idx, self.block_keys, cfg.width, **rkw)
         else:
             self.scores = torch.empty(rows, cfg.width, dtype=torch.float32, device=dev)
