@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 7
+#define CSA2_ABI_VERSION 8
 
 /* Status codes. */
 #define CSA2_OK 0
@@ -381,10 +381,15 @@ int32_t csa2_candidate_pool(const csa2_pool_args* args, void* workspace, size_t 
  * kv_scale and swa_scale NULL).  rope_inv_freq holds rope_dim/2 float64 frequencies in device
  * memory (see csa2_rope_inv_freq).
  *
- * Decode with few rows gives each (row, 16-head group) its own workgroup and
- * merges the partial softmax states of its waves on chip; no workspace is
- * needed (csa2_attn_workspace_size returns 0; the workspace arguments of
- * csa2_sparse_attn_decode are accepted and ignored).
+ * Decode with few rows gives each (row, 16-head group) its own workgroups: the
+ * row's entries are split over `splits` workgroups, whose waves merge their
+ * partial softmax states (running max, sum, weighted values) on chip; with
+ * more than one split each workgroup writes its state to the workspace and a
+ * second kernel merges the splits' states, normalises, rotates and stores.
+ * splits = 0 lets the library choose (enough workgroups to fill the GPU);
+ * 1..8 asks for that many.  csa2_attn_workspace_size returns the bytes for the
+ * same arguments (0 when no split is made, and for prefill); decode returns
+ * CSA2_ERR_WORKSPACE when the workspace is smaller.
  */
 typedef struct csa2_attn_args {
     uint32_t struct_size;       /* sizeof(csa2_attn_args) */
@@ -399,7 +404,8 @@ typedef struct csa2_attn_args {
     int32_t kv_dtype;
     int32_t swa_dtype;
     int32_t out_dtype;
-    int32_t splits;             /* reserved, must be 0 */
+    int32_t splits;             /* decode: workgroups per (row, head group) splitting the entries,
+                                 * 0 = the library's choice, at most 8; prefill: ignored, 0..8 */
     int32_t _pad0;
     int64_t swa_rows;           /* prefill: rows of the linear SWA array */
     int64_t swa_pos0;           /* prefill: position of linear SWA row 0 */
@@ -418,7 +424,7 @@ typedef struct csa2_attn_args {
     void* out;                  /* out: [rows, heads, dim] */
 } csa2_attn_args;
 
-/* Bytes of workspace csa2_sparse_attn_decode needs (currently always 0). */
+/* Bytes of workspace csa2_sparse_attn_decode needs for these sizes and splits (see above). */
 size_t csa2_attn_workspace_size(int32_t rows, int32_t heads, int32_t dim, int32_t window, int32_t topk,
                                 int32_t splits);
 

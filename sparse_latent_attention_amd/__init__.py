@@ -494,19 +494,28 @@ def _swa_row_len(dim, swa_fp8mx):
 
 def sparse_attn_decode(q, pos, idx, kv, kv_row_base, swa, sink, inv_freq, ratio, window, softmax_scale, out, *,
                        rope_dim=64, kv_scale=None, swa_scale=None, kv_fp4=False, swa_fp8=False, kv_nvfp4=False,
-                       swa_fp8mx=False, stream=None):
+                       swa_fp8mx=False, splits=0, workspace=None, stream=None):
     """Decode attention: ``swa`` is one ring [rows, window, D] per query row.
 
     ``kv_nvfp4`` with ``swa_fp8mx`` selects rows with inline scales: kv
     [*, D/2 + D/16] bytes (E2M1, then one E4M3 per 16) and swa
-    [rows, window, D + D/32] bytes (FP8-E4M3, then one E8M0 per 32)."""
+    [rows, window, D + D/32] bytes (FP8-E4M3, then one E8M0 per 32).
+    ``splits`` (0 = the library's choice) splits few rows' entries over workgroups; the
+    workspace for their partial states is allocated here unless given."""
+    _dev(workspace)
     a = _attn_args(q, pos, idx, kv, kv_scale, kv_row_base, swa, swa_scale, sink, inv_freq, ratio, window,
                    softmax_scale, out, rope_dim, kv_fp4, swa_fp8, kv_nvfp4, swa_fp8mx)
     if tuple(swa.shape) != (a.rows, a.window, _swa_row_len(a.dim, swa_fp8mx)):
         raise ValueError("csa2.sparse_attn_decode: swa must be [rows, window, dim]")
     if swa_fp8 and tuple(swa_scale.shape) != (a.rows, a.window):
         raise ValueError("csa2.sparse_attn_decode: swa_scale must be [rows, window]")
-    _check("csa2_sparse_attn_decode", _lib.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, _stream(stream)))
+    a.splits = int(splits)
+    need = attn_workspace_size(a.rows, a.heads, a.dim, a.window, a.topk, a.splits)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = _scratch(need, q.device, stream)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("csa2_sparse_attn_decode", _lib.csa2_sparse_attn_decode(ctypes.byref(a), _ptr(workspace), ws_bytes,
+                                                                   _stream(stream)))
     return out
 
 
@@ -635,7 +644,13 @@ def prepare_topk_select(*args, stream=None, **kw):
 
 
 def prepare_sparse_attn_decode(*args, stream=None, **kw):
-    return _prepare("csa2_sparse_attn_decode", lambda: sparse_attn_decode(*args, stream=stream, **kw), stream)
+    if kw.get("workspace") is None:
+        q, idx, swa = args[0], args[2], args[5]
+        need = attn_workspace_size(q.shape[0], q.shape[1], q.shape[2], args[9], idx.shape[1], kw.get("splits", 0))
+        kw["workspace"] = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    p = _prepare("csa2_sparse_attn_decode", lambda: sparse_attn_decode(*args, stream=stream, **kw), stream)
+    p.workspace = kw["workspace"]
+    return p
 
 
 def prepare_sparse_attn_prefill(*args, stream=None, **kw):

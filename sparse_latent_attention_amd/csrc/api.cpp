@@ -410,7 +410,7 @@ int32_t csa2_candidate_pool(const csa2_pool_args* a, void* workspace, size_t wor
 static int32_t validate_attn(const csa2_attn_args* a, bool decode) {
     if (a == nullptr || a->struct_size < sizeof(csa2_attn_args)) return CSA2_ERR_INVALID_ARG;
     if (a->rows < 0 || a->topk < 0 || a->topk > 2048 || a->window < 16 || a->window > 1024 || (a->window % 16) != 0 ||
-        (a->topk % 16) != 0 || a->splits != 0)
+        (a->topk % 16) != 0 || a->splits < 0 || a->splits > 8)
         return CSA2_ERR_INVALID_ARG;
     if (a->ratio != 1 && a->ratio != 2) return CSA2_ERR_INVALID_ARG;
     if (!(a->softmax_scale > 0.f) || !isfinite(a->softmax_scale)) return CSA2_ERR_INVALID_ARG;
@@ -436,21 +436,27 @@ static csa2::AttnParams attn_params(const csa2_attn_args* a) {
     p.swa_rows = a->swa_rows; p.swa_pos0 = a->swa_pos0; p.rows = a->rows;
     p.topk = a->topk; p.ratio = a->ratio; p.window = a->window;
     p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+    p.splits = 1;
+    p.part = nullptr;
     return p;
 }
 
 size_t csa2_attn_workspace_size(int32_t rows, int32_t heads, int32_t dim, int32_t window, int32_t topk,
                                 int32_t splits) {
-    (void)rows; (void)heads; (void)dim; (void)window; (void)topk; (void)splits;
-    return 0;  // partial softmax states are merged on chip
+    if (rows <= 0 || heads <= 0 || dim <= 0 || window < 0 || topk < 0 || splits < 0 || splits > 8) return 0;
+    return csa2::attn_decode_workspace(rows, heads, dim, csa2::attn_decode_splits(rows, heads, dim, window, topk, splits));
 }
 
 int32_t csa2_sparse_attn_decode(const csa2_attn_args* a, void* workspace, size_t workspace_bytes,
                                 csa2_stream_t stream) {
-    (void)workspace; (void)workspace_bytes;
     int32_t st = validate_attn(a, true);
     if (st != CSA2_OK || a->rows == 0) return st;
     csa2::AttnParams p = attn_params(a);
+    p.splits = csa2::attn_decode_splits(a->rows, a->heads, a->dim, a->window, a->topk, a->splits);
+    const size_t need = csa2::attn_decode_workspace(a->rows, a->heads, a->dim, p.splits);
+    if (workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 256))) return CSA2_ERR_INVALID_ARG;
+    p.part = static_cast<float*>(workspace);
     csa2::AttnShape s{a->heads, a->dim, a->rope_dim, a->q_dtype, a->kv_dtype, a->swa_dtype, a->out_dtype};
     return hip_status(csa2::launch_sparse_attn(p, s, true, reinterpret_cast<hipStream_t>(stream)));
 }

@@ -323,6 +323,7 @@ __device__ __forceinline__ void raw_convert(const RawPair& raw, int i, Pack8<CT>
 }
 
 constexpr int kMaxTiles = 192;  // (window + topk) / 16 at most (window <= 1024, topk <= 2048)
+constexpr int kMaxSplits = 8;   // decode workgroups per (row, head group) at most
 constexpr int kMaxTopk = 2048;
 
 // Per-row geometry the gather needs.
@@ -850,10 +851,12 @@ __global__ __launch_bounds__(256 * DS) void attn_decode_kernel(const AttnParams 
     const int grp = wave / DS, dh = wave % DS;
     const int gl = 64 * dh + lane;  // lane within the tile group
 
-    // Workgroups of one row share an XCD: ids are dispatched round-robin over 8 XCDs.
+    // Workgroups of one row share an XCD: ids are dispatched round-robin over 8 XCDs.  With
+    // splits > 1 the row's entries are also split over workgroups (virtual tile group 4 * split + grp).
+    const int S = p.splits;
     const int id = blockIdx.x;
-    const int blk = id / (8 * NHG), o = id % (8 * NHG);
-    const int hg = o / 8;
+    const int blk = id / (8 * NHG * S), o = id % (8 * NHG * S);
+    const int hg = (o / 8) % NHG, split = (o / 8) / NHG;
     RowCtx c;
     c.r = 8 * blk + (o % 8);
     if (c.r >= p.rows) return;  // padding workgroup (before any barrier)
@@ -871,9 +874,9 @@ __global__ __launch_bounds__(256 * DS) void attn_decode_kernel(const AttnParams 
     for (int s = 0; s < NQ; ++s)
         qf[s] = (h < H) ? load_q_frag<QT, CT, D>(p.q, ((int64_t)c.r * H + h) * D, (SPLIT ? dh * NQ : 0) + s, g)
                         : zero_frag8<CT>();
-    // Group 0 carries the sink (max = sink, sum = 1); the others start empty.
+    // Group 0 of split 0 carries the sink (max = sink, sum = 1); the others start empty.
     float m = kNegInf, l = 0.f;
-    if (grp == 0 && h < H) {
+    if (grp == 0 && split == 0 && h < H) {
         m = p.sink[h] * kLog2e;
         l = (g == 0) ? 1.f : 0.f;
     }
@@ -916,10 +919,11 @@ __global__ __launch_bounds__(256 * DS) void attn_decode_kernel(const AttnParams 
     if (tid < p.topk) sel[tid] = idx0;
     for (int i = tid + 256 * DS; i < p.topk; i += 256 * DS) sel[i] = p.idx[(int64_t)c.r * p.topk + i];
     __syncthreads();  // sel and rope_cs complete
-    const int rounds = (n_tiles + 3) / 4;
-    int t = grp;
+    const int tstep = 4 * S;  // tiles t = 4 split + grp, then every 4 S-th
+    const int rounds = (n_tiles + tstep - 1) / tstep;
+    int t = 4 * split + grp;
     if (t < n_tiles) load_tile(t);
-    for (int rd = 0; rd < rounds; ++rd, t += 4) {
+    for (int rd = 0; rd < rounds; ++rd, t += tstep) {
         const bool mine = t < n_tiles;  // the same for every wave of the group
         if (mine) {
 #pragma unroll
@@ -931,7 +935,7 @@ __global__ __launch_bounds__(256 * DS) void attn_decode_kernel(const AttnParams 
             }
         }
         __syncthreads();  // every group's tile is in LDS
-        if (t + 4 < n_tiles) load_tile(t + 4);  // next round's bytes in flight during this round
+        if (t + tstep < n_tiles) load_tile(t + tstep);  // next round's bytes in flight during this round
         if constexpr (SPLIT) {
             f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
             if (mine) st = tile_scores<D, CT, G::KS, NQ>(Kt, qf, g, li, 256 * dh);
@@ -972,13 +976,79 @@ __global__ __launch_bounds__(256 * DS) void attn_decode_kernel(const AttnParams 
     const float inv = L > 0.f ? 1.f / L : 0.f;
     const float* base = reinterpret_cast<const float*>(smem);
     const int64_t obase = ((int64_t)c.r * H + h) * D;
+    // split > 1: this workgroup's state (max mx in log2 units, -inf when it saw nothing; sum L and the
+    // weighted values, both relative to mu) goes to the workspace for attn_merge_kernel
+    float* part = S > 1 ? p.part + (((int64_t)c.r * NHG + hg) * S + split) * (16 * (2 + D)) : nullptr;
+    if (S > 1 && wave == 0 && g == 0) {
+        part[li] = mx;
+        part[16 + li] = L;
+    }
     for (int dt = wave; dt < D / 16; dt += 4 * DS) {
         const int off = li * ACC_STRIDE + 16 * dt + 4 * g;
         f32x4 sum = *reinterpret_cast<const f32x4*>(base + off);
 #pragma unroll
         for (int w = 1; w < 4; ++w) sum += *reinterpret_cast<const f32x4*>(base + w * 16 * ACC_STRIDE + off);
         const int d0 = 16 * dt + 4 * g;
-        emit4<D, R, OT>(p.out, obase + d0, d0, sum, inv, rope_cs);
+        if (S > 1) *reinterpret_cast<f32x4*>(part + 32 + li * D + d0) = sum;
+        else emit4<D, R, OT>(p.out, obase + d0, d0, sum, inv, rope_cs);
+    }
+}
+
+// Merge of the splits' partial states of one (row, 16-head group): the same combination as the
+// in-workgroup merge of the tile groups (max, weighted sums), then normalisation, the inverse
+// rotation of the rope tail and the store.
+// One workgroup per (row, head group, quarter of the D columns): 64 threads per head... every thread
+// owns 4 consecutive columns of one head; the splits' states are read once each, all loads issued
+// before any is used.
+template <int H, int D, int R, int OT>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const AttnParams p) {
+    constexpr int NHG = (H + 15) / 16;
+    constexpr int DQ = D / 4;             // columns per workgroup
+    constexpr int TPH = DQ / 4;           // threads per head (4 columns each)
+    constexpr int HPW = 256 / TPH;        // heads per pass
+    constexpr int PART = 16 * (2 + D);
+    static_assert(R <= DQ && TPH <= 256 && 256 % TPH == 0, "the rope tail lies in the last quarter");
+    __shared__ float rope_cs[R];
+    const int S = p.splits;
+    const int q4 = blockIdx.x % 4, rh = blockIdx.x / 4;
+    const int r = rh / NHG, hg = rh % NHG;
+    const int tid = threadIdx.x;
+    if (q4 == 3 && tid < R / 2) {  // the rope tail lies in the last quarter (R <= D / 4)
+        float cs, sn;
+        rope_angle(p.pos[r], p.inv_freq[tid], cs, sn);
+        rope_cs[2 * tid] = cs;
+        rope_cs[2 * tid + 1] = sn;
+    }
+    __syncthreads();
+    const float* part = p.part + (int64_t)rh * S * PART;
+    for (int hh = tid / TPH; hh < 16; hh += HPW) {
+        const int h = 16 * hg + hh;
+        const int d0 = q4 * DQ + 4 * (tid % TPH);
+        float ms[kMaxSplits], ls[kMaxSplits];
+        f32x4 vs[kMaxSplits];
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s) {
+            if (s < S) {
+                ms[s] = part[s * PART + hh];
+                ls[s] = part[s * PART + 16 + hh];
+                vs[s] = *reinterpret_cast<const f32x4*>(part + s * PART + 32 + hh * D + d0);
+            }
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s)
+            if (s < S) mx = fmaxf(mx, ms[s]);
+        float L = 0.f;
+        f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s) {
+            if (s < S) {
+                const float w = ms[s] == kNegInf ? 0.f : exp2f(ms[s] - mx);
+                L += ls[s] * w;
+                sum += vs[s] * w;
+            }
+        }
+        if (h < H) emit4<D, R, OT>(p.out, ((int64_t)r * H + h) * D + d0, d0, sum, L > 0.f ? 1.f / L : 0.f, rope_cs);
     }
 }
 
@@ -990,9 +1060,12 @@ static hipError_t launch_attn(const AttnParams& p, bool decode, hipStream_t stre
     // the 64-head shapes split each head group's output columns over two waves
     constexpr int DS = (H == 64 && D == 512) ? 2 : 1;
     if (decode && p.rows * NHG < 1024) {
-        const int blocks = ((p.rows + 7) / 8) * 8 * NHG;
+        const int blocks = ((p.rows + 7) / 8) * 8 * NHG * p.splits;
         hipLaunchKernelGGL((attn_decode_kernel<H, D, R, CT, QT, KVT, SWT, OT, DS>), dim3((unsigned)blocks),
                            dim3(256 * DS), 0, stream, p);
+        if (p.splits > 1)
+            hipLaunchKernelGGL((attn_merge_kernel<H, D, R, OT>), dim3((unsigned)(p.rows * NHG * 4)), dim3(256), 0,
+                               stream, p);
         return hipGetLastError();
     }
     if (decode)
@@ -1002,6 +1075,26 @@ static hipError_t launch_attn(const AttnParams& p, bool decode, hipStream_t stre
         hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, false, DS>), dim3((unsigned)p.rows),
                            dim3(NT * DS), 0, stream, p);
     return hipGetLastError();
+}
+
+// Splits of a decode row's entries: enough workgroups (one per CU: 158 KB of LDS each) to fill the
+// 256 CUs, each split group keeping at least two tiles; the caller may ask for a count (1..8).
+int attn_decode_splits(int rows, int heads, int dim, int window, int topk, int requested) {
+    const int nhg = (heads + 15) / 16;
+    if (rows <= 0 || rows * nhg >= 1024) return 1;  // many rows: one workgroup per row instead
+    if (requested > 0) return requested < kMaxSplits ? requested : kMaxSplits;
+    (void)dim;
+    const int n_tiles = (window + topk) / 16;
+    int s = 256 / (rows * nhg);
+    const int by_tiles = n_tiles / 8;  // 4 tile groups per workgroup, >= 2 tiles each
+    if (s > by_tiles) s = by_tiles;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s < 1 ? 1 : s;
+}
+
+size_t attn_decode_workspace(int rows, int heads, int dim, int splits) {
+    if (splits <= 1 || rows <= 0) return 0;
+    return (size_t)rows * ((heads + 15) / 16) * splits * 16 * (2 + dim) * sizeof(float);
 }
 
 bool attn_supported(const AttnShape& s) {

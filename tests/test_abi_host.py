@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(csa2.EXPORTED)
-    assert csa2.ABI_VERSION == 7
+    assert csa2.ABI_VERSION == 8
 
 
 def test_struct_layouts_match_c_compiler():
@@ -370,9 +370,25 @@ def test_attention_inline_scale_rows():
     assert run(kv_dtype=csa2.FP4_E2M1, kv_scale=ptr, swa_dtype=csa2.FP8_E4M3_E8M0G32) == csa2.ERR_UNSUPPORTED
 
 
-def test_decode_needs_no_workspace_and_rejects_reserved_field():
-    assert csa2.attn_workspace_size(8, 64, 512, 128, 512, 0) == 0
-    a = _attn_args(rows=8, splits=4)
+def test_decode_split_workspace_rules():
+    """Few decode rows split their entries over workgroups and need a workspace for the partial states;
+    many rows (one workgroup per row) and single splits need none; the split count is bounded."""
+    per = 4 * 16 * (2 + 512) * 4                                   # 4 head groups x 16 heads x (max, sum, 512 values)
+    assert csa2.attn_workspace_size(32, 64, 512, 128, 512, 0) == 32 * 2 * per    # 128 workgroups -> 2 splits
+    assert csa2.attn_workspace_size(32, 64, 512, 128, 512, 1) == 0
+    assert csa2.attn_workspace_size(32, 64, 512, 128, 512, 3) == 32 * 3 * per
+    assert csa2.attn_workspace_size(64, 64, 512, 128, 512, 0) == 0             # 256 workgroups already
+    assert csa2.attn_workspace_size(300, 64, 512, 128, 512, 0) == 0            # rows kernel
+    assert csa2.attn_workspace_size(1, 64, 512, 16, 16, 0) == 0                # too few tiles to split
+    assert csa2.attn_workspace_size(1, 64, 512, 128, 512, 0) == 1 * 5 * per    # 40 tiles: at most 5 splits
+    a = _attn_args(rows=32, splits=0)
+    need = csa2.attn_workspace_size(32, 64, 512, 128, 512, 0)
+    assert csa2._lib.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, None) == csa2.ERR_WORKSPACE
+    assert csa2._lib.csa2_sparse_attn_decode(ctypes.byref(a), ctypes.c_void_p(0x10000), need - 1, None) == \
+        csa2.ERR_WORKSPACE
+    assert csa2._lib.csa2_sparse_attn_decode(ctypes.byref(a), ctypes.c_void_p(0x10040), need, None) == \
+        csa2.ERR_INVALID_ARG                                        # not 256-byte aligned
+    a = _attn_args(rows=8, splits=9)
     assert csa2._lib.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, None) == csa2.ERR_INVALID_ARG
 
 

@@ -152,6 +152,30 @@ def test_attention_window_only(base, rows, window):
     assert_close(out[torch.from_numpy(sample).cuda()], ref, BF16_ATOL, BF16_RTOL, f"{base} W={window} k=0")
 
 
+@pytest.mark.parametrize("splits", [1, 2, 3, 8])
+@pytest.mark.parametrize("base", ["lowp_small", "full_decode_small", "pages_fp4_small"])
+def test_decode_split_entries(base, splits):
+    """The decode kernel with each row's entries split over 1, 2, 3 or 8 workgroups (partial softmax
+    states merged by a second kernel) against the oracle; empty splits (fewer tiles than split groups)
+    included: 8 splits x 4 groups > the 40 tiles of a 128 + 512 row."""
+    import sparse_latent_attention_amd as csa2
+    from workloads.step import attn_storage_args
+    cfg = SMALL[base]
+    x = make_inputs(cfg, 12, device="cuda")
+    idx = gpu_topk(cfg, x, gpu_scores(cfg, x))
+    L = x["layers"][0]
+    out = torch.empty_like(L["q"])
+    kv, kw = attn_storage_args(cfg, x)
+    csa2.sparse_attn_decode(L["q"], x["pos"], idx, kv, x["kv_row_base"], x["swa"], L["sink"],
+                            csa2.rope_inv_freq(cfg.rope_dim, cfg.rope_theta, cfg.yarn_factor, cfg.yarn_orig).cuda(),
+                            cfg.ratio, cfg.window, 1.0 / math.sqrt(cfg.dim), out, swa_scale=x["swa_scale"],
+                            splits=splits, **kw)
+    torch.cuda.synchronize()
+    ref = oracle_attention(cfg, x, idx.cpu().numpy(), np.arange(cfg.q_tokens))
+    e = assert_close(out, ref, BF16_ATOL, BF16_RTOL, f"{base} splits={splits}")
+    print(f"[splits] {base} {splits}: max_abs {e:.3e}")
+
+
 def test_injected_indices_and_masks():
     # -1 padding, duplicates, rows the group-causal mask hides, far out-of-range rows
     cfg = SMALL["lowp_small"]
