@@ -381,13 +381,14 @@ int32_t csa2_candidate_pool(const csa2_pool_args* args, void* workspace, size_t 
  * kv_scale and swa_scale NULL).  rope_inv_freq holds rope_dim/2 float64 frequencies in device
  * memory (see csa2_rope_inv_freq).
  *
- * Decode with few rows gives each (row, 16-head group) its own workgroups: the
- * row's entries are split over `splits` workgroups, whose waves merge their
- * partial softmax states (running max, sum, weighted values) on chip; with
- * more than one split each workgroup writes its state to the workspace and a
+ * Decode splits each row's entries over `splits` workgroups (a decode batch
+ * has few rows, and one workgroup per row would leave most of the GPU idle):
+ * with more than one split each workgroup writes its partial softmax state
+ * (running max, sum, unnormalised values, per head) to the workspace and a
  * second kernel merges the splits' states, normalises, rotates and stores.
- * splits = 0 lets the library choose (enough workgroups to fill the GPU);
- * 1..8 asks for that many.  csa2_attn_workspace_size returns the bytes for the
+ * splits = 0 lets the library choose (256 / rows, at most 8, at most 4 from
+ * 32 rows on, at most one per pair of 16-entry tiles); 1..8 asks for that
+ * many.  csa2_attn_workspace_size returns the bytes for the
  * same arguments (0 when no split is made, and for prefill); decode returns
  * CSA2_ERR_WORKSPACE when the workspace is smaller.
  */
@@ -404,7 +405,7 @@ typedef struct csa2_attn_args {
     int32_t kv_dtype;
     int32_t swa_dtype;
     int32_t out_dtype;
-    int32_t splits;             /* decode: workgroups per (row, head group) splitting the entries,
+    int32_t splits;             /* decode: workgroups per row splitting its entries,
                                  * 0 = the library's choice, at most 8; prefill: ignored, 0..8 */
     int32_t _pad0;
     int64_t swa_rows;           /* prefill: rows of the linear SWA array */

@@ -29,16 +29,14 @@
 // the 512 output columns, which halves the accumulator registers so that two
 // waves fit on each SIMD.
 //
-// Two kernels share that machinery:
-//   * attn_rows_kernel (prefill, and decode with many rows): one workgroup per
-//     query row, all waves on the same tiles, two tiles per round (each half
-//     of the threads gathers one) in two buffer sets, one barrier per round.
-//   * attn_decode_kernel (decode with few rows): one workgroup per (row,
-//     16-head group) so small batches still fill the chip; 4 groups of waves
-//     take interleaved tiles into private LDS buffers and merge their softmax
-//     states through LDS at the end -- no partial results leave the chip.
-//     The workgroups of one row sit on the same XCD, so the 4x re-gather of
-//     that row's entries is served by one L2.
+// attn_rows_kernel runs both phases: one workgroup per query row (all 64
+// heads: each tile is gathered and decoded once for all of them), all waves on
+// the same tiles, two tiles per round (each half of the threads gathers one) in
+// two buffer sets, one barrier per round.  A decode batch has few rows, so
+// there each row's tiles are also split over S workgroups (one per CU for the
+// LDS, S = 256 / rows up to 8); each leaves its softmax state (max, sum,
+// unnormalised values) in a workspace and attn_merge_kernel combines the S
+// states, normalises and stores.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -655,7 +653,8 @@ __device__ __forceinline__ void emit4(void* out, int64_t off, int d0, f32x4 a, f
 // SIMD and one wave's LDS reads and waits overlap the other's matrix work.
 template <int H, int D, int R, class CT, int QT, int KVT, int SWT, int OT, bool DECODE, int DS>
 __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(const AttnParams p) {
-    constexpr int NW = (H + 15) / 16 * DS;
+    constexpr int NHG = (H + 15) / 16;
+    constexpr int NW = NHG * DS;
     constexpr int NT = 64 * NW;
     typedef TileGeom<CT, D> G;
     constexpr int NS = D / 32, NDT = D / 16 / DS;
@@ -680,13 +679,20 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
     const int ts = tid / TT, tl = tid % TT;  // this thread's tile of a round, and its index there
+    // Decode may split a row's tiles over S workgroups (split = blockIdx.x % S): each takes an
+    // even-length run of tiles and leaves its softmax state for attn_merge_kernel.
+    const int S = DECODE ? p.splits : 1;
+    const int split = DECODE ? (int)(blockIdx.x % S) : 0;
     RowCtx c;
-    c.r = blockIdx.x;
+    c.r = DECODE ? (int)(blockIdx.x / S) : (int)blockIdx.x;
     c.pos = p.pos[c.r];
     c.nv = (c.pos + 1) / p.ratio;
     c.kv_base = p.kv_row_base[c.r];
     c.dummy = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)c.r * H * D * (QT == CSA2_F32 ? 4 : 2);
-    const int n_tiles = (p.window + p.topk) / 16;
+    const int n_all = (p.window + p.topk) / 16;
+    const int per = S > 1 ? ((n_all + S - 1) / S + 1) & ~1 : n_all;
+    const int tb = split * per;  // first tile of this workgroup
+    const int n_tiles = tb < n_all ? (n_all - tb < per ? n_all - tb : per) : 0;  // its tiles: tb ..
 
     // The first selected index of each thread is loaded before the float64 rope angles are
     // computed, so that latency and the angles overlap.
@@ -697,7 +703,7 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
         rope_cs[2 * tid] = cs;
         rope_cs[2 * tid + 1] = sn;
     }
-    for (int i = tid; i < n_tiles; i += NT) vmask[i] = 0u;
+    for (int i = tid; i < n_tiles; i += NT) vmask[tb + i] = 0u;
     if (tid < p.topk) sel[tid] = idx0;
     for (int i = tid + NT; i < p.topk; i += NT) sel[i] = p.idx[(int64_t)c.r * p.topk + i];
 
@@ -712,7 +718,7 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
         qf[s] = (H % 16 == 0 || h < H) ? load_q_frag<QT, CT, D>(p.q, ((int64_t)c.r * H + h) * D, s0 + s, g)
                                        : zero_frag8<CT>();
     float m = kNegInf, l = 0.f;
-    if (H % 16 == 0 || h < H) {
+    if ((H % 16 == 0 || h < H) && split == 0) {
         m = p.sink[h] * kLog2e;  // the sink is the initial state: max = sink, sum = 1
         l = (g == 0) ? 1.f : 0.f;
     }
@@ -769,19 +775,19 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     __syncthreads();  // rope table and vmask reset visible
     const int n_rounds = (n_tiles + TPR - 1) / TPR;
     if (ts < n_tiles) {
-        load_tile(ts);
-        store_tile(ts, ts);
+        load_tile(tb + ts);
+        store_tile(tb + ts, ts);
     } else if (PAIRED && ts == n_tiles) {
         zero_tile(ts);
     }
-    if (TPR + ts < n_tiles) load_tile(TPR + ts);
+    if (TPR + ts < n_tiles) load_tile(tb + TPR + ts);
     __syncthreads();
     for (int rd = 0; rd < n_rounds; ++rd) {
         const int bs = (rd & 1) * TPR;
         if constexpr (PAIRED) {
             // (an odd last tile is paired with the zero-filled buffer, under an empty mask)
             const int t = 2 * rd;
-            tile_pair_compute<NDT>(kbuf(bs), kbuf(bs + 1), vbuf(bs), vmask[t], t + 1 < n_tiles ? vmask[t + 1] : 0u,
+            tile_pair_compute<NDT>(kbuf(bs), kbuf(bs + 1), vbuf(bs), vmask[tb + t], t + 1 < n_tiles ? vmask[tb + t + 1] : 0u,
                                    qf, wave % 2, xch + 128 * wave, xch + 128 * (wave ^ 1), p.scale_log2, g, li,
                                    lane, m, l, acc, dt0);
         } else {
@@ -789,15 +795,15 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
             for (int jt = 0; jt < TPR; ++jt) {
                 const int t = rd * TPR + jt;
                 if (t < n_tiles)
-                    tile_compute<D, CT, G::KS, G::VS, NDT>(kbuf(bs + jt), vbuf(bs + jt), vmask[t], qf, p.scale_log2,
+                    tile_compute<D, CT, G::KS, G::VS, NDT>(kbuf(bs + jt), vbuf(bs + jt), vmask[tb + t], qf, p.scale_log2,
                                                            g, li, m, l, acc, dt0);
             }
         }
         // the next round's tiles go into the other buffer set; its loads were issued a round ago
         const int tn = (rd + 1) * TPR + ts;
         if (tn < n_tiles) {
-            store_tile(tn, (bs ^ TPR) + ts);
-            if (tn + TPR < n_tiles) load_tile(tn + TPR);
+            store_tile(tb + tn, (bs ^ TPR) + ts);
+            if (tn + TPR < n_tiles) load_tile(tb + tn + TPR);
         } else if (PAIRED && tn == n_tiles && (n_tiles & 1)) {
             zero_tile((bs ^ TPR) + ts);
         }
@@ -807,6 +813,17 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
     if (h >= H) return;
+    if (S > 1) {  // this split's state (max in log2 units, sum and values relative to it) for the merge
+        float* part = p.part + (((int64_t)c.r * NHG + wave / DS) * S + split) * (16 * (2 + D));
+        if (wave % DS == 0 && g == 0) {
+            part[li] = m;
+            part[16 + li] = l;
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            *reinterpret_cast<f32x4*>(part + 32 + li * D + 16 * (dt0 + dt) + 4 * g) = acc[dt];
+        return;
+    }
     const float inv = 1.f / l;
     const int64_t obase = ((int64_t)c.r * H + h) * D;
 #pragma unroll
@@ -816,187 +833,9 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     }
 }
 
-// ---------------------------------------------------------------------------
-// One workgroup per (query row, 16-head group).  Its waves form 4 groups of DS
-// waves; group w takes tiles w, w + 4, ... into its own LDS tile buffer.  The
-// DS waves of a group split each tile's gather and decode, compute the group's
-// scores and softmax state (identical in each) and accumulate 1/DS of the
-// output columns each: DS = 2 halves the per-wave decode work and the
-// accumulator, so two waves fit on each SIMD.  The groups' softmax states
-// merge through LDS at the end -- no partial results leave the chip.
-template <int H, int D, int R, class CT, int QT, int KVT, int SWT, int OT, int DS>
-__global__ __launch_bounds__(256 * DS) void attn_decode_kernel(const AttnParams p) {
-    constexpr int NHG = (H + 15) / 16;  // head groups per row
-    typedef TileGeom<CT, D> G;
-    constexpr int NS = D / 32, NDT = D / 16 / DS;  // NDT: 16-column output blocks per wave
-    constexpr int PAIRS = 4 * (D / 8);
-    constexpr int GL = 64 * DS;                     // lanes of a tile group
-    constexpr int PPL = (PAIRS + GL - 1) / GL;      // pairs per lane
-    constexpr int ACC_STRIDE = D + 4;               // merge slice row stride (floats)
-    constexpr int TILE_BYTES = G::BYTES;
-    constexpr int MERGE_BYTES = 4 * 16 * ACC_STRIDE * 4;
-    constexpr int SMEM = (4 * TILE_BYTES > MERGE_BYTES) ? 4 * TILE_BYTES : MERGE_BYTES;
-
-    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-    __shared__ float rope_cs[R];
-    __shared__ float ml[4][2][16];
-    __shared__ __attribute__((aligned(16))) int32_t sel[kMaxTopk];  // this row's selected indices
-    // BF16 512-wide with wave pairs: the two waves of a group each reduce the scores over half of
-    // the 512 dimensions and exchange the halves here (a + b == b + a: identical scores in both).
-    constexpr bool SPLIT = DS == 2 && D == 512 && sizeof(CT) == 2;
-    __shared__ f32x4 xch[SPLIT ? 64 * 4 * DS : 1];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, li = lane & 15;
-    const int grp = wave / DS, dh = wave % DS;
-    const int gl = 64 * dh + lane;  // lane within the tile group
-
-    // Workgroups of one row share an XCD: ids are dispatched round-robin over 8 XCDs.  With
-    // splits > 1 the row's entries are also split over workgroups (virtual tile group 4 * split + grp).
-    const int S = p.splits;
-    const int id = blockIdx.x;
-    const int blk = id / (8 * NHG * S), o = id % (8 * NHG * S);
-    const int hg = (o / 8) % NHG, split = (o / 8) / NHG;
-    RowCtx c;
-    c.r = 8 * blk + (o % 8);
-    if (c.r >= p.rows) return;  // padding workgroup (before any barrier)
-    c.pos = p.pos[c.r];
-    c.nv = (c.pos + 1) / p.ratio;
-    c.kv_base = p.kv_row_base[c.r];
-    c.dummy = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)c.r * H * D * (QT == CSA2_F32 ? 4 : 2);
-    const int n_tiles = (p.window + p.topk) / 16;
-
-    const int h = 16 * hg + li;
-    const int dt0 = dh * NDT;
-    constexpr int NQ = SPLIT ? NS / 2 : NS;
-    typename Mma<CT>::Frag8 qf[NQ];
-#pragma unroll
-    for (int s = 0; s < NQ; ++s)
-        qf[s] = (h < H) ? load_q_frag<QT, CT, D>(p.q, ((int64_t)c.r * H + h) * D, (SPLIT ? dh * NQ : 0) + s, g)
-                        : zero_frag8<CT>();
-    // Group 0 of split 0 carries the sink (max = sink, sum = 1); the others start empty.
-    float m = kNegInf, l = 0.f;
-    if (grp == 0 && split == 0 && h < H) {
-        m = p.sink[h] * kLog2e;
-        l = (g == 0) ? 1.f : 0.f;
-    }
-    // The float64 rope angles are computed while the query, sink and first index loads are in flight.
-    const int32_t idx0 = tid < p.topk ? p.idx[(int64_t)c.r * p.topk + tid] : 0;
-    if (tid < R / 2) {
-        float cs, sn;
-        rope_angle(c.pos, p.inv_freq[tid], cs, sn);
-        rope_cs[2 * tid] = cs;
-        rope_cs[2 * tid + 1] = sn;
-    }
-    wait_vmem_all();  // q, the sink and idx0 in registers before the tile loop starts gathering
-    f32x4 acc[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    CT* Kt = reinterpret_cast<CT*>(smem + grp * TILE_BYTES);
-    CT* Vt = Kt + G::K_ELEMS;
-    RawPair raw[PPL];
-    auto load_tile = [&](int tile) {
-#pragma unroll
-        for (int k = 0; k < PPL; ++k) {
-            const int pr = gl + GL * k;
-            if (pr < PAIRS) load_pair<D, KVT, SWT, true>(p, c, sel, tile, pr / (D / 8), pr % (D / 8), raw[k]);
-        }
-    };
-    // Validity of a tile's 16 entries (as load_pair decides it): lane e < 16 tests entry e.
-    auto tile_mask = [&](int tile) {
-        const int e = tile * 16 + li;
-        bool v;
-        if (tile * 16 < p.window) {
-            v = e <= c.pos;  // ring slot e was written
-        } else {
-            const int32_t ix = sel[e - p.window];
-            v = ix >= 0 && (int64_t)ix < c.nv;
-        }
-        return (uint32_t)__ballot(lane < 16 && v) & 0xffffu;
-    };
-
-    if (tid < p.topk) sel[tid] = idx0;
-    for (int i = tid + 256 * DS; i < p.topk; i += 256 * DS) sel[i] = p.idx[(int64_t)c.r * p.topk + i];
-    __syncthreads();  // sel and rope_cs complete
-    const int tstep = 4 * S;  // tiles t = 4 split + grp, then every 4 S-th
-    const int rounds = (n_tiles + tstep - 1) / tstep;
-    int t = 4 * split + grp;
-    if (t < n_tiles) load_tile(t);
-    for (int rd = 0; rd < rounds; ++rd, t += tstep) {
-        const bool mine = t < n_tiles;  // the same for every wave of the group
-        if (mine) {
-#pragma unroll
-            for (int k = 0; k < PPL; ++k) {
-                const int pr = gl + GL * k;
-                if (pr < PAIRS)
-                    store_pair<D, CT, G::KS, G::VS, KVT, SWT>(raw[k], t * 16 < p.window, Kt, Vt, pr / (D / 8),
-                                                              pr % (D / 8));
-            }
-        }
-        __syncthreads();  // every group's tile is in LDS
-        if (t + tstep < n_tiles) load_tile(t + tstep);  // next round's bytes in flight during this round
-        if constexpr (SPLIT) {
-            f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (mine) st = tile_scores<D, CT, G::KS, NQ>(Kt, qf, g, li, 256 * dh);
-            xch[64 * wave + lane] = st;
-            __syncthreads();  // both halves of every group's scores written
-            if (mine)
-                tile_update<D, CT, G::VS, NDT>(st + xch[64 * (wave ^ 1) + lane], Vt, tile_mask(t), p.scale_log2, g,
-                                               li, m, l, acc, dt0);
-        } else if (mine) {
-            const uint32_t vm = tile_mask(t);
-            tile_compute<D, CT, G::KS, G::VS, NDT>(Kt, Vt, vm, qf, p.scale_log2, g, li, m, l, acc, dt0);
-        }
-        __syncthreads();  // tile buffers free for the next round
-    }
-
-    // ---- merge the 4 groups' softmax states -----------------------------------
-    l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
-    if (dh == 0 && g == 0) {
-        ml[grp][0][li] = m;
-        ml[grp][1][li] = l;
-    }
-    __syncthreads();
-    float mx = kNegInf;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, ml[w][0][li]);
-    const float mu = (mx == kNegInf) ? 0.f : mx;
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) L += ml[w][1][li] * exp2f(ml[w][0][li] - mu);
-    const float mine_w = exp2f(m - mu);
-    float* slice = reinterpret_cast<float*>(smem) + grp * 16 * ACC_STRIDE;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-        *reinterpret_cast<f32x4*>(slice + li * ACC_STRIDE + 16 * (dt0 + dt) + 4 * g) = acc[dt] * mine_w;
-    __syncthreads();
-    if (h >= H) return;
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const float* base = reinterpret_cast<const float*>(smem);
-    const int64_t obase = ((int64_t)c.r * H + h) * D;
-    // split > 1: this workgroup's state (max mx in log2 units, -inf when it saw nothing; sum L and the
-    // weighted values, both relative to mu) goes to the workspace for attn_merge_kernel
-    float* part = S > 1 ? p.part + (((int64_t)c.r * NHG + hg) * S + split) * (16 * (2 + D)) : nullptr;
-    if (S > 1 && wave == 0 && g == 0) {
-        part[li] = mx;
-        part[16 + li] = L;
-    }
-    for (int dt = wave; dt < D / 16; dt += 4 * DS) {
-        const int off = li * ACC_STRIDE + 16 * dt + 4 * g;
-        f32x4 sum = *reinterpret_cast<const f32x4*>(base + off);
-#pragma unroll
-        for (int w = 1; w < 4; ++w) sum += *reinterpret_cast<const f32x4*>(base + w * 16 * ACC_STRIDE + off);
-        const int d0 = 16 * dt + 4 * g;
-        if (S > 1) *reinterpret_cast<f32x4*>(part + 32 + li * D + d0) = sum;
-        else emit4<D, R, OT>(p.out, obase + d0, d0, sum, inv, rope_cs);
-    }
-}
-
-// Merge of the splits' partial states of one (row, 16-head group): the same combination as the
-// in-workgroup merge of the tile groups (max, weighted sums), then normalisation, the inverse
-// rotation of the rope tail and the store.
+// Merge of the splits' partial states of one (row, 16-head group): the largest max, each state's
+// sum and values weighted by 2^(its max - that max), then normalisation, the inverse rotation of
+// the rope tail and the store.
 // One workgroup per (row, head group, quarter of the D columns): 64 threads per head... every thread
 // owns 4 consecutive columns of one head; the splits' states are read once each, all loads issued
 // before any is used.
@@ -1059,34 +898,30 @@ static hipError_t launch_attn(const AttnParams& p, bool decode, hipStream_t stre
     constexpr int NT = 64 * NHG;
     // the 64-head shapes split each head group's output columns over two waves
     constexpr int DS = (H == 64 && D == 512) ? 2 : 1;
-    if (decode && p.rows * NHG < 1024) {
-        const int blocks = ((p.rows + 7) / 8) * 8 * NHG * p.splits;
-        hipLaunchKernelGGL((attn_decode_kernel<H, D, R, CT, QT, KVT, SWT, OT, DS>), dim3((unsigned)blocks),
-                           dim3(256 * DS), 0, stream, p);
+    if (decode) {
+        hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, true, DS>),
+                           dim3((unsigned)(p.rows * p.splits)), dim3(NT * DS), 0, stream, p);
         if (p.splits > 1)
             hipLaunchKernelGGL((attn_merge_kernel<H, D, R, OT>), dim3((unsigned)(p.rows * NHG * 4)), dim3(256), 0,
                                stream, p);
-        return hipGetLastError();
-    }
-    if (decode)
-        hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, true, DS>), dim3((unsigned)p.rows),
-                           dim3(NT * DS), 0, stream, p);
-    else
+    } else
         hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, false, DS>), dim3((unsigned)p.rows),
                            dim3(NT * DS), 0, stream, p);
     return hipGetLastError();
 }
 
 // Splits of a decode row's entries: enough workgroups (one per CU: 158 KB of LDS each) to fill the
-// 256 CUs, each split group keeping at least two tiles; the caller may ask for a count (1..8).
+// 256 CUs, at most 4 from 32 rows on, each split keeping at least one pair of tiles; the caller may
+// ask for a count (1..8).
 int attn_decode_splits(int rows, int heads, int dim, int window, int topk, int requested) {
-    const int nhg = (heads + 15) / 16;
-    if (rows <= 0 || rows * nhg >= 1024) return 1;  // many rows: one workgroup per row instead
-    if (requested > 0) return requested < kMaxSplits ? requested : kMaxSplits;
+    (void)heads;
     (void)dim;
-    const int n_tiles = (window + topk) / 16;
-    int s = 256 / (rows * nhg);
-    const int by_tiles = n_tiles / 8;  // 4 tile groups per workgroup, >= 2 tiles each
+    if (rows <= 0) return 1;
+    if (requested > 0) return requested < kMaxSplits ? requested : kMaxSplits;
+    int s = 256 / rows;
+    // From 32 rows on, 4 splits measured faster than more (the merge reads every split's state)
+    if (rows >= 32 && s > 4) s = 4;
+    const int by_tiles = (window + topk) / 32;  // each split keeps at least one pair of tiles
     if (s > by_tiles) s = by_tiles;
     if (s > kMaxSplits) s = kMaxSplits;
     return s < 1 ? 1 : s;

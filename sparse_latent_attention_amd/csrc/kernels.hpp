@@ -103,12 +103,12 @@ struct AttnParams {
     int32_t ratio;
     int32_t window;
     float scale_log2;  // softmax_scale * log2(e)
-    int32_t splits;    // decode kernel: workgroups per (row, head group) that split the entries (1: none)
+    int32_t splits;    // decode: workgroups per row that split its entries (1: none)
     float* part;       // splits > 1: partial softmax states [rows, head groups, splits, 16 x (2 + dim)]
 };
 
-// Decode attention plan: splits of each (row, 16-head group)'s entries over workgroups (1 = no
-// split), and the workspace bytes their partial states take.
+// Decode attention plan: splits of each row's entries over workgroups (1 = no split), and the
+// workspace bytes their partial states take.
 int attn_decode_splits(int rows, int heads, int dim, int window, int topk, int requested);
 size_t attn_decode_workspace(int rows, int heads, int dim, int splits);
 

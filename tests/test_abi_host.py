@@ -371,16 +371,18 @@ def test_attention_inline_scale_rows():
 
 
 def test_decode_split_workspace_rules():
-    """Few decode rows split their entries over workgroups and need a workspace for the partial states;
-    many rows (one workgroup per row) and single splits need none; the split count is bounded."""
+    """Decode rows split their entries over workgroups (256 / rows, at most 8, at most 4 from 32 rows on,
+    at most one per pair of tiles) and need a workspace for the partial states; single splits need none."""
     per = 4 * 16 * (2 + 512) * 4                                   # 4 head groups x 16 heads x (max, sum, 512 values)
-    assert csa2.attn_workspace_size(32, 64, 512, 128, 512, 0) == 32 * 2 * per    # 128 workgroups -> 2 splits
+    assert csa2.attn_workspace_size(32, 64, 512, 128, 512, 0) == 32 * 4 * per    # 4 splits from 32 rows on
+    assert csa2.attn_workspace_size(16, 64, 512, 128, 512, 0) == 16 * 8 * per    # 256 workgroups
     assert csa2.attn_workspace_size(32, 64, 512, 128, 512, 1) == 0
     assert csa2.attn_workspace_size(32, 64, 512, 128, 512, 3) == 32 * 3 * per
-    assert csa2.attn_workspace_size(64, 64, 512, 128, 512, 0) == 0             # 256 workgroups already
-    assert csa2.attn_workspace_size(300, 64, 512, 128, 512, 0) == 0            # rows kernel
-    assert csa2.attn_workspace_size(1, 64, 512, 16, 16, 0) == 0                # too few tiles to split
-    assert csa2.attn_workspace_size(1, 64, 512, 128, 512, 0) == 1 * 5 * per    # 40 tiles: at most 5 splits
+    assert csa2.attn_workspace_size(64, 64, 512, 128, 512, 0) == 64 * 4 * per    # 4 splits
+    assert csa2.attn_workspace_size(300, 64, 512, 128, 512, 0) == 0            # one workgroup per row
+    assert csa2.attn_workspace_size(1, 64, 512, 16, 16, 0) == 0                # one pair of tiles: no split
+    assert csa2.attn_workspace_size(1, 64, 512, 128, 256, 0) == 1 * 8 * per    # 24 tiles: 8 splits
+    assert csa2.attn_workspace_size(1, 64, 512, 64, 64, 0) == 1 * 4 * per      # 8 tiles: at most 4 splits
     a = _attn_args(rows=32, splits=0)
     need = csa2.attn_workspace_size(32, 64, 512, 128, 512, 0)
     assert csa2._lib.csa2_sparse_attn_decode(ctypes.byref(a), None, 0, None) == csa2.ERR_WORKSPACE

@@ -100,8 +100,8 @@ def test_attention_all_layers(case):
 
 
 @pytest.mark.parametrize("rows", [1, 9, 300])
-def test_decode_kernels_agree(rows):
-    # few rows: one workgroup per (row, head group); 300 rows: one workgroup per row (shared tiles)
+def test_decode_row_counts(rows):
+    # 1 and 9 rows: the library's split choice; 300 rows: one workgroup per row, no merge pass
     cfg = SMALL["full_decode_small"].replace(batch=rows, q_tokens=rows)
     x = make_inputs(cfg, 5, device="cuda")
     idx = gpu_topk(cfg, x, gpu_scores(cfg, x))
@@ -115,8 +115,8 @@ def test_decode_kernels_agree(rows):
 @pytest.mark.parametrize("base,rows", [("full_decode_small", 5), ("full_decode_small", 300), ("lowp_small", 7),
                                        ("prefill_small", None)])
 def test_attention_ragged_tile_counts(base, rows, window, topk):
-    """(window + topk) / 16 = 2, 5, 7, 11 tiles: the decode kernel's four tile groups and the rows kernel's
-    two-tile rounds then end with idle groups / a half round; and the largest window and top-k the library
+    """(window + topk) / 16 = 2, 5, 7, 11 tiles: the two-tile rounds then end with a half round (and decode
+    splits with a short or empty last split); and the largest window and top-k the library
     takes (1024 + 2048: 192 tiles, the per-row index and validity buffers full)."""
     cfg = SMALL[base].replace(window=window, topk=topk)
     if rows is not None:
@@ -155,9 +155,9 @@ def test_attention_window_only(base, rows, window):
 @pytest.mark.parametrize("splits", [1, 2, 3, 8])
 @pytest.mark.parametrize("base", ["lowp_small", "full_decode_small", "pages_fp4_small"])
 def test_decode_split_entries(base, splits):
-    """The decode kernel with each row's entries split over 1, 2, 3 or 8 workgroups (partial softmax
-    states merged by a second kernel) against the oracle; empty splits (fewer tiles than split groups)
-    included: 8 splits x 4 groups > the 40 tiles of a 128 + 512 row."""
+    """Decode with each row's entries split over 1, 2, 3 or 8 workgroups (partial softmax states merged
+    by a second kernel) against the oracle; uneven and empty splits included: 3 splits of 14, 14 and 12
+    tiles, and 8 splits of 6 tiles cover the 40 tiles of a 128 + 512 row with the last split empty."""
     import sparse_latent_attention_amd as csa2
     from workloads.step import attn_storage_args
     cfg = SMALL[base]
