@@ -390,38 +390,33 @@ __device__ __forceinline__ void store_pair(const RawPair& raw, bool swa_tile, CT
     store_v4<CT, D, VS>(Vt, jb, x8, v);
 }
 
-// Tile pairs (BF16, D = 512): the two tiles of a pair share one PV copy in
-// which column d of entries 4jb .. 4jb + 3 holds the first tile's 4 values
-// and then the second tile's, so one 16-byte read gives a lane both halves
-// of its 16x16x32 operand.  Block jb starts at jb * kPairVS; column d sits at
-// 8 (d ^ ((d >> 3) & 7)) within it, which spreads a wave's 8-byte stores (one
-// column per lane, 8 columns apart) over the banks, while 8 lanes reading 8
-// consecutive columns still read 128 contiguous bytes.  The 64-element pad
-// shifts consecutive blocks by half a bank row.
-constexpr int kPairVS = 512 * 8 + 64;
-__device__ __forceinline__ int pair_vcol(int d) { return 8 * (d ^ ((d >> 3) & 7)); }
-
+// Tile pairs (BF16, D = 512): only the row-major K tiles live in LDS.  The PV
+// operand (8 entries of one column: 4 of each tile of the pair) is read from
+// them with the gfx950 transposing LDS read (ds_read_b64_tr_b16, see
+// lds_col4), so no transposed copy is written.
 template <int KVT, int SWT>
-__device__ __forceinline__ void store_pair_paired(const RawPair& raw, bool swa_tile, __bf16* Kt, __bf16* V01,
-                                                  int tip, int jb, int x8) {
-    Pack8<__bf16> v[4];
+__device__ __forceinline__ void store_pair_k(const RawPair& raw, bool swa_tile, __bf16* Kt, int jb, int x8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if (swa_tile) raw_convert<SWT, __bf16>(raw, i, v[i]);
-        else raw_convert<KVT, __bf16>(raw, i, v[i]);
-        store_k<__bf16, 512, 512>(Kt, 4 * jb + i, x8, v[i]);
+        Pack8<__bf16> v;
+        if (swa_tile) raw_convert<SWT, __bf16>(raw, i, v);
+        else raw_convert<KVT, __bf16>(raw, i, v);
+        store_k<__bf16, 512, 512>(Kt, 4 * jb + i, x8, v);
     }
-    __bf16* vb = V01 + jb * kPairVS + 4 * tip;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t lo01 = (v[0].w[q] & 0xffffu) | (v[1].w[q] << 16);
-        const uint32_t lo23 = (v[2].w[q] & 0xffffu) | (v[3].w[q] << 16);
-        const uint32_t hi01 = (v[0].w[q] >> 16) | (v[1].w[q] & 0xffff0000u);
-        const uint32_t hi23 = (v[2].w[q] >> 16) | (v[3].w[q] & 0xffff0000u);
-        const int d = 8 * x8 + 2 * q;
-        *reinterpret_cast<u32x2*>(vb + pair_vcol(d)) = u32x2{lo01, lo23};
-        *reinterpret_cast<u32x2*>(vb + pair_vcol(d + 1)) = u32x2{hi01, hi23};
-    }
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane j names 4 consecutive bf16 at its address; lane i then receives
+// element i % 4 of lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 (checked on
+// the device with a lane-layout probe).  So if lane j of group g points at
+// entry 4 g + j / 4, columns c0 + 4 (j % 4) .. + 3, lane i of that group gets
+// column c0 + i of entries 4 g .. 4 g + 3: the A-operand slots 8 g .. 8 g + 3
+// of a 16x16x32 MFMA whose rows are the 16 columns c0 ...
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_col4(const __bf16* p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<__bf16*>(p)));
+    return __builtin_bit_cast(u32x2, r);
 }
 
 template <class CT, int D>
@@ -544,20 +539,23 @@ __device__ __forceinline__ void tile_compute(const CT* Kt, const CT* Vt, uint32_
 // takes about as long as a 16x16x16 one (measured: 1.44 against 0.81 PFLOP/s
 // sustained), so this halves the PV matrix time.  Two score chains per tile.
 template <int NACC>
-__device__ __forceinline__ void tile_pair_compute(const __bf16* Kt0, const __bf16* Kt1, const __bf16* V01,
+__device__ __forceinline__ void tile_pair_compute(const __bf16* Kt0, const __bf16* Kt1,
                                                   uint32_t vm0, uint32_t vm1, const bf16x8* qf, int half,
                                                   f32x4* xch_mine, const f32x4* xch_partner, float scale_log2,
                                                   int g, int li, int lane, float& m, float& l, f32x4* acc, int dt0) {
     constexpr int NS = 512 / 32, NH = NS / 2;
-    // Operand offsets: the lane-dependent part takes 4 values (by s mod 4 for K, by dt mod 4 for
-    // the PV copy: pair_vcol(16 (dt0 + dt) + li) with dt0 a multiple of 8); the rest is constant.
+    // K operand offsets: the lane-dependent part takes 4 values (by s mod 4); the rest is constant.
     // This wave's half of the reduction is k-steps NH * half .. NH * half + NH - 1 (256 elements on).
-    int ko[4], vo[4];
+    int ko[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        ko[b] = li * 512 + 32 * (b ^ (li >> 2)) + 8 * (g ^ (li & 3)) + 256 * half;
-        vo[b] = g * kPairVS + 128 * dt0 + 8 * (16 * b + (li & 8) + ((li & 7) ^ ((2 * b + (li >> 3)) & 7)));
-    }
+    for (int b = 0; b < 4; ++b) ko[b] = li * 512 + 32 * (b ^ (li >> 2)) + 8 * (g ^ (li & 3)) + 256 * half;
+    // PV operand (lds_col4): lane (g, li) names entry e = 4 g + li / 4, columns c0 + 4 (li % 4) .. + 3
+    // with c0 = 16 (dt0 + dt), i.e. half (li % 2) of 16-byte chunk c0 / 8 + (li % 4) / 2, stored at
+    // chunk index ^ (e & 15).  dt0 is a multiple of 16, so the chunk is 2 dt0 + 16 (dt / 8) +
+    // ((2 (dt % 8) + (li % 4) / 2) ^ (e & 15)): the lane's part takes 8 values (by dt mod 8).
+    const int e = 4 * g + (li >> 2);
+    const int vrow = e * 512 + 4 * (li & 1) + 16 * dt0;
+    const int vx = ((li >> 1) & 1) ^ (e & 15);
     f32x4 part[4];  // chains 0, 1: tile 0; chains 2, 3: tile 1
 #pragma unroll
     for (int k = 0; k < 4; ++k) part[k] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -624,8 +622,11 @@ __device__ __forceinline__ void tile_pair_compute(const __bf16* Kt0, const __bf1
         bf16x8, u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]), pack_bf16x2(pr[4], pr[5]),
                       pack_bf16x2(pr[6], pr[7])});
 #pragma unroll
-    for (int dt = 0; dt < NACC; ++dt)
-        acc[dt] = Mma<__bf16>::k32(acc[dt], lds_frag8<__bf16>(V01 + vo[dt & 3] + 512 * (dt >> 2)), pb);
+    for (int dt = 0; dt < NACC; ++dt) {
+        const int v_off = vrow + 8 * (16 * (dt >> 3) + ((2 * (dt & 7)) ^ vx));
+        const u32x2 a0 = lds_col4(Kt0 + v_off), a1 = lds_col4(Kt1 + v_off);
+        acc[dt] = Mma<__bf16>::k32(acc[dt], __builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y}), pb);
+    }
 }
 
 // Normalises, rotates the rope tail back and stores 4 consecutive elements.
@@ -665,10 +666,10 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     constexpr int TT = NT / TPR;                // threads per tile
     constexpr int PPT = (PAIRS + TT - 1) / TT;  // pairs per thread
 
-    // Tile pairs (see kPairVS) for the BF16 512-wide shape with two tiles per round.
+    // Tile pairs (see store_pair_k) for the BF16 512-wide shape with two tiles per round.
     constexpr bool PAIRED = TPR == 2 && D == 512 && sizeof(CT) == 2;
-    // One buffer set per round parity: TPR tiles (paired: two K tiles, then their shared PV copy).
-    constexpr int SET_ELEMS = PAIRED ? 2 * G::K_ELEMS + 4 * kPairVS : TPR * (G::K_ELEMS + G::V_ELEMS);
+    // One buffer set per round parity: TPR tiles (paired: two K tiles, also read as the PV operand).
+    constexpr int SET_ELEMS = PAIRED ? 2 * G::K_ELEMS : TPR * (G::K_ELEMS + G::V_ELEMS);
     __shared__ __attribute__((aligned(16))) CT tiles[2][SET_ELEMS];
     // Paired: per wave, the partial scores of its half of the reduction (2 tiles x 64 lanes).
     __shared__ f32x4 xch[PAIRED ? 128 * NW : 1];
@@ -734,16 +735,13 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
             if (pr < PAIRS) load_pair<D, KVT, SWT, DECODE>(p, c, sel, tile, pr / (D / 8), pr % (D / 8), raw[k]);
         }
     };
-    // Tile buffer b = TPR * set + i: its K tile, and its PV copy (paired: the set's shared one).
+    // Tile buffer b = TPR * set + i: its K tile, and (not paired) its PV copy.
     auto kbuf = [&](int b) -> CT* {
         return tiles[b / TPR] + (b % TPR) * (PAIRED ? G::K_ELEMS : G::K_ELEMS + G::V_ELEMS);
     };
-    auto vbuf = [&](int b) -> CT* {
-        return PAIRED ? tiles[b / TPR] + 2 * G::K_ELEMS : kbuf(b) + G::K_ELEMS;
-    };
+    auto vbuf = [&](int b) -> CT* { return kbuf(b) + G::K_ELEMS; };
     auto store_tile = [&](int tile, int b) {  // tile into buffer b
         CT* Kt = kbuf(b);
-        CT* Vt = vbuf(b);
         uint32_t bits = 0;
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
@@ -751,9 +749,9 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
             if (pr < PAIRS) {
                 const int jb = pr / (D / 8), x8 = pr % (D / 8);
                 if constexpr (PAIRED)
-                    store_pair_paired<KVT, SWT>(raw[k], tile * 16 < p.window, Kt, Vt, b % TPR, jb, x8);
+                    store_pair_k<KVT, SWT>(raw[k], tile * 16 < p.window, Kt, jb, x8);
                 else
-                    store_pair<D, CT, G::KS, G::VS, KVT, SWT>(raw[k], tile * 16 < p.window, Kt, Vt, jb, x8);
+                    store_pair<D, CT, G::KS, G::VS, KVT, SWT>(raw[k], tile * 16 < p.window, Kt, vbuf(b), jb, x8);
                 if (x8 == 0) bits |= raw[k].valid << (4 * jb);
             }
         }
@@ -767,7 +765,7 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
 #pragma unroll
             for (int k = 0; k < PPT; ++k) {
                 const int pr = tl + k * TT;
-                if (pr < PAIRS) store_pair_paired<KVT, SWT>(z, false, kbuf(b), vbuf(b), b % TPR, pr / 64, pr % 64);
+                if (pr < PAIRS) store_pair_k<KVT, SWT>(z, false, kbuf(b), pr / 64, pr % 64);
             }
         }
     };
@@ -787,7 +785,7 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
         if constexpr (PAIRED) {
             // (an odd last tile is paired with the zero-filled buffer, under an empty mask)
             const int t = 2 * rd;
-            tile_pair_compute<NDT>(kbuf(bs), kbuf(bs + 1), vbuf(bs), vmask[tb + t], t + 1 < n_tiles ? vmask[tb + t + 1] : 0u,
+            tile_pair_compute<NDT>(kbuf(bs), kbuf(bs + 1), vmask[tb + t], t + 1 < n_tiles ? vmask[tb + t + 1] : 0u,
                                    qf, wave % 2, xch + 128 * wave, xch + 128 * (wave ^ 1), p.scale_log2, g, li,
                                    lane, m, l, acc, dt0);
         } else {
