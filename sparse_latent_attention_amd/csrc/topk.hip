@@ -67,6 +67,11 @@ struct Lds {
     uint32_t seg_start[kMaxSegs + 1];
 };
 
+// Set bits of m below this lane.
+__device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // Block-wide exclusive suffix sum (sum of v over threads with a larger index).
 __device__ __forceinline__ uint32_t block_suffix_excl(uint32_t v, Lds& s) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -481,6 +486,105 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const TopkParams 
     select_core(lsrc, p, r, s);
 }
 
+// One workgroup per FULL score row (no candidate blocks: the valid columns are
+// the visible prefix) of at most kRegCols columns, read once: each
+// thread holds 64 scores in registers (16 x 16-byte loads; thread (w, l) owns
+// columns 4096 w + 256 j + 4 l + e, so each load instruction covers 1 KiB of
+// the row).  The scores become keys in place (0 marks a column that is not
+// valid: no valid key is below 0x007fffff), the 12-bit histogram gives the bin
+// b1 of the k-th largest key, and the keys in bins >= b1 are compacted into LDS
+// in column order -- per wave in (j, lane, e) order with lane offsets from
+// three bit-plane ballots of the lane counts, waves in turn -- where
+// select_core finishes.  More than kLdsCand such keys (heavy ties): select_core
+// over the row in memory, as in topk_select_kernel.
+constexpr int kRegCols = kThreads * 64;
+
+__global__ __launch_bounds__(kThreads) void topk_regs_kernel(const TopkParams p) {
+    __shared__ Lds s;
+    __shared__ uint32_t lkeys[kLdsCand];
+    __shared__ int32_t lcols[kLdsCand];
+    __shared__ uint32_t wtot[kWaves];
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const RowSrc<kSrcScores> src = row_src<kSrcScores>(p, r);
+    const int n = src.n;
+    const uint32_t k = (uint32_t)p.k;
+    const int cbase = 4096 * wave + 4 * lane;
+    // the visible prefix as a buffer: loads past it return zeros, so none needs a branch
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(src.srow), (short)0, (n > 0 ? n : 0) * 4, 0x00020000);
+    u32x4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (cbase + 256 * j), 0, 0));
+    for (int b = tid; b < 4096; b += kThreads) s.hist[b] = 0u;
+    __syncthreads();
+    // Columns past the visible prefix (FULL rows: no candidate blocks) get key 0 and are counted
+    // in bin 0, below every valid key's bin, so the counting needs no branch.
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t live = 0u - (uint32_t)(cbase + 256 * j + e < n);  // all ones or zero
+            const uint32_t key = order_key(__uint_as_float(v[j][e])) & live;
+            v[j][e] = key;
+            atomicAdd(&s.hist[key >> 20], 1u);
+        }
+    }
+    __syncthreads();
+    const uint32_t total = hist_total(s) - s.hist[0];  // valid keys
+    uint32_t b1 = 0, above = 0;
+    if (total > k) find_bin(s, 4096, k, b1, above);  // b1 >= 7: bin 0 is never reached
+    const uint32_t n_cand = total > k ? above + s.hist[b1] : total;  // valid keys with bin >= b1
+    __syncthreads();  // every thread has read the histogram
+    if (n_cand > (uint32_t)kLdsCand) {
+        select_core(src, p, r, s);
+        return;
+    }
+    // key 0 (not valid) is in bin 0 < b1 whenever b1 is used; with total <= k every valid key is taken
+    auto take = [&](uint32_t key) { return key != 0u && (key >> 20) >= b1; };
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mine += take(v[j][e]) ? 1u : 0u;
+    uint32_t wsum = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) wsum += __shfl_xor(wsum, o, 64);
+    if (lane == 0) wtot[wave] = wsum;
+    __syncthreads();
+    uint32_t off = 0;
+    for (int w = 0; w < wave; ++w) off += wtot[w];
+    // the columns again, from a value the compiler cannot match with the first pass's (it would
+    // otherwise keep all 64 column numbers alive across the histogram, in scratch)
+    int cb = cbase;
+    asm volatile("" : "+v"(cb));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cnt += take(v[j][e]) ? 1u : 0u;
+        const uint64_t p0 = __ballot(cnt & 1u), p1 = __ballot(cnt & 2u), p2 = __ballot(cnt & 4u);
+        const uint32_t before = mbcnt64(p0) + 2u * mbcnt64(p1) + 4u * mbcnt64(p2);
+        uint32_t at = off + before;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (take(v[j][e])) {
+                lkeys[at] = v[j][e];
+                lcols[at] = cb + 256 * j + e;
+                ++at;
+            }
+        }
+        off += (uint32_t)(__builtin_popcountll(p0) + 2 * __builtin_popcountll(p1) + 4 * __builtin_popcountll(p2));
+    }
+    __syncthreads();
+    LdsCandSrc lsrc;
+    lsrc.keys = lkeys;
+    lsrc.cols = lcols;
+    lsrc.n = (int)n_cand;
+    select_core(lsrc, p, r, s);
+}
+
 template <int SRC>
 __global__ __launch_bounds__(kThreads) void topk_filter_kernel(const TopkParams p, const uint32_t* b1_in,
                                                                uint32_t* cand_keys, int32_t* cand_cols,
@@ -642,7 +746,11 @@ static hipError_t launch_topk_src(const TopkParams& p, int rows, void* ws, hipSt
     int chunk, nseg;
     topk_plan(rows, p.width, chunk, nseg, kSweep);
     if (nseg == 0) {
-        hipLaunchKernelGGL(topk_select_kernel<SRC>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+        if (SRC == kSrcScores && p.n_blocks == 0 && p.width <= kRegCols && p.width % 4 == 0 &&
+            reinterpret_cast<uintptr_t>(p.scores) % 16 == 0)
+            hipLaunchKernelGGL(topk_regs_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL(topk_select_kernel<SRC>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
         return hipGetLastError();
     }
     char* w = reinterpret_cast<char*>(ws);
