@@ -18,6 +18,23 @@ from harness import (BF16_ATOL, BF16_RTOL, F32_ATOL, F32_RTOL, SCORE_TOL, assert
 
 pytestmark = pytest.mark.gpu
 
+
+def _record(cfg, x, **fields):
+    """With CSA2_RESULTS_DIR set, merges these measurements into the (workload, seed) record there
+    (<workload>_s<seed>[_ragged].json); otherwise does nothing."""
+    import json
+    import os
+    d = os.environ.get("CSA2_RESULTS_DIR")
+    if not d:
+        return
+    os.makedirs(d, exist_ok=True)
+    path = os.path.join(d, f"{cfg.name}_s{x['_seed']}{'_ragged' if cfg.ragged else ''}.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {"workload": cfg.name, "seed": x["_seed"],
+                                                             "ragged": bool(cfg.ragged)}
+    rec.update(fields)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+
 # (workload, seed, ragged positions).  The two 1M decodes the measurements name run seeds 0, 1 and 2
 # plus a ragged-position batch; the 64K decode runs a ragged batch as well.
 CASES = [("tiny_full_fp32", 2, False), ("full_decode_64k", 2, False), ("full_decode_64k", 1, True),
@@ -46,6 +63,7 @@ def _run_path(cfg, x):
         torch.cuda.synchronize()
         assert torch.equal(step.idx, ref), "score-free top-k differs from topk_select over the written scores"
         print(f"[{cfg.name}] score-free top-k == topk_select(written scores) on all {cfg.q_tokens} rows")
+        _record(cfg, x, score_free_topk_equals_written_scores_rows=int(cfg.q_tokens))
     else:
         scores = step.scores
     return scores, step.idx, step.outs
@@ -112,17 +130,26 @@ def test_sampled_rows_scores_topk_attention(full):
     assert np.all(got[inval] == -np.inf) and np.all(s_ref[inval] == -np.inf)
     ratio = float((np.abs(got[~inval] - s_ref[~inval]) / bound[~inval]).max())
     print(f"[{cfg.name}] sampled rows {rows.tolist()[:6]}: score max |d|/A = {ratio:.3e}")
+    _record(cfg, x, rows_checked=[int(r) for r in rows], score_max_err_over_bound=ratio, score_tol=SCORE_TOL)
     assert ratio <= SCORE_TOL
     gi = idx[torch.from_numpy(rows).cuda()].cpu().numpy()
-    assert np.array_equal(gi, oracle_topk(cfg, x, got, rows)), "top-k of the GPU scores is not bit-exact"
+    exact = bool(np.array_equal(gi, oracle_topk(cfg, x, got, rows)))
+    _record(cfg, x, topk_bit_exact_on_gpu_scores=exact)
+    assert exact, "top-k of the GPU scores is not bit-exact"
     n_diff, n_bad = topk_band_mismatches(cfg, x, rows, gi, oracle_topk(cfg, x, s_ref, rows), s_ref, bound)
     print(f"[{cfg.name}] end-to-end index differences {n_diff}, outside the band {n_bad}")
+    _record(cfg, x, topk_index_differences_vs_oracle_scores=int(n_diff), topk_differences_outside_band=int(n_bad))
     assert n_bad == 0
     atol, rtol = (F32_ATOL, F32_RTOL) if cfg.out_dtype == "f32" else (BF16_ATOL, BF16_RTOL)
+    errs = []
     for layer, o in enumerate(outs):
         ref = oracle_attention(cfg, x, gi, rows, layer=layer)
-        e = assert_close(o[torch.from_numpy(rows).cuda()], ref, atol, rtol, f"{cfg.name} layer {layer}")
+        got_o = o[torch.from_numpy(rows).cuda()]
+        e = assert_close(got_o, ref, atol, rtol, f"{cfg.name} layer {layer}")
+        rel = float((np.abs(got_o.float().cpu().numpy().astype(np.float64) - ref) / np.maximum(np.abs(ref), atol)).max())
+        errs.append({"layer": layer, "max_abs": float(e), "max_rel_over_max_abs_atol": rel})
         print(f"[{cfg.name}] layer {layer} attention max_abs {e:.3e}")
+    _record(cfg, x, attention_errors=errs, attention_atol=atol, attention_rtol=rtol)
 
 
 def test_candidate_pool(full):
