@@ -232,33 +232,46 @@ struct RawPair {
     uint32_t valid;  // bit i: row i of the pair exists and is visible
 };
 
-// Loads the 8 elements of chunk x8 of one stored row (`rowp` points at the row;
-// `fsc` at its FP8 scale, `e8` at its E8M0 scales).  Callers point invalid rows
-// at a dummy in-bounds buffer, so the loads need no branches.
+// Byte offsets within a stored row of D elements: the 8 elements of chunk x8, and (formats with
+// inline scales) the scale byte that covers them.
 template <int DT, int D>
-__device__ __forceinline__ void raw_load_row(const uint8_t* rowp, const float* fsc, const uint8_t* e8, int x8,
+__device__ __forceinline__ int chunk_off(int x8) {
+    return DT == CSA2_F32 ? 32 * x8 : DT == CSA2_BF16 ? 16 * x8
+         : (DT == CSA2_FP8_E4M3 || DT == CSA2_FP8_E4M3_E8M0G32) ? 8 * x8 : 4 * x8;
+}
+template <int DT, int D>
+__device__ __forceinline__ int inline_scale_off(int x8) {
+    return DT == CSA2_FP4_E2M1_E4M3G16 ? D / 2 + (8 * x8) / 16 : DT == CSA2_FP8_E4M3_E8M0G32 ? D + (8 * x8) / 32 : 0;
+}
+
+// Loads the 8 elements of one row's chunk: `dp` points at them (chunk_off already added; an
+// invalid row points into the zero row, so the loads need no branch and decode to zeros), `fsc` at
+// the row's FP8 scale, `e8` at its E8M0 byte (planar FP4 scales); inline scale bytes sit at
+// dp + sdelta.
+template <int DT, int D>
+__device__ __forceinline__ void raw_load_row(const uint8_t* dp, const float* fsc, const uint8_t* e8, int sdelta,
                                              RawPair& raw, int i) {
     if (DT == CSA2_BF16) {
-        raw.v[i] = *reinterpret_cast<const u32x4*>(rowp + 16 * x8);
+        raw.v[i] = *reinterpret_cast<const u32x4*>(dp);
     } else if (DT == CSA2_F32) {
-        raw.v[i] = *reinterpret_cast<const u32x4*>(rowp + 32 * x8);
-        raw.v2[i] = *reinterpret_cast<const u32x4*>(rowp + 32 * x8 + 16);
+        raw.v[i] = *reinterpret_cast<const u32x4*>(dp);
+        raw.v2[i] = *reinterpret_cast<const u32x4*>(dp + 16);
     } else if (DT == CSA2_FP8_E4M3) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(rowp + 8 * x8);
+        const u32x2 w = *reinterpret_cast<const u32x2*>(dp);
         raw.v[i].x = w.x;
         raw.v[i].y = w.y;
         raw.s[i] = *fsc;
     } else if (DT == CSA2_FP4_E2M1) {  // FP4-E2M1 with one E8M0 per 32 (planar scales)
-        raw.v[i].x = *reinterpret_cast<const uint32_t*>(rowp + 4 * x8);
-        raw.sb[i] = e8[(8 * x8) / 32];
+        raw.v[i].x = *reinterpret_cast<const uint32_t*>(dp);
+        raw.sb[i] = *e8;
     } else if (DT == CSA2_FP4_E2M1_E4M3G16) {  // FP4-E2M1, then one E4M3 scale per 16, inline
-        raw.v[i].x = *reinterpret_cast<const uint32_t*>(rowp + 4 * x8);
-        raw.sb[i] = rowp[D / 2 + (8 * x8) / 16];
+        raw.v[i].x = *reinterpret_cast<const uint32_t*>(dp);
+        raw.sb[i] = dp[sdelta];
     } else {  // CSA2_FP8_E4M3_E8M0G32: FP8-E4M3, then one E8M0 scale per 32, inline
-        const u32x2 w = *reinterpret_cast<const u32x2*>(rowp + 8 * x8);
+        const u32x2 w = *reinterpret_cast<const u32x2*>(dp);
         raw.v[i].x = w.x;
         raw.v[i].y = w.y;
-        raw.sb[i] = rowp[D + (8 * x8) / 32];
+        raw.sb[i] = dp[sdelta];
     }
 }
 
@@ -268,19 +281,20 @@ constexpr int row_bytes(int d) {
          : DT == CSA2_FP4_E2M1_E4M3G16 ? d / 2 + d / 16 : DT == CSA2_FP8_E4M3_E8M0G32 ? d + d / 32 : d / 2;
 }
 
+// (Rows that are not there were loaded from the zero row: zero values and zero scale bytes, which
+// decode to zeros, so no validity select is needed here.)
 template <int DT, class CT>
 __device__ __forceinline__ void raw_convert(const RawPair& raw, int i, Pack8<CT>& o) {
-    const bool ok = (raw.valid >> i) & 1u;
     if constexpr (DT == CSA2_BF16) {
-        o.w[0] = ok ? raw.v[i].x : 0u;
-        o.w[1] = ok ? raw.v[i].y : 0u;
-        o.w[2] = ok ? raw.v[i].z : 0u;
-        o.w[3] = ok ? raw.v[i].w : 0u;
+        o.w[0] = raw.v[i].x;
+        o.w[1] = raw.v[i].y;
+        o.w[2] = raw.v[i].z;
+        o.w[3] = raw.v[i].w;
     } else if constexpr (DT == CSA2_F32) {
         const uint32_t u[8] = {raw.v[i].x, raw.v[i].y, raw.v[i].z, raw.v[i].w,
                                raw.v2[i].x, raw.v2[i].y, raw.v2[i].z, raw.v2[i].w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o.v[e] = ok ? __uint_as_float(u[e]) : 0.f;
+        for (int e = 0; e < 8; ++e) o.v[e] = __uint_as_float(u[e]);
     } else if constexpr (DT == CSA2_FP4_E2M1 && sizeof(CT) == 2) {
         // E2M1 pairs straight to bf16 pairs, multiplied by the power-of-two block scale (exact).
         // E8M0 byte 255 is NaN: every element of its block decodes to NaN (0 x NaN included),
@@ -293,10 +307,10 @@ __device__ __forceinline__ void raw_convert(const RawPair& raw, int i, Pack8<CT>
         const uint32_t b1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
         const uint32_t b2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
         const uint32_t b3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
-        o.w[0] = ok ? (nan_blk ? kNanPair : b0) : 0u;
-        o.w[1] = ok ? (nan_blk ? kNanPair : b1) : 0u;
-        o.w[2] = ok ? (nan_blk ? kNanPair : b2) : 0u;
-        o.w[3] = ok ? (nan_blk ? kNanPair : b3) : 0u;
+        o.w[0] = nan_blk ? kNanPair : b0;
+        o.w[1] = nan_blk ? kNanPair : b1;
+        o.w[2] = nan_blk ? kNanPair : b2;
+        o.w[3] = nan_blk ? kNanPair : b3;
     } else {
         // Exact in every case: an FP8 or FP4 value times a power of two, or an E2M1 value
         // (<= 2 significant bits) times an E4M3 scale (<= 4), fits bf16's 8 bits.
@@ -315,7 +329,7 @@ __device__ __forceinline__ void raw_convert(const RawPair& raw, int i, Pack8<CT>
             f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1]; f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = ok ? f[e] * sc : 0.f;
+        for (int e = 0; e < 8; ++e) f[e] = f[e] * sc;
         pack_from_floats<CT>(f, o);
     }
 }
@@ -324,54 +338,93 @@ constexpr int kMaxTiles = 192;  // (window + topk) / 16 at most (window <= 1024,
 constexpr int kMaxSplits = 8;   // decode workgroups per (row, head group) at most
 constexpr int kMaxTopk = 2048;
 
+// Rows that are not there (absent SWA slots, -1 or out-of-range indices, rows the group-causal mask
+// hides) are read from here instead: zeros, which decode to zeros in every stored format.  Never
+// written; 1 KiB covers the largest stored row (512 BF16 elements).
+__device__ __attribute__((aligned(64))) uint8_t g_zero_row[1024];
+
 // Per-row geometry the gather needs.
 struct RowCtx {
-    int64_t pos, nv, kv_base;
-    const uint8_t* dummy;  // in-bounds bytes (this row's q) that invalid entries load from
+    int64_t pos, nv;
     int r;
+    const uint8_t* swa0;   // window slot e's stored row at swa0 + e * (SWA row bytes)
+    const float* swas0;    // FP8 SWA rows: slot e's scale at swas0[e]
+    const uint8_t* kv0;    // selected row id at kv0 + id * (main row bytes)
+    const uint8_t* kvs0;   // planar E8M0 scales: row id's at kvs0 + id * (D / 32)
+    int win_lo, win_hi;    // window slots e with win_lo <= e < win_hi are there
+    uint32_t nv32;         // ids below this are visible (-1 is not: it wraps to the top)
 };
 
-// Loads the raw bytes of pair (jb, x8) of tile `tile` (predicated on validity).
-// `sel` is the row's selected-index list, staged in LDS.
+template <int D, int KVT, int SWT, bool DECODE>
+__device__ __forceinline__ void row_ctx_init(const AttnParams& p, RowCtx& c, int r) {
+    c.r = r;
+    c.pos = p.pos[r];
+    c.nv = (c.pos + 1) / p.ratio;
+    c.nv32 = (uint32_t)(c.nv < 0x7fffffff ? (c.nv > 0 ? c.nv : 0) : 0x7fffffff);
+    const int64_t kv_base = p.kv_row_base[r];
+    c.kv0 = reinterpret_cast<const uint8_t*>(p.kv) + kv_base * row_bytes<KVT>(D);
+    c.kvs0 = KVT == CSA2_FP4_E2M1 ? p.kv_scale + kv_base * (D / 32) : nullptr;
+    const int W = p.window;
+    int64_t s0, lo, hi;  // stored SWA row of slot 0, and the slots that are there
+    if (DECODE) {
+        // Ring slot e holds position pos - ((pos - e) mod W); that position is negative (the slot
+        // was never written) exactly when e > pos.
+        s0 = (int64_t)r * W;
+        lo = 0;
+        hi = c.pos + 1;
+    } else {
+        // slot e is linear window position a = pos - (W - 1) + e, stored row a - swa_pos0
+        s0 = c.pos - (W - 1) - p.swa_pos0;
+        lo = (W - 1) - c.pos;                         // a >= 0
+        if (lo < -s0) lo = -s0;                       // stored row >= 0
+        hi = p.swa_rows - s0;                         // stored row < swa_rows
+    }
+    if (lo < 0) lo = 0;
+    if (hi > W) hi = W;
+    if (hi < lo) hi = lo;
+    c.win_lo = (int)lo;
+    c.win_hi = (int)hi;
+    c.swa0 = reinterpret_cast<const uint8_t*>(p.swa) + s0 * row_bytes<SWT>(D);
+    c.swas0 = SWT == CSA2_FP8_E4M3 ? p.swa_scale + s0 : nullptr;
+}
+
+// Loads the raw bytes of pair (jb, x8) of tile `tile`: chunk x8 of 4 consecutive entries.
+// `sel` is the row's selected-index list, staged in LDS.  Each row address is one 32 x 32 -> 64
+// multiply-add on a per-row base and a select against the zero row.
 template <int D, int KVT, int SWT, bool DECODE>
 __device__ __forceinline__ void load_pair(const AttnParams& p, const RowCtx& c, const int32_t* sel, int tile, int jb,
                                           int x8, RawPair& raw) {
     const int W = p.window;
     raw.valid = 0u;
     if (tile * 16 < W) {
+        constexpr int RB = row_bytes<SWT>(D);
+        const int xo = chunk_off<SWT, D>(x8);
+        const int sd = inline_scale_off<SWT, D>(x8) - xo;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = tile * 16 + 4 * jb + i;
-            int64_t srow;
-            bool valid;
-            if (DECODE) {
-                // Ring slot e holds position pos - ((pos - e) mod W); that position is
-                // negative (the slot was never written) exactly when e > pos.
-                valid = e <= c.pos;
-                srow = (int64_t)c.r * W + e;
-            } else {
-                const int64_t a = c.pos - (W - 1) + e;                // linear window position
-                srow = a - p.swa_pos0;
-                valid = a >= 0 && srow >= 0 && srow < p.swa_rows;
-            }
-            constexpr int RB = row_bytes<SWT>(D);
-            const uint8_t* rp = valid ? reinterpret_cast<const uint8_t*>(p.swa) + srow * RB : c.dummy;
-            const float* fs = (SWT == CSA2_FP8_E4M3 && valid) ? p.swa_scale + srow : reinterpret_cast<const float*>(c.dummy);
-            raw_load_row<SWT, D>(rp, fs, c.dummy, x8, raw, i);
+            const bool valid = (uint32_t)(e - c.win_lo) < (uint32_t)(c.win_hi - c.win_lo);
+            const uint8_t* dp = valid ? c.swa0 + ((uint64_t)(uint32_t)e * RB + xo) : g_zero_row + xo;
+            const float* fs = SWT == CSA2_FP8_E4M3 ? (valid ? c.swas0 + e : reinterpret_cast<const float*>(g_zero_row))
+                                                   : nullptr;
+            raw_load_row<SWT, D>(dp, fs, nullptr, sd, raw, i);
             raw.valid |= (valid ? 1u : 0u) << i;
         }
     } else {
+        constexpr int RB = row_bytes<KVT>(D);
+        const int xo = chunk_off<KVT, D>(x8);
+        const int sd = inline_scale_off<KVT, D>(x8) - xo;
         // the pair's 4 selected indices with one 16-byte LDS read (W and 16 * tile are multiples of 16)
         const i32x4 ids = *reinterpret_cast<const i32x4*>(sel + tile * 16 + 4 * jb - W);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int32_t id = ids[i];
-            const bool valid = id >= 0 && (int64_t)id < c.nv;  // group-causal mask
-            constexpr int RB = row_bytes<KVT>(D);
-            const int64_t row = c.kv_base + (valid ? id : 0);
-            const uint8_t* rp = valid ? reinterpret_cast<const uint8_t*>(p.kv) + row * RB : c.dummy;
-            const uint8_t* e8 = (KVT == CSA2_FP4_E2M1 && valid) ? p.kv_scale + row * (D / 32) : c.dummy;
-            raw_load_row<KVT, D>(rp, nullptr, e8, x8, raw, i);
+            const uint32_t id = (uint32_t)ids[i];
+            const bool valid = id < c.nv32;  // group-causal mask; -1 wraps to the top
+            const uint8_t* dp = valid ? c.kv0 + ((uint64_t)id * RB + xo) : g_zero_row + xo;
+            const uint8_t* e8 = KVT == CSA2_FP4_E2M1
+                                    ? (valid ? c.kvs0 + ((uint64_t)id * (D / 32) + (8 * x8) / 32) : g_zero_row)
+                                    : nullptr;
+            raw_load_row<KVT, D>(dp, nullptr, e8, sd, raw, i);
             raw.valid |= (valid ? 1u : 0u) << i;
         }
     }
@@ -685,11 +738,7 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     const int S = DECODE ? p.splits : 1;
     const int split = DECODE ? (int)(blockIdx.x % S) : 0;
     RowCtx c;
-    c.r = DECODE ? (int)(blockIdx.x / S) : (int)blockIdx.x;
-    c.pos = p.pos[c.r];
-    c.nv = (c.pos + 1) / p.ratio;
-    c.kv_base = p.kv_row_base[c.r];
-    c.dummy = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)c.r * H * D * (QT == CSA2_F32 ? 4 : 2);
+    row_ctx_init<D, KVT, SWT, DECODE>(p, c, DECODE ? (int)(blockIdx.x / S) : (int)blockIdx.x);
     const int n_all = (p.window + p.topk) / 16;
     const int per = S > 1 ? ((n_all + S - 1) / S + 1) & ~1 : n_all;
     const int tb = split * per;  // first tile of this workgroup
