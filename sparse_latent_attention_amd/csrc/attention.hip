@@ -337,6 +337,14 @@ __device__ __forceinline__ void raw_convert(const RawPair& raw, int i, Pack8<CT>
 constexpr int kMaxTiles = 192;  // (window + topk) / 16 at most (window <= 1024, topk <= 2048)
 constexpr int kMaxSplits = 8;   // decode workgroups per (row, head group) at most
 constexpr int kMaxTopk = 2048;
+// Rounds of tile loads in flight in attn_rows_kernel: two for prefill (measured 7 % faster than one
+// on the 4096-row chunk), one for decode (two were 1 us slower: a decode workgroup has few rounds).
+#ifndef CSA2_ATTN_PREFILL_PF
+#define CSA2_ATTN_PREFILL_PF 2
+#endif
+#ifndef CSA2_ATTN_DECODE_PF
+#define CSA2_ATTN_DECODE_PF 1
+#endif
 
 // Rows that are not there (absent SWA slots, -1 or out-of-range indices, rows the group-causal mask
 // hides) are read from here instead: zeros, which decode to zeros in every stored format.  Never
@@ -776,12 +784,15 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    RawPair raw[PPT];
-    auto load_tile = [&](int tile) {
+    // The raw bytes of the next PF rounds' tiles are in flight in registers (slot q % PF holds round
+    // q's); the loop is unrolled by PF so every slot index is a constant.
+    constexpr int PF = DECODE ? CSA2_ATTN_DECODE_PF : CSA2_ATTN_PREFILL_PF;
+    RawPair raw[PF][PPT];
+    auto load_tile = [&](int tile, RawPair* rw) {
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
             const int pr = tl + k * TT;
-            if (pr < PAIRS) load_pair<D, KVT, SWT, DECODE>(p, c, sel, tile, pr / (D / 8), pr % (D / 8), raw[k]);
+            if (pr < PAIRS) load_pair<D, KVT, SWT, DECODE>(p, c, sel, tile, pr / (D / 8), pr % (D / 8), rw[k]);
         }
     };
     // Tile buffer b = TPR * set + i: its K tile, and (not paired) its PV copy.
@@ -789,7 +800,7 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
         return tiles[b / TPR] + (b % TPR) * (PAIRED ? G::K_ELEMS : G::K_ELEMS + G::V_ELEMS);
     };
     auto vbuf = [&](int b) -> CT* { return kbuf(b) + G::K_ELEMS; };
-    auto store_tile = [&](int tile, int b) {  // tile into buffer b
+    auto store_tile = [&](int tile, int b, const RawPair* raw) {  // tile into buffer b
         CT* Kt = kbuf(b);
         uint32_t bits = 0;
 #pragma unroll
@@ -822,14 +833,20 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     __syncthreads();  // rope table and vmask reset visible
     const int n_rounds = (n_tiles + TPR - 1) / TPR;
     if (ts < n_tiles) {
-        load_tile(tb + ts);
-        store_tile(tb + ts, ts);
+        load_tile(tb + ts, raw[0]);
+        store_tile(tb + ts, ts, raw[0]);
     } else if (PAIRED && ts == n_tiles) {
         zero_tile(ts);
     }
-    if (TPR + ts < n_tiles) load_tile(tb + TPR + ts);
+#pragma unroll
+    for (int j = 1; j <= PF; ++j)
+        if (TPR * j + ts < n_tiles) load_tile(tb + TPR * j + ts, raw[j % PF]);
     __syncthreads();
-    for (int rd = 0; rd < n_rounds; ++rd) {
+    for (int rd0 = 0; rd0 < n_rounds; rd0 += PF) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+        const int rd = rd0 + j;
+        if (rd >= n_rounds) break;  // the same in every wave
         const int bs = (rd & 1) * TPR;
         if constexpr (PAIRED) {
             // (an odd last tile is paired with the zero-filled buffer, under an empty mask)
@@ -846,15 +863,17 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
                                                            g, li, m, l, acc, dt0);
             }
         }
-        // the next round's tiles go into the other buffer set; its loads were issued a round ago
+        // the next round's tiles go into the other buffer set; their loads were issued PF rounds ago,
+        // and the slot they free takes the tiles PF rounds after them
         const int tn = (rd + 1) * TPR + ts;
         if (tn < n_tiles) {
-            store_tile(tb + tn, (bs ^ TPR) + ts);
-            if (tn + TPR < n_tiles) load_tile(tb + tn + TPR);
+            store_tile(tb + tn, (bs ^ TPR) + ts, raw[(j + 1) % PF]);
+            if (tn + PF * TPR < n_tiles) load_tile(tb + tn + PF * TPR, raw[(j + 1) % PF]);
         } else if (PAIRED && tn == n_tiles && (n_tiles & 1)) {
             zero_tile((bs ^ TPR) + ts);
         }
         __syncthreads();
+    }
     }
 
     l += shfl_xor(l, 16);
