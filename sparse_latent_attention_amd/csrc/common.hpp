@@ -165,6 +165,14 @@ __device__ __forceinline__ void wait_vmem_all() {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt 0; expcnt 7 and lgkmcnt 15: no wait
 }
 
+// Waits until at most N of this wave's vector memory loads are outstanding (expcnt, lgkmcnt: no
+// wait).  After it the compiler's own wait insertion knows that every older load has completed.
+template <int N>
+__device__ __forceinline__ void wait_vmem_below() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // Keeps the compiler from moving LDS accesses of one wave across this point.
 __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");

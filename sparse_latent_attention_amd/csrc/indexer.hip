@@ -841,9 +841,15 @@ __global__ __launch_bounds__(256) void indexer_rescore_kernel(const IndexParams 
         const_cast<void*>(KF::scale_base(p, base)), (short)0, n_rows * 4, kRsrcWord3);
 
     uint32_t n_out = 0;
-    // Re-scores queued blocks head .. head+cnt-1 (cnt 1..8) as one step and appends their candidates.
-    auto rescore = [&](int head, int cnt) {
+    // A step re-scores queued blocks head .. head+cnt-1 (cnt 1..8) and appends their candidates.  Its
+    // loads (issue) and its arithmetic (finish) are separate so that the next step's key rows are in
+    // flight while a step is computed; two register sets alternate (no copy between them, which would
+    // wait for the loads).
+    struct StepLoads {
         u32x4 buf[KF::kLoads];
+        uint32_t sw;
+    };
+    auto issue = [&](int head, int cnt, StepLoads& L) {
 #pragma unroll
         for (int j = 0; j < KF::kLoads; ++j) {
             // key kk of the step = row kk % 8 of queued block kk / 8; past the queue: an
@@ -851,19 +857,24 @@ __global__ __launch_bounds__(256) void indexer_rescore_kernel(const IndexParams 
             const int kk = j * (64 / KF::kLoads) + lane / KF::kChunks;
             const int blk = kk >> 3;
             const int row = blk < cnt ? q8[head + blk] * kKeyBlock + (kk & 7) : n_rows;
-            buf[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   krs, row * KF::kRowBytes + 16 * (lane % KF::kChunks), 0, kNT));
+            L.buf[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     krs, row * KF::kRowBytes + 16 * (lane % KF::kChunks), 0, kNT));
         }
         const int my_blk = lane / kKeyBlock;
         const int64_t col = my_blk < cnt
             ? (int64_t)q8[head + my_blk] * kKeyBlock + (lane % kKeyBlock) : n_valid;
-        const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(col < n_valid ? col : n_valid) * 4, 0, 0);
-        stage_put<KF>(my, scl, buf, sw, lane);
+        L.sw = __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(col < n_valid ? col : n_valid) * 4, 0, 0);
+    };
+    auto finish = [&](int head, int cnt, const StepLoads& L) {
+        const int my_blk = lane / kKeyBlock;
+        const int64_t col = my_blk < cnt
+            ? (int64_t)q8[head + my_blk] * kKeyBlock + (lane % kKeyBlock) : n_valid;
+        stage_put<KF>(my, scl, L.buf, L.sw, lane);
         float v[4];
         step_sums<KF>(my, scl, qa, qs, wr, g, li, v);
         const float kk = reduce_scatter(v, lane);
         const bool valid = col < n_valid;
-        const float sc = KF::score_scale(p.scale, sw, q_nan);
+        const float sc = KF::score_scale(p.scale, L.sw, q_nan);
         const uint32_t key = order_key(sc * kk);
         const bool take = valid && (key >> 20) >= b1;
         const uint64_t m = __ballot(take);
@@ -875,6 +886,7 @@ __global__ __launch_bounds__(256) void indexer_rescore_kernel(const IndexParams 
         }
         n_out += (uint32_t)__builtin_popcountll(m);
     };
+    StepLoads la, lb;
 
     if (c_hi > c_lo) {
         const int64_t blk_lo = c_lo / kKeyBlock, blk_hi = (c_hi + kKeyBlock - 1) / kKeyBlock;
@@ -896,7 +908,25 @@ __global__ __launch_bounds__(256) void indexer_rescore_kernel(const IndexParams 
                         (int32_t)(b0 + 64 * i + lane);
                 n_q += __builtin_popcountll(m);
             }
-            for (int h = 0; h < n_q; h += 8) rescore(h, n_q - h < 8 ? n_q - h : 8);
+            auto cnt_at = [&](int h) { return n_q - h < 8 ? n_q - h : 8; };  // <= 0: an empty step
+            // The first four steps run straight-line with the next step's loads in flight: every
+            // issue is unconditional (an empty step's loads fall past the descriptors and return
+            // zeros) so the loads keep one order on every path and the compiler waits for exactly
+            // the older step; only the arithmetic is skipped for empty steps.  (In a loop the
+            // compiler loses that order at the back edge and waits for both steps.)  Further steps,
+            // rare, run one at a time.
+            issue(0, cnt_at(0), la);
+            issue(8, cnt_at(8), lb);
+            if (n_q > 0) finish(0, cnt_at(0), la);
+            issue(16, cnt_at(16), la);
+            if (n_q > 8) finish(8, cnt_at(8), lb);
+            issue(24, cnt_at(24), lb);
+            if (n_q > 16) finish(16, cnt_at(16), la);
+            if (n_q > 24) finish(24, cnt_at(24), lb);
+            for (int h = 32; h < n_q; h += 8) {
+                issue(h, cnt_at(h), la);
+                finish(h, cnt_at(h), la);
+            }
         }
     }
     if (lane == 0) seg_count[(int64_t)r * nseg + seg] = n_out;
