@@ -202,28 +202,39 @@ struct LdsCandSrc {
 };
 
 template <class Src>
-__device__ __forceinline__ void select_core(const Src& src, const TopkParams& p, int r, Lds& s) {
+// known_b1 >= 0: every position holds a valid key, and the bin of the k-th largest key and the
+// count above it (known_above1) are already known -- pass 1 is skipped.
+__device__ __forceinline__ void select_core(const Src& src, const TopkParams& p, int r, Lds& s, int known_b1 = -1,
+                                            uint32_t known_above1 = 0) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     int32_t* orow = p.out + (int64_t)r * p.k;
     const uint32_t k = (uint32_t)p.k;
     const int n = src.n;
 
-    // pass 1: bits [31:20]
-    for (int b = tid; b < 4096; b += kThreads) s.hist[b] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += kThreads) {
-        uint32_t key;
-        int32_t col;
-        if (src.get(i, key, col)) atomicAdd(&s.hist[key >> 20], 1u);
+    uint32_t total = (uint32_t)n;
+    if (known_b1 < 0) {
+        // pass 1: bits [31:20]
+        for (int b = tid; b < 4096; b += kThreads) s.hist[b] = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += kThreads) {
+            uint32_t key;
+            int32_t col;
+            if (src.get(i, key, col)) atomicAdd(&s.hist[key >> 20], 1u);
+        }
+        __syncthreads();
+        total = hist_total(s);
     }
-    __syncthreads();
-    const uint32_t total = hist_total(s);
     const bool select_all = total <= k;
     uint32_t T = 0, n_gt = 0;
     if (!select_all) {
         uint32_t b1, above1, b2, above2, b3, above3;
-        find_bin(s, 4096, k, b1, above1);
+        if (known_b1 >= 0) {
+            b1 = (uint32_t)known_b1;
+            above1 = known_above1;
+        } else {
+            find_bin(s, 4096, k, b1, above1);
+        }
         // pass 2: bits [19:8] of keys in bin b1
         for (int b = tid; b < 4096; b += kThreads) s.hist[b] = 0;
         __syncthreads();
@@ -487,15 +498,17 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const TopkParams 
 }
 
 // One workgroup per FULL score row (no candidate blocks: the valid columns are
-// the visible prefix) of at most kRegCols columns, read once: each
-// thread holds 64 scores in registers (16 x 16-byte loads; thread (w, l) owns
-// columns 4096 w + 256 j + 4 l + e, so each load instruction covers 1 KiB of
-// the row).  The scores become keys in place (0 marks a column that is not
-// valid: no valid key is below 0x007fffff), the 12-bit histogram gives the bin
-// b1 of the k-th largest key, and the keys in bins >= b1 are compacted into LDS
-// in column order -- per wave in (j, lane, e) order with lane offsets from
-// three bit-plane ballots of the lane counts, waves in turn -- where
-// select_core finishes.  More than kLdsCand such keys (heavy ties): select_core
+// the visible prefix) of at most kRegCols columns, read once: each thread loads
+// 64 scores (16 x 16-byte buffer loads; thread (w, l) owns columns
+// 4096 w + 256 j + 4 l + e, so each load instruction covers 1 KiB of the row)
+// and keeps only their keys' 12-bit bins, two to a register (bin 0 marks a
+// column past the visible prefix: no valid key is in a bin below 7).  The
+// histogram gives the bin b1 of the k-th largest key; the columns in bins >=
+// b1 are compacted into LDS in column order -- per wave in (j, lane, e) order
+// with lane offsets from three bit-plane ballots of the lane counts, waves in
+// turn -- their scores are read again (about 1 % of the row, from L2) for the
+// full keys, and select_core finishes from its second pass (its first would
+// find b1 again).  More than kLdsCand such columns (heavy ties): select_core
 // over the row in memory, as in topk_select_kernel.
 constexpr int kRegCols = kThreads * 64;
 
@@ -513,26 +526,33 @@ __global__ __launch_bounds__(kThreads) void topk_regs_kernel(const TopkParams p)
     // the visible prefix as a buffer: loads past it return zeros, so none needs a branch
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(src.srow), (short)0, (n > 0 ? n : 0) * 4, 0x00020000);
-    u32x4 v[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-        v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (cbase + 256 * j), 0, 0));
     for (int b = tid; b < 4096; b += kThreads) s.hist[b] = 0u;
-    __syncthreads();
-    // Columns past the visible prefix (FULL rows: no candidate blocks) get key 0 and are counted
-    // in bin 0, below every valid key's bin, so the counting needs no branch.
+    uint32_t bp[32];  // bins of columns 4j + e (j < 16, e < 4): entry (4j + e) / 2, half (4j + e) % 2
+    {
+        u32x4 v[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 16; ++j)
+            v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (cbase + 256 * j), 0, 0));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t live = 0u - (uint32_t)(cbase + 256 * j + e < n);  // all ones or zero
-            const uint32_t key = order_key(__uint_as_float(v[j][e])) & live;
-            v[j][e] = key;
-            atomicAdd(&s.hist[key >> 20], 1u);
+        for (int j = 0; j < 16; ++j) {
+            uint32_t bins[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t live = 0u - (uint32_t)(cbase + 256 * j + e < n);  // all ones or zero
+                bins[e] = (order_key(__uint_as_float(v[j][e])) >> 20) & live;
+            }
+            bp[2 * j] = bins[0] | (bins[1] << 16);
+            bp[2 * j + 1] = bins[2] | (bins[3] << 16);
         }
     }
+    __syncthreads();  // histogram cleared
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+        atomicAdd(&s.hist[bp[q] & 0xffffu], 1u);
+        atomicAdd(&s.hist[bp[q] >> 16], 1u);
+    }
     __syncthreads();
-    const uint32_t total = hist_total(s) - s.hist[0];  // valid keys
+    const uint32_t total = hist_total(s) - s.hist[0];  // valid keys (bin 0: past the prefix)
     uint32_t b1 = 0, above = 0;
     if (total > k) find_bin(s, 4096, k, b1, above);  // b1 >= 7: bin 0 is never reached
     const uint32_t n_cand = total > k ? above + s.hist[b1] : total;  // valid keys with bin >= b1
@@ -541,13 +561,14 @@ __global__ __launch_bounds__(kThreads) void topk_regs_kernel(const TopkParams p)
         select_core(src, p, r, s);
         return;
     }
-    // key 0 (not valid) is in bin 0 < b1 whenever b1 is used; with total <= k every valid key is taken
-    auto take = [&](uint32_t key) { return key != 0u && (key >> 20) >= b1; };
+    // bin 0 (not valid) is below b1 whenever b1 is used; with total <= k every valid key is taken
+    auto bin_at = [&](int j, int e) { return (bp[2 * j + (e >> 1)] >> (16 * (e & 1))) & 0xffffu; };
+    auto take = [&](uint32_t bin) { return bin != 0u && bin >= b1; };
     uint32_t mine = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mine += take(v[j][e]) ? 1u : 0u;
+        for (int e = 0; e < 4; ++e) mine += take(bin_at(j, e)) ? 1u : 0u;
     uint32_t wsum = mine;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) wsum += __shfl_xor(wsum, o, 64);
@@ -563,14 +584,12 @@ __global__ __launch_bounds__(kThreads) void topk_regs_kernel(const TopkParams p)
     for (int j = 0; j < 16; ++j) {
         uint32_t cnt = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) cnt += take(v[j][e]) ? 1u : 0u;
+        for (int e = 0; e < 4; ++e) cnt += take(bin_at(j, e)) ? 1u : 0u;
         const uint64_t p0 = __ballot(cnt & 1u), p1 = __ballot(cnt & 2u), p2 = __ballot(cnt & 4u);
-        const uint32_t before = mbcnt64(p0) + 2u * mbcnt64(p1) + 4u * mbcnt64(p2);
-        uint32_t at = off + before;
+        uint32_t at = off + mbcnt64(p0) + 2u * mbcnt64(p1) + 4u * mbcnt64(p2);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if (take(v[j][e])) {
-                lkeys[at] = v[j][e];
+            if (take(bin_at(j, e))) {
                 lcols[at] = cb + 256 * j + e;
                 ++at;
             }
@@ -578,11 +597,14 @@ __global__ __launch_bounds__(kThreads) void topk_regs_kernel(const TopkParams p)
         off += (uint32_t)(__builtin_popcountll(p0) + 2 * __builtin_popcountll(p1) + 4 * __builtin_popcountll(p2));
     }
     __syncthreads();
+    // the candidates' full keys, from their scores (read again: the row has just gone through L2)
+    for (int i = tid; i < (int)n_cand; i += kThreads) lkeys[i] = order_key(src.srow[lcols[i]]);
+    __syncthreads();
     LdsCandSrc lsrc;
     lsrc.keys = lkeys;
     lsrc.cols = lcols;
     lsrc.n = (int)n_cand;
-    select_core(lsrc, p, r, s);
+    select_core(lsrc, p, r, s, (int)b1, above);
 }
 
 template <int SRC>
