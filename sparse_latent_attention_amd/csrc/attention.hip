@@ -339,6 +339,13 @@ constexpr int kMaxSplits = 8;   // decode workgroups per (row, head group) at mo
 constexpr int kMaxTopk = 2048;
 // Rounds of tile loads in flight in attn_rows_kernel: two for prefill (measured 7 % faster than one
 // on the 4096-row chunk), one for decode (two were 1 us slower: a decode workgroup has few rounds).
+// Workgroups per row (head slices) of the 64-head shape: two (32 heads each, two workgroups per CU)
+// for decode over BF16 rows, measured 2.8 us faster than one at 32 rows x 1M; one otherwise -- for
+// prefill and for FP4 / FP8 rows the second slice's repeated gather and decode cost more than the
+// overlap of two independent workgroups gains (prefill 3.92 -> 4.28 ms, FP4 decode 39 -> 43 us).
+#ifndef CSA2_ATTN_BF16_DECODE_SLICES
+#define CSA2_ATTN_BF16_DECODE_SLICES 2
+#endif
 #ifndef CSA2_ATTN_PREFILL_PF
 #define CSA2_ATTN_PREFILL_PF 2
 #endif
@@ -713,10 +720,12 @@ __device__ __forceinline__ void emit4(void* out, int64_t off, int d0, f32x4 a, f
 // the whole row (identical in all DS waves) and accumulates 1/DS of the output
 // columns.  DS = 2 halves the accumulator registers, so two waves fit on each
 // SIMD and one wave's LDS reads and waits overlap the other's matrix work.
-template <int H, int D, int R, class CT, int QT, int KVT, int SWT, int OT, bool DECODE, int DS>
-__global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(const AttnParams p) {
-    constexpr int NHG = (H + 15) / 16;
-    constexpr int NW = NHG * DS;
+template <int H, int D, int R, class CT, int QT, int KVT, int SWT, int OT, bool DECODE, int DS, int HS>
+__global__ __launch_bounds__(64 * ((H + 15) / 16 / HS) * DS, 2) void attn_rows_kernel(const AttnParams p) {
+    constexpr int NHG = (H + 15) / 16;  // 16-head groups of a row
+    constexpr int NHGW = NHG / HS;      // of which this workgroup's head slice holds
+    static_assert(NHG % HS == 0, "head slices of whole 16-head groups");
+    constexpr int NW = NHGW * DS;
     constexpr int NT = 64 * NW;
     typedef TileGeom<CT, D> G;
     constexpr int NS = D / 32, NDT = D / 16 / DS;
@@ -736,17 +745,31 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     __shared__ f32x4 xch[PAIRED ? 128 * NW : 1];
     __shared__ float rope_cs[R];
     __shared__ uint32_t vmask[kMaxTiles + 1];  // validity bits of each tile's 16 entries, written once
-    __shared__ __attribute__((aligned(16))) int32_t sel[kMaxTopk];  // this row's selected indices
+    // this row's selected indices (topk entries; sized at launch, so that two workgroups of the
+    // 64-head shape share a CU when topk is small)
+    extern __shared__ __attribute__((aligned(16))) int32_t sel[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
     const int ts = tid / TT, tl = tid % TT;  // this thread's tile of a round, and its index there
-    // Decode may split a row's tiles over S workgroups (split = blockIdx.x % S): each takes an
-    // even-length run of tiles and leaves its softmax state for attn_merge_kernel.
+    // Unit u is a row, or (decode) one of the S splits of a row's tiles: each split takes an
+    // even-length run of tiles and leaves its softmax state for attn_merge_kernel.  A unit's HS head
+    // slices are separate workgroups; their ids follow each other on one XCD (workgroup ids go
+    // round-robin over the 8 XCDs), so the slices gather the unit's rows through the same L2.
     const int S = DECODE ? p.splits : 1;
-    const int split = DECODE ? (int)(blockIdx.x % S) : 0;
+    int u, hs;
+    if constexpr (HS == 1) {
+        u = (int)blockIdx.x;
+        hs = 0;
+    } else {
+        const int s8 = (int)(blockIdx.x >> 3);
+        hs = s8 % HS;
+        u = ((s8 / HS) << 3) | (int)(blockIdx.x & 7);
+        if (u >= (DECODE ? p.rows * S : p.rows)) return;  // padding workgroup (before any barrier)
+    }
+    const int split = DECODE ? u % S : 0;
     RowCtx c;
-    row_ctx_init<D, KVT, SWT, DECODE>(p, c, DECODE ? (int)(blockIdx.x / S) : (int)blockIdx.x);
+    row_ctx_init<D, KVT, SWT, DECODE>(p, c, DECODE ? u / S : u);
     const int n_all = (p.window + p.topk) / 16;
     const int per = S > 1 ? ((n_all + S - 1) / S + 1) & ~1 : n_all;
     const int tb = split * per;  // first tile of this workgroup
@@ -765,7 +788,8 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     if (tid < p.topk) sel[tid] = idx0;
     for (int i = tid + NT; i < p.topk; i += NT) sel[i] = p.idx[(int64_t)c.r * p.topk + i];
 
-    const int h = 16 * (wave / DS) + li;
+    const int hg = NHGW * hs + wave / DS;  // this wave's 16-head group of the row
+    const int h = 16 * hg + li;
     const int dt0 = (wave % DS) * NDT;  // this wave's first 16-column output block
     // Paired: the two waves of a head group each hold and reduce over half of the query.
     constexpr int NQ = PAIRED ? NS / 2 : NS;
@@ -786,7 +810,7 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
 
     // The raw bytes of the next PF rounds' tiles are in flight in registers (slot q % PF holds round
     // q's); the loop is unrolled by PF so every slot index is a constant.
-    constexpr int PF = DECODE ? CSA2_ATTN_DECODE_PF : CSA2_ATTN_PREFILL_PF;
+    constexpr int PF = (DECODE || HS > 1) ? CSA2_ATTN_DECODE_PF : CSA2_ATTN_PREFILL_PF;
     RawPair raw[PF][PPT];
     auto load_tile = [&](int tile, RawPair* rw) {
 #pragma unroll
@@ -880,7 +904,7 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16) * DS) void attn_rows_kernel(co
     l += shfl_xor(l, 32);
     if (h >= H) return;
     if (S > 1) {  // this split's state (max in log2 units, sum and values relative to it) for the merge
-        float* part = p.part + (((int64_t)c.r * NHG + wave / DS) * S + split) * (16 * (2 + D));
+        float* part = p.part + (((int64_t)c.r * NHG + hg) * S + split) * (16 * (2 + D));
         if (wave % DS == 0 && g == 0) {
             part[li] = m;
             part[16 + li] = l;
@@ -961,18 +985,25 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnParams p) {
 template <int H, int D, int R, class CT, int QT, int KVT, int SWT, int OT>
 static hipError_t launch_attn(const AttnParams& p, bool decode, hipStream_t stream) {
     constexpr int NHG = (H + 15) / 16;
-    constexpr int NT = 64 * NHG;
-    // the 64-head shapes split each head group's output columns over two waves
+    // the 64-head shapes split each head group's output columns over two waves, and a row's heads
+    // over HS workgroups
     constexpr int DS = (H == 64 && D == 512) ? 2 : 1;
+    constexpr int HS = (H == 64 && D == 512 && KVT == CSA2_BF16 && SWT == CSA2_BF16) ? CSA2_ATTN_BF16_DECODE_SLICES : 1;
+    const size_t sel_bytes = (size_t)(p.topk > 4 ? p.topk : 4) * sizeof(int32_t);
     if (decode) {
-        hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, true, DS>),
-                           dim3((unsigned)(p.rows * p.splits)), dim3(NT * DS), 0, stream, p);
+        constexpr int NT = 64 * (NHG / HS) * DS;
+        const int units = p.rows * p.splits;
+        const unsigned grid = HS == 1 ? (unsigned)units : (unsigned)(8 * HS * ((units + 7) / 8));
+        hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, true, DS, HS>), dim3(grid), dim3(NT),
+                           sel_bytes, stream, p);
         if (p.splits > 1)
             hipLaunchKernelGGL((attn_merge_kernel<H, D, R, OT>), dim3((unsigned)(p.rows * NHG * 4)), dim3(256), 0,
                                stream, p);
-    } else
-        hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, false, DS>), dim3((unsigned)p.rows),
-                           dim3(NT * DS), 0, stream, p);
+    } else {
+        constexpr int NT = 64 * NHG * DS;
+        hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, false, DS, 1>), dim3((unsigned)p.rows),
+                           dim3(NT), sel_bytes, stream, p);
+    }
     return hipGetLastError();
 }
 
