@@ -349,6 +349,13 @@ constexpr int kMaxTopk = 2048;
 #ifndef CSA2_ATTN_PREFILL_PF
 #define CSA2_ATTN_PREFILL_PF 2
 #endif
+// Prefill rows of the 64-head shape on attn_prefill_kernel (32x32x16 MFMAs, 32 heads per wave).
+#ifndef CSA2_ATTN_PREFILL_WIDE
+#define CSA2_ATTN_PREFILL_WIDE 1
+#endif
+#ifndef CSA2_ATTN_WIDE_PF
+#define CSA2_ATTN_WIDE_PF 1
+#endif
 #ifndef CSA2_ATTN_DECODE_PF
 #define CSA2_ATTN_DECODE_PF 1
 #endif
@@ -923,6 +930,338 @@ __global__ __launch_bounds__(64 * ((H + 15) / 16 / HS) * DS, 2) void attn_rows_k
     }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill rows of the 64-head, 512-wide shape over BF16 rows, on 32x32x16
+// MFMAs: one workgroup of four waves per query row, one wave per SIMD (its
+// 128 accumulator registers in AGPRs).  Wave w owns the 32 heads 32 (w / 2) ..
+// + 31; the two waves of a 32-head block split the QK reduction (256
+// dimensions each; partial scores exchanged through LDS, and a + b == b + a, so
+// both form bit-identical scores and softmax states) and the output columns
+// (256 each).  A round takes the two tiles of 16 entries that one 32-row MFMA
+// operand spans:
+//   S^T (32 entries x 32 heads) = K . q^T   (A: K rows from LDS, B: q in registers)
+//   out^T (32 columns x 32 heads) += V^T . P^T
+// The result layout of the first (lane l: head l % 32; register i: entry
+// 8 (i / 4) + 4 (l / 32) + i % 4) is the P^T operand of the second once the
+// reduction slots are relabelled -- slot 8 (l / 32) + e of k-step t is entry
+// 16 t + 8 (e / 4) + 4 (l / 32) + e % 4 in both operands -- so probabilities
+// stay in registers, and the V^T operand is two transposing LDS reads
+// (lds_col4) of the row-major K tile.  Each K element read from LDS feeds 32
+// heads (16 with the 16x16 shape), and a lane's accumulator is one head's.
+//
+// One wave per SIMD has no second wave to hide its latencies, so the rounds are
+// software-pipelined over three tile sets, with the work of different rounds
+// side by side in straight-line code the compiler can interleave:
+//   (1) QK of round r (its accumulator starts at the entries' score bias), the
+//       stores of round r + 1's tiles (loaded PF rounds before) and the loads
+//       of round r + 1 + PF, the probabilities of round r - 1 and its PV;
+//   (2) the exchange of partial scores: the round's one barrier;
+//   (3) the running max of round r and, rarely, the lazy rescale.
+// One barrier per round suffices: a tile set's last reader is the PV of its
+// round, in the next round's phase (1), and the set is rewritten in the phase
+// (1) after that, past that round's barrier; the exchange buffer alternates
+// with the round's parity.  Every row address is
+// prepared once per workgroup (absent rows and the rounds past the end point at
+// the zero row and carry a -inf score bias), so the gather has no branch.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+// global-memory view of a row address held as an integer (a flat load would also count against the
+// LDS wait counter)
+typedef __attribute__((address_space(1))) u32x4 gu32x4;
+
+__device__ __forceinline__ f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// a *= s for an accumulator that lives in AGPRs.  Written as explicit AGPR reads and writes: a
+// plain vector multiply inside the loop made the compiler keep all 128 accumulator registers in
+// VGPRs (copying them to AGPRs around every MFMA) and spill.
+__device__ __forceinline__ void acc_scale(f32x16& a, float s) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float t, u;
+        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(t) : "a"(a[i]));
+        t *= s;
+        asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(u) : "v"(t));
+        a[i] = u;
+    }
+}
+
+// The larger of v over the wave's two 32-lane halves, in every lane (v_permlane32_swap: no LDS).
+__device__ __forceinline__ float max_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Entries (window + topk) a row of attn_prefill_kernel may have (longer rows go to attn_rows_kernel),
+// and the per-row tables: every entry, then a round of zero rows.
+constexpr int kWideMaxSel = 1536;
+constexpr int kWideEntries = kWideMaxSel + 64;
+
+__global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const AttnParams p) {
+    constexpr int H = 64, D = 512, R = 64, NT = 256;
+    constexpr int TE = 16 * 512;  // elements of one K tile
+    constexpr int RB = 2 * D;     // bytes of one stored row
+    constexpr int PF = CSA2_ATTN_WIDE_PF;
+    __shared__ __attribute__((aligned(16))) __bf16 tiles[3][2 * TE];
+    __shared__ f32x4 xch[2][4][4][64];  // by round parity, per wave: its partial S^T, register quad q of every lane
+    __shared__ __attribute__((aligned(16))) uint64_t eaddr[kWideEntries];  // entry e's row
+    __shared__ __attribute__((aligned(16))) float ebias[kWideEntries];     // 0, or -inf: not there
+    __shared__ float rope_cs[R];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int gk = lane >> 5, li = lane & 15, a16 = (lane >> 4) & 1;
+    const int hb = wave >> 1, half = wave & 1;
+    const int h = 32 * hb + (lane & 31);
+    RowCtx c;
+    row_ctx_init<D, CSA2_BF16, CSA2_BF16, false>(p, c, (int)blockIdx.x);
+    const int W = p.window;
+    const int n_sel = W + p.topk;
+    const int n_rounds = (n_sel + 31) / 32;
+    const int n_ent = 32 * (n_rounds + 1);
+
+    if (tid < R / 2) {
+        float cs, sn;
+        rope_angle(c.pos, p.inv_freq[tid], cs, sn);
+        rope_cs[2 * tid] = cs;
+        rope_cs[2 * tid + 1] = sn;
+    }
+    for (int e = tid; e < n_ent; e += NT) {
+        const uint8_t* a = g_zero_row;
+        bool valid = false;
+        if (e < W) {
+            valid = (uint32_t)(e - c.win_lo) < (uint32_t)(c.win_hi - c.win_lo);
+            if (valid) a = c.swa0 + (uint64_t)e * RB;
+        } else if (e < n_sel) {
+            const uint32_t id = (uint32_t)p.idx[(int64_t)c.r * p.topk + (e - W)];
+            valid = id < c.nv32;  // group-causal mask; -1 wraps to the top
+            if (valid) a = c.kv0 + (uint64_t)id * RB;
+        }
+        eaddr[e] = reinterpret_cast<uint64_t>(a);
+        ebias[e] = valid ? 0.f : kNegInf;
+    }
+    // round 2's set is read (as round -1, under zero probabilities) before anything is stored there
+    {
+        u32x4* z = reinterpret_cast<u32x4*>(tiles[2]) + tid;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) z[NT * k] = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    // q^T operand of k-step s: head h, dimensions 256 half + 16 s + 8 gk .. + 7
+    bf16x8 qf[16];
+    {
+        const uint16_t* q16 = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)c.r * H + h) * D + 256 * half + 8 * gk;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q16 + 16 * s));
+    }
+    float m = p.sink[h] * kLog2e;  // the sink is the initial state: max = sink, sum = 1
+    float l = gk == 0 ? 1.f : 0.f;
+    f32x16 acc[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[cb][i] = 0.f;
+
+    // Tile layout: row j of a K tile holds its 64 16-byte chunks with chunk c at c ^ sw(j), sw(j)
+    // the row's two 2-bit halves swapped.  The QK read (16 rows, one chunk) and the transposing PV
+    // read (4 consecutive rows x 4 consecutive chunks) then both touch 16 distinct chunk slots of
+    // the 64 banks; with c ^ j the PV read put its 4 rows on the same 4 slots.
+    auto sw = [](int j) { return ((j & 3) << 2) | (j >> 2); };
+    // K operand (QK): lane l reads entry l % 32 of the round (tile (l % 32) / 16, row jr), chunk
+    // 32 half + 2 s + gk; the lane-dependent part takes 8 values (s mod 8).
+    const int jr = lane & 15;
+    int ko[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) ko[b] = a16 * TE + jr * 512 + 256 * half + 8 * ((2 * b + gk) ^ sw(jr));
+    // V^T operand (PV, lds_col4): lane j of a 16-lane group names row 4 gk + j / 4 (+ 8 for the second
+    // read) of tile t, columns 256 half + 32 cb + 16 a16 + 4 (j % 4) .. + 3: chunk 32 half + 4 cb +
+    // 2 a16 + (j % 4) / 2, element 4 (j % 2) of it.
+    const int vr0 = 4 * gk + (li >> 2), vr1 = vr0 + 8;
+    const int vcb = 2 * a16 + ((li & 3) >> 1);
+    int vo0[4], vo1[4];  // by cb mod 4 (cb / 4 adds 16 chunks, beyond the XOR's 4 bits)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        vo0[b] = vr0 * 512 + 256 * half + 8 * ((4 * b + vcb) ^ sw(vr0)) + 4 * (li & 1);
+        vo1[b] = vr1 * 512 + 256 * half + 8 * ((4 * b + vcb) ^ sw(vr1)) + 4 * (li & 1);
+    }
+    // Gather: thread t takes tile t / 128 of a round, rows 4 ((t % 128) / 64 + 2 k) .. + 3 (k = 0, 1),
+    // 16-byte chunk t % 64 of each: one load instruction covers whole rows.
+    const int gt = tid >> 7, gx = tid & 63, gj = (tid >> 6) & 1;
+    const int xo = 16 * gx;
+    u32x4 raw[PF][2][4];
+    auto load_round = [&](int q, u32x4(&rw)[2][4]) {
+        q = q < n_rounds ? q : n_rounds;  // rounds past the end read the zero rows after the last
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const u64x2* ea = reinterpret_cast<const u64x2*>(eaddr + 32 * q + 16 * gt + 4 * (gj + 2 * k));
+            const u64x2 a01 = ea[0], a23 = ea[1];
+            rw[k][0] = *reinterpret_cast<const gu32x4*>(a01[0] + xo);
+            rw[k][1] = *reinterpret_cast<const gu32x4*>(a01[1] + xo);
+            rw[k][2] = *reinterpret_cast<const gu32x4*>(a23[0] + xo);
+            rw[k][3] = *reinterpret_cast<const gu32x4*>(a23[1] + xo);
+        }
+    };
+    auto store_round = [&](int set, const u32x4(&rw)[2][4]) {
+        __bf16* Kt = tiles[set] + gt * TE;
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = 4 * (gj + 2 * k) + i;
+                *reinterpret_cast<u32x4*>(Kt + j * 512 + 8 * (gx ^ sw(j))) = rw[k][i];
+            }
+    };
+
+    __syncthreads();  // row addresses, biases, rope table and the zeroed set visible
+    load_round(0, raw[0]);
+    store_round(0, raw[0]);
+#pragma unroll
+    for (int j = 1; j <= PF; ++j) load_round(j, raw[j % PF]);
+    float xp[16];  // the previous round's scores (scaled by scale_log2 when used): none yet
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xp[i] = kNegInf;
+    int s_cur = 0, s_next = 1, s_prev = 2;
+    __syncthreads();
+    for (int rd0 = 0; rd0 < n_rounds; rd0 += PF) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+        const int rd = rd0 + j;
+        if (rd >= n_rounds) break;  // the same in every wave
+        const __bf16* set = tiles[s_cur];
+        // (1) QK of this round over the wave's 256 dimensions (one accumulation chain, started at the
+        // entries' bias: 0, or -inf for entries that are not there -- both waves of the pair add it, and
+        // -inf + -inf = -inf) ...
+        f32x16 sc;
+        {
+            const f32x4* eb = reinterpret_cast<const f32x4*>(ebias + 32 * rd + 4 * gk);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 b = eb[2 * q];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sc[4 * q + e] = b[e];
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+            sc = mma32(lds_frag8<__bf16>(set + ko[s & 7] + 128 * (s >> 3)), qf[s], sc);
+        // ... the next round's tiles into their set, and loads PF rounds ahead ...
+        store_round(s_next, raw[(j + 1) % PF]);
+        load_round(rd + 1 + PF, raw[(j + 1) % PF]);
+        // ... and the previous round's probabilities (x - m_use <= 8; -inf -> 0)
+        const float m_use = (m == kNegInf) ? 0.f : m;
+        float pr[16];
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(xp[i], p.scale_log2, -m_use));
+            psum += pr[i];
+        }
+        l += psum;
+        bf16x8 pb[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            pb[t] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(pr[8 * t], pr[8 * t + 1]),
+                                                     pack_bf16x2(pr[8 * t + 2], pr[8 * t + 3]),
+                                                     pack_bf16x2(pr[8 * t + 4], pr[8 * t + 5]),
+                                                     pack_bf16x2(pr[8 * t + 6], pr[8 * t + 7])});
+        // ... and PV of the previous round over the wave's 256 columns (its tiles and probabilities are
+        // ready, so it needs no exchange)
+        {
+            const __bf16* pset = tiles[s_prev];
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const __bf16* Kt = pset + t * TE + 128 * (cb >> 2);
+                    const u32x2 v0 = lds_col4(Kt + vo0[cb & 3]), v1 = lds_col4(Kt + vo1[cb & 3]);
+                    acc[cb] = mma32(__builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y}), pb[t], acc[cb]);
+                }
+            }
+        }
+        // (2) the exchange of partial scores
+        f32x16 st = sc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xch[rd & 1][wave][q][lane] = f32x4{st[4 * q], st[4 * q + 1], st[4 * q + 2], st[4 * q + 3]};
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 o = xch[rd & 1][wave ^ 1][q][lane];
+            st[4 * q] += o[0];
+            st[4 * q + 1] += o[1];
+            st[4 * q + 2] += o[2];
+            st[4 * q + 3] += o[3];
+        }
+        // (3) the running max of this round's scores (register i: entry 32 rd + 8 (i / 4) + 4 gk + i % 4)
+        // over both halves of the wave, in log2 units (scale_log2 > 0, so scaling commutes with the max)
+        float tmax = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
+#pragma unroll
+        for (int i = 4; i < 16; i += 4) tmax = fmaxf(tmax, fmaxf(fmaxf(st[i], st[i + 1]), fmaxf(st[i + 2], st[i + 3])));
+        tmax = max_halves(tmax) * p.scale_log2;
+        // Lazy rescaling: m is only a reference point, moved (with acc and l rescaled) only when a
+        // head's scores exceed it by more than 2^8; the probabilities then stay below 256.  acc
+        // here holds every round up to the previous one, whose probabilities used the old m.
+        const uint64_t need_rescale = __ballot(tmax > m + 8.f);
+        if (__builtin_expect(__builtin_amdgcn_readfirstlane((uint32_t)(need_rescale | (need_rescale >> 32))) != 0u, 0)) {
+            const float m_new = fmaxf(m, tmax);
+            const float alpha = exp2f(m - m_new);  // 0 when m was -inf
+            l *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) acc_scale(acc[cb], alpha);
+            m = m_new;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xp[i] = st[i];
+        const int s_old = s_prev;
+        s_prev = s_cur;
+        s_cur = s_next;
+        s_next = s_old;
+    }
+    }
+    // the last round's probabilities and PV
+    {
+        const float m_use = (m == kNegInf) ? 0.f : m;
+        float pr[16];
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(xp[i], p.scale_log2, -m_use));
+            psum += pr[i];
+        }
+        l += psum;
+        bf16x8 pb[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            pb[t] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(pr[8 * t], pr[8 * t + 1]),
+                                                     pack_bf16x2(pr[8 * t + 2], pr[8 * t + 3]),
+                                                     pack_bf16x2(pr[8 * t + 4], pr[8 * t + 5]),
+                                                     pack_bf16x2(pr[8 * t + 6], pr[8 * t + 7])});
+        const __bf16* pset = tiles[s_prev];
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const __bf16* Kt = pset + t * TE + 128 * (cb >> 2);
+                const u32x2 v0 = lds_col4(Kt + vo0[cb & 3]), v1 = lds_col4(Kt + vo1[cb & 3]);
+                acc[cb] = mma32(__builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y}), pb[t], acc[cb]);
+            }
+        }
+    }
+
+    l += shfl_xor(l, 32);
+    const float inv = 1.f / l;
+    const int64_t obase = ((int64_t)c.r * H + h) * D;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int d0 = 256 * half + 32 * cb + 8 * q + 4 * gk;
+            emit4<D, R, CSA2_BF16>(p.out, obase + d0, d0,
+                                   f32x4{acc[cb][4 * q], acc[cb][4 * q + 1], acc[cb][4 * q + 2], acc[cb][4 * q + 3]},
+                                   inv, rope_cs);
+        }
+    }
+}
+
 // Merge of the splits' partial states of one (row, 16-head group): the largest max, each state's
 // sum and values weighted by 2^(its max - that max), then normalisation, the inverse rotation of
 // the rope tail and the store.
@@ -999,6 +1338,9 @@ static hipError_t launch_attn(const AttnParams& p, bool decode, hipStream_t stre
         if (p.splits > 1)
             hipLaunchKernelGGL((attn_merge_kernel<H, D, R, OT>), dim3((unsigned)(p.rows * NHG * 4)), dim3(256), 0,
                                stream, p);
+    } else if (H == 64 && D == 512 && KVT == CSA2_BF16 && SWT == CSA2_BF16 && CSA2_ATTN_PREFILL_WIDE &&
+               p.window + p.topk <= kWideMaxSel) {
+        hipLaunchKernelGGL(attn_prefill_kernel, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
     } else {
         constexpr int NT = 64 * NHG * DS;
         hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, false, DS, 1>), dim3((unsigned)p.rows),

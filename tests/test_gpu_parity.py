@@ -176,11 +176,15 @@ def test_decode_split_entries(base, splits):
     print(f"[splits] {base} {splits}: max_abs {e:.3e}")
 
 
-def test_injected_indices_and_masks():
-    # -1 padding, duplicates, rows the group-causal mask hides, far out-of-range rows
-    cfg = SMALL["lowp_small"]
+@pytest.mark.parametrize("base", ["lowp_small", "prefill_small"])
+def test_injected_indices_and_masks(base):
+    """-1 padding, duplicates, rows the group-causal mask hides, far out-of-range rows; for decode and
+    for prefill (where the prefill kernel turns them into zero-row addresses and -inf score biases)."""
+    cfg = SMALL[base]
+    if cfg.phase == "prefill":
+        cfg = cfg.replace(reuse_layers=0)
     x = make_inputs(cfg, 3, device="cuda")
-    B, k = cfg.batch, cfg.topk
+    B, k = cfg.q_tokens, cfg.topk
     g = torch.Generator().manual_seed(0)
     idx = torch.randint(0, cfg.n_main_rows, (B, k), generator=g, dtype=torch.int32)
     idx[:, 0:16] = -1
@@ -188,20 +192,26 @@ def test_injected_indices_and_masks():
     idx[:, 48] = cfg.n_main_rows + 5                  # beyond the plane: masked (never read)
     idx[:, 49] = 2 ** 31 - 1
     idx[:, 50] = -7
+    idx[1, :] = -1                                    # a row with no selected entry at all
     idx = idx.cuda()
     out = gpu_attention(cfg, x, idx)
-    ref = oracle_attention(cfg, x, idx.cpu().numpy(), np.arange(B))
-    assert_close(out, ref, BF16_ATOL, BF16_RTOL, "injected indices")
+    rows = np.unique(np.linspace(0, B - 1, min(B, 24)).astype(int))
+    ref = oracle_attention(cfg, x, idx.cpu().numpy()[rows], rows)
+    assert_close(out[torch.from_numpy(rows).cuda()], ref, BF16_ATOL, BF16_RTOL, f"injected indices {base}")
 
 
-def test_sink_minus_inf():
-    cfg = SMALL["full_decode_small_unit"]
+@pytest.mark.parametrize("base", ["full_decode_small_unit", "prefill_small"])
+def test_sink_minus_inf(base):
+    cfg = SMALL[base]
+    if cfg.phase == "prefill":
+        cfg = cfg.replace(reuse_layers=0)
     x = make_inputs(cfg, 4, device="cuda")
     x["layers"][0]["sink"] = torch.full_like(x["layers"][0]["sink"], -math.inf)
     idx = gpu_topk(cfg, x, gpu_scores(cfg, x))
     out = gpu_attention(cfg, x, idx)
-    ref = oracle_attention(cfg, x, idx.cpu().numpy(), np.arange(cfg.q_tokens))
-    assert_close(out, ref, BF16_ATOL, BF16_RTOL, "sink=-inf")
+    rows = np.unique(np.linspace(0, cfg.q_tokens - 1, min(cfg.q_tokens, 24)).astype(int))
+    ref = oracle_attention(cfg, x, idx.cpu().numpy()[rows], rows)
+    assert_close(out[torch.from_numpy(rows).cuda()], ref, BF16_ATOL, BF16_RTOL, f"sink=-inf {base}")
 
 
 def test_topk_crafted_scores():
