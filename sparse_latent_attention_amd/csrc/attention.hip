@@ -704,9 +704,9 @@ __device__ __forceinline__ void tile_pair_compute(const __bf16* Kt0, const __bf1
     }
 }
 
-// Normalises, rotates the rope tail back and stores 4 consecutive elements.
-template <int D, int R, int OT>
-__device__ __forceinline__ void emit4(void* out, int64_t off, int d0, f32x4 a, float inv, const float* rope_cs) {
+// Normalises 4 consecutive elements (columns d0 .. d0 + 3) and rotates the rope tail back.
+template <int D, int R>
+__device__ __forceinline__ f32x4 finish4(int d0, f32x4 a, float inv, const float* rope_cs) {
     float o0 = a[0] * inv, o1 = a[1] * inv, o2 = a[2] * inv, o3 = a[3] * inv;
     if (d0 >= D - R) {
         const int i0 = (d0 - (D - R)) / 2;
@@ -716,7 +716,14 @@ __device__ __forceinline__ void emit4(void* out, int64_t off, int d0, f32x4 a, f
         const float b2 = o2 * c1 + o3 * s1, b3 = o3 * c1 - o2 * s1;
         o0 = b0; o1 = b1; o2 = b2; o3 = b3;
     }
-    store_out4<OT>(out, off, o0, o1, o2, o3);
+    return f32x4{o0, o1, o2, o3};
+}
+
+// ... and stores them.
+template <int D, int R, int OT>
+__device__ __forceinline__ void emit4(void* out, int64_t off, int d0, f32x4 a, float inv, const float* rope_cs) {
+    const f32x4 o = finish4<D, R>(d0, a, inv, rope_cs);
+    store_out4<OT>(out, off, o[0], o[1], o[2], o[3]);
 }
 
 }  // namespace
@@ -1026,19 +1033,34 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const AttnParams p
         rope_cs[2 * tid] = cs;
         rope_cs[2 * tid + 1] = sn;
     }
-    for (int e = tid; e < n_ent; e += NT) {
-        const uint8_t* a = g_zero_row;
-        bool valid = false;
-        if (e < W) {
-            valid = (uint32_t)(e - c.win_lo) < (uint32_t)(c.win_hi - c.win_lo);
-            if (valid) a = c.swa0 + (uint64_t)e * RB;
-        } else if (e < n_sel) {
-            const uint32_t id = (uint32_t)p.idx[(int64_t)c.r * p.topk + (e - W)];
-            valid = id < c.nv32;  // group-causal mask; -1 wraps to the top
-            if (valid) a = c.kv0 + (uint64_t)id * RB;
+    // (every selected index is loaded first, with clamped positions, so the loads are in flight
+    // together rather than one round trip per entry)
+    constexpr int KE = (kWideEntries + NT - 1) / NT;
+    uint32_t ids[KE];
+    if (p.topk > 0) {
+        const int32_t* idr = p.idx + (int64_t)c.r * p.topk;
+#pragma unroll
+        for (int k = 0; k < KE; ++k) {
+            const int j = tid + NT * k - W;
+            ids[k] = (uint32_t)idr[j < 0 ? 0 : (j < p.topk ? j : p.topk - 1)];
         }
-        eaddr[e] = reinterpret_cast<uint64_t>(a);
-        ebias[e] = valid ? 0.f : kNegInf;
+    }
+#pragma unroll
+    for (int k = 0; k < KE; ++k) {
+        const int e = tid + NT * k;
+        if (e < n_ent) {
+            const uint8_t* a = g_zero_row;
+            bool valid = false;
+            if (e < W) {
+                valid = (uint32_t)(e - c.win_lo) < (uint32_t)(c.win_hi - c.win_lo);
+                if (valid) a = c.swa0 + (uint64_t)e * RB;
+            } else if (e < n_sel) {
+                valid = ids[k] < c.nv32;  // group-causal mask; -1 wraps to the top
+                if (valid) a = c.kv0 + (uint64_t)ids[k] * RB;
+            }
+            eaddr[e] = reinterpret_cast<uint64_t>(a);
+            ebias[e] = valid ? 0.f : kNegInf;
+        }
     }
     // round 2's set is read (as round -1, under zero probabilities) before anything is stored there
     {
@@ -1247,17 +1269,34 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const AttnParams p
         }
     }
 
+    // The output goes through LDS so that it leaves as whole rows: a lane holds 4-column pieces of
+    // one head, so storing them directly wrote 64 scattered 8-byte pieces per instruction.  The two
+    // tile sets the last rounds no longer read (all waves passed the last barrier since their last
+    // use) take the wave's 32 heads x 256 columns, 16-byte chunk j of head row hh at j ^ hh.
     l += shfl_xor(l, 32);
     const float inv = 1.f / l;
-    const int64_t obase = ((int64_t)c.r * H + h) * D;
+    {
+        uint16_t* ot = reinterpret_cast<uint16_t*>(tiles[(wave >> 1) ? s_next : s_cur]) + (wave & 1) * (32 * 256);
+        const int hh = lane & 31;
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
+        for (int cb = 0; cb < 8; ++cb) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int d0 = 256 * half + 32 * cb + 8 * q + 4 * gk;
-            emit4<D, R, CSA2_BF16>(p.out, obase + d0, d0,
-                                   f32x4{acc[cb][4 * q], acc[cb][4 * q + 1], acc[cb][4 * q + 2], acc[cb][4 * q + 3]},
-                                   inv, rope_cs);
+            for (int q = 0; q < 4; ++q) {
+                const int c0 = 32 * cb + 8 * q + 4 * gk;  // column within the wave's half
+                const f32x4 o = finish4<D, R>(256 * half + c0, f32x4{acc[cb][4 * q], acc[cb][4 * q + 1],
+                                                                     acc[cb][4 * q + 2], acc[cb][4 * q + 3]},
+                                              inv, rope_cs);
+                *reinterpret_cast<u32x2*>(ot + hh * 256 + 8 * ((c0 >> 3) ^ hh) + (c0 & 7)) =
+                    u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            }
+        }
+        // each instruction: heads 2 j and 2 j + 1 (lanes 0-31 and 32-63), 16 bytes per lane
+        uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + ((int64_t)c.r * H + 32 * hb) * D + 256 * half;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int hr = 2 * j + gk, ch = lane & 31;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ot + hr * 256 + 8 * (ch ^ hr));
+            *reinterpret_cast<u32x4*>(orow + (int64_t)hr * D + 8 * ch) = v;
         }
     }
 }
