@@ -1001,67 +1001,85 @@ __device__ __forceinline__ float max_halves(float v) {
 }
 
 // Entries (window + topk) a row of attn_prefill_kernel may have (longer rows go to attn_rows_kernel),
-// and the per-row tables: every entry, then a round of zero rows.
-constexpr int kWideMaxSel = 1536;
-constexpr int kWideEntries = kWideMaxSel + 64;
+// and a row's tables: every entry, then one round of zero rows.  Two rows' tables are kept: the
+// current row's and the next one's, built while the current row is computed.
+constexpr int kWideMaxSel = 1024;
+constexpr int kWideEntries = kWideMaxSel + 32;
 
-__global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const AttnParams p) {
+// A row's geometry for the wide kernel's tables.
+__device__ __forceinline__ void wide_row_setup(const AttnParams& p, int r, RowCtx& c) {
+    row_ctx_init<512, CSA2_BF16, CSA2_BF16, false>(p, c, r);
+}
+
+// Workgroup b takes the contiguous rows [row0, row0 + nk) (consecutive rows share most of their
+// window rows, which then stay in this CU's caches).  The rounds of all its rows form one stream:
+// the gather runs PF + 1 rounds ahead across row boundaries, and at a boundary the finished row's
+// output is normalised and stored while the next row's first rounds are computed.  A row's tables
+// and rope angles are built during the row before it; its query is loaded at the end of that row.
+__global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const AttnParams p, int rows_per_wg) {
     constexpr int H = 64, D = 512, R = 64, NT = 256;
     constexpr int TE = 16 * 512;  // elements of one K tile
     constexpr int RB = 2 * D;     // bytes of one stored row
     constexpr int PF = CSA2_ATTN_WIDE_PF;
+    constexpr int KE = (kWideEntries + NT - 1) / NT;
     __shared__ __attribute__((aligned(16))) __bf16 tiles[3][2 * TE];
     __shared__ f32x4 xch[2][4][4][64];  // by round parity, per wave: its partial S^T, register quad q of every lane
-    __shared__ __attribute__((aligned(16))) uint64_t eaddr[kWideEntries];  // entry e's row
-    __shared__ __attribute__((aligned(16))) float ebias[kWideEntries];     // 0, or -inf: not there
-    __shared__ float rope_cs[R];
+    __shared__ __attribute__((aligned(16))) uint64_t eaddr[2][kWideEntries];  // by row parity: entry e's row
+    __shared__ __attribute__((aligned(16))) float ebias[2][kWideEntries];     // 0, or -inf: not there
+    __shared__ float rope_cs[2][R];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int gk = lane >> 5, li = lane & 15, a16 = (lane >> 4) & 1;
     const int hb = wave >> 1, half = wave & 1;
     const int h = 32 * hb + (lane & 31);
-    RowCtx c;
-    row_ctx_init<D, CSA2_BF16, CSA2_BF16, false>(p, c, (int)blockIdx.x);
+    const int row0 = (int)blockIdx.x * rows_per_wg;
+    const int nk = p.rows - row0 < rows_per_wg ? p.rows - row0 : rows_per_wg;  // rows of this workgroup (>= 1)
     const int W = p.window;
     const int n_sel = W + p.topk;
-    const int n_rounds = (n_sel + 31) / 32;
-    const int n_ent = 32 * (n_rounds + 1);
+    const int n = (n_sel + 31) / 32;  // rounds per row
 
-    if (tid < R / 2) {
-        float cs, sn;
-        rope_angle(c.pos, p.inv_freq[tid], cs, sn);
-        rope_cs[2 * tid] = cs;
-        rope_cs[2 * tid + 1] = sn;
-    }
-    // (every selected index is loaded first, with clamped positions, so the loads are in flight
-    // together rather than one round trip per entry)
-    constexpr int KE = (kWideEntries + NT - 1) / NT;
+    // Table of row slot k: entry e's row address (the zero row where there is none) and score bias.
     uint32_t ids[KE];
-    if (p.topk > 0) {
-        const int32_t* idr = p.idx + (int64_t)c.r * p.topk;
+    auto load_ids = [&](int r) {
+        if (p.topk > 0) {
+            const int32_t* idr = p.idx + (int64_t)r * p.topk;
+#pragma unroll
+            for (int k = 0; k < KE; ++k) {
+                const int j = tid + NT * k - W;
+                ids[k] = (uint32_t)idr[j < 0 ? 0 : (j < p.topk ? j : p.topk - 1)];
+            }
+        }
+    };
+    auto build_tables = [&](const RowCtx& rc, int buf) {
 #pragma unroll
         for (int k = 0; k < KE; ++k) {
-            const int j = tid + NT * k - W;
-            ids[k] = (uint32_t)idr[j < 0 ? 0 : (j < p.topk ? j : p.topk - 1)];
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < KE; ++k) {
-        const int e = tid + NT * k;
-        if (e < n_ent) {
-            const uint8_t* a = g_zero_row;
-            bool valid = false;
-            if (e < W) {
-                valid = (uint32_t)(e - c.win_lo) < (uint32_t)(c.win_hi - c.win_lo);
-                if (valid) a = c.swa0 + (uint64_t)e * RB;
-            } else if (e < n_sel) {
-                valid = ids[k] < c.nv32;  // group-causal mask; -1 wraps to the top
-                if (valid) a = c.kv0 + (uint64_t)ids[k] * RB;
+            const int e = tid + NT * k;
+            if (e < 32 * (n + 1)) {
+                const uint8_t* a = g_zero_row;
+                bool valid = false;
+                if (e < W) {
+                    valid = (uint32_t)(e - rc.win_lo) < (uint32_t)(rc.win_hi - rc.win_lo);
+                    if (valid) a = rc.swa0 + (uint64_t)e * RB;
+                } else if (e < n_sel) {
+                    valid = ids[k] < rc.nv32;  // group-causal mask; -1 wraps to the top
+                    if (valid) a = rc.kv0 + (uint64_t)ids[k] * RB;
+                }
+                eaddr[buf][e] = reinterpret_cast<uint64_t>(a);
+                ebias[buf][e] = valid ? 0.f : kNegInf;
             }
-            eaddr[e] = reinterpret_cast<uint64_t>(a);
-            ebias[e] = valid ? 0.f : kNegInf;
         }
-    }
+        if (tid < R / 2) {
+            float cs, sn;
+            rope_angle(rc.pos, p.inv_freq[tid], cs, sn);
+            rope_cs[buf][2 * tid] = cs;
+            rope_cs[buf][2 * tid + 1] = sn;
+        }
+    };
+
+    RowCtx c;
+    wide_row_setup(p, row0, c);
+    load_ids(row0);
+    build_tables(c, 0);
     // round 2's set is read (as round -1, under zero probabilities) before anything is stored there
     {
         u32x4* z = reinterpret_cast<u32x4*>(tiles[2]) + tid;
@@ -1071,12 +1089,14 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const AttnParams p
 
     // q^T operand of k-step s: head h, dimensions 256 half + 16 s + 8 gk .. + 7
     bf16x8 qf[16];
-    {
-        const uint16_t* q16 = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)c.r * H + h) * D + 256 * half + 8 * gk;
+    auto load_q = [&](int r) {
+        const uint16_t* q16 = reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)r * H + h) * D + 256 * half + 8 * gk;
 #pragma unroll
         for (int s = 0; s < 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q16 + 16 * s));
-    }
-    float m = p.sink[h] * kLog2e;  // the sink is the initial state: max = sink, sum = 1
+    };
+    load_q(row0);
+    const float sink_m = p.sink[h] * kLog2e;  // the sink is each row's initial state: max = sink, sum = 1
+    float m = sink_m;
     float l = gk == 0 ? 1.f : 0.f;
     f32x16 acc[8];
 #pragma unroll
@@ -1111,11 +1131,12 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const AttnParams p
     const int gt = tid >> 7, gx = tid & 63, gj = (tid >> 6) & 1;
     const int xo = 16 * gx;
     u32x4 raw[PF][2][4];
-    auto load_round = [&](int q, u32x4(&rw)[2][4]) {
-        q = q < n_rounds ? q : n_rounds;  // rounds past the end read the zero rows after the last
+    // the round (lk, lrd) of row slot lk; past the last row: the last row's round of zero rows
+    auto load_round = [&](int lk, int lrd, u32x4(&rw)[2][4]) {
+        const int base = lk < nk ? (lk & 1) * kWideEntries + 32 * lrd : ((nk - 1) & 1) * kWideEntries + 32 * n;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const u64x2* ea = reinterpret_cast<const u64x2*>(eaddr + 32 * q + 16 * gt + 4 * (gj + 2 * k));
+            const u64x2* ea = reinterpret_cast<const u64x2*>(&eaddr[0][0] + base + 16 * gt + 4 * (gj + 2 * k));
             const u64x2 a01 = ea[0], a23 = ea[1];
             rw[k][0] = *reinterpret_cast<const gu32x4*>(a01[0] + xo);
             rw[k][1] = *reinterpret_cast<const gu32x4*>(a01[1] + xo);
@@ -1133,29 +1154,60 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const AttnParams p
                 *reinterpret_cast<u32x4*>(Kt + j * 512 + 8 * (gx ^ sw(j))) = rw[k][i];
             }
     };
+    // Normalises, rotates back and stores the finished row of slot k (its output rows leave as 8-byte
+    // pieces; done once per row, in the middle of the stream).
+    auto emit_row = [&](int k, float lsum) {
+        const float inv = 1.f / lsum;
+        const int64_t obase = ((int64_t)(row0 + k) * H + h) * D;
+        const float* rcs = rope_cs[k & 1];
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int d0 = 256 * half + 32 * cb + 8 * q + 4 * gk;
+                emit4<D, R, CSA2_BF16>(p.out, obase + d0, d0,
+                                       f32x4{acc[cb][4 * q], acc[cb][4 * q + 1], acc[cb][4 * q + 2], acc[cb][4 * q + 3]},
+                                       inv, rcs);
+            }
+        }
+    };
 
-    __syncthreads();  // row addresses, biases, rope table and the zeroed set visible
-    load_round(0, raw[0]);
+    __syncthreads();  // row 0's tables and rope angles, and the zeroed set, visible
+    int lk = 0, lrd = 0;  // the gather's next round
+    auto advance = [&](int& kk, int& rr) {
+        if (++rr == n) {
+            rr = 0;
+            ++kk;
+        }
+    };
+    load_round(lk, lrd, raw[0]);
+    advance(lk, lrd);
     store_round(0, raw[0]);
 #pragma unroll
-    for (int j = 1; j <= PF; ++j) load_round(j, raw[j % PF]);
+    for (int j = 1; j <= PF; ++j) {
+        load_round(lk, lrd, raw[j % PF]);
+        advance(lk, lrd);
+    }
     float xp[16];  // the previous round's scores (scaled by scale_log2 when used): none yet
 #pragma unroll
     for (int i = 0; i < 16; ++i) xp[i] = kNegInf;
     int s_cur = 0, s_next = 1, s_prev = 2;
+    RowCtx cn;  // the next row's geometry, while its tables are built
     __syncthreads();
-    for (int rd0 = 0; rd0 < n_rounds; rd0 += PF) {
+    const int total = nk * n;
+    int k = 0, rd = 0;  // this round: row slot k, round rd of that row
+    for (int g0 = 0; g0 < total; g0 += PF) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
-        const int rd = rd0 + j;
-        if (rd >= n_rounds) break;  // the same in every wave
+        const int g = g0 + j;
+        if (g >= total) break;  // the same in every wave
         const __bf16* set = tiles[s_cur];
         // (1) QK of this round over the wave's 256 dimensions (one accumulation chain, started at the
         // entries' bias: 0, or -inf for entries that are not there -- both waves of the pair add it, and
         // -inf + -inf = -inf) ...
         f32x16 sc;
         {
-            const f32x4* eb = reinterpret_cast<const f32x4*>(ebias + 32 * rd + 4 * gk);
+            const f32x4* eb = reinterpret_cast<const f32x4*>(&ebias[k & 1][32 * rd + 4 * gk]);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x4 b = eb[2 * q];
@@ -1168,8 +1220,11 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const AttnParams p
             sc = mma32(lds_frag8<__bf16>(set + ko[s & 7] + 128 * (s >> 3)), qf[s], sc);
         // ... the next round's tiles into their set, and loads PF rounds ahead ...
         store_round(s_next, raw[(j + 1) % PF]);
-        load_round(rd + 1 + PF, raw[(j + 1) % PF]);
-        // ... and the previous round's probabilities (x - m_use <= 8; -inf -> 0)
+        load_round(lk, lrd, raw[(j + 1) % PF]);
+        advance(lk, lrd);
+        // ... and the previous round's probabilities (x - m_use <= 8; -inf -> 0) and PV (its tiles and
+        // probabilities are ready, so it needs no exchange; at a row boundary they are the last round
+        // of the row before, with its softmax state)
         const float m_use = (m == kNegInf) ? 0.f : m;
         float pr[16];
         float psum = 0.f;
@@ -1186,8 +1241,6 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const AttnParams p
                                                      pack_bf16x2(pr[8 * t + 2], pr[8 * t + 3]),
                                                      pack_bf16x2(pr[8 * t + 4], pr[8 * t + 5]),
                                                      pack_bf16x2(pr[8 * t + 6], pr[8 * t + 7])});
-        // ... and PV of the previous round over the wave's 256 columns (its tiles and probabilities are
-        // ready, so it needs no exchange)
         {
             const __bf16* pset = tiles[s_prev];
 #pragma unroll
@@ -1203,17 +1256,38 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const AttnParams p
         // (2) the exchange of partial scores
         f32x16 st = sc;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) xch[rd & 1][wave][q][lane] = f32x4{st[4 * q], st[4 * q + 1], st[4 * q + 2], st[4 * q + 3]};
+        for (int q = 0; q < 4; ++q) xch[g & 1][wave][q][lane] = f32x4{st[4 * q], st[4 * q + 1], st[4 * q + 2], st[4 * q + 3]};
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const f32x4 o = xch[rd & 1][wave ^ 1][q][lane];
+            const f32x4 o = xch[g & 1][wave ^ 1][q][lane];
             st[4 * q] += o[0];
             st[4 * q + 1] += o[1];
             st[4 * q + 2] += o[2];
             st[4 * q + 3] += o[3];
         }
-        // (3) the running max of this round's scores (register i: entry 32 rd + 8 (i / 4) + 4 gk + i % 4)
+        // (3) at a row boundary, the finished row leaves and the softmax state restarts at the sink
+        if (rd == 0 && k > 0) {
+            emit_row(k - 1, l + shfl_xor(l, 32));
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[cb][i] = 0.f;
+            m = sink_m;
+            l = gk == 0 ? 1.f : 0.f;
+        }
+        // The next row's tables: its indices are loaded in its predecessor's first round and written
+        // in the second, after that round's barrier (the buffer's last readers are two rounds back);
+        // the gather first reads them at least two barriers later.
+        if (k + 1 < nk) {
+            if (rd == 0) {
+                wide_row_setup(p, row0 + k + 1, cn);
+                load_ids(row0 + k + 1);
+            } else if (rd == 1) {
+                build_tables(cn, (k + 1) & 1);
+            }
+        }
+        // the running max of this round's scores (register i: entry 32 rd + 8 (i / 4) + 4 gk + i % 4)
         // over both halves of the wave, in log2 units (scale_log2 > 0, so scaling commutes with the max)
         float tmax = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
 #pragma unroll
@@ -1221,7 +1295,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const AttnParams p
         tmax = max_halves(tmax) * p.scale_log2;
         // Lazy rescaling: m is only a reference point, moved (with acc and l rescaled) only when a
         // head's scores exceed it by more than 2^8; the probabilities then stay below 256.  acc
-        // here holds every round up to the previous one, whose probabilities used the old m.
+        // here holds every round of the row up to the previous one, whose probabilities used the old m.
         const uint64_t need_rescale = __ballot(tmax > m + 8.f);
         if (__builtin_expect(__builtin_amdgcn_readfirstlane((uint32_t)(need_rescale | (need_rescale >> 32))) != 0u, 0)) {
             const float m_new = fmaxf(m, tmax);
@@ -1233,13 +1307,19 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const AttnParams p
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) xp[i] = st[i];
+        // the next row's query, once this row's last QK has used the current one
+        if (rd == n - 1 && k + 1 < nk) load_q(row0 + k + 1);
         const int s_old = s_prev;
         s_prev = s_cur;
         s_cur = s_next;
         s_next = s_old;
+        if (++rd == n) {
+            rd = 0;
+            ++k;
+        }
     }
     }
-    // the last round's probabilities and PV
+    // the last round's probabilities and PV, and the last row's output
     {
         const float m_use = (m == kNegInf) ? 0.f : m;
         float pr[16];
@@ -1268,37 +1348,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const AttnParams p
             }
         }
     }
-
-    // The output goes through LDS so that it leaves as whole rows: a lane holds 4-column pieces of
-    // one head, so storing them directly wrote 64 scattered 8-byte pieces per instruction.  The two
-    // tile sets the last rounds no longer read (all waves passed the last barrier since their last
-    // use) take the wave's 32 heads x 256 columns, 16-byte chunk j of head row hh at j ^ hh.
-    l += shfl_xor(l, 32);
-    const float inv = 1.f / l;
-    {
-        uint16_t* ot = reinterpret_cast<uint16_t*>(tiles[(wave >> 1) ? s_next : s_cur]) + (wave & 1) * (32 * 256);
-        const int hh = lane & 31;
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c0 = 32 * cb + 8 * q + 4 * gk;  // column within the wave's half
-                const f32x4 o = finish4<D, R>(256 * half + c0, f32x4{acc[cb][4 * q], acc[cb][4 * q + 1],
-                                                                     acc[cb][4 * q + 2], acc[cb][4 * q + 3]},
-                                              inv, rope_cs);
-                *reinterpret_cast<u32x2*>(ot + hh * 256 + 8 * ((c0 >> 3) ^ hh) + (c0 & 7)) =
-                    u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-            }
-        }
-        // each instruction: heads 2 j and 2 j + 1 (lanes 0-31 and 32-63), 16 bytes per lane
-        uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + ((int64_t)c.r * H + 32 * hb) * D + 256 * half;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int hr = 2 * j + gk, ch = lane & 31;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(ot + hr * 256 + 8 * (ch ^ hr));
-            *reinterpret_cast<u32x4*>(orow + (int64_t)hr * D + 8 * ch) = v;
-        }
-    }
+    emit_row(nk - 1, l + shfl_xor(l, 32));
 }
 
 // Merge of the splits' partial states of one (row, 16-head group): the largest max, each state's
@@ -1359,6 +1409,19 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnParams p) {
     }
 }
 
+// Compute units of the current device (cached per device).
+static int device_cu_count() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cached[dev] = v;
+    }
+    return cached[dev];
+}
+
 // ---------------------------------------------------------------------------
 template <int H, int D, int R, class CT, int QT, int KVT, int SWT, int OT>
 static hipError_t launch_attn(const AttnParams& p, bool decode, hipStream_t stream) {
@@ -1379,7 +1442,17 @@ static hipError_t launch_attn(const AttnParams& p, bool decode, hipStream_t stre
                                stream, p);
     } else if (H == 64 && D == 512 && KVT == CSA2_BF16 && SWT == CSA2_BF16 && CSA2_ATTN_PREFILL_WIDE &&
                p.window + p.topk <= kWideMaxSel) {
-        hipLaunchKernelGGL(attn_prefill_kernel, dim3((unsigned)p.rows), dim3(256), 0, stream, p);
+        // one workgroup per CU, each over a contiguous run of rows (the stream needs rows of at least
+        // PF + 4 rounds for its next-row tables; shorter rows get one workgroup each)
+        if (p.rows <= 0) return hipSuccess;
+        const int n_rounds = (p.window + p.topk + 31) / 32;
+        int per = 1;
+        if (n_rounds >= CSA2_ATTN_WIDE_PF + 4) {
+            const int cus = device_cu_count();
+            per = (p.rows + cus - 1) / cus;
+        }
+        const int grid = (p.rows + per - 1) / per;
+        hipLaunchKernelGGL(attn_prefill_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p, per);
     } else {
         constexpr int NT = 64 * NHG * DS;
         hipLaunchKernelGGL((attn_rows_kernel<H, D, R, CT, QT, KVT, SWT, OT, false, DS, 1>), dim3((unsigned)p.rows),

@@ -132,6 +132,24 @@ def test_attention_ragged_tile_counts(base, rows, window, topk):
     assert_close(out[torch.from_numpy(sample).cuda()], ref, BF16_ATOL, BF16_RTOL, f"{base} W={window} k={topk}")
 
 
+@pytest.mark.parametrize("rows,window,topk", [(517, 128, 512), (1000, 64, 128), (777, 16, 144)])
+def test_prefill_row_stream(rows, window, topk):
+    """Prefill rows streamed through one workgroup per CU (several consecutive rows each, the next
+    row's tables built and its first tiles gathered during the row before): row counts that leave the
+    last workgroup short, and rows of 20, 6 and 5 rounds.  Rows are sampled at every workgroup's
+    first and last row over the first workgroups, and at the end."""
+    cfg = SMALL["prefill_small"].replace(q_tokens=rows, context=2400, reuse_layers=0, window=window, topk=topk)
+    print(f"\n[row stream] rows={rows} W={window} k={topk}", flush=True)
+    x = make_inputs(cfg, 12, device="cuda")
+    idx = gpu_topk(cfg, x, gpu_scores(cfg, x))
+    out = gpu_attention(cfg, x, idx)
+    per = -(-rows // 256)
+    pick = sorted({r for b in range(0, 6) for r in (b * per, b * per + per - 1)} | {rows - 2, rows - 1})
+    pick = np.array([r for r in pick if 0 <= r < rows])
+    ref = oracle_attention(cfg, x, idx.cpu().numpy()[pick], pick)
+    assert_close(out[torch.from_numpy(pick).cuda()], ref, BF16_ATOL, BF16_RTOL, f"row stream {rows}")
+
+
 @pytest.mark.parametrize("window", [16, 48])
 @pytest.mark.parametrize("base,rows", [("full_decode_small", 5), ("full_decode_small", 300), ("lowp_small", 7),
                                        ("prefill_small", None)])
