@@ -9,34 +9,23 @@
 //
 // Shared design.  A query row's entry list is W SWA entries followed by topk
 // selected rows, walked in tiles of 16 entries (W and topk are multiples of 16,
-// so a tile comes from one source).  A tile is gathered once from HBM: each
-// thread owns "pairs" (4 rows x 8 contiguous elements; one wave load
-// instruction covers a whole row), decodes FP4/FP8 in registers, and stores
-// the tile twice into LDS -- row-major Kt[j][d] (the QK^T operand) and
-// Vt[j/4][d][j%4] (the PV operand, 4 entries of one column contiguous).  K == V,
-// so both copies come from one read.  A wave owns 16 heads: 16x16x32 MFMAs give
-// S^T[16 entries x 16 heads] = Kt . q^T with q in registers, an online softmax
-// updates the running max/sum per head, and out^T[d][h] += Vt^T . P^T with
-// 16x16x16 MFMAs; the S^T result layout is exactly the P^T operand layout, so
-// P never leaves registers.  The sink is the initial softmax state (max =
-// sink, sum = 1).  Invalid entries (absent SWA slots, -1 or out-of-range
-// indices, rows the group-causal mask hides) are zero-filled and get
-// probability 0.  The raw bytes of the next tile are loaded into registers
-// while the current tile is computed.
+// so a tile comes from one source).  A tile is gathered once from HBM (an
+// absent row is read from a zero row, so no load needs a branch), FP4/FP8 rows
+// are decoded in registers, and the tile is stored once into LDS, row-major
+// with XOR-swizzled 16-byte chunks.  QK^T reads it as the MFMA operand; PV
+// reads it through the gfx950 transposing LDS read, so no transposed copy is
+// written (K == V).  The score result layout of the QK MFMA is the probability
+// operand of the PV MFMA, so probabilities never leave registers.  The sink is
+// the initial softmax state (max = sink, sum = 1); invalid entries (absent SWA
+// slots, -1 or out-of-range indices, rows the group-causal mask hides) get
+// probability 0.
 //
-// For the 64-head shape a 16-head group has two waves: both compute the
-// group's scores and softmax state (identical) and each accumulates half of
-// the 512 output columns, which halves the accumulator registers so that two
-// waves fit on each SIMD.
-//
-// attn_rows_kernel runs both phases: one workgroup per query row (all 64
-// heads: each tile is gathered and decoded once for all of them), all waves on
-// the same tiles, two tiles per round (each half of the threads gathers one) in
-// two buffer sets, one barrier per round.  A decode batch has few rows, so
-// there each row's tiles are also split over S workgroups (one per CU for the
-// LDS, S = 256 / rows up to 8); each leaves its softmax state (max, sum,
-// unnormalised values) in a workspace and attn_merge_kernel combines the S
-// states, normalises and stores.
+// attn_rows_kernel (16x16 MFMAs; 16-head groups of two waves) serves decode
+// rows, whose entries are also split over S workgroups (each leaves its softmax
+// state; attn_merge_kernel combines them), and prefill rows outside the next
+// kernel's shape.  attn_prefill_kernel (32x32x16 MFMAs; four waves of 32 heads
+// per row, one per SIMD) serves prefill rows over BF16 planes: one workgroup per
+// CU streams a contiguous run of rows.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -336,7 +325,6 @@ __device__ __forceinline__ void raw_convert(const RawPair& raw, int i, Pack8<CT>
 
 constexpr int kMaxTiles = 192;  // (window + topk) / 16 at most (window <= 1024, topk <= 2048)
 constexpr int kMaxSplits = 8;   // decode workgroups per (row, head group) at most
-constexpr int kMaxTopk = 2048;
 // Rounds of tile loads in flight in attn_rows_kernel: two for prefill (measured 7 % faster than one
 // on the 4096-row chunk), one for decode (two were 1 us slower: a decode workgroup has few rounds).
 // Workgroups per row (head slices) of the 64-head shape: two (32 heads each, two workgroups per CU)
