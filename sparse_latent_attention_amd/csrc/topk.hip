@@ -24,8 +24,8 @@
 //     keys, i.e. heavy ties: the select reads the row from memory instead);
 //   * wide rows (the 1M-column decode): the row is cut into chunks handled by
 //     separate workgroups.  (1) each chunk adds its 12-bit histogram into a
-//     per-row global histogram; (2) one workgroup per row finds the bin b1 of
-//     the k-th largest key; (3) each chunk compacts, in column order, the
+//     per-row global histogram; (2) each chunk's workgroup finds from it the
+//     bin b1 of the k-th largest key and (3) compacts, in column order, the
 //     (key, column) pairs of its valid keys whose bin is >= b1 -- every key
 //     >= T is among them -- into its own slot range; (4) one workgroup per row
 //     runs the exact select over that short, still column-ordered list.  A
@@ -348,18 +348,16 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const TopkParams p,
         if (h[b]) atomicAdd(&g[b], h[b]);
 }
 
-// grid rows: bin of the k-th largest key (0 when every valid key is selected).
-// hist holds `parts` histograms per row ([rows, parts, 4096]); they are added
-// in order.
-__global__ __launch_bounds__(kThreads) void topk_threshold_kernel(const TopkParams p, const uint32_t* hist,
-                                                                  uint32_t* b1_out, int parts) {
+// Bin of row r's k-th largest key (0 when every valid key is selected), from
+// `parts` histograms of the row ([parts, 4096], added in order); every thread
+// of the workgroup gets it.
+__device__ __forceinline__ uint32_t row_threshold_bin(const TopkParams& p, const uint32_t* hist, int parts, Lds& s) {
     static_assert(4 * kThreads == 4096, "four bins per thread");
-    __shared__ Lds s;
-    const int r = blockIdx.x, t = threadIdx.x;
+    const int t = threadIdx.x;
     // Thread t adds bins t + 1024e (e < 4) over the parts, eight parts' loads in
     // flight at once (a part index past the end re-reads the last part, whose
     // values are then dropped).
-    const uint32_t* hr = hist + (int64_t)r * parts * 4096 + t;
+    const uint32_t* hr = hist + t;
     uint32_t acc[4] = {0u, 0u, 0u, 0u};
     for (int q0 = 0; q0 < parts; q0 += 8) {
         uint32_t v[8][4];
@@ -391,7 +389,16 @@ __global__ __launch_bounds__(kThreads) void topk_threshold_kernel(const TopkPara
         above += hv[b];
     }
     __syncthreads();
-    if (t == 0) b1_out[r] = s.sel[1] > need ? s.sel[0] : 0u;
+    return s.sel[1] > need ? s.sel[0] : 0u;
+}
+
+// grid rows: row_threshold_bin of each row into b1_out.
+__global__ __launch_bounds__(kThreads) void topk_threshold_kernel(const TopkParams p, const uint32_t* hist,
+                                                                  uint32_t* b1_out, int parts) {
+    __shared__ Lds s;
+    const int r = blockIdx.x;
+    const uint32_t b1 = row_threshold_bin(p, hist + (int64_t)r * parts * 4096, parts, s);
+    if (threadIdx.x == 0) b1_out[r] = b1;
 }
 
 // grid (nseg, rows): ordered compaction of the chunk's keys with bin >= b1.
@@ -607,15 +614,19 @@ __global__ __launch_bounds__(kThreads) void topk_regs_kernel(const TopkParams p)
     select_core(lsrc, p, r, s, (int)b1, above);
 }
 
+// Each workgroup first finds its row's threshold bin b1 from the row's histogram
+// (the same for every segment of the row; this spares a launch between the
+// histogram and the filter).
 template <int SRC>
-__global__ __launch_bounds__(kThreads) void topk_filter_kernel(const TopkParams p, const uint32_t* b1_in,
+__global__ __launch_bounds__(kThreads) void topk_filter_kernel(const TopkParams p, const uint32_t* hist,
                                                                uint32_t* cand_keys, int32_t* cand_cols,
                                                                uint32_t* seg_count, int chunk, int nseg) {
+    __shared__ Lds s;
     __shared__ uint32_t cnt[2][kWaves];
     const int r = blockIdx.y, seg = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const RowSrc<SRC> src = row_src<SRC>(p, r);
-    const uint32_t b1 = b1_in[r];
+    const uint32_t b1 = row_threshold_bin(p, hist + (int64_t)r * 4096, 1, s);
     const int64_t base = ((int64_t)r * nseg + seg) * kCap;
     const int c0 = seg * chunk;
     const int c1 = (c0 + chunk < src.n) ? c0 + chunk : src.n;
@@ -759,7 +770,7 @@ size_t topk_workspace_bytes(int rows, int64_t width) {
     int chunk, nseg;
     topk_plan(rows, width, chunk, nseg, kSweep);
     if (nseg == 0) return 0;
-    return align256((size_t)rows * 4096 * 4) + align256((size_t)rows * 4) + align256((size_t)rows * nseg * 4) +
+    return align256((size_t)rows * 4096 * 4) + align256((size_t)rows * nseg * 4) +
            2 * align256((size_t)rows * nseg * kCap * 4);
 }
 
@@ -778,8 +789,6 @@ static hipError_t launch_topk_src(const TopkParams& p, int rows, void* ws, hipSt
     char* w = reinterpret_cast<char*>(ws);
     uint32_t* hist = reinterpret_cast<uint32_t*>(w);
     w += align256((size_t)rows * 4096 * 4);
-    uint32_t* b1 = reinterpret_cast<uint32_t*>(w);
-    w += align256((size_t)rows * 4);
     uint32_t* seg_count = reinterpret_cast<uint32_t*>(w);
     w += align256((size_t)rows * nseg * 4);
     uint32_t* keys = reinterpret_cast<uint32_t*>(w);
@@ -795,8 +804,7 @@ static hipError_t launch_topk_src(const TopkParams& p, int rows, void* ws, hipSt
                            hist, chunk);
         h = hist;
     }
-    hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, h, b1, 1);
-    hipLaunchKernelGGL(topk_filter_kernel<SRC>, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0, stream, p, b1,
+    hipLaunchKernelGGL(topk_filter_kernel<SRC>, dim3((unsigned)nseg, (unsigned)rows), dim3(kThreads), 0, stream, p, h,
                        keys, cols, seg_count, chunk, nseg);
     hipLaunchKernelGGL(topk_final_kernel<SRC>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p, keys, cols,
                        seg_count, nseg, kCap);
