@@ -55,7 +55,7 @@ def _unique_plane_rows(base, rows_read):
     return int(torch.unique(torch.cat(seen)).numel()) if seen else 0
 
 
-def algorithmic_work(cfg, x, idx_host=None, score_free=False):
+def algorithmic_work(cfg, x, idx_host=None, score_free=False, bk_bytes=4):
     """Per kernel of one step: the bytes it must move at least once (every distinct input byte read
     once, every output byte written once) and the multiply-add flops it must do.
 
@@ -85,13 +85,14 @@ def algorithmic_work(cfg, x, idx_host=None, score_free=False):
         extra = 0
     nbm = -(-cfg.width // cfg.block_rows) if cfg.pool_blocks else 0
     if score_free:
-        # scores stay on chip: only the 8-column block keys are written
+        # scores stay on chip: only the 8-column block keys are written (bk_bytes each: 4, or 2 when
+        # only their top 16 bits are kept)
         nbk = -(-cfg.width // 8)
-        idx_bytes = unique_rows * idx_row + qI + rows * nbk * 4
+        idx_bytes = unique_rows * idx_row + qI + rows * nbk * bk_bytes
         nbm = nbk if cfg.pool_blocks else 0  # the pool ranks the same block keys
         # the select reads the block keys (re-scored candidate rows and the second look at the block
         # keys are not counted: they are extra work of this route, not bytes the result needs)
-        topk_bytes = rows * nbk * 4 + rows * cfg.topk * 4
+        topk_bytes = rows * nbk * bk_bytes + rows * cfg.topk * 4
     else:
         idx_bytes = unique_rows * idx_row + qI + extra + rows * cfg.width * 4 + rows * nbm * 4
         topk_bytes = rows * cfg.width * 4 + rows * cfg.topk * 4 + extra
@@ -349,7 +350,9 @@ def main():
         ms_step = wall * 1e3 / args.steps
     kern_ms = {n: sum(a.elapsed_time(b) for a, b in evs[n]) / args.steps for n in names}
 
-    work = algorithmic_work(cfg, x, step_calls.idx.cpu() if cfg.phase == "prefill" else None, step_calls.score_free)
+    bk = step_calls.block_keys
+    work = algorithmic_work(cfg, x, step_calls.idx.cpu() if cfg.phase == "prefill" else None, step_calls.score_free,
+                            4 if bk is None else bk.element_size())
     dominant = max(names, key=lambda n: kern_ms[n])
     roofline = roofline_of(work[dominant], kern_ms[dominant])
     roofline.update({"kernel": dominant, "traffic": measured_traffic(dominant, cfg.name),

@@ -135,9 +135,17 @@ const char* csa2_status_string(int32_t status);
  * may then read row_base[0] only and stage each key tile once for several
  * query rows (BF16 planes of 64 x 128 without key_hist or block_max); the
  * scores are bit-identical to those of the same call without the flag.
+ *
+ * CSA2_INDEX_BLOCK_KEYS16 (score-free mode over FP8 or MXFP4 planes, not with
+ * CSA2_INDEX_SHARED_PLANE): block_keys holds uint16_t entries, the top 16 bits
+ * of each block key, which are all the select reads of them (it ranks blocks
+ * by the keys' top 12 bits); half the bytes of the 32-bit keys.  The same flag
+ * must then be given to csa2_topk_rescore.  Such keys cannot feed
+ * csa2_candidate_pool, which ranks blocks by the full key.
  * Other bits must be 0.
  */
 #define CSA2_INDEX_SHARED_PLANE 1
+#define CSA2_INDEX_BLOCK_KEYS16 2
 typedef struct csa2_index_args {
     uint32_t struct_size;       /* sizeof(csa2_index_args) */
     int32_t mode;               /* CSA2_MODE_FULL | CSA2_MODE_REINDEX */
@@ -150,7 +158,7 @@ typedef struct csa2_index_args {
     int32_t n_blocks;           /* REINDEX: candidate blocks per row (ignored for FULL) */
     int32_t block_rows;         /* REINDEX: rows per candidate block, 1..64.  FULL with block_max:
                                  * rows per pooled block, a power of two in 4..64.  Else ignored. */
-    int32_t flags;              /* CSA2_INDEX_SHARED_PLANE or 0 */
+    int32_t flags;              /* CSA2_INDEX_SHARED_PLANE, CSA2_INDEX_BLOCK_KEYS16, or 0 */
     int64_t width;              /* columns per score row (FULL: >= every n_visible) */
     const void* q;              /* [rows, heads, dim] */
     const float* w;             /* [rows, heads] effective head weights */
@@ -177,7 +185,9 @@ typedef struct csa2_index_args {
                                  * visible row ((n_visible - 1) / block_rows) gets +inf; blocks with
                                  * no visible column get -inf.  Written in the same pass as the
                                  * scores (no second read of them). */
-    uint32_t* block_keys;       /* score-free mode only (scores == NULL), out: [rows, ceil(width / 8)].
+    uint32_t* block_keys;       /* score-free mode only (scores == NULL), out: [rows, ceil(width / 8)]
+                                 * (uint16_t entries, the keys' top 16 bits, with
+                                 * CSA2_INDEX_BLOCK_KEYS16).
                                  * Entry b holds the largest key of the valid columns 8b .. 8b+7,
                                  * or 0 when none is valid; a column's key is its order key (as for
                                  * key_hist), except that a NaN score counts as 0x007FFFFE, just

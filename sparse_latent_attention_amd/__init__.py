@@ -253,9 +253,13 @@ def _index_args(q, w, k, row_base, pos, ratio, scale, scores, width, k_scale, ca
             raise ValueError(f"csa2.indexer_score: block_max must be [rows, {nb}]")
         a.block_rows = int(block_rows)
     if block_keys is not None:
-        _need(block_keys, torch.int32, "block_keys")
+        # int32: the full 32-bit block keys; int16: their top 16 bits (INDEX_BLOCK_KEYS16)
+        if block_keys.dtype not in (torch.int32, torch.int16):
+            raise ValueError("csa2: block_keys must be int32 or int16")
         if tuple(block_keys.shape) != (rows, -(-a.width // 8)):
-            raise ValueError("csa2.indexer_score: block_keys must be int32 [rows, ceil(width / 8)]")
+            raise ValueError("csa2.indexer_score: block_keys must be [rows, ceil(width / 8)]")
+        if block_keys.dtype == torch.int16:
+            a.flags |= INDEX_BLOCK_KEYS16
     a.block_max, a.block_keys = _ptr(block_max), _ptr(block_keys)
     if fp4:
         a.q_scale_e8m0, a.k_scale_e8m0 = _ptr(q_scale), _ptr(k_scale)
@@ -269,6 +273,7 @@ def _index_args(q, w, k, row_base, pos, ratio, scale, scores, width, k_scale, ca
 
 
 INDEX_SHARED_PLANE = 1
+INDEX_BLOCK_KEYS16 = 2
 
 
 def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None, cand=None, block_rows=8,
@@ -285,15 +290,17 @@ def indexer_score(q, w, k, row_base, pos, ratio, scale, scores, *, k_scale=None,
     optionally receives the score-key histogram topk_select can reuse.
     ``block_max`` (FULL only, float32 [rows, ceil(width / block_rows)])
     optionally receives the candidate pool's block scores.  ``scores=None``
-    (with ``width`` and ``block_keys`` int32 [rows, ceil(width / 8)], no
-    ``key_hist``) selects the score-free mode whose top-k ``topk_rescore`` takes.
+    (with ``width`` and ``block_keys`` [rows, ceil(width / 8)], no ``key_hist``)
+    selects the score-free mode whose top-k ``topk_rescore`` takes; int32 block
+    keys are the full keys, int16 ones their top 16 bits (FP8 / MXFP4 planes: half
+    the bytes, and all the select needs; the candidate pool needs int32).
     ``shared_plane=True`` (FULL only) states that every row reads the plane rows of
     ``row_base[0]`` (a prefill chunk of one sequence); the library may then stage
     key tiles once for several rows (same results).
     """
     a = _index_args(q, w, k, row_base, pos, ratio, scale, scores, width, k_scale, cand, block_rows, fp8, key_hist,
                     block_max, block_keys, fp4, q_scale)
-    a.flags = INDEX_SHARED_PLANE if shared_plane else 0
+    a.flags |= INDEX_SHARED_PLANE if shared_plane else 0
     _check("csa2_indexer_score", _lib.csa2_indexer_score(ctypes.byref(a), _stream(stream)))
     return scores
 
@@ -328,7 +335,7 @@ def topk_rescore(q, w, k, row_base, pos, ratio, scale, out, block_keys, width, *
     _need(out, torch.int32, "out")
     a = _index_args(q, w, k, row_base, pos, ratio, scale, None, width, k_scale, None, 8, not (fp4 or dense), None,
                     None, block_keys, fp4, q_scale)
-    a.flags = INDEX_SHARED_PLANE if shared_plane else 0
+    a.flags |= INDEX_SHARED_PLANE if shared_plane else 0
     if out.shape[0] != a.rows:
         raise ValueError("csa2.topk_rescore: out rows")
     need = topk_rescore_workspace_size(a.rows, a.width, out.shape[1])

@@ -98,7 +98,9 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
     if (a->q_dtype != a->k_dtype || elem_bytes(a->k_dtype) == 0) return CSA2_ERR_UNSUPPORTED;
     if (!csa2::indexer_supported(a->heads, a->dim, a->k_dtype)) return CSA2_ERR_UNSUPPORTED;
     const bool reindex = a->mode == CSA2_MODE_REINDEX;
-    if ((a->flags & ~CSA2_INDEX_SHARED_PLANE) != 0 || (reindex && a->flags != 0)) return CSA2_ERR_INVALID_ARG;
+    if ((a->flags & ~(CSA2_INDEX_SHARED_PLANE | CSA2_INDEX_BLOCK_KEYS16)) != 0 || (reindex && a->flags != 0))
+        return CSA2_ERR_INVALID_ARG;
+    const bool bk16 = (a->flags & CSA2_INDEX_BLOCK_KEYS16) != 0;
     if (a->k_dtype == CSA2_FP4_E2M1 && reindex && a->block_rows != 8) return CSA2_ERR_UNSUPPORTED;
     if (reindex) {
         if (a->cand == nullptr || a->n_blocks <= 0 || a->block_rows <= 0 || a->block_rows > 64) return CSA2_ERR_INVALID_ARG;
@@ -120,6 +122,9 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
             return CSA2_ERR_UNSUPPORTED;
         if (a->width >= (1LL << 24) && !dense_score_free(a)) return CSA2_ERR_UNSUPPORTED;
         if (!aligned(a->block_keys, 4)) return CSA2_ERR_INVALID_ARG;
+        if (bk16 && dense_score_free(a)) return CSA2_ERR_INVALID_ARG;  // that route ranks full keys
+    } else if (bk16) {
+        return CSA2_ERR_INVALID_ARG;  // 16-bit block keys exist in score-free mode only
     }
     if (a->q == nullptr || a->w == nullptr || a->k == nullptr || a->row_base == nullptr || a->pos == nullptr)
         return CSA2_ERR_INVALID_ARG;
@@ -136,6 +141,7 @@ int32_t csa2_indexer_score(const csa2_index_args* a, csa2_stream_t stream) {
     p.n_blocks = reindex ? a->n_blocks : 0; p.block_rows = reindex ? a->block_rows : 1; p.ratio = a->ratio;
     p.scale = a->scale;
     p.shared_plane = (a->flags & CSA2_INDEX_SHARED_PLANE) != 0;
+    p.bk16 = bk16;
     p.block_max = reindex ? nullptr : a->block_max;
     p.block_keys = score_free ? a->block_keys : nullptr;
     p.bm_rows = p.block_max != nullptr ? a->block_rows : 4;
@@ -206,7 +212,7 @@ static int32_t dense_rescore(const csa2_index_args* a, int32_t k, int32_t* out, 
     ip.q_e8 = nullptr; ip.k_e8 = nullptr; ip.cand = cand; ip.scores = sc; ip.key_hist = nullptr;
     ip.block_max = nullptr; ip.block_keys = nullptr; ip.width = 8 * (int64_t)k; ip.cols_per_wg = 0;
     ip.bm_blocks = 0; ip.n_blocks = k; ip.block_rows = 8; ip.bm_rows = 4; ip.ratio = a->ratio; ip.scale = a->scale;
-    ip.shared_plane = false;
+    ip.shared_plane = false; ip.bk16 = false;
     if (e == hipSuccess) e = csa2::launch_indexer_score(ip, rows, 64, 128, CSA2_BF16, true, st);
 
     csa2::TopkParams fp;  // the exact select over them
@@ -222,8 +228,11 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
     if (a == nullptr || a->struct_size < sizeof(csa2_index_args)) return CSA2_ERR_INVALID_ARG;
     if (a->mode != CSA2_MODE_FULL || a->rows < 0 || a->width < 0 || (a->ratio != 1 && a->ratio != 2))
         return CSA2_ERR_INVALID_ARG;
-    if (k < 1 || k > 2048 || (a->flags & ~CSA2_INDEX_SHARED_PLANE) != 0) return CSA2_ERR_INVALID_ARG;
+    if (k < 1 || k > 2048 || (a->flags & ~(CSA2_INDEX_SHARED_PLANE | CSA2_INDEX_BLOCK_KEYS16)) != 0)
+        return CSA2_ERR_INVALID_ARG;
     const bool dense = a->q_dtype == a->k_dtype && dense_score_free(a);
+    const bool bk16 = (a->flags & CSA2_INDEX_BLOCK_KEYS16) != 0;
+    if (bk16 && dense) return CSA2_ERR_INVALID_ARG;
     if (!dense && (a->q_dtype != a->k_dtype || !csa2::indexer_rescore_supported(a->heads, a->dim, a->k_dtype)))
         return CSA2_ERR_UNSUPPORTED;
     if (a->rows == 0) return CSA2_OK;
@@ -248,6 +257,7 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
     ip.cand = nullptr; ip.scores = nullptr; ip.key_hist = nullptr; ip.block_max = nullptr;
     ip.block_keys = a->block_keys; ip.width = a->width; ip.cols_per_wg = 0; ip.bm_blocks = 0; ip.n_blocks = 0;
     ip.block_rows = 1; ip.bm_rows = 4; ip.ratio = a->ratio; ip.scale = a->scale; ip.shared_plane = false;
+    ip.bk16 = bk16;
     csa2::TopkParams tp;
     tp.scores = nullptr; tp.pos = a->pos; tp.cand = nullptr; tp.out = out; tp.key_hist = nullptr;
     tp.width = a->width; tp.k = k; tp.ratio = a->ratio; tp.n_blocks = 0; tp.block_rows = 1; tp.col_group = 1;
@@ -264,7 +274,7 @@ int32_t csa2_topk_rescore(const csa2_index_args* a, int32_t k, int32_t* out, voi
     w += align256((size_t)a->rows * nseg * chunk * 4);
     uint32_t* hist = reinterpret_cast<uint32_t*>(w);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = csa2::launch_block_key_hist(a->block_keys, (a->width + 7) / 8, a->rows, hist, st);
+    hipError_t e = csa2::launch_block_key_hist(a->block_keys, bk16, (a->width + 7) / 8, a->rows, hist, st);
     if (e == hipSuccess)
         e = csa2::launch_topk_threshold(tp, a->rows, hist, csa2::block_key_hist_parts((a->width + 7) / 8), b1, st);
     if (e == hipSuccess)

@@ -768,11 +768,25 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(const IndexParams p
     int64_t cb = cb0;
     if (c_live > cb0) cb += 256 * ((c_live - cb0 + 255) / 256);
     for (; cb < c_end; cb += 256) store_invisible<BMAX, SCORES, BKEYS>(p, r, cb, c_end, lane, srow, bkl, c_begin);
-    if (BKEYS) {  // the workgroup's block keys in one contiguous burst
+    if (BKEYS) {  // the workgroup's block keys in one contiguous burst (32-bit, or their top 16 bits)
         __syncthreads();
         const int nbk = (int)((c_end - c_begin + kKeyBlock - 1) / kKeyBlock);
-        uint32_t* gk = p.block_keys + (int64_t)r * ((p.width + kKeyBlock - 1) / kKeyBlock) + c_begin / kKeyBlock;
-        for (int i = threadIdx.x; i < nbk; i += 256) __builtin_nontemporal_store(bkl[i], gk + i);
+        const int64_t at = (int64_t)r * ((p.width + kKeyBlock - 1) / kKeyBlock) + c_begin / kKeyBlock;
+        if (p.bk16 && (at & 1) == 0) {  // pairs of keys as 32-bit stores
+            uint32_t* gk = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(p.block_keys) + at);
+            for (int i = threadIdx.x; 2 * i < nbk; i += 256) {
+                if (2 * i + 1 < nbk)
+                    __builtin_nontemporal_store((bkl[2 * i] >> 16) | (bkl[2 * i + 1] & 0xffff0000u), gk + i);
+                else
+                    __builtin_nontemporal_store((uint16_t)(bkl[2 * i] >> 16), reinterpret_cast<uint16_t*>(gk + i));
+            }
+        } else if (p.bk16) {
+            uint16_t* gk = reinterpret_cast<uint16_t*>(p.block_keys) + at;
+            for (int i = threadIdx.x; i < nbk; i += 256) __builtin_nontemporal_store((uint16_t)(bkl[i] >> 16), gk + i);
+        } else {
+            uint32_t* gk = p.block_keys + at;
+            for (int i = threadIdx.x; i < nbk; i += 256) __builtin_nontemporal_store(bkl[i], gk + i);
+        }
     }
     if (HIST) {
         __syncthreads();
@@ -799,7 +813,7 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(const IndexParams p
 constexpr int kRescoreBatch = 16;                  // block keys per lane per batch
 constexpr int kRescoreQueue = 64 * kRescoreBatch;  // blocks per batch
 
-template <class KF>
+template <class KF, bool BK16>
 __global__ __launch_bounds__(256) void indexer_rescore_kernel(const IndexParams p, const uint32_t* b1_in, int chunk,
                                                               int nseg, uint32_t* cand_keys, int32_t* cand_cols,
                                                               uint32_t* seg_count) {
@@ -821,6 +835,7 @@ __global__ __launch_bounds__(256) void indexer_rescore_kernel(const IndexParams 
     const int64_t c_hi = c_lo + chunk < n_valid ? c_lo + chunk : n_valid;
     const int64_t nbk_row = (p.width + kKeyBlock - 1) / kKeyBlock;
     const uint32_t* bkeys = p.block_keys + (int64_t)r * nbk_row;
+    const uint16_t* bkeys16 = reinterpret_cast<const uint16_t*>(p.block_keys) + (int64_t)r * nbk_row;
     uint32_t* okeys = cand_keys + ((int64_t)r * nseg + seg) * chunk;
     int32_t* ocols = cand_cols + ((int64_t)r * nseg + seg) * chunk;
     uint8_t* my = stage[wave];
@@ -891,12 +906,19 @@ __global__ __launch_bounds__(256) void indexer_rescore_kernel(const IndexParams 
     if (c_hi > c_lo) {
         const int64_t blk_lo = c_lo / kKeyBlock, blk_hi = (c_hi + kKeyBlock - 1) / kKeyBlock;
         for (int64_t b0 = blk_lo; b0 < blk_hi; b0 += kRescoreQueue) {
+            // All loads first, unconditional (past the end: the segment's last block, dropped below), so
+            // they are in flight together; 16-bit keys are their top halves, which carry the bins
+            // compared below.
             uint32_t bk[kRescoreBatch];
 #pragma unroll
             for (int i = 0; i < kRescoreBatch; ++i) {
                 const int64_t b = b0 + 64 * i + lane;
-                bk[i] = b < blk_hi ? bkeys[b] : 0u;
+                const int64_t bc = b < blk_hi ? b : blk_hi - 1;
+                bk[i] = BK16 ? (uint32_t)bkeys16[bc] : bkeys[bc];
             }
+#pragma unroll
+            for (int i = 0; i < kRescoreBatch; ++i)
+                bk[i] = b0 + 64 * i + lane < blk_hi ? (BK16 ? bk[i] << 16 : bk[i]) : 0u;
             int n_q = 0;  // wave-uniform queue length
 #pragma unroll
             for (int i = 0; i < kRescoreBatch; ++i) {
@@ -935,12 +957,18 @@ __global__ __launch_bounds__(256) void indexer_rescore_kernel(const IndexParams 
 hipError_t launch_indexer_rescore(const IndexParams& p, int rows, int dtype, const uint32_t* b1, int chunk, int nseg,
                                   uint32_t* cand_keys, int32_t* cand_cols, uint32_t* seg_count, hipStream_t stream) {
     const dim3 grid((unsigned)((nseg + 3) / 4), (unsigned)rows);
-    if (dtype == CSA2_FP4_E2M1)
-        hipLaunchKernelGGL(indexer_rescore_kernel<Fp4Keys>, grid, dim3(256), 0, stream, p, b1, chunk, nseg, cand_keys,
-                           cand_cols, seg_count);
+    if (dtype == CSA2_FP4_E2M1 && p.bk16)
+        hipLaunchKernelGGL((indexer_rescore_kernel<Fp4Keys, true>), grid, dim3(256), 0, stream, p, b1, chunk, nseg,
+                           cand_keys, cand_cols, seg_count);
+    else if (dtype == CSA2_FP4_E2M1)
+        hipLaunchKernelGGL((indexer_rescore_kernel<Fp4Keys, false>), grid, dim3(256), 0, stream, p, b1, chunk, nseg,
+                           cand_keys, cand_cols, seg_count);
+    else if (p.bk16)
+        hipLaunchKernelGGL((indexer_rescore_kernel<Fp8Keys, true>), grid, dim3(256), 0, stream, p, b1, chunk, nseg,
+                           cand_keys, cand_cols, seg_count);
     else
-        hipLaunchKernelGGL(indexer_rescore_kernel<Fp8Keys>, grid, dim3(256), 0, stream, p, b1, chunk, nseg, cand_keys,
-                           cand_cols, seg_count);
+        hipLaunchKernelGGL((indexer_rescore_kernel<Fp8Keys, false>), grid, dim3(256), 0, stream, p, b1, chunk, nseg,
+                           cand_keys, cand_cols, seg_count);
     return hipGetLastError();
 }
 

@@ -31,6 +31,7 @@ struct IndexParams {
     int32_t ratio;
     float scale;
     bool shared_plane;   // every row reads the plane rows of row_base[0]
+    bool bk16;           // block_keys holds uint16_t entries: the keys' top 16 bits
 };
 
 hipError_t launch_indexer_score(const IndexParams& p, int rows, int heads, int dim, int dtype, bool reindex,
@@ -69,7 +70,8 @@ void topk_plan(int rows, int64_t width, int& chunk, int& nseg, int min_chunk);
 // Per-row histograms of block keys' top 12 bits as [rows, parts, 4096] partial
 // counts (parts = block_key_hist_parts(nbk_row)).
 int block_key_hist_parts(int64_t nbk_row);
-hipError_t launch_block_key_hist(const uint32_t* bkeys, int64_t nbk_row, int rows, uint32_t* hist, hipStream_t stream);
+hipError_t launch_block_key_hist(const uint32_t* bkeys, bool bk16, int64_t nbk_row, int rows, uint32_t* hist,
+                                 hipStream_t stream);
 hipError_t launch_topk_threshold(const TopkParams& p, int rows, const uint32_t* key_hist, int parts, uint32_t* b1,
                                  hipStream_t stream);
 hipError_t launch_topk_final(const TopkParams& p, int rows, const uint32_t* cand_keys, const int32_t* cand_cols,

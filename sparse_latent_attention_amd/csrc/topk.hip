@@ -821,8 +821,8 @@ hipError_t launch_topk_select(const TopkParams& p, int rows, void* ws, hipStream
 // workgroup counts seg_len consecutive keys of its row in LDS and writes all
 // 4096 bins to its own slot hist[(r * nseg + seg) * 4096 ...] (no atomics, no
 // zeroing; topk_threshold_kernel adds the slots).  Keys of 0 (blocks without a
-// valid column) are not counted.
-template <int NT, bool VEC>
+// valid column) are not counted.  BK16: the keys are the uint16_t top halves.
+template <int NT, bool VEC, bool BK16>
 __global__ __launch_bounds__(NT) void block_key_hist_kernel(const uint32_t* bkeys, int64_t nbk_row, int seg_len,
                                                             uint32_t* hist) {
     __shared__ uint32_t h[4096];
@@ -831,18 +831,38 @@ __global__ __launch_bounds__(NT) void block_key_hist_kernel(const uint32_t* bkey
     __syncthreads();
     const int64_t i0 = (int64_t)blockIdx.x * seg_len;
     const int64_t i1 = i0 + seg_len < nbk_row ? i0 + seg_len : nbk_row;
-    const uint32_t* row = bkeys + (int64_t)r * nbk_row;
-    if (VEC) {  // 16-byte loads: the segment and the row are multiples of 4 keys, 16-byte aligned
-        for (int64_t i = i0 + 4 * threadIdx.x; i < i1; i += 4 * NT) {
-            const u32x4 k = *reinterpret_cast<const u32x4*>(row + i);
+    if (BK16) {
+        const uint16_t* row = reinterpret_cast<const uint16_t*>(bkeys) + (int64_t)r * nbk_row;
+        if (VEC) {  // 16-byte loads: the segment and the row are multiples of 8 keys, 16-byte aligned
+            for (int64_t i = i0 + 8 * threadIdx.x; i < i1; i += 8 * NT) {
+                const u32x4 k = *reinterpret_cast<const u32x4*>(row + i);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (k[e] != 0u) atomicAdd(&h[k[e] >> 20], 1u);
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = k[e] & 0xffffu, hi = k[e] >> 16;
+                    if (lo != 0u) atomicAdd(&h[lo >> 4], 1u);
+                    if (hi != 0u) atomicAdd(&h[hi >> 4], 1u);
+                }
+            }
+        } else {
+            for (int64_t i = i0 + threadIdx.x; i < i1; i += NT) {
+                const uint32_t k = row[i];
+                if (k != 0u) atomicAdd(&h[k >> 4], 1u);
+            }
         }
     } else {
-        for (int64_t i = i0 + threadIdx.x; i < i1; i += NT) {
-            const uint32_t k = row[i];
-            if (k != 0u) atomicAdd(&h[k >> 20], 1u);
+        const uint32_t* row = bkeys + (int64_t)r * nbk_row;
+        if (VEC) {  // 16-byte loads: the segment and the row are multiples of 4 keys, 16-byte aligned
+            for (int64_t i = i0 + 4 * threadIdx.x; i < i1; i += 4 * NT) {
+                const u32x4 k = *reinterpret_cast<const u32x4*>(row + i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (k[e] != 0u) atomicAdd(&h[k[e] >> 20], 1u);
+            }
+        } else {
+            for (int64_t i = i0 + threadIdx.x; i < i1; i += NT) {
+                const uint32_t k = row[i];
+                if (k != 0u) atomicAdd(&h[k >> 20], 1u);
+            }
         }
     }
     __syncthreads();
@@ -855,14 +875,22 @@ constexpr int kBkhSeg = 16384;
 
 int block_key_hist_parts(int64_t nbk_row) { return (int)((nbk_row + kBkhSeg - 1) / kBkhSeg); }
 
-hipError_t launch_block_key_hist(const uint32_t* bkeys, int64_t nbk_row, int rows, uint32_t* hist, hipStream_t stream) {
+hipError_t launch_block_key_hist(const uint32_t* bkeys, bool bk16, int64_t nbk_row, int rows, uint32_t* hist,
+                                 hipStream_t stream) {
     const dim3 grid((unsigned)((nbk_row + kBkhSeg - 1) / kBkhSeg), (unsigned)rows);
-    if (nbk_row % 4 == 0 && reinterpret_cast<uintptr_t>(bkeys) % 16 == 0)
-        hipLaunchKernelGGL((block_key_hist_kernel<kBkhThreads, true>), grid, dim3(kBkhThreads), 0, stream, bkeys, nbk_row,
-                           kBkhSeg, hist);
-    else
-        hipLaunchKernelGGL((block_key_hist_kernel<kBkhThreads, false>), grid, dim3(kBkhThreads), 0, stream, bkeys,
+    const bool vec = nbk_row % (bk16 ? 8 : 4) == 0 && reinterpret_cast<uintptr_t>(bkeys) % 16 == 0;
+    if (bk16 && vec)
+        hipLaunchKernelGGL((block_key_hist_kernel<kBkhThreads, true, true>), grid, dim3(kBkhThreads), 0, stream, bkeys,
                            nbk_row, kBkhSeg, hist);
+    else if (bk16)
+        hipLaunchKernelGGL((block_key_hist_kernel<kBkhThreads, false, true>), grid, dim3(kBkhThreads), 0, stream, bkeys,
+                           nbk_row, kBkhSeg, hist);
+    else if (vec)
+        hipLaunchKernelGGL((block_key_hist_kernel<kBkhThreads, true, false>), grid, dim3(kBkhThreads), 0, stream, bkeys,
+                           nbk_row, kBkhSeg, hist);
+    else
+        hipLaunchKernelGGL((block_key_hist_kernel<kBkhThreads, false, false>), grid, dim3(kBkhThreads), 0, stream,
+                           bkeys, nbk_row, kBkhSeg, hist);
     return hipGetLastError();
 }
 

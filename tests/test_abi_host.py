@@ -92,7 +92,8 @@ def _index_args(**kw):
     ("q", None, csa2.ERR_INVALID_ARG),
     ("k_scale", ctypes.c_void_p(0x1000), csa2.ERR_INVALID_ARG),
     ("scale", float("nan"), csa2.ERR_INVALID_ARG),
-    ("flags", 2, csa2.ERR_INVALID_ARG),
+    ("flags", 2, csa2.ERR_INVALID_ARG),      # 16-bit block keys: score-free mode only
+    ("flags", 4, csa2.ERR_INVALID_ARG),
     ("flags", -1, csa2.ERR_INVALID_ARG),
 ])
 def test_indexer_validation(field, value, status):
@@ -224,6 +225,31 @@ def test_topk_rescore_workspace_rules():
     # narrow rows: no quantised plan, but the BF16 shared-plane plan (the chosen blocks and their re-computed
     # scores) sizes the workspace
     assert csa2.topk_rescore_workspace_size(4, 4000, 512) >= 4 * 512 * 4 + 4 * 4096 * 4
+
+
+def test_block_keys16_rules():
+    """16-bit block keys: score-free FP8 / MXFP4 planes only (not the BF16 shared-plane route, which ranks
+    full keys, nor REINDEX), and the re-scoring select takes them with the same flag."""
+    ptr = ctypes.c_void_p(0x1000)
+    fp8 = dict(q_dtype=csa2.FP8_E4M3, k_dtype=csa2.FP8_E4M3, k_scale=ptr, width=1 << 20, scores=None,
+               block_keys=ptr, flags=csa2.INDEX_BLOCK_KEYS16)
+    a = _index_args(rows=0, **fp8)
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.OK
+    a = _index_args(**dict(fp8, scores=ptr, block_keys=None))
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+    a = _index_args(**dict(fp8, mode=csa2.MODE_REINDEX, cand=ptr, n_blocks=2048, block_rows=8, width=16384))
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+    dense = dict(q_dtype=csa2.BF16, k_dtype=csa2.BF16, width=70000, scores=None, block_keys=ptr, rows=4096,
+                 flags=csa2.INDEX_SHARED_PLANE | csa2.INDEX_BLOCK_KEYS16)
+    a = _index_args(**dense)
+    assert csa2._lib.csa2_indexer_score(ctypes.byref(a), None) == csa2.ERR_INVALID_ARG
+    assert csa2._lib.csa2_topk_rescore(ctypes.byref(a), 512, ptr, ctypes.c_void_p(0x10000), 1 << 30, None) == \
+        csa2.ERR_INVALID_ARG
+    # accepted by the select: the workspace check is the next one it makes
+    a = _index_args(**fp8)
+    ws = csa2.topk_rescore_workspace_size(a.rows, a.width, 512)
+    assert csa2._lib.csa2_topk_rescore(ctypes.byref(a), 512, ptr, ctypes.c_void_p(0x10000), ws - 1, None) == \
+        csa2.ERR_WORKSPACE
 
 
 def test_topk_rescore_bf16_shared_plane_rules():

@@ -85,10 +85,11 @@ def test_indexer_and_topk_with_nan_codes(cfg):
     assert n_bad == 0
 
 
+@pytest.mark.parametrize("bk16", [False, True])
 @pytest.mark.parametrize("base", ["lowp", "pages"])
-def test_score_free_topk_with_nan_codes(base):
-    """The score-free route (block keys, re-scoring) returns what topk_select returns over the written
-    NaN-bearing scores."""
+def test_score_free_topk_with_nan_codes(base, bk16):
+    """The score-free route (block keys, 32-bit or their top 16 bits, then re-scoring) returns what
+    topk_select returns over the written NaN-bearing scores."""
     import sparse_latent_attention_amd as csa2
     cfg = (LOWP if base == "lowp" else PAGES).replace(context=30011)
     x = make_inputs(cfg, 62, device="cuda")
@@ -100,7 +101,7 @@ def test_score_free_topk_with_nan_codes(base):
     assert csa2.topk_rescore_supported(rows, cfg.width, cfg.topk, fp8=cfg.idx_dtype == "fp8",
                                        fp4=cfg.idx_dtype == "fp4")
     kI, ikw = index_plane_args(cfg, x)
-    bkeys = torch.empty(rows, -(-cfg.width // 8), dtype=torch.int32, device="cuda")
+    bkeys = torch.empty(rows, -(-cfg.width // 8), dtype=torch.int16 if bk16 else torch.int32, device="cuda")
     csa2.indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, index_scale(cfg), None,
                        width=cfg.width, block_keys=bkeys, **ikw)
     out = torch.full((rows, cfg.topk), -7, dtype=torch.int32, device="cuda")

@@ -6,7 +6,8 @@ materialised path on the same inputs, which in turn is checked against the
 oracle (tests/test_gpu_parity.py, tests/test_gpu_fullsize.py):
   * (the select counts the block keys' bins itself; its threshold is checked
     through the top-k below);
-  * each block key equals the largest order key of its 8 written scores;
+  * each block key equals the largest order key of its 8 written scores (16-bit
+    keys: its top 16 bits, all the select reads);
   * the top-k equals topk_select of the written scores, and the oracle's top-k
     of them.
 Inputs include ragged histories (rows with fewer visible rows than k, a row
@@ -32,11 +33,11 @@ def _order_keys(s):
     return np.where(u & 0x80000000, ~u, u | 0x80000000).astype(np.uint32)
 
 
-def _score_free(cfg, x, k):
+def _score_free(cfg, x, k, bk16=False):
     import sparse_latent_attention_amd as csa2
     rows = x["pos"].shape[0]
     dev = x["pos"].device
-    bkeys = torch.full((rows, -(-cfg.width // 8)), 12345, dtype=torch.int32, device=dev)
+    bkeys = torch.full((rows, -(-cfg.width // 8)), 12345, dtype=torch.int16 if bk16 else torch.int32, device=dev)
     kI, ikw = index_plane_args(cfg, x)
     csa2.indexer_score(x["qI"], x["w"], kI, x["kv_row_base"], x["pos"], cfg.ratio, index_scale(cfg), None,
                        width=cfg.width, block_keys=bkeys, **ikw)
@@ -67,11 +68,15 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_score_free_matches_written_scores(name):
+BK16_CASES = ["ragged_100k", "short_rows", "k2048", "ties", "full_1m", "k1_short_rows", "mx_short_rows", "mx_ties",
+              "mx_full_1m"]
+
+
+@pytest.mark.parametrize("name,bk16", [(n, False) for n in CASES] + [(n, True) for n in BK16_CASES])
+def test_score_free_matches_written_scores(name, bk16):
     import sparse_latent_attention_amd as csa2
     cfg, k = CASES[name]
-    print(f"\n[rescore] {name} rows={cfg.q_tokens} width={cfg.width} k={k}", flush=True)
+    print(f"\n[rescore] {name} rows={cfg.q_tokens} width={cfg.width} k={k} bk16={bk16}", flush=True)
     x = make_inputs(cfg, 51, device="cuda")
     rows = cfg.q_tokens
     if name.endswith("short_rows"):
@@ -85,7 +90,7 @@ def test_score_free_matches_written_scores(name):
         sc = x["kI_scale"].view(rows, -1, *x["kI_scale"].shape[2:])
         sc[:, ::40] = sc[:, 17:18]
     assert csa2.topk_rescore_supported(rows, cfg.width, k, fp8=cfg.idx_dtype == "fp8", fp4=cfg.idx_dtype == "fp4")
-    bkeys, out = _score_free(cfg, x, k)
+    bkeys, out = _score_free(cfg, x, k, bk16)
 
     scores = gpu_scores(cfg, x)
     ref_idx = gpu_topk(cfg, x, scores, k=k)
@@ -94,7 +99,10 @@ def test_score_free_matches_written_scores(name):
     keys = np.where(valid, _order_keys(s_np), 0).astype(np.uint32)
     pad = (-cfg.width) % 8
     want_bk = np.pad(keys, ((0, 0), (0, pad))).reshape(rows, -1, 8).max(axis=2)
-    assert np.array_equal(bkeys.cpu().numpy().view(np.uint32), want_bk)
+    if bk16:
+        assert np.array_equal(bkeys.cpu().numpy().view(np.uint16), (want_bk >> 16).astype(np.uint16))
+    else:
+        assert np.array_equal(bkeys.cpu().numpy().view(np.uint32), want_bk)
     got = out.cpu().numpy()
     assert np.array_equal(got, ref_idx.cpu().numpy()), "score-free top-k differs from topk_select of written scores"
     assert np.array_equal(got, oracle_topk(cfg, x, s_np.astype(np.float64), np.arange(rows), k=k))

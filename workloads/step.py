@@ -95,7 +95,10 @@ class Step:
         if score_free:
             self.scores = None
             self.key_hist = None
-            self.block_keys = torch.empty(rows, -(-cfg.width // 8), dtype=torch.int32, device=dev)
+            # the select needs the block keys' top 16 bits only; the candidate pool and the BF16 route rank
+            # blocks by the full keys
+            bk_dtype = torch.int32 if (cfg.pool_blocks or dense) else torch.int16
+            self.block_keys = torch.empty(rows, -(-cfg.width // 8), dtype=bk_dtype, device=dev)
             # the pool's block scores come from the block keys: no block_max pass
             self.block_max = None
             call_idx = csa2.prepare_indexer_score(*idx_common, None, width=cfg.width, block_keys=self.block_keys,
