@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 8
+#define CSA2_ABI_VERSION 9
 
 /* Status codes. */
 #define CSA2_OK 0

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(csa2.EXPORTED)
-    assert csa2.ABI_VERSION == 8
+    assert csa2.ABI_VERSION == 9
 
 
 def test_struct_layouts_match_c_compiler():
