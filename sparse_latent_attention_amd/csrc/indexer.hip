@@ -1028,12 +1028,17 @@ __device__ __forceinline__ void step_sums_bf16(const uint8_t* my, const bf16x8 (
     }
 }
 
-constexpr int kReindexMaxSteps = 8;  // 64-column steps per wave at most (the step loop is unrolled)
+#ifndef CSA2_REINDEX_MAX_STEPS
+#define CSA2_REINDEX_MAX_STEPS 8
+#endif
+constexpr int kReindexMaxSteps = CSA2_REINDEX_MAX_STEPS;  // 64-column steps per wave at most (the loop is unrolled)
 
 #ifndef CSA2_REINDEX_MIN_WG
 #define CSA2_REINDEX_MIN_WG 1
 #endif
-template <class KF, bool HIST, int DEPTH>
+// SEQ: a FULL row read as its consecutive 8-row blocks (slot i is block i; p.cand is not read):
+// the same staged stream over every visible row.
+template <class KF, bool HIST, int DEPTH, bool SEQ = false>
 __global__ __launch_bounds__(256, CSA2_REINDEX_MIN_WG) void indexer_reindex_kernel(const IndexParams p, int steps_per_wave) {
     __shared__ uint32_t hist[HIST ? kKeyBins : 1];
     __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * KF::kRowBytes];
@@ -1055,13 +1060,13 @@ __global__ __launch_bounds__(256, CSA2_REINDEX_MIN_WG) void indexer_reindex_kern
     // Candidate ids of this wave's steps first (every load address depends on them): creg[h] in
     // lane 8 i' + k holds slot k of step 8 h + i' (-1 past the row's slots; the last register
     // serves the loads issued past the last step).
-    const int32_t* crow = p.cand + (int64_t)r * nb;
+    const int32_t* crow = SEQ ? nullptr : p.cand + (int64_t)r * nb;
     int32_t creg[kReindexMaxSteps / 8 + 1];
 #pragma unroll
     for (int h = 0; h < kReindexMaxSteps / 8; ++h) {
         const int i = 8 * h + (lane >> 3);
         const int slot = 8 * (step0 + 4 * i) + (lane & 7);
-        creg[h] = (i < steps_per_wave && slot < nb) ? crow[slot] : -1;
+        creg[h] = (i < steps_per_wave && slot < nb) ? (SEQ ? slot : crow[slot]) : -1;
     }
     creg[kReindexMaxSteps / 8] = -1;
 
@@ -1257,7 +1262,8 @@ constexpr int kReindexDepth = CSA2_REINDEX_DEPTH;
 
 // REINDEX over 8-row blocks: as many waves as fit the chip in one round (BF16: ~300 registers,
 // one wave per SIMD; FP8 / MXFP4: two), each taking up to kReindexMaxSteps steps of its row.
-template <class KF>
+// SEQ: a FULL row's consecutive blocks (p.n_blocks = its width in blocks).
+template <class KF, bool SEQ = false>
 static hipError_t launch_reindex(const IndexParams& p, int rows, hipStream_t stream) {
     const int n_steps = (p.n_blocks + 7) / 8;
     const int64_t total = (int64_t)n_steps * rows;
@@ -1271,11 +1277,31 @@ static hipError_t launch_reindex(const IndexParams& p, int rows, hipStream_t str
         const int64_t nh = (int64_t)rows * kKeyBins;
         hipLaunchKernelGGL(key_hist_zero_kernel, dim3((unsigned)((nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024)),
                            dim3(256), 0, stream, p.key_hist, nh);
-        hipLaunchKernelGGL((indexer_reindex_kernel<KF, true, kReindexDepth>), grid, dim3(256), 0, stream, p, (int)spw);
+        hipLaunchKernelGGL((indexer_reindex_kernel<KF, true, kReindexDepth, SEQ>), grid, dim3(256), 0, stream, p,
+                           (int)spw);
     } else {
-        hipLaunchKernelGGL((indexer_reindex_kernel<KF, false, kReindexDepth>), grid, dim3(256), 0, stream, p, (int)spw);
+        hipLaunchKernelGGL((indexer_reindex_kernel<KF, false, kReindexDepth, SEQ>), grid, dim3(256), 0, stream, p,
+                           (int)spw);
     }
     return hipGetLastError();
+}
+
+// FULL rows of BF16 keys (64 x 128) with scores and nothing else per block: the REINDEX kernel's
+// staged stream over the row's consecutive 8-row blocks, whose scores are bit-identical to the
+// per-row kernel's.
+#ifndef CSA2_FULL_BF16_SEQ
+#define CSA2_FULL_BF16_SEQ 1
+#endif
+static bool full_bf16_seq(const IndexParams& p) {
+    return CSA2_FULL_BF16_SEQ && !p.shared_plane && p.scores != nullptr && p.block_max == nullptr &&
+           p.block_keys == nullptr && p.width > 0 && (p.width + 7) / 8 < (1LL << 31);
+}
+
+static hipError_t launch_full_bf16_seq(IndexParams p, int rows, hipStream_t stream) {
+    p.n_blocks = (int32_t)((p.width + 7) / 8);
+    p.block_rows = 8;
+    p.cand = nullptr;
+    return launch_reindex<Bf16Keys, true>(p, rows, stream);
 }
 
 // Rows sharing one BF16 plane: scores only (no histogram, no block scores), or in score-free mode
@@ -1310,7 +1336,8 @@ hipError_t launch_indexer_score(const IndexParams& p, int rows, int heads, int d
         const bool blocks8 = reindex && p.block_rows == 8;  // the pages' 8-row candidate blocks
         if (dtype == CSA2_BF16) return blocks8 ? launch_reindex<Bf16Keys>(p, rows, stream)
                                      : reindex ? launch_one<CSA2_BF16, 64, 128, true>(p, rows, stream)
-                                               : launch_one<CSA2_BF16, 64, 128, false>(p, rows, stream);
+                                     : full_bf16_seq(p) ? launch_full_bf16_seq(p, rows, stream)
+                                                        : launch_one<CSA2_BF16, 64, 128, false>(p, rows, stream);
         if (dtype == CSA2_FP8_E4M3) return blocks8 ? launch_reindex<Fp8Keys>(p, rows, stream)
                                          : reindex ? launch_one<CSA2_FP8_E4M3, 64, 128, true>(p, rows, stream)
                                                    : launch_stream_full<Fp8Keys>(p, rows, stream);

@@ -62,7 +62,7 @@ __device__ __forceinline__ int32_t col_to_row(const TopkParams& p, int r, int32_
 struct Lds {
     uint32_t hist[4096];
     uint32_t wave_tot[kWaves];
-    uint32_t sel[2];
+    uint32_t sel[3];
     uint32_t flags_cnt[2][2 * kWaves];
     uint32_t seg_start[kMaxSegs + 1];
 };
@@ -72,38 +72,42 @@ __device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Block-wide exclusive suffix sum (sum of v over threads with a larger index).
-__device__ __forceinline__ uint32_t block_suffix_excl(uint32_t v, Lds& s) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_down(x, o, 64);
-        if (lane + o < 64) x += y;
-    }
-    if (lane == 0) s.wave_tot[wave] = x;
-    __syncthreads();
-    uint32_t later = 0;
-    for (int w = wave + 1; w < kWaves; ++w) later += s.wave_tot[w];
-    __syncthreads();
-    return later + x - v;
+// Inclusive prefix sum over the wave (lane i: lanes 0..i) in registers: DPP shifts within each
+// row of 16 lanes, then the row broadcasts of lanes 15 and 31 (rows 1, 3 and 2, 3).
+__device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
 }
 
-// Sum of all bins (4096) of s.hist, returned to every thread.
-__device__ __forceinline__ uint32_t hist_total(Lds& s) {
-    const int t = threadIdx.x;
-    const uint32_t local = s.hist[4 * t] + s.hist[4 * t + 1] + s.hist[4 * t + 2] + s.hist[4 * t + 3];
-    const uint32_t later = block_suffix_excl(local, s);
-    if (t == 0) s.sel[0] = later + local;
+// Sum over the wave, in every lane.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_prefix_incl(x), 63);
+}
+
+// Block-wide exclusive suffix sum (sum of v over threads with a larger index).
+__device__ __forceinline__ uint32_t block_suffix_excl(uint32_t v, Lds& s) {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t incl = wave_prefix_incl(v);
+    const uint32_t wtotal = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    if (lane == 0) s.wave_tot[wave] = wtotal;
     __syncthreads();
-    const uint32_t total = s.sel[0];
+    uint32_t later = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) later += w > wave ? s.wave_tot[w] : 0u;
     __syncthreads();
-    return total;
+    return later + (wtotal - incl);
 }
 
 // Scanning bins from the top, the bin where the running count first reaches
-// `need` (>= 1, <= total), and the count in the bins above it.
-__device__ __forceinline__ void find_bin(Lds& s, int nbins, uint32_t need, uint32_t& bin, uint32_t& above_out) {
+// `need` (>= 1) and the count in the bins above it; returns the count over all
+// bins (bin and above_out are meaningful only when it is >= need).
+__device__ __forceinline__ uint32_t find_bin_total(Lds& s, int nbins, uint32_t need, uint32_t& bin,
+                                                   uint32_t& above_out) {
     const int per = nbins / kThreads;
     const int t = threadIdx.x;
     int b0 = 0, b1 = 0;
@@ -117,6 +121,7 @@ __device__ __forceinline__ void find_bin(Lds& s, int nbins, uint32_t need, uint3
     uint32_t local = 0;
     for (int b = b0; b < b1; ++b) local += s.hist[b];
     uint32_t above = block_suffix_excl(local, s);
+    if (t == 0) s.sel[2] = above + local;
     for (int b = b1 - 1; b >= b0; --b) {
         const uint32_t h = s.hist[b];
         if (above < need && above + h >= need) {
@@ -128,7 +133,13 @@ __device__ __forceinline__ void find_bin(Lds& s, int nbins, uint32_t need, uint3
     __syncthreads();
     bin = s.sel[0];
     above_out = s.sel[1];
+    const uint32_t total = s.sel[2];
     __syncthreads();
+    return total;
+}
+
+__device__ __forceinline__ void find_bin(Lds& s, int nbins, uint32_t need, uint32_t& bin, uint32_t& above_out) {
+    (void)find_bin_total(s, nbins, need, bin, above_out);
 }
 
 // Rank key of a pool column from its block key (the newest column pinned to +inf).
@@ -213,6 +224,7 @@ __device__ __forceinline__ void select_core(const Src& src, const TopkParams& p,
     const int n = src.n;
 
     uint32_t total = (uint32_t)n;
+    uint32_t b1 = (uint32_t)known_b1, above1 = known_above1;
     if (known_b1 < 0) {
         // pass 1: bits [31:20]
         for (int b = tid; b < 4096; b += kThreads) s.hist[b] = 0;
@@ -223,18 +235,12 @@ __device__ __forceinline__ void select_core(const Src& src, const TopkParams& p,
             if (src.get(i, key, col)) atomicAdd(&s.hist[key >> 20], 1u);
         }
         __syncthreads();
-        total = hist_total(s);
+        total = find_bin_total(s, 4096, k, b1, above1);  // b1, above1 used only when total > k
     }
     const bool select_all = total <= k;
     uint32_t T = 0, n_gt = 0;
     if (!select_all) {
-        uint32_t b1, above1, b2, above2, b3, above3;
-        if (known_b1 >= 0) {
-            b1 = (uint32_t)known_b1;
-            above1 = known_above1;
-        } else {
-            find_bin(s, 4096, k, b1, above1);
-        }
+        uint32_t b2, above2, b3, above3;
         // pass 2: bits [19:8] of keys in bin b1
         for (int b = tid; b < 4096; b += kThreads) s.hist[b] = 0;
         __syncthreads();
@@ -445,9 +451,9 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const TopkParams 
         }
     }
     __syncthreads();
-    const uint32_t total = hist_total(s);
     uint32_t b1 = 0, above = 0;
-    if (total > k) find_bin(s, 4096, k, b1, above);
+    const uint32_t total = find_bin_total(s, 4096, k, b1, above);
+    if (total <= k) b1 = above = 0;
     const uint32_t n_cand = total > k ? above + s.hist[b1] : total;  // valid keys with bin >= b1
     __syncthreads();  // every thread has read the histogram
     if (n_cand > (uint32_t)kLdsCand) {
@@ -504,91 +510,166 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const TopkParams 
     select_core(lsrc, p, r, s);
 }
 
-// One workgroup per FULL score row (no candidate blocks: the valid columns are
-// the visible prefix) of at most kRegCols columns, read once: each thread loads
-// 64 scores (16 x 16-byte buffer loads; thread (w, l) owns columns
-// 4096 w + 256 j + 4 l + e, so each load instruction covers 1 KiB of the row)
-// and keeps only their keys' 12-bit bins, two to a register (bin 0 marks a
-// column past the visible prefix: no valid key is in a bin below 7).  The
-// histogram gives the bin b1 of the k-th largest key; the columns in bins >=
-// b1 are compacted into LDS in column order -- per wave in (j, lane, e) order
-// with lane offsets from three bit-plane ballots of the lane counts, waves in
-// turn -- their scores are read again (about 1 % of the row, from L2) for the
-// full keys, and select_core finishes from its second pass (its first would
-// find b1 again).  More than kLdsCand such columns (heavy ties): select_core
-// over the row in memory, as in topk_select_kernel.
+// One workgroup per score row of at most kRegCols columns, read once.  Thread
+// (w, l) owns columns 256 J w + 256 j + 4 l + e (j < J, e < 4; J = 4, 8 or 16
+// as the width needs), each load instruction covering 1 KiB of the row.  A
+// column that is not valid (past the visible prefix, or of a candidate block
+// that is -1 or not yet visible) gets key 0, below every valid key (a valid
+// key is at least 0x007fffff, bin 7).
+//
+// Bin floor F: the k-th largest valid key T lies in a bin >= F, where
+//   * k <= kThreads: F is the bin of the k-th largest of the threads' largest
+//     bins -- k threads hold a key in a bin >= F, k distinct columns, so T is
+//     in such a bin too.  This costs one LDS atomic per thread instead of one
+//     per key: an LDS atomic wave instruction keeps the CU's LDS busy for about
+//     25 cycles, and counting every key was half of a 64K-wide row's select;
+//   * otherwise -- k > kThreads, fewer than k threads hold a valid key, or more
+//     than kLdsCand keys lie in bins >= the first F -- F is the bin of the k-th
+//     largest key from the histogram of every key (1, every valid key, when
+//     there are at most k).
+// The valid keys in bins >= F -- every key >= T is among them -- are compacted
+// in column order into LDS (per wave in (j, lane, e) order, lane offsets from
+// three bit-plane ballots of the lane counts, waves in turn) and select_core
+// finishes there.  J = 16 keeps only the 12-bit bins, two to a register, and
+// reads the candidates' scores again (a few per cent of the row, from L2).
+// More than kLdsCand candidates even then (heavy ties): select_core over the
+// row in memory, as in topk_select_kernel.
+//
+// BLK: 0 FULL validity (the visible prefix); 8 candidate blocks of 8 rows (the
+// four columns of a load are in one block: one id per load); 1 candidate
+// blocks of any height (one id per column).
 constexpr int kRegCols = kThreads * 64;
 
+template <int J, int BLK>
 __global__ __launch_bounds__(kThreads) void topk_regs_kernel(const TopkParams p) {
+    constexpr bool kKeys = J <= 8;  // full keys in registers (else bins, two per register)
+    constexpr int kHeld = kKeys ? 4 * J : 2 * J;
     __shared__ Lds s;
     __shared__ uint32_t lkeys[kLdsCand];
     __shared__ int32_t lcols[kLdsCand];
     __shared__ uint32_t wtot[kWaves];
     const int r = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const RowSrc<kSrcScores> src = row_src<kSrcScores>(p, r);
-    const int n = src.n;
+    const int n = src.n;  // FULL: the visible prefix within the row; blocks: the width
+    const int64_t nv = src.nv;
     const uint32_t k = (uint32_t)p.k;
-    const int cbase = 4096 * wave + 4 * lane;
-    // the visible prefix as a buffer: loads past it return zeros, so none needs a branch
+    const int cbase = 256 * J * wave + 4 * lane;
+    // the n columns as a buffer: loads past them return zeros, so none needs a branch
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(src.srow), (short)0, (n > 0 ? n : 0) * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(BLK != 0 ? p.cand + (int64_t)r * p.n_blocks : p.cand), (short)0,
+        BLK != 0 ? p.n_blocks * 4 : 0, 0x00020000);
     for (int b = tid; b < 4096; b += kThreads) s.hist[b] = 0u;
-    uint32_t bp[32];  // bins of columns 4j + e (j < 16, e < 4): entry (4j + e) / 2, half (4j + e) % 2
-    {
-        u32x4 v[16];
+    uint32_t held[kHeld];  // keys of columns (j, e) at 4 j + e, or their bins at (4 j + e) / 2, half (4 j + e) % 2
+    uint32_t mx = 0;       // largest bin of this thread's valid keys (0: none)
+    // Loads in groups of at most 8 (16 with BLK 8 would hold 80 registers of loads at once).
+    constexpr int JH = J < 8 ? J : 8;
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-            v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (cbase + 256 * j), 0, 0));
+    for (int h = 0; h < J; h += JH) {
+        u32x4 v[JH];
+        int32_t ids[JH];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            uint32_t bins[4];
+        for (int jj = 0; jj < JH; ++jj)
+            v[jj] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (cbase + 256 * (h + jj)), 0, 0));
+        if (BLK == 8) {
+#pragma unroll
+            for (int jj = 0; jj < JH; ++jj)
+                ids[jj] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rc, 4 * ((cbase + 256 * (h + jj)) >> 3), 0, 0);
+        }
+#pragma unroll
+        for (int jj = 0; jj < JH; ++jj) {
+            const int j = h + jj;
+            // BLK 8: rows t < lim of this load's block are visible (0 for a slot of -1)
+            int lim = 8;
+            if (BLK == 8) {
+                const int64_t rem = nv - (int64_t)ids[jj] * 8;
+                lim = ids[jj] < 0 ? 0 : (rem >= 8 ? 8 : (rem <= 0 ? 0 : (int)rem));
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t live = 0u - (uint32_t)(cbase + 256 * j + e < n);  // all ones or zero
-                bins[e] = (order_key(__uint_as_float(v[j][e])) >> 20) & live;
+                const int c = cbase + 256 * j + e;
+                bool ok = c < n;
+                if (BLK == 8) {
+                    ok = ok & ((c & 7) < lim);
+                } else if (BLK == 1) {
+                    const int bi = c / p.block_rows;
+                    const int32_t id = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rc, 4 * bi, 0, 0);
+                    ok = ok & (id >= 0) & ((int64_t)id * p.block_rows + (c - bi * p.block_rows) < nv);
+                }
+                const uint32_t key = order_key(__uint_as_float(v[jj][e])) & (0u - (uint32_t)ok);
+                mx = max(mx, key >> 20);
+                if (kKeys) held[4 * j + e] = key;
+                else if (e & 1) held[(4 * j + e) / 2] |= (key >> 20) << 16;
+                else held[(4 * j + e) / 2] = key >> 20;
             }
-            bp[2 * j] = bins[0] | (bins[1] << 16);
-            bp[2 * j + 1] = bins[2] | (bins[3] << 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keeps the next group's loads behind this group's use
+    }
+    auto bin_at = [&](int j, int e) -> uint32_t {
+        if (kKeys) return held[4 * j + e] >> 20;
+        return (held[(4 * j + e) / 2] >> (16 * (e & 1))) & 0xffffu;
+    };
+    // Keys in bins >= fb: this thread's offset among them (column order) and their count.
+    auto count_floor = [&](uint32_t fb, uint32_t& off_out, uint32_t& n_out) {
+        uint32_t mine = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mine += bin_at(j, e) >= fb ? 1u : 0u;
+        const uint32_t wsum = wave_sum(mine);
+        if (lane == 0) wtot[wave] = wsum;
+        __syncthreads();
+        uint32_t o = 0, all = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            const uint32_t t = wtot[w];
+            o += w < wave ? t : 0u;
+            all += t;
+        }
+        off_out = o;
+        n_out = all;
+    };
+    // The floor from the threads' largest bins (k <= kThreads); from every key when k is larger,
+    // fewer than k threads hold a valid key, or more than kLdsCand keys lie above the first floor.
+    uint32_t floor_bin = 1, off = 0, n_cand = 0, above_unused;
+    bool fits = false;
+    if (k <= (uint32_t)kThreads) {
+        __syncthreads();  // histogram cleared
+        if (mx != 0u) atomicAdd(&s.hist[mx], 1u);
+        __syncthreads();
+        if (find_bin_total(s, 4096, k, floor_bin, above_unused) >= k) {
+            count_floor(floor_bin, off, n_cand);
+            fits = n_cand <= (uint32_t)kLdsCand;
+        }
+        if (!fits)
+            for (int b = tid; b < 4096; b += kThreads) s.hist[b] = 0u;
+    }
+    if (!fits) {
+        __syncthreads();  // histogram cleared
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (bin_at(j, e) != 0u) atomicAdd(&s.hist[bin_at(j, e)], 1u);
+        __syncthreads();
+        uint32_t fb;
+        // at most k valid keys: floor 1, every one of them (bin >= 7; bin 0 is not valid)
+        floor_bin = find_bin_total(s, 4096, k, fb, above_unused) >= k ? fb : 1u;
+        count_floor(floor_bin, off, n_cand);
+        if (n_cand > (uint32_t)kLdsCand) {
+            select_core(src, p, r, s);
+            return;
         }
     }
-    __syncthreads();  // histogram cleared
-#pragma unroll
-    for (int q = 0; q < 32; ++q) {
-        atomicAdd(&s.hist[bp[q] & 0xffffu], 1u);
-        atomicAdd(&s.hist[bp[q] >> 16], 1u);
-    }
-    __syncthreads();
-    const uint32_t total = hist_total(s) - s.hist[0];  // valid keys (bin 0: past the prefix)
-    uint32_t b1 = 0, above = 0;
-    if (total > k) find_bin(s, 4096, k, b1, above);  // b1 >= 7: bin 0 is never reached
-    const uint32_t n_cand = total > k ? above + s.hist[b1] : total;  // valid keys with bin >= b1
-    __syncthreads();  // every thread has read the histogram
-    if (n_cand > (uint32_t)kLdsCand) {
-        select_core(src, p, r, s);
-        return;
-    }
-    // bin 0 (not valid) is below b1 whenever b1 is used; with total <= k every valid key is taken
-    auto bin_at = [&](int j, int e) { return (bp[2 * j + (e >> 1)] >> (16 * (e & 1))) & 0xffffu; };
-    auto take = [&](uint32_t bin) { return bin != 0u && bin >= b1; };
-    uint32_t mine = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mine += take(bin_at(j, e)) ? 1u : 0u;
-    uint32_t wsum = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) wsum += __shfl_xor(wsum, o, 64);
-    if (lane == 0) wtot[wave] = wsum;
-    __syncthreads();
-    uint32_t off = 0;
-    for (int w = 0; w < wave; ++w) off += wtot[w];
+    auto take = [&](uint32_t bin) { return bin >= floor_bin; };
     // the columns again, from a value the compiler cannot match with the first pass's (it would
-    // otherwise keep all 64 column numbers alive across the histogram, in scratch)
+    // otherwise keep all the column numbers alive across the histogram, in scratch)
     int cb = cbase;
     asm volatile("" : "+v"(cb));
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < J; ++j) {
         uint32_t cnt = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) cnt += take(bin_at(j, e)) ? 1u : 0u;
@@ -598,20 +679,23 @@ __global__ __launch_bounds__(kThreads) void topk_regs_kernel(const TopkParams p)
         for (int e = 0; e < 4; ++e) {
             if (take(bin_at(j, e))) {
                 lcols[at] = cb + 256 * j + e;
+                if (kKeys) lkeys[at] = held[4 * j + e];
                 ++at;
             }
         }
         off += (uint32_t)(__builtin_popcountll(p0) + 2 * __builtin_popcountll(p1) + 4 * __builtin_popcountll(p2));
     }
     __syncthreads();
-    // the candidates' full keys, from their scores (read again: the row has just gone through L2)
-    for (int i = tid; i < (int)n_cand; i += kThreads) lkeys[i] = order_key(src.srow[lcols[i]]);
-    __syncthreads();
+    if (!kKeys) {
+        // the candidates' full keys, from their scores (read again: the row has just gone through L2)
+        for (int i = tid; i < (int)n_cand; i += kThreads) lkeys[i] = order_key(src.srow[lcols[i]]);
+        __syncthreads();
+    }
     LdsCandSrc lsrc;
     lsrc.keys = lkeys;
     lsrc.cols = lcols;
     lsrc.n = (int)n_cand;
-    select_core(lsrc, p, r, s, (int)b1, above);
+    select_core(lsrc, p, r, s);
 }
 
 // Each workgroup first finds its row's threshold bin b1 from the row's histogram
@@ -766,7 +850,15 @@ void topk_plan(int rows, int64_t width, int& chunk, int& nseg, int min_chunk) {
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Rows up to this width take one workgroup per row (topk_regs_kernel where it applies): no
+// histogram from the indexer and no workspace.
+#ifndef CSA2_TOPK_REGS_MAX
+#define CSA2_TOPK_REGS_MAX 65536
+#endif
+static_assert(CSA2_TOPK_REGS_MAX <= kRegCols, "row kernel width");
+
 size_t topk_workspace_bytes(int rows, int64_t width) {
+    if (width <= CSA2_TOPK_REGS_MAX) return 0;
     int chunk, nseg;
     topk_plan(rows, width, chunk, nseg, kSweep);
     if (nseg == 0) return 0;
@@ -774,16 +866,29 @@ size_t topk_workspace_bytes(int rows, int64_t width) {
            2 * align256((size_t)rows * nseg * kCap * 4);
 }
 
+template <int J>
+static void launch_regs_j(const TopkParams& p, int rows, hipStream_t stream) {
+    if (p.n_blocks == 0)
+        hipLaunchKernelGGL((topk_regs_kernel<J, 0>), dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+    else if (p.block_rows == 8)
+        hipLaunchKernelGGL((topk_regs_kernel<J, 8>), dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((topk_regs_kernel<J, 1>), dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+}
+
 template <int SRC>
 static hipError_t launch_topk_src(const TopkParams& p, int rows, void* ws, hipStream_t stream) {
-    int chunk, nseg;
-    topk_plan(rows, p.width, chunk, nseg, kSweep);
+    int chunk = 0, nseg = 0;
+    if (p.width > CSA2_TOPK_REGS_MAX) topk_plan(rows, p.width, chunk, nseg, kSweep);
     if (nseg == 0) {
-        if (SRC == kSrcScores && p.n_blocks == 0 && p.width <= kRegCols && p.width % 4 == 0 &&
-            reinterpret_cast<uintptr_t>(p.scores) % 16 == 0)
-            hipLaunchKernelGGL(topk_regs_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
-        else
+        if (SRC == kSrcScores && p.width > 0 && p.width <= kRegCols && p.width % 4 == 0 &&
+            reinterpret_cast<uintptr_t>(p.scores) % 16 == 0) {
+            if (p.width <= 16 * kThreads) launch_regs_j<4>(p, rows, stream);
+            else if (p.width <= 32 * kThreads) launch_regs_j<8>(p, rows, stream);
+            else launch_regs_j<16>(p, rows, stream);
+        } else {
             hipLaunchKernelGGL(topk_select_kernel<SRC>, dim3((unsigned)rows), dim3(kThreads), 0, stream, p);
+        }
         return hipGetLastError();
     }
     char* w = reinterpret_cast<char*>(ws);

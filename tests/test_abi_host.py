@@ -348,11 +348,14 @@ def test_topk_noalloc_rejects_sizes_beyond_its_scratch():
     t = csa2.TopkArgs()
     t.struct_size, t.k, t.ratio = ctypes.sizeof(csa2.TopkArgs), 512, 1
     t.scores = t.pos = t.out = ctypes.c_void_p(0x1000)
-    t.rows, t.width = 1023, 65536
-    assert csa2.topk_workspace_size(1023, 65536, 512) > cap
+    t.rows, t.width = 1023, 131072
+    assert csa2.topk_workspace_size(1023, 131072, 512) > cap
     assert csa2._lib.csa2_topk_select_noalloc(ctypes.byref(t), None) == csa2.ERR_WORKSPACE
-    for rows, width in ((32, 32768), (64, 1 << 20), (256, 1 << 20)):
+    for rows, width in ((32, 65537), (64, 1 << 20), (256, 1 << 20)):
         assert 0 < csa2.topk_workspace_size(rows, width, 512) <= cap
+    # rows up to 65536 wide take one workgroup per row: no workspace at any row count
+    for rows, width in ((1, 65536), (32, 16384), (1023, 65536), (4096, 65536)):
+        assert csa2.topk_workspace_size(rows, width, 512) == 0
     t.rows = 0
     assert csa2._lib.csa2_topk_select_noalloc(ctypes.byref(t), None) == csa2.OK
 

@@ -280,6 +280,68 @@ def test_topk_row_kernel(rows, width, kind, k):
     assert np.array_equal(out.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("rows,width,kind,k,br", [
+    (7, 16384, "normal", 512, 0),      # 16 columns per thread, keys held in registers
+    (7, 32768, "normal", 512, 0),      # 32 per thread
+    (5, 65536, "normal", 512, 0),      # 64 per thread, bins held, candidates' scores read again
+    (6, 16384, "reindex", 512, 8),     # 8-row candidate blocks: -1 slots, blocks not yet visible
+    (4, 32768, "reindex", 1, 8),
+    (3, 65536, "reindex", 2048, 8),    # k > 1024: the floor from every key
+    (4, 16000, "reindex", 512, 4),     # other block heights: one id per column
+    (3, 48000, "reindex", 1024, 16),   # the largest k the threads' maxima bound
+    (3, 65536, "skewed", 512, 0),      # the maxima's floor leaves too many keys: the floor from every key
+    (4, 65536, "ties", 512, 0),        # heavy ties: the row from memory
+    (5, 32768, "short", 1025, 0),      # fewer valid columns than threads or than k
+    (9, 20000, "crafted", 512, 0),     # NaN, -0, -inf
+    (3, 16386, "normal", 512, 0),      # width not a multiple of 4: the two-pass kernel
+])
+def test_topk_row_kernel_shapes(rows, width, kind, k, br):
+    """Rows up to 65536 wide: one workgroup per row, bit-exact against the oracle's top-k."""
+    import sparse_latent_attention_amd as csa2
+    print(f"\n[topk row shapes] rows={rows} width={width} kind={kind} k={k} block_rows={br}", flush=True)
+    rng = np.random.default_rng(rows * 7 + width + k)
+    s = rng.standard_normal((rows, width)).astype(np.float32)
+    pos = np.full(rows, width - 1, dtype=np.int64)
+    cand = None
+    if kind == "skewed":
+        # most keys in one bin; the largest 2000 all in the first 4096 columns (64 threads' columns)
+        s[:] = 1.01
+        s[:, rng.choice(4096, 2000, replace=False)] = 2.0 + rng.random((rows, 2000)).astype(np.float32) * 6
+    if kind == "ties":
+        s = rng.integers(0, 3, (rows, width)).astype(np.float32)
+        s[0] = 4.0
+    if kind == "short":
+        pos[0] = 300
+        pos[1] = 5000
+        pos[2] = 0
+    if kind == "crafted":
+        s[0, rng.random(width) < 0.3] = np.nan
+        s[1, rng.random(width) < 0.5] = -0.0
+        s[2] = -np.inf
+        s[3, ::3] = np.nan
+        s[3, 1::3] = -np.inf
+        pos[4] = 700
+        s[5] = np.round(s[5] * 4) / 4
+    if kind == "reindex":
+        nb = width // br
+        pos[:] = 10 * width
+        cand = np.stack([np.sort(rng.choice(10 * width // br, nb, replace=False)) for _ in range(rows)]).astype(np.int32)
+        cand[1, -100:] = -1
+        cand[0, ::37] = -1
+        pos[2 % rows] = int(cand[2 % rows, nb // 2]) * br + br // 2   # half the blocks not visible, one in part
+    sc = torch.from_numpy(s).cuda()
+    pt = torch.from_numpy(pos).cuda()
+    out = torch.full((rows, k), -9, dtype=torch.int32, device="cuda")
+    assert csa2.topk_workspace_size(rows, width, k) == 0
+    ct = None if cand is None else torch.from_numpy(cand).cuda()
+    csa2.topk_select(sc, pt, 1, out, cand=ct, block_rows=br if br else 8)
+    if cand is None:
+        ref = oracle.topk.topk_full(s.astype(np.float64), pos, 1, k)
+    else:
+        ref = oracle.topk.topk_reindex(s.astype(np.float64), pos, 1, cand, br, k)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
 def test_deterministic():
     cfg = SMALL["reindex_small"]
     x = make_inputs(cfg, 8, device="cuda")
@@ -357,21 +419,49 @@ def test_reindex_equals_full_then_gather(name):
         assert np.array_equal(re_s[r].view(np.uint32), want.view(np.uint32)), f"row {r}"
 
 
+@pytest.mark.parametrize("kw", [
+    dict(batch=7, q_tokens=7, context=3001, ragged=True),      # ragged rows, width not a multiple of 64
+    dict(batch=4, q_tokens=4, context=40003, ragged=True),
+    dict(batch=3, q_tokens=3, context=150001),                 # more steps than one wave takes
+])
+def test_full_bf16_stream_equals_row_kernel(kw):
+    """FULL rows of BF16 keys with scores only go through the staged block stream; asked for block
+    scores as well, the call takes the per-row kernel.  Both write bit-identical scores, and the
+    stream's key histogram equals a host recount."""
+    cfg = CONFIGS["full_decode_64k"].replace(**kw)
+    print(f"\n[full bf16 stream] {kw}", flush=True)
+    x = make_inputs(cfg, 23, device="cuda")
+    rows = cfg.q_tokens
+    x["pos"][0] = 0                                   # one visible row
+    h = torch.full((rows, 4096), 777, dtype=torch.int32, device="cuda")
+    a = gpu_scores(cfg, x, key_hist=h)
+    bm = torch.empty(rows, -(-cfg.width // 8), dtype=torch.float32, device="cuda")
+    b = gpu_scores(cfg, x, block_max=bm)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    s_np = a.cpu().numpy()
+    valid = np.isfinite(oracle_score_bound(cfg, x, np.arange(rows)))
+    assert np.array_equal(h.cpu().numpy().astype(np.int64), host_key_hist(s_np, valid))
+    assert np.all(np.isneginf(s_np[~valid]))
+
+
 @pytest.mark.parametrize("name,kw", [
     ("lowp_full_decode_1m", dict(batch=6, q_tokens=6, context=100003, ragged=True)),
     ("full_decode_64k", dict(batch=5, q_tokens=5, context=40000, ragged=True)),
-    ("reindex_decode_1m", dict(batch=5, q_tokens=5, context=300000, ragged=True, n_blocks=8192)),
+    ("full_decode_64k", dict(batch=4, q_tokens=4, context=200001, ragged=True)),
+    ("reindex_decode_1m", dict(batch=5, q_tokens=5, context=300000, ragged=True, n_blocks=9000)),
     ("reindex_fp8_decode_1m", dict(batch=5, q_tokens=5, context=300000, ragged=True, n_blocks=8192)),
-    ("reindex_pages_decode_1m", dict(batch=5, q_tokens=5, context=300000, ragged=True, n_blocks=8192)),
+    ("reindex_pages_decode_1m", dict(batch=5, q_tokens=5, context=300000, ragged=True, n_blocks=9000)),
 ])
 def test_key_hist_path(name, kw):
-    """Indexer-built key histogram == host recount of the GPU scores; top-k through it is exact."""
+    """Indexer-built key histogram == host recount of the GPU scores; top-k through it is exact (rows
+    wider than 65536 columns read it; narrower rows are selected one workgroup per row without it)."""
     import sparse_latent_attention_amd as csa2
     cfg = CONFIGS[name].replace(**kw)
     print(f"\n[key_hist] {name} {kw}", flush=True)
     x = make_inputs(cfg, 21, device="cuda")
     rows = cfg.q_tokens
-    assert csa2.topk_uses_key_hist(rows, cfg.width, cfg.topk)
+    assert csa2.topk_uses_key_hist(rows, cfg.width, cfg.topk) == (cfg.width > 65536)
     h = torch.empty(rows, 4096, dtype=torch.int32, device="cuda")
     h.fill_(12345)                                   # the call must zero it
     scores = gpu_scores(cfg, x, key_hist=h)

@@ -57,8 +57,8 @@ def test_noalloc_equals_workspace_call(order):
 
 def test_noalloc_refuses_oversized_shapes():
     import sparse_latent_attention_amd as csa2
-    scores = torch.zeros(1023, 65536, dtype=torch.float32, device="cuda")
-    pos = torch.full((1023,), 65535, dtype=torch.int64, device="cuda")
+    scores = torch.zeros(1023, 131072, dtype=torch.float32, device="cuda")
+    pos = torch.full((1023,), 131071, dtype=torch.int64, device="cuda")
     out = torch.empty(1023, 512, dtype=torch.int32, device="cuda")
     with pytest.raises(csa2.Csa2Error) as e:
         csa2.topk_select_noalloc(scores, pos, 1, out)
