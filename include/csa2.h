@@ -177,7 +177,9 @@ typedef struct csa2_index_args {
                                  * key is the order-preserving 32-bit key csa2_topk_select ranks by
                                  * (bits | 0x80000000 for scores >= +0, ~bits below, NaN as -inf,
                                  * -0 as +0).  Passing it on to csa2_topk_select saves that call a
-                                 * full pass over the scores.  NULL in score-free mode. */
+                                 * full pass over the scores of rows wider than 65536 columns (it
+                                 * reads narrower rows once and does not use it).  NULL in
+                                 * score-free mode. */
     float* block_max;           /* optional out, FULL only: [rows, ceil(width / block_rows)], or NULL.
                                  * Block b of row r gets the block score csa2_candidate_pool ranks:
                                  * the largest score over its visible columns, with NaN read as -inf
@@ -273,7 +275,8 @@ typedef struct csa2_topk_args {
                                  * these scores and this validity, or NULL */
 } csa2_topk_args;
 
-/* Bytes of workspace csa2_topk_select needs for these sizes (may be 0). */
+/* Bytes of workspace csa2_topk_select needs for these sizes: 0 for rows up to 65536 columns wide (one
+ * workgroup per row; key_hist is then not read), and for 1024 or more rows. */
 size_t csa2_topk_workspace_size(int32_t rows, int64_t width, int32_t k);
 
 int32_t csa2_topk_select(const csa2_topk_args* args, void* workspace, size_t workspace_bytes,
@@ -289,7 +292,7 @@ int32_t csa2_topk_select(const csa2_topk_args* args, void* workspace, size_t wor
  *     the call uses the current device, which must be the stream's.
  *   - Sizes whose csa2_topk_workspace_size exceeds CSA2_TOPK_NOALLOC_SCRATCH_BYTES return
  *     CSA2_ERR_WORKSPACE before anything is launched (40 MiB covers, e.g., 256 rows of
- *     2^20 columns; rows >= 1024 and widths < 8192 need no workspace at all).
+ *     2^20 columns; rows >= 1024 and widths up to 65536 need no workspace at all).
  *   - Every call on one GPU shares that GPU's array and leaves its contents behind; the
  *     call's own kernels initialise everything they read, so nothing needs clearing.
  *     Calls that overlap on one GPU (concurrent streams, several host threads) race on
