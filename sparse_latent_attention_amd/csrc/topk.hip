@@ -17,12 +17,16 @@
 // order, so nothing is sorted.
 //
 // Two ways to feed that select:
-//   * narrow rows or many rows: one 1024-thread workgroup per row reads the
-//     score row twice -- a histogram of the keys' top 12 bits gives the bin b1
-//     of the k-th largest key, then the keys in bins >= b1 are compacted in
-//     column order into LDS, where the select runs (more than kLdsCand such
-//     keys, i.e. heavy ties: the select reads the row from memory instead);
-//   * wide rows (the 1M-column decode): the row is cut into chunks handled by
+//   * rows up to 65536 columns (and any row of 1024 or more rows): one
+//     1024-thread workgroup per row.  topk_regs_kernel reads the row once into
+//     registers, finds a bin floor the k-th largest key cannot lie below (from
+//     the threads' largest bins, or from the histogram of every key), and
+//     compacts the keys above it in column order into LDS, where the select
+//     runs; topk_select_kernel does the same in two reads of the row for the
+//     other sources (candidate-pool and block keys, unaligned rows).  More than
+//     kLdsCand candidates, i.e. heavy ties: the select reads the row from
+//     memory instead;
+//   * wider rows (the 1M-column decode): the row is cut into chunks handled by
 //     separate workgroups.  (1) each chunk adds its 12-bit histogram into a
 //     per-row global histogram; (2) each chunk's workgroup finds from it the
 //     bin b1 of the k-th largest key and (3) compacts, in column order, the
