@@ -284,6 +284,9 @@ def main():
     ap.add_argument("--flush", choices=["auto", "on", "off"], default="auto",
                     help="read 512 MiB between timed steps (outside the timed events) so the planes come from HBM; "
                          "auto: on for the workloads about the size of the MALL (64K decode, 1M REINDEX decodes)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the same step captured once in a HIP graph and replayed (reported under "
+                         "\"graph\"; value stays the eager launches)")
     ap.add_argument("--calibrate", action="store_true",
                     help="after the bench, run a plain 1 GiB float32 copy kernel 3 times (the reference for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE scaling: 1 GiB read + 1 GiB written per launch)")
@@ -407,6 +410,37 @@ def main():
         "kernels_roofline": {n: roofline_of(work[n], kern_ms[n]) for n in names},
         "roofline": roofline,
     }
+    if args.graph:
+        # The step's calls prepared again on a side stream (a graph is captured on one), captured once, and
+        # replayed K times: the kernels are the same, the launches come from the graph.
+        gs = torch.cuda.Stream()
+        with torch.cuda.stream(gs):
+            g_step = Step(cfg, x)
+            g_step()
+        gs.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            g_step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g_evs = []
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            if flush:
+                flush_buf.sum()
+                a = torch.cuda.Event(enable_timing=True)
+                a.record()
+            graph.replay()
+            if flush:
+                b = torch.cuda.Event(enable_timing=True)
+                b.record()
+                g_evs.append((a, b))
+        torch.cuda.synchronize()
+        g_wall = time.perf_counter() - t1
+        g_ms = mean_ms(g_evs) if flush else g_wall * 1e3 / args.steps
+        line["graph"] = {"ms_per_step": round(g_ms, 4), "value": round(q_tokens / (g_ms * 1e-3), 1),
+                         "timing": "HIP events around each replay" if flush else "wall clock over the replays"}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_budget)
