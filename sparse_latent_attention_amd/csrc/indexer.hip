@@ -804,22 +804,84 @@ __global__ __launch_bounds__(256) void indexer_stream_kernel(const IndexParams p
 // columns with keys in bins >= b1, so the row's k-th largest column key is in
 // a bin >= b1 too: every selected column has a key in bin >= b1, and so has
 // the largest key of its kKeyBlock-column block.  One wave handles one segment on its own (no
-// barriers): per batch of 1024 blocks it loads the block keys (16 per lane, at
-// once), queues in column order the blocks whose key reaches bin b1 in an LDS
-// list, then re-scores the queue 8 blocks (one 64-key step) at a time with
-// exactly the scoring pass's arithmetic, appending the (key, column) pairs of
-// valid columns in bins >= b1, in column order, to the segment's list
-// (capacity chunk, so it never overflows).  seg_count gets the list length.
-constexpr int kRescoreBatch = 16;                  // block keys per lane per batch
-constexpr int kRescoreQueue = 64 * kRescoreBatch;  // blocks per batch
+// barriers).  It loads the block keys of up to kRescoreGroups x 256 blocks at once, before its
+// query (lane l of group i holds blocks 256 i + 4 l .. 256 i + 4 l + 3), queues in column order
+// the blocks whose key reaches bin b1 in an LDS list (each lane's place from a wave prefix sum of
+// the lanes' counts), then re-scores the queue 8 blocks (one 64-key step) at a time with exactly
+// the scoring pass's arithmetic, appending the (key, column) pairs of valid columns in bins >= b1,
+// in column order, to the segment's list (capacity chunk, so it never overflows).  Segments with
+// more than kRescoreQueue queued blocks (heavy ties) queue and re-score one group at a time.
+// seg_count gets the list length.
+constexpr int kRescoreGroups = 8;    // groups of 256 blocks whose keys are loaded together
+constexpr int kRescoreQueue = 256;   // queued blocks per wave (one group always fits)
 
-template <class KF, bool BK16>
+// The four block keys of lanes' group slot (as 32-bit keys; 16-bit keys are their top halves), and a
+// bit per key whose block is queued.  VEC: one 8- or 16-byte load (the row's keys are a multiple of 4
+// long and 16-byte aligned); otherwise four loads.  Blocks past blk_hi read as 0 (not queued); the
+// load itself stays inside the row.
+template <bool BK16, bool VEC>
+__device__ __forceinline__ void rescore_load_keys(const uint32_t* bkeys, const uint16_t* bkeys16, int64_t b,
+                                                  int64_t blk_hi, int64_t nbk_row, uint32_t (&raw)[BK16 ? 2 : 4]) {
+    if constexpr (VEC) {
+        const int64_t bq = b + 4 <= nbk_row ? b : nbk_row - 4;
+        if constexpr (BK16) {
+            const uint2 v = *reinterpret_cast<const uint2*>(bkeys16 + bq);
+            raw[0] = v.x; raw[1] = v.y;
+        } else {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(bkeys + bq);
+            raw[0] = v[0]; raw[1] = v[1]; raw[2] = v[2]; raw[3] = v[3];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t bc = b + e < blk_hi ? b + e : blk_hi - 1;
+            if constexpr (BK16) {
+                const uint32_t k = bkeys16[bc];
+                if (e & 1) raw[e >> 1] |= k << 16;
+                else raw[e >> 1] = k;
+            } else {
+                raw[e] = bkeys[bc];
+            }
+        }
+    }
+}
+
+template <bool BK16>
+__device__ __forceinline__ uint32_t rescore_take(const uint32_t (&raw)[BK16 ? 2 : 4], int64_t b, int64_t blk_hi,
+                                                 uint32_t b1) {
+    uint32_t tk = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t k = BK16 ? (e & 1 ? raw[e >> 1] & 0xffff0000u : raw[e >> 1] << 16) : raw[e];
+        if (b + e < blk_hi && k != 0u && (k >> 20) >= b1) tk |= 1u << e;
+    }
+    return tk;
+}
+
+// Appends the queued blocks of one group (tk: this lane's bits for blocks b .. b + 3) to q8 at n_q, in
+// column order, and returns how many the wave queued.  Each lane's place is the number of queued
+// blocks of the lanes before it: the prefix sum of the lane counts (0..4) from their three bit planes.
+__device__ __forceinline__ int rescore_queue(int32_t* q8, int n_q, uint32_t tk, int64_t b) {
+    const uint32_t c = (uint32_t)__builtin_popcount(tk);
+    const uint64_t m0 = __ballot(c & 1u), m1 = __ballot(c & 2u), m2 = __ballot(c & 4u);
+    auto below = [](uint64_t m) {
+        return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    };
+    int at = n_q + (int)(below(m0) + 2u * below(m1) + 4u * below(m2));
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (tk & (1u << e)) q8[at++] = (int32_t)(b + e);
+    return __builtin_popcountll(m0) + 2 * __builtin_popcountll(m1) + 4 * __builtin_popcountll(m2);
+}
+
+template <class KF, bool BK16, bool VEC>
 __global__ __launch_bounds__(256) void indexer_rescore_kernel(const IndexParams p, const uint32_t* b1_in, int chunk,
                                                               int nseg, uint32_t* cand_keys, int32_t* cand_cols,
                                                               uint32_t* seg_count) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * KF::kRowBytes];
     __shared__ uint32_t scl_all[4][KF::kScaleInScore ? 1 : 64];
     __shared__ int32_t queue[4][kRescoreQueue];
+    constexpr int KW = BK16 ? 2 : 4;  // dwords of a lane's four keys
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, li = lane & 15;
@@ -833,14 +895,25 @@ __global__ __launch_bounds__(256) void indexer_rescore_kernel(const IndexParams 
     const uint32_t b1 = __builtin_amdgcn_readfirstlane(b1_in[r]);
     const int64_t c_lo = (int64_t)seg * chunk;
     const int64_t c_hi = c_lo + chunk < n_valid ? c_lo + chunk : n_valid;
+    if (c_hi <= c_lo) {  // nothing visible in this segment
+        if (lane == 0) seg_count[(int64_t)r * nseg + seg] = 0u;
+        return;
+    }
     const int64_t nbk_row = (p.width + kKeyBlock - 1) / kKeyBlock;
     const uint32_t* bkeys = p.block_keys + (int64_t)r * nbk_row;
     const uint16_t* bkeys16 = reinterpret_cast<const uint16_t*>(p.block_keys) + (int64_t)r * nbk_row;
+    const int64_t blk_lo = c_lo / kKeyBlock, blk_hi = (c_hi + kKeyBlock - 1) / kKeyBlock;
     uint32_t* okeys = cand_keys + ((int64_t)r * nseg + seg) * chunk;
     int32_t* ocols = cand_cols + ((int64_t)r * nseg + seg) * chunk;
     uint8_t* my = stage[wave];
     uint32_t* scl = scl_all[wave];
     int32_t* q8 = queue[wave];
+
+    // The first keys are in flight before the query is loaded: queueing needs only the keys.
+    uint32_t raw[kRescoreGroups][KW];
+#pragma unroll
+    for (int i = 0; i < kRescoreGroups; ++i)
+        rescore_load_keys<BK16, VEC>(bkeys, bkeys16, blk_lo + 256 * i + 4 * lane, blk_hi, nbk_row, raw[i]);
 
     i32x8 qa[4];
     uint32_t qs[4];
@@ -848,7 +921,7 @@ __global__ __launch_bounds__(256) void indexer_rescore_kernel(const IndexParams 
     load_query<KF>(p, r, g, li, qa, qs, wr);
     const bool q_nan = KF::query_nan(qa, qs);
     // the row's visible key rows and their scales; loads beyond them return zeros
-    const int n_rows = (int)(n_valid > 0 ? n_valid : 0);
+    const int n_rows = (int)n_valid;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.k) + base * KF::kRowBytes), (short)0,
         n_rows * KF::kRowBytes, kRsrcWord3);
@@ -902,73 +975,85 @@ __global__ __launch_bounds__(256) void indexer_rescore_kernel(const IndexParams 
         n_out += (uint32_t)__builtin_popcountll(m);
     };
     StepLoads la, lb;
+    // Re-scores queue entries 0 .. n_q - 1.  The first four steps run straight-line with the next
+    // step's loads in flight: every issue is unconditional (an empty step's loads fall past the
+    // descriptors and return zeros) so the loads keep one order on every path and the compiler waits
+    // for exactly the older step; only the arithmetic is skipped for empty steps.  (In a loop the
+    // compiler loses that order at the back edge and waits for both steps.)  Further steps, rare, run
+    // one at a time.
+    auto drain = [&](int n_q) {
+        auto cnt_at = [&](int h) { return n_q - h < 8 ? n_q - h : 8; };  // <= 0: an empty step
+        issue(0, cnt_at(0), la);
+        issue(8, cnt_at(8), lb);
+        if (n_q > 0) finish(0, cnt_at(0), la);
+        issue(16, cnt_at(16), la);
+        if (n_q > 8) finish(8, cnt_at(8), lb);
+        issue(24, cnt_at(24), lb);
+        if (n_q > 16) finish(16, cnt_at(16), la);
+        if (n_q > 24) finish(24, cnt_at(24), lb);
+        for (int h = 32; h < n_q; h += 8) {
+            issue(h, cnt_at(h), la);
+            finish(h, cnt_at(h), la);
+        }
+    };
 
-    if (c_hi > c_lo) {
-        const int64_t blk_lo = c_lo / kKeyBlock, blk_hi = (c_hi + kKeyBlock - 1) / kKeyBlock;
-        for (int64_t b0 = blk_lo; b0 < blk_hi; b0 += kRescoreQueue) {
-            // All loads first, unconditional (past the end: the segment's last block, dropped below), so
-            // they are in flight together; 16-bit keys are their top halves, which carry the bins
-            // compared below.
-            uint32_t bk[kRescoreBatch];
+    for (int64_t b0 = blk_lo;;) {
+        uint32_t tk[kRescoreGroups];
+        int total = 0;
 #pragma unroll
-            for (int i = 0; i < kRescoreBatch; ++i) {
-                const int64_t b = b0 + 64 * i + lane;
-                const int64_t bc = b < blk_hi ? b : blk_hi - 1;
-                bk[i] = BK16 ? (uint32_t)bkeys16[bc] : bkeys[bc];
-            }
+        for (int i = 0; i < kRescoreGroups; ++i) {
+            tk[i] = rescore_take<BK16>(raw[i], b0 + 256 * i + 4 * lane, blk_hi, b1);
+            total += (int)__builtin_popcount(tk[i]);
+        }
 #pragma unroll
-            for (int i = 0; i < kRescoreBatch; ++i)
-                bk[i] = b0 + 64 * i + lane < blk_hi ? (BK16 ? bk[i] << 16 : bk[i]) : 0u;
-            int n_q = 0;  // wave-uniform queue length
+        for (int o = 1; o < 64; o <<= 1) total += (int)shfl_xor((uint32_t)total, o);
+        total = __builtin_amdgcn_readfirstlane(total);
+        if (total <= kRescoreQueue) {  // the usual case: one queue for all groups
+            int n_q = 0;
 #pragma unroll
-            for (int i = 0; i < kRescoreBatch; ++i) {
-                const bool take = bk[i] != 0u && (bk[i] >> 20) >= b1;
-                const uint64_t m = __ballot(take);
-                if (take)
-                    q8[n_q + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
-                        (int32_t)(b0 + 64 * i + lane);
-                n_q += __builtin_popcountll(m);
-            }
-            auto cnt_at = [&](int h) { return n_q - h < 8 ? n_q - h : 8; };  // <= 0: an empty step
-            // The first four steps run straight-line with the next step's loads in flight: every
-            // issue is unconditional (an empty step's loads fall past the descriptors and return
-            // zeros) so the loads keep one order on every path and the compiler waits for exactly
-            // the older step; only the arithmetic is skipped for empty steps.  (In a loop the
-            // compiler loses that order at the back edge and waits for both steps.)  Further steps,
-            // rare, run one at a time.
-            issue(0, cnt_at(0), la);
-            issue(8, cnt_at(8), lb);
-            if (n_q > 0) finish(0, cnt_at(0), la);
-            issue(16, cnt_at(16), la);
-            if (n_q > 8) finish(8, cnt_at(8), lb);
-            issue(24, cnt_at(24), lb);
-            if (n_q > 16) finish(16, cnt_at(16), la);
-            if (n_q > 24) finish(24, cnt_at(24), lb);
-            for (int h = 32; h < n_q; h += 8) {
-                issue(h, cnt_at(h), la);
-                finish(h, cnt_at(h), la);
+            for (int i = 0; i < kRescoreGroups; ++i) n_q += rescore_queue(q8, n_q, tk[i], b0 + 256 * i + 4 * lane);
+            drain(n_q);
+        } else {  // heavy ties: a group at a time, its keys read again
+            for (int i = 0; i < kRescoreGroups; ++i) {
+                uint32_t rw[KW];
+                const int64_t b = b0 + 256 * i + 4 * lane;
+                rescore_load_keys<BK16, VEC>(bkeys, bkeys16, b, blk_hi, nbk_row, rw);
+                drain(rescore_queue(q8, 0, rescore_take<BK16>(rw, b, blk_hi, b1), b));
             }
         }
+        b0 += 256 * kRescoreGroups;
+        if (b0 >= blk_hi) break;
+#pragma unroll
+        for (int i = 0; i < kRescoreGroups; ++i)
+            rescore_load_keys<BK16, VEC>(bkeys, bkeys16, b0 + 256 * i + 4 * lane, blk_hi, nbk_row, raw[i]);
     }
     if (lane == 0) seg_count[(int64_t)r * nseg + seg] = n_out;
+}
+
+template <class KF, bool BK16>
+static void launch_rescore_kf(const IndexParams& p, bool vec, dim3 grid, const uint32_t* b1, int chunk, int nseg,
+                              uint32_t* cand_keys, int32_t* cand_cols, uint32_t* seg_count, hipStream_t stream) {
+    if (vec)
+        hipLaunchKernelGGL((indexer_rescore_kernel<KF, BK16, true>), grid, dim3(256), 0, stream, p, b1, chunk, nseg,
+                           cand_keys, cand_cols, seg_count);
+    else
+        hipLaunchKernelGGL((indexer_rescore_kernel<KF, BK16, false>), grid, dim3(256), 0, stream, p, b1, chunk, nseg,
+                           cand_keys, cand_cols, seg_count);
 }
 
 hipError_t launch_indexer_rescore(const IndexParams& p, int rows, int dtype, const uint32_t* b1, int chunk, int nseg,
                                   uint32_t* cand_keys, int32_t* cand_cols, uint32_t* seg_count, hipStream_t stream) {
     const dim3 grid((unsigned)((nseg + 3) / 4), (unsigned)rows);
+    const int64_t nbk_row = (p.width + kKeyBlock - 1) / kKeyBlock;
+    const bool vec = nbk_row >= 4 && nbk_row % 4 == 0 && reinterpret_cast<uintptr_t>(p.block_keys) % 16 == 0;
     if (dtype == CSA2_FP4_E2M1 && p.bk16)
-        hipLaunchKernelGGL((indexer_rescore_kernel<Fp4Keys, true>), grid, dim3(256), 0, stream, p, b1, chunk, nseg,
-                           cand_keys, cand_cols, seg_count);
+        launch_rescore_kf<Fp4Keys, true>(p, vec, grid, b1, chunk, nseg, cand_keys, cand_cols, seg_count, stream);
     else if (dtype == CSA2_FP4_E2M1)
-        hipLaunchKernelGGL((indexer_rescore_kernel<Fp4Keys, false>), grid, dim3(256), 0, stream, p, b1, chunk, nseg,
-                           cand_keys, cand_cols, seg_count);
+        launch_rescore_kf<Fp4Keys, false>(p, vec, grid, b1, chunk, nseg, cand_keys, cand_cols, seg_count, stream);
     else if (p.bk16)
-        hipLaunchKernelGGL((indexer_rescore_kernel<Fp8Keys, true>), grid, dim3(256), 0, stream, p, b1, chunk, nseg,
-                           cand_keys, cand_cols, seg_count);
+        launch_rescore_kf<Fp8Keys, true>(p, vec, grid, b1, chunk, nseg, cand_keys, cand_cols, seg_count, stream);
     else
-        hipLaunchKernelGGL((indexer_rescore_kernel<Fp8Keys, false>), grid, dim3(256), 0, stream, p, b1, chunk, nseg,
-                           cand_keys, cand_cols, seg_count);
+        launch_rescore_kf<Fp8Keys, false>(p, vec, grid, b1, chunk, nseg, cand_keys, cand_cols, seg_count, stream);
     return hipGetLastError();
 }
 

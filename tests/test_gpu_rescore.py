@@ -57,6 +57,10 @@ CASES = {
     "ratio2": (CONFIGS["lowp_full_decode_1m"].replace(batch=4, q_tokens=4, context=80001, ratio=2, ragged=True), 512),
     "ties": (CONFIGS["lowp_full_decode_1m"].replace(batch=4, q_tokens=4, context=40000), 512),
     "full_1m": (CONFIGS["lowp_full_decode_1m"].replace(batch=3, q_tokens=3), 512),
+    # every key row equal: every block queued (more blocks in a segment than the re-score's queue holds)
+    "all_equal": (CONFIGS["lowp_full_decode_1m"].replace(batch=4, q_tokens=4, context=40000), 512),
+    # 128 rows of 600000 columns: segments of 19456 columns, more block keys than one wave loads at once
+    "wide_segments": (CONFIGS["lowp_full_decode_1m"].replace(batch=128, q_tokens=128, context=600000), 512),
     "k1_short_rows": (CONFIGS["lowp_full_decode_1m"].replace(batch=5, q_tokens=5, context=60000, ragged=True), 1),
     # MXFP4 index plane and query
     "mx_ragged_100k": (_MX.replace(batch=6, q_tokens=6, context=100003, ragged=True), 512),
@@ -68,8 +72,8 @@ CASES = {
 }
 
 
-BK16_CASES = ["ragged_100k", "short_rows", "k2048", "ties", "full_1m", "k1_short_rows", "mx_short_rows", "mx_ties",
-              "mx_full_1m"]
+BK16_CASES = ["ragged_100k", "short_rows", "k2048", "ties", "full_1m", "k1_short_rows", "all_equal", "wide_segments",
+              "mx_short_rows", "mx_ties", "mx_full_1m"]
 
 
 @pytest.mark.parametrize("name,bk16", [(n, False) for n in CASES] + [(n, True) for n in BK16_CASES])
@@ -89,13 +93,22 @@ def test_score_free_matches_written_scores(name, bk16):
         kI[:, ::40] = kI[:, 17:18]
         sc = x["kI_scale"].view(rows, -1, *x["kI_scale"].shape[2:])
         sc[:, ::40] = sc[:, 17:18]
+    if name == "all_equal":
+        kI = x["kI"].view(rows, -1, x["kI"].shape[-1])
+        kI[:] = kI[:, 17:18]
+        sc = x["kI_scale"].view(rows, -1, *x["kI_scale"].shape[2:])
+        sc[:] = sc[:, 17:18]
     assert csa2.topk_rescore_supported(rows, cfg.width, k, fp8=cfg.idx_dtype == "fp8", fp4=cfg.idx_dtype == "fp4")
     bkeys, out = _score_free(cfg, x, k, bk16)
 
     scores = gpu_scores(cfg, x)
     ref_idx = gpu_topk(cfg, x, scores, k=k)
     s_np = scores.cpu().numpy()
-    valid = np.isfinite(oracle_score_bound(cfg, x, np.arange(rows)))
+    if rows <= 16:
+        valid = np.isfinite(oracle_score_bound(cfg, x, np.arange(rows)))
+    else:  # the columns each row sees (finite inputs: the same mask, without the float64 bound of every score)
+        nv = (x["pos"].cpu().numpy().astype(np.int64) + 1) // cfg.ratio
+        valid = np.arange(cfg.width)[None, :] < nv[:, None]
     keys = np.where(valid, _order_keys(s_np), 0).astype(np.uint32)
     pad = (-cfg.width) % 8
     want_bk = np.pad(keys, ((0, 0), (0, pad))).reshape(rows, -1, 8).max(axis=2)
@@ -152,6 +165,11 @@ def test_score_free_bf16_chunk_matches_written_scores(name):
         kI = x["kI"]
         kI[::40] = kI[17:18]          # every 40th key row equals row 17: equal scores across blocks
         kI[5::40] = kI[17:18]
+    if name == "all_equal":
+        kI = x["kI"].view(rows, -1, x["kI"].shape[-1])
+        kI[:] = kI[:, 17:18]
+        sc = x["kI_scale"].view(rows, -1, *x["kI_scale"].shape[2:])
+        sc[:] = sc[:, 17:18]
     assert csa2.topk_rescore_supported(rows, cfg.width, k, fp8=False, fp4=False, shared_plane=True)
     dev = x["pos"].device
     bkeys = torch.full((rows, -(-cfg.width // 8)), 12345, dtype=torch.int32, device=dev)
@@ -165,7 +183,11 @@ def test_score_free_bf16_chunk_matches_written_scores(name):
     ref_idx = gpu_topk(cfg, x, scores, k=k)
     torch.cuda.synchronize()
     s_np = scores.cpu().numpy()
-    valid = np.isfinite(oracle_score_bound(cfg, x, np.arange(rows)))
+    if rows <= 16:
+        valid = np.isfinite(oracle_score_bound(cfg, x, np.arange(rows)))
+    else:  # the columns each row sees (finite inputs: the same mask, without the float64 bound of every score)
+        nv = (x["pos"].cpu().numpy().astype(np.int64) + 1) // cfg.ratio
+        valid = np.arange(cfg.width)[None, :] < nv[:, None]
     keys = np.where(valid, _order_keys(s_np), 0).astype(np.uint32)
     pad = (-cfg.width) % 8
     want_bk = np.pad(keys, ((0, 0), (0, pad))).reshape(rows, -1, 8).max(axis=2)
