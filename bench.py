@@ -155,7 +155,7 @@ def roofline_of(work, ms):
 
 KERNEL_SOURCES = {
     "indexer_score": ["indexer.hip", "common.hpp", "kernels.hpp"],
-    "topk_select": ["topk.hip", "common.hpp", "kernels.hpp"],
+    "topk_select": ["topk.hip", "indexer.hip", "common.hpp", "kernels.hpp"],  # the score-free select re-scores
     "candidate_pool": ["topk.hip", "pool.hip", "common.hpp", "kernels.hpp"],
     "compress": ["compress.hip", "common.hpp", "kernels.hpp"],
     "sparse_attn": ["attention.hip", "common.hpp", "kernels.hpp"],
@@ -287,6 +287,10 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also time the same step captured once in a HIP graph and replayed (reported under "
                          "\"graph\"; value stays the eager launches)")
+    ap.add_argument("--topk-route", choices=["auto", "scores", "score-free"], default="auto",
+                    help="how the FULL layer's top-k is found: auto (score-free for wide FP8/MXFP4 rows, written "
+                         "scores otherwise), scores (write the score rows, then topk_select) or score-free (block "
+                         "keys only, then topk_rescore; the prefill chunk's BF16 rows take it only when asked)")
     ap.add_argument("--calibrate", action="store_true",
                     help="after the bench, run a plain 1 GiB float32 copy kernel 3 times (the reference for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE scaling: 1 GiB read + 1 GiB written per launch)")
@@ -309,7 +313,8 @@ def main():
 
     rows = x["pos"].shape[0]
     # Arguments are marshalled once; each step only crosses into the library.
-    step_calls = Step(cfg, x)
+    route = {"auto": None, "scores": False, "score-free": True}[args.topk_route]
+    step_calls = Step(cfg, x, score_free=route)
     names = list(step_calls.groups)
     flush = args.flush == "on" or (args.flush == "auto" and cfg.name in FLUSH_DEFAULT)
     flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if flush else None
@@ -415,7 +420,7 @@ def main():
         # replayed K times: the kernels are the same, the launches come from the graph.
         gs = torch.cuda.Stream()
         with torch.cuda.stream(gs):
-            g_step = Step(cfg, x)
+            g_step = Step(cfg, x, score_free=route)
             g_step()
         gs.synchronize()
         graph = torch.cuda.CUDAGraph()
