@@ -36,14 +36,17 @@ def _record(cfg, x, **fields):
         json.dump(rec, f, indent=1, sort_keys=True)
 
 # (workload, seed, ragged positions).  The two 1M decodes the measurements name run seeds 0, 1 and 2
-# plus a ragged-position batch; the 64K decode runs a ragged batch as well.
-CASES = [("tiny_full_fp32", 2, False), ("full_decode_64k", 2, False), ("full_decode_64k", 1, True),
-         ("prefill_4096_at_128k", 2, False),
+# plus a ragged-position batch; the 64K decode runs a ragged batch as well; the 64K decode, the prefill
+# chunk and the pages' formats run a second seed.
+CASES = [("tiny_full_fp32", 2, False), ("full_decode_64k", 2, False), ("full_decode_64k", 0, False),
+         ("full_decode_64k", 1, True),
+         ("prefill_4096_at_128k", 2, False), ("prefill_4096_at_128k", 0, False),
          ("reindex_decode_1m", 0, False), ("reindex_decode_1m", 1, False), ("reindex_decode_1m", 2, False),
          ("reindex_decode_1m", 3, True), ("reindex_fp8_decode_1m", 2, False), ("reindex_pages_decode_1m", 2, False),
          ("lowp_full_decode_1m", 0, False), ("lowp_full_decode_1m", 1, False), ("lowp_full_decode_1m", 2, False),
          ("lowp_full_decode_1m", 3, True),
-         ("lowp_pool_decode_1m", 2, False), ("pages_fp4_decode_1m", 2, False), ("lowp_owner_decode_1m", 2, False),
+         ("lowp_pool_decode_1m", 2, False), ("pages_fp4_decode_1m", 2, False), ("pages_fp4_decode_1m", 0, False),
+         ("lowp_owner_decode_1m", 2, False),
          ("prefill_owner_4096_at_128k", 2, False)]
 
 
