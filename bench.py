@@ -2,6 +2,7 @@
 """Throughput of the CSA2 hot path on one MI355X, with roofline and CPU-oracle baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+                    [--topk-route auto|scores|score-free] [--flush auto|on|off] [--graph] [--calibrate]
 
 A step is one pass of the whole path over one batch of synthetic inputs that
 are already resident in HBM:
@@ -11,7 +12,9 @@ are already resident in HBM:
             builds the REINDEX candidate pool adds candidate_pool from the block
             scores the indexer wrote)
   prefill : indexer_score -> topk_select -> sparse_attn_prefill for the FULL
-            layer and every REUSE layer (same indices, own q / SWA / sink)
+            layer and every REUSE layer (same indices, own q / SWA / sink);
+            --topk-route score-free takes the chunk's score-free route instead
+            (block keys, the best blocks re-scored, exact select)
 The default workload is the 1M-context low-precision decode (64 sequences,
 FP8 index plane, FP4 main plane, FP8 SWA ring).  Prints one JSON line.
 
